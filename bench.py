@@ -1,0 +1,167 @@
+#!/usr/bin/env python3
+"""Benchmark of the k-d tree build on one MI355X.
+
+One step = one complete build (every round's radix passes and tag updates,
+the column copy and the level-order placement) of the headline workload:
+N = 16,777,216 points, k = 3, float32, from a 64-component Gaussian mixture
+with 5% of coordinates snapped to a 2^-10 grid (seed 3). Inputs, outputs and
+the workspace are resident in HBM before the timed region starts.
+
+Prints ONE JSON line on stdout (progress goes to stderr):
+  value      whole-job build throughput, Mpoints/s (= N / seconds per build)
+  roofline   the dominant kernel's algorithmic bytes per launch / its average
+             launch duration (HIP events on the build's stream), against the
+             8 TB/s HBM peak
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published figure
+
+
+def log(msg):
+    sys.stderr.write(msg + "\n")
+    sys.stderr.flush()
+
+
+def cpu_baseline(name, sample_n):
+    import oracle  # test infrastructure, used only for this reported baseline
+    from tree_construction_amd import datagen
+    pts = datagen.generate(name, n=sample_n)
+    oracle.load_lib()
+    t0 = time.perf_counter()
+    oracle.build_tree(pts)
+    dt = time.perf_counter() - t0
+    w = datagen.WORKLOADS[name]
+    return {"value": round(sample_n / dt / 1e6, 3), "unit": "Mpoints/s",
+            "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": "same recipe and seed as %s at N=%d (k=%d), %.1f s wall"
+                      % (name, sample_n, w.k, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=1 << 22)
+    ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event loop")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        log("bench.py: this build runs on one GPU only (no multi-GPU path); "
+            "run it with --gpus 1")
+        sys.exit(2)
+
+    import torch
+    from tree_construction_amd import datagen, kdt
+
+    name = args.workload or datagen.HEADLINE
+    w = datagen.WORKLOADS[name]
+    log("bench: generating %s (%s)" % (name, w.note))
+    pts = datagen.cached(name)
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(pts).to(dev)
+    n, k = pts.shape
+    builder = kdt.Builder(n, k, dev)
+    perm = torch.empty(n, dtype=torch.int32, device=dev)
+    tree = torch.empty_like(x)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize(dev)
+
+    log("bench: %d warmup builds" % args.warmup)
+    for _ in range(args.warmup):
+        builder.build(x, perm, tree)
+    torch.cuda.synchronize(dev)
+
+    log("bench: timing %d builds" % args.steps)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        builder.build(x, perm, tree)
+    stop.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    ms_per_step = start.elapsed_time(stop) / args.steps
+    value = n / (ms_per_step * 1e-3) / 1e6
+    log("bench: %.3f ms/build (wall %.3f ms), %.1f Mpoints/s"
+        % (ms_per_step, wall * 1e3 / args.steps, value))
+
+    roofline, kernels = None, None
+    if not args.no_profile:
+        log("bench: per-kernel event timing over %d builds" % args.steps)
+        agg = {}
+        for _ in range(args.steps):
+            for kind, rec in builder.build_profiled(x, perm, tree).items():
+                a = agg.setdefault(kind, {"launches": 0, "ms": 0.0, "bytes": 0.0})
+                for f in a:
+                    a[f] += rec[f]
+        kernels = {}
+        for kind, a in agg.items():
+            if a["launches"] == 0:
+                continue
+            per_launch_ms = a["ms"] / a["launches"]
+            gbs = a["bytes"] / (a["ms"] * 1e-3) / 1e9 if a["ms"] > 0 else 0.0
+            kernels[kind] = {"launches_per_build": a["launches"] // args.steps,
+                             "avg_us": round(per_launch_ms * 1e3, 2),
+                             "ms_per_build": round(a["ms"] / args.steps, 4),
+                             "bytes_per_launch": int(a["bytes"] / a["launches"]),
+                             "GBps": round(gbs, 1)}
+        dom = max(kernels, key=lambda kk: kernels[kk]["ms_per_build"])
+        d = kernels[dom]
+        achieved = d["GBps"]
+        roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": dom, "avg_us": d["avg_us"], "bytes_per_launch": d["bytes_per_launch"]}
+        passes = [kk for kk in kernels if kk.startswith("sweep") or kk == "hist"]
+        tot_b = sum(agg[kk]["bytes"] for kk in passes)
+        tot_ms = sum(agg[kk]["ms"] for kk in passes)
+        roofline["sort_and_update_passes"] = {
+            "GBps": round(tot_b / (tot_ms * 1e-3) / 1e9, 1),
+            "frac": round(tot_b / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        for kind, kv in sorted(kernels.items()):
+            log("  %-12s %4d/build  avg %8.2f us  %8.1f GB/s  %.3f ms/build"
+                % (kind, kv["launches_per_build"], kv["avg_us"], kv["GBps"], kv["ms_per_build"]))
+
+    base = None
+    if not args.no_cpu_baseline:
+        log("bench: CPU oracle baseline on %d points" % args.cpu_sample)
+        base = cpu_baseline(name, args.cpu_sample)
+        log("  %s" % base)
+
+    out = {
+        "metric": "k-d tree build Mpoints/s at N=16M k=3 fp32; achieved HBM GB/s vs peak",
+        "value": round(value, 2),
+        "unit": "Mpoints/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u64",
+        "data": "synthetic",
+        "config": {"workload": name, "n_points": n, "k": k, "coords": "f32",
+                   "description": w.note},
+        "roofline": roofline,
+        "cpu_baseline": base,
+        "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

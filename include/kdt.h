@@ -1,0 +1,125 @@
+/*
+ * kdt.h -- C ABI of the MI355X (gfx950) left-balanced k-d tree builder.
+ *
+ * What it builds: the left-balanced, complete k-d tree over N points of
+ * dimension k, stored in level order with no pointers (node s has children
+ * 2s+1 and 2s+2; node s on level l = floor(log2(s+1)) splits in dimension
+ * l mod k), as defined in I. Wald, "GPU-friendly, Parallel, and
+ * (Almost-)In-Place Construction of Left-Balanced k-d Trees" (arXiv
+ * 2211.00120): the problem statement (k-d condition plus balancing
+ * condition), the indexing paragraph (level-order ids, lChild/rChild, level,
+ * numLevels, F(l)) and the assumptions paragraph (dimension l mod k).
+ * Coordinates are ordered by IEEE '<' (so -0.0 == +0.0) with the original
+ * point index as the tie-break, which makes the tree unique.
+ *
+ * How: the paper's tag-based "trickle-down" construction. Every point
+ * carries a 32-bit tag, the id of its ancestor on the current level (tag
+ * paragraph); each round sorts all points by (tag, coordinate l mod k,
+ * original index) and refines every tag from the closed-form subtree sizes
+ * and segment starts (sort-order and sb/ss paragraphs). Rounds run on the
+ * GPU as LSD radix passes over 64-bit keys with a fused tag update.
+ *
+ * Conventions for every entry point:
+ *   - All pointers marked "device" are HIP device pointers on the current
+ *     device. The caller owns every buffer; the library allocates nothing,
+ *     keeps no global state and is re-entrant: calls on different streams
+ *     with different workspaces may run concurrently.
+ *   - All work is enqueued on `stream` (0 = the null stream) and the call
+ *     returns before it finishes; synchronise the stream before reading
+ *     outputs. Argument errors are detected before anything is enqueued.
+ *   - Limits: 0 <= N <= 2^31 - 1, 1 <= k <= 65535. NaN coordinates are
+ *     outside the definition: the build stays in bounds and returns some
+ *     permutation, but which one is unspecified.
+ */
+#ifndef KDT_H
+#define KDT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as HIP's hipStream_t (redeclaring an identical typedef is legal). */
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum {
+    KDT_OK = 0,
+    KDT_ERR_INVALID_ARG = 1, /* bad N or k, NULL pointer, overlapping buffers */
+    KDT_ERR_WORKSPACE = 2,   /* workspace NULL or smaller than kdt_workspace_size() */
+    KDT_ERR_HIP = 3          /* a kernel launch failed (hipGetLastError) */
+} kdt_status;
+
+/* Bytes of device workspace kdt_build() needs for N points of dimension k.
+ * Pure host arithmetic, no HIP call. Returns 0 when N or k is out of range
+ * (and for N <= 1, which needs none). */
+size_t kdt_workspace_size(int64_t N, int32_t k);
+
+/* Build the tree.
+ *   points    device, N*k float32, row-major: point i's coordinate d is
+ *             points[i*k + d]. Read only.
+ *   perm_out  device, N int32: perm_out[s] = original index of the point at
+ *             level-order node s.
+ *   tree_out  device, N*k float32 or NULL: tree_out[s*k + d] =
+ *             points[perm_out[s]*k + d], a bit copy (-0.0 stays -0.0).
+ *   workspace device, at least kdt_workspace_size(N, k) bytes, 256-byte
+ *             aligned; its contents on entry do not matter and are
+ *             clobbered. May be NULL when N <= 1.
+ * perm_out and tree_out must not overlap points, each other or the
+ * workspace. On any error the outputs are unspecified. */
+kdt_status kdt_build(const float* points, int64_t N, int32_t k,
+                     int32_t* perm_out, float* tree_out,
+                     void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/* Diagnostic: run only the first `rounds` sort+update rounds (0 <= rounds
+ * <= numLevels(N) - 1) and copy every point's tag to tags_out (device, N
+ * uint32, indexed by original point index). After r rounds the tag of a
+ * point is its final node's ancestor on level r (or the node itself when it
+ * sits on a level < r), as the paper's tag paragraph states. Same workspace
+ * and error rules as kdt_build. */
+kdt_status kdt_debug_tags(const float* points, int64_t N, int32_t k, int32_t rounds,
+                          uint32_t* tags_out, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/* Per-kernel-kind timing of one build, for benchmarking. */
+#define KDT_PROFILE_MAX_KINDS 8
+typedef struct {
+    int32_t kinds;                        /* entries filled below */
+    char name[KDT_PROFILE_MAX_KINDS][24]; /* kernel kind, e.g. "sweep_mid" */
+    int64_t launches[KDT_PROFILE_MAX_KINDS];
+    double ms[KDT_PROFILE_MAX_KINDS];     /* summed GPU duration (HIP events) */
+    double bytes[KDT_PROFILE_MAX_KINDS];  /* summed algorithmic bytes: each array
+                                             a kernel must read or write, once */
+} kdt_profile;
+
+/* kdt_build with a HIP event pair recorded on `stream` around every kernel
+ * launch. Synchronises the stream before returning, then fills *profile
+ * (durations include only GPU time between each pair). Same arguments and
+ * errors as kdt_build, plus KDT_ERR_INVALID_ARG for profile == NULL. */
+kdt_status kdt_build_profiled(const float* points, int64_t N, int32_t k,
+                              int32_t* perm_out, float* tree_out,
+                              void* workspace, size_t workspace_bytes,
+                              hipStream_t stream, kdt_profile* profile);
+
+/* Host copies of the closed forms the kernels evaluate (no HIP call), for
+ * tests: the size of level-order subtree s in a complete tree of N nodes
+ * (0 if s >= N), and the first sorted position of subtree s's points after
+ * the round that fixes level l (s on level l, 0 <= l <= numLevels(N) - 1;
+ * returns -1 when s is not on level l or the arguments are out of range). */
+int64_t kdt_closed_subtree_size(int64_t N, int64_t s);
+int64_t kdt_closed_segment_begin(int64_t N, int64_t s, int32_t l);
+
+/* Number of radix passes the round that fixes level l uses (keys of
+ * 32 + tag bits, 8 bits per pass); -1 when l is out of range for N. */
+int32_t kdt_round_passes(int64_t N, int32_t l);
+
+/* Static description of a status code. */
+const char* kdt_status_string(kdt_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDT_H */

@@ -1,0 +1,115 @@
+"""Host-side tests of the C ABI (no GPU: nothing here launches a kernel).
+
+* libkdt.so loads and exports every function include/kdt.h declares;
+* the closed forms the kernels evaluate (subtree size, segment begin) equal
+  the oracle's counting definition and the prefix-sum definition;
+* workspace sizing and argument validation return the documented codes
+  before anything is enqueued.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from tree_construction_amd import kdt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "kdt.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kdt_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(kdt.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    handle = ctypes.CDLL(kdt.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(handle, name), name
+
+
+def test_closed_subtree_size_matches_counting():
+    for N in list(range(1, 200)) + [1000, 4095, 4096, 4097, (1 << 20) + 12345]:
+        cs = [c for c in range(min(N, 200))] + [N - 1, N, 2 * N + 1]
+        for c in cs:
+            assert kdt.closed_subtree_size(N, c) == oracle.subtree_size(N, c), (N, c)
+    rng = np.random.default_rng(0)
+    for N in rng.integers(1, 2**31 - 1, 50):
+        for c in rng.integers(0, N, 20):
+            assert kdt.closed_subtree_size(int(N), int(c)) == oracle.subtree_size(int(N), int(c))
+
+
+def test_closed_segment_begin_is_prefix_sum():
+    """Start of subtree s's points after the round fixing level l: the F(l)
+    fixed nodes, then every level-l subtree to the left of s."""
+    for N in list(range(1, 130)) + [1000, 5000, 65537]:
+        levels = N.bit_length()
+        for l in range(levels):
+            first = (1 << l) - 1
+            pos = first
+            for s in range(first, min(2 * first + 1, N)):
+                assert kdt.closed_segment_begin(N, s, l) == pos, (N, s, l)
+                pos += oracle.subtree_size(N, s)
+    assert kdt.closed_segment_begin(10, 3, 1) == -1  # node 3 is on level 2
+
+
+def test_round_passes():
+    assert kdt.round_passes(1, 0) == -1
+    assert kdt.round_passes(2, 0) == 4
+    assert kdt.round_passes(2, 1) == -1
+    n = 1 << 24  # 25 levels, 24 rounds
+    got = [kdt.round_passes(n, l) for l in range(24)]
+    assert got == [4] + [5] * 7 + [6] * 8 + [7] * 8
+    assert sum(got) == 143
+
+
+def test_workspace_size():
+    assert kdt.workspace_size(0, 3) == 0
+    assert kdt.workspace_size(1, 3) == 0
+    assert kdt.workspace_size(2, 0) == 0
+    assert kdt.workspace_size(-1, 3) == 0
+    assert kdt.workspace_size(2**31, 3) == 0
+    a = kdt.workspace_size(1 << 20, 3)
+    b = kdt.workspace_size(1 << 21, 3)
+    assert 0 < a < b
+    assert a % 256 == 0
+
+
+FAKE = 1 << 40  # never dereferenced: validation fails before any launch
+
+
+@pytest.mark.parametrize("args,code", [
+    ((FAKE, 10, 0, FAKE + 2**20, 0, FAKE + 2**21, 1 << 20, None), 1),   # k = 0
+    ((FAKE, -1, 3, FAKE + 2**20, 0, FAKE + 2**21, 1 << 20, None), 1),   # N < 0
+    ((FAKE, 2**31, 3, FAKE + 2**36, 0, FAKE + 2**37, 1 << 20, None), 1),  # N too big
+    ((0, 10, 3, FAKE + 2**20, 0, FAKE + 2**21, 1 << 20, None), 1),      # points NULL
+    ((FAKE, 10, 3, 0, 0, FAKE + 2**21, 1 << 20, None), 1),              # perm NULL
+    ((FAKE, 10, 3, FAKE + 2**20, 0, 0, 1 << 20, None), 2),              # workspace NULL
+    ((FAKE, 10, 3, FAKE + 2**20, 0, FAKE + 2**21, 16, None), 2),        # workspace small
+    ((FAKE, 10, 3, FAKE + 2**20, 0, FAKE + 2**21 + 4, 1 << 20, None), 2),  # misaligned
+    ((FAKE, 10, 3, FAKE + 8, 0, FAKE + 2**21, 1 << 20, None), 1),       # perm overlaps points
+    ((FAKE, 10, 3, FAKE + 2**20, FAKE + 2**20 + 16, FAKE + 2**21, 1 << 20, None), 1),  # tree/perm
+    ((FAKE, 10, 3, FAKE + 2**20, 0, FAKE, 1 << 20, None), 1),           # workspace overlaps
+    ((0, 0, 3, 0, 0, 0, 0, None), 0),                                   # N = 0: nothing to do
+])
+def test_build_rejects_bad_arguments_before_launch(args, code):
+    assert kdt.lib().kdt_build(*args) == code
+
+
+def test_debug_tags_rejects_bad_rounds():
+    ws = kdt.workspace_size(10, 3)
+    # 10 points -> 4 levels -> at most 3 rounds
+    assert kdt.lib().kdt_debug_tags(FAKE, 10, 3, 4, FAKE + 2**20, FAKE + 2**21, ws, None) == 1
+    assert kdt.lib().kdt_debug_tags(FAKE, 10, 3, -1, FAKE + 2**20, FAKE + 2**21, ws, None) == 1
+
+
+def test_status_strings():
+    for code in range(4):
+        assert kdt.lib().kdt_status_string(code)

@@ -1,0 +1,711 @@
+// Left-balanced k-d tree build for MI355X (gfx950): the tag-based
+// "trickle-down" construction of I. Wald, "GPU-friendly, Parallel, and
+// (Almost-)In-Place Construction of Left-Balanced k-d Trees" (arXiv
+// 2211.00120), cited as [W] with the paragraph that states each fact.
+//
+// Pipeline per build (all on the caller's stream, nothing allocated):
+//   k_init       AoS points -> one contiguous column per split dimension,
+//                clears the radix bookkeeping.
+//   per round l = 0 .. numLevels(N)-2  (round l fixes level l):
+//     k_hist     digit histograms of key = tag<<32 | fkey(x[l mod k]) for
+//                every radix pass of the round, from index order.
+//     k_onesweep P passes of a stable LSD radix sort, 8-bit digits; pass 0
+//                builds the keys from the tags and the column with the
+//                original index as payload, so equal (tag, coordinate)
+//                pairs stay in index order; the last pass does not write
+//                the sorted array but updates every tag in place from its
+//                sorted position.
+//   k_place      perm[tag[i]] = i and the level-order coordinate copy.
+//
+// The radix pass is a one-sweep design: per-tile digit counts from wave64
+// ballots (multi-split ranking), cross-tile offsets by decoupled look-back
+// over agent-scope atomics (Merrill & Garland's single-pass prefix scan),
+// digit bases from the histogram, and an LDS-staged scatter so that the
+// global writes of one digit are contiguous.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kdt.h"
+
+namespace {
+
+typedef uint8_t u8;
+typedef uint32_t u32;
+typedef uint64_t u64;
+typedef int64_t i64;
+
+constexpr int kRadixBits = 8;
+constexpr int kRadix = 1 << kRadixBits;
+constexpr int kBlock = 256;                // threads per workgroup
+constexpr int kWaves = kBlock / 64;        // wave64
+constexpr int kItems = 16;                 // keys per thread in a radix tile
+constexpr int kTile = kBlock * kItems;     // keys per radix tile
+constexpr int kMaxPasses = 8;              // 64-bit keys
+constexpr int kHistBlocksMax = 2048;
+constexpr u64 kFlagShift = 62;
+constexpr u64 kFlagAggregate = 1ull << kFlagShift;
+constexpr u64 kFlagPrefix = 2ull << kFlagShift;
+constexpr u64 kCountMask = (1ull << kFlagShift) - 1;
+static_assert(kBlock == kRadix, "the look-back maps one thread to one digit");
+constexpr int kHistWords = 2 * kMaxPasses * kRadix;  // two rounds' histograms
+constexpr int kTicketWords = 64;                      // two tile tickets, padded
+
+// ------------------------------------------------------------ tree geometry
+// Level-order complete tree with N nodes ([W], indexing paragraph):
+// level(i) = floor(log2(i+1)), numLevels(N) = level(N-1)+1, F(l) = 2^l - 1.
+
+struct Geometry {
+    i64 n;      // nodes (= points)
+    int levels; // L = numLevels(N)
+    i64 last;   // nodes on the last level: N - F(L-1)
+};
+
+__host__ __device__ inline int level_of(u64 i) { return 63 - __builtin_clzll(i + 1); }
+__host__ __device__ inline u64 full_nodes(int l) { return (1ull << l) - 1; }
+
+__host__ __device__ inline Geometry make_geometry(i64 n) {
+    Geometry g;
+    g.n = n;
+    g.levels = level_of((u64)(n - 1)) + 1;
+    g.last = n - (i64)full_nodes(g.levels - 1);
+    return g;
+}
+
+// Size of the subtree rooted at s ([W], sb/ss paragraph; the closed form is
+// not in the extracted text and is derived here): the dd = L-1-level(s)
+// levels below s's own are full (2^dd - 1 nodes), and of the 2^dd
+// last-level slots under s, which start at id (s+1)*2^dd - 1, only those
+// below N exist.
+__host__ __device__ inline u64 subtree_size(const Geometry& g, u64 s) {
+    if (s >= (u64)g.n) return 0;
+    int dd = g.levels - 1 - level_of(s);
+    u64 span = 1ull << dd;
+    i64 first_last = (i64)((s + 1) << dd) - 1;
+    i64 extra = g.n - first_last;
+    if (extra < 0) extra = 0;
+    if (extra > (i64)span) extra = (i64)span;
+    return (span - 1) + (u64)extra;
+}
+
+// First sorted position of subtree s (on level l) in the round that fixes
+// level l ([W], sb/ss paragraph; derived): the F(l) nodes above level l are
+// already fixed and sort first in tag order, then the j = s - F(l) subtrees
+// left of s on level l, each with 2^dd - 1 full-level nodes, plus the
+// last-level nodes under them, min(M, j * 2^dd).
+__host__ __device__ inline u64 segment_begin(const Geometry& g, u64 s, int l) {
+    u64 j = s - full_nodes(l);
+    int dd = g.levels - 1 - l;
+    u64 under = j << dd;
+    if (under > (u64)g.last) under = (u64)g.last;
+    return full_nodes(l) + j * ((1ull << dd) - 1) + under;
+}
+
+// Radix passes of round l: the key holds 32 coordinate bits plus the tag,
+// whose largest value in round l is F(l+1)-1 (l+1 bits; all tags are 0 in
+// round 0).
+__host__ __device__ inline int round_passes(int l) {
+    int bits = 32 + (l == 0 ? 0 : l + 1);
+    return (bits + kRadixBits - 1) / kRadixBits;
+}
+
+// Order-preserving map of float bits to unsigned: IEEE order with -0 == +0.
+// Pure bit tests, so denormals are never flushed.
+__device__ inline u32 float_key(u32 b) {
+    if ((b & 0x7fffffffu) == 0) return 0x80000000u;
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// ------------------------------------------------------------- block scans
+
+__device__ inline u32 wave_inclusive_scan(u32 v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        u32 t = __shfl_up(v, o, 64);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+// Exclusive scan of one value per thread across the workgroup.
+__device__ inline u32 block_exclusive_scan(u32 v, u32* s_wave) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    u32 inc = wave_inclusive_scan(v);
+    if (lane == 63) s_wave[w] = inc;
+    __syncthreads();
+    u32 off = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i)
+        if (i < w) off += s_wave[i];
+    __syncthreads();
+    return off + inc - v;
+}
+
+__device__ inline u64 status_load(const u64* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void status_store(u64* p, u64 v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ----------------------------------------------------------------- kernels
+
+// Column copy of the split dimensions and clearing of the radix bookkeeping.
+__global__ __launch_bounds__(kBlock) void k_init(const float* __restrict__ pts, i64 n, int k,
+                                                 int kcols, float* __restrict__ cols,
+                                                 u64* __restrict__ status0, i64 status_words,
+                                                 u32* __restrict__ small, int small_words) {
+    const i64 stride = (i64)gridDim.x * kBlock;
+    for (i64 e = (i64)blockIdx.x * kBlock + threadIdx.x; e < n; e += stride) {
+        const float* row = pts + e * k;
+        for (int d = 0; d < kcols; ++d) cols[(i64)d * n + e] = row[d];
+    }
+    for (i64 i = (i64)blockIdx.x * kBlock + threadIdx.x; i < status_words; i += stride)
+        status0[i] = 0;
+    if (blockIdx.x == 0)
+        for (int i = threadIdx.x; i < small_words; i += kBlock) small[i] = 0;
+}
+
+struct KeySource {
+    const u32* tag;   // nullptr in round 0 (all tags are 0)
+    const float* col; // coordinate column of dimension l mod k
+};
+
+__device__ inline u64 make_key(const KeySource& src, i64 e) {
+    u32 t = src.tag ? src.tag[e] : 0u;
+    u32 x = __float_as_uint(src.col[e]);
+    return ((u64)t << 32) | float_key(x);
+}
+
+// All digit histograms of one round's keys (read once, in index order).
+__global__ __launch_bounds__(kBlock) void k_hist(KeySource src, i64 n, int passes,
+                                                 u32* __restrict__ hist) {
+    __shared__ u32 h[kWaves][kMaxPasses][kRadix];
+    const int w = threadIdx.x >> 6;
+    for (int i = threadIdx.x; i < kWaves * kMaxPasses * kRadix; i += kBlock) (&h[0][0][0])[i] = 0;
+    __syncthreads();
+    const i64 stride = (i64)gridDim.x * kBlock;
+    for (i64 e = (i64)blockIdx.x * kBlock + threadIdx.x; e < n; e += stride) {
+        u64 key = make_key(src, e);
+        for (int p = 0; p < passes; ++p)
+            atomicAdd(&h[w][p][(u32)(key >> (p * kRadixBits)) & (kRadix - 1)], 1u);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < passes * kRadix; i += kBlock) {
+        u32 s = 0;
+        for (int v = 0; v < kWaves; ++v) s += (&h[v][0][0])[i];
+        if (s) atomicAdd(&hist[i], s);
+    }
+}
+
+enum PassMode { kFirst = 0, kMiddle = 1, kLast = 2 };
+
+struct PassArgs {
+    i64 n;
+    int shift;                 // digit = (key >> shift) & 255
+    KeySource src;             // kFirst
+    const u64* keys_in;        // kMiddle, kLast
+    const u32* vals_in;
+    u64* keys_out;             // kFirst, kMiddle
+    u32* vals_out;
+    u32* tag_out;              // kLast
+    const u32* digit_hist;     // 256 counts of this pass's digit over all keys
+    u64* status;               // this pass's look-back words, zero on entry
+    u64* status_next;          // next pass's words: cleared here
+    u32* ticket;               // tile counter, zeroed once per build
+    u32 ticket_base;           // tickets of this pass: [ticket_base, ticket_base + tiles)
+    u32* clear;                // kFirst: the next round's histogram, cleared here
+    int clear_words;
+    Geometry geo;              // kLast
+    int round;                 // kLast
+};
+
+template <int kMode>
+__global__ __launch_bounds__(kBlock) void k_onesweep(PassArgs a) {
+    __shared__ union {
+        u32 count[kWaves][kRadix];  // ranking: per-wave digit counts, then prefixes
+        u64 keys[kTile];            // staging of the sorted tile
+        u32 vals[kTile];
+    } sm;
+    __shared__ u8 s_digit[kTile];
+    __shared__ u32 s_local[kRadix];  // first tile-local slot of each digit
+    __shared__ u32 s_base[kRadix];   // global slot of tile-local slot 0 of each digit
+    __shared__ u32 s_wave[kWaves];
+    __shared__ u32 s_tile;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // Tiles are numbered in the order workgroups start, so every tile a
+    // look-back waits on is already running.
+    if (tid == 0) s_tile = atomicAdd(a.ticket, 1u) - a.ticket_base;
+    const u32 hist_count = a.digit_hist[tid];
+    __syncthreads();
+    const u32 tile = s_tile;
+    if (tile >= gridDim.x) return;  // cannot happen: one ticket per workgroup
+    // First global slot of digit `tid`: exclusive scan of the histogram.
+    const u32 digit_start = block_exclusive_scan(hist_count, s_wave);
+
+    a.status_next[(u64)tile * kRadix + tid] = 0;
+    if (kMode == kFirst)
+        for (int i = (int)tile * kBlock + tid; i < a.clear_words; i += (int)gridDim.x * kBlock)
+            a.clear[i] = 0;
+
+    // Load: wave w owns kItems rows of 64 consecutive keys.
+    const i64 base = (i64)tile * kTile;
+    const i64 wbase = base + (i64)w * (64 * kItems) + lane;
+    u64 key[kItems];
+    u32 val[kItems];
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+        const i64 e = wbase + (i64)j * 64;
+        key[j] = 0;
+        val[j] = 0;
+        if (e < a.n) {
+            if (kMode == kFirst) {
+                key[j] = make_key(a.src, e);
+                val[j] = (u32)e;
+            } else {
+                key[j] = a.keys_in[e];
+                val[j] = a.vals_in[e];
+            }
+        }
+    }
+
+    // Rank inside the wave: lanes holding the same digit are found with eight
+    // ballots; the lowest such lane bumps the wave's counter for the digit.
+    for (int i = lane; i < kRadix; i += 64) sm.count[w][i] = 0;
+    const u64 below = (1ull << lane) - 1;
+    u32 rank[kItems];
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+        const bool valid = (wbase + (i64)j * 64) < a.n;
+        const u32 d = (u32)(key[j] >> a.shift) & (kRadix - 1);
+        u64 peers = __ballot(valid);
+#pragma unroll
+        for (int b = 0; b < kRadixBits; ++b) {
+            const bool bit = (d >> b) & 1;
+            const u64 vote = __ballot(bit);
+            peers &= bit ? vote : ~vote;
+        }
+        const u32 before = __popcll(peers & below);
+        const u32 total = __popcll(peers);
+        u32 seen = 0;
+        if (valid) seen = sm.count[w][d];
+        rank[j] = seen + before;
+        if (valid && before == 0) sm.count[w][d] = seen + total;
+    }
+    __syncthreads();
+
+    // Thread tid owns digit tid: tile total, per-wave prefixes, look-back.
+    u32 agg = 0;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+        const u32 c = sm.count[v][tid];
+        sm.count[v][tid] = agg;
+        agg += c;
+    }
+    u64* mine = a.status + (u64)tile * kRadix + tid;
+    status_store(mine, (tile == 0 ? kFlagPrefix : kFlagAggregate) | agg);
+    const u32 local_start = block_exclusive_scan(agg, s_wave);
+    u64 exclusive = 0;
+    if (tile > 0) {
+        for (i64 pred = (i64)tile - 1; pred >= 0; --pred) {
+            const u64* p = a.status + (u64)pred * kRadix + tid;
+            u64 v = status_load(p);
+            while ((v >> kFlagShift) == 0) {
+                __builtin_amdgcn_s_sleep(1);
+                v = status_load(p);
+            }
+            exclusive += v & kCountMask;
+            if ((v >> kFlagShift) == 2) break;
+        }
+        status_store(mine, kFlagPrefix | (exclusive + agg));
+    }
+    const u32 global_start = digit_start + (u32)exclusive;
+    s_local[tid] = local_start;
+    s_base[tid] = global_start - local_start;  // modular; base + local slot < n
+
+    u32 digit[kItems];
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+        digit[j] = (u32)(key[j] >> a.shift) & (kRadix - 1);
+        if ((wbase + (i64)j * 64) < a.n) rank[j] += sm.count[w][digit[j]];
+    }
+    __syncthreads();
+
+    if (kMode == kLast) {
+        // Tag update ([W], tag and sort-order paragraphs): a point of subtree
+        // s (s on level l, so s >= F(l)) at sorted position p moves to the
+        // left child if p is before the pivot, to the right child if after,
+        // and stays as node s if it is the pivot; pivot = start of s's
+        // segment + size of the left subtree. Tags < F(l) are final.
+        const u64 fl = full_nodes(a.round);
+#pragma unroll
+        for (int j = 0; j < kItems; ++j) {
+            if ((wbase + (i64)j * 64) >= a.n) continue;
+            const u64 s = key[j] >> 32;
+            if (s < fl) continue;
+            const u64 p = (u64)(s_base[digit[j]] + s_local[digit[j]] + rank[j]);
+            const u64 pivot = segment_begin(a.geo, s, a.round) + subtree_size(a.geo, 2 * s + 1);
+            const u64 t = p < pivot ? 2 * s + 1 : (p > pivot ? 2 * s + 2 : s);
+            if (val[j] < (u64)a.n) a.tag_out[val[j]] = (u32)t;
+        }
+        return;
+    }
+
+    const int valid_here = (int)((a.n - base) < kTile ? (a.n - base) : kTile);
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+        if ((wbase + (i64)j * 64) >= a.n) continue;
+        const u32 slot = s_local[digit[j]] + rank[j];
+        sm.keys[slot] = key[j];
+        s_digit[slot] = (u8)digit[j];
+    }
+    __syncthreads();
+    for (int i = tid; i < valid_here; i += kBlock) {
+        const u32 dst = s_base[s_digit[i]] + (u32)i;
+        if (dst < (u64)a.n) a.keys_out[dst] = sm.keys[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+        if ((wbase + (i64)j * 64) >= a.n) continue;
+        sm.vals[s_local[digit[j]] + rank[j]] = val[j];
+    }
+    __syncthreads();
+    for (int i = tid; i < valid_here; i += kBlock) {
+        const u32 dst = s_base[s_digit[i]] + (u32)i;
+        if (dst < (u64)a.n) a.vals_out[dst] = sm.vals[i];
+    }
+}
+
+// perm[node] = i and the level-order copy of the coordinates.
+__global__ __launch_bounds__(kBlock) void k_place(const float* __restrict__ pts, i64 n, int k,
+                                                  const u32* __restrict__ tag,
+                                                  int32_t* __restrict__ perm,
+                                                  float* __restrict__ tree) {
+    const i64 stride = (i64)gridDim.x * kBlock;
+    for (i64 e = (i64)blockIdx.x * kBlock + threadIdx.x; e < n; e += stride) {
+        const i64 node = tag ? (i64)tag[e] : e;
+        if (node >= n) continue;  // cannot happen: tags are node ids < n
+        perm[node] = (int32_t)e;
+        if (tree)
+            for (int d = 0; d < k; ++d) tree[node * k + d] = pts[e * k + d];
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_copy_tags(const u32* __restrict__ tag, i64 n,
+                                                      u32* __restrict__ out) {
+    const i64 stride = (i64)gridDim.x * kBlock;
+    for (i64 e = (i64)blockIdx.x * kBlock + threadIdx.x; e < n; e += stride)
+        out[e] = tag ? tag[e] : 0u;
+}
+
+// ------------------------------------------------------------ host driver
+
+inline size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct Layout {
+    int kcols;          // split dimensions actually used
+    i64 tiles;
+    size_t cols, tag, keys0, keys1, vals0, vals1, small, status, total;
+};
+
+bool make_layout(i64 n, int k, Layout* out) {
+    if (n < 0 || n > INT32_MAX || k < 1 || k > 65535) return false;
+    Layout lay{};
+    if (n <= 1) {
+        *out = lay;
+        return true;
+    }
+    const int rounds = make_geometry(n).levels - 1;
+    lay.kcols = rounds < k ? rounds : k;
+    lay.tiles = (n + kTile - 1) / kTile;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align_up(off + bytes);
+        return at;
+    };
+    lay.cols = take((size_t)lay.kcols * n * sizeof(float));
+    lay.tag = take((size_t)n * sizeof(u32));
+    lay.keys0 = take((size_t)n * sizeof(u64));
+    lay.keys1 = take((size_t)n * sizeof(u64));
+    lay.vals0 = take((size_t)n * sizeof(u32));
+    lay.vals1 = take((size_t)n * sizeof(u32));
+    lay.small = take((kHistWords + kTicketWords) * sizeof(u32));  // histograms, tickets
+    lay.status = take(2 * (size_t)lay.tiles * kRadix * sizeof(u64));
+    lay.total = off;
+    *out = lay;
+    return true;
+}
+
+inline int grid_for(i64 work, int per_block, int cap) {
+    i64 g = (work + per_block - 1) / per_block;
+    if (g < 1) g = 1;
+    if (g > cap) g = cap;
+    return (int)g;
+}
+
+bool ranges_overlap(const void* a, size_t an, const void* b, size_t bn) {
+    if (!a || !b || an == 0 || bn == 0) return false;
+    uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + bn && b0 < a0 + an;
+}
+
+// Optional per-kernel timing: an event pair around every launch.
+enum Kind { kKindInit, kKindHist, kKindFirst, kKindMid, kKindLast, kKindPlace, kKinds };
+const char* const kKindNames[kKinds] = {"init", "hist", "sweep_first", "sweep_mid",
+                                        "sweep_last", "place"};
+
+struct Profiler {
+    struct Rec {
+        int kind;
+        double bytes;
+        hipEvent_t start, stop;
+    };
+    Rec recs[1024];
+    int count = 0;
+    bool failed = false;
+    hipStream_t stream;
+
+    void begin(int kind, double bytes) {
+        if (count >= 1024) { failed = true; return; }
+        Rec& r = recs[count];
+        r.kind = kind;
+        r.bytes = bytes;
+        if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess) {
+            failed = true;
+            return;
+        }
+        hipEventRecord(r.start, stream);
+    }
+    void end() {
+        if (failed) return;
+        hipEventRecord(recs[count].stop, stream);
+        ++count;
+    }
+};
+
+struct Timer {  // no-op unless a Profiler is attached
+    Profiler* p;
+    void begin(int kind, double bytes) { if (p) p->begin(kind, bytes); }
+    void end() { if (p) p->end(); }
+};
+
+// Runs the first `rounds` rounds; leaves the tags in the workspace.
+kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, const Layout& lay,
+                      hipStream_t stream, Timer timer) {
+    const Geometry geo = make_geometry(n);
+    float* cols = (float*)(ws + lay.cols);
+    u32* tag = (u32*)(ws + lay.tag);
+    u64* keys[2] = {(u64*)(ws + lay.keys0), (u64*)(ws + lay.keys1)};
+    u32* vals[2] = {(u32*)(ws + lay.vals0), (u32*)(ws + lay.vals1)};
+    u32* hist = (u32*)(ws + lay.small);
+    u32* tickets = hist + kHistWords;
+    u64* status = (u64*)(ws + lay.status);
+    const i64 status_words = lay.tiles * kRadix;
+
+    const int grid_elems = grid_for(n, kBlock * 4, 8192);
+    // Clears the first pass's look-back words, both histogram halves and the
+    // tile tickets (a kernel rather than a memset node, so the sequence can
+    // be captured into a graph).
+    timer.begin(kKindInit, (double)n * lay.kcols * 8);
+    k_init<<<grid_elems, kBlock, 0, stream>>>(pts, n, k, lay.kcols, cols, status, status_words,
+                                              hist, kHistWords + kTicketWords);
+    timer.end();
+
+    int pass_index = 0;
+    for (int l = 0; l < rounds; ++l) {
+        const int d = l % k;
+        const int passes = round_passes(l);
+        u32* h = hist + (size_t)(l & 1) * kMaxPasses * kRadix;
+        u32* h_next = hist + (size_t)((l + 1) & 1) * kMaxPasses * kRadix;
+        KeySource src{l == 0 ? nullptr : tag, cols + (size_t)d * n};
+        const double key_src_bytes = (double)n * (l == 0 ? 4 : 8);  // (tag +) column
+        timer.begin(kKindHist, key_src_bytes);
+        k_hist<<<grid_for(n, kBlock * 16, kHistBlocksMax), kBlock, 0, stream>>>(src, n, passes, h);
+        timer.end();
+        for (int p = 0; p < passes; ++p, ++pass_index) {
+            PassArgs a{};
+            a.n = n;
+            a.shift = p * kRadixBits;
+            a.src = src;
+            a.keys_in = keys[(p + 1) & 1];
+            a.vals_in = vals[(p + 1) & 1];
+            a.keys_out = keys[p & 1];
+            a.vals_out = vals[p & 1];
+            a.tag_out = tag;
+            a.digit_hist = h + (size_t)p * kRadix;
+            a.status = status + (size_t)(pass_index & 1) * status_words;
+            a.status_next = status + (size_t)((pass_index + 1) & 1) * status_words;
+            a.ticket = tickets;
+            a.ticket_base = (u32)((u64)pass_index * (u64)lay.tiles);
+            a.clear = h_next;
+            a.clear_words = kMaxPasses * kRadix;
+            a.geo = geo;
+            a.round = l;
+            const dim3 grid((unsigned)lay.tiles);
+            if (p == 0) {
+                timer.begin(kKindFirst, key_src_bytes + (double)n * 12);
+                k_onesweep<kFirst><<<grid, kBlock, 0, stream>>>(a);
+            } else if (p == passes - 1) {
+                timer.begin(kKindLast, (double)n * 16);  // key+val in, tag out
+                k_onesweep<kLast><<<grid, kBlock, 0, stream>>>(a);
+            } else {
+                timer.begin(kKindMid, (double)n * 24);
+                k_onesweep<kMiddle><<<grid, kBlock, 0, stream>>>(a);
+            }
+            timer.end();
+        }
+    }
+    return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
+}
+
+kdt_status validate(const float* pts, i64 n, int k, const void* out0, size_t out0_bytes,
+                    const void* out1, size_t out1_bytes, void* ws, size_t ws_bytes,
+                    Layout* lay) {
+    if (!make_layout(n, k, lay)) return KDT_ERR_INVALID_ARG;
+    if (n == 0) return KDT_OK;
+    if (!pts || !out0) return KDT_ERR_INVALID_ARG;
+    const size_t pts_bytes = (size_t)n * k * sizeof(float);
+    if (ranges_overlap(pts, pts_bytes, out0, out0_bytes) ||
+        ranges_overlap(pts, pts_bytes, out1, out1_bytes) ||
+        ranges_overlap(out0, out0_bytes, out1, out1_bytes))
+        return KDT_ERR_INVALID_ARG;
+    if (lay->total > 0) {
+        if (!ws || ws_bytes < lay->total || ((uintptr_t)ws & 255)) return KDT_ERR_WORKSPACE;
+        if (ranges_overlap(ws, lay->total, pts, pts_bytes) ||
+            ranges_overlap(ws, lay->total, out0, out0_bytes) ||
+            ranges_overlap(ws, lay->total, out1, out1_bytes))
+            return KDT_ERR_INVALID_ARG;
+    }
+    return KDT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kdt_workspace_size(int64_t N, int32_t k) {
+    Layout lay;
+    if (!make_layout(N, k, &lay)) return 0;
+    return lay.total;
+}
+
+namespace {
+
+kdt_status build_impl(const float* points, int64_t N, int32_t k, int32_t* perm_out,
+                      float* tree_out, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream, Timer timer) {
+    Layout lay;
+    const size_t perm_bytes = (size_t)(N > 0 ? N : 0) * sizeof(int32_t);
+    const size_t tree_bytes = tree_out ? (size_t)(N > 0 ? N : 0) * (k > 0 ? k : 0) * sizeof(float) : 0;
+    kdt_status st = validate(points, N, k, perm_out, perm_bytes, tree_out, tree_bytes, workspace,
+                             workspace_bytes, &lay);
+    if (st != KDT_OK || N == 0) return st;
+    const int rounds = make_geometry(N).levels - 1;
+    const u32* tag = nullptr;
+    if (rounds > 0) {
+        st = run_rounds(points, N, k, rounds, (char*)workspace, lay, stream, timer);
+        if (st != KDT_OK) return st;
+        tag = (const u32*)((char*)workspace + lay.tag);
+    }
+    timer.begin(kKindPlace, (double)N * ((tag ? 4 : 0) + 4 + (tree_out ? 8.0 * k : 0)));
+    k_place<<<grid_for(N, kBlock * 4, 8192), kBlock, 0, stream>>>(points, N, k, tag, perm_out,
+                                                                  tree_out);
+    timer.end();
+    return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
+}
+
+}  // namespace
+
+kdt_status kdt_build(const float* points, int64_t N, int32_t k, int32_t* perm_out,
+                     float* tree_out, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+    return build_impl(points, N, k, perm_out, tree_out, workspace, workspace_bytes, stream,
+                      Timer{nullptr});
+}
+
+kdt_status kdt_build_profiled(const float* points, int64_t N, int32_t k, int32_t* perm_out,
+                              float* tree_out, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream, kdt_profile* profile) {
+    if (!profile) return KDT_ERR_INVALID_ARG;
+    Profiler* prof = new Profiler();
+    prof->stream = stream;
+    kdt_status st = build_impl(points, N, k, perm_out, tree_out, workspace, workspace_bytes,
+                               stream, Timer{prof});
+    if (hipStreamSynchronize(stream) != hipSuccess && st == KDT_OK) st = KDT_ERR_HIP;
+    *profile = kdt_profile{};
+    profile->kinds = kKinds;
+    for (int i = 0; i < kKinds; ++i) {
+        for (int c = 0; kKindNames[i][c] && c < 23; ++c) profile->name[i][c] = kKindNames[i][c];
+    }
+    for (int i = 0; i < prof->count; ++i) {
+        Profiler::Rec& r = prof->recs[i];
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess && st == KDT_OK)
+            st = KDT_ERR_HIP;
+        profile->ms[r.kind] += ms;
+        profile->launches[r.kind] += 1;
+        profile->bytes[r.kind] += r.bytes;
+    }
+    for (int i = 0; i < prof->count; ++i) {
+        hipEventDestroy(prof->recs[i].start);
+        hipEventDestroy(prof->recs[i].stop);
+    }
+    if (prof->failed && st == KDT_OK) st = KDT_ERR_HIP;
+    delete prof;
+    return st;
+}
+
+kdt_status kdt_debug_tags(const float* points, int64_t N, int32_t k, int32_t rounds,
+                          uint32_t* tags_out, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+    Layout lay;
+    const size_t tag_bytes = (size_t)(N > 0 ? N : 0) * sizeof(u32);
+    kdt_status st = validate(points, N, k, tags_out, tag_bytes, nullptr, 0, workspace,
+                             workspace_bytes, &lay);
+    if (st != KDT_OK || N == 0) return st;
+    const int max_rounds = make_geometry(N).levels - 1;
+    if (rounds < 0 || rounds > max_rounds) return KDT_ERR_INVALID_ARG;
+    const u32* tag = nullptr;
+    if (rounds > 0) {
+        st = run_rounds(points, N, k, rounds, (char*)workspace, lay, stream, Timer{nullptr});
+        if (st != KDT_OK) return st;
+        tag = (const u32*)((char*)workspace + lay.tag);
+    }
+    k_copy_tags<<<grid_for(N, kBlock * 4, 8192), kBlock, 0, stream>>>(tag, N, tags_out);
+    return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
+}
+
+int64_t kdt_closed_subtree_size(int64_t N, int64_t s) {
+    if (N <= 0 || N > INT32_MAX || s < 0) return 0;
+    if (s >= N) return 0;
+    return (int64_t)subtree_size(make_geometry(N), (u64)s);
+}
+
+int64_t kdt_closed_segment_begin(int64_t N, int64_t s, int32_t l) {
+    if (N <= 0 || N > INT32_MAX || s < 0 || s >= N) return -1;
+    const Geometry g = make_geometry(N);
+    if (l < 0 || l >= g.levels || level_of((u64)s) != l) return -1;
+    return (int64_t)segment_begin(g, (u64)s, l);
+}
+
+int32_t kdt_round_passes(int64_t N, int32_t l) {
+    if (N <= 1 || N > INT32_MAX) return -1;
+    if (l < 0 || l >= make_geometry(N).levels - 1) return -1;
+    return round_passes(l);
+}
+
+const char* kdt_status_string(kdt_status status) {
+    switch (status) {
+        case KDT_OK: return "ok";
+        case KDT_ERR_INVALID_ARG: return "invalid argument";
+        case KDT_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+        case KDT_ERR_HIP: return "HIP kernel launch failed";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,181 @@
+"""Python binding of the C ABI in include/kdt.h (ctypes; argument marshalling only).
+
+Every step of the build runs in libkdt.so's HIP kernels; this module only
+allocates device buffers with torch, passes raw pointers and the current HIP
+stream, and turns status codes into exceptions. If libkdt.so is missing the
+import-time load fails loudly: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libkdt.so")
+
+KDT_OK = 0
+STATUS_NAMES = {0: "KDT_OK", 1: "KDT_ERR_INVALID_ARG", 2: "KDT_ERR_WORKSPACE", 3: "KDT_ERR_HIP"}
+
+PROFILE_MAX_KINDS = 8
+
+
+class Profile(ctypes.Structure):
+    """Mirror of kdt_profile."""
+    _fields_ = [("kinds", ctypes.c_int32),
+                ("name", (ctypes.c_char * 24) * PROFILE_MAX_KINDS),
+                ("launches", ctypes.c_int64 * PROFILE_MAX_KINDS),
+                ("ms", ctypes.c_double * PROFILE_MAX_KINDS),
+                ("bytes", ctypes.c_double * PROFILE_MAX_KINDS)]
+
+    def as_dict(self):
+        return {self.name[i].value.decode(): {"launches": int(self.launches[i]),
+                                              "ms": float(self.ms[i]),
+                                              "bytes": float(self.bytes[i])}
+                for i in range(self.kinds)}
+
+
+# Every function include/kdt.h declares: name -> (restype, argtypes).
+_VOIDP, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+SIGNATURES = {
+    "kdt_workspace_size": (_SZ, [_I64, _I32]),
+    "kdt_build": (ctypes.c_int, [_VOIDP, _I64, _I32, _VOIDP, _VOIDP, _VOIDP, _SZ, _VOIDP]),
+    "kdt_debug_tags": (ctypes.c_int, [_VOIDP, _I64, _I32, _I32, _VOIDP, _VOIDP, _SZ, _VOIDP]),
+    "kdt_build_profiled": (ctypes.c_int, [_VOIDP, _I64, _I32, _VOIDP, _VOIDP, _VOIDP, _SZ, _VOIDP,
+                                          ctypes.POINTER(Profile)]),
+    "kdt_closed_subtree_size": (_I64, [_I64, _I64]),
+    "kdt_closed_segment_begin": (_I64, [_I64, _I64, _I32]),
+    "kdt_round_passes": (_I32, [_I64, _I32]),
+    "kdt_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class KdtError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (%s)" % (where, STATUS_NAMES.get(status, status),
+                                          lib().kdt_status_string(status).decode()))
+
+
+def lib():
+    """The loaded libkdt.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError("libkdt.so not built: run __graft_entry__.build() "
+                                   "or python -m tree_construction_amd.build_lib")
+            handle = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in SIGNATURES.items():
+                fn = getattr(handle, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = handle
+    return _lib
+
+
+def workspace_size(n: int, k: int) -> int:
+    return int(lib().kdt_workspace_size(int(n), int(k)))
+
+
+def closed_subtree_size(n: int, s: int) -> int:
+    return int(lib().kdt_closed_subtree_size(int(n), int(s)))
+
+
+def closed_segment_begin(n: int, s: int, level: int) -> int:
+    return int(lib().kdt_closed_segment_begin(int(n), int(s), int(level)))
+
+
+def round_passes(n: int, level: int) -> int:
+    return int(lib().kdt_round_passes(int(n), int(level)))
+
+
+def _check(status: int, where: str):
+    if status != KDT_OK:
+        raise KdtError(status, where)
+
+
+def _stream_handle(device, stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _validate_points(points):
+    import torch
+    if not isinstance(points, torch.Tensor) or points.dtype != torch.float32 or points.dim() != 2:
+        raise TypeError("points must be a 2-D float32 torch tensor")
+    if not points.is_cuda:
+        raise ValueError("points must be on a HIP device")
+    if not points.is_contiguous():
+        raise ValueError("points must be contiguous (row-major N x k)")
+
+
+class Builder:
+    """Holds a workspace sized for (N, k) so repeated builds allocate nothing."""
+
+    def __init__(self, n: int, k: int, device="cuda"):
+        import torch
+        self.n, self.k = int(n), int(k)
+        self.device = torch.device(device)
+        nbytes = workspace_size(self.n, self.k)
+        if nbytes == 0 and self.n > 1:
+            raise ValueError("unsupported size N=%d k=%d" % (self.n, self.k))
+        self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=self.device)
+        self.workspace_bytes = nbytes
+
+    def build(self, points, perm=None, tree=None, want_tree=True, stream=None):
+        import torch
+        _validate_points(points)
+        if tuple(points.shape) != (self.n, self.k):
+            raise ValueError("points shape %s != (%d, %d)" % (tuple(points.shape), self.n, self.k))
+        if perm is None:
+            perm = torch.empty(self.n, dtype=torch.int32, device=points.device)
+        if tree is None and want_tree:
+            tree = torch.empty_like(points)
+        st = lib().kdt_build(ctypes.c_void_p(points.data_ptr()), self.n, self.k,
+                             ctypes.c_void_p(perm.data_ptr()),
+                             ctypes.c_void_p(tree.data_ptr() if tree is not None else 0),
+                             ctypes.c_void_p(self.workspace.data_ptr()), self.workspace_bytes,
+                             _stream_handle(points.device, stream))
+        _check(st, "kdt_build")
+        return perm, tree
+
+    def build_profiled(self, points, perm, tree=None, stream=None):
+        """One build with a HIP event pair around every kernel; synchronises
+        and returns {kernel kind: {launches, ms, bytes}}."""
+        _validate_points(points)
+        prof = Profile()
+        st = lib().kdt_build_profiled(ctypes.c_void_p(points.data_ptr()), self.n, self.k,
+                                      ctypes.c_void_p(perm.data_ptr()),
+                                      ctypes.c_void_p(tree.data_ptr() if tree is not None else 0),
+                                      ctypes.c_void_p(self.workspace.data_ptr()),
+                                      self.workspace_bytes, _stream_handle(points.device, stream),
+                                      ctypes.byref(prof))
+        _check(st, "kdt_build_profiled")
+        return prof.as_dict()
+
+    def debug_tags(self, points, rounds: int, stream=None):
+        """int32 tensor holding the uint32 tags after `rounds` rounds."""
+        import torch
+        _validate_points(points)
+        out = torch.empty(self.n, dtype=torch.int32, device=points.device)
+        st = lib().kdt_debug_tags(ctypes.c_void_p(points.data_ptr()), self.n, self.k, int(rounds),
+                                  ctypes.c_void_p(out.data_ptr()),
+                                  ctypes.c_void_p(self.workspace.data_ptr()), self.workspace_bytes,
+                                  _stream_handle(points.device, stream))
+        _check(st, "kdt_debug_tags")
+        return out
+
+
+def build(points, want_tree: bool = True, stream=None):
+    """Build the level-order tree of `points` ((N, k) float32 on a HIP device).
+
+    Returns (perm, tree): perm[s] (int32) is the original index of the point at
+    node s; tree[s] = points[perm[s]] (None when want_tree is False)."""
+    _validate_points(points)
+    n, k = points.shape
+    return Builder(n, k, points.device).build(points, want_tree=want_tree, stream=stream)
