@@ -379,6 +379,223 @@ __global__ __launch_bounds__(kBlock) void k_onesweep(PassArgs a) {
     }
 }
 
+// --------------------------------------------- subtrees finished in LDS
+// Once every subtree on some level l0 holds at most kLocalMax points, the
+// remaining rounds of each subtree only ever compare points of that subtree:
+// a point's sorted position inside its segment, and therefore its next tag,
+// depends on its own segment alone. One workgroup then runs those rounds for
+// one subtree -- the same sort by (tag, coordinate, index) and the same tag
+// update, with subtree-local tags and positions -- entirely in LDS, and
+// writes the subtree's level-order output. The subtree rooted at global node
+// c is itself the complete left-balanced tree of |S(c)| nodes (its share of
+// the last level is a left-aligned run), so its local geometry is
+// make_geometry(|S(c)|) and local node j on local level t is global node
+// (c+1)*2^t - 1 + (j - F(t)).
+
+constexpr int kLocalItems = 16;
+constexpr int kLocalMax = kBlock * kLocalItems;  // points per subtree
+constexpr int kCachedDims = 3;                   // sorted orders kept in LDS
+
+struct LocalShared {
+    u64 exch[kLocalMax];            // record exchange of the radix passes
+    u32 count[kWaves][kRadix];      // per-wave digit counters, then prefixes
+    u32 start[kRadix];              // first slot of each digit
+    u32 wave[kWaves];
+    uint16_t tag[kLocalMax];        // local tag of each point (by index rank)
+    uint16_t order[kCachedDims][kLocalMax];  // points sorted by (coordinate, index)
+};
+
+// Slot of item j of this thread: each wave owns kLocalItems rows of 64.
+__device__ inline int local_slot(int j) {
+    return (threadIdx.x >> 6) * (64 * kLocalItems) + j * 64 + (threadIdx.x & 63);
+}
+
+// One stable pass over all kLocalMax records of the workgroup by the 8-bit
+// digit at `shift`. Unused slots hold all-ones records: they sit at the end
+// and keep digit 255, so they stay behind every real record.
+__device__ void local_pass(u64 (&rec)[kLocalItems], int shift, LocalShared& sh) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    for (int i = lane; i < kRadix; i += 64) sh.count[w][i] = 0;
+    const u64 below = (1ull << lane) - 1;
+    u32 rank[kLocalItems], dig[kLocalItems];
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) {
+        const u32 d = (u32)(rec[j] >> shift) & (kRadix - 1);
+        dig[j] = d;
+        u64 peers = ~0ull;
+#pragma unroll
+        for (int b = 0; b < kRadixBits; ++b) {
+            const bool bit = (d >> b) & 1;
+            const u64 vote = __ballot(bit);
+            peers &= bit ? vote : ~vote;
+        }
+        const u32 before = __popcll(peers & below);
+        const u32 seen = sh.count[w][d];
+        rank[j] = seen + before;
+        if (before == 0) sh.count[w][d] = seen + (u32)__popcll(peers);
+    }
+    __syncthreads();
+    u32 agg = 0;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+        const u32 c = sh.count[v][tid];
+        sh.count[v][tid] = agg;
+        agg += c;
+    }
+    sh.start[tid] = block_exclusive_scan(agg, sh.wave);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j)
+        sh.exch[sh.start[dig[j]] + sh.count[w][dig[j]] + rank[j]] = rec[j];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) rec[j] = sh.exch[local_slot(j)];
+    __syncthreads();
+}
+
+struct SubtreeArgs {
+    const float* pts;
+    i64 n;
+    int k;
+    int l0;                 // level of the subtree roots
+    Geometry geo;
+    const u32* sorted;      // point indices in the sorted order of round l0-1 (l0 > 0)
+    int index_passes;       // radix passes to order a subtree's point indices
+    int32_t* perm;
+    float* tree;
+};
+
+// order[q] = slot (index rank) of the q-th point of the subtree by
+// (coordinate dim, original index): stable sort by the coordinate key,
+// starting from index order.
+__device__ void local_order(const SubtreeArgs& a, const u32 (&idx)[kLocalItems], u32 nc, int dim,
+                            uint16_t* order, LocalShared& sh) {
+    u64 rec[kLocalItems];
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) {
+        const int e = local_slot(j);
+        rec[j] = ~0ull;
+        if ((u32)e < nc) {
+            const u32 x = __float_as_uint(a.pts[(i64)idx[j] * a.k + dim]);
+            rec[j] = ((u64)float_key(x) << 16) | (u32)e;
+        }
+    }
+    for (int p = 0; p < 4; ++p) local_pass(rec, 16 + 8 * p, sh);
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) {
+        const int q = local_slot(j);
+        if ((u32)q < nc) order[q] = (uint16_t)(rec[j] & 0xffff);
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(kBlock) void k_subtree(SubtreeArgs a) {
+    __shared__ LocalShared sh;
+
+    const u64 c = full_nodes(a.l0) + blockIdx.x;  // subtree root (global node id)
+    const u32 nc = (u32)subtree_size(a.geo, c);
+    if (nc == 0) return;
+    u64 first = 0;  // where the subtree's points start in round l0-1's sorted order
+    if (a.l0 > 0) {
+        const u64 parent = (c - 1) / 2;
+        const u64 seg = segment_begin(a.geo, parent, a.l0 - 1);
+        const u64 pivot = seg + subtree_size(a.geo, 2 * parent + 1);
+        first = (c == 2 * parent + 1) ? seg : pivot + 1;
+    }
+
+    // Order the subtree's points by original index: slot e = index rank.
+    u64 rec[kLocalItems];
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) {
+        const int q = local_slot(j);
+        rec[j] = ~0ull;
+        if ((u32)q < nc) {
+            const u32 i = a.sorted ? a.sorted[first + q] : (u32)q;
+            rec[j] = ((u64)i << 16) | (u32)q;
+        }
+    }
+    for (int p = 0; p < a.index_passes; ++p) local_pass(rec, 16 + 8 * p, sh);
+    u32 idx[kLocalItems];
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) {
+        idx[j] = (u32)(rec[j] >> 16);
+        if ((u32)local_slot(j) < nc) sh.tag[local_slot(j)] = 0;
+    }
+
+    const Geometry lg = make_geometry((i64)nc);
+    const int rounds = lg.levels - 1;
+    const bool cached = a.k <= kCachedDims;
+    if (cached)
+        for (int u = 0; u < a.k && u < rounds; ++u)
+            local_order(a, idx, nc, (a.l0 + u) % a.k, sh.order[u], sh);
+    __syncthreads();
+
+    for (int t = 0; t < rounds; ++t) {
+        uint16_t* order = sh.order[cached ? t % a.k : 0];
+        if (!cached) local_order(a, idx, nc, (a.l0 + t) % a.k, order, sh);
+        // Sort the points of every segment by (tag, coordinate, index): a
+        // stable sort by tag of the (coordinate, index) order.
+#pragma unroll
+        for (int j = 0; j < kLocalItems; ++j) {
+            const int q = local_slot(j);
+            rec[j] = ~0ull;
+            if ((u32)q < nc) {
+                const u32 e = order[q];
+                rec[j] = ((u64)sh.tag[e] << 16) | e;
+            }
+        }
+        if (t > 0)  // round 0: every tag is 0, the order is already sorted
+            for (int sft = 16; sft < 16 + t + 1; sft += kRadixBits) local_pass(rec, sft, sh);
+        else
+            __syncthreads();
+        const u64 fl = full_nodes(t);
+#pragma unroll
+        for (int j = 0; j < kLocalItems; ++j) {
+            const u64 q = (u64)local_slot(j);
+            if (q >= nc) continue;
+            const u64 s = rec[j] >> 16;
+            if (s < fl) continue;
+            const u64 pivot = segment_begin(lg, s, t) + subtree_size(lg, 2 * s + 1);
+            sh.tag[rec[j] & 0xffff] = (uint16_t)(q < pivot ? 2 * s + 1 : (q > pivot ? 2 * s + 2 : s));
+        }
+        __syncthreads();
+    }
+
+    // Level-order output of the subtree.
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) {
+        const int e = local_slot(j);
+        if ((u32)e >= nc) continue;
+        const u64 node = sh.tag[e];
+        const int lvl = level_of(node);
+        const u64 g = ((c + 1) << lvl) - 1 + (node - full_nodes(lvl));
+        if (g >= (u64)a.n) continue;  // cannot happen: local nodes map inside the tree
+        a.perm[g] = (int32_t)idx[j];
+        if (a.tree)
+            for (int d = 0; d < a.k; ++d) a.tree[(i64)g * a.k + d] = a.pts[(i64)idx[j] * a.k + d];
+    }
+}
+
+// Nodes above level l0: the F(l0-1) nodes fixed before round l0-1 sit at
+// their own id in that round's sorted order, and each node s on level l0-1
+// is its segment's pivot.
+__global__ __launch_bounds__(kBlock) void k_place_top(const float* __restrict__ pts, int k,
+                                                      Geometry geo, int l0,
+                                                      const u32* __restrict__ sorted,
+                                                      int32_t* __restrict__ perm,
+                                                      float* __restrict__ tree) {
+    const u64 s = (u64)blockIdx.x * kBlock + threadIdx.x;
+    if (s >= full_nodes(l0)) return;
+    u64 p = s;
+    if (s >= full_nodes(l0 - 1))
+        p = segment_begin(geo, s, l0 - 1) + subtree_size(geo, 2 * s + 1);
+    if (p >= (u64)geo.n) return;
+    const u32 i = sorted[p];
+    perm[s] = (int32_t)i;
+    if (tree)
+        for (int d = 0; d < k; ++d) tree[(i64)s * k + d] = pts[(i64)i * k + d];
+}
+
 // perm[node] = i and the level-order copy of the coordinates.
 __global__ __launch_bounds__(kBlock) void k_place(const float* __restrict__ pts, i64 n, int k,
                                                   const u32* __restrict__ tag,
@@ -454,9 +671,10 @@ bool ranges_overlap(const void* a, size_t an, const void* b, size_t bn) {
 }
 
 // Optional per-kernel timing: an event pair around every launch.
-enum Kind { kKindInit, kKindHist, kKindFirst, kKindMid, kKindLast, kKindPlace, kKinds };
+enum Kind { kKindInit, kKindHist, kKindFirst, kKindMid, kKindLast, kKindPlace, kKindSubtree,
+            kKinds };
 const char* const kKindNames[kKinds] = {"init", "hist", "sweep_first", "sweep_mid",
-                                        "sweep_last", "place"};
+                                        "sweep_last", "place", "subtree"};
 
 struct Profiler {
     struct Rec {
@@ -493,9 +711,13 @@ struct Timer {  // no-op unless a Profiler is attached
     void end() { if (p) p->end(); }
 };
 
-// Runs the first `rounds` rounds; leaves the tags in the workspace.
+// Runs the first `rounds` rounds on the whole point set. With keep_sorted,
+// the last round writes its sorted order (point indices, returned in
+// *sorted_out) instead of updating the tags; otherwise the tags after
+// `rounds` rounds are left in the workspace.
 kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, const Layout& lay,
-                      hipStream_t stream, Timer timer) {
+                      hipStream_t stream, Timer timer, bool keep_sorted = false,
+                      const u32** sorted_out = nullptr) {
     const Geometry geo = make_geometry(n);
     float* cols = (float*)(ws + lay.cols);
     u32* tag = (u32*)(ws + lay.tag);
@@ -546,10 +768,12 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
             a.geo = geo;
             a.round = l;
             const dim3 grid((unsigned)lay.tiles);
+            const bool sorted_last = keep_sorted && l == rounds - 1 && p == passes - 1;
+            if (sorted_last && sorted_out) *sorted_out = vals[p & 1];
             if (p == 0) {
                 timer.begin(kKindFirst, key_src_bytes + (double)n * 12);
                 k_onesweep<kFirst><<<grid, kBlock, 0, stream>>>(a);
-            } else if (p == passes - 1) {
+            } else if (p == passes - 1 && !sorted_last) {
                 timer.begin(kKindLast, (double)n * 16);  // key+val in, tag out
                 k_onesweep<kLast><<<grid, kBlock, 0, stream>>>(a);
             } else {
@@ -595,6 +819,12 @@ size_t kdt_workspace_size(int64_t N, int32_t k) {
 
 namespace {
 
+int split_level(const Geometry& g) {
+    int l = 0;
+    while (subtree_size(g, full_nodes(l)) > (u64)kLocalMax) ++l;
+    return l;
+}
+
 kdt_status build_impl(const float* points, int64_t N, int32_t k, int32_t* perm_out,
                       float* tree_out, void* workspace, size_t workspace_bytes,
                       hipStream_t stream, Timer timer) {
@@ -604,16 +834,34 @@ kdt_status build_impl(const float* points, int64_t N, int32_t k, int32_t* perm_o
     kdt_status st = validate(points, N, k, perm_out, perm_bytes, tree_out, tree_bytes, workspace,
                              workspace_bytes, &lay);
     if (st != KDT_OK || N == 0) return st;
-    const int rounds = make_geometry(N).levels - 1;
-    const u32* tag = nullptr;
-    if (rounds > 0) {
-        st = run_rounds(points, N, k, rounds, (char*)workspace, lay, stream, timer);
+    const Geometry geo = make_geometry(N);
+    const int l0 = split_level(geo);
+    const u32* sorted = nullptr;
+    if (l0 > 0) {
+        // Global rounds 0 .. l0-1; the last one leaves its sorted order.
+        st = run_rounds(points, N, k, l0, (char*)workspace, lay, stream, timer, true, &sorted);
         if (st != KDT_OK) return st;
-        tag = (const u32*)((char*)workspace + lay.tag);
+        const u64 top = full_nodes(l0);
+        timer.begin(kKindPlace, (double)top * (4 + 4 + (tree_out ? 8.0 * k : 0)));
+        k_place_top<<<(unsigned)((top + kBlock - 1) / kBlock), kBlock, 0, stream>>>(
+            points, k, geo, l0, sorted, perm_out, tree_out);
+        timer.end();
     }
-    timer.begin(kKindPlace, (double)N * ((tag ? 4 : 0) + 4 + (tree_out ? 8.0 * k : 0)));
-    k_place<<<grid_for(N, kBlock * 4, 8192), kBlock, 0, stream>>>(points, N, k, tag, perm_out,
-                                                                  tree_out);
+    SubtreeArgs sa{};
+    sa.pts = points;
+    sa.n = N;
+    sa.k = k;
+    sa.l0 = l0;
+    sa.geo = geo;
+    sa.sorted = sorted;
+    int bits = 0;
+    for (u64 v = (u64)(N - 1); v; v >>= 1) ++bits;
+    sa.index_passes = l0 > 0 ? (bits + kRadixBits - 1) / kRadixBits : 0;
+    sa.perm = perm_out;
+    sa.tree = tree_out;
+    const i64 below = N - (i64)full_nodes(l0);  // points in the level-l0 subtrees
+    timer.begin(kKindSubtree, (double)below * ((l0 > 0 ? 4 : 0) + 4 + (tree_out ? 8.0 * k : 4.0 * k)));
+    k_subtree<<<(unsigned)(1ull << l0), kBlock, 0, stream>>>(sa);
     timer.end();
     return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
 }
