@@ -125,7 +125,8 @@ def main():
         roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                     "kernel": dom, "avg_us": d["avg_us"], "bytes_per_launch": d["bytes_per_launch"]}
-        passes = [kk for kk in kernels if kk.startswith("sweep") or kk == "hist"]
+        passes = [kk for kk in kernels
+                  if kk in ("hist", "presort", "tag_pass", "tag_update", "final_pass")]
         tot_b = sum(agg[kk]["bytes"] for kk in passes)
         tot_ms = sum(agg[kk]["ms"] for kk in passes)
         roofline["sort_and_update_passes"] = {
@@ -152,7 +153,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u64",
+        "dtype": "u32",
         "data": "synthetic",
         "config": {"workload": name, "n_points": n, "k": k, "coords": "f32",
                    "description": w.note},

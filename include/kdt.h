@@ -16,8 +16,12 @@
  * carries a 32-bit tag, the id of its ancestor on the current level (tag
  * paragraph); each round sorts all points by (tag, coordinate l mod k,
  * original index) and refines every tag from the closed-form subtree sizes
- * and segment starts (sort-order and sb/ss paragraphs). Rounds run on the
- * GPU as LSD radix passes over 64-bit keys with a fused tag update.
+ * and segment starts (sort-order and sb/ss paragraphs). On the GPU the sort
+ * is a stable LSD radix sort from index order; its coordinate-digit passes
+ * are the same in every round that splits on a dimension, so they run once
+ * per dimension and each round runs only its tag-digit passes, the last one
+ * fused with the tag update. Subtrees of at most 4096 points finish their
+ * remaining rounds inside one workgroup's LDS.
  *
  * Conventions for every entry point:
  *   - All pointers marked "device" are HIP device pointers on the current
@@ -111,8 +115,10 @@ kdt_status kdt_build_profiled(const float* points, int64_t N, int32_t k,
 int64_t kdt_closed_subtree_size(int64_t N, int64_t s);
 int64_t kdt_closed_segment_begin(int64_t N, int64_t s, int32_t l);
 
-/* Number of radix passes the round that fixes level l uses (keys of
- * 32 + tag bits, 8 bits per pass); -1 when l is out of range for N. */
+/* Number of 8-bit radix passes over the tag that round l (the round that
+ * fixes level l) runs on top of the cached per-dimension coordinate order:
+ * ceil((l+1)/8), and 0 for round 0 whose tags are all zero. -1 when l is out
+ * of range for N. */
 int32_t kdt_round_passes(int64_t N, int32_t l);
 
 /* Static description of a status code. */

@@ -62,12 +62,11 @@ def test_closed_segment_begin_is_prefix_sum():
 
 def test_round_passes():
     assert kdt.round_passes(1, 0) == -1
-    assert kdt.round_passes(2, 0) == 4
+    assert kdt.round_passes(2, 0) == 0
     assert kdt.round_passes(2, 1) == -1
-    n = 1 << 24  # 25 levels, 24 rounds
+    n = 1 << 24  # 25 levels, 24 rounds; tags of round l have l+1 bits
     got = [kdt.round_passes(n, l) for l in range(24)]
-    assert got == [4] + [5] * 7 + [6] * 8 + [7] * 8
-    assert sum(got) == 143
+    assert got == [0] + [1] * 7 + [2] * 8 + [3] * 8
 
 
 def test_workspace_size():

@@ -3,25 +3,36 @@
 // (Almost-)In-Place Construction of Left-Balanced k-d Trees" (arXiv
 // 2211.00120), cited as [W] with the paragraph that states each fact.
 //
-// Pipeline per build (all on the caller's stream, nothing allocated):
-//   k_init       AoS points -> one contiguous column per split dimension,
-//                clears the radix bookkeeping.
-//   per round l = 0 .. numLevels(N)-2  (round l fixes level l):
-//     k_hist     digit histograms of key = tag<<32 | fkey(x[l mod k]) for
-//                every radix pass of the round, from index order.
-//     k_onesweep P passes of a stable LSD radix sort, 8-bit digits; pass 0
-//                builds the keys from the tags and the column with the
-//                original index as payload, so equal (tag, coordinate)
-//                pairs stay in index order; the last pass does not write
-//                the sorted array but updates every tag in place from its
-//                sorted position.
-//   k_place      perm[tag[i]] = i and the level-order coordinate copy.
+// Round l of [W] sorts every point by (tag, coordinate l mod k, original
+// index) and refines every tag from its sorted position. Here that sort is a
+// stable LSD radix sort from index order with 8-bit digits. Its first
+// passes, over the coordinate's bytes, do not depend on the tags: they always
+// produce the points ordered by (coordinate d, index), whatever the round.
+// That order is computed once per split dimension ("presort") and every
+// round then runs only its tag-digit passes over it; the last tag pass
+// updates the tags in place from the sorted positions.
 //
-// The radix pass is a one-sweep design: per-tile digit counts from wave64
+// Pipeline per build (all on the caller's stream, nothing allocated):
+//   k_init       AoS points -> one column per split dimension; clears the
+//                radix bookkeeping.
+//   k_col_hist   byte histograms of each column's order-preserving keys.
+//   k_sweep x4   per dimension: stable sort of (key(x_d), index) -> order_d.
+//   k_round0     round 0 (all tags 0): tags straight from order_0.
+//   per round l = 1 .. l0-1:
+//     k_tag_hist tag-digit histograms, from the closed-form subtree sizes.
+//     k_sweep    1-2 passes by tag over order_{l mod k} (the first gathers
+//                each point's tag); the last one updates the tags, or, in
+//                round l0-1, writes the sorted order for the next stage.
+//   k_place_top  nodes above level l0.
+//   k_subtree    one workgroup per level-l0 subtree (<= 4096 points) runs
+//                that subtree's remaining rounds in LDS and writes its
+//                level-order output.
+//
+// A radix pass is a one-sweep design: per-tile digit counts from wave64
 // ballots (multi-split ranking), cross-tile offsets by decoupled look-back
 // over agent-scope atomics (Merrill & Garland's single-pass prefix scan),
-// digit bases from the histogram, and an LDS-staged scatter so that the
-// global writes of one digit are contiguous.
+// digit bases from a histogram, and an LDS-staged scatter so that the global
+// writes of one digit are contiguous.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -39,17 +50,16 @@ constexpr int kRadixBits = 8;
 constexpr int kRadix = 1 << kRadixBits;
 constexpr int kBlock = 256;                // threads per workgroup
 constexpr int kWaves = kBlock / 64;        // wave64
-constexpr int kItems = 16;                 // keys per thread in a radix tile
-constexpr int kTile = kBlock * kItems;     // keys per radix tile
-constexpr int kMaxPasses = 8;              // 64-bit keys
-constexpr int kHistBlocksMax = 2048;
+constexpr int kItems = 16;                 // records per thread in a radix tile
+constexpr int kTile = kBlock * kItems;     // records per radix tile
+constexpr int kKeyBytes = 4;               // order-preserving coordinate key
+constexpr int kMaxTagPasses = 4;           // 32-bit tags
 constexpr u64 kFlagShift = 62;
 constexpr u64 kFlagAggregate = 1ull << kFlagShift;
 constexpr u64 kFlagPrefix = 2ull << kFlagShift;
 constexpr u64 kCountMask = (1ull << kFlagShift) - 1;
 static_assert(kBlock == kRadix, "the look-back maps one thread to one digit");
-constexpr int kHistWords = 2 * kMaxPasses * kRadix;  // two rounds' histograms
-constexpr int kTicketWords = 64;                      // two tile tickets, padded
+constexpr int kTicketWords = 64;
 
 // ------------------------------------------------------------ tree geometry
 // Level-order complete tree with N nodes ([W], indexing paragraph):
@@ -101,14 +111,6 @@ __host__ __device__ inline u64 segment_begin(const Geometry& g, u64 s, int l) {
     return full_nodes(l) + j * ((1ull << dd) - 1) + under;
 }
 
-// Radix passes of round l: the key holds 32 coordinate bits plus the tag,
-// whose largest value in round l is F(l+1)-1 (l+1 bits; all tags are 0 in
-// round 0).
-__host__ __device__ inline int round_passes(int l) {
-    int bits = 32 + (l == 0 ? 0 : l + 1);
-    return (bits + kRadixBits - 1) / kRadixBits;
-}
-
 // Order-preserving map of float bits to unsigned: IEEE order with -0 == +0.
 // Pure bit tests, so denormals are never flushed.
 __device__ inline u32 float_key(u32 b) {
@@ -149,9 +151,14 @@ __device__ inline void status_store(u64* p, u64 v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// ----------------------------------------------------------------- kernels
+// Radix passes over the tag in round l: tags there are < F(l+1) = 2^(l+1) - 1.
+__host__ __device__ inline int tag_passes(int l) { return (l + 1 + kRadixBits - 1) / kRadixBits; }
 
-// Column copy of the split dimensions and clearing of the radix bookkeeping.
+// ------------------------------------------------------ global-phase kernels
+
+// Column copy of the split dimensions; clears the first pass's look-back
+// words, the histograms and the tile ticket (a kernel rather than memset
+// nodes, so the sequence can be captured into a graph).
 __global__ __launch_bounds__(kBlock) void k_init(const float* __restrict__ pts, i64 n, int k,
                                                  int kcols, float* __restrict__ cols,
                                                  u64* __restrict__ status0, i64 status_words,
@@ -167,65 +174,104 @@ __global__ __launch_bounds__(kBlock) void k_init(const float* __restrict__ pts, 
         for (int i = threadIdx.x; i < small_words; i += kBlock) small[i] = 0;
 }
 
-struct KeySource {
-    const u32* tag;   // nullptr in round 0 (all tags are 0)
-    const float* col; // coordinate column of dimension l mod k
-};
-
-__device__ inline u64 make_key(const KeySource& src, i64 e) {
-    u32 t = src.tag ? src.tag[e] : 0u;
-    u32 x = __float_as_uint(src.col[e]);
-    return ((u64)t << 32) | float_key(x);
-}
-
-// All digit histograms of one round's keys (read once, in index order).
-__global__ __launch_bounds__(kBlock) void k_hist(KeySource src, i64 n, int passes,
-                                                 u32* __restrict__ hist) {
-    __shared__ u32 h[kWaves][kMaxPasses][kRadix];
+// Histograms of the four bytes of key(x) over one column. Each thread
+// counts runs of equal digits before touching LDS, which keeps the heavily
+// skewed high bytes (exponents of clustered data) off a single LDS bank.
+__global__ __launch_bounds__(kBlock) void k_col_hist(const float* __restrict__ col, i64 n,
+                                                     u32* __restrict__ hist) {
+    __shared__ u32 h[kWaves][kKeyBytes][kRadix];
     const int w = threadIdx.x >> 6;
-    for (int i = threadIdx.x; i < kWaves * kMaxPasses * kRadix; i += kBlock) (&h[0][0][0])[i] = 0;
+    for (int i = threadIdx.x; i < kWaves * kKeyBytes * kRadix; i += kBlock) (&h[0][0][0])[i] = 0;
     __syncthreads();
+    u32 last[kKeyBytes], run[kKeyBytes];
+#pragma unroll
+    for (int b = 0; b < kKeyBytes; ++b) {
+        last[b] = 0;
+        run[b] = 0;
+    }
     const i64 stride = (i64)gridDim.x * kBlock;
     for (i64 e = (i64)blockIdx.x * kBlock + threadIdx.x; e < n; e += stride) {
-        u64 key = make_key(src, e);
-        for (int p = 0; p < passes; ++p)
-            atomicAdd(&h[w][p][(u32)(key >> (p * kRadixBits)) & (kRadix - 1)], 1u);
+        const u32 key = float_key(__float_as_uint(col[e]));
+#pragma unroll
+        for (int b = 0; b < kKeyBytes; ++b) {
+            const u32 d = (key >> (8 * b)) & (kRadix - 1);
+            if (run[b] && d != last[b]) {
+                atomicAdd(&h[w][b][last[b]], run[b]);
+                run[b] = 0;
+            }
+            last[b] = d;
+            ++run[b];
+        }
     }
+#pragma unroll
+    for (int b = 0; b < kKeyBytes; ++b)
+        if (run[b]) atomicAdd(&h[w][b][last[b]], run[b]);
     __syncthreads();
-    for (int i = threadIdx.x; i < passes * kRadix; i += kBlock) {
+    for (int i = threadIdx.x; i < kKeyBytes * kRadix; i += kBlock) {
         u32 s = 0;
         for (int v = 0; v < kWaves; ++v) s += (&h[v][0][0])[i];
         if (s) atomicAdd(&hist[i], s);
     }
 }
 
-enum PassMode { kFirst = 0, kMiddle = 1, kLast = 2 };
+// Byte histograms of the tags in round l without reading any point: F(l)
+// fixed nodes hold one point each and live subtree s holds |S(s)| points.
+// One workgroup; overwrites hist[0 .. passes*256).
+__global__ __launch_bounds__(kBlock) void k_tag_hist(Geometry geo, int l, int passes,
+                                                     u32* __restrict__ hist) {
+    __shared__ u32 h[kMaxTagPasses][kRadix];
+    for (int i = threadIdx.x; i < kMaxTagPasses * kRadix; i += kBlock) (&h[0][0])[i] = 0;
+    __syncthreads();
+    const u64 fixed = full_nodes(l), end = full_nodes(l + 1);
+    for (u64 t = threadIdx.x; t < end; t += kBlock) {
+        const u64 c = t < fixed ? 1 : subtree_size(geo, t);
+        if (c == 0) continue;
+        for (int b = 0; b < passes; ++b) atomicAdd(&h[b][(t >> (8 * b)) & (kRadix - 1)], (u32)c);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < passes * kRadix; i += kBlock) hist[i] = (&h[0][0])[i];
+}
 
-struct PassArgs {
+// Round 0: every tag is 0, so the sorted order is order_0 itself and the
+// pivot sits at position |S(1)|.
+__global__ __launch_bounds__(kBlock) void k_round0(const u32* __restrict__ order, Geometry geo,
+                                                   u32* __restrict__ tag) {
+    const u64 pivot = subtree_size(geo, 1);
+    const i64 stride = (i64)gridDim.x * kBlock;
+    for (i64 r = (i64)blockIdx.x * kBlock + threadIdx.x; r < geo.n; r += stride) {
+        const u32 i = order[r];
+        if (i < (u64)geo.n) tag[i] = (u64)r < pivot ? 1u : ((u64)r > pivot ? 2u : 0u);
+    }
+}
+
+enum Src { kSrcColumn = 0, kSrcArrays = 1, kSrcGather = 2 };
+enum Sink { kSinkArrays = 0, kSinkVals = 1, kSinkTags = 2 };
+
+struct SweepArgs {
     i64 n;
     int shift;                 // digit = (key >> shift) & 255
-    KeySource src;             // kFirst
-    const u64* keys_in;        // kMiddle, kLast
-    const u32* vals_in;
-    u64* keys_out;             // kFirst, kMiddle
-    u32* vals_out;
-    u32* tag_out;              // kLast
-    const u32* digit_hist;     // 256 counts of this pass's digit over all keys
+    const float* col;          // kSrcColumn: key = key(col[i]), val = i
+    const u32* keys_in;        // kSrcArrays
+    const u32* vals_in;        // kSrcArrays; kSrcGather: the list of point indices
+    const u32* gather;         // kSrcGather: key = gather[val] (the point's tag)
+    u32* keys_out;             // kSinkArrays
+    u32* vals_out;             // kSinkArrays, kSinkVals
+    u32* tag_out;              // kSinkTags
+    const u32* digit_hist;     // 256 counts of this pass's digit over all records
     u64* status;               // this pass's look-back words, zero on entry
     u64* status_next;          // next pass's words: cleared here
     u32* ticket;               // tile counter, zeroed once per build
     u32 ticket_base;           // tickets of this pass: [ticket_base, ticket_base + tiles)
-    u32* clear;                // kFirst: the next round's histogram, cleared here
-    int clear_words;
-    Geometry geo;              // kLast
-    int round;                 // kLast
+    Geometry geo;              // kSinkTags
+    int round;                 // kSinkTags
 };
 
-template <int kMode>
-__global__ __launch_bounds__(kBlock) void k_onesweep(PassArgs a) {
+// One stable radix pass over n (key, val) records.
+template <int kSrc, int kSink>
+__global__ __launch_bounds__(kBlock) void k_sweep(SweepArgs a) {
     __shared__ union {
         u32 count[kWaves][kRadix];  // ranking: per-wave digit counts, then prefixes
-        u64 keys[kTile];            // staging of the sorted tile
+        u32 keys[kTile];            // staging of the sorted tile
         u32 vals[kTile];
     } sm;
     __shared__ u8 s_digit[kTile];
@@ -242,33 +288,32 @@ __global__ __launch_bounds__(kBlock) void k_onesweep(PassArgs a) {
     __syncthreads();
     const u32 tile = s_tile;
     if (tile >= gridDim.x) return;  // cannot happen: one ticket per workgroup
-    // First global slot of digit `tid`: exclusive scan of the histogram.
     const u32 digit_start = block_exclusive_scan(hist_count, s_wave);
-
     a.status_next[(u64)tile * kRadix + tid] = 0;
-    if (kMode == kFirst)
-        for (int i = (int)tile * kBlock + tid; i < a.clear_words; i += (int)gridDim.x * kBlock)
-            a.clear[i] = 0;
 
-    // Load: wave w owns kItems rows of 64 consecutive keys.
+    // Load: wave w owns kItems rows of 64 consecutive records.
     const i64 base = (i64)tile * kTile;
     const i64 wbase = base + (i64)w * (64 * kItems) + lane;
-    u64 key[kItems];
-    u32 val[kItems];
+    u32 key[kItems], val[kItems];
 #pragma unroll
     for (int j = 0; j < kItems; ++j) {
         const i64 e = wbase + (i64)j * 64;
         key[j] = 0;
         val[j] = 0;
         if (e < a.n) {
-            if (kMode == kFirst) {
-                key[j] = make_key(a.src, e);
+            if (kSrc == kSrcColumn) {
+                key[j] = float_key(__float_as_uint(a.col[e]));
                 val[j] = (u32)e;
             } else {
-                key[j] = a.keys_in[e];
                 val[j] = a.vals_in[e];
+                if (kSrc == kSrcArrays) key[j] = a.keys_in[e];
             }
         }
+    }
+    if (kSrc == kSrcGather) {
+#pragma unroll
+        for (int j = 0; j < kItems; ++j)
+            if (wbase + (i64)j * 64 < a.n && val[j] < (u64)a.n) key[j] = a.gather[val[j]];
     }
 
     // Rank inside the wave: lanes holding the same digit are found with eight
@@ -279,7 +324,7 @@ __global__ __launch_bounds__(kBlock) void k_onesweep(PassArgs a) {
 #pragma unroll
     for (int j = 0; j < kItems; ++j) {
         const bool valid = (wbase + (i64)j * 64) < a.n;
-        const u32 d = (u32)(key[j] >> a.shift) & (kRadix - 1);
+        const u32 d = (key[j] >> a.shift) & (kRadix - 1);
         u64 peers = __ballot(valid);
 #pragma unroll
         for (int b = 0; b < kRadixBits; ++b) {
@@ -288,11 +333,10 @@ __global__ __launch_bounds__(kBlock) void k_onesweep(PassArgs a) {
             peers &= bit ? vote : ~vote;
         }
         const u32 before = __popcll(peers & below);
-        const u32 total = __popcll(peers);
         u32 seen = 0;
         if (valid) seen = sm.count[w][d];
         rank[j] = seen + before;
-        if (valid && before == 0) sm.count[w][d] = seen + total;
+        if (valid && before == 0) sm.count[w][d] = seen + (u32)__popcll(peers);
     }
     __syncthreads();
 
@@ -321,19 +365,18 @@ __global__ __launch_bounds__(kBlock) void k_onesweep(PassArgs a) {
         }
         status_store(mine, kFlagPrefix | (exclusive + agg));
     }
-    const u32 global_start = digit_start + (u32)exclusive;
     s_local[tid] = local_start;
-    s_base[tid] = global_start - local_start;  // modular; base + local slot < n
+    s_base[tid] = digit_start + (u32)exclusive - local_start;  // modular; base + slot < n
 
     u32 digit[kItems];
 #pragma unroll
     for (int j = 0; j < kItems; ++j) {
-        digit[j] = (u32)(key[j] >> a.shift) & (kRadix - 1);
+        digit[j] = (key[j] >> a.shift) & (kRadix - 1);
         if ((wbase + (i64)j * 64) < a.n) rank[j] += sm.count[w][digit[j]];
     }
     __syncthreads();
 
-    if (kMode == kLast) {
+    if (kSink == kSinkTags) {
         // Tag update ([W], tag and sort-order paragraphs): a point of subtree
         // s (s on level l, so s >= F(l)) at sorted position p moves to the
         // left child if p is before the pivot, to the right child if after,
@@ -343,7 +386,7 @@ __global__ __launch_bounds__(kBlock) void k_onesweep(PassArgs a) {
 #pragma unroll
         for (int j = 0; j < kItems; ++j) {
             if ((wbase + (i64)j * 64) >= a.n) continue;
-            const u64 s = key[j] >> 32;
+            const u64 s = key[j];
             if (s < fl) continue;
             const u64 p = (u64)(s_base[digit[j]] + s_local[digit[j]] + rank[j]);
             const u64 pivot = segment_begin(a.geo, s, a.round) + subtree_size(a.geo, 2 * s + 1);
@@ -354,23 +397,27 @@ __global__ __launch_bounds__(kBlock) void k_onesweep(PassArgs a) {
     }
 
     const int valid_here = (int)((a.n - base) < kTile ? (a.n - base) : kTile);
+    if (kSink == kSinkArrays) {
+#pragma unroll
+        for (int j = 0; j < kItems; ++j) {
+            if ((wbase + (i64)j * 64) >= a.n) continue;
+            const u32 slot = s_local[digit[j]] + rank[j];
+            sm.keys[slot] = key[j];
+            s_digit[slot] = (u8)digit[j];
+        }
+        __syncthreads();
+        for (int i = tid; i < valid_here; i += kBlock) {
+            const u32 dst = s_base[s_digit[i]] + (u32)i;
+            if (dst < (u64)a.n) a.keys_out[dst] = sm.keys[i];
+        }
+        __syncthreads();
+    }
 #pragma unroll
     for (int j = 0; j < kItems; ++j) {
         if ((wbase + (i64)j * 64) >= a.n) continue;
         const u32 slot = s_local[digit[j]] + rank[j];
-        sm.keys[slot] = key[j];
-        s_digit[slot] = (u8)digit[j];
-    }
-    __syncthreads();
-    for (int i = tid; i < valid_here; i += kBlock) {
-        const u32 dst = s_base[s_digit[i]] + (u32)i;
-        if (dst < (u64)a.n) a.keys_out[dst] = sm.keys[i];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kItems; ++j) {
-        if ((wbase + (i64)j * 64) >= a.n) continue;
-        sm.vals[s_local[digit[j]] + rank[j]] = val[j];
+        sm.vals[slot] = val[j];
+        if (kSink == kSinkVals) s_digit[slot] = (u8)digit[j];
     }
     __syncthreads();
     for (int i = tid; i < valid_here; i += kBlock) {
@@ -596,21 +643,6 @@ __global__ __launch_bounds__(kBlock) void k_place_top(const float* __restrict__ 
         for (int d = 0; d < k; ++d) tree[(i64)s * k + d] = pts[(i64)i * k + d];
 }
 
-// perm[node] = i and the level-order copy of the coordinates.
-__global__ __launch_bounds__(kBlock) void k_place(const float* __restrict__ pts, i64 n, int k,
-                                                  const u32* __restrict__ tag,
-                                                  int32_t* __restrict__ perm,
-                                                  float* __restrict__ tree) {
-    const i64 stride = (i64)gridDim.x * kBlock;
-    for (i64 e = (i64)blockIdx.x * kBlock + threadIdx.x; e < n; e += stride) {
-        const i64 node = tag ? (i64)tag[e] : e;
-        if (node >= n) continue;  // cannot happen: tags are node ids < n
-        perm[node] = (int32_t)e;
-        if (tree)
-            for (int d = 0; d < k; ++d) tree[node * k + d] = pts[e * k + d];
-    }
-}
-
 __global__ __launch_bounds__(kBlock) void k_copy_tags(const u32* __restrict__ tag, i64 n,
                                                       u32* __restrict__ out) {
     const i64 stride = (i64)gridDim.x * kBlock;
@@ -623,9 +655,11 @@ __global__ __launch_bounds__(kBlock) void k_copy_tags(const u32* __restrict__ ta
 inline size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-    int kcols;          // split dimensions actually used
+    int kcols;          // split dimensions the global rounds can use
     i64 tiles;
-    size_t cols, tag, keys0, keys1, vals0, vals1, small, status, total;
+    size_t cols, orders, tag, keys0, keys1, vals0, vals1, small, status, total;
+    // inside `small` (u32 words): column histograms, tag histograms, ticket
+    int col_hist_words, tag_hist_off, ticket_off, small_words;
 };
 
 bool make_layout(i64 n, int k, Layout* out) {
@@ -638,6 +672,10 @@ bool make_layout(i64 n, int k, Layout* out) {
     const int rounds = make_geometry(n).levels - 1;
     lay.kcols = rounds < k ? rounds : k;
     lay.tiles = (n + kTile - 1) / kTile;
+    lay.col_hist_words = lay.kcols * kKeyBytes * kRadix;
+    lay.tag_hist_off = lay.col_hist_words;
+    lay.ticket_off = lay.tag_hist_off + kMaxTagPasses * kRadix;
+    lay.small_words = lay.ticket_off + kTicketWords;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t at = off;
@@ -645,12 +683,13 @@ bool make_layout(i64 n, int k, Layout* out) {
         return at;
     };
     lay.cols = take((size_t)lay.kcols * n * sizeof(float));
+    lay.orders = take((size_t)lay.kcols * n * sizeof(u32));
     lay.tag = take((size_t)n * sizeof(u32));
-    lay.keys0 = take((size_t)n * sizeof(u64));
-    lay.keys1 = take((size_t)n * sizeof(u64));
+    lay.keys0 = take((size_t)n * sizeof(u32));
+    lay.keys1 = take((size_t)n * sizeof(u32));
     lay.vals0 = take((size_t)n * sizeof(u32));
     lay.vals1 = take((size_t)n * sizeof(u32));
-    lay.small = take((kHistWords + kTicketWords) * sizeof(u32));  // histograms, tickets
+    lay.small = take((size_t)lay.small_words * sizeof(u32));
     lay.status = take(2 * (size_t)lay.tiles * kRadix * sizeof(u64));
     lay.total = off;
     *out = lay;
@@ -671,10 +710,11 @@ bool ranges_overlap(const void* a, size_t an, const void* b, size_t bn) {
 }
 
 // Optional per-kernel timing: an event pair around every launch.
-enum Kind { kKindInit, kKindHist, kKindFirst, kKindMid, kKindLast, kKindPlace, kKindSubtree,
-            kKinds };
-const char* const kKindNames[kKinds] = {"init", "hist", "sweep_first", "sweep_mid",
-                                        "sweep_last", "place", "subtree"};
+enum Kind { kKindInit, kKindHist, kKindPresort, kKindTagPass, kKindUpdate, kKindFinal,
+            kKindPlace, kKindSubtree, kKinds };
+const char* const kKindNames[kKinds] = {"init", "hist", "presort", "tag_pass", "tag_update",
+                                        "final_pass", "place_top", "subtree"};
+static_assert(kKinds <= KDT_PROFILE_MAX_KINDS, "profile kinds");
 
 struct Profiler {
     struct Rec {
@@ -682,17 +722,19 @@ struct Profiler {
         double bytes;
         hipEvent_t start, stop;
     };
-    Rec recs[1024];
+    Rec recs[2048];
     int count = 0;
     bool failed = false;
     hipStream_t stream;
 
     void begin(int kind, double bytes) {
-        if (count >= 1024) { failed = true; return; }
+        if (count >= 2048) { failed = true; return; }
         Rec& r = recs[count];
         r.kind = kind;
         r.bytes = bytes;
-        if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess) {
+        if (hipEventCreate(&r.start) != hipSuccess) { failed = true; return; }
+        if (hipEventCreate(&r.stop) != hipSuccess) {
+            hipEventDestroy(r.start);
             failed = true;
             return;
         }
@@ -711,76 +753,123 @@ struct Timer {  // no-op unless a Profiler is attached
     void end() { if (p) p->end(); }
 };
 
-// Runs the first `rounds` rounds on the whole point set. With keep_sorted,
-// the last round writes its sorted order (point indices, returned in
-// *sorted_out) instead of updating the tags; otherwise the tags after
-// `rounds` rounds are left in the workspace.
-kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, const Layout& lay,
-                      hipStream_t stream, Timer timer, bool keep_sorted = false,
-                      const u32** sorted_out = nullptr) {
-    const Geometry geo = make_geometry(n);
-    float* cols = (float*)(ws + lay.cols);
-    u32* tag = (u32*)(ws + lay.tag);
-    u64* keys[2] = {(u64*)(ws + lay.keys0), (u64*)(ws + lay.keys1)};
-    u32* vals[2] = {(u32*)(ws + lay.vals0), (u32*)(ws + lay.vals1)};
-    u32* hist = (u32*)(ws + lay.small);
-    u32* tickets = hist + kHistWords;
-    u64* status = (u64*)(ws + lay.status);
-    const i64 status_words = lay.tiles * kRadix;
+// Launches one radix pass; keeps the look-back word and ticket bookkeeping.
+struct SweepLauncher {
+    const Layout& lay;
+    u64* status;
+    u32* ticket;
+    hipStream_t stream;
+    Timer timer;
+    int pass_index = 0;
 
-    const int grid_elems = grid_for(n, kBlock * 4, 8192);
-    // Clears the first pass's look-back words, both histogram halves and the
-    // tile tickets (a kernel rather than a memset node, so the sequence can
-    // be captured into a graph).
-    timer.begin(kKindInit, (double)n * lay.kcols * 8);
-    k_init<<<grid_elems, kBlock, 0, stream>>>(pts, n, k, lay.kcols, cols, status, status_words,
-                                              hist, kHistWords + kTicketWords);
+    template <int kSrc, int kSink>
+    void run(SweepArgs a, int kind, double bytes) {
+        const i64 words = lay.tiles * kRadix;
+        a.status = status + (size_t)(pass_index & 1) * words;
+        a.status_next = status + (size_t)((pass_index + 1) & 1) * words;
+        a.ticket = ticket;
+        a.ticket_base = (u32)((u64)pass_index * (u64)lay.tiles);
+        ++pass_index;
+        timer.begin(kind, bytes);
+        k_sweep<kSrc, kSink><<<(unsigned)lay.tiles, kBlock, 0, stream>>>(a);
+        timer.end();
+    }
+};
+
+// Runs rounds 0 .. rounds-1 on the whole point set. With keep_sorted the
+// last round writes its sorted order (point indices, returned in
+// *sorted_out) instead of updating the tags; otherwise the tags after
+// `rounds` rounds are left in the workspace's tag array.
+kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, const Layout& lay,
+                      hipStream_t stream, Timer timer, bool keep_sorted,
+                      const u32** sorted_out) {
+    const Geometry geo = make_geometry(n);
+    const int kc = rounds < k ? rounds : k;  // dimensions these rounds split on
+    float* cols = (float*)(ws + lay.cols);
+    u32* orders = (u32*)(ws + lay.orders);
+    u32* tag = (u32*)(ws + lay.tag);
+    u32* keys[2] = {(u32*)(ws + lay.keys0), (u32*)(ws + lay.keys1)};
+    u32* vals[2] = {(u32*)(ws + lay.vals0), (u32*)(ws + lay.vals1)};
+    u32* small = (u32*)(ws + lay.small);
+    u32* col_hist = small;
+    u32* tag_hist = small + lay.tag_hist_off;
+    u64* status = (u64*)(ws + lay.status);
+    SweepLauncher sweep{lay, status, small + lay.ticket_off, stream, timer};
+    const double N = (double)n;
+
+    timer.begin(kKindInit, N * kc * 8);
+    k_init<<<grid_for(n, kBlock * 4, 8192), kBlock, 0, stream>>>(
+        pts, n, k, kc, cols, status, lay.tiles * kRadix, small, lay.small_words);
     timer.end();
 
-    int pass_index = 0;
-    for (int l = 0; l < rounds; ++l) {
-        const int d = l % k;
-        const int passes = round_passes(l);
-        u32* h = hist + (size_t)(l & 1) * kMaxPasses * kRadix;
-        u32* h_next = hist + (size_t)((l + 1) & 1) * kMaxPasses * kRadix;
-        KeySource src{l == 0 ? nullptr : tag, cols + (size_t)d * n};
-        const double key_src_bytes = (double)n * (l == 0 ? 4 : 8);  // (tag +) column
-        timer.begin(kKindHist, key_src_bytes);
-        k_hist<<<grid_for(n, kBlock * 16, kHistBlocksMax), kBlock, 0, stream>>>(src, n, passes, h);
+    // Presort: order_d = point indices by (coordinate d, index).
+    for (int d = 0; d < kc; ++d) {
+        const float* col = cols + (size_t)d * n;
+        u32* hist = col_hist + (size_t)d * kKeyBytes * kRadix;
+        timer.begin(kKindHist, N * 4);
+        k_col_hist<<<grid_for(n, kBlock * 16, 2048), kBlock, 0, stream>>>(col, n, hist);
         timer.end();
-        for (int p = 0; p < passes; ++p, ++pass_index) {
-            PassArgs a{};
+        for (int p = 0; p < kKeyBytes; ++p) {
+            SweepArgs a{};
             a.n = n;
-            a.shift = p * kRadixBits;
-            a.src = src;
+            a.shift = 8 * p;
+            a.col = col;
             a.keys_in = keys[(p + 1) & 1];
             a.vals_in = vals[(p + 1) & 1];
             a.keys_out = keys[p & 1];
+            a.vals_out = p == kKeyBytes - 1 ? orders + (size_t)d * n : vals[p & 1];
+            a.digit_hist = hist + p * kRadix;
+            if (p == 0)
+                sweep.run<kSrcColumn, kSinkArrays>(a, kKindPresort, N * 12);
+            else if (p < kKeyBytes - 1)
+                sweep.run<kSrcArrays, kSinkArrays>(a, kKindPresort, N * 16);
+            else
+                sweep.run<kSrcArrays, kSinkVals>(a, kKindPresort, N * 12);
+        }
+    }
+
+    // Round 0: all tags are 0.
+    if (keep_sorted && rounds == 1) {
+        *sorted_out = orders;
+    } else {
+        timer.begin(kKindUpdate, N * 8);
+        k_round0<<<grid_for(n, kBlock * 4, 8192), kBlock, 0, stream>>>(orders, geo, tag);
+        timer.end();
+    }
+
+    for (int l = 1; l < rounds; ++l) {
+        const int d = l % k;
+        const int passes = tag_passes(l);
+        const bool final = keep_sorted && l == rounds - 1;
+        timer.begin(kKindHist, 0);
+        k_tag_hist<<<1, kBlock, 0, stream>>>(geo, l, passes, tag_hist);
+        timer.end();
+        for (int p = 0; p < passes; ++p) {
+            SweepArgs a{};
+            a.n = n;
+            a.shift = 8 * p;
+            a.gather = tag;
+            a.keys_in = keys[(p + 1) & 1];
+            a.vals_in = p == 0 ? orders + (size_t)d * n : vals[(p + 1) & 1];
+            a.keys_out = keys[p & 1];
             a.vals_out = vals[p & 1];
             a.tag_out = tag;
-            a.digit_hist = h + (size_t)p * kRadix;
-            a.status = status + (size_t)(pass_index & 1) * status_words;
-            a.status_next = status + (size_t)((pass_index + 1) & 1) * status_words;
-            a.ticket = tickets;
-            a.ticket_base = (u32)((u64)pass_index * (u64)lay.tiles);
-            a.clear = h_next;
-            a.clear_words = kMaxPasses * kRadix;
+            a.digit_hist = tag_hist + p * kRadix;
             a.geo = geo;
             a.round = l;
-            const dim3 grid((unsigned)lay.tiles);
-            const bool sorted_last = keep_sorted && l == rounds - 1 && p == passes - 1;
-            if (sorted_last && sorted_out) *sorted_out = vals[p & 1];
-            if (p == 0) {
-                timer.begin(kKindFirst, key_src_bytes + (double)n * 12);
-                k_onesweep<kFirst><<<grid, kBlock, 0, stream>>>(a);
-            } else if (p == passes - 1 && !sorted_last) {
-                timer.begin(kKindLast, (double)n * 16);  // key+val in, tag out
-                k_onesweep<kLast><<<grid, kBlock, 0, stream>>>(a);
+            const bool last = p == passes - 1;
+            const double in = p == 0 ? N * 8 : N * 8;  // list + gathered tag, or records
+            if (!last) {
+                if (p == 0) sweep.run<kSrcGather, kSinkArrays>(a, kKindTagPass, in + N * 8);
+                else sweep.run<kSrcArrays, kSinkArrays>(a, kKindTagPass, in + N * 8);
+            } else if (final) {
+                *sorted_out = vals[p & 1];
+                if (p == 0) sweep.run<kSrcGather, kSinkVals>(a, kKindFinal, in + N * 4);
+                else sweep.run<kSrcArrays, kSinkVals>(a, kKindFinal, in + N * 4);
             } else {
-                timer.begin(kKindMid, (double)n * 24);
-                k_onesweep<kMiddle><<<grid, kBlock, 0, stream>>>(a);
+                if (p == 0) sweep.run<kSrcGather, kSinkTags>(a, kKindUpdate, in + N * 4);
+                else sweep.run<kSrcArrays, kSinkTags>(a, kKindUpdate, in + N * 4);
             }
-            timer.end();
         }
     }
     return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
@@ -807,18 +896,8 @@ kdt_status validate(const float* pts, i64 n, int k, const void* out0, size_t out
     return KDT_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t kdt_workspace_size(int64_t N, int32_t k) {
-    Layout lay;
-    if (!make_layout(N, k, &lay)) return 0;
-    return lay.total;
-}
-
-namespace {
-
+// First level whose subtrees all fit one workgroup (the leftmost subtree of
+// a level is the largest one).
 int split_level(const Geometry& g) {
     int l = 0;
     while (subtree_size(g, full_nodes(l)) > (u64)kLocalMax) ++l;
@@ -868,6 +947,14 @@ kdt_status build_impl(const float* points, int64_t N, int32_t k, int32_t* perm_o
 
 }  // namespace
 
+extern "C" {
+
+size_t kdt_workspace_size(int64_t N, int32_t k) {
+    Layout lay;
+    if (!make_layout(N, k, &lay)) return 0;
+    return lay.total;
+}
+
 kdt_status kdt_build(const float* points, int64_t N, int32_t k, int32_t* perm_out,
                      float* tree_out, void* workspace, size_t workspace_bytes,
                      hipStream_t stream) {
@@ -886,9 +973,8 @@ kdt_status kdt_build_profiled(const float* points, int64_t N, int32_t k, int32_t
     if (hipStreamSynchronize(stream) != hipSuccess && st == KDT_OK) st = KDT_ERR_HIP;
     *profile = kdt_profile{};
     profile->kinds = kKinds;
-    for (int i = 0; i < kKinds; ++i) {
+    for (int i = 0; i < kKinds; ++i)
         for (int c = 0; kKindNames[i][c] && c < 23; ++c) profile->name[i][c] = kKindNames[i][c];
-    }
     for (int i = 0; i < prof->count; ++i) {
         Profiler::Rec& r = prof->recs[i];
         float ms = 0.f;
@@ -919,7 +1005,8 @@ kdt_status kdt_debug_tags(const float* points, int64_t N, int32_t k, int32_t rou
     if (rounds < 0 || rounds > max_rounds) return KDT_ERR_INVALID_ARG;
     const u32* tag = nullptr;
     if (rounds > 0) {
-        st = run_rounds(points, N, k, rounds, (char*)workspace, lay, stream, Timer{nullptr});
+        st = run_rounds(points, N, k, rounds, (char*)workspace, lay, stream, Timer{nullptr},
+                        false, nullptr);
         if (st != KDT_OK) return st;
         tag = (const u32*)((char*)workspace + lay.tag);
     }
@@ -943,7 +1030,7 @@ int64_t kdt_closed_segment_begin(int64_t N, int64_t s, int32_t l) {
 int32_t kdt_round_passes(int64_t N, int32_t l) {
     if (N <= 1 || N > INT32_MAX) return -1;
     if (l < 0 || l >= make_geometry(N).levels - 1) return -1;
-    return round_passes(l);
+    return l == 0 ? 0 : tag_passes(l);
 }
 
 const char* kdt_status_string(kdt_status status) {
