@@ -56,6 +56,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1 << 22)
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event loop")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="first run one plain 256 MiB device-to-device copy, the reference "
+                         "dispatch for scaling hardware traffic counters")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -78,6 +81,14 @@ def main():
     tree = torch.empty_like(x)
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize(dev)
+
+    if args.calibration_copy:
+        src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize(dev)
+        dst.copy_(src)  # reads 256 MiB, writes 256 MiB
+        torch.cuda.synchronize(dev)
+        del src, dst
 
     log("bench: %d warmup builds" % args.warmup)
     for _ in range(args.warmup):

@@ -54,12 +54,7 @@ constexpr int kItems = 16;                 // records per thread in a radix tile
 constexpr int kTile = kBlock * kItems;     // records per radix tile
 constexpr int kKeyBytes = 4;               // order-preserving coordinate key
 constexpr int kMaxTagPasses = 4;           // 32-bit tags
-constexpr u64 kFlagShift = 62;
-constexpr u64 kFlagAggregate = 1ull << kFlagShift;
-constexpr u64 kFlagPrefix = 2ull << kFlagShift;
-constexpr u64 kCountMask = (1ull << kFlagShift) - 1;
-static_assert(kBlock == kRadix, "the look-back maps one thread to one digit");
-constexpr int kTicketWords = 64;
+static_assert(kBlock == kRadix, "the tile kernels map one thread to one digit");
 
 // ------------------------------------------------------------ tree geometry
 // Level-order complete tree with N nodes ([W], indexing paragraph):
@@ -144,32 +139,22 @@ __device__ inline u32 block_exclusive_scan(u32 v, u32* s_wave) {
     return off + inc - v;
 }
 
-__device__ inline u64 status_load(const u64* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline void status_store(u64* p, u64 v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Radix passes over the tag in round l: tags there are < F(l+1) = 2^(l+1) - 1.
 __host__ __device__ inline int tag_passes(int l) { return (l + 1 + kRadixBits - 1) / kRadixBits; }
 
 // ------------------------------------------------------ global-phase kernels
 
-// Column copy of the split dimensions; clears the first pass's look-back
-// words, the histograms and the tile ticket (a kernel rather than memset
-// nodes, so the sequence can be captured into a graph).
+// Column copy of the split dimensions; clears the column histograms (a
+// kernel rather than a memset node, so the sequence can be captured into a
+// graph).
 __global__ __launch_bounds__(kBlock) void k_init(const float* __restrict__ pts, i64 n, int k,
                                                  int kcols, float* __restrict__ cols,
-                                                 u64* __restrict__ status0, i64 status_words,
                                                  u32* __restrict__ small, int small_words) {
     const i64 stride = (i64)gridDim.x * kBlock;
     for (i64 e = (i64)blockIdx.x * kBlock + threadIdx.x; e < n; e += stride) {
         const float* row = pts + e * k;
         for (int d = 0; d < kcols; ++d) cols[(i64)d * n + e] = row[d];
     }
-    for (i64 i = (i64)blockIdx.x * kBlock + threadIdx.x; i < status_words; i += stride)
-        status0[i] = 0;
     if (blockIdx.x == 0)
         for (int i = threadIdx.x; i < small_words; i += kBlock) small[i] = 0;
 }
@@ -247,54 +232,35 @@ __global__ __launch_bounds__(kBlock) void k_round0(const u32* __restrict__ order
 enum Src { kSrcColumn = 0, kSrcArrays = 1, kSrcGather = 2 };
 enum Sink { kSinkArrays = 0, kSinkVals = 1, kSinkTags = 2 };
 
-struct SweepArgs {
+// One stable radix pass over n (key, val) records is three launches
+// (reduce-then-scan; no workgroup ever waits on another):
+//   k_tile_count  digit counts of every tile of kTile records,
+//   k_tile_scan   per digit, exclusive scan over the tiles plus the digit's
+//                 first slot -> the first global slot of (tile, digit),
+//   k_tile_scatter rank each tile again and move its records there.
+struct PassArgs {
     i64 n;
     int shift;                 // digit = (key >> shift) & 255
     const float* col;          // kSrcColumn: key = key(col[i]), val = i
     const u32* keys_in;        // kSrcArrays
     const u32* vals_in;        // kSrcArrays; kSrcGather: the list of point indices
     const u32* gather;         // kSrcGather: key = gather[val] (the point's tag)
-    u32* keys_out;             // kSinkArrays
-    u32* vals_out;             // kSinkArrays, kSinkVals
+    u32* keys_out;             // scatter: kSinkArrays; count with kSrcGather: the
+    u32* vals_out;             //   gathered records, in list order; kSinkVals
     u32* tag_out;              // kSinkTags
     const u32* digit_hist;     // 256 counts of this pass's digit over all records
-    u64* status;               // this pass's look-back words, zero on entry
-    u64* status_next;          // next pass's words: cleared here
-    u32* ticket;               // tile counter, zeroed once per build
-    u32 ticket_base;           // tickets of this pass: [ticket_base, ticket_base + tiles)
+    u32* tile_slots;           // tiles x 256: counts, then first global slots
+    u32* scatter_keys;         // kSrcGather: where the scatter writes (keys_out/vals_out
+    u32* scatter_vals;         //   then hold the gathered records)
     Geometry geo;              // kSinkTags
     int round;                 // kSinkTags
 };
 
-// One stable radix pass over n (key, val) records.
-template <int kSrc, int kSink>
-__global__ __launch_bounds__(kBlock) void k_sweep(SweepArgs a) {
-    __shared__ union {
-        u32 count[kWaves][kRadix];  // ranking: per-wave digit counts, then prefixes
-        u32 keys[kTile];            // staging of the sorted tile
-        u32 vals[kTile];
-    } sm;
-    __shared__ u8 s_digit[kTile];
-    __shared__ u32 s_local[kRadix];  // first tile-local slot of each digit
-    __shared__ u32 s_base[kRadix];   // global slot of tile-local slot 0 of each digit
-    __shared__ u32 s_wave[kWaves];
-    __shared__ u32 s_tile;
-
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    // Tiles are numbered in the order workgroups start, so every tile a
-    // look-back waits on is already running.
-    if (tid == 0) s_tile = atomicAdd(a.ticket, 1u) - a.ticket_base;
-    const u32 hist_count = a.digit_hist[tid];
-    __syncthreads();
-    const u32 tile = s_tile;
-    if (tile >= gridDim.x) return;  // cannot happen: one ticket per workgroup
-    const u32 digit_start = block_exclusive_scan(hist_count, s_wave);
-    a.status_next[(u64)tile * kRadix + tid] = 0;
-
-    // Load: wave w owns kItems rows of 64 consecutive records.
-    const i64 base = (i64)tile * kTile;
-    const i64 wbase = base + (i64)w * (64 * kItems) + lane;
-    u32 key[kItems], val[kItems];
+// Records of item j of this thread: wave w owns kItems rows of 64
+// consecutive records of the tile.
+template <int kSrc>
+__device__ inline void load_tile(const PassArgs& a, i64 wbase, u32 (&key)[kItems],
+                                 u32 (&val)[kItems]) {
 #pragma unroll
     for (int j = 0; j < kItems; ++j) {
         const i64 e = wbase + (i64)j * 64;
@@ -315,16 +281,20 @@ __global__ __launch_bounds__(kBlock) void k_sweep(SweepArgs a) {
         for (int j = 0; j < kItems; ++j)
             if (wbase + (i64)j * 64 < a.n && val[j] < (u64)a.n) key[j] = a.gather[val[j]];
     }
+}
 
-    // Rank inside the wave: lanes holding the same digit are found with eight
-    // ballots; the lowest such lane bumps the wave's counter for the digit.
-    for (int i = lane; i < kRadix; i += 64) sm.count[w][i] = 0;
+// Rank inside the wave: lanes holding the same digit are found with eight
+// ballots; the lowest such lane bumps the wave's counter for the digit.
+// rank[j] = records of the same digit earlier in the wave's rows.
+__device__ inline void wave_rank(const u32 (&key)[kItems], i64 wbase, i64 n, int shift,
+                                 u32* count, u32 (&rank)[kItems]) {
+    const int lane = threadIdx.x & 63;
+    for (int i = lane; i < kRadix; i += 64) count[i] = 0;
     const u64 below = (1ull << lane) - 1;
-    u32 rank[kItems];
 #pragma unroll
     for (int j = 0; j < kItems; ++j) {
-        const bool valid = (wbase + (i64)j * 64) < a.n;
-        const u32 d = (key[j] >> a.shift) & (kRadix - 1);
+        const bool valid = (wbase + (i64)j * 64) < n;
+        const u32 d = (key[j] >> shift) & (kRadix - 1);
         u64 peers = __ballot(valid);
 #pragma unroll
         for (int b = 0; b < kRadixBits; ++b) {
@@ -334,13 +304,86 @@ __global__ __launch_bounds__(kBlock) void k_sweep(SweepArgs a) {
         }
         const u32 before = __popcll(peers & below);
         u32 seen = 0;
-        if (valid) seen = sm.count[w][d];
+        if (valid) seen = count[d];
         rank[j] = seen + before;
-        if (valid && before == 0) sm.count[w][d] = seen + (u32)__popcll(peers);
+        if (valid && before == 0) count[d] = seen + (u32)__popcll(peers);
     }
+}
+
+template <int kSrc>
+__global__ __launch_bounds__(kBlock) void k_tile_count(PassArgs a) {
+    __shared__ u32 count[kWaves][kRadix];
+    const int tid = threadIdx.x, w = tid >> 6;
+    const i64 base = (i64)blockIdx.x * kTile;
+    const i64 wbase = base + (i64)w * (64 * kItems) + (tid & 63);
+    u32 key[kItems], val[kItems], rank[kItems];
+    load_tile<kSrc>(a, wbase, key, val);
+    if (kSrc == kSrcGather) {
+#pragma unroll
+        for (int j = 0; j < kItems; ++j) {
+            const i64 e = wbase + (i64)j * 64;
+            if (e < a.n) {
+                a.keys_out[e] = key[j];
+                a.vals_out[e] = val[j];
+            }
+        }
+    }
+    wave_rank(key, wbase, a.n, a.shift, count[w], rank);
+    __syncthreads();
+    u32 total = 0;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) total += count[v][tid];
+    a.tile_slots[(u64)blockIdx.x * kRadix + tid] = total;
+}
+
+// One workgroup per digit d: slots[t][d] = start(d) + counts of d in tiles
+// before t, where start(d) is the exclusive prefix of the digit totals.
+__global__ __launch_bounds__(kBlock) void k_tile_scan(const u32* __restrict__ digit_hist,
+                                                      u32* __restrict__ slots, i64 tiles) {
+    __shared__ u32 s_wave[kWaves];
+    const int tid = threadIdx.x, d = blockIdx.x;
+    const u32 before = tid < d ? digit_hist[tid] : 0u;
+    u32 start = block_exclusive_scan(before, s_wave);  // + before = inclusive
+    start += before;
+    // every thread needs the total over tid < d: the last thread holds it
+    __shared__ u32 s_start;
+    if (tid == kBlock - 1) s_start = start;
+    __syncthreads();
+    u32 run = s_start;
+    const i64 per = (tiles + kBlock - 1) / kBlock;
+    const i64 t0 = tid * per, t1 = t0 + per < tiles ? t0 + per : tiles;
+    u32 sum = 0;
+    for (i64 t = t0; t < t1; ++t) sum += slots[(u64)t * kRadix + d];
+    u32 off = block_exclusive_scan(sum, s_wave) + run;
+    for (i64 t = t0; t < t1; ++t) {
+        const u32 c = slots[(u64)t * kRadix + d];
+        slots[(u64)t * kRadix + d] = off;
+        off += c;
+    }
+}
+
+template <int kSrc, int kSink>
+__global__ __launch_bounds__(kBlock) void k_tile_scatter(PassArgs a) {
+    __shared__ union {
+        u32 count[kWaves][kRadix];  // ranking: per-wave digit counts, then prefixes
+        u32 keys[kTile];            // staging of the sorted tile
+        u32 vals[kTile];
+    } sm;
+    __shared__ u8 s_digit[kTile];
+    __shared__ u32 s_local[kRadix];  // first tile-local slot of each digit
+    __shared__ u32 s_base[kRadix];   // global slot of tile-local slot 0 of each digit
+    __shared__ u32 s_wave[kWaves];
+
+    const int tid = threadIdx.x, w = tid >> 6;
+    const i64 base = (i64)blockIdx.x * kTile;
+    const i64 wbase = base + (i64)w * (64 * kItems) + (tid & 63);
+    const u32 global_start = a.tile_slots[(u64)blockIdx.x * kRadix + tid];
+    u32 key[kItems], val[kItems], rank[kItems];
+    load_tile<kSrc>(a, wbase, key, val);
+    wave_rank(key, wbase, a.n, a.shift, sm.count[w], rank);
     __syncthreads();
 
-    // Thread tid owns digit tid: tile total, per-wave prefixes, look-back.
+    // Thread tid owns digit tid: per-wave prefixes and the tile total.
     u32 agg = 0;
 #pragma unroll
     for (int v = 0; v < kWaves; ++v) {
@@ -348,25 +391,9 @@ __global__ __launch_bounds__(kBlock) void k_sweep(SweepArgs a) {
         sm.count[v][tid] = agg;
         agg += c;
     }
-    u64* mine = a.status + (u64)tile * kRadix + tid;
-    status_store(mine, (tile == 0 ? kFlagPrefix : kFlagAggregate) | agg);
     const u32 local_start = block_exclusive_scan(agg, s_wave);
-    u64 exclusive = 0;
-    if (tile > 0) {
-        for (i64 pred = (i64)tile - 1; pred >= 0; --pred) {
-            const u64* p = a.status + (u64)pred * kRadix + tid;
-            u64 v = status_load(p);
-            while ((v >> kFlagShift) == 0) {
-                __builtin_amdgcn_s_sleep(1);
-                v = status_load(p);
-            }
-            exclusive += v & kCountMask;
-            if ((v >> kFlagShift) == 2) break;
-        }
-        status_store(mine, kFlagPrefix | (exclusive + agg));
-    }
     s_local[tid] = local_start;
-    s_base[tid] = digit_start + (u32)exclusive - local_start;  // modular; base + slot < n
+    s_base[tid] = global_start - local_start;  // modular; base + slot < n
 
     u32 digit[kItems];
 #pragma unroll
@@ -439,22 +466,71 @@ __global__ __launch_bounds__(kBlock) void k_sweep(SweepArgs a) {
 // make_geometry(|S(c)|) and local node j on local level t is global node
 // (c+1)*2^t - 1 + (j - F(t)).
 
-constexpr int kLocalItems = 16;
-constexpr int kLocalMax = kBlock * kLocalItems;  // points per subtree
-constexpr int kCachedDims = 3;                   // sorted orders kept in LDS
+constexpr int kLocalBlock = 512;                      // threads per subtree workgroup
+constexpr int kLocalWaves = kLocalBlock / 64;
+constexpr int kLocalItems = 8;                        // records per thread
+constexpr int kLocalMax = kLocalBlock * kLocalItems;  // points per subtree
+constexpr int kCachedDims = 3;                        // sorted orders kept in LDS
+static_assert(kLocalBlock >= kRadix, "one thread per digit");
 
 struct LocalShared {
-    u64 exch[kLocalMax];            // record exchange of the radix passes
-    u32 count[kWaves][kRadix];      // per-wave digit counters, then prefixes
-    u32 start[kRadix];              // first slot of each digit
-    u32 wave[kWaves];
-    uint16_t tag[kLocalMax];        // local tag of each point (by index rank)
+    u64 exch[kLocalMax];                  // record exchange of the radix passes
+    u32 count[kLocalWaves][kRadix];       // per-wave digit counters, then prefixes
+    u32 start[kRadix];                    // first slot of each digit
+    u32 wave[kLocalWaves];
+    u64 reduce[2][kLocalWaves];           // AND / OR of the keys, per wave
+    uint16_t tag[kLocalMax];              // local tag of each point (by index rank)
     uint16_t order[kCachedDims][kLocalMax];  // points sorted by (coordinate, index)
 };
 
 // Slot of item j of this thread: each wave owns kLocalItems rows of 64.
 __device__ inline int local_slot(int j) {
     return (threadIdx.x >> 6) * (64 * kLocalItems) + j * 64 + (threadIdx.x & 63);
+}
+
+__device__ inline u32 local_exclusive_scan(u32 v, u32* s_wave) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    u32 inc = wave_inclusive_scan(v);
+    if (lane == 63) s_wave[w] = inc;
+    __syncthreads();
+    u32 off = 0;
+#pragma unroll
+    for (int i = 0; i < kLocalWaves; ++i)
+        if (i < w) off += s_wave[i];
+    __syncthreads();
+    return off + inc - v;
+}
+
+// Mask of key bits on which the records (all of the workgroup's valid
+// ones) disagree; a radix pass over a byte outside it would not move
+// anything and is skipped.
+__device__ u64 local_varying_bits(const u64 (&rec)[kLocalItems], u32 nc, LocalShared& sh) {
+    u64 all_and = ~0ull, all_or = 0;
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j)
+        if ((u32)local_slot(j) < nc) {
+            all_and &= rec[j];
+            all_or |= rec[j];
+        }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        all_and &= __shfl_xor(all_and, o, 64);
+        all_or |= __shfl_xor(all_or, o, 64);
+    }
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        sh.reduce[0][w] = all_and;
+        sh.reduce[1][w] = all_or;
+    }
+    __syncthreads();
+    u64 a = ~0ull, b = 0;
+#pragma unroll
+    for (int v = 0; v < kLocalWaves; ++v) {
+        a &= sh.reduce[0][v];
+        b |= sh.reduce[1][v];
+    }
+    __syncthreads();
+    return a ^ b;
 }
 
 // One stable pass over all kLocalMax records of the workgroup by the 8-bit
@@ -464,11 +540,12 @@ __device__ void local_pass(u64 (&rec)[kLocalItems], int shift, LocalShared& sh) 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     for (int i = lane; i < kRadix; i += 64) sh.count[w][i] = 0;
     const u64 below = (1ull << lane) - 1;
-    u32 rank[kLocalItems], dig[kLocalItems];
+    // Rank inside the wave: lanes holding the same digit are found with eight
+    // ballots; the lowest such lane bumps the wave's counter for the digit.
+    u32 rank[kLocalItems];
 #pragma unroll
     for (int j = 0; j < kLocalItems; ++j) {
         const u32 d = (u32)(rec[j] >> shift) & (kRadix - 1);
-        dig[j] = d;
         u64 peers = ~0ull;
 #pragma unroll
         for (int b = 0; b < kRadixBits; ++b) {
@@ -483,21 +560,45 @@ __device__ void local_pass(u64 (&rec)[kLocalItems], int shift, LocalShared& sh) 
     }
     __syncthreads();
     u32 agg = 0;
+    if (tid < kRadix) {
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
-        const u32 c = sh.count[v][tid];
-        sh.count[v][tid] = agg;
-        agg += c;
+        for (int v = 0; v < kLocalWaves; ++v) {
+            const u32 c = sh.count[v][tid];
+            sh.count[v][tid] = agg;
+            agg += c;
+        }
     }
-    sh.start[tid] = block_exclusive_scan(agg, sh.wave);
+    // Exclusive scan of the digit totals (threads >= kRadix contribute 0).
+    const u32 inc = wave_inclusive_scan(agg);
+    if (lane == 63) sh.wave[w] = inc;
+    __syncthreads();
+    if (tid < kRadix) {
+        u32 off = 0;
+#pragma unroll
+        for (int i = 0; i < kLocalWaves; ++i)
+            if (i < w) off += sh.wave[i];
+        sh.start[tid] = off + inc - agg;
+    }
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < kLocalItems; ++j)
-        sh.exch[sh.start[dig[j]] + sh.count[w][dig[j]] + rank[j]] = rec[j];
+    for (int j = 0; j < kLocalItems; ++j) {
+        const u32 d = (u32)(rec[j] >> shift) & (kRadix - 1);
+        sh.exch[sh.start[d] + sh.count[w][d] + rank[j]] = rec[j];
+    }
     __syncthreads();
+    // The next pass's first barrier orders these reads before its writes.
 #pragma unroll
     for (int j = 0; j < kLocalItems; ++j) rec[j] = sh.exch[local_slot(j)];
-    __syncthreads();
+}
+
+// Stable sort of the records by bits [lo, lo + 8*bytes), skipping bytes on
+// which every valid record agrees.
+__device__ void local_sort(u64 (&rec)[kLocalItems], int lo, int bytes, u32 nc, LocalShared& sh) {
+    const u64 vary = local_varying_bits(rec, nc, sh);
+    for (int b = 0; b < bytes; ++b) {
+        const int shift = lo + 8 * b;
+        if ((vary >> shift) & (kRadix - 1)) local_pass(rec, shift, sh);
+    }
 }
 
 struct SubtreeArgs {
@@ -507,7 +608,7 @@ struct SubtreeArgs {
     int l0;                 // level of the subtree roots
     Geometry geo;
     const u32* sorted;      // point indices in the sorted order of round l0-1 (l0 > 0)
-    int index_passes;       // radix passes to order a subtree's point indices
+    int index_bytes;        // bytes of a point index that can differ
     int32_t* perm;
     float* tree;
 };
@@ -527,7 +628,7 @@ __device__ void local_order(const SubtreeArgs& a, const u32 (&idx)[kLocalItems],
             rec[j] = ((u64)float_key(x) << 16) | (u32)e;
         }
     }
-    for (int p = 0; p < 4; ++p) local_pass(rec, 16 + 8 * p, sh);
+    local_sort(rec, 16, kKeyBytes, nc, sh);
 #pragma unroll
     for (int j = 0; j < kLocalItems; ++j) {
         const int q = local_slot(j);
@@ -536,7 +637,7 @@ __device__ void local_order(const SubtreeArgs& a, const u32 (&idx)[kLocalItems],
     __syncthreads();
 }
 
-__global__ __launch_bounds__(kBlock) void k_subtree(SubtreeArgs a) {
+__global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
     __shared__ LocalShared sh;
 
     const u64 c = full_nodes(a.l0) + blockIdx.x;  // subtree root (global node id)
@@ -561,7 +662,7 @@ __global__ __launch_bounds__(kBlock) void k_subtree(SubtreeArgs a) {
             rec[j] = ((u64)i << 16) | (u32)q;
         }
     }
-    for (int p = 0; p < a.index_passes; ++p) local_pass(rec, 16 + 8 * p, sh);
+    if (a.sorted) local_sort(rec, 16, a.index_bytes, nc, sh);
     u32 idx[kLocalItems];
 #pragma unroll
     for (int j = 0; j < kLocalItems; ++j) {
@@ -657,9 +758,9 @@ inline size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 struct Layout {
     int kcols;          // split dimensions the global rounds can use
     i64 tiles;
-    size_t cols, orders, tag, keys0, keys1, vals0, vals1, small, status, total;
-    // inside `small` (u32 words): column histograms, tag histograms, ticket
-    int col_hist_words, tag_hist_off, ticket_off, small_words;
+    size_t cols, orders, tag, keys0, keys1, vals0, vals1, small, slots, total;
+    // inside `small` (u32 words): column histograms, tag histograms
+    int col_hist_words, tag_hist_off, small_words;
 };
 
 bool make_layout(i64 n, int k, Layout* out) {
@@ -674,8 +775,7 @@ bool make_layout(i64 n, int k, Layout* out) {
     lay.tiles = (n + kTile - 1) / kTile;
     lay.col_hist_words = lay.kcols * kKeyBytes * kRadix;
     lay.tag_hist_off = lay.col_hist_words;
-    lay.ticket_off = lay.tag_hist_off + kMaxTagPasses * kRadix;
-    lay.small_words = lay.ticket_off + kTicketWords;
+    lay.small_words = lay.tag_hist_off + kMaxTagPasses * kRadix;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t at = off;
@@ -690,7 +790,7 @@ bool make_layout(i64 n, int k, Layout* out) {
     lay.vals0 = take((size_t)n * sizeof(u32));
     lay.vals1 = take((size_t)n * sizeof(u32));
     lay.small = take((size_t)lay.small_words * sizeof(u32));
-    lay.status = take(2 * (size_t)lay.tiles * kRadix * sizeof(u64));
+    lay.slots = take((size_t)lay.tiles * kRadix * sizeof(u32));
     lay.total = off;
     *out = lay;
     return true;
@@ -734,15 +834,15 @@ struct Profiler {
         r.bytes = bytes;
         if (hipEventCreate(&r.start) != hipSuccess) { failed = true; return; }
         if (hipEventCreate(&r.stop) != hipSuccess) {
-            hipEventDestroy(r.start);
+            (void)hipEventDestroy(r.start);
             failed = true;
             return;
         }
-        hipEventRecord(r.start, stream);
+        if (hipEventRecord(r.start, stream) != hipSuccess) failed = true;
     }
     void end() {
         if (failed) return;
-        hipEventRecord(recs[count].stop, stream);
+        if (hipEventRecord(recs[count].stop, stream) != hipSuccess) failed = true;
         ++count;
     }
 };
@@ -753,25 +853,29 @@ struct Timer {  // no-op unless a Profiler is attached
     void end() { if (p) p->end(); }
 };
 
-// Launches one radix pass; keeps the look-back word and ticket bookkeeping.
-struct SweepLauncher {
+// Launches the three kernels of one radix pass.
+struct PassLauncher {
     const Layout& lay;
-    u64* status;
-    u32* ticket;
+    u32* slots;
     hipStream_t stream;
     Timer timer;
-    int pass_index = 0;
 
     template <int kSrc, int kSink>
-    void run(SweepArgs a, int kind, double bytes) {
-        const i64 words = lay.tiles * kRadix;
-        a.status = status + (size_t)(pass_index & 1) * words;
-        a.status_next = status + (size_t)((pass_index + 1) & 1) * words;
-        a.ticket = ticket;
-        a.ticket_base = (u32)((u64)pass_index * (u64)lay.tiles);
-        ++pass_index;
+    void run(PassArgs a, int kind, double bytes) {
+        a.tile_slots = slots;
+        const unsigned tiles = (unsigned)lay.tiles;
         timer.begin(kind, bytes);
-        k_sweep<kSrc, kSink><<<(unsigned)lay.tiles, kBlock, 0, stream>>>(a);
+        k_tile_count<kSrc><<<tiles, kBlock, 0, stream>>>(a);
+        k_tile_scan<<<kRadix, kBlock, 0, stream>>>(a.digit_hist, slots, lay.tiles);
+        if (kSrc == kSrcGather) {  // the count kernel wrote the gathered records
+            a.keys_in = a.keys_out;
+            a.vals_in = a.vals_out;
+            a.keys_out = a.scatter_keys;
+            a.vals_out = a.scatter_vals;
+            k_tile_scatter<kSrcArrays, kSink><<<tiles, kBlock, 0, stream>>>(a);
+        } else {
+            k_tile_scatter<kSrc, kSink><<<tiles, kBlock, 0, stream>>>(a);
+        }
         timer.end();
     }
 };
@@ -793,16 +897,16 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
     u32* small = (u32*)(ws + lay.small);
     u32* col_hist = small;
     u32* tag_hist = small + lay.tag_hist_off;
-    u64* status = (u64*)(ws + lay.status);
-    SweepLauncher sweep{lay, status, small + lay.ticket_off, stream, timer};
+    PassLauncher pass{lay, (u32*)(ws + lay.slots), stream, timer};
     const double N = (double)n;
 
     timer.begin(kKindInit, N * kc * 8);
-    k_init<<<grid_for(n, kBlock * 4, 8192), kBlock, 0, stream>>>(
-        pts, n, k, kc, cols, status, lay.tiles * kRadix, small, lay.small_words);
+    k_init<<<grid_for(n, kBlock * 4, 8192), kBlock, 0, stream>>>(pts, n, k, kc, cols, small,
+                                                                lay.small_words);
     timer.end();
 
-    // Presort: order_d = point indices by (coordinate d, index).
+    // Presort: order_d = point indices by (coordinate d, index). Pass p
+    // reads buffer (p+1)&1 and writes buffer p&1; the last writes order_d.
     for (int d = 0; d < kc; ++d) {
         const float* col = cols + (size_t)d * n;
         u32* hist = col_hist + (size_t)d * kKeyBytes * kRadix;
@@ -810,7 +914,7 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
         k_col_hist<<<grid_for(n, kBlock * 16, 2048), kBlock, 0, stream>>>(col, n, hist);
         timer.end();
         for (int p = 0; p < kKeyBytes; ++p) {
-            SweepArgs a{};
+            PassArgs a{};
             a.n = n;
             a.shift = 8 * p;
             a.col = col;
@@ -820,11 +924,11 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
             a.vals_out = p == kKeyBytes - 1 ? orders + (size_t)d * n : vals[p & 1];
             a.digit_hist = hist + p * kRadix;
             if (p == 0)
-                sweep.run<kSrcColumn, kSinkArrays>(a, kKindPresort, N * 12);
+                pass.run<kSrcColumn, kSinkArrays>(a, kKindPresort, N * 12);
             else if (p < kKeyBytes - 1)
-                sweep.run<kSrcArrays, kSinkArrays>(a, kKindPresort, N * 16);
+                pass.run<kSrcArrays, kSinkArrays>(a, kKindPresort, N * 16);
             else
-                sweep.run<kSrcArrays, kSinkVals>(a, kKindPresort, N * 12);
+                pass.run<kSrcArrays, kSinkVals>(a, kKindPresort, N * 12);
         }
     }
 
@@ -837,6 +941,9 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
         timer.end();
     }
 
+    // Round l: stable sort of order_{l mod k} by tag, one pass per tag byte.
+    // Pass 0 gathers each point's tag into buffer 0; pass p writes buffer
+    // (p+1)&1 and the next pass reads it.
     for (int l = 1; l < rounds; ++l) {
         const int d = l % k;
         const int passes = tag_passes(l);
@@ -845,30 +952,41 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
         k_tag_hist<<<1, kBlock, 0, stream>>>(geo, l, passes, tag_hist);
         timer.end();
         for (int p = 0; p < passes; ++p) {
-            SweepArgs a{};
+            PassArgs a{};
             a.n = n;
             a.shift = 8 * p;
             a.gather = tag;
-            a.keys_in = keys[(p + 1) & 1];
-            a.vals_in = p == 0 ? orders + (size_t)d * n : vals[(p + 1) & 1];
-            a.keys_out = keys[p & 1];
-            a.vals_out = vals[p & 1];
             a.tag_out = tag;
             a.digit_hist = tag_hist + p * kRadix;
             a.geo = geo;
             a.round = l;
-            const bool last = p == passes - 1;
-            const double in = p == 0 ? N * 8 : N * 8;  // list + gathered tag, or records
-            if (!last) {
-                if (p == 0) sweep.run<kSrcGather, kSinkArrays>(a, kKindTagPass, in + N * 8);
-                else sweep.run<kSrcArrays, kSinkArrays>(a, kKindTagPass, in + N * 8);
-            } else if (final) {
-                *sorted_out = vals[p & 1];
-                if (p == 0) sweep.run<kSrcGather, kSinkVals>(a, kKindFinal, in + N * 4);
-                else sweep.run<kSrcArrays, kSinkVals>(a, kKindFinal, in + N * 4);
+            u32* out_keys = keys[(p + 1) & 1];
+            u32* out_vals = vals[(p + 1) & 1];
+            if (p == 0) {
+                a.vals_in = orders + (size_t)d * n;
+                a.keys_out = keys[0];  // gathered (tag, index) records
+                a.vals_out = vals[0];
+                a.scatter_keys = out_keys;
+                a.scatter_vals = out_vals;
             } else {
-                if (p == 0) sweep.run<kSrcGather, kSinkTags>(a, kKindUpdate, in + N * 4);
-                else sweep.run<kSrcArrays, kSinkTags>(a, kKindUpdate, in + N * 4);
+                a.keys_in = keys[p & 1];
+                a.vals_in = vals[p & 1];
+                a.keys_out = out_keys;
+                a.vals_out = out_vals;
+            }
+            const bool last = p == passes - 1;
+            // list + gathered tag + records written and read back, or records
+            const double in = p == 0 ? N * 24 : N * 8;
+            if (!last) {
+                if (p == 0) pass.run<kSrcGather, kSinkArrays>(a, kKindTagPass, in + N * 8);
+                else pass.run<kSrcArrays, kSinkArrays>(a, kKindTagPass, in + N * 8);
+            } else if (final) {
+                *sorted_out = out_vals;
+                if (p == 0) pass.run<kSrcGather, kSinkVals>(a, kKindFinal, in + N * 4);
+                else pass.run<kSrcArrays, kSinkVals>(a, kKindFinal, in + N * 4);
+            } else {
+                if (p == 0) pass.run<kSrcGather, kSinkTags>(a, kKindUpdate, in + N * 4);
+                else pass.run<kSrcArrays, kSinkTags>(a, kKindUpdate, in + N * 4);
             }
         }
     }
@@ -935,12 +1053,12 @@ kdt_status build_impl(const float* points, int64_t N, int32_t k, int32_t* perm_o
     sa.sorted = sorted;
     int bits = 0;
     for (u64 v = (u64)(N - 1); v; v >>= 1) ++bits;
-    sa.index_passes = l0 > 0 ? (bits + kRadixBits - 1) / kRadixBits : 0;
+    sa.index_bytes = (bits + kRadixBits - 1) / kRadixBits;
     sa.perm = perm_out;
     sa.tree = tree_out;
     const i64 below = N - (i64)full_nodes(l0);  // points in the level-l0 subtrees
     timer.begin(kKindSubtree, (double)below * ((l0 > 0 ? 4 : 0) + 4 + (tree_out ? 8.0 * k : 4.0 * k)));
-    k_subtree<<<(unsigned)(1ull << l0), kBlock, 0, stream>>>(sa);
+    k_subtree<<<(unsigned)(1ull << l0), kLocalBlock, 0, stream>>>(sa);
     timer.end();
     return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
 }
@@ -985,8 +1103,8 @@ kdt_status kdt_build_profiled(const float* points, int64_t N, int32_t k, int32_t
         profile->bytes[r.kind] += r.bytes;
     }
     for (int i = 0; i < prof->count; ++i) {
-        hipEventDestroy(prof->recs[i].start);
-        hipEventDestroy(prof->recs[i].stop);
+        (void)hipEventDestroy(prof->recs[i].start);
+        (void)hipEventDestroy(prof->recs[i].stop);
     }
     if (prof->failed && st == KDT_OK) st = KDT_ERR_HIP;
     delete prof;
