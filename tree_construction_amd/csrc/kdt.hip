@@ -16,23 +16,28 @@
 //   k_init       AoS points -> one column per split dimension; clears the
 //                radix bookkeeping.
 //   k_col_hist   byte histograms of each column's order-preserving keys.
-//   k_sweep x4   per dimension: stable sort of (key(x_d), index) -> order_d.
+//   4 passes     per dimension: stable sort of (key(x_d), index) -> order_d
+//                (the points by coordinate d, then index).
+//   k_invert     rank_d[order_d[r]] = r.
+//   k_cross      next_d[r] = position in order_{d+1} of the r-th point of
+//                order_d (all writes; no random reads).
 //   k_round0     round 0 (all tags 0): tags straight from order_0.
-//   per round l = 1 .. l0-1:
+//   per round l = 1 .. l0-1, d = l mod k:
 //     k_tag_hist tag-digit histograms, from the closed-form subtree sizes.
-//     k_sweep    1-2 passes by tag over order_{l mod k} (the first gathers
-//                each point's tag); the last one updates the tags, or, in
-//                round l0-1, writes the sorted order for the next stage.
+//     1-2 passes stable sort by tag of the records (tag, next_d) kept in
+//                order_d order; the last one computes each point's new tag
+//                and writes it where round l+1 reads it (tags are kept in
+//                the order of the dimension that reads them), or, in round
+//                l0-1, writes the sorted point indices for the next stage.
 //   k_place_top  nodes above level l0.
 //   k_subtree    one workgroup per level-l0 subtree (<= 4096 points) runs
 //                that subtree's remaining rounds in LDS and writes its
 //                level-order output.
 //
-// A radix pass is a one-sweep design: per-tile digit counts from wave64
-// ballots (multi-split ranking), cross-tile offsets by decoupled look-back
-// over agent-scope atomics (Merrill & Garland's single-pass prefix scan),
-// digit bases from a histogram, and an LDS-staged scatter so that the global
-// writes of one digit are contiguous.
+// A radix pass is reduce-then-scan: per-tile digit counts from wave64
+// ballots (multi-split ranking), a scan over tiles per digit, and a scatter
+// that re-ranks each tile and stages it in LDS so that the global writes of
+// one digit are contiguous. No workgroup ever waits on another.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -217,19 +222,53 @@ __global__ __launch_bounds__(kBlock) void k_tag_hist(Geometry geo, int l, int pa
     for (int i = threadIdx.x; i < passes * kRadix; i += kBlock) hist[i] = (&h[0][0])[i];
 }
 
-// Round 0: every tag is 0, so the sorted order is order_0 itself and the
-// pivot sits at position |S(1)|.
-__global__ __launch_bounds__(kBlock) void k_round0(const u32* __restrict__ order, Geometry geo,
-                                                   u32* __restrict__ tag) {
-    const u64 pivot = subtree_size(geo, 1);
+// rank[order[r]] = r: where each point sits in order_d.
+__global__ __launch_bounds__(kBlock) void k_invert(const u32* __restrict__ order, i64 n,
+                                                   u32* __restrict__ rank) {
     const i64 stride = (i64)gridDim.x * kBlock;
-    for (i64 r = (i64)blockIdx.x * kBlock + threadIdx.x; r < geo.n; r += stride) {
+    for (i64 r = (i64)blockIdx.x * kBlock + threadIdx.x; r < n; r += stride) {
         const u32 i = order[r];
-        if (i < (u64)geo.n) tag[i] = (u64)r < pivot ? 1u : ((u64)r > pivot ? 2u : 0u);
+        if (i < (u64)n) rank[i] = (u32)r;
     }
 }
 
-enum Src { kSrcColumn = 0, kSrcArrays = 1, kSrcGather = 2 };
+// next[rank_d[i]] = rank_e[i]: for the r-th point of order_d, its position
+// in order_e. Reads both ranks in index order, writes scattered.
+__global__ __launch_bounds__(kBlock) void k_cross(const u32* __restrict__ rank_d,
+                                                  const u32* __restrict__ rank_e, i64 n,
+                                                  u32* __restrict__ next) {
+    const i64 stride = (i64)gridDim.x * kBlock;
+    for (i64 i = (i64)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride) {
+        const u32 r = rank_d[i];
+        if (r < (u64)n) next[r] = rank_e[i];
+    }
+}
+
+// Round 0: every tag is 0, so the sorted order is order_0 itself and the
+// pivot sits at position |S(1)|. Writes each point's new tag at its
+// position in the order round 1 reads.
+__global__ __launch_bounds__(kBlock) void k_round0(const u32* __restrict__ next, Geometry geo,
+                                                   u32* __restrict__ tag_next) {
+    const u64 pivot = subtree_size(geo, 1);
+    const i64 stride = (i64)gridDim.x * kBlock;
+    for (i64 r = (i64)blockIdx.x * kBlock + threadIdx.x; r < geo.n; r += stride) {
+        const u32 q = next[r];
+        if (q < (u64)geo.n) tag_next[q] = (u64)r < pivot ? 1u : ((u64)r > pivot ? 2u : 0u);
+    }
+}
+
+// Tags after some rounds, back in original index order (diagnostics only).
+__global__ __launch_bounds__(kBlock) void k_unpermute(const u32* __restrict__ tagq,
+                                                      const u32* __restrict__ order, i64 n,
+                                                      u32* __restrict__ out) {
+    const i64 stride = (i64)gridDim.x * kBlock;
+    for (i64 r = (i64)blockIdx.x * kBlock + threadIdx.x; r < n; r += stride) {
+        const u32 i = order[r];
+        if (i < (u64)n) out[i] = tagq ? tagq[r] : 0u;
+    }
+}
+
+enum Src { kSrcColumn = 0, kSrcArrays = 1 };
 enum Sink { kSinkArrays = 0, kSinkVals = 1, kSinkTags = 2 };
 
 // One stable radix pass over n (key, val) records is three launches
@@ -243,15 +282,12 @@ struct PassArgs {
     int shift;                 // digit = (key >> shift) & 255
     const float* col;          // kSrcColumn: key = key(col[i]), val = i
     const u32* keys_in;        // kSrcArrays
-    const u32* vals_in;        // kSrcArrays; kSrcGather: the list of point indices
-    const u32* gather;         // kSrcGather: key = gather[val] (the point's tag)
-    u32* keys_out;             // scatter: kSinkArrays; count with kSrcGather: the
-    u32* vals_out;             //   gathered records, in list order; kSinkVals
-    u32* tag_out;              // kSinkTags
+    const u32* vals_in;        // kSrcArrays
+    u32* keys_out;             // kSinkArrays
+    u32* vals_out;             // kSinkArrays, kSinkVals
+    u32* tag_out;              // kSinkTags: tag_out[val] = the record's new tag
     const u32* digit_hist;     // 256 counts of this pass's digit over all records
     u32* tile_slots;           // tiles x 256: counts, then first global slots
-    u32* scatter_keys;         // kSrcGather: where the scatter writes (keys_out/vals_out
-    u32* scatter_vals;         //   then hold the gathered records)
     Geometry geo;              // kSinkTags
     int round;                 // kSinkTags
 };
@@ -271,15 +307,10 @@ __device__ inline void load_tile(const PassArgs& a, i64 wbase, u32 (&key)[kItems
                 key[j] = float_key(__float_as_uint(a.col[e]));
                 val[j] = (u32)e;
             } else {
+                key[j] = a.keys_in[e];
                 val[j] = a.vals_in[e];
-                if (kSrc == kSrcArrays) key[j] = a.keys_in[e];
             }
         }
-    }
-    if (kSrc == kSrcGather) {
-#pragma unroll
-        for (int j = 0; j < kItems; ++j)
-            if (wbase + (i64)j * 64 < a.n && val[j] < (u64)a.n) key[j] = a.gather[val[j]];
     }
 }
 
@@ -318,16 +349,6 @@ __global__ __launch_bounds__(kBlock) void k_tile_count(PassArgs a) {
     const i64 wbase = base + (i64)w * (64 * kItems) + (tid & 63);
     u32 key[kItems], val[kItems], rank[kItems];
     load_tile<kSrc>(a, wbase, key, val);
-    if (kSrc == kSrcGather) {
-#pragma unroll
-        for (int j = 0; j < kItems; ++j) {
-            const i64 e = wbase + (i64)j * 64;
-            if (e < a.n) {
-                a.keys_out[e] = key[j];
-                a.vals_out[e] = val[j];
-            }
-        }
-    }
     wave_rank(key, wbase, a.n, a.shift, count[w], rank);
     __syncthreads();
     u32 total = 0;
@@ -408,16 +429,19 @@ __global__ __launch_bounds__(kBlock) void k_tile_scatter(PassArgs a) {
         // s (s on level l, so s >= F(l)) at sorted position p moves to the
         // left child if p is before the pivot, to the right child if after,
         // and stays as node s if it is the pivot; pivot = start of s's
-        // segment + size of the left subtree. Tags < F(l) are final.
+        // segment + size of the left subtree. Tags < F(l) are final and are
+        // carried over unchanged.
         const u64 fl = full_nodes(a.round);
 #pragma unroll
         for (int j = 0; j < kItems; ++j) {
             if ((wbase + (i64)j * 64) >= a.n) continue;
             const u64 s = key[j];
-            if (s < fl) continue;
-            const u64 p = (u64)(s_base[digit[j]] + s_local[digit[j]] + rank[j]);
-            const u64 pivot = segment_begin(a.geo, s, a.round) + subtree_size(a.geo, 2 * s + 1);
-            const u64 t = p < pivot ? 2 * s + 1 : (p > pivot ? 2 * s + 2 : s);
+            u64 t = s;
+            if (s >= fl) {
+                const u64 p = (u64)(s_base[digit[j]] + s_local[digit[j]] + rank[j]);
+                const u64 pivot = segment_begin(a.geo, s, a.round) + subtree_size(a.geo, 2 * s + 1);
+                t = p < pivot ? 2 * s + 1 : (p > pivot ? 2 * s + 2 : s);
+            }
             if (val[j] < (u64)a.n) a.tag_out[val[j]] = (u32)t;
         }
         return;
@@ -609,6 +633,8 @@ struct SubtreeArgs {
     Geometry geo;
     const u32* sorted;      // point indices in the sorted order of round l0-1 (l0 > 0)
     int index_bytes;        // bytes of a point index that can differ
+    u32* stage;             // (k+1) x n words: index, then coordinate columns; the
+                            // subtree owns [first, first + |S(c)|) of each
     int32_t* perm;
     float* tree;
 };
@@ -616,17 +642,14 @@ struct SubtreeArgs {
 // order[q] = slot (index rank) of the q-th point of the subtree by
 // (coordinate dim, original index): stable sort by the coordinate key,
 // starting from index order.
-__device__ void local_order(const SubtreeArgs& a, const u32 (&idx)[kLocalItems], u32 nc, int dim,
-                            uint16_t* order, LocalShared& sh) {
+__device__ void local_order(const u32* __restrict__ col, u32 nc, uint16_t* order,
+                            LocalShared& sh) {
     u64 rec[kLocalItems];
 #pragma unroll
     for (int j = 0; j < kLocalItems; ++j) {
         const int e = local_slot(j);
         rec[j] = ~0ull;
-        if ((u32)e < nc) {
-            const u32 x = __float_as_uint(a.pts[(i64)idx[j] * a.k + dim]);
-            rec[j] = ((u64)float_key(x) << 16) | (u32)e;
-        }
+        if ((u32)e < nc) rec[j] = ((u64)float_key(col[e]) << 16) | (u32)e;
     }
     local_sort(rec, 16, kKeyBytes, nc, sh);
 #pragma unroll
@@ -663,24 +686,33 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
         }
     }
     if (a.sorted) local_sort(rec, 16, a.index_bytes, nc, sh);
-    u32 idx[kLocalItems];
+    // Stage the subtree's points once, by index rank: their indices and their
+    // coordinate columns (each row of `points` is read exactly once here).
+    u32* stage_idx = a.stage + first;
 #pragma unroll
     for (int j = 0; j < kLocalItems; ++j) {
-        idx[j] = (u32)(rec[j] >> 16);
-        if ((u32)local_slot(j) < nc) sh.tag[local_slot(j)] = 0;
+        const int e = local_slot(j);
+        if ((u32)e >= nc) continue;
+        const u32 i = (u32)(rec[j] >> 16);
+        stage_idx[e] = i;
+        const float* row = a.pts + (i64)i * a.k;
+        for (int d = 0; d < a.k; ++d)
+            a.stage[(u64)(d + 1) * a.n + first + e] = __float_as_uint(row[d]);
+        sh.tag[e] = 0;
     }
+    auto column = [&](int d) { return a.stage + (u64)(d + 1) * a.n + first; };
 
     const Geometry lg = make_geometry((i64)nc);
     const int rounds = lg.levels - 1;
     const bool cached = a.k <= kCachedDims;
     if (cached)
         for (int u = 0; u < a.k && u < rounds; ++u)
-            local_order(a, idx, nc, (a.l0 + u) % a.k, sh.order[u], sh);
+            local_order(column((a.l0 + u) % a.k), nc, sh.order[u], sh);
     __syncthreads();
 
     for (int t = 0; t < rounds; ++t) {
         uint16_t* order = sh.order[cached ? t % a.k : 0];
-        if (!cached) local_order(a, idx, nc, (a.l0 + t) % a.k, order, sh);
+        if (!cached) local_order(column((a.l0 + t) % a.k), nc, order, sh);
         // Sort the points of every segment by (tag, coordinate, index): a
         // stable sort by tag of the (coordinate, index) order.
 #pragma unroll
@@ -709,19 +741,34 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
         __syncthreads();
     }
 
-    // Level-order output of the subtree.
+    // Level-order output of the subtree, in node order: the nodes of each
+    // local level are one contiguous range of global ids, so the writes of
+    // consecutive threads are contiguous.
+    uint16_t* slot_of = sh.order[0];  // the orders are no longer needed
 #pragma unroll
     for (int j = 0; j < kLocalItems; ++j) {
         const int e = local_slot(j);
-        if ((u32)e >= nc) continue;
-        const u64 node = sh.tag[e];
+        if ((u32)e < nc) slot_of[sh.tag[e]] = (uint16_t)e;
+    }
+    __syncthreads();
+    for (u32 node = threadIdx.x; node < nc; node += kLocalBlock) {
+        const u32 e = slot_of[node];
         const int lvl = level_of(node);
         const u64 g = ((c + 1) << lvl) - 1 + (node - full_nodes(lvl));
         if (g >= (u64)a.n) continue;  // cannot happen: local nodes map inside the tree
-        a.perm[g] = (int32_t)idx[j];
+        a.perm[g] = (int32_t)stage_idx[e];
         if (a.tree)
-            for (int d = 0; d < a.k; ++d) a.tree[(i64)g * a.k + d] = a.pts[(i64)idx[j] * a.k + d];
+            for (int d = 0; d < a.k; ++d)
+                a.tree[(i64)g * a.k + d] = __uint_as_float(a.stage[(u64)(d + 1) * a.n + first + e]);
     }
+}
+
+// A single point is the whole tree (no workspace is needed for N = 1).
+__global__ void k_single(const float* __restrict__ pts, int k, int32_t* __restrict__ perm,
+                         float* __restrict__ tree) {
+    if (threadIdx.x == 0) perm[0] = 0;
+    if (tree)
+        for (int d = threadIdx.x; d < k; d += blockDim.x) tree[d] = pts[d];
 }
 
 // Nodes above level l0: the F(l0-1) nodes fixed before round l0-1 sit at
@@ -758,7 +805,7 @@ inline size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 struct Layout {
     int kcols;          // split dimensions the global rounds can use
     i64 tiles;
-    size_t cols, orders, tag, keys0, keys1, vals0, vals1, small, slots, total;
+    size_t cols, orders, ranks, next, tagq, keys0, keys1, vals0, vals1, small, slots, stage, total;
     // inside `small` (u32 words): column histograms, tag histograms
     int col_hist_words, tag_hist_off, small_words;
 };
@@ -770,8 +817,10 @@ bool make_layout(i64 n, int k, Layout* out) {
         *out = lay;
         return true;
     }
-    const int rounds = make_geometry(n).levels - 1;
-    lay.kcols = rounds < k ? rounds : k;
+    const int levels = make_geometry(n).levels;
+    // dimensions the global rounds touch: the split dimensions of rounds
+    // 0 .. L-2 plus the one whose order the last written tags are kept in
+    lay.kcols = levels < k ? levels : k;
     lay.tiles = (n + kTile - 1) / kTile;
     lay.col_hist_words = lay.kcols * kKeyBytes * kRadix;
     lay.tag_hist_off = lay.col_hist_words;
@@ -784,13 +833,16 @@ bool make_layout(i64 n, int k, Layout* out) {
     };
     lay.cols = take((size_t)lay.kcols * n * sizeof(float));
     lay.orders = take((size_t)lay.kcols * n * sizeof(u32));
-    lay.tag = take((size_t)n * sizeof(u32));
+    lay.ranks = take((size_t)lay.kcols * n * sizeof(u32));
+    lay.next = take((size_t)lay.kcols * n * sizeof(u32));
+    lay.tagq = take((size_t)lay.kcols * n * sizeof(u32));
     lay.keys0 = take((size_t)n * sizeof(u32));
     lay.keys1 = take((size_t)n * sizeof(u32));
     lay.vals0 = take((size_t)n * sizeof(u32));
     lay.vals1 = take((size_t)n * sizeof(u32));
     lay.small = take((size_t)lay.small_words * sizeof(u32));
     lay.slots = take((size_t)lay.tiles * kRadix * sizeof(u32));
+    lay.stage = take((size_t)(k + 1) * n * sizeof(u32));
     lay.total = off;
     *out = lay;
     return true;
@@ -810,10 +862,11 @@ bool ranges_overlap(const void* a, size_t an, const void* b, size_t bn) {
 }
 
 // Optional per-kernel timing: an event pair around every launch.
-enum Kind { kKindInit, kKindHist, kKindPresort, kKindTagPass, kKindUpdate, kKindFinal,
-            kKindPlace, kKindSubtree, kKinds };
-const char* const kKindNames[kKinds] = {"init", "hist", "presort", "tag_pass", "tag_update",
-                                        "final_pass", "place_top", "subtree"};
+enum Kind { kKindInit, kKindHist, kKindPresort, kKindMaps, kKindTagPass, kKindUpdate, kKindFinal,
+            kKindSubtree, kKinds };
+const char* const kKindNames[kKinds] = {"init", "hist", "presort", "maps", "tag_pass",
+                                        "tag_update", "final_pass", "subtree"};
+constexpr int kKindPlace = kKindSubtree;  // placement of the top nodes counts with the subtrees
 static_assert(kKinds <= KDT_PROFILE_MAX_KINDS, "profile kinds");
 
 struct Profiler {
@@ -867,42 +920,41 @@ struct PassLauncher {
         timer.begin(kind, bytes);
         k_tile_count<kSrc><<<tiles, kBlock, 0, stream>>>(a);
         k_tile_scan<<<kRadix, kBlock, 0, stream>>>(a.digit_hist, slots, lay.tiles);
-        if (kSrc == kSrcGather) {  // the count kernel wrote the gathered records
-            a.keys_in = a.keys_out;
-            a.vals_in = a.vals_out;
-            a.keys_out = a.scatter_keys;
-            a.vals_out = a.scatter_vals;
-            k_tile_scatter<kSrcArrays, kSink><<<tiles, kBlock, 0, stream>>>(a);
-        } else {
-            k_tile_scatter<kSrc, kSink><<<tiles, kBlock, 0, stream>>>(a);
-        }
+        k_tile_scatter<kSrc, kSink><<<tiles, kBlock, 0, stream>>>(a);
         timer.end();
     }
 };
 
 // Runs rounds 0 .. rounds-1 on the whole point set. With keep_sorted the
 // last round writes its sorted order (point indices, returned in
-// *sorted_out) instead of updating the tags; otherwise the tags after
-// `rounds` rounds are left in the workspace's tag array.
+// *sorted_out) instead of updating the tags. Otherwise the tags after
+// `rounds` rounds are left in tagq of dimension rounds mod k, in that
+// dimension's (coordinate, index) order, which *tags_dim returns.
 kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, const Layout& lay,
                       hipStream_t stream, Timer timer, bool keep_sorted,
-                      const u32** sorted_out) {
+                      const u32** sorted_out, int* tags_dim) {
     const Geometry geo = make_geometry(n);
-    const int kc = rounds < k ? rounds : k;  // dimensions these rounds split on
+    const int writes = keep_sorted ? rounds - 1 : rounds;  // rounds that write tags
+    // dimensions touched: split dimensions of rounds 0 .. rounds-1 and the
+    // one each written round hands its tags to
+    const int span = writes + 1 > rounds ? writes + 1 : rounds;
+    const int kc = span < k ? span : k;
     float* cols = (float*)(ws + lay.cols);
-    u32* orders = (u32*)(ws + lay.orders);
-    u32* tag = (u32*)(ws + lay.tag);
-    u32* keys[2] = {(u32*)(ws + lay.keys0), (u32*)(ws + lay.keys1)};
-    u32* vals[2] = {(u32*)(ws + lay.vals0), (u32*)(ws + lay.vals1)};
     u32* small = (u32*)(ws + lay.small);
     u32* col_hist = small;
     u32* tag_hist = small + lay.tag_hist_off;
+    u32* keys[2] = {(u32*)(ws + lay.keys0), (u32*)(ws + lay.keys1)};
+    u32* vals[2] = {(u32*)(ws + lay.vals0), (u32*)(ws + lay.vals1)};
+    auto order = [&](int d) { return (u32*)(ws + lay.orders) + (size_t)d * n; };
+    auto rank = [&](int d) { return (u32*)(ws + lay.ranks) + (size_t)d * n; };
+    auto next = [&](int d) { return (u32*)(ws + lay.next) + (size_t)d * n; };
+    auto tagq = [&](int d) { return (u32*)(ws + lay.tagq) + (size_t)d * n; };
     PassLauncher pass{lay, (u32*)(ws + lay.slots), stream, timer};
     const double N = (double)n;
+    const int grid = grid_for(n, kBlock * 4, 8192);
 
     timer.begin(kKindInit, N * kc * 8);
-    k_init<<<grid_for(n, kBlock * 4, 8192), kBlock, 0, stream>>>(pts, n, k, kc, cols, small,
-                                                                lay.small_words);
+    k_init<<<grid, kBlock, 0, stream>>>(pts, n, k, kc, cols, small, lay.small_words);
     timer.end();
 
     // Presort: order_d = point indices by (coordinate d, index). Pass p
@@ -921,7 +973,7 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
             a.keys_in = keys[(p + 1) & 1];
             a.vals_in = vals[(p + 1) & 1];
             a.keys_out = keys[p & 1];
-            a.vals_out = p == kKeyBytes - 1 ? orders + (size_t)d * n : vals[p & 1];
+            a.vals_out = p == kKeyBytes - 1 ? order(d) : vals[p & 1];
             a.digit_hist = hist + p * kRadix;
             if (p == 0)
                 pass.run<kSrcColumn, kSinkArrays>(a, kKindPresort, N * 12);
@@ -932,18 +984,34 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
         }
     }
 
+    // next_d maps the r-th point of order_d to its position in order_(d+1):
+    // round l's new tags go straight to where round l+1 reads them.
+    const int knext = writes < k ? writes : k;
+    if (knext > 0) {
+        for (int d = 0; d < kc; ++d) {
+            timer.begin(kKindMaps, N * 8);
+            k_invert<<<grid, kBlock, 0, stream>>>(order(d), n, rank(d));
+            timer.end();
+        }
+        for (int d = 0; d < knext; ++d) {
+            timer.begin(kKindMaps, N * 12);
+            k_cross<<<grid, kBlock, 0, stream>>>(rank(d), rank((d + 1) % k), n, next(d));
+            timer.end();
+        }
+    }
+
     // Round 0: all tags are 0.
-    if (keep_sorted && rounds == 1) {
-        *sorted_out = orders;
+    if (writes == 0) {
+        *sorted_out = order(0);  // keep_sorted with a single round
     } else {
         timer.begin(kKindUpdate, N * 8);
-        k_round0<<<grid_for(n, kBlock * 4, 8192), kBlock, 0, stream>>>(orders, geo, tag);
+        k_round0<<<grid, kBlock, 0, stream>>>(next(0), geo, tagq(1 % k));
         timer.end();
     }
 
-    // Round l: stable sort of order_{l mod k} by tag, one pass per tag byte.
-    // Pass 0 gathers each point's tag into buffer 0; pass p writes buffer
-    // (p+1)&1 and the next pass reads it.
+    // Round l: stable sort of the records (tag, next_d[r]) -- or (tag, point
+    // index) in the final round -- kept in order_d order, by tag, one pass
+    // per tag byte; pass p reads buffer p&1 and writes buffer (p+1)&1.
     for (int l = 1; l < rounds; ++l) {
         const int d = l % k;
         const int passes = tag_passes(l);
@@ -955,41 +1023,26 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
             PassArgs a{};
             a.n = n;
             a.shift = 8 * p;
-            a.gather = tag;
-            a.tag_out = tag;
             a.digit_hist = tag_hist + p * kRadix;
             a.geo = geo;
             a.round = l;
-            u32* out_keys = keys[(p + 1) & 1];
-            u32* out_vals = vals[(p + 1) & 1];
-            if (p == 0) {
-                a.vals_in = orders + (size_t)d * n;
-                a.keys_out = keys[0];  // gathered (tag, index) records
-                a.vals_out = vals[0];
-                a.scatter_keys = out_keys;
-                a.scatter_vals = out_vals;
-            } else {
-                a.keys_in = keys[p & 1];
-                a.vals_in = vals[p & 1];
-                a.keys_out = out_keys;
-                a.vals_out = out_vals;
-            }
+            a.keys_in = p == 0 ? tagq(d) : keys[p & 1];
+            a.vals_in = p == 0 ? (final ? order(d) : next(d)) : vals[p & 1];
+            a.keys_out = keys[(p + 1) & 1];
+            a.vals_out = vals[(p + 1) & 1];
+            a.tag_out = tagq((l + 1) % k);
             const bool last = p == passes - 1;
-            // list + gathered tag + records written and read back, or records
-            const double in = p == 0 ? N * 24 : N * 8;
             if (!last) {
-                if (p == 0) pass.run<kSrcGather, kSinkArrays>(a, kKindTagPass, in + N * 8);
-                else pass.run<kSrcArrays, kSinkArrays>(a, kKindTagPass, in + N * 8);
+                pass.run<kSrcArrays, kSinkArrays>(a, kKindTagPass, N * 20);
             } else if (final) {
-                *sorted_out = out_vals;
-                if (p == 0) pass.run<kSrcGather, kSinkVals>(a, kKindFinal, in + N * 4);
-                else pass.run<kSrcArrays, kSinkVals>(a, kKindFinal, in + N * 4);
+                *sorted_out = a.vals_out;
+                pass.run<kSrcArrays, kSinkVals>(a, kKindFinal, N * 16);
             } else {
-                if (p == 0) pass.run<kSrcGather, kSinkTags>(a, kKindUpdate, in + N * 4);
-                else pass.run<kSrcArrays, kSinkTags>(a, kKindUpdate, in + N * 4);
+                pass.run<kSrcArrays, kSinkTags>(a, kKindUpdate, N * 16);
             }
         }
     }
+    if (tags_dim) *tags_dim = rounds % k;
     return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
 }
 
@@ -1031,12 +1084,19 @@ kdt_status build_impl(const float* points, int64_t N, int32_t k, int32_t* perm_o
     kdt_status st = validate(points, N, k, perm_out, perm_bytes, tree_out, tree_bytes, workspace,
                              workspace_bytes, &lay);
     if (st != KDT_OK || N == 0) return st;
+    if (N == 1) {
+        timer.begin(kKindPlace, 4.0 + (tree_out ? 8.0 * k : 0));
+        k_single<<<1, 64, 0, stream>>>(points, k, perm_out, tree_out);
+        timer.end();
+        return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
+    }
     const Geometry geo = make_geometry(N);
     const int l0 = split_level(geo);
     const u32* sorted = nullptr;
     if (l0 > 0) {
         // Global rounds 0 .. l0-1; the last one leaves its sorted order.
-        st = run_rounds(points, N, k, l0, (char*)workspace, lay, stream, timer, true, &sorted);
+        st = run_rounds(points, N, k, l0, (char*)workspace, lay, stream, timer, true, &sorted,
+                        nullptr);
         if (st != KDT_OK) return st;
         const u64 top = full_nodes(l0);
         timer.begin(kKindPlace, (double)top * (4 + 4 + (tree_out ? 8.0 * k : 0)));
@@ -1054,6 +1114,7 @@ kdt_status build_impl(const float* points, int64_t N, int32_t k, int32_t* perm_o
     int bits = 0;
     for (u64 v = (u64)(N - 1); v; v >>= 1) ++bits;
     sa.index_bytes = (bits + kRadixBits - 1) / kRadixBits;
+    sa.stage = (u32*)((char*)workspace + lay.stage);
     sa.perm = perm_out;
     sa.tree = tree_out;
     const i64 below = N - (i64)full_nodes(l0);  // points in the level-l0 subtrees
@@ -1121,14 +1182,17 @@ kdt_status kdt_debug_tags(const float* points, int64_t N, int32_t k, int32_t rou
     if (st != KDT_OK || N == 0) return st;
     const int max_rounds = make_geometry(N).levels - 1;
     if (rounds < 0 || rounds > max_rounds) return KDT_ERR_INVALID_ARG;
-    const u32* tag = nullptr;
-    if (rounds > 0) {
-        st = run_rounds(points, N, k, rounds, (char*)workspace, lay, stream, Timer{nullptr},
-                        false, nullptr);
-        if (st != KDT_OK) return st;
-        tag = (const u32*)((char*)workspace + lay.tag);
+    if (rounds == 0) {
+        k_copy_tags<<<grid_for(N, kBlock * 4, 8192), kBlock, 0, stream>>>(nullptr, N, tags_out);
+        return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
     }
-    k_copy_tags<<<grid_for(N, kBlock * 4, 8192), kBlock, 0, stream>>>(tag, N, tags_out);
+    int d = 0;
+    st = run_rounds(points, N, k, rounds, (char*)workspace, lay, stream, Timer{nullptr}, false,
+                    nullptr, &d);
+    if (st != KDT_OK) return st;
+    const u32* tagq = (const u32*)((char*)workspace + lay.tagq) + (size_t)d * N;
+    const u32* order = (const u32*)((char*)workspace + lay.orders) + (size_t)d * N;
+    k_unpermute<<<grid_for(N, kBlock * 4, 8192), kBlock, 0, stream>>>(tagq, order, N, tags_out);
     return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
 }
 
