@@ -315,8 +315,10 @@ __device__ inline void load_tile(const PassArgs& a, i64 wbase, u32 (&key)[kItems
 }
 
 // Rank inside the wave: lanes holding the same digit are found with eight
-// ballots; the lowest such lane bumps the wave's counter for the digit.
-// rank[j] = records of the same digit earlier in the wave's rows.
+// ballots (a lane's peers are the lanes that never disagree with it on a
+// bit: the OR over bits of vote ^ own-bit-mask, inverted); the lowest such
+// lane bumps the wave's counter for the digit. rank[j] = records of the
+// same digit earlier in the wave's rows.
 __device__ inline void wave_rank(const u32 (&key)[kItems], i64 wbase, i64 n, int shift,
                                  u32* count, u32 (&rank)[kItems]) {
     const int lane = threadIdx.x & 63;
@@ -326,13 +328,15 @@ __device__ inline void wave_rank(const u32 (&key)[kItems], i64 wbase, i64 n, int
     for (int j = 0; j < kItems; ++j) {
         const bool valid = (wbase + (i64)j * 64) < n;
         const u32 d = (key[j] >> shift) & (kRadix - 1);
-        u64 peers = __ballot(valid);
+        u32 miss_lo = 0, miss_hi = 0;
 #pragma unroll
         for (int b = 0; b < kRadixBits; ++b) {
-            const bool bit = (d >> b) & 1;
-            const u64 vote = __ballot(bit);
-            peers &= bit ? vote : ~vote;
+            const u64 vote = __ballot((d >> b) & 1);
+            const u32 m = (u32)((int)(d << (31 - b)) >> 31);  // all ones where the bit is set
+            miss_lo |= (u32)vote ^ m;
+            miss_hi |= (u32)(vote >> 32) ^ m;
         }
+        const u64 peers = __ballot(valid) & ~(((u64)miss_hi << 32) | miss_lo);
         const u32 before = __popcll(peers & below);
         u32 seen = 0;
         if (valid) seen = count[d];
@@ -570,13 +574,15 @@ __device__ void local_pass(u64 (&rec)[kLocalItems], int shift, LocalShared& sh) 
 #pragma unroll
     for (int j = 0; j < kLocalItems; ++j) {
         const u32 d = (u32)(rec[j] >> shift) & (kRadix - 1);
-        u64 peers = ~0ull;
+        u32 miss_lo = 0, miss_hi = 0;
 #pragma unroll
         for (int b = 0; b < kRadixBits; ++b) {
-            const bool bit = (d >> b) & 1;
-            const u64 vote = __ballot(bit);
-            peers &= bit ? vote : ~vote;
+            const u64 vote = __ballot((d >> b) & 1);
+            const u32 m = (u32)((int)(d << (31 - b)) >> 31);  // all ones where the bit is set
+            miss_lo |= (u32)vote ^ m;
+            miss_hi |= (u32)(vote >> 32) ^ m;
         }
+        const u64 peers = ~(((u64)miss_hi << 32) | miss_lo);
         const u32 before = __popcll(peers & below);
         const u32 seen = sh.count[w][d];
         rank[j] = seen + before;
@@ -710,33 +716,64 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
             local_order(column((a.l0 + u) % a.k), nc, sh.order[u], sh);
     __syncthreads();
 
+    // Round t sorts every segment's points by (tag, coordinate, index) and
+    // moves each point to the child its sorted position falls in. Segment
+    // s starts at a closed-form position, so a point's sorted position is
+    // that start plus its rank among the points of s earlier in the
+    // (coordinate, index) order; that rank is all the round needs, and no
+    // record has to move. It is counted per wave over the 2^t live
+    // segments (ballot match on s - F(t)), then prefixed across waves.
+    uint16_t* seg_count = reinterpret_cast<uint16_t*>(sh.exch);  // [kLocalWaves][2^t]
     for (int t = 0; t < rounds; ++t) {
         uint16_t* order = sh.order[cached ? t % a.k : 0];
         if (!cached) local_order(column((a.l0 + t) % a.k), nc, order, sh);
-        // Sort the points of every segment by (tag, coordinate, index): a
-        // stable sort by tag of the (coordinate, index) order.
+        const u32 fl = (u32)full_nodes(t);
+        const int segs = 1 << t;
+        const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        for (int i = threadIdx.x; i < kLocalWaves * segs; i += kLocalBlock) seg_count[i] = 0;
+        __syncthreads();
+        const u64 below = (1ull << lane) - 1;
+        u32 seg[kLocalItems], rank[kLocalItems];
 #pragma unroll
         for (int j = 0; j < kLocalItems; ++j) {
-            const int q = local_slot(j);
-            rec[j] = ~0ull;
-            if ((u32)q < nc) {
-                const u32 e = order[q];
-                rec[j] = ((u64)sh.tag[e] << 16) | e;
+            const u32 q = (u32)local_slot(j);
+            u32 st = fl;  // fixed points (tags < F(t)) are not ranked
+            if (q < nc) st = sh.tag[order[q]];
+            const bool live = st >= fl && q < nc;
+            const u32 b = live ? st - fl : 0;
+            seg[j] = st;
+            u32 miss_lo = 0, miss_hi = 0;
+            for (int bit = 0; bit < t; ++bit) {
+                const u64 vote = __ballot((b >> bit) & 1);
+                const u32 m = (u32)((int)(b << (31 - bit)) >> 31);
+                miss_lo |= (u32)vote ^ m;
+                miss_hi |= (u32)(vote >> 32) ^ m;
+            }
+            const u64 peers = __ballot(live) & ~(((u64)miss_hi << 32) | miss_lo);
+            const u32 before = __popcll(peers & below);
+            u32 seen = 0;
+            if (live) seen = seg_count[w * segs + b];
+            rank[j] = seen + before;
+            if (live && before == 0) seg_count[w * segs + b] = (uint16_t)(seen + __popcll(peers));
+        }
+        __syncthreads();
+        for (int b = threadIdx.x; b < segs; b += kLocalBlock) {
+            u32 run = 0;
+            for (int v = 0; v < kLocalWaves; ++v) {
+                const u32 c = seg_count[v * segs + b];
+                seg_count[v * segs + b] = (uint16_t)run;
+                run += c;
             }
         }
-        if (t > 0)  // round 0: every tag is 0, the order is already sorted
-            for (int sft = 16; sft < 16 + t + 1; sft += kRadixBits) local_pass(rec, sft, sh);
-        else
-            __syncthreads();
-        const u64 fl = full_nodes(t);
+        __syncthreads();
 #pragma unroll
         for (int j = 0; j < kLocalItems; ++j) {
-            const u64 q = (u64)local_slot(j);
-            if (q >= nc) continue;
-            const u64 s = rec[j] >> 16;
-            if (s < fl) continue;
+            const u32 q = (u32)local_slot(j);
+            const u64 s = seg[j];
+            if (q >= nc || s < fl) continue;
+            const u64 p = segment_begin(lg, s, t) + seg_count[w * segs + (s - fl)] + rank[j];
             const u64 pivot = segment_begin(lg, s, t) + subtree_size(lg, 2 * s + 1);
-            sh.tag[rec[j] & 0xffff] = (uint16_t)(q < pivot ? 2 * s + 1 : (q > pivot ? 2 * s + 2 : s));
+            sh.tag[order[q]] = (uint16_t)(p < pivot ? 2 * s + 1 : (p > pivot ? 2 * s + 2 : s));
         }
         __syncthreads();
     }
