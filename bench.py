@@ -15,9 +15,15 @@ Prints ONE JSON line on stdout (progress goes to stderr):
   cpu_baseline  the CPU oracle on a bounded sample of the same workload
 """
 import argparse
+import csv
+import glob
 import json
 import os
+import re
+import shutil
+import subprocess
 import sys
+import tempfile
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -25,6 +31,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published figure
+COPY_BYTES = 256 << 20  # the --calibration-copy dispatch reads and writes this much
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
 def log(msg):
@@ -47,6 +55,49 @@ def cpu_baseline(name, sample_n):
                       % (name, sample_n, w.k, dt)}
 
 
+def kernel_short_name(name):
+    """'void (anonymous namespace)::k_x<1, 2>((anonymous namespace)::Args)' -> 'k_x<1, 2>'."""
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return re.sub(r"\(.*", "", name).strip()
+
+
+def counter_traffic(workload, kernel):
+    """Per-launch HBM bytes of `kernel` from two rocprofv3 counter runs of this
+    benchmark (FETCH_SIZE, then WRITE_SIZE), each scaled by what the counter
+    reads for a plain 256 MiB device copy. None if rocprofv3 is unavailable."""
+    prof = shutil.which("rocprofv3")
+    if prof is None:
+        return None
+    out = {}
+    with tempfile.TemporaryDirectory(prefix="kdt_pmc_") as tmp:
+        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            d = os.path.join(tmp, counter)
+            cmd = ["timeout", "-s", "KILL", "150", prof, "--pmc", counter, "--output-format", "csv",
+                   "-d", d, "-o", "kdt", "--", sys.executable, os.path.abspath(__file__),
+                   "--workload", workload, "--steps", "1", "--warmup", "1", "--no-profile",
+                   "--no-cpu-baseline", "--no-counters", "--calibration-copy"]
+            r = subprocess.run(cmd, stdout=subprocess.DEVNULL, stderr=subprocess.PIPE, text=True)
+            files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+            if r.returncode != 0 or not files:
+                log("bench: %s counter run failed (rc %d)" % (counter, r.returncode))
+                return None
+            per, copy = [], []
+            with open(files[0]) as f:
+                for row in csv.DictReader(f):
+                    if row.get("Counter_Name") != counter:
+                        continue
+                    kname = kernel_short_name(row["Kernel_Name"])
+                    if kname == kernel:
+                        per.append(float(row["Counter_Value"]))
+                    elif kname == COPY_KERNEL:
+                        copy.append(float(row["Counter_Value"]))
+            if not per or not copy:
+                return None
+            scale = (COPY_BYTES / 1024.0) / copy[0]
+            out[counter] = {"bytes": sum(per) / len(per) * 1024.0 * scale, "scale": round(scale, 3)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -56,6 +107,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1 << 22)
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event loop")
+    ap.add_argument("--no-counters", action="store_true",
+                    help="skip the rocprofv3 FETCH_SIZE/WRITE_SIZE runs behind roofline.traffic")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy, the reference "
                          "dispatch for scaling hardware traffic counters")
@@ -136,16 +189,30 @@ def main():
         roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                     "kernel": dom, "avg_us": d["avg_us"], "bytes_per_launch": d["bytes_per_launch"]}
-        passes = [kk for kk in kernels
-                  if kk in ("hist", "presort", "tag_pass", "tag_update", "final_pass")]
+        passes = [kk for kk in kernels if kk.startswith(("k_tile_", "k_col_hist", "k_tag_hist",
+                                                         "k_invert", "k_cross", "k_round0"))]
         tot_b = sum(agg[kk]["bytes"] for kk in passes)
         tot_ms = sum(agg[kk]["ms"] for kk in passes)
         roofline["sort_and_update_passes"] = {
             "GBps": round(tot_b / (tot_ms * 1e-3) / 1e9, 1),
-            "frac": round(tot_b / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-        for kind, kv in sorted(kernels.items()):
-            log("  %-12s %4d/build  avg %8.2f us  %8.1f GB/s  %.3f ms/build"
+            "frac": round(tot_b / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "ms_per_build": round(tot_ms / args.steps, 4)}
+        for kind, kv in sorted(kernels.items(), key=lambda kv: -kv[1]["ms_per_build"]):
+            log("  %-22s %4d/build  avg %8.2f us  %8.1f GB/s  %.3f ms/build"
                 % (kind, kv["launches_per_build"], kv["avg_us"], kv["GBps"], kv["ms_per_build"]))
+        if not args.no_counters:
+            log("bench: rocprofv3 FETCH_SIZE / WRITE_SIZE runs for %s" % dom)
+            tr = counter_traffic(name, dom)
+            if tr:
+                total = tr["FETCH_SIZE"]["bytes"] + tr["WRITE_SIZE"]["bytes"]
+                roofline["traffic"] = int(total)
+                roofline["traffic_detail"] = {
+                    "fetch_bytes": int(tr["FETCH_SIZE"]["bytes"]),
+                    "write_bytes": int(tr["WRITE_SIZE"]["bytes"]),
+                    "counter_scale": {"FETCH_SIZE": tr["FETCH_SIZE"]["scale"],
+                                      "WRITE_SIZE": tr["WRITE_SIZE"]["scale"]},
+                    "GBps": round(total / (d["avg_us"] * 1e-6) / 1e9, 1)}
+                log("  traffic %s" % roofline["traffic_detail"])
 
     base = None
     if not args.no_cpu_baseline:

@@ -363,27 +363,38 @@ __global__ __launch_bounds__(kBlock) void k_tile_count(PassArgs a) {
 
 // One workgroup per digit d: slots[t][d] = start(d) + counts of d in tiles
 // before t, where start(d) is the exclusive prefix of the digit totals.
+// Each thread scans a contiguous run of tiles; its loads are issued in
+// batches of 8 so that they are in flight together.
 __global__ __launch_bounds__(kBlock) void k_tile_scan(const u32* __restrict__ digit_hist,
                                                       u32* __restrict__ slots, i64 tiles) {
     __shared__ u32 s_wave[kWaves];
+    __shared__ u32 s_start;
+    constexpr int kBatch = 8;
     const int tid = threadIdx.x, d = blockIdx.x;
     const u32 before = tid < d ? digit_hist[tid] : 0u;
-    u32 start = block_exclusive_scan(before, s_wave);  // + before = inclusive
-    start += before;
-    // every thread needs the total over tid < d: the last thread holds it
-    __shared__ u32 s_start;
-    if (tid == kBlock - 1) s_start = start;
-    __syncthreads();
-    u32 run = s_start;
+    const u32 prefix = block_exclusive_scan(before, s_wave) + before;
+    if (tid == kBlock - 1) s_start = prefix;  // sum of the totals of digits < d
     const i64 per = (tiles + kBlock - 1) / kBlock;
     const i64 t0 = tid * per, t1 = t0 + per < tiles ? t0 + per : tiles;
     u32 sum = 0;
-    for (i64 t = t0; t < t1; ++t) sum += slots[(u64)t * kRadix + d];
-    u32 off = block_exclusive_scan(sum, s_wave) + run;
-    for (i64 t = t0; t < t1; ++t) {
-        const u32 c = slots[(u64)t * kRadix + d];
-        slots[(u64)t * kRadix + d] = off;
-        off += c;
+    for (i64 t = t0; t < t1; t += kBatch) {
+        u32 v[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) v[i] = t + i < t1 ? slots[(u64)(t + i) * kRadix + d] : 0u;
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) sum += v[i];
+    }
+    __syncthreads();
+    u32 off = block_exclusive_scan(sum, s_wave) + s_start;
+    for (i64 t = t0; t < t1; t += kBatch) {
+        u32 v[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) v[i] = t + i < t1 ? slots[(u64)(t + i) * kRadix + d] : 0u;
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            if (t + i < t1) slots[(u64)(t + i) * kRadix + d] = off;
+            off += v[i];
+        }
     }
 }
 
@@ -898,14 +909,9 @@ bool ranges_overlap(const void* a, size_t an, const void* b, size_t bn) {
     return a0 < b0 + bn && b0 < a0 + an;
 }
 
-// Optional per-kernel timing: an event pair around every launch.
-enum Kind { kKindInit, kKindHist, kKindPresort, kKindMaps, kKindTagPass, kKindUpdate, kKindFinal,
-            kKindSubtree, kKinds };
-const char* const kKindNames[kKinds] = {"init", "hist", "presort", "maps", "tag_pass",
-                                        "tag_update", "final_pass", "subtree"};
-constexpr int kKindPlace = kKindSubtree;  // placement of the top nodes counts with the subtrees
-static_assert(kKinds <= KDT_PROFILE_MAX_KINDS, "profile kinds");
-
+// Optional per-kernel timing: an event pair around every launch, grouped
+// by kernel (names as the profiler prints them) with each launch's
+// algorithmic bytes: every array the kernel must read or write, once.
 struct Profiler {
     struct Rec {
         int kind;
@@ -914,11 +920,21 @@ struct Profiler {
     };
     Rec recs[2048];
     int count = 0;
+    const char* names[KDT_PROFILE_MAX_KINDS];
+    int kinds = 0;
     bool failed = false;
     hipStream_t stream;
 
-    void begin(int kind, double bytes) {
-        if (count >= 2048) { failed = true; return; }
+    int kind_of(const char* name) {
+        for (int i = 0; i < kinds; ++i)
+            if (names[i] == name) return i;
+        if (kinds == KDT_PROFILE_MAX_KINDS) return -1;
+        names[kinds] = name;
+        return kinds++;
+    }
+    void begin(const char* name, double bytes) {
+        const int kind = kind_of(name);
+        if (count >= 2048 || kind < 0) { failed = true; return; }
         Rec& r = recs[count];
         r.kind = kind;
         r.bytes = bytes;
@@ -939,7 +955,7 @@ struct Profiler {
 
 struct Timer {  // no-op unless a Profiler is attached
     Profiler* p;
-    void begin(int kind, double bytes) { if (p) p->begin(kind, bytes); }
+    void begin(const char* name, double bytes) { if (p) p->begin(name, bytes); }
     void end() { if (p) p->end(); }
 };
 
@@ -951,12 +967,23 @@ struct PassLauncher {
     Timer timer;
 
     template <int kSrc, int kSink>
-    void run(PassArgs a, int kind, double bytes) {
+    void run(PassArgs a) {
         a.tile_slots = slots;
         const unsigned tiles = (unsigned)lay.tiles;
-        timer.begin(kind, bytes);
+        const double n = (double)a.n;
+        static const char* const count_names[2] = {"k_tile_count<0>", "k_tile_count<1>"};
+        static const char* const scatter_names[2][3] = {
+            {"k_tile_scatter<0, 0>", "k_tile_scatter<0, 1>", "k_tile_scatter<0, 2>"},
+            {"k_tile_scatter<1, 0>", "k_tile_scatter<1, 1>", "k_tile_scatter<1, 2>"}};
+        timer.begin(count_names[kSrc], n * 4);  // keys (or the column)
         k_tile_count<kSrc><<<tiles, kBlock, 0, stream>>>(a);
+        timer.end();
+        timer.begin("k_tile_scan", (double)lay.tiles * kRadix * 8);
         k_tile_scan<<<kRadix, kBlock, 0, stream>>>(a.digit_hist, slots, lay.tiles);
+        timer.end();
+        // in: column (4) or key+val (8); out: key+val (8) or one word (4)
+        const double in = kSrc == kSrcColumn ? 4 : 8, out = kSink == kSinkArrays ? 8 : 4;
+        timer.begin(scatter_names[kSrc][kSink], n * (in + out));
         k_tile_scatter<kSrc, kSink><<<tiles, kBlock, 0, stream>>>(a);
         timer.end();
     }
@@ -990,7 +1017,7 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
     const double N = (double)n;
     const int grid = grid_for(n, kBlock * 4, 8192);
 
-    timer.begin(kKindInit, N * kc * 8);
+    timer.begin("k_init", N * kc * 8);
     k_init<<<grid, kBlock, 0, stream>>>(pts, n, k, kc, cols, small, lay.small_words);
     timer.end();
 
@@ -999,7 +1026,7 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
     for (int d = 0; d < kc; ++d) {
         const float* col = cols + (size_t)d * n;
         u32* hist = col_hist + (size_t)d * kKeyBytes * kRadix;
-        timer.begin(kKindHist, N * 4);
+        timer.begin("k_col_hist", N * 4);
         k_col_hist<<<grid_for(n, kBlock * 16, 2048), kBlock, 0, stream>>>(col, n, hist);
         timer.end();
         for (int p = 0; p < kKeyBytes; ++p) {
@@ -1013,11 +1040,11 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
             a.vals_out = p == kKeyBytes - 1 ? order(d) : vals[p & 1];
             a.digit_hist = hist + p * kRadix;
             if (p == 0)
-                pass.run<kSrcColumn, kSinkArrays>(a, kKindPresort, N * 12);
+                pass.run<kSrcColumn, kSinkArrays>(a);
             else if (p < kKeyBytes - 1)
-                pass.run<kSrcArrays, kSinkArrays>(a, kKindPresort, N * 16);
+                pass.run<kSrcArrays, kSinkArrays>(a);
             else
-                pass.run<kSrcArrays, kSinkVals>(a, kKindPresort, N * 12);
+                pass.run<kSrcArrays, kSinkVals>(a);
         }
     }
 
@@ -1026,12 +1053,12 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
     const int knext = writes < k ? writes : k;
     if (knext > 0) {
         for (int d = 0; d < kc; ++d) {
-            timer.begin(kKindMaps, N * 8);
+            timer.begin("k_invert", N * 8);
             k_invert<<<grid, kBlock, 0, stream>>>(order(d), n, rank(d));
             timer.end();
         }
         for (int d = 0; d < knext; ++d) {
-            timer.begin(kKindMaps, N * 12);
+            timer.begin("k_cross", N * 12);
             k_cross<<<grid, kBlock, 0, stream>>>(rank(d), rank((d + 1) % k), n, next(d));
             timer.end();
         }
@@ -1041,7 +1068,7 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
     if (writes == 0) {
         *sorted_out = order(0);  // keep_sorted with a single round
     } else {
-        timer.begin(kKindUpdate, N * 8);
+        timer.begin("k_round0", N * 8);
         k_round0<<<grid, kBlock, 0, stream>>>(next(0), geo, tagq(1 % k));
         timer.end();
     }
@@ -1053,7 +1080,7 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
         const int d = l % k;
         const int passes = tag_passes(l);
         const bool final = keep_sorted && l == rounds - 1;
-        timer.begin(kKindHist, 0);
+        timer.begin("k_tag_hist", 0);
         k_tag_hist<<<1, kBlock, 0, stream>>>(geo, l, passes, tag_hist);
         timer.end();
         for (int p = 0; p < passes; ++p) {
@@ -1070,12 +1097,12 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
             a.tag_out = tagq((l + 1) % k);
             const bool last = p == passes - 1;
             if (!last) {
-                pass.run<kSrcArrays, kSinkArrays>(a, kKindTagPass, N * 20);
+                pass.run<kSrcArrays, kSinkArrays>(a);
             } else if (final) {
                 *sorted_out = a.vals_out;
-                pass.run<kSrcArrays, kSinkVals>(a, kKindFinal, N * 16);
+                pass.run<kSrcArrays, kSinkVals>(a);
             } else {
-                pass.run<kSrcArrays, kSinkTags>(a, kKindUpdate, N * 16);
+                pass.run<kSrcArrays, kSinkTags>(a);
             }
         }
     }
@@ -1122,7 +1149,7 @@ kdt_status build_impl(const float* points, int64_t N, int32_t k, int32_t* perm_o
                              workspace_bytes, &lay);
     if (st != KDT_OK || N == 0) return st;
     if (N == 1) {
-        timer.begin(kKindPlace, 4.0 + (tree_out ? 8.0 * k : 0));
+        timer.begin("k_single", 4.0 + (tree_out ? 8.0 * k : 0));
         k_single<<<1, 64, 0, stream>>>(points, k, perm_out, tree_out);
         timer.end();
         return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
@@ -1136,7 +1163,7 @@ kdt_status build_impl(const float* points, int64_t N, int32_t k, int32_t* perm_o
                         nullptr);
         if (st != KDT_OK) return st;
         const u64 top = full_nodes(l0);
-        timer.begin(kKindPlace, (double)top * (4 + 4 + (tree_out ? 8.0 * k : 0)));
+        timer.begin("k_place_top", (double)top * (4 + 4 + (tree_out ? 8.0 * k : 0)));
         k_place_top<<<(unsigned)((top + kBlock - 1) / kBlock), kBlock, 0, stream>>>(
             points, k, geo, l0, sorted, perm_out, tree_out);
         timer.end();
@@ -1155,7 +1182,11 @@ kdt_status build_impl(const float* points, int64_t N, int32_t k, int32_t* perm_o
     sa.perm = perm_out;
     sa.tree = tree_out;
     const i64 below = N - (i64)full_nodes(l0);  // points in the level-l0 subtrees
-    timer.begin(kKindSubtree, (double)below * ((l0 > 0 ? 4 : 0) + 4 + (tree_out ? 8.0 * k : 4.0 * k)));
+    // indices in (when l0 > 0), one row gathered, index + row staged and read
+    // back, perm and tree out
+    const double row = 4.0 * k;
+    timer.begin("k_subtree", (double)below * ((l0 > 0 ? 4 : 0) + row + 2 * (4 + row) + 4 +
+                                             (tree_out ? row : 0)));
     k_subtree<<<(unsigned)(1ull << l0), kLocalBlock, 0, stream>>>(sa);
     timer.end();
     return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
@@ -1188,9 +1219,9 @@ kdt_status kdt_build_profiled(const float* points, int64_t N, int32_t k, int32_t
                                stream, Timer{prof});
     if (hipStreamSynchronize(stream) != hipSuccess && st == KDT_OK) st = KDT_ERR_HIP;
     *profile = kdt_profile{};
-    profile->kinds = kKinds;
-    for (int i = 0; i < kKinds; ++i)
-        for (int c = 0; kKindNames[i][c] && c < 23; ++c) profile->name[i][c] = kKindNames[i][c];
+    profile->kinds = prof->kinds;
+    for (int i = 0; i < prof->kinds; ++i)
+        for (int c = 0; prof->names[i][c] && c < 23; ++c) profile->name[i][c] = prof->names[i][c];
     for (int i = 0; i < prof->count; ++i) {
         Profiler::Rec& r = prof->recs[i];
         float ms = 0.f;
