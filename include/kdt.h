@@ -88,7 +88,7 @@ kdt_status kdt_debug_tags(const float* points, int64_t N, int32_t k, int32_t rou
                           hipStream_t stream);
 
 /* Per-kernel-kind timing of one build, for benchmarking. */
-#define KDT_PROFILE_MAX_KINDS 16
+#define KDT_PROFILE_MAX_KINDS 32
 typedef struct {
     int32_t kinds;                        /* entries filled below */
     char name[KDT_PROFILE_MAX_KINDS][24]; /* kernel, e.g. "k_tile_scatter<1, 2>" */

@@ -286,6 +286,8 @@ struct PassArgs {
     u32* keys_out;             // kSinkArrays
     u32* vals_out;             // kSinkArrays, kSinkVals
     u32* tag_out;              // kSinkTags: tag_out[val] = the record's new tag
+    const u32* extra_in;       // optional second payload (nullptr: none); with
+    u32* extra_out;            //   kSrcColumn it is indexed by point index
     const u32* digit_hist;     // 256 counts of this pass's digit over all records
     u32* tile_slots;           // tiles x 256: counts, then first global slots
     Geometry geo;              // kSinkTags
@@ -297,6 +299,7 @@ struct PassArgs {
 template <int kSrc>
 __device__ inline void load_tile(const PassArgs& a, i64 wbase, u32 (&key)[kItems],
                                  u32 (&val)[kItems]) {
+    // (the optional second payload is loaded by the scatter kernel itself)
 #pragma unroll
     for (int j = 0; j < kItems; ++j) {
         const i64 e = wbase + (i64)j * 64;
@@ -398,7 +401,7 @@ __global__ __launch_bounds__(kBlock) void k_tile_scan(const u32* __restrict__ di
     }
 }
 
-template <int kSrc, int kSink>
+template <int kSrc, int kSink, bool kExtra>
 __global__ __launch_bounds__(kBlock) void k_tile_scatter(PassArgs a) {
     __shared__ union {
         u32 count[kWaves][kRadix];  // ranking: per-wave digit counts, then prefixes
@@ -414,8 +417,15 @@ __global__ __launch_bounds__(kBlock) void k_tile_scatter(PassArgs a) {
     const i64 base = (i64)blockIdx.x * kTile;
     const i64 wbase = base + (i64)w * (64 * kItems) + (tid & 63);
     const u32 global_start = a.tile_slots[(u64)blockIdx.x * kRadix + tid];
-    u32 key[kItems], val[kItems], rank[kItems];
+    u32 key[kItems], val[kItems], rank[kItems], extra[kItems];
     load_tile<kSrc>(a, wbase, key, val);
+    if (kExtra) {
+#pragma unroll
+        for (int j = 0; j < kItems; ++j) {
+            const i64 e = wbase + (i64)j * 64;
+            extra[j] = e < a.n ? a.extra_in[e] : 0u;
+        }
+    }
     wave_rank(key, wbase, a.n, a.shift, sm.count[w], rank);
     __syncthreads();
 
@@ -489,6 +499,19 @@ __global__ __launch_bounds__(kBlock) void k_tile_scatter(PassArgs a) {
     for (int i = tid; i < valid_here; i += kBlock) {
         const u32 dst = s_base[s_digit[i]] + (u32)i;
         if (dst < (u64)a.n) a.vals_out[dst] = sm.vals[i];
+    }
+    if (kExtra) {
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kItems; ++j) {
+            if ((wbase + (i64)j * 64) >= a.n) continue;
+            sm.vals[s_local[digit[j]] + rank[j]] = extra[j];
+        }
+        __syncthreads();
+        for (int i = tid; i < valid_here; i += kBlock) {
+            const u32 dst = s_base[s_digit[i]] + (u32)i;
+            if (dst < (u64)a.n) a.extra_out[dst] = sm.vals[i];
+        }
     }
 }
 
@@ -722,9 +745,22 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
     const Geometry lg = make_geometry((i64)nc);
     const int rounds = lg.levels - 1;
     const bool cached = a.k <= kCachedDims;
+    // The points arrived in round l0-1's sorted order, i.e. ordered by
+    // (coordinate (l0-1) mod k, index): that is already the subtree's order
+    // for that dimension (slot of the arrival position q = rec's low bits).
+    const int arrived_dim = a.sorted ? (a.l0 - 1) % a.k : -1;
+    uint16_t* arrived = a.sorted ? sh.order[cached ? a.k - 1 : 1] : nullptr;
+    if (arrived) {
+#pragma unroll
+        for (int j = 0; j < kLocalItems; ++j) {
+            const int e = local_slot(j);
+            if ((u32)e < nc) arrived[rec[j] & 0xffff] = (uint16_t)e;
+        }
+    }
     if (cached)
         for (int u = 0; u < a.k && u < rounds; ++u)
-            local_order(column((a.l0 + u) % a.k), nc, sh.order[u], sh);
+            if ((a.l0 + u) % a.k != arrived_dim)
+                local_order(column((a.l0 + u) % a.k), nc, sh.order[u], sh);
     __syncthreads();
 
     // Round t sorts every segment's points by (tag, coordinate, index) and
@@ -737,7 +773,10 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
     uint16_t* seg_count = reinterpret_cast<uint16_t*>(sh.exch);  // [kLocalWaves][2^t]
     for (int t = 0; t < rounds; ++t) {
         uint16_t* order = sh.order[cached ? t % a.k : 0];
-        if (!cached) local_order(column((a.l0 + t) % a.k), nc, order, sh);
+        if (!cached) {
+            if ((a.l0 + t) % a.k == arrived_dim) order = arrived;
+            else local_order(column((a.l0 + t) % a.k), nc, order, sh);
+        }
         const u32 fl = (u32)full_nodes(t);
         const int segs = 1 << t;
         const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -853,7 +892,8 @@ inline size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 struct Layout {
     int kcols;          // split dimensions the global rounds can use
     i64 tiles;
-    size_t cols, orders, ranks, next, tagq, keys0, keys1, vals0, vals1, small, slots, stage, total;
+    size_t cols, orders, ranks, next, tagq, keys0, keys1, vals0, vals1, extra0, extra1, small,
+        slots, stage, total;
     // inside `small` (u32 words): column histograms, tag histograms
     int col_hist_words, tag_hist_off, small_words;
 };
@@ -888,6 +928,8 @@ bool make_layout(i64 n, int k, Layout* out) {
     lay.keys1 = take((size_t)n * sizeof(u32));
     lay.vals0 = take((size_t)n * sizeof(u32));
     lay.vals1 = take((size_t)n * sizeof(u32));
+    lay.extra0 = take((size_t)n * sizeof(u32));
+    lay.extra1 = take((size_t)n * sizeof(u32));
     lay.small = take((size_t)lay.small_words * sizeof(u32));
     lay.slots = take((size_t)lay.tiles * kRadix * sizeof(u32));
     lay.stage = take((size_t)(k + 1) * n * sizeof(u32));
@@ -972,9 +1014,14 @@ struct PassLauncher {
         const unsigned tiles = (unsigned)lay.tiles;
         const double n = (double)a.n;
         static const char* const count_names[2] = {"k_tile_count<0>", "k_tile_count<1>"};
-        static const char* const scatter_names[2][3] = {
-            {"k_tile_scatter<0, 0>", "k_tile_scatter<0, 1>", "k_tile_scatter<0, 2>"},
-            {"k_tile_scatter<1, 0>", "k_tile_scatter<1, 1>", "k_tile_scatter<1, 2>"}};
+        static const char* const scatter_names[2][3][2] = {
+            {{"k_tile_scatter<0, 0, false>", "k_tile_scatter<0, 0, true>"},
+             {"k_tile_scatter<0, 1, false>", "k_tile_scatter<0, 1, true>"},
+             {"k_tile_scatter<0, 2, false>", "k_tile_scatter<0, 2, true>"}},
+            {{"k_tile_scatter<1, 0, false>", "k_tile_scatter<1, 0, true>"},
+             {"k_tile_scatter<1, 1, false>", "k_tile_scatter<1, 1, true>"},
+             {"k_tile_scatter<1, 2, false>", "k_tile_scatter<1, 2, true>"}}};
+        const bool extra = a.extra_in != nullptr;
         timer.begin(count_names[kSrc], n * 4);  // keys (or the column)
         k_tile_count<kSrc><<<tiles, kBlock, 0, stream>>>(a);
         timer.end();
@@ -982,9 +1029,13 @@ struct PassLauncher {
         k_tile_scan<<<kRadix, kBlock, 0, stream>>>(a.digit_hist, slots, lay.tiles);
         timer.end();
         // in: column (4) or key+val (8); out: key+val (8) or one word (4)
-        const double in = kSrc == kSrcColumn ? 4 : 8, out = kSink == kSinkArrays ? 8 : 4;
-        timer.begin(scatter_names[kSrc][kSink], n * (in + out));
-        k_tile_scatter<kSrc, kSink><<<tiles, kBlock, 0, stream>>>(a);
+        const double in = (kSrc == kSrcColumn ? 4 : 8) + (extra ? 4 : 0);
+        const double out = (kSink == kSinkArrays ? 8 : 4) + (extra ? 4 : 0);
+        timer.begin(scatter_names[kSrc][kSink][extra], n * (in + out));
+        if (extra)
+            k_tile_scatter<kSrc, kSink, true><<<tiles, kBlock, 0, stream>>>(a);
+        else
+            k_tile_scatter<kSrc, kSink, false><<<tiles, kBlock, 0, stream>>>(a);
         timer.end();
     }
 };
@@ -1021,14 +1072,24 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
     k_init<<<grid, kBlock, 0, stream>>>(pts, n, k, kc, cols, small, lay.small_words);
     timer.end();
 
-    // Presort: order_d = point indices by (coordinate d, index). Pass p
-    // reads buffer (p+1)&1 and writes buffer p&1; the last writes order_d.
-    for (int d = 0; d < kc; ++d) {
+    // next_d maps the r-th point of order_d to its position in order_(d+1):
+    // round l's new tags go straight to where round l+1 reads them. For
+    // d >= 1 the presort of d carries rank_(d+1) (a point's position in
+    // order_(d+1), in index order) as a second payload, so its sorted output
+    // is next_d; the dimensions are presorted as 0, kc-1, ..., 1 so that
+    // rank_(d+1) exists by then. next_0 comes from two scattered ranks.
+    const int knext = writes < k ? writes : k;  // next_d needed for d < knext
+    u32* extra[2] = {(u32*)(ws + lay.extra0), (u32*)(ws + lay.extra1)};
+    for (int step = 0; step < kc; ++step) {
+        const int d = step == 0 ? 0 : kc - step;
         const float* col = cols + (size_t)d * n;
         u32* hist = col_hist + (size_t)d * kKeyBytes * kRadix;
+        const bool carry = d >= 1 && d < knext;
         timer.begin("k_col_hist", N * 4);
         k_col_hist<<<grid_for(n, kBlock * 16, 2048), kBlock, 0, stream>>>(col, n, hist);
         timer.end();
+        // Presort: order_d = point indices by (coordinate d, index). Pass p
+        // reads buffer (p+1)&1 and writes buffer p&1; the last writes order_d.
         for (int p = 0; p < kKeyBytes; ++p) {
             PassArgs a{};
             a.n = n;
@@ -1038,6 +1099,10 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
             a.vals_in = vals[(p + 1) & 1];
             a.keys_out = keys[p & 1];
             a.vals_out = p == kKeyBytes - 1 ? order(d) : vals[p & 1];
+            if (carry) {
+                a.extra_in = p == 0 ? rank((d + 1) % k) : extra[(p + 1) & 1];
+                a.extra_out = p == kKeyBytes - 1 ? next(d) : extra[p & 1];
+            }
             a.digit_hist = hist + p * kRadix;
             if (p == 0)
                 pass.run<kSrcColumn, kSinkArrays>(a);
@@ -1046,22 +1111,16 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
             else
                 pass.run<kSrcArrays, kSinkVals>(a);
         }
-    }
-
-    // next_d maps the r-th point of order_d to its position in order_(d+1):
-    // round l's new tags go straight to where round l+1 reads them.
-    const int knext = writes < k ? writes : k;
-    if (knext > 0) {
-        for (int d = 0; d < kc; ++d) {
+        if (knext > 0) {
             timer.begin("k_invert", N * 8);
             k_invert<<<grid, kBlock, 0, stream>>>(order(d), n, rank(d));
             timer.end();
         }
-        for (int d = 0; d < knext; ++d) {
-            timer.begin("k_cross", N * 12);
-            k_cross<<<grid, kBlock, 0, stream>>>(rank(d), rank((d + 1) % k), n, next(d));
-            timer.end();
-        }
+    }
+    if (knext > 0) {
+        timer.begin("k_cross", N * 12);
+        k_cross<<<grid, kBlock, 0, stream>>>(rank(0), rank(1 % k), n, next(0));
+        timer.end();
     }
 
     // Round 0: all tags are 0.
@@ -1235,7 +1294,7 @@ kdt_status kdt_build_profiled(const float* points, int64_t N, int32_t k, int32_t
         (void)hipEventDestroy(prof->recs[i].start);
         (void)hipEventDestroy(prof->recs[i].stop);
     }
-    if (prof->failed && st == KDT_OK) st = KDT_ERR_HIP;
+    if (prof->failed && st == KDT_OK) st = KDT_ERR_HIP;  // event API failure or > 32 kernels
     delete prof;
     return st;
 }

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(PKG, "libkdt.so")
 KDT_OK = 0
 STATUS_NAMES = {0: "KDT_OK", 1: "KDT_ERR_INVALID_ARG", 2: "KDT_ERR_WORKSPACE", 3: "KDT_ERR_HIP"}
 
-PROFILE_MAX_KINDS = 16
+PROFILE_MAX_KINDS = 32
 
 
 class Profile(ctypes.Structure):
