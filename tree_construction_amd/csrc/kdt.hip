@@ -365,37 +365,33 @@ __global__ __launch_bounds__(kBlock) void k_tile_count(PassArgs a) {
 }
 
 // One workgroup per digit d: slots[t][d] = start(d) + counts of d in tiles
-// before t, where start(d) is the exclusive prefix of the digit totals.
-// Each thread scans a contiguous run of tiles; its loads are issued in
-// batches of 8 so that they are in flight together.
+// before t, where start(d) is the exclusive prefix of the digit totals. Each
+// thread scans a contiguous run of up to kScanRun tiles held in registers
+// (one batch of loads); longer inputs loop over runs.
+constexpr int kScanRun = 16;
 __global__ __launch_bounds__(kBlock) void k_tile_scan(const u32* __restrict__ digit_hist,
                                                       u32* __restrict__ slots, i64 tiles) {
     __shared__ u32 s_wave[kWaves];
-    __shared__ u32 s_start;
-    constexpr int kBatch = 8;
+    __shared__ u32 s_carry;
     const int tid = threadIdx.x, d = blockIdx.x;
-    const u32 before = tid < d ? digit_hist[tid] : 0u;
-    const u32 prefix = block_exclusive_scan(before, s_wave) + before;
-    if (tid == kBlock - 1) s_start = prefix;  // sum of the totals of digits < d
-    const i64 per = (tiles + kBlock - 1) / kBlock;
-    const i64 t0 = tid * per, t1 = t0 + per < tiles ? t0 + per : tiles;
-    u32 sum = 0;
-    for (i64 t = t0; t < t1; t += kBatch) {
-        u32 v[kBatch];
+    const u32 below = tid < d ? digit_hist[tid] : 0u;
+    const u32 start = block_exclusive_scan(below, s_wave) + below;
+    if (tid == kBlock - 1) s_carry = start;  // sum of the totals of digits < d
+    for (i64 t0 = 0; t0 < tiles; t0 += (i64)kBlock * kScanRun) {
+        const i64 mine = t0 + (i64)tid * kScanRun;
+        u32 v[kScanRun], sum = 0;
 #pragma unroll
-        for (int i = 0; i < kBatch; ++i) v[i] = t + i < t1 ? slots[(u64)(t + i) * kRadix + d] : 0u;
+        for (int i = 0; i < kScanRun; ++i) {
+            v[i] = mine + i < tiles ? slots[(u64)(mine + i) * kRadix + d] : 0u;
+            sum += v[i];
+        }
+        __syncthreads();  // s_carry written
+        const u32 carry = s_carry;
+        u32 off = block_exclusive_scan(sum, s_wave) + carry;
+        if (tid == kBlock - 1) s_carry = off + sum;
 #pragma unroll
-        for (int i = 0; i < kBatch; ++i) sum += v[i];
-    }
-    __syncthreads();
-    u32 off = block_exclusive_scan(sum, s_wave) + s_start;
-    for (i64 t = t0; t < t1; t += kBatch) {
-        u32 v[kBatch];
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i) v[i] = t + i < t1 ? slots[(u64)(t + i) * kRadix + d] : 0u;
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
-            if (t + i < t1) slots[(u64)(t + i) * kRadix + d] = off;
+        for (int i = 0; i < kScanRun; ++i) {
+            if (mine + i < tiles) slots[(u64)(mine + i) * kRadix + d] = off;
             off += v[i];
         }
     }
@@ -407,6 +403,7 @@ __global__ __launch_bounds__(kBlock) void k_tile_scatter(PassArgs a) {
         u32 count[kWaves][kRadix];  // ranking: per-wave digit counts, then prefixes
         u32 keys[kTile];            // staging of the sorted tile
         u32 vals[kTile];
+        u64 pairs[kExtra && kSink == kSinkVals ? kTile : 1];  // value + second payload
     } sm;
     __shared__ u8 s_digit[kTile];
     __shared__ u32 s_local[kRadix];  // first tile-local slot of each digit
@@ -488,19 +485,30 @@ __global__ __launch_bounds__(kBlock) void k_tile_scatter(PassArgs a) {
         }
         __syncthreads();
     }
+    // Values; the optional second payload shares the value's 64-bit slot
+    // when they are the only outputs, else it gets a staging round of its own.
+    constexpr bool kPairs = kExtra && kSink == kSinkVals;
 #pragma unroll
     for (int j = 0; j < kItems; ++j) {
         if ((wbase + (i64)j * 64) >= a.n) continue;
         const u32 slot = s_local[digit[j]] + rank[j];
-        sm.vals[slot] = val[j];
+        if (kPairs) sm.pairs[slot] = ((u64)extra[j] << 32) | val[j];
+        else sm.vals[slot] = val[j];
         if (kSink == kSinkVals) s_digit[slot] = (u8)digit[j];
     }
     __syncthreads();
     for (int i = tid; i < valid_here; i += kBlock) {
         const u32 dst = s_base[s_digit[i]] + (u32)i;
-        if (dst < (u64)a.n) a.vals_out[dst] = sm.vals[i];
+        if (dst >= (u64)a.n) continue;
+        if (kPairs) {
+            const u64 pv = sm.pairs[i];
+            a.vals_out[dst] = (u32)pv;
+            a.extra_out[dst] = (u32)(pv >> 32);
+        } else {
+            a.vals_out[dst] = sm.vals[i];
+        }
     }
-    if (kExtra) {
+    if (kExtra && !kPairs) {
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < kItems; ++j) {
@@ -700,6 +708,72 @@ __device__ void local_order(const u32* __restrict__ col, u32 nc, uint16_t* order
     __syncthreads();
 }
 
+// Round t sorts every segment's points by (tag, coordinate, index) and
+// moves each point to the child its sorted position falls in. Segment s
+// starts at a closed-form position, so a point's sorted position is that
+// start plus its rank among the points of s earlier in the (coordinate,
+// index) order; that rank is all the round needs, and no record has to
+// move. It is counted per wave over the 2^t live segments (ballot match on
+// s - F(t)), then prefixed across waves. Count is the counter type: a
+// segment on local level t of a subtree of at most kLocalMax points holds at
+// most 2^(levels-t) - 1 points, so 8-bit counters would suffice wherever
+// 16-bit ones no longer fit the exchange buffer (with 4096-point subtrees
+// 16-bit ones always fit).
+template <typename Count>
+__device__ void local_round(const uint16_t* order, u32 nc, int t, const Geometry& lg,
+                            LocalShared& sh) {
+    Count* seg_count = reinterpret_cast<Count*>(sh.exch);  // [kLocalWaves][2^t]
+    const u32 fl = (u32)full_nodes(t);
+    const int segs = 1 << t;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int i = threadIdx.x; i < kLocalWaves * segs; i += kLocalBlock) seg_count[i] = 0;
+    __syncthreads();
+    const u64 below = (1ull << lane) - 1;
+    u32 seg[kLocalItems], rank[kLocalItems];
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) {
+        const u32 q = (u32)local_slot(j);
+        u32 st = fl;  // fixed points (tags < F(t)) are not ranked
+        if (q < nc) st = sh.tag[order[q]];
+        const bool live = st >= fl && q < nc;
+        const u32 b = live ? st - fl : 0;
+        seg[j] = st;
+        u32 miss_lo = 0, miss_hi = 0;
+        for (int bit = 0; bit < t; ++bit) {
+            const u64 vote = __ballot((b >> bit) & 1);
+            const u32 m = (u32)((int)(b << (31 - bit)) >> 31);
+            miss_lo |= (u32)vote ^ m;
+            miss_hi |= (u32)(vote >> 32) ^ m;
+        }
+        const u64 peers = __ballot(live) & ~(((u64)miss_hi << 32) | miss_lo);
+        const u32 before = __popcll(peers & below);
+        u32 seen = 0;
+        if (live) seen = seg_count[w * segs + b];
+        rank[j] = seen + before;
+        if (live && before == 0) seg_count[w * segs + b] = (Count)(seen + __popcll(peers));
+    }
+    __syncthreads();
+    for (int b = threadIdx.x; b < segs; b += kLocalBlock) {
+        u32 run = 0;
+        for (int v = 0; v < kLocalWaves; ++v) {
+            const u32 c = seg_count[v * segs + b];
+            seg_count[v * segs + b] = (Count)run;
+            run += c;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) {
+        const u32 q = (u32)local_slot(j);
+        const u64 s = seg[j];
+        if (q >= nc || s < fl) continue;
+        const u64 p = segment_begin(lg, s, t) + seg_count[w * segs + (s - fl)] + rank[j];
+        const u64 pivot = segment_begin(lg, s, t) + subtree_size(lg, 2 * s + 1);
+        sh.tag[order[q]] = (uint16_t)(p < pivot ? 2 * s + 1 : (p > pivot ? 2 * s + 2 : s));
+    }
+    __syncthreads();
+}
+
 __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
     __shared__ LocalShared sh;
 
@@ -763,69 +837,18 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
                 local_order(column((a.l0 + u) % a.k), nc, sh.order[u], sh);
     __syncthreads();
 
-    // Round t sorts every segment's points by (tag, coordinate, index) and
-    // moves each point to the child its sorted position falls in. Segment
-    // s starts at a closed-form position, so a point's sorted position is
-    // that start plus its rank among the points of s earlier in the
-    // (coordinate, index) order; that rank is all the round needs, and no
-    // record has to move. It is counted per wave over the 2^t live
-    // segments (ballot match on s - F(t)), then prefixed across waves.
-    uint16_t* seg_count = reinterpret_cast<uint16_t*>(sh.exch);  // [kLocalWaves][2^t]
     for (int t = 0; t < rounds; ++t) {
         uint16_t* order = sh.order[cached ? t % a.k : 0];
         if (!cached) {
             if ((a.l0 + t) % a.k == arrived_dim) order = arrived;
             else local_order(column((a.l0 + t) % a.k), nc, order, sh);
         }
-        const u32 fl = (u32)full_nodes(t);
-        const int segs = 1 << t;
-        const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-        for (int i = threadIdx.x; i < kLocalWaves * segs; i += kLocalBlock) seg_count[i] = 0;
-        __syncthreads();
-        const u64 below = (1ull << lane) - 1;
-        u32 seg[kLocalItems], rank[kLocalItems];
-#pragma unroll
-        for (int j = 0; j < kLocalItems; ++j) {
-            const u32 q = (u32)local_slot(j);
-            u32 st = fl;  // fixed points (tags < F(t)) are not ranked
-            if (q < nc) st = sh.tag[order[q]];
-            const bool live = st >= fl && q < nc;
-            const u32 b = live ? st - fl : 0;
-            seg[j] = st;
-            u32 miss_lo = 0, miss_hi = 0;
-            for (int bit = 0; bit < t; ++bit) {
-                const u64 vote = __ballot((b >> bit) & 1);
-                const u32 m = (u32)((int)(b << (31 - bit)) >> 31);
-                miss_lo |= (u32)vote ^ m;
-                miss_hi |= (u32)(vote >> 32) ^ m;
-            }
-            const u64 peers = __ballot(live) & ~(((u64)miss_hi << 32) | miss_lo);
-            const u32 before = __popcll(peers & below);
-            u32 seen = 0;
-            if (live) seen = seg_count[w * segs + b];
-            rank[j] = seen + before;
-            if (live && before == 0) seg_count[w * segs + b] = (uint16_t)(seen + __popcll(peers));
-        }
-        __syncthreads();
-        for (int b = threadIdx.x; b < segs; b += kLocalBlock) {
-            u32 run = 0;
-            for (int v = 0; v < kLocalWaves; ++v) {
-                const u32 c = seg_count[v * segs + b];
-                seg_count[v * segs + b] = (uint16_t)run;
-                run += c;
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < kLocalItems; ++j) {
-            const u32 q = (u32)local_slot(j);
-            const u64 s = seg[j];
-            if (q >= nc || s < fl) continue;
-            const u64 p = segment_begin(lg, s, t) + seg_count[w * segs + (s - fl)] + rank[j];
-            const u64 pivot = segment_begin(lg, s, t) + subtree_size(lg, 2 * s + 1);
-            sh.tag[order[q]] = (uint16_t)(p < pivot ? 2 * s + 1 : (p > pivot ? 2 * s + 2 : s));
-        }
-        __syncthreads();
+        // Counters live in the exchange buffer: 16-bit while they fit, else
+        // 8-bit (then segments hold at most 3 points, see below).
+        if ((size_t)kLocalWaves * ((size_t)2 << t) <= sizeof(sh.exch))
+            local_round<uint16_t>(order, nc, t, lg, sh);
+        else
+            local_round<uint8_t>(order, nc, t, lg, sh);
     }
 
     // Level-order output of the subtree, in node order: the nodes of each
