@@ -59,7 +59,9 @@ constexpr int kItems = 16;                 // records per thread in a radix tile
 constexpr int kTile = kBlock * kItems;     // records per radix tile
 constexpr int kKeyBytes = 4;               // order-preserving coordinate key
 constexpr int kMaxTagPasses = 4;           // 32-bit tags
+constexpr int kChunkTiles = 4;             // tiles per digit-count chunk
 static_assert(kBlock == kRadix, "the tile kernels map one thread to one digit");
+static_assert(kBlock * kChunkTiles <= 1024, "one workgroup counts a whole chunk");
 
 // ------------------------------------------------------------ tree geometry
 // Level-order complete tree with N nodes ([W], indexing paragraph):
@@ -289,7 +291,9 @@ struct PassArgs {
     const u32* extra_in;       // optional second payload (nullptr: none); with
     u32* extra_out;            //   kSrcColumn it is indexed by point index
     const u32* digit_hist;     // 256 counts of this pass's digit over all records
-    u32* tile_slots;           // tiles x 256: counts, then first global slots
+    u32* tile_counts;          // tiles x 256: digit counts of each tile
+    u32* chunk_slots;          // chunks x 256: digit counts of each chunk of
+                               //   kChunkTiles tiles, then its first global slots
     Geometry geo;              // kSinkTags
     int round;                 // kSinkTags
 };
@@ -348,41 +352,86 @@ __device__ inline void wave_rank(const u32 (&key)[kItems], i64 wbase, i64 n, int
     }
 }
 
+// Keys of item j of this thread (the same record layout as load_tile).
 template <int kSrc>
-__global__ __launch_bounds__(kBlock) void k_tile_count(PassArgs a) {
-    __shared__ u32 count[kWaves][kRadix];
-    const int tid = threadIdx.x, w = tid >> 6;
-    const i64 base = (i64)blockIdx.x * kTile;
-    const i64 wbase = base + (i64)w * (64 * kItems) + (tid & 63);
-    u32 key[kItems], val[kItems], rank[kItems];
-    load_tile<kSrc>(a, wbase, key, val);
-    wave_rank(key, wbase, a.n, a.shift, count[w], rank);
-    __syncthreads();
-    u32 total = 0;
+__device__ inline void load_keys(const PassArgs& a, i64 wbase, u32 (&key)[kItems]) {
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) total += count[v][tid];
-    a.tile_slots[(u64)blockIdx.x * kRadix + tid] = total;
+    for (int j = 0; j < kItems; ++j) {
+        const i64 e = wbase + (i64)j * 64;
+        key[j] = 0;
+        if (e < a.n)
+            key[j] = kSrc == kSrcColumn ? float_key(__float_as_uint(a.col[e])) : a.keys_in[e];
+    }
 }
 
-// One workgroup per digit d: slots[t][d] = start(d) + counts of d in tiles
-// before t, where start(d) is the exclusive prefix of the digit totals. Each
-// thread scans a contiguous run of up to kScanRun tiles held in registers
-// (one batch of loads); longer inputs loop over runs.
+// Digit counts of kChunkTiles consecutive tiles: one row per tile and the
+// chunk's total. Each group of kBlock threads counts one tile (the same
+// record layout as the scatter's tiles), all tiles of the chunk at once.
+// Counting needs no ranks, only LDS atomics; each thread merges runs of
+// equal digits among its own records first, which keeps the skewed high
+// bytes of clustered keys from piling onto one counter.
+constexpr int kCountBlock = kBlock * kChunkTiles;
+template <int kSrc>
+__global__ __launch_bounds__(kCountBlock) void k_tile_count(PassArgs a) {
+    __shared__ u32 hist[kCountBlock / 64][kRadix];
+    __shared__ u32 rows[kChunkTiles][kRadix];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int g = tid / kBlock;  // tile of the chunk this thread counts
+    const int gw = w % kWaves;   // wave within that tile
+    const i64 t = (i64)blockIdx.x * kChunkTiles + g;
+    const i64 wbase = t * kTile + (i64)gw * (64 * kItems) + lane;
+    u32 key[kItems];
+    load_keys<kSrc>(a, wbase, key);
+    for (int i = lane; i < kRadix; i += 64) hist[w][i] = 0;  // this wave's own row
+    u32 last = 0, run = 0;
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+        if (wbase + (i64)j * 64 >= a.n) break;
+        const u32 d = (key[j] >> a.shift) & (kRadix - 1);
+        if (run && d != last) {
+            atomicAdd(&hist[w][last], run);
+            run = 0;
+        }
+        last = d;
+        ++run;
+    }
+    if (run) atomicAdd(&hist[w][last], run);
+    __syncthreads();
+    const int d = tid % kRadix;
+    u32 total = 0;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) total += hist[g * kWaves + v][d];
+    const i64 tiles = (a.n + kTile - 1) / kTile;
+    if (t < tiles) a.tile_counts[(u64)t * kRadix + d] = total;
+    rows[g][d] = total;
+    __syncthreads();
+    if (tid < kRadix) {
+        u32 sum = 0;
+#pragma unroll
+        for (int c = 0; c < kChunkTiles; ++c) sum += rows[c][tid];
+        a.chunk_slots[(u64)blockIdx.x * kRadix + tid] = sum;
+    }
+}
+
+// One workgroup per digit d: slots[c][d] = start(d) + counts of d in the
+// chunks before c, where start(d) is the exclusive prefix of the digit
+// totals. Each thread scans a contiguous run of up to kScanRun chunks held in
+// registers (one batch of loads); longer inputs loop over runs.
 constexpr int kScanRun = 16;
 __global__ __launch_bounds__(kBlock) void k_tile_scan(const u32* __restrict__ digit_hist,
-                                                      u32* __restrict__ slots, i64 tiles) {
+                                                      u32* __restrict__ slots, i64 chunks) {
     __shared__ u32 s_wave[kWaves];
     __shared__ u32 s_carry;
     const int tid = threadIdx.x, d = blockIdx.x;
     const u32 below = tid < d ? digit_hist[tid] : 0u;
     const u32 start = block_exclusive_scan(below, s_wave) + below;
     if (tid == kBlock - 1) s_carry = start;  // sum of the totals of digits < d
-    for (i64 t0 = 0; t0 < tiles; t0 += (i64)kBlock * kScanRun) {
+    for (i64 t0 = 0; t0 < chunks; t0 += (i64)kBlock * kScanRun) {
         const i64 mine = t0 + (i64)tid * kScanRun;
         u32 v[kScanRun], sum = 0;
 #pragma unroll
         for (int i = 0; i < kScanRun; ++i) {
-            v[i] = mine + i < tiles ? slots[(u64)(mine + i) * kRadix + d] : 0u;
+            v[i] = mine + i < chunks ? slots[(u64)(mine + i) * kRadix + d] : 0u;
             sum += v[i];
         }
         __syncthreads();  // s_carry written
@@ -391,7 +440,7 @@ __global__ __launch_bounds__(kBlock) void k_tile_scan(const u32* __restrict__ di
         if (tid == kBlock - 1) s_carry = off + sum;
 #pragma unroll
         for (int i = 0; i < kScanRun; ++i) {
-            if (mine + i < tiles) slots[(u64)(mine + i) * kRadix + d] = off;
+            if (mine + i < chunks) slots[(u64)(mine + i) * kRadix + d] = off;
             off += v[i];
         }
     }
@@ -413,9 +462,17 @@ __global__ __launch_bounds__(kBlock) void k_tile_scatter(PassArgs a) {
     const int tid = threadIdx.x, w = tid >> 6;
     const i64 base = (i64)blockIdx.x * kTile;
     const i64 wbase = base + (i64)w * (64 * kItems) + (tid & 63);
-    const u32 global_start = a.tile_slots[(u64)blockIdx.x * kRadix + tid];
     u32 key[kItems], val[kItems], rank[kItems], extra[kItems];
     load_tile<kSrc>(a, wbase, key, val);
+    // First global slot of digit tid in this tile: its chunk's slot plus the
+    // counts of the chunk's earlier tiles.
+    const i64 chunk = blockIdx.x / kChunkTiles;
+    u32 global_start = a.chunk_slots[(u64)chunk * kRadix + tid];
+#pragma unroll
+    for (int c = 0; c < kChunkTiles - 1; ++c) {
+        const i64 t = chunk * kChunkTiles + c;
+        if (t < (i64)blockIdx.x) global_start += a.tile_counts[(u64)t * kRadix + tid];
+    }
     if (kExtra) {
 #pragma unroll
         for (int j = 0; j < kItems; ++j) {
@@ -914,9 +971,9 @@ inline size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
     int kcols;          // split dimensions the global rounds can use
-    i64 tiles;
+    i64 tiles, chunks;
     size_t cols, orders, ranks, next, tagq, keys0, keys1, vals0, vals1, extra0, extra1, small,
-        slots, stage, total;
+        slots, chunk_slots, stage, total;
     // inside `small` (u32 words): column histograms, tag histograms
     int col_hist_words, tag_hist_off, small_words;
 };
@@ -933,6 +990,7 @@ bool make_layout(i64 n, int k, Layout* out) {
     // 0 .. L-2 plus the one whose order the last written tags are kept in
     lay.kcols = levels < k ? levels : k;
     lay.tiles = (n + kTile - 1) / kTile;
+    lay.chunks = (lay.tiles + kChunkTiles - 1) / kChunkTiles;
     lay.col_hist_words = lay.kcols * kKeyBytes * kRadix;
     lay.tag_hist_off = lay.col_hist_words;
     lay.small_words = lay.tag_hist_off + kMaxTagPasses * kRadix;
@@ -955,6 +1013,7 @@ bool make_layout(i64 n, int k, Layout* out) {
     lay.extra1 = take((size_t)n * sizeof(u32));
     lay.small = take((size_t)lay.small_words * sizeof(u32));
     lay.slots = take((size_t)lay.tiles * kRadix * sizeof(u32));
+    lay.chunk_slots = take((size_t)lay.chunks * kRadix * sizeof(u32));
     lay.stage = take((size_t)(k + 1) * n * sizeof(u32));
     lay.total = off;
     *out = lay;
@@ -1027,14 +1086,16 @@ struct Timer {  // no-op unless a Profiler is attached
 // Launches the three kernels of one radix pass.
 struct PassLauncher {
     const Layout& lay;
-    u32* slots;
+    u32* tile_counts;
+    u32* chunk_slots;
     hipStream_t stream;
     Timer timer;
 
     template <int kSrc, int kSink>
     void run(PassArgs a) {
-        a.tile_slots = slots;
-        const unsigned tiles = (unsigned)lay.tiles;
+        a.tile_counts = tile_counts;
+        a.chunk_slots = chunk_slots;
+        const unsigned tiles = (unsigned)lay.tiles, chunks = (unsigned)lay.chunks;
         const double n = (double)a.n;
         static const char* const count_names[2] = {"k_tile_count<0>", "k_tile_count<1>"};
         static const char* const scatter_names[2][3][2] = {
@@ -1046,10 +1107,10 @@ struct PassLauncher {
              {"k_tile_scatter<1, 2, false>", "k_tile_scatter<1, 2, true>"}}};
         const bool extra = a.extra_in != nullptr;
         timer.begin(count_names[kSrc], n * 4);  // keys (or the column)
-        k_tile_count<kSrc><<<tiles, kBlock, 0, stream>>>(a);
+        k_tile_count<kSrc><<<chunks, kCountBlock, 0, stream>>>(a);
         timer.end();
-        timer.begin("k_tile_scan", (double)lay.tiles * kRadix * 8);
-        k_tile_scan<<<kRadix, kBlock, 0, stream>>>(a.digit_hist, slots, lay.tiles);
+        timer.begin("k_tile_scan", (double)lay.chunks * kRadix * 8);
+        k_tile_scan<<<kRadix, kBlock, 0, stream>>>(a.digit_hist, chunk_slots, lay.chunks);
         timer.end();
         // in: column (4) or key+val (8); out: key+val (8) or one word (4)
         const double in = (kSrc == kSrcColumn ? 4 : 8) + (extra ? 4 : 0);
@@ -1087,9 +1148,9 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
     auto rank = [&](int d) { return (u32*)(ws + lay.ranks) + (size_t)d * n; };
     auto next = [&](int d) { return (u32*)(ws + lay.next) + (size_t)d * n; };
     auto tagq = [&](int d) { return (u32*)(ws + lay.tagq) + (size_t)d * n; };
-    PassLauncher pass{lay, (u32*)(ws + lay.slots), stream, timer};
+    PassLauncher pass{lay, (u32*)(ws + lay.slots), (u32*)(ws + lay.chunk_slots), stream, timer};
     const double N = (double)n;
-    const int grid = grid_for(n, kBlock * 4, 8192);
+    const int grid = grid_for(n, kBlock, 1 << 30);  // one element per thread: more writes in flight
 
     timer.begin("k_init", N * kc * 8);
     k_init<<<grid, kBlock, 0, stream>>>(pts, n, k, kc, cols, small, lay.small_words);
