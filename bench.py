@@ -189,7 +189,7 @@ def main():
         roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                     "kernel": dom, "avg_us": d["avg_us"], "bytes_per_launch": d["bytes_per_launch"]}
-        passes = [kk for kk in kernels if kk.startswith(("k_tile_", "k_col_hist", "k_tag_hist",
+        passes = [kk for kk in kernels if kk.startswith(("k_tile_",
                                                          "k_invert", "k_cross", "k_round0"))]
         tot_b = sum(agg[kk]["bytes"] for kk in passes)
         tot_ms = sum(agg[kk]["ms"] for kk in passes)

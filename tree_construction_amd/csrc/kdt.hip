@@ -13,17 +13,15 @@
 // updates the tags in place from the sorted positions.
 //
 // Pipeline per build (all on the caller's stream, nothing allocated):
-//   k_init       AoS points -> one column per split dimension; clears the
-//                radix bookkeeping.
-//   k_col_hist   byte histograms of each column's order-preserving keys.
+//   k_init       AoS points -> one column per split dimension.
 //   4 passes     per dimension: stable sort of (key(x_d), index) -> order_d
-//                (the points by coordinate d, then index).
+//                (the points by coordinate d, then index). Dimensions d >= 1
+//                carry rank_(d+1) as a second payload, which lands as next_d.
 //   k_invert     rank_d[order_d[r]] = r.
-//   k_cross      next_d[r] = position in order_{d+1} of the r-th point of
-//                order_d (all writes; no random reads).
+//   k_cross      next_0[r] = position in order_1 of the r-th point of
+//                order_0 (all writes; no random reads).
 //   k_round0     round 0 (all tags 0): tags straight from order_0.
 //   per round l = 1 .. l0-1, d = l mod k:
-//     k_tag_hist tag-digit histograms, from the closed-form subtree sizes.
 //     1-2 passes stable sort by tag of the records (tag, next_d) kept in
 //                order_d order; the last one computes each point's new tag
 //                and writes it where round l+1 reads it (tags are kept in
@@ -34,10 +32,12 @@
 //                that subtree's remaining rounds in LDS and writes its
 //                level-order output.
 //
-// A radix pass is reduce-then-scan: per-tile digit counts from wave64
-// ballots (multi-split ranking), a scan over tiles per digit, and a scatter
-// that re-ranks each tile and stages it in LDS so that the global writes of
-// one digit are contiguous. No workgroup ever waits on another.
+// A radix pass is reduce-then-scan: digit counts of each tile (LDS
+// atomics), a scan of the per-chunk counts per digit that also yields the
+// digit totals, and a scatter that ranks each tile (wave64 ballots, stable
+// multi-split), places it from those counts and stages it in LDS so that the
+// global writes of one digit are contiguous. No workgroup ever waits on
+// another.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -58,7 +58,6 @@ constexpr int kWaves = kBlock / 64;        // wave64
 constexpr int kItems = 16;                 // records per thread in a radix tile
 constexpr int kTile = kBlock * kItems;     // records per radix tile
 constexpr int kKeyBytes = 4;               // order-preserving coordinate key
-constexpr int kMaxTagPasses = 4;           // 32-bit tags
 constexpr int kChunkTiles = 4;             // tiles per digit-count chunk
 static_assert(kBlock == kRadix, "the tile kernels map one thread to one digit");
 static_assert(kBlock * kChunkTiles <= 1024, "one workgroup counts a whole chunk");
@@ -146,82 +145,44 @@ __device__ inline u32 block_exclusive_scan(u32 v, u32* s_wave) {
     return off + inc - v;
 }
 
+__device__ inline u64 wave_inclusive_scan64(u64 v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        u64 t = __shfl_up(v, o, 64);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+// Exclusive scan of one 64-bit value per thread across the workgroup (used
+// for two 32-bit scans at once whose sums cannot carry out of 32 bits).
+__device__ inline u64 block_exclusive_scan64(u64 v, u64* s_wave) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    u64 inc = wave_inclusive_scan64(v);
+    if (lane == 63) s_wave[w] = inc;
+    __syncthreads();
+    u64 off = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i)
+        if (i < w) off += s_wave[i];
+    __syncthreads();
+    return off + inc - v;
+}
+
 // Radix passes over the tag in round l: tags there are < F(l+1) = 2^(l+1) - 1.
 __host__ __device__ inline int tag_passes(int l) { return (l + 1 + kRadixBits - 1) / kRadixBits; }
 
 // ------------------------------------------------------ global-phase kernels
 
-// Column copy of the split dimensions; clears the column histograms (a
-// kernel rather than a memset node, so the sequence can be captured into a
-// graph).
+// Column copy of the split dimensions.
 __global__ __launch_bounds__(kBlock) void k_init(const float* __restrict__ pts, i64 n, int k,
-                                                 int kcols, float* __restrict__ cols,
-                                                 u32* __restrict__ small, int small_words) {
+                                                 int kcols, float* __restrict__ cols) {
     const i64 stride = (i64)gridDim.x * kBlock;
     for (i64 e = (i64)blockIdx.x * kBlock + threadIdx.x; e < n; e += stride) {
         const float* row = pts + e * k;
         for (int d = 0; d < kcols; ++d) cols[(i64)d * n + e] = row[d];
     }
-    if (blockIdx.x == 0)
-        for (int i = threadIdx.x; i < small_words; i += kBlock) small[i] = 0;
-}
-
-// Histograms of the four bytes of key(x) over one column. Each thread
-// counts runs of equal digits before touching LDS, which keeps the heavily
-// skewed high bytes (exponents of clustered data) off a single LDS bank.
-__global__ __launch_bounds__(kBlock) void k_col_hist(const float* __restrict__ col, i64 n,
-                                                     u32* __restrict__ hist) {
-    __shared__ u32 h[kWaves][kKeyBytes][kRadix];
-    const int w = threadIdx.x >> 6;
-    for (int i = threadIdx.x; i < kWaves * kKeyBytes * kRadix; i += kBlock) (&h[0][0][0])[i] = 0;
-    __syncthreads();
-    u32 last[kKeyBytes], run[kKeyBytes];
-#pragma unroll
-    for (int b = 0; b < kKeyBytes; ++b) {
-        last[b] = 0;
-        run[b] = 0;
-    }
-    const i64 stride = (i64)gridDim.x * kBlock;
-    for (i64 e = (i64)blockIdx.x * kBlock + threadIdx.x; e < n; e += stride) {
-        const u32 key = float_key(__float_as_uint(col[e]));
-#pragma unroll
-        for (int b = 0; b < kKeyBytes; ++b) {
-            const u32 d = (key >> (8 * b)) & (kRadix - 1);
-            if (run[b] && d != last[b]) {
-                atomicAdd(&h[w][b][last[b]], run[b]);
-                run[b] = 0;
-            }
-            last[b] = d;
-            ++run[b];
-        }
-    }
-#pragma unroll
-    for (int b = 0; b < kKeyBytes; ++b)
-        if (run[b]) atomicAdd(&h[w][b][last[b]], run[b]);
-    __syncthreads();
-    for (int i = threadIdx.x; i < kKeyBytes * kRadix; i += kBlock) {
-        u32 s = 0;
-        for (int v = 0; v < kWaves; ++v) s += (&h[v][0][0])[i];
-        if (s) atomicAdd(&hist[i], s);
-    }
-}
-
-// Byte histograms of the tags in round l without reading any point: F(l)
-// fixed nodes hold one point each and live subtree s holds |S(s)| points.
-// One workgroup; overwrites hist[0 .. passes*256).
-__global__ __launch_bounds__(kBlock) void k_tag_hist(Geometry geo, int l, int passes,
-                                                     u32* __restrict__ hist) {
-    __shared__ u32 h[kMaxTagPasses][kRadix];
-    for (int i = threadIdx.x; i < kMaxTagPasses * kRadix; i += kBlock) (&h[0][0])[i] = 0;
-    __syncthreads();
-    const u64 fixed = full_nodes(l), end = full_nodes(l + 1);
-    for (u64 t = threadIdx.x; t < end; t += kBlock) {
-        const u64 c = t < fixed ? 1 : subtree_size(geo, t);
-        if (c == 0) continue;
-        for (int b = 0; b < passes; ++b) atomicAdd(&h[b][(t >> (8 * b)) & (kRadix - 1)], (u32)c);
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < passes * kRadix; i += kBlock) hist[i] = (&h[0][0])[i];
 }
 
 // rank[order[r]] = r: where each point sits in order_d.
@@ -290,10 +251,11 @@ struct PassArgs {
     u32* tag_out;              // kSinkTags: tag_out[val] = the record's new tag
     const u32* extra_in;       // optional second payload (nullptr: none); with
     u32* extra_out;            //   kSrcColumn it is indexed by point index
-    const u32* digit_hist;     // 256 counts of this pass's digit over all records
+    u32* digit_totals;         // 256 counts of this pass's digit over all records
     u32* tile_counts;          // tiles x 256: digit counts of each tile
     u32* chunk_slots;          // chunks x 256: digit counts of each chunk of
-                               //   kChunkTiles tiles, then its first global slots
+                               //   kChunkTiles tiles, then the counts of the
+                               //   digit in the chunks before it
     Geometry geo;              // kSinkTags
     int round;                 // kSinkTags
 };
@@ -413,19 +375,17 @@ __global__ __launch_bounds__(kCountBlock) void k_tile_count(PassArgs a) {
     }
 }
 
-// One workgroup per digit d: slots[c][d] = start(d) + counts of d in the
-// chunks before c, where start(d) is the exclusive prefix of the digit
-// totals. Each thread scans a contiguous run of up to kScanRun chunks held in
-// registers (one batch of loads); longer inputs loop over runs.
+// One workgroup per digit d: slots[c][d] = counts of d in the chunks before
+// c; totals[d] = all counts of d. Each thread scans a contiguous run of up
+// to kScanRun chunks held in registers (one batch of loads); longer inputs
+// loop over runs.
 constexpr int kScanRun = 16;
-__global__ __launch_bounds__(kBlock) void k_tile_scan(const u32* __restrict__ digit_hist,
-                                                      u32* __restrict__ slots, i64 chunks) {
+__global__ __launch_bounds__(kBlock) void k_tile_scan(u32* __restrict__ slots, i64 chunks,
+                                                      u32* __restrict__ totals) {
     __shared__ u32 s_wave[kWaves];
     __shared__ u32 s_carry;
     const int tid = threadIdx.x, d = blockIdx.x;
-    const u32 below = tid < d ? digit_hist[tid] : 0u;
-    const u32 start = block_exclusive_scan(below, s_wave) + below;
-    if (tid == kBlock - 1) s_carry = start;  // sum of the totals of digits < d
+    if (tid == kBlock - 1) s_carry = 0;
     for (i64 t0 = 0; t0 < chunks; t0 += (i64)kBlock * kScanRun) {
         const i64 mine = t0 + (i64)tid * kScanRun;
         u32 v[kScanRun], sum = 0;
@@ -444,6 +404,8 @@ __global__ __launch_bounds__(kBlock) void k_tile_scan(const u32* __restrict__ di
             off += v[i];
         }
     }
+    __syncthreads();
+    if (tid == 0) totals[d] = s_carry;
 }
 
 template <int kSrc, int kSink, bool kExtra>
@@ -457,15 +419,17 @@ __global__ __launch_bounds__(kBlock) void k_tile_scatter(PassArgs a) {
     __shared__ u8 s_digit[kTile];
     __shared__ u32 s_local[kRadix];  // first tile-local slot of each digit
     __shared__ u32 s_base[kRadix];   // global slot of tile-local slot 0 of each digit
-    __shared__ u32 s_wave[kWaves];
+    __shared__ u64 s_wave[kWaves];
 
     const int tid = threadIdx.x, w = tid >> 6;
     const i64 base = (i64)blockIdx.x * kTile;
     const i64 wbase = base + (i64)w * (64 * kItems) + (tid & 63);
     u32 key[kItems], val[kItems], rank[kItems], extra[kItems];
     load_tile<kSrc>(a, wbase, key, val);
-    // First global slot of digit tid in this tile: its chunk's slot plus the
-    // counts of the chunk's earlier tiles.
+    // First global slot of digit tid in this tile: where the digit starts in
+    // the output, plus its counts in earlier chunks and in the chunk's
+    // earlier tiles.
+    const u32 digit_total = a.digit_totals[tid];
     const i64 chunk = blockIdx.x / kChunkTiles;
     u32 global_start = a.chunk_slots[(u64)chunk * kRadix + tid];
 #pragma unroll
@@ -491,7 +455,11 @@ __global__ __launch_bounds__(kBlock) void k_tile_scatter(PassArgs a) {
         sm.count[v][tid] = agg;
         agg += c;
     }
-    const u32 local_start = block_exclusive_scan(agg, s_wave);
+    // Both exclusive scans at once: digit totals (high word) and the tile's
+    // digit counts (low word, at most kTile in all).
+    const u64 starts = block_exclusive_scan64(((u64)digit_total << 32) | agg, s_wave);
+    const u32 local_start = (u32)starts;
+    global_start += (u32)(starts >> 32);
     s_local[tid] = local_start;
     s_base[tid] = global_start - local_start;  // modular; base + slot < n
 
@@ -598,6 +566,7 @@ constexpr int kLocalWaves = kLocalBlock / 64;
 constexpr int kLocalItems = 8;                        // records per thread
 constexpr int kLocalMax = kLocalBlock * kLocalItems;  // points per subtree
 constexpr int kCachedDims = 3;                        // sorted orders kept in LDS
+constexpr int kRowRegs = 4;                           // row loads batched up to this k
 static_assert(kLocalBlock >= kRadix, "one thread per digit");
 
 struct LocalShared {
@@ -860,16 +829,39 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
     // Stage the subtree's points once, by index rank: their indices and their
     // coordinate columns (each row of `points` is read exactly once here).
     u32* stage_idx = a.stage + first;
+    if (a.k <= kRowRegs) {
+        // All of this thread's row loads are issued before the first store.
+        u32 row[kLocalItems][kRowRegs];
 #pragma unroll
-    for (int j = 0; j < kLocalItems; ++j) {
-        const int e = local_slot(j);
-        if ((u32)e >= nc) continue;
-        const u32 i = (u32)(rec[j] >> 16);
-        stage_idx[e] = i;
-        const float* row = a.pts + (i64)i * a.k;
-        for (int d = 0; d < a.k; ++d)
-            a.stage[(u64)(d + 1) * a.n + first + e] = __float_as_uint(row[d]);
-        sh.tag[e] = 0;
+        for (int j = 0; j < kLocalItems; ++j) {
+            const u32 i = (u32)(rec[j] >> 16);
+            const bool ok = (u32)local_slot(j) < nc;
+#pragma unroll
+            for (int d = 0; d < kRowRegs; ++d)
+                row[j][d] = ok && d < a.k ? __float_as_uint(a.pts[(i64)i * a.k + d]) : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < kLocalItems; ++j) {
+            const int e = local_slot(j);
+            if ((u32)e >= nc) continue;
+            stage_idx[e] = (u32)(rec[j] >> 16);
+#pragma unroll
+            for (int d = 0; d < kRowRegs; ++d)
+                if (d < a.k) a.stage[(u64)(d + 1) * a.n + first + e] = row[j][d];
+            sh.tag[e] = 0;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kLocalItems; ++j) {
+            const int e = local_slot(j);
+            if ((u32)e >= nc) continue;
+            const u32 i = (u32)(rec[j] >> 16);
+            stage_idx[e] = i;
+            const float* row = a.pts + (i64)i * a.k;
+            for (int d = 0; d < a.k; ++d)
+                a.stage[(u64)(d + 1) * a.n + first + e] = __float_as_uint(row[d]);
+            sh.tag[e] = 0;
+        }
     }
     auto column = [&](int d) { return a.stage + (u64)(d + 1) * a.n + first; };
 
@@ -924,9 +916,19 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
         const u64 g = ((c + 1) << lvl) - 1 + (node - full_nodes(lvl));
         if (g >= (u64)a.n) continue;  // cannot happen: local nodes map inside the tree
         a.perm[g] = (int32_t)stage_idx[e];
-        if (a.tree)
+        if (!a.tree) continue;
+        if (a.k <= kRowRegs) {
+            u32 row[kRowRegs];
+#pragma unroll
+            for (int d = 0; d < kRowRegs; ++d)
+                row[d] = d < a.k ? a.stage[(u64)(d + 1) * a.n + first + e] : 0u;
+#pragma unroll
+            for (int d = 0; d < kRowRegs; ++d)
+                if (d < a.k) a.tree[(i64)g * a.k + d] = __uint_as_float(row[d]);
+        } else {
             for (int d = 0; d < a.k; ++d)
                 a.tree[(i64)g * a.k + d] = __uint_as_float(a.stage[(u64)(d + 1) * a.n + first + e]);
+        }
     }
 }
 
@@ -972,10 +974,8 @@ inline size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 struct Layout {
     int kcols;          // split dimensions the global rounds can use
     i64 tiles, chunks;
-    size_t cols, orders, ranks, next, tagq, keys0, keys1, vals0, vals1, extra0, extra1, small,
+    size_t cols, orders, ranks, next, tagq, keys0, keys1, vals0, vals1, extra0, extra1, totals,
         slots, chunk_slots, stage, total;
-    // inside `small` (u32 words): column histograms, tag histograms
-    int col_hist_words, tag_hist_off, small_words;
 };
 
 bool make_layout(i64 n, int k, Layout* out) {
@@ -991,9 +991,6 @@ bool make_layout(i64 n, int k, Layout* out) {
     lay.kcols = levels < k ? levels : k;
     lay.tiles = (n + kTile - 1) / kTile;
     lay.chunks = (lay.tiles + kChunkTiles - 1) / kChunkTiles;
-    lay.col_hist_words = lay.kcols * kKeyBytes * kRadix;
-    lay.tag_hist_off = lay.col_hist_words;
-    lay.small_words = lay.tag_hist_off + kMaxTagPasses * kRadix;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t at = off;
@@ -1011,7 +1008,7 @@ bool make_layout(i64 n, int k, Layout* out) {
     lay.vals1 = take((size_t)n * sizeof(u32));
     lay.extra0 = take((size_t)n * sizeof(u32));
     lay.extra1 = take((size_t)n * sizeof(u32));
-    lay.small = take((size_t)lay.small_words * sizeof(u32));
+    lay.totals = take((size_t)kRadix * sizeof(u32));
     lay.slots = take((size_t)lay.tiles * kRadix * sizeof(u32));
     lay.chunk_slots = take((size_t)lay.chunks * kRadix * sizeof(u32));
     lay.stage = take((size_t)(k + 1) * n * sizeof(u32));
@@ -1110,7 +1107,7 @@ struct PassLauncher {
         k_tile_count<kSrc><<<chunks, kCountBlock, 0, stream>>>(a);
         timer.end();
         timer.begin("k_tile_scan", (double)lay.chunks * kRadix * 8);
-        k_tile_scan<<<kRadix, kBlock, 0, stream>>>(a.digit_hist, chunk_slots, lay.chunks);
+        k_tile_scan<<<kRadix, kBlock, 0, stream>>>(chunk_slots, lay.chunks, a.digit_totals);
         timer.end();
         // in: column (4) or key+val (8); out: key+val (8) or one word (4)
         const double in = (kSrc == kSrcColumn ? 4 : 8) + (extra ? 4 : 0);
@@ -1139,9 +1136,7 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
     const int span = writes + 1 > rounds ? writes + 1 : rounds;
     const int kc = span < k ? span : k;
     float* cols = (float*)(ws + lay.cols);
-    u32* small = (u32*)(ws + lay.small);
-    u32* col_hist = small;
-    u32* tag_hist = small + lay.tag_hist_off;
+    u32* totals = (u32*)(ws + lay.totals);
     u32* keys[2] = {(u32*)(ws + lay.keys0), (u32*)(ws + lay.keys1)};
     u32* vals[2] = {(u32*)(ws + lay.vals0), (u32*)(ws + lay.vals1)};
     auto order = [&](int d) { return (u32*)(ws + lay.orders) + (size_t)d * n; };
@@ -1153,7 +1148,7 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
     const int grid = grid_for(n, kBlock, 1 << 30);  // one element per thread: more writes in flight
 
     timer.begin("k_init", N * kc * 8);
-    k_init<<<grid, kBlock, 0, stream>>>(pts, n, k, kc, cols, small, lay.small_words);
+    k_init<<<grid, kBlock, 0, stream>>>(pts, n, k, kc, cols);
     timer.end();
 
     // next_d maps the r-th point of order_d to its position in order_(d+1):
@@ -1167,11 +1162,7 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
     for (int step = 0; step < kc; ++step) {
         const int d = step == 0 ? 0 : kc - step;
         const float* col = cols + (size_t)d * n;
-        u32* hist = col_hist + (size_t)d * kKeyBytes * kRadix;
         const bool carry = d >= 1 && d < knext;
-        timer.begin("k_col_hist", N * 4);
-        k_col_hist<<<grid_for(n, kBlock * 16, 2048), kBlock, 0, stream>>>(col, n, hist);
-        timer.end();
         // Presort: order_d = point indices by (coordinate d, index). Pass p
         // reads buffer (p+1)&1 and writes buffer p&1; the last writes order_d.
         for (int p = 0; p < kKeyBytes; ++p) {
@@ -1187,7 +1178,7 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
                 a.extra_in = p == 0 ? rank((d + 1) % k) : extra[(p + 1) & 1];
                 a.extra_out = p == kKeyBytes - 1 ? next(d) : extra[p & 1];
             }
-            a.digit_hist = hist + p * kRadix;
+            a.digit_totals = totals;
             if (p == 0)
                 pass.run<kSrcColumn, kSinkArrays>(a);
             else if (p < kKeyBytes - 1)
@@ -1223,14 +1214,11 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
         const int d = l % k;
         const int passes = tag_passes(l);
         const bool final = keep_sorted && l == rounds - 1;
-        timer.begin("k_tag_hist", 0);
-        k_tag_hist<<<1, kBlock, 0, stream>>>(geo, l, passes, tag_hist);
-        timer.end();
         for (int p = 0; p < passes; ++p) {
             PassArgs a{};
             a.n = n;
             a.shift = 8 * p;
-            a.digit_hist = tag_hist + p * kRadix;
+            a.digit_totals = totals;
             a.geo = geo;
             a.round = l;
             a.keys_in = p == 0 ? tagq(d) : keys[p & 1];
