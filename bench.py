@@ -198,7 +198,7 @@ def main():
             "frac": round(tot_b / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "ms_per_build": round(tot_ms / args.steps, 4)}
         for kind, kv in sorted(kernels.items(), key=lambda kv: -kv[1]["ms_per_build"]):
-            log("  %-22s %4d/build  avg %8.2f us  %8.1f GB/s  %.3f ms/build"
+            log("  %-36s %4d/build  avg %8.2f us  %8.1f GB/s  %.3f ms/build"
                 % (kind, kv["launches_per_build"], kv["avg_us"], kv["GBps"], kv["ms_per_build"]))
         if not args.no_counters:
             log("bench: rocprofv3 FETCH_SIZE / WRITE_SIZE runs for %s" % dom)

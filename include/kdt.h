@@ -117,8 +117,9 @@ int64_t kdt_closed_segment_begin(int64_t N, int64_t s, int32_t l);
 
 /* Number of 8-bit radix passes over the tag that round l (the round that
  * fixes level l) runs on top of the cached per-dimension coordinate order:
- * ceil((l+1)/8), and 0 for round 0 whose tags are all zero. -1 when l is out
- * of range for N. */
+ * only the 2^l live tags F(l) .. F(l+1)-1 are sorted, by their l-bit offset
+ * from F(l), so ceil(l/8); 0 for round 0 whose tags are all zero. -1 when l
+ * is out of range for N. */
 int32_t kdt_round_passes(int64_t N, int32_t l);
 
 /* Static description of a status code. */

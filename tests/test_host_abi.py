@@ -64,9 +64,9 @@ def test_round_passes():
     assert kdt.round_passes(1, 0) == -1
     assert kdt.round_passes(2, 0) == 0
     assert kdt.round_passes(2, 1) == -1
-    n = 1 << 24  # 25 levels, 24 rounds; tags of round l have l+1 bits
+    n = 1 << 24  # 25 levels, 24 rounds; round l sorts 2^l live tags (l offset bits)
     got = [kdt.round_passes(n, l) for l in range(24)]
-    assert got == [0] + [1] * 7 + [2] * 8 + [3] * 8
+    assert got == [0] + [1] * 8 + [2] * 8 + [3] * 7
 
 
 def test_workspace_size():

@@ -170,8 +170,9 @@ __device__ inline u64 block_exclusive_scan64(u64 v, u64* s_wave) {
     return off + inc - v;
 }
 
-// Radix passes over the tag in round l: tags there are < F(l+1) = 2^(l+1) - 1.
-__host__ __device__ inline int tag_passes(int l) { return (l + 1 + kRadixBits - 1) / kRadixBits; }
+// Radix passes over the tag in round l >= 1: only the 2^l live tags
+// F(l) .. F(l+1)-1 are sorted, by their offset from F(l) (l bits).
+__host__ __device__ inline int tag_passes(int l) { return (l + kRadixBits - 1) / kRadixBits; }
 
 // ------------------------------------------------------ global-phase kernels
 
@@ -241,8 +242,11 @@ enum Sink { kSinkArrays = 0, kSinkVals = 1, kSinkTags = 2 };
 //                 first slot -> the first global slot of (tile, digit),
 //   k_tile_scatter rank each tile again and move its records there.
 struct PassArgs {
-    i64 n;
-    int shift;                 // digit = (key >> shift) & 255
+    i64 n;                     // records of this pass
+    i64 n_all;                 // points (bound of tag_out and fixed_*)
+    int shift;                 // digit = ((key - key_base) >> shift) & 255
+    u32 key_base;              // records with key < key_base are fixed: they
+                               //   are not sorted and go to a fixed_* array
     const float* col;          // kSrcColumn: key = key(col[i]), val = i
     const u32* keys_in;        // kSrcArrays
     const u32* vals_in;        // kSrcArrays
@@ -256,6 +260,9 @@ struct PassArgs {
     u32* chunk_slots;          // chunks x 256: digit counts of each chunk of
                                //   kChunkTiles tiles, then the counts of the
                                //   digit in the chunks before it
+    u32* fixed_tags;           // fixed record: fixed_tags[val] = key (its tag)
+    u32* fixed_vals;           // fixed record: fixed_vals[key] = val (node key
+                               //   sits at sorted position key)
     Geometry geo;              // kSinkTags
     int round;                 // kSinkTags
 };
@@ -287,7 +294,10 @@ __device__ inline void load_tile(const PassArgs& a, i64 wbase, u32 (&key)[kItems
 // ballots (a lane's peers are the lanes that never disagree with it on a
 // bit: the OR over bits of vote ^ own-bit-mask, inverted); the lowest such
 // lane bumps the wave's counter for the digit. rank[j] = records of the
-// same digit earlier in the wave's rows.
+// same digit earlier in the wave's rows. Records past the end, and with
+// kTags those whose key (an offset from F(l)) wrapped below zero (fixed
+// points), are not ranked.
+template <bool kTags>
 __device__ inline void wave_rank(const u32 (&key)[kItems], i64 wbase, i64 n, int shift,
                                  u32* count, u32 (&rank)[kItems]) {
     const int lane = threadIdx.x & 63;
@@ -295,7 +305,7 @@ __device__ inline void wave_rank(const u32 (&key)[kItems], i64 wbase, i64 n, int
     const u64 below = (1ull << lane) - 1;
 #pragma unroll
     for (int j = 0; j < kItems; ++j) {
-        const bool valid = (wbase + (i64)j * 64) < n;
+        const bool valid = (wbase + (i64)j * 64) < n && (!kTags || (int)key[j] >= 0);
         const u32 d = (key[j] >> shift) & (kRadix - 1);
         u32 miss_lo = 0, miss_hi = 0;
 #pragma unroll
@@ -327,7 +337,7 @@ __device__ inline void load_keys(const PassArgs& a, i64 wbase, u32 (&key)[kItems
 }
 
 // Digit counts of kChunkTiles consecutive tiles: one row per tile and the
-// chunk's total. Each group of kBlock threads counts one tile (the same
+// chunk's total (fixed records are not counted). Each group of kBlock threads counts one tile (the same
 // record layout as the scatter's tiles), all tiles of the chunk at once.
 // Counting needs no ranks, only LDS atomics; each thread merges runs of
 // equal digits among its own records first, which keeps the skewed high
@@ -349,7 +359,8 @@ __global__ __launch_bounds__(kCountBlock) void k_tile_count(PassArgs a) {
 #pragma unroll
     for (int j = 0; j < kItems; ++j) {
         if (wbase + (i64)j * 64 >= a.n) break;
-        const u32 d = (key[j] >> a.shift) & (kRadix - 1);
+        if (key[j] < a.key_base) continue;  // fixed: not sorted
+        const u32 d = ((key[j] - a.key_base) >> a.shift) & (kRadix - 1);
         if (run && d != last) {
             atomicAdd(&hist[w][last], run);
             run = 0;
@@ -408,7 +419,8 @@ __global__ __launch_bounds__(kBlock) void k_tile_scan(u32* __restrict__ slots, i
     if (tid == 0) totals[d] = s_carry;
 }
 
-template <int kSrc, int kSink, bool kExtra>
+// kTags: a tag pass, whose records below key_base are fixed (not sorted).
+template <int kSrc, int kSink, bool kExtra, bool kTags>
 __global__ __launch_bounds__(kBlock) void k_tile_scatter(PassArgs a) {
     __shared__ union {
         u32 count[kWaves][kRadix];  // ranking: per-wave digit counts, then prefixes
@@ -420,6 +432,7 @@ __global__ __launch_bounds__(kBlock) void k_tile_scatter(PassArgs a) {
     __shared__ u32 s_local[kRadix];  // first tile-local slot of each digit
     __shared__ u32 s_base[kRadix];   // global slot of tile-local slot 0 of each digit
     __shared__ u64 s_wave[kWaves];
+    __shared__ u32 s_live;           // records of the tile that are sorted
 
     const int tid = threadIdx.x, w = tid >> 6;
     const i64 base = (i64)blockIdx.x * kTile;
@@ -444,7 +457,25 @@ __global__ __launch_bounds__(kBlock) void k_tile_scatter(PassArgs a) {
             extra[j] = e < a.n ? a.extra_in[e] : 0u;
         }
     }
-    wave_rank(key, wbase, a.n, a.shift, sm.count[w], rank);
+    // Tag passes work on the offset of the tag from F(l): live tags map to
+    // 0 .. 2^l - 1 and fixed ones wrap to values >= 2^31.
+    const u32 kbase = kTags ? a.key_base : 0u;
+    if (kTags) {
+#pragma unroll
+        for (int j = 0; j < kItems; ++j) {
+            key[j] -= kbase;
+            if ((wbase + (i64)j * 64) >= a.n || (int)key[j] >= 0) continue;
+            // A fixed record goes straight to its final place: its tag for
+            // the next round, or its node's slot of the sorted order.
+            const u32 s = key[j] + kbase;  // the fixed node's id
+            if (a.fixed_tags) {
+                if (val[j] < (u64)a.n_all) a.fixed_tags[val[j]] = s;
+            } else if (a.fixed_vals) {
+                if (s < (u64)a.n_all) a.fixed_vals[s] = val[j];
+            }
+        }
+    }
+    wave_rank<kTags>(key, wbase, a.n, a.shift, sm.count[w], rank);
     __syncthreads();
 
     // Thread tid owns digit tid: per-wave prefixes and the tile total.
@@ -462,46 +493,48 @@ __global__ __launch_bounds__(kBlock) void k_tile_scatter(PassArgs a) {
     global_start += (u32)(starts >> 32);
     s_local[tid] = local_start;
     s_base[tid] = global_start - local_start;  // modular; base + slot < n
+    if (tid == kBlock - 1) s_live = local_start + agg;
 
-    u32 digit[kItems];
+    // (recomputed where needed rather than held in registers)
+    auto live = [&](int j) { return (wbase + (i64)j * 64) < a.n && (!kTags || (int)key[j] >= 0); };
+    auto digit = [&](int j) { return (key[j] >> a.shift) & (kRadix - 1); };
 #pragma unroll
-    for (int j = 0; j < kItems; ++j) {
-        digit[j] = (key[j] >> a.shift) & (kRadix - 1);
-        if ((wbase + (i64)j * 64) < a.n) rank[j] += sm.count[w][digit[j]];
-    }
-    __syncthreads();
+    for (int j = 0; j < kItems; ++j)
+        if (live(j)) rank[j] += sm.count[w][digit(j)];
+    __syncthreads();  // s_local written
 
     if (kSink == kSinkTags) {
         // Tag update ([W], tag and sort-order paragraphs): a point of subtree
         // s (s on level l, so s >= F(l)) at sorted position p moves to the
         // left child if p is before the pivot, to the right child if after,
         // and stays as node s if it is the pivot; pivot = start of s's
-        // segment + size of the left subtree. Tags < F(l) are final and are
-        // carried over unchanged.
-        const u64 fl = full_nodes(a.round);
+        // segment + size of the left subtree. Tags < F(l) are final (carried
+        // over above). Those F(l) fixed points sort first, one per node id,
+        // so the live ones, ranked here, start at position F(l).
 #pragma unroll
         for (int j = 0; j < kItems; ++j) {
-            if ((wbase + (i64)j * 64) >= a.n) continue;
-            const u64 s = key[j];
-            u64 t = s;
-            if (s >= fl) {
-                const u64 p = (u64)(s_base[digit[j]] + s_local[digit[j]] + rank[j]);
-                const u64 pivot = segment_begin(a.geo, s, a.round) + subtree_size(a.geo, 2 * s + 1);
-                t = p < pivot ? 2 * s + 1 : (p > pivot ? 2 * s + 2 : s);
-            }
-            if (val[j] < (u64)a.n) a.tag_out[val[j]] = (u32)t;
+            if (!live(j)) continue;  // fixed ones are written already
+            const u64 s = (u32)(key[j] + kbase);
+            const u32 d = digit(j);
+            const u64 p = (u64)kbase + (u32)(s_base[d] + s_local[d] + rank[j]);
+            const u64 pivot = segment_begin(a.geo, s, a.round) + subtree_size(a.geo, 2 * s + 1);
+            const u64 t = p < pivot ? 2 * s + 1 : (p > pivot ? 2 * s + 2 : s);
+            if (val[j] < (u64)a.n_all) a.tag_out[val[j]] = (u32)t;
         }
         return;
     }
 
-    const int valid_here = (int)((a.n - base) < kTile ? (a.n - base) : kTile);
+    const int valid_here = (int)s_live;
+    // rank[j] becomes the record's slot in the tile's sorted order.
+#pragma unroll
+    for (int j = 0; j < kItems; ++j)
+        if (live(j)) rank[j] += s_local[digit(j)];
     if (kSink == kSinkArrays) {
 #pragma unroll
         for (int j = 0; j < kItems; ++j) {
-            if ((wbase + (i64)j * 64) >= a.n) continue;
-            const u32 slot = s_local[digit[j]] + rank[j];
-            sm.keys[slot] = key[j];
-            s_digit[slot] = (u8)digit[j];
+            if (!live(j)) continue;
+            sm.keys[rank[j]] = key[j] + kbase;
+            s_digit[rank[j]] = (u8)digit(j);
         }
         __syncthreads();
         for (int i = tid; i < valid_here; i += kBlock) {
@@ -515,11 +548,10 @@ __global__ __launch_bounds__(kBlock) void k_tile_scatter(PassArgs a) {
     constexpr bool kPairs = kExtra && kSink == kSinkVals;
 #pragma unroll
     for (int j = 0; j < kItems; ++j) {
-        if ((wbase + (i64)j * 64) >= a.n) continue;
-        const u32 slot = s_local[digit[j]] + rank[j];
-        if (kPairs) sm.pairs[slot] = ((u64)extra[j] << 32) | val[j];
-        else sm.vals[slot] = val[j];
-        if (kSink == kSinkVals) s_digit[slot] = (u8)digit[j];
+        if (!live(j)) continue;
+        if (kPairs) sm.pairs[rank[j]] = ((u64)extra[j] << 32) | val[j];
+        else sm.vals[rank[j]] = val[j];
+        if (kSink == kSinkVals) s_digit[rank[j]] = (u8)digit(j);
     }
     __syncthreads();
     for (int i = tid; i < valid_here; i += kBlock) {
@@ -537,8 +569,8 @@ __global__ __launch_bounds__(kBlock) void k_tile_scatter(PassArgs a) {
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < kItems; ++j) {
-            if ((wbase + (i64)j * 64) >= a.n) continue;
-            sm.vals[s_local[digit[j]] + rank[j]] = extra[j];
+            if (!live(j)) continue;
+            sm.vals[rank[j]] = extra[j];
         }
         __syncthreads();
         for (int i = tid; i < valid_here; i += kBlock) {
@@ -567,17 +599,23 @@ constexpr int kLocalItems = 8;                        // records per thread
 constexpr int kLocalMax = kLocalBlock * kLocalItems;  // points per subtree
 constexpr int kCachedDims = 3;                        // sorted orders kept in LDS
 constexpr int kRowRegs = 4;                           // row loads batched up to this k
+constexpr int kRowBatch = 4;                          // items whose rows load together
 static_assert(kLocalBlock >= kRadix, "one thread per digit");
 
 struct LocalShared {
-    u64 exch[kLocalMax];                  // record exchange of the radix passes
-    u32 count[kLocalWaves][kRadix];       // per-wave digit counters, then prefixes
+    u32 exch[kLocalMax];                  // record exchange of the radix passes
+    uint16_t count[kLocalWaves][kRadix];  // per-wave digit counters, then prefixes
     u32 start[kRadix];                    // first slot of each digit
     u32 wave[kLocalWaves];
     u64 reduce[2][kLocalWaves];           // AND / OR of the keys, per wave
     uint16_t tag[kLocalMax];              // local tag of each point (by index rank)
     uint16_t order[kCachedDims][kLocalMax];  // points sorted by (coordinate, index)
 };
+
+// The tag rounds keep per-wave segment counters in the exchange buffer: at
+// local level t there are 2^t segments, t <= 11 for kLocalMax points, and
+// 8-bit counters for 2048 segments must fit.
+static_assert(kLocalWaves * (kLocalMax / 2) <= sizeof(LocalShared::exch), "round counters");
 
 // Slot of item j of this thread: each wave owns kLocalItems rows of 64.
 __device__ inline int local_slot(int j) {
@@ -678,15 +716,27 @@ __device__ void local_pass(u64 (&rec)[kLocalItems], int shift, LocalShared& sh) 
         sh.start[tid] = off + inc - agg;
     }
     __syncthreads();
+    // A record is a 32-bit key above a 16-bit slot (bits 16..47; all-ones
+    // records read back as 48 one bits, still behind every real record): it
+    // moves in two exchanges, which keeps the buffer at 4 bytes a record.
 #pragma unroll
     for (int j = 0; j < kLocalItems; ++j) {
         const u32 d = (u32)(rec[j] >> shift) & (kRadix - 1);
-        sh.exch[sh.start[d] + sh.count[w][d] + rank[j]] = rec[j];
+        rank[j] += sh.start[d] + sh.count[w][d];
+        sh.exch[rank[j]] = (u32)(rec[j] >> 16);
     }
+    __syncthreads();
+    u32 hi[kLocalItems];
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) hi[j] = sh.exch[local_slot(j)];
+    __syncthreads();
+    uint16_t* exch16 = reinterpret_cast<uint16_t*>(sh.exch);
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) exch16[rank[j]] = (uint16_t)rec[j];
     __syncthreads();
     // The next pass's first barrier orders these reads before its writes.
 #pragma unroll
-    for (int j = 0; j < kLocalItems; ++j) rec[j] = sh.exch[local_slot(j)];
+    for (int j = 0; j < kLocalItems; ++j) rec[j] = ((u64)hi[j] << 16) | exch16[local_slot(j)];
 }
 
 // Stable sort of the records by bits [lo, lo + 8*bytes), skipping bytes on
@@ -830,25 +880,28 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
     // coordinate columns (each row of `points` is read exactly once here).
     u32* stage_idx = a.stage + first;
     if (a.k <= kRowRegs) {
-        // All of this thread's row loads are issued before the first store.
-        u32 row[kLocalItems][kRowRegs];
+        // Row loads are issued kRowBatch items at a time, before their stores.
 #pragma unroll
-        for (int j = 0; j < kLocalItems; ++j) {
-            const u32 i = (u32)(rec[j] >> 16);
-            const bool ok = (u32)local_slot(j) < nc;
+        for (int j0 = 0; j0 < kLocalItems; j0 += kRowBatch) {
+            u32 row[kRowBatch][kRowRegs];
 #pragma unroll
-            for (int d = 0; d < kRowRegs; ++d)
-                row[j][d] = ok && d < a.k ? __float_as_uint(a.pts[(i64)i * a.k + d]) : 0u;
-        }
+            for (int j = 0; j < kRowBatch; ++j) {
+                const u32 i = (u32)(rec[j0 + j] >> 16);
+                const bool ok = (u32)local_slot(j0 + j) < nc;
 #pragma unroll
-        for (int j = 0; j < kLocalItems; ++j) {
-            const int e = local_slot(j);
-            if ((u32)e >= nc) continue;
-            stage_idx[e] = (u32)(rec[j] >> 16);
+                for (int d = 0; d < kRowRegs; ++d)
+                    row[j][d] = ok && d < a.k ? __float_as_uint(a.pts[(i64)i * a.k + d]) : 0u;
+            }
 #pragma unroll
-            for (int d = 0; d < kRowRegs; ++d)
-                if (d < a.k) a.stage[(u64)(d + 1) * a.n + first + e] = row[j][d];
-            sh.tag[e] = 0;
+            for (int j = 0; j < kRowBatch; ++j) {
+                const int e = local_slot(j0 + j);
+                if ((u32)e >= nc) continue;
+                stage_idx[e] = (u32)(rec[j0 + j] >> 16);
+#pragma unroll
+                for (int d = 0; d < kRowRegs; ++d)
+                    if (d < a.k) a.stage[(u64)(d + 1) * a.n + first + e] = row[j][d];
+                sh.tag[e] = 0;
+            }
         }
     } else {
 #pragma unroll
@@ -1088,35 +1141,45 @@ struct PassLauncher {
     hipStream_t stream;
     Timer timer;
 
-    template <int kSrc, int kSink>
+    template <int kSrc, int kSink, bool kTags = false>
     void run(PassArgs a) {
         a.tile_counts = tile_counts;
         a.chunk_slots = chunk_slots;
-        const unsigned tiles = (unsigned)lay.tiles, chunks = (unsigned)lay.chunks;
+        // this pass's records (at most the layout's n)
+        const i64 tiles64 = (a.n + kTile - 1) / kTile;
+        const unsigned tiles = (unsigned)tiles64;
+        const unsigned chunks = (unsigned)((tiles64 + kChunkTiles - 1) / kChunkTiles);
         const double n = (double)a.n;
         static const char* const count_names[2] = {"k_tile_count<0>", "k_tile_count<1>"};
-        static const char* const scatter_names[2][3][2] = {
-            {{"k_tile_scatter<0, 0, false>", "k_tile_scatter<0, 0, true>"},
-             {"k_tile_scatter<0, 1, false>", "k_tile_scatter<0, 1, true>"},
-             {"k_tile_scatter<0, 2, false>", "k_tile_scatter<0, 2, true>"}},
-            {{"k_tile_scatter<1, 0, false>", "k_tile_scatter<1, 0, true>"},
-             {"k_tile_scatter<1, 1, false>", "k_tile_scatter<1, 1, true>"},
-             {"k_tile_scatter<1, 2, false>", "k_tile_scatter<1, 2, true>"}}};
+        // [kSrc][kSink][extra][kTags], as the profiler prints the kernels
+        static const char* const scatter_names[2][3][2][2] = {
+            {{{"k_tile_scatter<0, 0, false, false>", "k_tile_scatter<0, 0, false, true>"},
+              {"k_tile_scatter<0, 0, true, false>", "k_tile_scatter<0, 0, true, true>"}},
+             {{"k_tile_scatter<0, 1, false, false>", "k_tile_scatter<0, 1, false, true>"},
+              {"k_tile_scatter<0, 1, true, false>", "k_tile_scatter<0, 1, true, true>"}},
+             {{"k_tile_scatter<0, 2, false, false>", "k_tile_scatter<0, 2, false, true>"},
+              {"k_tile_scatter<0, 2, true, false>", "k_tile_scatter<0, 2, true, true>"}}},
+            {{{"k_tile_scatter<1, 0, false, false>", "k_tile_scatter<1, 0, false, true>"},
+              {"k_tile_scatter<1, 0, true, false>", "k_tile_scatter<1, 0, true, true>"}},
+             {{"k_tile_scatter<1, 1, false, false>", "k_tile_scatter<1, 1, false, true>"},
+              {"k_tile_scatter<1, 1, true, false>", "k_tile_scatter<1, 1, true, true>"}},
+             {{"k_tile_scatter<1, 2, false, false>", "k_tile_scatter<1, 2, false, true>"},
+              {"k_tile_scatter<1, 2, true, false>", "k_tile_scatter<1, 2, true, true>"}}}};
         const bool extra = a.extra_in != nullptr;
         timer.begin(count_names[kSrc], n * 4);  // keys (or the column)
         k_tile_count<kSrc><<<chunks, kCountBlock, 0, stream>>>(a);
         timer.end();
-        timer.begin("k_tile_scan", (double)lay.chunks * kRadix * 8);
-        k_tile_scan<<<kRadix, kBlock, 0, stream>>>(chunk_slots, lay.chunks, a.digit_totals);
+        timer.begin("k_tile_scan", (double)chunks * kRadix * 8);
+        k_tile_scan<<<kRadix, kBlock, 0, stream>>>(chunk_slots, chunks, a.digit_totals);
         timer.end();
         // in: column (4) or key+val (8); out: key+val (8) or one word (4)
         const double in = (kSrc == kSrcColumn ? 4 : 8) + (extra ? 4 : 0);
         const double out = (kSink == kSinkArrays ? 8 : 4) + (extra ? 4 : 0);
-        timer.begin(scatter_names[kSrc][kSink][extra], n * (in + out));
+        timer.begin(scatter_names[kSrc][kSink][extra][kTags], n * (in + out));
         if (extra)
-            k_tile_scatter<kSrc, kSink, true><<<tiles, kBlock, 0, stream>>>(a);
+            k_tile_scatter<kSrc, kSink, true, kTags><<<tiles, kBlock, 0, stream>>>(a);
         else
-            k_tile_scatter<kSrc, kSink, false><<<tiles, kBlock, 0, stream>>>(a);
+            k_tile_scatter<kSrc, kSink, false, kTags><<<tiles, kBlock, 0, stream>>>(a);
         timer.end();
     }
 };
@@ -1168,6 +1231,7 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
         for (int p = 0; p < kKeyBytes; ++p) {
             PassArgs a{};
             a.n = n;
+            a.n_all = n;
             a.shift = 8 * p;
             a.col = col;
             a.keys_in = keys[(p + 1) & 1];
@@ -1209,15 +1273,23 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
 
     // Round l: stable sort of the records (tag, next_d[r]) -- or (tag, point
     // index) in the final round -- kept in order_d order, by tag, one pass
-    // per tag byte; pass p reads buffer p&1 and writes buffer (p+1)&1.
+    // per byte of the live tags' offset from F(l); pass p reads buffer p&1
+    // and writes buffer (p+1)&1. The F(l) fixed records are not sorted: the
+    // first pass writes them straight to where they end up (their tag for
+    // the next round, or their node's slot of the sorted order), and later
+    // passes see only the N - F(l) live records.
     for (int l = 1; l < rounds; ++l) {
         const int d = l % k;
         const int passes = tag_passes(l);
         const bool final = keep_sorted && l == rounds - 1;
+        const u32 fl = (u32)full_nodes(l);
+        u32* sorted = vals[passes & 1];  // final round: the whole sorted order
         for (int p = 0; p < passes; ++p) {
             PassArgs a{};
-            a.n = n;
+            a.n = p == 0 ? n : n - (i64)fl;
+            a.n_all = n;
             a.shift = 8 * p;
+            a.key_base = fl;
             a.digit_totals = totals;
             a.geo = geo;
             a.round = l;
@@ -1226,14 +1298,17 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
             a.keys_out = keys[(p + 1) & 1];
             a.vals_out = vals[(p + 1) & 1];
             a.tag_out = tagq((l + 1) % k);
+            if (final) a.fixed_vals = sorted;
+            else a.fixed_tags = a.tag_out;
             const bool last = p == passes - 1;
             if (!last) {
-                pass.run<kSrcArrays, kSinkArrays>(a);
+                pass.run<kSrcArrays, kSinkArrays, true>(a);
             } else if (final) {
-                *sorted_out = a.vals_out;
-                pass.run<kSrcArrays, kSinkVals>(a);
+                a.vals_out = sorted + fl;  // live records follow the F(l) fixed ones
+                *sorted_out = sorted;
+                pass.run<kSrcArrays, kSinkVals, true>(a);
             } else {
-                pass.run<kSrcArrays, kSinkTags>(a);
+                pass.run<kSrcArrays, kSinkTags, true>(a);
             }
         }
     }
