@@ -89,9 +89,12 @@ kdt_status kdt_debug_tags(const float* points, int64_t N, int32_t k, int32_t rou
 
 /* Per-kernel-kind timing of one build, for benchmarking. */
 #define KDT_PROFILE_MAX_KINDS 32
+#define KDT_PROFILE_NAME_LEN 48
 typedef struct {
     int32_t kinds;                        /* entries filled below */
-    char name[KDT_PROFILE_MAX_KINDS][24]; /* kernel, e.g. "k_tile_scatter<1, 2>" */
+    char name[KDT_PROFILE_MAX_KINDS][KDT_PROFILE_NAME_LEN]; /* kernel as the profiler
+                                             prints it, NUL-terminated, e.g.
+                                             "k_tile_scatter<1, 2, false, true>" */
     int64_t launches[KDT_PROFILE_MAX_KINDS];
     double ms[KDT_PROFILE_MAX_KINDS];     /* summed GPU duration (HIP events) */
     double bytes[KDT_PROFILE_MAX_KINDS];  /* summed algorithmic bytes: each array

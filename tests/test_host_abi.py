@@ -29,6 +29,17 @@ def test_header_and_binding_agree():
     assert declared_functions() == sorted(kdt.SIGNATURES)
 
 
+def test_profile_struct_matches_header():
+    text = open(os.path.join(ROOT, "include", "kdt.h")).read()
+    defines = dict(re.findall(r"#define (KDT_PROFILE_[A-Z_]+) (\d+)", text))
+    assert int(defines["KDT_PROFILE_MAX_KINDS"]) == kdt.PROFILE_MAX_KINDS
+    assert int(defines["KDT_PROFILE_NAME_LEN"]) == kdt.PROFILE_NAME_LEN
+    # int32 count, the name table, then three arrays of 8-byte fields
+    names = kdt.PROFILE_MAX_KINDS * kdt.PROFILE_NAME_LEN
+    expect = (4 + names + 7) // 8 * 8 + 3 * 8 * kdt.PROFILE_MAX_KINDS
+    assert ctypes.sizeof(kdt.Profile) == expect
+
+
 def test_library_exports_every_declared_symbol():
     handle = ctypes.CDLL(kdt.LIB_PATH)
     for name in declared_functions():

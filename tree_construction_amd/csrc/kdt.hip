@@ -15,9 +15,10 @@
 // Pipeline per build (all on the caller's stream, nothing allocated):
 //   k_init       AoS points -> one column per split dimension.
 //   4 passes     per dimension: stable sort of (key(x_d), index) -> order_d
-//                (the points by coordinate d, then index). Dimensions d >= 1
-//                carry rank_(d+1) as a second payload, which lands as next_d.
-//   k_invert     rank_d[order_d[r]] = r.
+//                (the points by coordinate d, then index); the last pass
+//                also writes the inverse, rank_d[order_d[r]] = r. Dimensions
+//                d >= 1 carry rank_(d+1) as a second payload, which lands as
+//                next_d.
 //   k_cross      next_0[r] = position in order_1 of the r-th point of
 //                order_0 (all writes; no random reads).
 //   k_round0     round 0 (all tags 0): tags straight from order_0.
@@ -186,16 +187,6 @@ __global__ __launch_bounds__(kBlock) void k_init(const float* __restrict__ pts, 
     }
 }
 
-// rank[order[r]] = r: where each point sits in order_d.
-__global__ __launch_bounds__(kBlock) void k_invert(const u32* __restrict__ order, i64 n,
-                                                   u32* __restrict__ rank) {
-    const i64 stride = (i64)gridDim.x * kBlock;
-    for (i64 r = (i64)blockIdx.x * kBlock + threadIdx.x; r < n; r += stride) {
-        const u32 i = order[r];
-        if (i < (u64)n) rank[i] = (u32)r;
-    }
-}
-
 // next[rank_d[i]] = rank_e[i]: for the r-th point of order_d, its position
 // in order_e. Reads both ranks in index order, writes scattered.
 __global__ __launch_bounds__(kBlock) void k_cross(const u32* __restrict__ rank_d,
@@ -253,6 +244,7 @@ struct PassArgs {
     u32* keys_out;             // kSinkArrays
     u32* vals_out;             // kSinkArrays, kSinkVals
     u32* tag_out;              // kSinkTags: tag_out[val] = the record's new tag
+    u32* rank_out;             // kSinkVals, optional: rank_out[val] = val's slot
     const u32* extra_in;       // optional second payload (nullptr: none); with
     u32* extra_out;            //   kSrcColumn it is indexed by point index
     u32* digit_totals;         // 256 counts of this pass's digit over all records
@@ -557,13 +549,17 @@ __global__ __launch_bounds__(kBlock) void k_tile_scatter(PassArgs a) {
     for (int i = tid; i < valid_here; i += kBlock) {
         const u32 dst = s_base[s_digit[i]] + (u32)i;
         if (dst >= (u64)a.n) continue;
+        u32 v;
         if (kPairs) {
             const u64 pv = sm.pairs[i];
-            a.vals_out[dst] = (u32)pv;
+            v = (u32)pv;
             a.extra_out[dst] = (u32)(pv >> 32);
         } else {
-            a.vals_out[dst] = sm.vals[i];
+            v = sm.vals[i];
         }
+        a.vals_out[dst] = v;
+        // The inverse permutation, written where the records are placed.
+        if (kSink == kSinkVals && a.rank_out && v < (u64)a.n_all) a.rank_out[v] = dst;
     }
     if (kExtra && !kPairs) {
         __syncthreads();
@@ -1174,7 +1170,7 @@ struct PassLauncher {
         timer.end();
         // in: column (4) or key+val (8); out: key+val (8) or one word (4)
         const double in = (kSrc == kSrcColumn ? 4 : 8) + (extra ? 4 : 0);
-        const double out = (kSink == kSinkArrays ? 8 : 4) + (extra ? 4 : 0);
+        const double out = (kSink == kSinkArrays ? 8 : 4) + (extra ? 4 : 0) + (a.rank_out ? 4 : 0);
         timer.begin(scatter_names[kSrc][kSink][extra][kTags], n * (in + out));
         if (extra)
             k_tile_scatter<kSrc, kSink, true, kTags><<<tiles, kBlock, 0, stream>>>(a);
@@ -1242,6 +1238,7 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
                 a.extra_in = p == 0 ? rank((d + 1) % k) : extra[(p + 1) & 1];
                 a.extra_out = p == kKeyBytes - 1 ? next(d) : extra[p & 1];
             }
+            if (p == kKeyBytes - 1 && knext > 0) a.rank_out = rank(d);
             a.digit_totals = totals;
             if (p == 0)
                 pass.run<kSrcColumn, kSinkArrays>(a);
@@ -1249,11 +1246,6 @@ kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, cons
                 pass.run<kSrcArrays, kSinkArrays>(a);
             else
                 pass.run<kSrcArrays, kSinkVals>(a);
-        }
-        if (knext > 0) {
-            timer.begin("k_invert", N * 8);
-            k_invert<<<grid, kBlock, 0, stream>>>(order(d), n, rank(d));
-            timer.end();
         }
     }
     if (knext > 0) {
@@ -1427,7 +1419,8 @@ kdt_status kdt_build_profiled(const float* points, int64_t N, int32_t k, int32_t
     *profile = kdt_profile{};
     profile->kinds = prof->kinds;
     for (int i = 0; i < prof->kinds; ++i)
-        for (int c = 0; prof->names[i][c] && c < 23; ++c) profile->name[i][c] = prof->names[i][c];
+        for (int c = 0; prof->names[i][c] && c < KDT_PROFILE_NAME_LEN - 1; ++c)
+            profile->name[i][c] = prof->names[i][c];
     for (int i = 0; i < prof->count; ++i) {
         Profiler::Rec& r = prof->recs[i];
         float ms = 0.f;

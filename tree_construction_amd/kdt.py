@@ -18,12 +18,13 @@ KDT_OK = 0
 STATUS_NAMES = {0: "KDT_OK", 1: "KDT_ERR_INVALID_ARG", 2: "KDT_ERR_WORKSPACE", 3: "KDT_ERR_HIP"}
 
 PROFILE_MAX_KINDS = 32
+PROFILE_NAME_LEN = 48
 
 
 class Profile(ctypes.Structure):
     """Mirror of kdt_profile."""
     _fields_ = [("kinds", ctypes.c_int32),
-                ("name", (ctypes.c_char * 24) * PROFILE_MAX_KINDS),
+                ("name", (ctypes.c_char * PROFILE_NAME_LEN) * PROFILE_MAX_KINDS),
                 ("launches", ctypes.c_int64 * PROFILE_MAX_KINDS),
                 ("ms", ctypes.c_double * PROFILE_MAX_KINDS),
                 ("bytes", ctypes.c_double * PROFILE_MAX_KINDS)]
