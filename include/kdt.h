@@ -13,15 +13,18 @@
  * point index as the tie-break, which makes the tree unique.
  *
  * How: the paper's tag-based "trickle-down" construction. Every point
- * carries a 32-bit tag, the id of its ancestor on the current level (tag
+ * carries a tag, the id of its ancestor on the current level (tag
  * paragraph); each round sorts all points by (tag, coordinate l mod k,
  * original index) and refines every tag from the closed-form subtree sizes
- * and segment starts (sort-order and sb/ss paragraphs). On the GPU the sort
- * is a stable LSD radix sort from index order; its coordinate-digit passes
- * are the same in every round that splits on a dimension, so they run once
- * per dimension and each round runs only its tag-digit passes, the last one
- * fused with the tag update. Subtrees of at most 4096 points finish their
- * remaining rounds inside one workgroup's LDS.
+ * and segment starts (sort-order and sb/ss paragraphs). On the GPU each
+ * split dimension keeps an array of point records in that round order,
+ * built by a stable LSD radix sort of (coordinate, index) when the
+ * dimension is first used. A tag update is a comparison with the pivot of
+ * the point's node, so a round re-sorts its dimension's array by the new
+ * tags with one stable radix pass whose digit is the point's path down the
+ * pivots of the levels since that array was last sorted; the pivots of the
+ * round then sit at closed-form positions. Subtrees of at most 4096 points
+ * finish their remaining rounds inside one workgroup's LDS.
  *
  * Conventions for every entry point:
  *   - All pointers marked "device" are HIP device pointers on the current
@@ -78,14 +81,20 @@ kdt_status kdt_build(const float* points, int64_t N, int32_t k,
                      hipStream_t stream);
 
 /* Diagnostic: run only the first `rounds` sort+update rounds (0 <= rounds
- * <= numLevels(N) - 1) and copy every point's tag to tags_out (device, N
- * uint32, indexed by original point index). After r rounds the tag of a
- * point is its final node's ancestor on level r (or the node itself when it
- * sits on a level < r), as the paper's tag paragraph states. Same workspace
- * and error rules as kdt_build. */
+ * <= numLevels(N) - 1) over the whole point set and copy every point's tag
+ * to tags_out (device, N uint32, indexed by original point index). After r
+ * rounds the tag of a point is its final node's ancestor on level r (or the
+ * node itself when it sits on a level < r), as the paper's tag paragraph
+ * states; here it is read off the pivots those rounds fixed. The workspace
+ * must hold kdt_debug_workspace_size(N, k, rounds) bytes; otherwise the
+ * same error rules as kdt_build. */
 kdt_status kdt_debug_tags(const float* points, int64_t N, int32_t k, int32_t rounds,
                           uint32_t* tags_out, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
+
+/* Bytes of workspace kdt_debug_tags() needs (pure host arithmetic; 0 when
+ * the arguments are out of range or no workspace is needed). */
+size_t kdt_debug_workspace_size(int64_t N, int32_t k, int32_t rounds);
 
 /* Per-kernel-kind timing of one build, for benchmarking. */
 #define KDT_PROFILE_MAX_KINDS 32
@@ -94,7 +103,7 @@ typedef struct {
     int32_t kinds;                        /* entries filled below */
     char name[KDT_PROFILE_MAX_KINDS][KDT_PROFILE_NAME_LEN]; /* kernel as the profiler
                                              prints it, NUL-terminated, e.g.
-                                             "k_tile_scatter<1, 2, false, true>" */
+                                             "k_part_scatter<4>" */
     int64_t launches[KDT_PROFILE_MAX_KINDS];
     double ms[KDT_PROFILE_MAX_KINDS];     /* summed GPU duration (HIP events) */
     double bytes[KDT_PROFILE_MAX_KINDS];  /* summed algorithmic bytes: each array
@@ -118,12 +127,21 @@ kdt_status kdt_build_profiled(const float* points, int64_t N, int32_t k,
 int64_t kdt_closed_subtree_size(int64_t N, int64_t s);
 int64_t kdt_closed_segment_begin(int64_t N, int64_t s, int32_t l);
 
-/* Number of 8-bit radix passes over the tag that round l (the round that
- * fixes level l) runs on top of the cached per-dimension coordinate order:
- * only the 2^l live tags F(l) .. F(l+1)-1 are sorted, by their l-bit offset
- * from F(l), so ceil(l/8); 0 for round 0 whose tags are all zero. -1 when l
- * is out of range for N. */
-int32_t kdt_round_passes(int64_t N, int32_t l);
+/* Host copies of the closed forms the per-round re-sort evaluates (no HIP
+ * call), for tests. A point is live on level l when it is not yet a node
+ * above l; in round l's order the live points of the subtree of the j-th
+ * node on level l start at live position kdt_closed_segment_begin(N,
+ * F(l)+j, l) - F(l).
+ *   kdt_closed_live_segment: the j whose subtree holds live position p on
+ *     level l (-1 when l or p is out of range).
+ *   kdt_closed_bin_prefix: the number of points in the subtrees of the
+ *     first j0 nodes on level l1 - delta whose ancestor on level l1 is the
+ *     b-th level-l1 node below their level-(l1 - delta) one, i.e. the sum
+ *     of |S| over the level-l1 nodes with in-level index j*2^delta + b,
+ *     j < j0 (0 <= delta <= min(l1, 8), 0 <= j0 <= 2^(l1-delta),
+ *     0 <= b < 2^delta; -1 otherwise). */
+int64_t kdt_closed_live_segment(int64_t N, int32_t l, int64_t p);
+int64_t kdt_closed_bin_prefix(int64_t N, int32_t l1, int32_t delta, int64_t j0, int64_t b);
 
 /* Static description of a status code. */
 const char* kdt_status_string(kdt_status status);

@@ -71,13 +71,61 @@ def test_closed_segment_begin_is_prefix_sum():
     assert kdt.closed_segment_begin(10, 3, 1) == -1  # node 3 is on level 2
 
 
-def test_round_passes():
-    assert kdt.round_passes(1, 0) == -1
-    assert kdt.round_passes(2, 0) == 0
-    assert kdt.round_passes(2, 1) == -1
-    n = 1 << 24  # 25 levels, 24 rounds; round l sorts 2^l live tags (l offset bits)
-    got = [kdt.round_passes(n, l) for l in range(24)]
-    assert got == [0] + [1] * 8 + [2] * 8 + [3] * 7
+def _level_sizes(N, l):
+    """Subtree sizes of the nodes on level l, by the oracle's counting."""
+    first = (1 << l) - 1
+    return [oracle.subtree_size(N, s) for s in range(first, min(2 * first + 1, N))]
+
+
+def test_closed_live_segment_inverts_the_prefix_sum():
+    """Live position p on level l (points not yet fixed above l, in round-l
+    order) lies in the subtree of the j-th level-l node: the j whose running
+    sum of subtree sizes first exceeds p."""
+    for N in list(range(2, 70)) + [1000, 4097, 5000]:
+        levels = N.bit_length()
+        for l in range(levels):
+            p = 0
+            for j, size in enumerate(_level_sizes(N, l)):
+                for q in range(p, p + size):
+                    assert kdt.closed_live_segment(N, l, q) == j, (N, l, q)
+                p += size
+            assert p == N - ((1 << l) - 1)
+            assert kdt.closed_live_segment(N, l, p) == -1  # past the live points
+    rng = np.random.default_rng(1)
+    for N in rng.integers(1 << 20, 1 << 31, 10):
+        N = int(N)
+        for l in (3, 11, N.bit_length() - 2):
+            # segment starts from the (separately pinned) segment_begin closed form
+            first = (1 << l) - 1
+            for j in rng.integers(0, 1 << l, 20):
+                j = int(j)
+                start = kdt.closed_segment_begin(N, first + j, l) - first
+                size = kdt.closed_subtree_size(N, first + j)
+                for q in (start, start + size // 2, start + size - 1):
+                    assert kdt.closed_live_segment(N, l, int(q)) == j, (N, l, q)
+    assert kdt.closed_live_segment(10, 4, 0) == -1  # 10 nodes: levels 0..3
+
+
+def test_closed_bin_prefix_is_a_strided_sum_of_subtree_sizes():
+    """Points of the first j0 level-(l1-delta) subtrees that fall into the
+    b-th level-l1 subtree below their own: the sizes of the level-l1 nodes
+    with in-level index j*2^delta + b, j < j0, counted by the oracle."""
+    for N in list(range(2, 80)) + [1000, 4097, 65537]:
+        levels = N.bit_length()
+        for l1 in range(levels):
+            sizes = _level_sizes(N, l1) + [0] * ((1 << l1) - len(_level_sizes(N, l1)))
+            for delta in range(0, min(l1, 8) + 1):
+                for b in range(1 << delta):
+                    acc = 0
+                    for j0 in range((1 << (l1 - delta)) + 1):
+                        assert kdt.closed_bin_prefix(N, l1, delta, j0, b) == acc, (N, l1, delta, j0, b)
+                        if j0 < (1 << (l1 - delta)):
+                            acc += sizes[(j0 << delta) + b]
+    # delta = 0 is the live start of node j0 on level l1
+    assert kdt.closed_bin_prefix(1000, 5, 0, 7, 0) == kdt.closed_segment_begin(1000, 31 + 7, 5) - 31
+    assert kdt.closed_bin_prefix(1000, 5, 6, 0, 0) == -1   # delta > l1
+    assert kdt.closed_bin_prefix(1000, 5, 2, 9, 0) == -1   # j0 > 2^(l1-delta)
+    assert kdt.closed_bin_prefix(1000, 5, 2, 1, 4) == -1   # b >= 2^delta
 
 
 def test_workspace_size():
@@ -113,8 +161,17 @@ def test_build_rejects_bad_arguments_before_launch(args, code):
     assert kdt.lib().kdt_build(*args) == code
 
 
+def test_debug_workspace_size():
+    assert kdt.debug_workspace_size(10, 3, 0) == 0
+    assert kdt.debug_workspace_size(10, 3, 4) == 0     # 10 points -> at most 3 rounds
+    assert kdt.debug_workspace_size(1, 3, 0) == 0
+    a = kdt.debug_workspace_size(1 << 20, 3, 5)
+    b = kdt.debug_workspace_size(1 << 20, 3, 19)
+    assert 0 < a < b and a % 256 == 0
+
+
 def test_debug_tags_rejects_bad_rounds():
-    ws = kdt.workspace_size(10, 3)
+    ws = kdt.debug_workspace_size(10, 3, 3)
     # 10 points -> 4 levels -> at most 3 rounds
     assert kdt.lib().kdt_debug_tags(FAKE, 10, 3, 4, FAKE + 2**20, FAKE + 2**21, ws, None) == 1
     assert kdt.lib().kdt_debug_tags(FAKE, 10, 3, -1, FAKE + 2**20, FAKE + 2**21, ws, None) == 1

@@ -4,41 +4,37 @@
 // 2211.00120), cited as [W] with the paragraph that states each fact.
 //
 // Round l of [W] sorts every point by (tag, coordinate l mod k, original
-// index) and refines every tag from its sorted position. Here that sort is a
-// stable LSD radix sort from index order with 8-bit digits. Its first
-// passes, over the coordinate's bytes, do not depend on the tags: they always
-// produce the points ordered by (coordinate d, index), whatever the round.
-// That order is computed once per split dimension ("presort") and every
-// round then runs only its tag-digit passes over it; the last tag pass
-// updates the tags in place from the sorted positions.
+// index) and refines every tag from its sorted position: in the segment of
+// tag s, the point at position sb(s) + ss(2s+1) becomes node s, the points
+// before it take tag 2s+1 and the points after it tag 2s+2.
 //
-// Pipeline per build (all on the caller's stream, nothing allocated):
-//   k_init       AoS points -> one column per split dimension.
-//   4 passes     per dimension: stable sort of (key(x_d), index) -> order_d
-//                (the points by coordinate d, then index); the last pass
-//                also writes the inverse, rank_d[order_d[r]] = r. Dimensions
-//                d >= 1 carry rank_(d+1) as a second payload, which lands as
-//                next_d.
-//   k_cross      next_0[r] = position in order_1 of the r-th point of
-//                order_0 (all writes; no random reads).
-//   k_round0     round 0 (all tags 0): tags straight from order_0.
-//   per round l = 1 .. l0-1, d = l mod k:
-//     1-2 passes stable sort by tag of the records (tag, next_d) kept in
-//                order_d order; the last one computes each point's new tag
-//                and writes it where round l+1 reads it (tags are kept in
-//                the order of the dimension that reads them), or, in round
-//                l0-1, writes the sorted point indices for the next stage.
-//   k_place_top  nodes above level l0.
-//   k_subtree    one workgroup per level-l0 subtree (<= 4096 points) runs
-//                that subtree's remaining rounds in LDS and writes its
-//                level-order output.
+// How the rounds are organised here:
+//   * Every split dimension d has an array A_d of point records (the
+//     coordinates the global rounds split on, then the original index) kept
+//     in round order: sorted by (tag, coordinate d, index). When d is first
+//     used all tags are still those of one level, and A_d is built by a
+//     stable LSD radix sort of (key(x_d), index) from index order whose last
+//     pass writes the records ("presort").
+//   * A tag update only ever compares a point with the pivot of its node:
+//     the point moves left iff its (coordinate, index) is below the pivot's.
+//     So from the pivots (one 8-byte entry per node, a few KB) any array can
+//     recompute the tags of its own points, and no per-point tag ever has to
+//     move between arrays. Round l re-sorts A_(l mod k) from the tags it had
+//     when last used (level l0) to level-l tags: one stable radix pass whose
+//     digit is the point's path down the l - l0 levels in between, found by
+//     walking the pivots. Equal digits keep their order, so each new segment
+//     is still sorted by (coordinate, index): the array is in round l's sort
+//     order. The records of one digit of a tile go to one contiguous run of
+//     the output, so every global pass streams.
+//   * The pivot of each node on level l then sits at its closed-form
+//     position; it is copied to the pivot table and to the output.
+//   * Once every subtree on some level holds at most 4096 points, one
+//     workgroup per subtree runs the remaining rounds in LDS.
 //
-// A radix pass is reduce-then-scan: digit counts of each tile (LDS
-// atomics), a scan of the per-chunk counts per digit that also yields the
-// digit totals, and a scatter that ranks each tile (wave64 ballots, stable
-// multi-split), places it from those counts and stages it in LDS so that the
-// global writes of one digit are contiguous. No workgroup ever waits on
-// another.
+// A radix pass is reduce-then-scan: digit counts of each tile, a scan of
+// the per-chunk counts per digit, and a scatter that ranks each tile again
+// (wave64 ballots, stable multi-split) and writes it. No workgroup ever
+// waits on another.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -56,10 +52,14 @@ constexpr int kRadixBits = 8;
 constexpr int kRadix = 1 << kRadixBits;
 constexpr int kBlock = 256;                // threads per workgroup
 constexpr int kWaves = kBlock / 64;        // wave64
-constexpr int kItems = 16;                 // records per thread in a radix tile
-constexpr int kTile = kBlock * kItems;     // records per radix tile
+constexpr int kItems = 16;                 // records per thread in a tile
+constexpr int kTile = kBlock * kItems;     // records per tile
 constexpr int kKeyBytes = 4;               // order-preserving coordinate key
 constexpr int kChunkTiles = 4;             // tiles per digit-count chunk
+constexpr int kMaxDescent = kRadixBits;    // levels one re-sort pass walks
+constexpr int kPartItems = 8;              // records per thread in a re-sort tile
+constexpr int kPartTile = kBlock * kPartItems;
+constexpr int kMaxRounds = 32;             // global rounds (levels) at most
 static_assert(kBlock == kRadix, "the tile kernels map one thread to one digit");
 static_assert(kBlock * kChunkTiles <= 1024, "one workgroup counts a whole chunk");
 
@@ -70,7 +70,7 @@ static_assert(kBlock * kChunkTiles <= 1024, "one workgroup counts a whole chunk"
 struct Geometry {
     i64 n;      // nodes (= points)
     int levels; // L = numLevels(N)
-    i64 last;   // nodes on the last level: N - F(L-1)
+    i64 last;   // nodes on the last level: M = N - F(L-1)
 };
 
 __host__ __device__ inline int level_of(u64 i) { return 63 - __builtin_clzll(i + 1); }
@@ -100,22 +100,63 @@ __host__ __device__ inline u64 subtree_size(const Geometry& g, u64 s) {
     return (span - 1) + (u64)extra;
 }
 
-// First sorted position of subtree s (on level l) in the round that fixes
-// level l ([W], sb/ss paragraph; derived): the F(l) nodes above level l are
-// already fixed and sort first in tag order, then the j = s - F(l) subtrees
-// left of s on level l, each with 2^dd - 1 full-level nodes, plus the
+// Live position of the first point of the j-th subtree on level l: its
+// position in round l's sorted order counted after the F(l) points already
+// fixed above level l ([W], sb/ss paragraph: sb = F(l) + this; derived).
+// The j subtrees to its left hold 2^dd - 1 full-level nodes each plus the
 // last-level nodes under them, min(M, j * 2^dd).
-__host__ __device__ inline u64 segment_begin(const Geometry& g, u64 s, int l) {
-    u64 j = s - full_nodes(l);
+__host__ __device__ inline u64 live_begin(const Geometry& g, u64 j, int l) {
     int dd = g.levels - 1 - l;
     u64 under = j << dd;
     if (under > (u64)g.last) under = (u64)g.last;
-    return full_nodes(l) + j * ((1ull << dd) - 1) + under;
+    return j * ((1ull << dd) - 1) + under;
+}
+
+// First sorted position of subtree s (on level l) in the round that fixes
+// level l: the F(l) fixed nodes sort first, then the live segments.
+__host__ __device__ inline u64 segment_begin(const Geometry& g, u64 s, int l) {
+    return full_nodes(l) + live_begin(g, s - full_nodes(l), l);
+}
+
+// Inverse of live_begin: the j whose segment on level l holds live position
+// p. The first q = M >> dd subtrees have a full share of the last level
+// (2u - 1 points, u = 2^dd), subtree q a share of r = M mod u, the rest none
+// (u - 1 points).
+__host__ __device__ inline u64 live_segment(const Geometry& g, u64 p, int l) {
+    const int dd = g.levels - 1 - l;
+    if (dd == 0) return p;  // last level: one point per segment
+    const u64 u = 1ull << dd;
+    const u64 q = (u64)g.last >> dd, r = (u64)g.last & (u - 1);
+    const u64 full = q * (2 * u - 1);
+    // positions and divisors stay below 2^32 (N < 2^31), so 32-bit division
+    if (p < full) return (u32)p / (u32)(2 * u - 1);
+    const u64 rest = p - full;
+    if (rest < u - 1 + r) return q;
+    return q + 1 + (u32)(rest - (u - 1 + r)) / (u32)(u - 1);
+}
+
+// Points of the first j0 subtrees on level l0 whose level-l1 ancestor
+// (l1 = l0 + delta) is the b-th level-l1 node under their level-l0 one:
+// the sizes of the level-l1 subtrees with in-level index j*2^delta + b,
+// j < j0. A level-l1 subtree with in-level index i holds u - 1 full-level
+// nodes plus u, r or 0 last-level ones for i < q, i == q, i > q (u = 2^dd,
+// q = M >> dd, r = M mod u).
+__host__ __device__ inline u64 bin_prefix(const Geometry& g, u64 j0, u32 b, int l1, int delta) {
+    const int dd = g.levels - 1 - l1;
+    const u64 u = 1ull << dd;
+    const u64 q = (u64)g.last >> dd, r = (u64)g.last & (u - 1);
+    u64 h = j0 * (u - 1);
+    if (q > b) {
+        const u64 c = ((q - b - 1) >> delta) + 1;  // i = j*2^delta + b < q
+        h += u * (c < j0 ? c : j0);
+    }
+    if (q >= b && ((q - b) & ((1ull << delta) - 1)) == 0 && ((q - b) >> delta) < j0) h += r;
+    return h;
 }
 
 // Order-preserving map of float bits to unsigned: IEEE order with -0 == +0.
 // Pure bit tests, so denormals are never flushed.
-__device__ inline u32 float_key(u32 b) {
+__host__ __device__ inline u32 float_key(u32 b) {
     if ((b & 0x7fffffffu) == 0) return 0x80000000u;
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
@@ -171,13 +212,41 @@ __device__ inline u64 block_exclusive_scan64(u64 v, u64* s_wave) {
     return off + inc - v;
 }
 
-// Radix passes over the tag in round l >= 1: only the 2^l live tags
-// F(l) .. F(l+1)-1 are sorted, by their offset from F(l) (l bits).
-__host__ __device__ inline int tag_passes(int l) { return (l + kRadixBits - 1) / kRadixBits; }
+// Rank inside the wave of each of this thread's records by its digit
+// (nbits bits): lanes holding the same digit are found with nbits ballots
+// (a lane's peers are the lanes that never disagree with it on a bit: the OR
+// over bits of vote ^ own-bit-mask, inverted), and the lowest such lane
+// bumps the wave's counter for the digit. rank[j] = records of the same
+// digit earlier in the wave's rows (row j of every lane precedes row j+1).
+// Invalid records are neither ranked nor counted. count[] (the wave's own
+// row) must be zero on entry and holds the wave's digit totals on return.
+template <int kN>
+__device__ inline void wave_rank(const u32 (&digit)[kN], const bool (&valid)[kN], int nbits,
+                                 u32* count, u32 (&rank)[kN]) {
+    const int lane = threadIdx.x & 63;
+    const u64 below = (1ull << lane) - 1;
+#pragma unroll
+    for (int j = 0; j < kN; ++j) {
+        const u32 d = digit[j];
+        u32 miss_lo = 0, miss_hi = 0;
+        for (int b = 0; b < nbits; ++b) {
+            const u64 vote = __ballot((d >> b) & 1);
+            const u32 m = (u32)((int)(d << (31 - b)) >> 31);  // all ones where the bit is set
+            miss_lo |= (u32)vote ^ m;
+            miss_hi |= (u32)(vote >> 32) ^ m;
+        }
+        const u64 peers = __ballot(valid[j]) & ~(((u64)miss_hi << 32) | miss_lo);
+        const u32 before = __popcll(peers & below);
+        u32 seen = 0;
+        if (valid[j]) seen = count[d];
+        rank[j] = seen + before;
+        if (valid[j] && before == 0) count[d] = seen + (u32)__popcll(peers);
+    }
+}
 
-// ------------------------------------------------------ global-phase kernels
+// ------------------------------------------------- presort (LSD radix sort)
 
-// Column copy of the split dimensions.
+// Column copy of the split dimensions the global rounds use.
 __global__ __launch_bounds__(kBlock) void k_init(const float* __restrict__ pts, i64 n, int k,
                                                  int kcols, float* __restrict__ cols) {
     const i64 stride = (i64)gridDim.x * kBlock;
@@ -187,76 +256,32 @@ __global__ __launch_bounds__(kBlock) void k_init(const float* __restrict__ pts, 
     }
 }
 
-// next[rank_d[i]] = rank_e[i]: for the r-th point of order_d, its position
-// in order_e. Reads both ranks in index order, writes scattered.
-__global__ __launch_bounds__(kBlock) void k_cross(const u32* __restrict__ rank_d,
-                                                  const u32* __restrict__ rank_e, i64 n,
-                                                  u32* __restrict__ next) {
-    const i64 stride = (i64)gridDim.x * kBlock;
-    for (i64 i = (i64)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride) {
-        const u32 r = rank_d[i];
-        if (r < (u64)n) next[r] = rank_e[i];
-    }
-}
-
-// Round 0: every tag is 0, so the sorted order is order_0 itself and the
-// pivot sits at position |S(1)|. Writes each point's new tag at its
-// position in the order round 1 reads.
-__global__ __launch_bounds__(kBlock) void k_round0(const u32* __restrict__ next, Geometry geo,
-                                                   u32* __restrict__ tag_next) {
-    const u64 pivot = subtree_size(geo, 1);
-    const i64 stride = (i64)gridDim.x * kBlock;
-    for (i64 r = (i64)blockIdx.x * kBlock + threadIdx.x; r < geo.n; r += stride) {
-        const u32 q = next[r];
-        if (q < (u64)geo.n) tag_next[q] = (u64)r < pivot ? 1u : ((u64)r > pivot ? 2u : 0u);
-    }
-}
-
-// Tags after some rounds, back in original index order (diagnostics only).
-__global__ __launch_bounds__(kBlock) void k_unpermute(const u32* __restrict__ tagq,
-                                                      const u32* __restrict__ order, i64 n,
-                                                      u32* __restrict__ out) {
-    const i64 stride = (i64)gridDim.x * kBlock;
-    for (i64 r = (i64)blockIdx.x * kBlock + threadIdx.x; r < n; r += stride) {
-        const u32 i = order[r];
-        if (i < (u64)n) out[i] = tagq ? tagq[r] : 0u;
-    }
-}
-
 enum Src { kSrcColumn = 0, kSrcArrays = 1 };
-enum Sink { kSinkArrays = 0, kSinkVals = 1, kSinkTags = 2 };
+enum Sink { kSinkArrays = 0, kSinkRecords = 1 };
 
-// One stable radix pass over n (key, val) records is three launches
-// (reduce-then-scan; no workgroup ever waits on another):
-//   k_tile_count  digit counts of every tile of kTile records,
-//   k_tile_scan   per digit, exclusive scan over the tiles plus the digit's
-//                 first slot -> the first global slot of (tile, digit),
-//   k_tile_scatter rank each tile again and move its records there.
+// One stable radix pass over n (key, val) records is three launches:
+//   k_tile_count  digit counts of every tile of kTile records, and of every
+//                 chunk of kChunkTiles tiles,
+//   k_tile_scan   per digit, exclusive scan over the chunks,
+//   k_tile_scatter rank each tile again and move its records.
+// The presort of dimension d runs kKeyBytes passes from index order; the
+// last one writes records instead of (key, val) pairs.
 struct PassArgs {
-    i64 n;                     // records of this pass
-    i64 n_all;                 // points (bound of tag_out and fixed_*)
-    int shift;                 // digit = ((key - key_base) >> shift) & 255
-    u32 key_base;              // records with key < key_base are fixed: they
-                               //   are not sorted and go to a fixed_* array
+    i64 n;                     // records
+    int shift;                 // digit = (key >> shift) & 255
     const float* col;          // kSrcColumn: key = key(col[i]), val = i
     const u32* keys_in;        // kSrcArrays
     const u32* vals_in;        // kSrcArrays
     u32* keys_out;             // kSinkArrays
-    u32* vals_out;             // kSinkArrays, kSinkVals
-    u32* tag_out;              // kSinkTags: tag_out[val] = the record's new tag
-    u32* rank_out;             // kSinkVals, optional: rank_out[val] = val's slot
-    const u32* extra_in;       // optional second payload (nullptr: none); with
-    u32* extra_out;            //   kSrcColumn it is indexed by point index
+    u32* vals_out;             // kSinkArrays
+    u32* recs_out;             // kSinkRecords: the record of point val at its slot:
+    int words;                 //   its first words-1 coordinates (bits), then val
+    const float* pts;          // kSinkRecords: the input points (rows of k)
+    int k;
     u32* digit_totals;         // 256 counts of this pass's digit over all records
     u32* tile_counts;          // tiles x 256: digit counts of each tile
-    u32* chunk_slots;          // chunks x 256: digit counts of each chunk of
-                               //   kChunkTiles tiles, then the counts of the
-                               //   digit in the chunks before it
-    u32* fixed_tags;           // fixed record: fixed_tags[val] = key (its tag)
-    u32* fixed_vals;           // fixed record: fixed_vals[key] = val (node key
-                               //   sits at sorted position key)
-    Geometry geo;              // kSinkTags
-    int round;                 // kSinkTags
+    u32* chunk_slots;          // chunks x 256: digit counts of each chunk, then the
+                               //   counts of the digit in the chunks before it
 };
 
 // Records of item j of this thread: wave w owns kItems rows of 64
@@ -264,7 +289,6 @@ struct PassArgs {
 template <int kSrc>
 __device__ inline void load_tile(const PassArgs& a, i64 wbase, u32 (&key)[kItems],
                                  u32 (&val)[kItems]) {
-    // (the optional second payload is loaded by the scatter kernel itself)
 #pragma unroll
     for (int j = 0; j < kItems; ++j) {
         const i64 e = wbase + (i64)j * 64;
@@ -282,54 +306,8 @@ __device__ inline void load_tile(const PassArgs& a, i64 wbase, u32 (&key)[kItems
     }
 }
 
-// Rank inside the wave: lanes holding the same digit are found with eight
-// ballots (a lane's peers are the lanes that never disagree with it on a
-// bit: the OR over bits of vote ^ own-bit-mask, inverted); the lowest such
-// lane bumps the wave's counter for the digit. rank[j] = records of the
-// same digit earlier in the wave's rows. Records past the end, and with
-// kTags those whose key (an offset from F(l)) wrapped below zero (fixed
-// points), are not ranked.
-template <bool kTags>
-__device__ inline void wave_rank(const u32 (&key)[kItems], i64 wbase, i64 n, int shift,
-                                 u32* count, u32 (&rank)[kItems]) {
-    const int lane = threadIdx.x & 63;
-    for (int i = lane; i < kRadix; i += 64) count[i] = 0;
-    const u64 below = (1ull << lane) - 1;
-#pragma unroll
-    for (int j = 0; j < kItems; ++j) {
-        const bool valid = (wbase + (i64)j * 64) < n && (!kTags || (int)key[j] >= 0);
-        const u32 d = (key[j] >> shift) & (kRadix - 1);
-        u32 miss_lo = 0, miss_hi = 0;
-#pragma unroll
-        for (int b = 0; b < kRadixBits; ++b) {
-            const u64 vote = __ballot((d >> b) & 1);
-            const u32 m = (u32)((int)(d << (31 - b)) >> 31);  // all ones where the bit is set
-            miss_lo |= (u32)vote ^ m;
-            miss_hi |= (u32)(vote >> 32) ^ m;
-        }
-        const u64 peers = __ballot(valid) & ~(((u64)miss_hi << 32) | miss_lo);
-        const u32 before = __popcll(peers & below);
-        u32 seen = 0;
-        if (valid) seen = count[d];
-        rank[j] = seen + before;
-        if (valid && before == 0) count[d] = seen + (u32)__popcll(peers);
-    }
-}
-
-// Keys of item j of this thread (the same record layout as load_tile).
-template <int kSrc>
-__device__ inline void load_keys(const PassArgs& a, i64 wbase, u32 (&key)[kItems]) {
-#pragma unroll
-    for (int j = 0; j < kItems; ++j) {
-        const i64 e = wbase + (i64)j * 64;
-        key[j] = 0;
-        if (e < a.n)
-            key[j] = kSrc == kSrcColumn ? float_key(__float_as_uint(a.col[e])) : a.keys_in[e];
-    }
-}
-
 // Digit counts of kChunkTiles consecutive tiles: one row per tile and the
-// chunk's total (fixed records are not counted). Each group of kBlock threads counts one tile (the same
+// chunk's total. Each group of kBlock threads counts one tile (the same
 // record layout as the scatter's tiles), all tiles of the chunk at once.
 // Counting needs no ranks, only LDS atomics; each thread merges runs of
 // equal digits among its own records first, which keeps the skewed high
@@ -345,14 +323,19 @@ __global__ __launch_bounds__(kCountBlock) void k_tile_count(PassArgs a) {
     const i64 t = (i64)blockIdx.x * kChunkTiles + g;
     const i64 wbase = t * kTile + (i64)gw * (64 * kItems) + lane;
     u32 key[kItems];
-    load_keys<kSrc>(a, wbase, key);
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+        const i64 e = wbase + (i64)j * 64;
+        key[j] = 0;
+        if (e < a.n)
+            key[j] = kSrc == kSrcColumn ? float_key(__float_as_uint(a.col[e])) : a.keys_in[e];
+    }
     for (int i = lane; i < kRadix; i += 64) hist[w][i] = 0;  // this wave's own row
     u32 last = 0, run = 0;
 #pragma unroll
     for (int j = 0; j < kItems; ++j) {
         if (wbase + (i64)j * 64 >= a.n) break;
-        if (key[j] < a.key_base) continue;  // fixed: not sorted
-        const u32 d = ((key[j] - a.key_base) >> a.shift) & (kRadix - 1);
+        const u32 d = (key[j] >> a.shift) & (kRadix - 1);
         if (run && d != last) {
             atomicAdd(&hist[w][last], run);
             run = 0;
@@ -379,12 +362,12 @@ __global__ __launch_bounds__(kCountBlock) void k_tile_count(PassArgs a) {
 }
 
 // One workgroup per digit d: slots[c][d] = counts of d in the chunks before
-// c; totals[d] = all counts of d. Each thread scans a contiguous run of up
-// to kScanRun chunks held in registers (one batch of loads); longer inputs
-// loop over runs.
+// c (rows of `bins` digits); totals[d] = all counts of d (if totals is
+// given). Each thread scans a contiguous run of up to kScanRun chunks held
+// in registers (one batch of loads); longer inputs loop over runs.
 constexpr int kScanRun = 16;
 __global__ __launch_bounds__(kBlock) void k_tile_scan(u32* __restrict__ slots, i64 chunks,
-                                                      u32* __restrict__ totals) {
+                                                      int bins, u32* __restrict__ totals) {
     __shared__ u32 s_wave[kWaves];
     __shared__ u32 s_carry;
     const int tid = threadIdx.x, d = blockIdx.x;
@@ -394,7 +377,7 @@ __global__ __launch_bounds__(kBlock) void k_tile_scan(u32* __restrict__ slots, i
         u32 v[kScanRun], sum = 0;
 #pragma unroll
         for (int i = 0; i < kScanRun; ++i) {
-            v[i] = mine + i < chunks ? slots[(u64)(mine + i) * kRadix + d] : 0u;
+            v[i] = mine + i < chunks ? slots[(u64)(mine + i) * bins + d] : 0u;
             sum += v[i];
         }
         __syncthreads();  // s_carry written
@@ -403,34 +386,55 @@ __global__ __launch_bounds__(kBlock) void k_tile_scan(u32* __restrict__ slots, i
         if (tid == kBlock - 1) s_carry = off + sum;
 #pragma unroll
         for (int i = 0; i < kScanRun; ++i) {
-            if (mine + i < chunks) slots[(u64)(mine + i) * kRadix + d] = off;
+            if (mine + i < chunks) slots[(u64)(mine + i) * bins + d] = off;
             off += v[i];
         }
     }
     __syncthreads();
-    if (tid == 0) totals[d] = s_carry;
+    if (totals && tid == 0) totals[d] = s_carry;
 }
 
-// kTags: a tag pass, whose records below key_base are fixed (not sorted).
-template <int kSrc, int kSink, bool kExtra, bool kTags>
+// Writes the record of point v (its first words-1 coordinates, then v) to
+// record slot dst. kW > 0: compile-time record width; 0: a.words.
+template <int kW>
+__device__ inline void write_point_record(const PassArgs& a, u64 dst, u32 v) {
+    const u32* row = reinterpret_cast<const u32*>(a.pts) + (u64)v * a.k;
+    if constexpr (kW == 4) {
+        *reinterpret_cast<uint4*>(a.recs_out + dst * 4) = make_uint4(row[0], row[1], row[2], v);
+    } else if constexpr (kW == 2) {
+        *reinterpret_cast<uint2*>(a.recs_out + dst * 2) = make_uint2(row[0], v);
+    } else {
+        const int words = kW > 0 ? kW : a.words;
+        u32* out = a.recs_out + dst * words;
+        for (int d = 0; d < words - 1; ++d) out[d] = row[d];
+        out[words - 1] = v;
+    }
+}
+
+template <int kSrc, int kSink, int kW>
 __global__ __launch_bounds__(kBlock) void k_tile_scatter(PassArgs a) {
     __shared__ union {
         u32 count[kWaves][kRadix];  // ranking: per-wave digit counts, then prefixes
         u32 keys[kTile];            // staging of the sorted tile
         u32 vals[kTile];
-        u64 pairs[kExtra && kSink == kSinkVals ? kTile : 1];  // value + second payload
     } sm;
     __shared__ u8 s_digit[kTile];
     __shared__ u32 s_local[kRadix];  // first tile-local slot of each digit
     __shared__ u32 s_base[kRadix];   // global slot of tile-local slot 0 of each digit
     __shared__ u64 s_wave[kWaves];
-    __shared__ u32 s_live;           // records of the tile that are sorted
+    __shared__ u32 s_valid;          // records of the tile
 
     const int tid = threadIdx.x, w = tid >> 6;
     const i64 base = (i64)blockIdx.x * kTile;
     const i64 wbase = base + (i64)w * (64 * kItems) + (tid & 63);
-    u32 key[kItems], val[kItems], rank[kItems], extra[kItems];
+    u32 key[kItems], val[kItems], rank[kItems], digit[kItems];
+    bool valid[kItems];
     load_tile<kSrc>(a, wbase, key, val);
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+        valid[j] = (wbase + (i64)j * 64) < a.n;
+        digit[j] = (key[j] >> a.shift) & (kRadix - 1);
+    }
     // First global slot of digit tid in this tile: where the digit starts in
     // the output, plus its counts in earlier chunks and in the chunk's
     // earlier tiles.
@@ -442,32 +446,8 @@ __global__ __launch_bounds__(kBlock) void k_tile_scatter(PassArgs a) {
         const i64 t = chunk * kChunkTiles + c;
         if (t < (i64)blockIdx.x) global_start += a.tile_counts[(u64)t * kRadix + tid];
     }
-    if (kExtra) {
-#pragma unroll
-        for (int j = 0; j < kItems; ++j) {
-            const i64 e = wbase + (i64)j * 64;
-            extra[j] = e < a.n ? a.extra_in[e] : 0u;
-        }
-    }
-    // Tag passes work on the offset of the tag from F(l): live tags map to
-    // 0 .. 2^l - 1 and fixed ones wrap to values >= 2^31.
-    const u32 kbase = kTags ? a.key_base : 0u;
-    if (kTags) {
-#pragma unroll
-        for (int j = 0; j < kItems; ++j) {
-            key[j] -= kbase;
-            if ((wbase + (i64)j * 64) >= a.n || (int)key[j] >= 0) continue;
-            // A fixed record goes straight to its final place: its tag for
-            // the next round, or its node's slot of the sorted order.
-            const u32 s = key[j] + kbase;  // the fixed node's id
-            if (a.fixed_tags) {
-                if (val[j] < (u64)a.n_all) a.fixed_tags[val[j]] = s;
-            } else if (a.fixed_vals) {
-                if (s < (u64)a.n_all) a.fixed_vals[s] = val[j];
-            }
-        }
-    }
-    wave_rank<kTags>(key, wbase, a.n, a.shift, sm.count[w], rank);
+    for (int i = tid & 63; i < kRadix; i += 64) sm.count[w][i] = 0;
+    wave_rank(digit, valid, kRadixBits, sm.count[w], rank);
     __syncthreads();
 
     // Thread tid owns digit tid: per-wave prefixes and the tile total.
@@ -485,48 +465,23 @@ __global__ __launch_bounds__(kBlock) void k_tile_scatter(PassArgs a) {
     global_start += (u32)(starts >> 32);
     s_local[tid] = local_start;
     s_base[tid] = global_start - local_start;  // modular; base + slot < n
-    if (tid == kBlock - 1) s_live = local_start + agg;
-
-    // (recomputed where needed rather than held in registers)
-    auto live = [&](int j) { return (wbase + (i64)j * 64) < a.n && (!kTags || (int)key[j] >= 0); };
-    auto digit = [&](int j) { return (key[j] >> a.shift) & (kRadix - 1); };
+    if (tid == kBlock - 1) s_valid = local_start + agg;
 #pragma unroll
     for (int j = 0; j < kItems; ++j)
-        if (live(j)) rank[j] += sm.count[w][digit(j)];
-    __syncthreads();  // s_local written
+        if (valid[j]) rank[j] += sm.count[w][digit[j]];
+    __syncthreads();  // s_local written, count reads done
 
-    if (kSink == kSinkTags) {
-        // Tag update ([W], tag and sort-order paragraphs): a point of subtree
-        // s (s on level l, so s >= F(l)) at sorted position p moves to the
-        // left child if p is before the pivot, to the right child if after,
-        // and stays as node s if it is the pivot; pivot = start of s's
-        // segment + size of the left subtree. Tags < F(l) are final (carried
-        // over above). Those F(l) fixed points sort first, one per node id,
-        // so the live ones, ranked here, start at position F(l).
-#pragma unroll
-        for (int j = 0; j < kItems; ++j) {
-            if (!live(j)) continue;  // fixed ones are written already
-            const u64 s = (u32)(key[j] + kbase);
-            const u32 d = digit(j);
-            const u64 p = (u64)kbase + (u32)(s_base[d] + s_local[d] + rank[j]);
-            const u64 pivot = segment_begin(a.geo, s, a.round) + subtree_size(a.geo, 2 * s + 1);
-            const u64 t = p < pivot ? 2 * s + 1 : (p > pivot ? 2 * s + 2 : s);
-            if (val[j] < (u64)a.n_all) a.tag_out[val[j]] = (u32)t;
-        }
-        return;
-    }
-
-    const int valid_here = (int)s_live;
+    const int valid_here = (int)s_valid;
     // rank[j] becomes the record's slot in the tile's sorted order.
 #pragma unroll
     for (int j = 0; j < kItems; ++j)
-        if (live(j)) rank[j] += s_local[digit(j)];
+        if (valid[j]) rank[j] += s_local[digit[j]];
     if (kSink == kSinkArrays) {
 #pragma unroll
         for (int j = 0; j < kItems; ++j) {
-            if (!live(j)) continue;
-            sm.keys[rank[j]] = key[j] + kbase;
-            s_digit[rank[j]] = (u8)digit(j);
+            if (!valid[j]) continue;
+            sm.keys[rank[j]] = key[j];
+            s_digit[rank[j]] = (u8)digit[j];
         }
         __syncthreads();
         for (int i = tid; i < valid_here; i += kBlock) {
@@ -535,45 +490,272 @@ __global__ __launch_bounds__(kBlock) void k_tile_scatter(PassArgs a) {
         }
         __syncthreads();
     }
-    // Values; the optional second payload shares the value's 64-bit slot
-    // when they are the only outputs, else it gets a staging round of its own.
-    constexpr bool kPairs = kExtra && kSink == kSinkVals;
 #pragma unroll
     for (int j = 0; j < kItems; ++j) {
-        if (!live(j)) continue;
-        if (kPairs) sm.pairs[rank[j]] = ((u64)extra[j] << 32) | val[j];
-        else sm.vals[rank[j]] = val[j];
-        if (kSink == kSinkVals) s_digit[rank[j]] = (u8)digit(j);
+        if (!valid[j]) continue;
+        sm.vals[rank[j]] = val[j];
+        if (kSink == kSinkRecords) s_digit[rank[j]] = (u8)digit[j];
     }
     __syncthreads();
     for (int i = tid; i < valid_here; i += kBlock) {
         const u32 dst = s_base[s_digit[i]] + (u32)i;
         if (dst >= (u64)a.n) continue;
-        u32 v;
-        if (kPairs) {
-            const u64 pv = sm.pairs[i];
-            v = (u32)pv;
-            a.extra_out[dst] = (u32)(pv >> 32);
-        } else {
-            v = sm.vals[i];
-        }
-        a.vals_out[dst] = v;
-        // The inverse permutation, written where the records are placed.
-        if (kSink == kSinkVals && a.rank_out && v < (u64)a.n_all) a.rank_out[v] = dst;
+        const u32 v = sm.vals[i];
+        if (kSink == kSinkArrays) a.vals_out[dst] = v;
+        else if (v < (u64)a.n) write_point_record<kW>(a, dst, v);
     }
-    if (kExtra && !kPairs) {
-        __syncthreads();
+}
+
+// ------------------------------------- re-sort by tag: the per-round pass
+// Array `in` holds the records of the points still live on level l0 (not
+// yet a node above it) in round-l0 order: segment j of level l0 at live
+// positions [live_begin(j), live_begin(j+1)), each sorted by (coordinate,
+// index). The pass moves every point to its segment on level l1 = l0 +
+// delta, keeping the order inside each segment; the pivots of the levels in
+// between drop out (they are nodes already). A point's digit is the offset
+// of its level-l1 node below its level-l0 node (delta bits); its output
+// position is
+//   live_begin(its level-l1 node)
+//   + (points of its digit before it in `in`)
+//   - (those in earlier level-l0 segments: bin_prefix, closed form).
+struct PartArgs {
+    const u32* in;     // records live on level l0: n_in x words
+    u32* out;          // records live on level l1: n_out x words
+    i64 n_in, n_out;
+    int words;         // record width: coordinates 0 .. words-2, then the index
+    int k;             // dimensions: level l splits coordinate l mod k
+    int l0, l1;        // levels before and after (1 <= l1 - l0 <= kMaxDescent)
+    int dim0;          // l0 mod k
+    Geometry geo;
+    const u64* piv;    // pivot of node s: key(coordinate) << 32 | index
+    u32* chunk_slots;  // tiles x bins: digit counts of each tile, then the
+                       //   counts of the digit in the tiles before it
+};
+
+// This thread's records of a tile. kW > 0 (at most 4 words): held in
+// registers, one array per word so that every index is a compile-time
+// constant; kW = 0 (wider records): words are read from `in` when needed.
+template <int kW>
+struct TileRecords {
+    static_assert(kW >= 0 && kW <= 4 && kW != 1, "record width");
+    u32 w0[kPartItems], w1[kPartItems], w2[kPartItems], w3[kPartItems];
+
+    __device__ __forceinline__ void load(const PartArgs& a, i64 wbase) {
+        if constexpr (kW > 0) {
 #pragma unroll
-        for (int j = 0; j < kItems; ++j) {
-            if (!live(j)) continue;
-            sm.vals[rank[j]] = extra[j];
-        }
-        __syncthreads();
-        for (int i = tid; i < valid_here; i += kBlock) {
-            const u32 dst = s_base[s_digit[i]] + (u32)i;
-            if (dst < (u64)a.n) a.extra_out[dst] = sm.vals[i];
+            for (int j = 0; j < kPartItems; ++j) {
+                const i64 e = wbase + (i64)j * 64;
+                w0[j] = w1[j] = w2[j] = w3[j] = 0;
+                if (e >= a.n_in) continue;
+                const u32* src = a.in + (u64)e * kW;
+                if constexpr (kW == 4) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(src);
+                    w0[j] = v.x;
+                    w1[j] = v.y;
+                    w2[j] = v.z;
+                    w3[j] = v.w;
+                } else if constexpr (kW == 3) {
+                    w0[j] = src[0];
+                    w1[j] = src[1];
+                    w2[j] = src[2];
+                } else {
+                    const uint2 v = *reinterpret_cast<const uint2*>(src);
+                    w0[j] = v.x;
+                    w1[j] = v.y;
+                }
+            }
         }
     }
+    // Word w of item j (record e); w is uniform across the wave. The word is
+    // picked with masks, not a select, so that the compiler cannot turn the
+    // choice back into an indexed (scratch) array.
+    __device__ __forceinline__ u32 word(const PartArgs& a, int j, i64 e, int w) const {
+        if constexpr (kW == 0) {
+            return a.in[(u64)e * a.words + w];
+        } else {
+            const u32 m0 = w == 0 ? ~0u : 0u, m1 = w == 1 ? ~0u : 0u;
+            const u32 m2 = w == 2 ? ~0u : 0u, m3 = w == 3 ? ~0u : 0u;
+            u32 v = (w0[j] & m0) | (w1[j] & m1);
+            if constexpr (kW > 2) v |= w2[j] & m2;
+            if constexpr (kW > 3) v |= w3[j] & m3;
+            return v;
+        }
+    }
+    __device__ __forceinline__ void store(const PartArgs& a, int j, i64 e, u64 pos) const {
+        if constexpr (kW == 4) {
+            *reinterpret_cast<uint4*>(a.out + pos * 4) = make_uint4(w0[j], w1[j], w2[j], w3[j]);
+        } else if constexpr (kW == 3) {
+            a.out[pos * 3] = w0[j];
+            a.out[pos * 3 + 1] = w1[j];
+            a.out[pos * 3 + 2] = w2[j];
+        } else if constexpr (kW == 2) {
+            *reinterpret_cast<uint2*>(a.out + pos * 2) = make_uint2(w0[j], w1[j]);
+        } else {
+            const u32* src = a.in + (u64)e * a.words;
+            u32* dst = a.out + pos * a.words;
+            for (int w = 0; w < a.words; ++w) dst[w] = src[w];
+        }
+    }
+};
+
+// For every item: node[j], the in-level index of its node on level l1,
+// which is (j0 << delta) | digit for its level-l0 segment j0 and its digit
+// (offset of the level-l1 node below the level-l0 one); valid = false for
+// records past the end and for the pivots of levels l0 .. l1-1. The walk
+// compares (key(coordinate l mod k), index) with the pivot of the current
+// node on each level l ([W], tag paragraph: before the pivot -> left child).
+template <int kW>
+__device__ __forceinline__ void part_nodes(const PartArgs& a, const TileRecords<kW>& tr,
+                                           i64 wbase, u32 (&node)[kPartItems],
+                                           bool (&valid)[kPartItems]) {
+#pragma unroll
+    for (int j = 0; j < kPartItems; ++j) {
+        const i64 e = wbase + (i64)j * 64;
+        valid[j] = e < a.n_in;
+        node[j] = (u32)full_nodes(a.l0) + (valid[j] ? (u32)live_segment(a.geo, (u64)e, a.l0) : 0u);
+    }
+    int dim = a.dim0;
+    for (int l = a.l0; l < a.l1; ++l) {
+#pragma unroll
+        for (int j = 0; j < kPartItems; ++j) {
+            const i64 e = wbase + (i64)j * 64;
+            const u64 me = ((u64)float_key(tr.word(a, j, e, dim)) << 32) |
+                           tr.word(a, j, e, a.words - 1);
+            const u64 p = valid[j] ? a.piv[node[j]] : 0;
+            if (me == p) valid[j] = false;  // the pivot itself: a node already
+            node[j] = 2 * node[j] + (me < p ? 1u : 2u);
+        }
+        if (++dim == a.k) dim = 0;
+    }
+    const u32 first = (u32)full_nodes(a.l1);
+#pragma unroll
+    for (int j = 0; j < kPartItems; ++j) node[j] -= first;
+}
+
+// Digit counts of one tile of a re-sort pass (a row of `bins`; the tiles
+// are the chunks of the scan).
+template <int kW>
+__global__ __launch_bounds__(kBlock) void k_part_count(PartArgs a) {
+    __shared__ u32 hist[kWaves][kRadix];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const i64 wbase = (i64)blockIdx.x * kPartTile + (i64)w * (64 * kPartItems) + lane;
+    const int bins = 1 << (a.l1 - a.l0);
+    TileRecords<kW> tr;
+    tr.load(a, wbase);
+    u32 node[kPartItems];
+    bool valid[kPartItems];
+    part_nodes<kW>(a, tr, wbase, node, valid);
+    for (int i = lane; i < bins; i += 64) hist[w][i] = 0;  // this wave's own row
+    u32 last = 0, run = 0;
+#pragma unroll
+    for (int j = 0; j < kPartItems; ++j) {
+        if (!valid[j]) continue;
+        const u32 digit = node[j] & (bins - 1);
+        if (run && digit != last) {
+            atomicAdd(&hist[w][last], run);
+            run = 0;
+        }
+        last = digit;
+        ++run;
+    }
+    if (run) atomicAdd(&hist[w][last], run);
+    __syncthreads();
+    if (tid < bins) {
+        u32 total = 0;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) total += hist[v][tid];
+        a.chunk_slots[(u64)blockIdx.x * bins + tid] = total;
+    }
+}
+
+template <int kW>
+__global__ __launch_bounds__(kBlock) void k_part_scatter(PartArgs a) {
+    __shared__ u32 count[kWaves][kRadix];  // per-wave digit counts, then first slots
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const i64 wbase = (i64)blockIdx.x * kPartTile + (i64)w * (64 * kPartItems) + lane;
+    const int delta = a.l1 - a.l0;
+    const int bins = 1 << delta;
+    TileRecords<kW> tr;
+    tr.load(a, wbase);
+    u32 node[kPartItems], rank[kPartItems];
+    bool valid[kPartItems];
+    part_nodes<kW>(a, tr, wbase, node, valid);
+    for (int i = lane; i < bins; i += 64) count[w][i] = 0;
+    {
+        u32 digit[kPartItems];
+#pragma unroll
+        for (int j = 0; j < kPartItems; ++j) digit[j] = node[j] & (bins - 1);
+        wave_rank(digit, valid, delta, count[w], rank);
+    }
+    __syncthreads();
+    if (tid < bins) {
+        // points of this digit before the tile, then before each wave
+        u32 run = a.chunk_slots[(u64)blockIdx.x * bins + tid];
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) {
+            const u32 c = count[v][tid];
+            count[v][tid] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPartItems; ++j) {
+        if (!valid[j]) continue;
+        const u32 digit = node[j] & (bins - 1);
+        const u64 pos = live_begin(a.geo, node[j], a.l1) -
+                        bin_prefix(a.geo, node[j] >> delta, digit, a.l1, delta) +
+                        count[w][digit] + rank[j];
+        if (pos < (u64)a.n_out) tr.store(a, j, wbase + (i64)j * 64, pos);
+    }
+}
+
+// Round l's nodes: the pivot of node s = F(l) + j is the record at live
+// position live_begin(j) + |S(2s+1)| of the array sorted for round l
+// ([W], sb/ss paragraph). It goes to the pivot table, perm and tree.
+__global__ __launch_bounds__(kBlock) void k_pivots(const u32* __restrict__ recs, int words,
+                                                   Geometry geo, int l, int dim,
+                                                   u64* __restrict__ piv,
+                                                   const float* __restrict__ pts, int k,
+                                                   int32_t* __restrict__ perm,
+                                                   float* __restrict__ tree) {
+    const u64 j = (u64)blockIdx.x * kBlock + threadIdx.x;
+    if (j >= (1ull << l)) return;
+    const u64 s = full_nodes(l) + j;
+    const u64 p = live_begin(geo, j, l) + subtree_size(geo, 2 * s + 1);
+    if (s >= (u64)geo.n || p >= (u64)geo.n - full_nodes(l)) return;  // not for l < L-1
+    const u32* r = recs + p * words;
+    const u32 idx = r[words - 1];
+    piv[s] = ((u64)float_key(r[dim]) << 32) | idx;
+    if (perm) perm[s] = (int32_t)idx;
+    if (tree && idx < (u64)geo.n)
+        for (int d = 0; d < k; ++d) tree[s * k + d] = pts[(u64)idx * k + d];
+}
+
+// Tags after `rounds` rounds by walking the pivots from the root (the node
+// the point reaches, or the node it became): diagnostics only.
+__global__ __launch_bounds__(kBlock) void k_descend_tags(const float* __restrict__ pts, i64 n,
+                                                         int k, int rounds,
+                                                         const u64* __restrict__ piv,
+                                                         u32* __restrict__ tags) {
+    const i64 stride = (i64)gridDim.x * kBlock;
+    for (i64 i = (i64)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride) {
+        u64 s = 0;
+        int dim = 0;
+        for (int l = 0; l < rounds; ++l) {
+            const u64 me = ((u64)float_key(__float_as_uint(pts[i * k + dim])) << 32) | (u64)i;
+            const u64 p = piv[s];
+            if (me == p) break;
+            s = me < p ? 2 * s + 1 : 2 * s + 2;
+            if (++dim == k) dim = 0;
+        }
+        tags[i] = (u32)s;
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_zero(u32* __restrict__ out, i64 n) {
+    const i64 stride = (i64)gridDim.x * kBlock;
+    for (i64 e = (i64)blockIdx.x * kBlock + threadIdx.x; e < n; e += stride) out[e] = 0u;
 }
 
 // --------------------------------------------- subtrees finished in LDS
@@ -751,7 +933,8 @@ struct SubtreeArgs {
     int k;
     int l0;                 // level of the subtree roots
     Geometry geo;
-    const u32* sorted;      // point indices in the sorted order of round l0-1 (l0 > 0)
+    const u32* recs;        // l0 > 0: records (coordinates 0 .. words-2, then the
+    int words;              // index) live on level l0-1, in round l0-1's order
     int index_bytes;        // bytes of a point index that can differ
     u32* stage;             // (k+1) x n words: index, then coordinate columns; the
                             // subtree owns [first, first + |S(c)|) of each
@@ -852,13 +1035,21 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
     const u64 c = full_nodes(a.l0) + blockIdx.x;  // subtree root (global node id)
     const u32 nc = (u32)subtree_size(a.geo, c);
     if (nc == 0) return;
-    u64 first = 0;  // where the subtree's points start in round l0-1's sorted order
+    u64 first = 0;  // live position of the subtree's first point in round l0-1's order
     if (a.l0 > 0) {
         const u64 parent = (c - 1) / 2;
-        const u64 seg = segment_begin(a.geo, parent, a.l0 - 1);
+        const u64 seg = live_begin(a.geo, parent - full_nodes(a.l0 - 1), a.l0 - 1);
         const u64 pivot = seg + subtree_size(a.geo, 2 * parent + 1);
         first = (c == 2 * parent + 1) ? seg : pivot + 1;
     }
+    // Coordinate d (bits) of the point with index i that arrived at
+    // position q: from its record while the record carries it, else from
+    // its row of `points`.
+    const int kr = a.recs ? a.words - 1 : 0;
+    auto coord = [&](u32 q, u32 i, int d) -> u32 {
+        return d < kr ? a.recs[(first + q) * a.words + d]
+                      : __float_as_uint(a.pts[(i64)i * a.k + d]);
+    };
 
     // Order the subtree's points by original index: slot e = index rank.
     u64 rec[kLocalItems];
@@ -867,13 +1058,13 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
         const int q = local_slot(j);
         rec[j] = ~0ull;
         if ((u32)q < nc) {
-            const u32 i = a.sorted ? a.sorted[first + q] : (u32)q;
+            const u32 i = a.recs ? a.recs[(first + q) * a.words + a.words - 1] : (u32)q;
             rec[j] = ((u64)i << 16) | (u32)q;
         }
     }
-    if (a.sorted) local_sort(rec, 16, a.index_bytes, nc, sh);
+    if (a.recs) local_sort(rec, 16, a.index_bytes, nc, sh);
     // Stage the subtree's points once, by index rank: their indices and their
-    // coordinate columns (each row of `points` is read exactly once here).
+    // coordinate columns (each point is read exactly once here).
     u32* stage_idx = a.stage + first;
     if (a.k <= kRowRegs) {
         // Row loads are issued kRowBatch items at a time, before their stores.
@@ -882,11 +1073,10 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
             u32 row[kRowBatch][kRowRegs];
 #pragma unroll
             for (int j = 0; j < kRowBatch; ++j) {
-                const u32 i = (u32)(rec[j0 + j] >> 16);
+                const u32 i = (u32)(rec[j0 + j] >> 16), q = (u32)(rec[j0 + j] & 0xffff);
                 const bool ok = (u32)local_slot(j0 + j) < nc;
 #pragma unroll
-                for (int d = 0; d < kRowRegs; ++d)
-                    row[j][d] = ok && d < a.k ? __float_as_uint(a.pts[(i64)i * a.k + d]) : 0u;
+                for (int d = 0; d < kRowRegs; ++d) row[j][d] = ok && d < a.k ? coord(q, i, d) : 0u;
             }
 #pragma unroll
             for (int j = 0; j < kRowBatch; ++j) {
@@ -904,11 +1094,9 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
         for (int j = 0; j < kLocalItems; ++j) {
             const int e = local_slot(j);
             if ((u32)e >= nc) continue;
-            const u32 i = (u32)(rec[j] >> 16);
+            const u32 i = (u32)(rec[j] >> 16), q = (u32)(rec[j] & 0xffff);
             stage_idx[e] = i;
-            const float* row = a.pts + (i64)i * a.k;
-            for (int d = 0; d < a.k; ++d)
-                a.stage[(u64)(d + 1) * a.n + first + e] = __float_as_uint(row[d]);
+            for (int d = 0; d < a.k; ++d) a.stage[(u64)(d + 1) * a.n + first + e] = coord(q, i, d);
             sh.tag[e] = 0;
         }
     }
@@ -920,8 +1108,8 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
     // The points arrived in round l0-1's sorted order, i.e. ordered by
     // (coordinate (l0-1) mod k, index): that is already the subtree's order
     // for that dimension (slot of the arrival position q = rec's low bits).
-    const int arrived_dim = a.sorted ? (a.l0 - 1) % a.k : -1;
-    uint16_t* arrived = a.sorted ? sh.order[cached ? a.k - 1 : 1] : nullptr;
+    const int arrived_dim = a.recs ? (a.l0 - 1) % a.k : -1;
+    uint16_t* arrived = a.recs ? sh.order[cached ? a.k - 1 : 1] : nullptr;
     if (arrived) {
 #pragma unroll
         for (int j = 0; j < kLocalItems; ++j) {
@@ -989,78 +1177,60 @@ __global__ void k_single(const float* __restrict__ pts, int k, int32_t* __restri
         for (int d = threadIdx.x; d < k; d += blockDim.x) tree[d] = pts[d];
 }
 
-// Nodes above level l0: the F(l0-1) nodes fixed before round l0-1 sit at
-// their own id in that round's sorted order, and each node s on level l0-1
-// is its segment's pivot.
-__global__ __launch_bounds__(kBlock) void k_place_top(const float* __restrict__ pts, int k,
-                                                      Geometry geo, int l0,
-                                                      const u32* __restrict__ sorted,
-                                                      int32_t* __restrict__ perm,
-                                                      float* __restrict__ tree) {
-    const u64 s = (u64)blockIdx.x * kBlock + threadIdx.x;
-    if (s >= full_nodes(l0)) return;
-    u64 p = s;
-    if (s >= full_nodes(l0 - 1))
-        p = segment_begin(geo, s, l0 - 1) + subtree_size(geo, 2 * s + 1);
-    if (p >= (u64)geo.n) return;
-    const u32 i = sorted[p];
-    perm[s] = (int32_t)i;
-    if (tree)
-        for (int d = 0; d < k; ++d) tree[(i64)s * k + d] = pts[(i64)i * k + d];
-}
-
-__global__ __launch_bounds__(kBlock) void k_copy_tags(const u32* __restrict__ tag, i64 n,
-                                                      u32* __restrict__ out) {
-    const i64 stride = (i64)gridDim.x * kBlock;
-    for (i64 e = (i64)blockIdx.x * kBlock + threadIdx.x; e < n; e += stride)
-        out[e] = tag ? tag[e] : 0u;
-}
 
 // ------------------------------------------------------------ host driver
 
 inline size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-    int kcols;          // split dimensions the global rounds can use
-    i64 tiles, chunks;
-    size_t cols, orders, ranks, next, tagq, keys0, keys1, vals0, vals1, extra0, extra1, totals,
-        slots, chunk_slots, stage, total;
+    int rounds;          // global rounds: levels fixed before the subtree stage
+    int kr;              // coordinates a record carries: dimensions 0 .. kr-1
+    int words;           // record width, kr + 1
+    int nbuf;            // record arrays
+    i64 tiles, chunks;   // of a pass over all n points
+    size_t cols, keys0, keys1, vals0, vals1, recs, piv, totals, slots, chunk_slots, part_slots,
+        stage, total;
 };
 
-bool make_layout(i64 n, int k, Layout* out) {
-    if (n < 0 || n > INT32_MAX || k < 1 || k > 65535) return false;
+// Workspace of `rounds` global rounds and, with `stage`, of the subtree stage.
+bool make_layout(i64 n, int k, int rounds, bool stage, Layout* out) {
+    if (n < 0 || n > INT32_MAX || k < 1 || k > 65535 || rounds < 0 || rounds >= kMaxRounds)
+        return false;
     Layout lay{};
     if (n <= 1) {
         *out = lay;
         return true;
     }
-    const int levels = make_geometry(n).levels;
-    // dimensions the global rounds touch: the split dimensions of rounds
-    // 0 .. L-2 plus the one whose order the last written tags are kept in
-    lay.kcols = levels < k ? levels : k;
-    lay.tiles = (n + kTile - 1) / kTile;
-    lay.chunks = (lay.tiles + kChunkTiles - 1) / kChunkTiles;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t at = off;
         off = align_up(off + bytes);
         return at;
     };
-    lay.cols = take((size_t)lay.kcols * n * sizeof(float));
-    lay.orders = take((size_t)lay.kcols * n * sizeof(u32));
-    lay.ranks = take((size_t)lay.kcols * n * sizeof(u32));
-    lay.next = take((size_t)lay.kcols * n * sizeof(u32));
-    lay.tagq = take((size_t)lay.kcols * n * sizeof(u32));
-    lay.keys0 = take((size_t)n * sizeof(u32));
-    lay.keys1 = take((size_t)n * sizeof(u32));
-    lay.vals0 = take((size_t)n * sizeof(u32));
-    lay.vals1 = take((size_t)n * sizeof(u32));
-    lay.extra0 = take((size_t)n * sizeof(u32));
-    lay.extra1 = take((size_t)n * sizeof(u32));
-    lay.totals = take((size_t)kRadix * sizeof(u32));
-    lay.slots = take((size_t)lay.tiles * kRadix * sizeof(u32));
-    lay.chunk_slots = take((size_t)lay.chunks * kRadix * sizeof(u32));
-    lay.stage = take((size_t)(k + 1) * n * sizeof(u32));
+    lay.rounds = rounds;
+    if (rounds > 0) {
+        // level l splits dimension l mod k, so the rounds use dimensions
+        // 0 .. min(k, rounds)-1
+        lay.kr = k < rounds ? k : rounds;
+        lay.words = lay.kr + 1;
+        // every dimension used again keeps its array, plus one to re-sort
+        // into (a dimension used once needs its array only for its round)
+        lay.nbuf = (k < rounds ? k : 1) + 1;
+        lay.tiles = (n + kTile - 1) / kTile;
+        lay.chunks = (lay.tiles + kChunkTiles - 1) / kChunkTiles;
+        lay.cols = take((size_t)lay.kr * n * sizeof(float));
+        lay.keys0 = take((size_t)n * sizeof(u32));
+        lay.keys1 = take((size_t)n * sizeof(u32));
+        lay.vals0 = take((size_t)n * sizeof(u32));
+        lay.vals1 = take((size_t)n * sizeof(u32));
+        lay.recs = take((size_t)lay.nbuf * n * lay.words * sizeof(u32));
+        lay.piv = take((size_t)full_nodes(rounds) * sizeof(u64));
+        lay.totals = take((size_t)kRadix * sizeof(u32));
+        lay.slots = take((size_t)lay.tiles * kRadix * sizeof(u32));
+        lay.chunk_slots = take((size_t)lay.chunks * kRadix * sizeof(u32));
+        lay.part_slots = take((size_t)((n + kPartTile - 1) / kPartTile) * kRadix * sizeof(u32));
+    }
+    if (stage) lay.stage = take((size_t)(k + 1) * n * sizeof(u32));
     lay.total = off;
     *out = lay;
     return true;
@@ -1129,189 +1299,187 @@ struct Timer {  // no-op unless a Profiler is attached
     void end() { if (p) p->end(); }
 };
 
-// Launches the three kernels of one radix pass.
-struct PassLauncher {
-    const Layout& lay;
+// Kernel names as the profiler prints them, per record width 0, 2, 3, 4.
+int width_slot(int words) { return words == 2 ? 1 : words == 3 ? 2 : words == 4 ? 3 : 0; }
+const char* const kRecordScatterNames[4] = {"k_tile_scatter<1, 1, 0>", "k_tile_scatter<1, 1, 2>",
+                                            "k_tile_scatter<1, 1, 3>", "k_tile_scatter<1, 1, 4>"};
+const char* const kPartCountNames[4] = {"k_part_count<0>", "k_part_count<2>", "k_part_count<3>",
+                                        "k_part_count<4>"};
+const char* const kPartScatterNames[4] = {"k_part_scatter<0>", "k_part_scatter<2>",
+                                          "k_part_scatter<3>", "k_part_scatter<4>"};
+
+struct Launcher {
     u32* tile_counts;
     u32* chunk_slots;
+    u32* part_slots;
+    u32* totals;
     hipStream_t stream;
     Timer timer;
 
-    template <int kSrc, int kSink, bool kTags = false>
-    void run(PassArgs a) {
+    // One stable pass of the presort (count, scan, scatter).
+    template <int kSrc, int kSink, int kW>
+    void pass(PassArgs a) {
         a.tile_counts = tile_counts;
         a.chunk_slots = chunk_slots;
-        // this pass's records (at most the layout's n)
-        const i64 tiles64 = (a.n + kTile - 1) / kTile;
-        const unsigned tiles = (unsigned)tiles64;
-        const unsigned chunks = (unsigned)((tiles64 + kChunkTiles - 1) / kChunkTiles);
+        a.digit_totals = totals;
+        const i64 tiles = (a.n + kTile - 1) / kTile;
+        const i64 chunks = (tiles + kChunkTiles - 1) / kChunkTiles;
         const double n = (double)a.n;
-        static const char* const count_names[2] = {"k_tile_count<0>", "k_tile_count<1>"};
-        // [kSrc][kSink][extra][kTags], as the profiler prints the kernels
-        static const char* const scatter_names[2][3][2][2] = {
-            {{{"k_tile_scatter<0, 0, false, false>", "k_tile_scatter<0, 0, false, true>"},
-              {"k_tile_scatter<0, 0, true, false>", "k_tile_scatter<0, 0, true, true>"}},
-             {{"k_tile_scatter<0, 1, false, false>", "k_tile_scatter<0, 1, false, true>"},
-              {"k_tile_scatter<0, 1, true, false>", "k_tile_scatter<0, 1, true, true>"}},
-             {{"k_tile_scatter<0, 2, false, false>", "k_tile_scatter<0, 2, false, true>"},
-              {"k_tile_scatter<0, 2, true, false>", "k_tile_scatter<0, 2, true, true>"}}},
-            {{{"k_tile_scatter<1, 0, false, false>", "k_tile_scatter<1, 0, false, true>"},
-              {"k_tile_scatter<1, 0, true, false>", "k_tile_scatter<1, 0, true, true>"}},
-             {{"k_tile_scatter<1, 1, false, false>", "k_tile_scatter<1, 1, false, true>"},
-              {"k_tile_scatter<1, 1, true, false>", "k_tile_scatter<1, 1, true, true>"}},
-             {{"k_tile_scatter<1, 2, false, false>", "k_tile_scatter<1, 2, false, true>"},
-              {"k_tile_scatter<1, 2, true, false>", "k_tile_scatter<1, 2, true, true>"}}}};
-        const bool extra = a.extra_in != nullptr;
-        timer.begin(count_names[kSrc], n * 4);  // keys (or the column)
-        k_tile_count<kSrc><<<chunks, kCountBlock, 0, stream>>>(a);
+        timer.begin(kSrc == kSrcColumn ? "k_tile_count<0>" : "k_tile_count<1>", n * 4);
+        k_tile_count<kSrc><<<(unsigned)chunks, kCountBlock, 0, stream>>>(a);
         timer.end();
         timer.begin("k_tile_scan", (double)chunks * kRadix * 8);
-        k_tile_scan<<<kRadix, kBlock, 0, stream>>>(chunk_slots, chunks, a.digit_totals);
+        k_tile_scan<<<kRadix, kBlock, 0, stream>>>(chunk_slots, chunks, kRadix, totals);
         timer.end();
-        // in: column (4) or key+val (8); out: key+val (8) or one word (4)
-        const double in = (kSrc == kSrcColumn ? 4 : 8) + (extra ? 4 : 0);
-        const double out = (kSink == kSinkArrays ? 8 : 4) + (extra ? 4 : 0) + (a.rank_out ? 4 : 0);
-        timer.begin(scatter_names[kSrc][kSink][extra][kTags], n * (in + out));
-        if (extra)
-            k_tile_scatter<kSrc, kSink, true, kTags><<<tiles, kBlock, 0, stream>>>(a);
-        else
-            k_tile_scatter<kSrc, kSink, false, kTags><<<tiles, kBlock, 0, stream>>>(a);
+        // in: the column (4) or key + val (8); out: key + val (8), or the
+        // gathered row and the record
+        const double in = kSrc == kSrcColumn ? 4 : 8;
+        const double out = kSink == kSinkArrays ? 8 : 4.0 * (a.words - 1) + 4.0 * a.words;
+        const char* name = kSink == kSinkRecords ? kRecordScatterNames[width_slot(a.words)]
+                           : kSrc == kSrcColumn  ? "k_tile_scatter<0, 0, 0>"
+                                                 : "k_tile_scatter<1, 0, 0>";
+        timer.begin(name, n * (in + out));
+        k_tile_scatter<kSrc, kSink, kW><<<(unsigned)tiles, kBlock, 0, stream>>>(a);
         timer.end();
+    }
+
+    // One re-sort pass by tag (count, scan, scatter).
+    template <int kW>
+    void part(PartArgs a) {
+        a.chunk_slots = part_slots;  // one row of digit counts per tile
+        const i64 tiles = (a.n_in + kPartTile - 1) / kPartTile;
+        const int bins = 1 << (a.l1 - a.l0);
+        const double rec = 4.0 * a.words;
+        timer.begin(kPartCountNames[width_slot(kW)], (double)a.n_in * rec);
+        k_part_count<kW><<<(unsigned)tiles, kBlock, 0, stream>>>(a);
+        timer.end();
+        timer.begin("k_tile_scan", (double)tiles * bins * 8);
+        k_tile_scan<<<bins, kBlock, 0, stream>>>(part_slots, tiles, bins, nullptr);
+        timer.end();
+        timer.begin(kPartScatterNames[width_slot(kW)], (double)(a.n_in + a.n_out) * rec);
+        k_part_scatter<kW><<<(unsigned)tiles, kBlock, 0, stream>>>(a);
+        timer.end();
+    }
+    void part_any(const PartArgs& a) {
+        switch (a.words) {
+            case 2: part<2>(a); break;
+            case 3: part<3>(a); break;
+            case 4: part<4>(a); break;
+            default: part<0>(a); break;
+        }
     }
 };
 
-// Runs rounds 0 .. rounds-1 on the whole point set. With keep_sorted the
-// last round writes its sorted order (point indices, returned in
-// *sorted_out) instead of updating the tags. Otherwise the tags after
-// `rounds` rounds are left in tagq of dimension rounds mod k, in that
-// dimension's (coordinate, index) order, which *tags_dim returns.
-kdt_status run_rounds(const float* pts, i64 n, int k, int rounds, char* ws, const Layout& lay,
-                      hipStream_t stream, Timer timer, bool keep_sorted,
-                      const u32** sorted_out, int* tags_dim) {
+// Global rounds 0 .. lay.rounds-1 over all points: presorts each dimension
+// at its first use, re-sorts one array per round and writes the pivots of
+// every level to the pivot table (and to perm / tree when given). On return
+// *last holds the array of round rounds-1 (live on that level).
+kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* ws,
+                      hipStream_t stream, Timer timer, int32_t* perm, float* tree,
+                      const u32** last) {
+    const int R = lay.rounds, W = lay.words;
     const Geometry geo = make_geometry(n);
-    const int writes = keep_sorted ? rounds - 1 : rounds;  // rounds that write tags
-    // dimensions touched: split dimensions of rounds 0 .. rounds-1 and the
-    // one each written round hands its tags to
-    const int span = writes + 1 > rounds ? writes + 1 : rounds;
-    const int kc = span < k ? span : k;
     float* cols = (float*)(ws + lay.cols);
-    u32* totals = (u32*)(ws + lay.totals);
     u32* keys[2] = {(u32*)(ws + lay.keys0), (u32*)(ws + lay.keys1)};
     u32* vals[2] = {(u32*)(ws + lay.vals0), (u32*)(ws + lay.vals1)};
-    auto order = [&](int d) { return (u32*)(ws + lay.orders) + (size_t)d * n; };
-    auto rank = [&](int d) { return (u32*)(ws + lay.ranks) + (size_t)d * n; };
-    auto next = [&](int d) { return (u32*)(ws + lay.next) + (size_t)d * n; };
-    auto tagq = [&](int d) { return (u32*)(ws + lay.tagq) + (size_t)d * n; };
-    PassLauncher pass{lay, (u32*)(ws + lay.slots), (u32*)(ws + lay.chunk_slots), stream, timer};
+    u64* piv = (u64*)(ws + lay.piv);
+    auto recs = [&](int b) { return (u32*)(ws + lay.recs) + (size_t)b * n * W; };
+    Launcher launch{(u32*)(ws + lay.slots), (u32*)(ws + lay.chunk_slots),
+                    (u32*)(ws + lay.part_slots), (u32*)(ws + lay.totals), stream, timer};
     const double N = (double)n;
-    const int grid = grid_for(n, kBlock, 1 << 30);  // one element per thread: more writes in flight
 
-    timer.begin("k_init", N * kc * 8);
-    k_init<<<grid, kBlock, 0, stream>>>(pts, n, k, kc, cols);
+    timer.begin("k_init", N * lay.kr * 8);
+    k_init<<<grid_for(n, kBlock, 1 << 30), kBlock, 0, stream>>>(pts, n, k, lay.kr, cols);
     timer.end();
 
-    // next_d maps the r-th point of order_d to its position in order_(d+1):
-    // round l's new tags go straight to where round l+1 reads them. For
-    // d >= 1 the presort of d carries rank_(d+1) (a point's position in
-    // order_(d+1), in index order) as a second payload, so its sorted output
-    // is next_d; the dimensions are presorted as 0, kc-1, ..., 1 so that
-    // rank_(d+1) exists by then. next_0 comes from two scattered ranks.
-    const int knext = writes < k ? writes : k;  // next_d needed for d < knext
-    u32* extra[2] = {(u32*)(ws + lay.extra0), (u32*)(ws + lay.extra1)};
-    for (int step = 0; step < kc; ++step) {
-        const int d = step == 0 ? 0 : kc - step;
-        const float* col = cols + (size_t)d * n;
-        const bool carry = d >= 1 && d < knext;
-        // Presort: order_d = point indices by (coordinate d, index). Pass p
-        // reads buffer (p+1)&1 and writes buffer p&1; the last writes order_d.
-        for (int p = 0; p < kKeyBytes; ++p) {
-            PassArgs a{};
-            a.n = n;
-            a.n_all = n;
-            a.shift = 8 * p;
-            a.col = col;
-            a.keys_in = keys[(p + 1) & 1];
-            a.vals_in = vals[(p + 1) & 1];
-            a.keys_out = keys[p & 1];
-            a.vals_out = p == kKeyBytes - 1 ? order(d) : vals[p & 1];
-            if (carry) {
-                a.extra_in = p == 0 ? rank((d + 1) % k) : extra[(p + 1) & 1];
-                a.extra_out = p == kKeyBytes - 1 ? next(d) : extra[p & 1];
-            }
-            if (p == kKeyBytes - 1 && knext > 0) a.rank_out = rank(d);
-            a.digit_totals = totals;
-            if (p == 0)
-                pass.run<kSrcColumn, kSinkArrays>(a);
-            else if (p < kKeyBytes - 1)
-                pass.run<kSrcArrays, kSinkArrays>(a);
-            else
-                pass.run<kSrcArrays, kSinkVals>(a);
-        }
-    }
-    if (knext > 0) {
-        timer.begin("k_cross", N * 12);
-        k_cross<<<grid, kBlock, 0, stream>>>(rank(0), rank(1 % k), n, next(0));
-        timer.end();
-    }
+    int holder[kMaxRounds + 1];  // dimension whose array a buffer holds, or -1
+    for (int b = 0; b <= kMaxRounds; ++b) holder[b] = -1;
+    int buf_of[kMaxRounds], level_of[kMaxRounds];
+    auto take = [&](int avoid) {
+        for (int b = 0; b < lay.nbuf; ++b)
+            if (holder[b] < 0 && b != avoid) return b;
+        return -1;
+    };
 
-    // Round 0: all tags are 0.
-    if (writes == 0) {
-        *sorted_out = order(0);  // keep_sorted with a single round
-    } else {
-        timer.begin("k_round0", N * 8);
-        k_round0<<<grid, kBlock, 0, stream>>>(next(0), geo, tagq(1 % k));
-        timer.end();
-    }
-
-    // Round l: stable sort of the records (tag, next_d[r]) -- or (tag, point
-    // index) in the final round -- kept in order_d order, by tag, one pass
-    // per byte of the live tags' offset from F(l); pass p reads buffer p&1
-    // and writes buffer (p+1)&1. The F(l) fixed records are not sorted: the
-    // first pass writes them straight to where they end up (their tag for
-    // the next round, or their node's slot of the sorted order), and later
-    // passes see only the N - F(l) live records.
-    for (int l = 1; l < rounds; ++l) {
+    for (int l = 0; l < R; ++l) {
         const int d = l % k;
-        const int passes = tag_passes(l);
-        const bool final = keep_sorted && l == rounds - 1;
-        const u32 fl = (u32)full_nodes(l);
-        u32* sorted = vals[passes & 1];  // final round: the whole sorted order
-        for (int p = 0; p < passes; ++p) {
-            PassArgs a{};
-            a.n = p == 0 ? n : n - (i64)fl;
-            a.n_all = n;
-            a.shift = 8 * p;
-            a.key_base = fl;
-            a.digit_totals = totals;
-            a.geo = geo;
-            a.round = l;
-            a.keys_in = p == 0 ? tagq(d) : keys[p & 1];
-            a.vals_in = p == 0 ? (final ? order(d) : next(d)) : vals[p & 1];
-            a.keys_out = keys[(p + 1) & 1];
-            a.vals_out = vals[(p + 1) & 1];
-            a.tag_out = tagq((l + 1) % k);
-            if (final) a.fixed_vals = sorted;
-            else a.fixed_tags = a.tag_out;
-            const bool last = p == passes - 1;
-            if (!last) {
-                pass.run<kSrcArrays, kSinkArrays, true>(a);
-            } else if (final) {
-                a.vals_out = sorted + fl;  // live records follow the F(l) fixed ones
-                *sorted_out = sorted;
-                pass.run<kSrcArrays, kSinkVals, true>(a);
-            } else {
-                pass.run<kSrcArrays, kSinkTags, true>(a);
+        if (l < k) {
+            // First use of dimension d: A_d = the points by (coordinate d,
+            // index), one level-0 segment. Pass p reads buffer (p+1)&1 and
+            // writes buffer p&1; the last one writes the records.
+            const int b = take(-1);
+            if (b < 0) return KDT_ERR_WORKSPACE;  // cannot happen: nbuf covers the rounds
+            for (int p = 0; p < kKeyBytes; ++p) {
+                PassArgs a{};
+                a.n = n;
+                a.shift = 8 * p;
+                a.col = cols + (size_t)d * n;
+                a.keys_in = keys[(p + 1) & 1];
+                a.vals_in = vals[(p + 1) & 1];
+                a.keys_out = keys[p & 1];
+                a.vals_out = vals[p & 1];
+                a.recs_out = recs(b);
+                a.words = W;
+                a.pts = pts;
+                a.k = k;
+                if (p == 0) {
+                    launch.pass<kSrcColumn, kSinkArrays, 0>(a);
+                } else if (p < kKeyBytes - 1) {
+                    launch.pass<kSrcArrays, kSinkArrays, 0>(a);
+                } else {
+                    switch (W) {
+                        case 2: launch.pass<kSrcArrays, kSinkRecords, 2>(a); break;
+                        case 3: launch.pass<kSrcArrays, kSinkRecords, 3>(a); break;
+                        case 4: launch.pass<kSrcArrays, kSinkRecords, 4>(a); break;
+                        default: launch.pass<kSrcArrays, kSinkRecords, 0>(a); break;
+                    }
+                }
             }
+            holder[b] = d;
+            buf_of[d] = b;
+            level_of[d] = 0;
         }
+        // Bring A_d from the tags of its last use to the level-l tags, at
+        // most kMaxDescent levels per pass.
+        while (level_of[d] < l) {
+            const int l1 = level_of[d] + kMaxDescent < l ? level_of[d] + kMaxDescent : l;
+            const int b = take(buf_of[d]);
+            if (b < 0) return KDT_ERR_WORKSPACE;
+            PartArgs a{};
+            a.in = recs(buf_of[d]);
+            a.out = recs(b);
+            a.n_in = n - (i64)full_nodes(level_of[d]);
+            a.n_out = n - (i64)full_nodes(l1);
+            a.words = W;
+            a.k = k;
+            a.l0 = level_of[d];
+            a.l1 = l1;
+            a.dim0 = level_of[d] % k;
+            a.geo = geo;
+            a.piv = piv;
+            launch.part_any(a);
+            holder[buf_of[d]] = -1;
+            holder[b] = d;
+            buf_of[d] = b;
+            level_of[d] = l1;
+        }
+        // Round l's nodes and their pivots.
+        const u64 nodes = 1ull << l;
+        timer.begin("k_pivots", (double)nodes * (4.0 * W + 8 + (perm ? 4 : 0) + (tree ? 8.0 * k : 0)));
+        k_pivots<<<(unsigned)((nodes + kBlock - 1) / kBlock), kBlock, 0, stream>>>(
+            recs(buf_of[d]), W, geo, l, d, piv, pts, k, perm, tree);
+        timer.end();
+        // A dimension not split on again frees its array (except the last
+        // round's, which the subtree stage reads).
+        if (l + k >= R && l != R - 1) holder[buf_of[d]] = -1;
     }
-    if (tags_dim) *tags_dim = rounds % k;
+    *last = recs(buf_of[(R - 1) % k]);
     return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
 }
 
 kdt_status validate(const float* pts, i64 n, int k, const void* out0, size_t out0_bytes,
                     const void* out1, size_t out1_bytes, void* ws, size_t ws_bytes,
-                    Layout* lay) {
-    if (!make_layout(n, k, lay)) return KDT_ERR_INVALID_ARG;
+                    const Layout& lay) {
     if (n == 0) return KDT_OK;
     if (!pts || !out0) return KDT_ERR_INVALID_ARG;
     const size_t pts_bytes = (size_t)n * k * sizeof(float);
@@ -1319,19 +1487,23 @@ kdt_status validate(const float* pts, i64 n, int k, const void* out0, size_t out
         ranges_overlap(pts, pts_bytes, out1, out1_bytes) ||
         ranges_overlap(out0, out0_bytes, out1, out1_bytes))
         return KDT_ERR_INVALID_ARG;
-    if (lay->total > 0) {
-        if (!ws || ws_bytes < lay->total || ((uintptr_t)ws & 255)) return KDT_ERR_WORKSPACE;
-        if (ranges_overlap(ws, lay->total, pts, pts_bytes) ||
-            ranges_overlap(ws, lay->total, out0, out0_bytes) ||
-            ranges_overlap(ws, lay->total, out1, out1_bytes))
+    if (lay.total > 0) {
+        if (!ws || ws_bytes < lay.total || ((uintptr_t)ws & 255)) return KDT_ERR_WORKSPACE;
+        if (ranges_overlap(ws, lay.total, pts, pts_bytes) ||
+            ranges_overlap(ws, lay.total, out0, out0_bytes) ||
+            ranges_overlap(ws, lay.total, out1, out1_bytes))
             return KDT_ERR_INVALID_ARG;
     }
     return KDT_OK;
 }
 
+bool valid_size(i64 n, int k) { return n >= 0 && n <= INT32_MAX && k >= 1 && k <= 65535; }
+
 // First level whose subtrees all fit one workgroup (the leftmost subtree of
 // a level is the largest one).
-int split_level(const Geometry& g) {
+int split_level(i64 n) {
+    if (n <= 1) return 0;
+    const Geometry g = make_geometry(n);
     int l = 0;
     while (subtree_size(g, full_nodes(l)) > (u64)kLocalMax) ++l;
     return l;
@@ -1340,11 +1512,14 @@ int split_level(const Geometry& g) {
 kdt_status build_impl(const float* points, int64_t N, int32_t k, int32_t* perm_out,
                       float* tree_out, void* workspace, size_t workspace_bytes,
                       hipStream_t stream, Timer timer) {
+    if (!valid_size(N, k)) return KDT_ERR_INVALID_ARG;
+    const int l0 = split_level(N);
     Layout lay;
-    const size_t perm_bytes = (size_t)(N > 0 ? N : 0) * sizeof(int32_t);
-    const size_t tree_bytes = tree_out ? (size_t)(N > 0 ? N : 0) * (k > 0 ? k : 0) * sizeof(float) : 0;
+    if (!make_layout(N, k, l0, true, &lay)) return KDT_ERR_INVALID_ARG;
+    const size_t perm_bytes = (size_t)N * sizeof(int32_t);
+    const size_t tree_bytes = tree_out ? (size_t)N * k * sizeof(float) : 0;
     kdt_status st = validate(points, N, k, perm_out, perm_bytes, tree_out, tree_bytes, workspace,
-                             workspace_bytes, &lay);
+                             workspace_bytes, lay);
     if (st != KDT_OK || N == 0) return st;
     if (N == 1) {
         timer.begin("k_single", 4.0 + (tree_out ? 8.0 * k : 0));
@@ -1353,18 +1528,11 @@ kdt_status build_impl(const float* points, int64_t N, int32_t k, int32_t* perm_o
         return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
     }
     const Geometry geo = make_geometry(N);
-    const int l0 = split_level(geo);
-    const u32* sorted = nullptr;
+    const u32* recs = nullptr;
     if (l0 > 0) {
-        // Global rounds 0 .. l0-1; the last one leaves its sorted order.
-        st = run_rounds(points, N, k, l0, (char*)workspace, lay, stream, timer, true, &sorted,
-                        nullptr);
+        st = run_global(points, N, k, lay, (char*)workspace, stream, timer, perm_out, tree_out,
+                        &recs);
         if (st != KDT_OK) return st;
-        const u64 top = full_nodes(l0);
-        timer.begin("k_place_top", (double)top * (4 + 4 + (tree_out ? 8.0 * k : 0)));
-        k_place_top<<<(unsigned)((top + kBlock - 1) / kBlock), kBlock, 0, stream>>>(
-            points, k, geo, l0, sorted, perm_out, tree_out);
-        timer.end();
     }
     SubtreeArgs sa{};
     sa.pts = points;
@@ -1372,7 +1540,8 @@ kdt_status build_impl(const float* points, int64_t N, int32_t k, int32_t* perm_o
     sa.k = k;
     sa.l0 = l0;
     sa.geo = geo;
-    sa.sorted = sorted;
+    sa.recs = recs;
+    sa.words = lay.words;
     int bits = 0;
     for (u64 v = (u64)(N - 1); v; v >>= 1) ++bits;
     sa.index_bytes = (bits + kRadixBits - 1) / kRadixBits;
@@ -1380,11 +1549,11 @@ kdt_status build_impl(const float* points, int64_t N, int32_t k, int32_t* perm_o
     sa.perm = perm_out;
     sa.tree = tree_out;
     const i64 below = N - (i64)full_nodes(l0);  // points in the level-l0 subtrees
-    // indices in (when l0 > 0), one row gathered, index + row staged and read
-    // back, perm and tree out
+    // the record (or the row) in, index + row staged and read back, perm and
+    // tree out
     const double row = 4.0 * k;
-    timer.begin("k_subtree", (double)below * ((l0 > 0 ? 4 : 0) + row + 2 * (4 + row) + 4 +
-                                             (tree_out ? row : 0)));
+    const double in = l0 > 0 ? 4.0 * lay.words + 4.0 * (k - lay.kr) : row;
+    timer.begin("k_subtree", (double)below * (in + 2 * (4 + row) + 4 + (tree_out ? row : 0)));
     k_subtree<<<(unsigned)(1ull << l0), kLocalBlock, 0, stream>>>(sa);
     timer.end();
     return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
@@ -1395,8 +1564,17 @@ kdt_status build_impl(const float* points, int64_t N, int32_t k, int32_t* perm_o
 extern "C" {
 
 size_t kdt_workspace_size(int64_t N, int32_t k) {
+    if (!valid_size(N, k)) return 0;
     Layout lay;
-    if (!make_layout(N, k, &lay)) return 0;
+    if (!make_layout(N, k, split_level(N), true, &lay)) return 0;
+    return lay.total;
+}
+
+size_t kdt_debug_workspace_size(int64_t N, int32_t k, int32_t rounds) {
+    if (!valid_size(N, k) || N <= 1) return 0;
+    if (rounds < 0 || rounds > make_geometry(N).levels - 1) return 0;
+    Layout lay;
+    if (!make_layout(N, k, rounds, false, &lay)) return 0;
     return lay.total;
 }
 
@@ -1434,7 +1612,7 @@ kdt_status kdt_build_profiled(const float* points, int64_t N, int32_t k, int32_t
         (void)hipEventDestroy(prof->recs[i].start);
         (void)hipEventDestroy(prof->recs[i].stop);
     }
-    if (prof->failed && st == KDT_OK) st = KDT_ERR_HIP;  // event API failure or > 32 kernels
+    if (prof->failed && st == KDT_OK) st = KDT_ERR_HIP;  // event API failure or too many kinds
     delete prof;
     return st;
 }
@@ -1442,24 +1620,27 @@ kdt_status kdt_build_profiled(const float* points, int64_t N, int32_t k, int32_t
 kdt_status kdt_debug_tags(const float* points, int64_t N, int32_t k, int32_t rounds,
                           uint32_t* tags_out, void* workspace, size_t workspace_bytes,
                           hipStream_t stream) {
-    Layout lay;
-    const size_t tag_bytes = (size_t)(N > 0 ? N : 0) * sizeof(u32);
-    kdt_status st = validate(points, N, k, tags_out, tag_bytes, nullptr, 0, workspace,
-                             workspace_bytes, &lay);
-    if (st != KDT_OK || N == 0) return st;
+    if (!valid_size(N, k)) return KDT_ERR_INVALID_ARG;
+    if (N == 0) return KDT_OK;
     const int max_rounds = make_geometry(N).levels - 1;
     if (rounds < 0 || rounds > max_rounds) return KDT_ERR_INVALID_ARG;
+    Layout lay;
+    if (!make_layout(N, k, rounds, false, &lay)) return KDT_ERR_INVALID_ARG;
+    const size_t tag_bytes = (size_t)N * sizeof(u32);
+    kdt_status st = validate(points, N, k, tags_out, tag_bytes, nullptr, 0, workspace,
+                             workspace_bytes, lay);
+    if (st != KDT_OK) return st;
+    const int grid = grid_for(N, kBlock * 4, 8192);
     if (rounds == 0) {
-        k_copy_tags<<<grid_for(N, kBlock * 4, 8192), kBlock, 0, stream>>>(nullptr, N, tags_out);
+        k_zero<<<grid, kBlock, 0, stream>>>(tags_out, N);
         return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
     }
-    int d = 0;
-    st = run_rounds(points, N, k, rounds, (char*)workspace, lay, stream, Timer{nullptr}, false,
-                    nullptr, &d);
+    const u32* last = nullptr;
+    st = run_global(points, N, k, lay, (char*)workspace, stream, Timer{nullptr}, nullptr, nullptr,
+                    &last);
     if (st != KDT_OK) return st;
-    const u32* tagq = (const u32*)((char*)workspace + lay.tagq) + (size_t)d * N;
-    const u32* order = (const u32*)((char*)workspace + lay.orders) + (size_t)d * N;
-    k_unpermute<<<grid_for(N, kBlock * 4, 8192), kBlock, 0, stream>>>(tagq, order, N, tags_out);
+    k_descend_tags<<<grid, kBlock, 0, stream>>>(points, N, k, rounds,
+                                               (const u64*)((char*)workspace + lay.piv), tags_out);
     return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
 }
 
@@ -1476,10 +1657,20 @@ int64_t kdt_closed_segment_begin(int64_t N, int64_t s, int32_t l) {
     return (int64_t)segment_begin(g, (u64)s, l);
 }
 
-int32_t kdt_round_passes(int64_t N, int32_t l) {
-    if (N <= 1 || N > INT32_MAX) return -1;
-    if (l < 0 || l >= make_geometry(N).levels - 1) return -1;
-    return l == 0 ? 0 : tag_passes(l);
+int64_t kdt_closed_live_segment(int64_t N, int32_t l, int64_t p) {
+    if (N <= 0 || N > INT32_MAX) return -1;
+    const Geometry g = make_geometry(N);
+    if (l < 0 || l >= g.levels || p < 0 || p >= N - (int64_t)full_nodes(l)) return -1;
+    return (int64_t)live_segment(g, (u64)p, l);
+}
+
+int64_t kdt_closed_bin_prefix(int64_t N, int32_t l1, int32_t delta, int64_t j0, int64_t b) {
+    if (N <= 0 || N > INT32_MAX) return -1;
+    const Geometry g = make_geometry(N);
+    if (l1 < 0 || l1 >= g.levels || delta < 0 || delta > l1 || delta > kMaxDescent) return -1;
+    if (j0 < 0 || j0 > (int64_t)(1ull << (l1 - delta)) || b < 0 || b >= (int64_t)(1ull << delta))
+        return -1;
+    return (int64_t)bin_prefix(g, (u64)j0, (u32)b, l1, delta);
 }
 
 const char* kdt_status_string(kdt_status status) {

@@ -46,7 +46,9 @@ SIGNATURES = {
                                           ctypes.POINTER(Profile)]),
     "kdt_closed_subtree_size": (_I64, [_I64, _I64]),
     "kdt_closed_segment_begin": (_I64, [_I64, _I64, _I32]),
-    "kdt_round_passes": (_I32, [_I64, _I32]),
+    "kdt_debug_workspace_size": (_SZ, [_I64, _I32, _I32]),
+    "kdt_closed_live_segment": (_I64, [_I64, _I32, _I64]),
+    "kdt_closed_bin_prefix": (_I64, [_I64, _I32, _I32, _I64, _I64]),
     "kdt_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -90,8 +92,16 @@ def closed_segment_begin(n: int, s: int, level: int) -> int:
     return int(lib().kdt_closed_segment_begin(int(n), int(s), int(level)))
 
 
-def round_passes(n: int, level: int) -> int:
-    return int(lib().kdt_round_passes(int(n), int(level)))
+def debug_workspace_size(n: int, k: int, rounds: int) -> int:
+    return int(lib().kdt_debug_workspace_size(int(n), int(k), int(rounds)))
+
+
+def closed_live_segment(n: int, level: int, p: int) -> int:
+    return int(lib().kdt_closed_live_segment(int(n), int(level), int(p)))
+
+
+def closed_bin_prefix(n: int, l1: int, delta: int, j0: int, b: int) -> int:
+    return int(lib().kdt_closed_bin_prefix(int(n), int(l1), int(delta), int(j0), int(b)))
 
 
 def _check(status: int, where: str):
@@ -160,14 +170,16 @@ class Builder:
         return prof.as_dict()
 
     def debug_tags(self, points, rounds: int, stream=None):
-        """int32 tensor holding the uint32 tags after `rounds` rounds."""
+        """int32 tensor holding the uint32 tags after `rounds` rounds (uses a
+        workspace of its own, sized by kdt_debug_workspace_size)."""
         import torch
         _validate_points(points)
         out = torch.empty(self.n, dtype=torch.int32, device=points.device)
+        nbytes = debug_workspace_size(self.n, self.k, rounds)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=points.device)
         st = lib().kdt_debug_tags(ctypes.c_void_p(points.data_ptr()), self.n, self.k, int(rounds),
-                                  ctypes.c_void_p(out.data_ptr()),
-                                  ctypes.c_void_p(self.workspace.data_ptr()), self.workspace_bytes,
-                                  _stream_handle(points.device, stream))
+                                  ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
+                                  nbytes, _stream_handle(points.device, stream))
         _check(st, "kdt_debug_tags")
         return out
 
