@@ -154,6 +154,38 @@ __host__ __device__ inline u64 bin_prefix(const Geometry& g, u64 j0, u32 b, int 
     return h;
 }
 
+// The same closed forms for one level in 32-bit arithmetic (every value is
+// at most N < 2^31), with the level's constants precomputed: u = 2^dd,
+// q = M >> dd, r = M mod u.
+struct LevelShape {
+    u32 dd, q, r, last;  // last = M
+};
+
+inline LevelShape level_shape(const Geometry& g, int l) {
+    LevelShape s;
+    s.dd = (u32)(g.levels - 1 - l);
+    s.q = (u32)((u64)g.last >> s.dd);
+    s.r = (u32)((u64)g.last & ((1ull << s.dd) - 1));
+    s.last = (u32)g.last;
+    return s;
+}
+
+__device__ inline u32 live_begin32(const LevelShape& s, u32 j) {
+    const u32 under = j << s.dd;
+    return j * ((1u << s.dd) - 1) + (under < s.last ? under : s.last);
+}
+
+__device__ inline u32 bin_prefix32(const LevelShape& s, u32 j0, u32 b, int delta) {
+    const u32 u = 1u << s.dd;
+    u32 h = j0 * (u - 1);
+    if (s.q > b) {
+        const u32 c = ((s.q - b - 1) >> delta) + 1;
+        h += u * (c < j0 ? c : j0);
+    }
+    if (s.q >= b && ((s.q - b) & ((1u << delta) - 1)) == 0 && ((s.q - b) >> delta) < j0) h += s.r;
+    return h;
+}
+
 // Order-preserving map of float bits to unsigned: IEEE order with -0 == +0.
 // Pure bit tests, so denormals are never flushed.
 __host__ __device__ inline u32 float_key(u32 b) {
@@ -527,6 +559,7 @@ struct PartArgs {
     int l0, l1;        // levels before and after (1 <= l1 - l0 <= kMaxDescent)
     int dim0;          // l0 mod k
     Geometry geo;
+    LevelShape s0, s1; // the closed-form constants of levels l0 and l1
     const u64* piv;    // pivot of node s: key(coordinate) << 32 | index
     u32* chunk_slots;  // tiles x bins: digit counts of each tile, then the
                        //   counts of the digit in the tiles before it
@@ -608,12 +641,25 @@ template <int kW>
 __device__ __forceinline__ void part_nodes(const PartArgs& a, const TileRecords<kW>& tr,
                                            i64 wbase, u32 (&node)[kPartItems],
                                            bool (&valid)[kPartItems]) {
+    // Level-l0 segment of each record: one division for the wave's first
+    // record, then each lane steps over the segment starts it passes (its
+    // records are 64 positions apart, in increasing order).
+    const u32 wfirst = (u32)(wbase - (threadIdx.x & 63));
+    u32 j0 = (u32)live_segment(a.geo, wfirst, a.l0);
+    u32 next = live_begin32(a.s0, j0 + 1);
 #pragma unroll
     for (int j = 0; j < kPartItems; ++j) {
-        const i64 e = wbase + (i64)j * 64;
-        valid[j] = e < a.n_in;
-        node[j] = (u32)full_nodes(a.l0) + (valid[j] ? (u32)live_segment(a.geo, (u64)e, a.l0) : 0u);
+        const u32 e = (u32)(wbase + (i64)j * 64);
+        valid[j] = e < (u64)a.n_in;
+        if (valid[j]) {
+            while (e >= next) {
+                ++j0;
+                next = live_begin32(a.s0, j0 + 1);
+            }
+        }
+        node[j] = (u32)full_nodes(a.l0) + j0;
     }
+    // One level at a time: compare with the pivot of the current node.
     int dim = a.dim0;
     for (int l = a.l0; l < a.l1; ++l) {
 #pragma unroll
@@ -703,9 +749,9 @@ __global__ __launch_bounds__(kBlock) void k_part_scatter(PartArgs a) {
     for (int j = 0; j < kPartItems; ++j) {
         if (!valid[j]) continue;
         const u32 digit = node[j] & (bins - 1);
-        const u64 pos = live_begin(a.geo, node[j], a.l1) -
-                        bin_prefix(a.geo, node[j] >> delta, digit, a.l1, delta) +
-                        count[w][digit] + rank[j];
+        const u32 pos = live_begin32(a.s1, node[j]) -
+                        bin_prefix32(a.s1, node[j] >> delta, digit, delta) + count[w][digit] +
+                        rank[j];
         if (pos < (u64)a.n_out) tr.store(a, j, wbase + (i64)j * 64, pos);
     }
 }
@@ -1456,6 +1502,8 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
             a.l1 = l1;
             a.dim0 = level_of[d] % k;
             a.geo = geo;
+            a.s0 = level_shape(geo, a.l0);
+            a.s1 = level_shape(geo, a.l1);
             a.piv = piv;
             launch.part_any(a);
             holder[buf_of[d]] = -1;
