@@ -52,16 +52,12 @@ constexpr int kRadixBits = 8;
 constexpr int kRadix = 1 << kRadixBits;
 constexpr int kBlock = 256;                // threads per workgroup
 constexpr int kWaves = kBlock / 64;        // wave64
-constexpr int kItems = 16;                 // records per thread in a tile
-constexpr int kTile = kBlock * kItems;     // records per tile
+constexpr int kPartItems = 8;              // records per thread in a tile
+constexpr int kPartTile = kBlock * kPartItems;  // records per tile
 constexpr int kKeyBytes = 4;               // order-preserving coordinate key
-constexpr int kChunkTiles = 4;             // tiles per digit-count chunk
 constexpr int kMaxDescent = kRadixBits;    // levels one re-sort pass walks
-constexpr int kPartItems = 8;              // records per thread in a re-sort tile
-constexpr int kPartTile = kBlock * kPartItems;
 constexpr int kMaxRounds = 32;             // global rounds (levels) at most
 static_assert(kBlock == kRadix, "the tile kernels map one thread to one digit");
-static_assert(kBlock * kChunkTiles <= 1024, "one workgroup counts a whole chunk");
 
 // ------------------------------------------------------------ tree geometry
 // Level-order complete tree with N nodes ([W], indexing paragraph):
@@ -276,127 +272,121 @@ __device__ inline void wave_rank(const u32 (&digit)[kN], const bool (&valid)[kN]
     }
 }
 
-// ------------------------------------------------- presort (LSD radix sort)
+// ---------------------------------------------------- tiles of point records
+// Every global pass works on tiles of kPartTile consecutive records, wave w
+// owning kPartItems rows of 64 (item j of a lane is record wbase + 64 j).
+// Workgroups are dealt to the 8 XCDs in turn, so tile t of workgroup b is
+// chosen to give each XCD one contiguous range of tiles: the cache lines two
+// neighbouring tiles both write then meet in one L2.
+constexpr int kXcds = 8;
 
-// Column copy of the split dimensions the global rounds use.
-__global__ __launch_bounds__(kBlock) void k_init(const float* __restrict__ pts, i64 n, int k,
-                                                 int kcols, float* __restrict__ cols) {
-    const i64 stride = (i64)gridDim.x * kBlock;
-    for (i64 e = (i64)blockIdx.x * kBlock + threadIdx.x; e < n; e += stride) {
-        const float* row = pts + e * k;
-        for (int d = 0; d < kcols; ++d) cols[(i64)d * n + e] = row[d];
-    }
+__device__ inline u32 xcd_tile(u32 tiles) {
+    const u32 per = (tiles + kXcds - 1) / kXcds;
+    return (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
 }
 
-enum Src { kSrcColumn = 0, kSrcArrays = 1 };
-enum Sink { kSinkArrays = 0, kSinkRecords = 1 };
+inline u32 xcd_grid(u64 tiles) { return (u32)((tiles + kXcds - 1) / kXcds * kXcds); }
 
-// One stable radix pass over n (key, val) records is three launches:
-//   k_tile_count  digit counts of every tile of kTile records, and of every
-//                 chunk of kChunkTiles tiles,
-//   k_tile_scan   per digit, exclusive scan over the chunks,
-//   k_tile_scatter rank each tile again and move its records.
-// The presort of dimension d runs kKeyBytes passes from index order; the
-// last one writes records instead of (key, val) pairs.
-struct PassArgs {
-    i64 n;                     // records
-    int shift;                 // digit = (key >> shift) & 255
-    const float* col;          // kSrcColumn: key = key(col[i]), val = i
-    const u32* keys_in;        // kSrcArrays
-    const u32* vals_in;        // kSrcArrays
-    u32* keys_out;             // kSinkArrays
-    u32* vals_out;             // kSinkArrays
-    u32* recs_out;             // kSinkRecords: the record of point val at its slot:
-    int words;                 //   its first words-1 coordinates (bits), then val
-    const float* pts;          // kSinkRecords: the input points (rows of k)
+enum Src { kSrcRows = 0, kSrcRecords = 1 };
+
+// Where the records of a pass come from: kSrcRows builds the record of
+// point e from its row of `points` (its first words-1 coordinates as bits,
+// then e), in index order; kSrcRecords reads records of `words` words.
+struct RecordSource {
+    const float* pts;
     int k;
-    u32* digit_totals;         // 256 counts of this pass's digit over all records
-    u32* tile_counts;          // tiles x 256: digit counts of each tile
-    u32* chunk_slots;          // chunks x 256: digit counts of each chunk, then the
-                               //   counts of the digit in the chunks before it
+    const u32* in;
+    int words;
+    i64 n;
 };
 
-// Records of item j of this thread: wave w owns kItems rows of 64
-// consecutive records of the tile.
 template <int kSrc>
-__device__ inline void load_tile(const PassArgs& a, i64 wbase, u32 (&key)[kItems],
-                                 u32 (&val)[kItems]) {
+__device__ inline u32 source_word(const RecordSource& s, u64 e, int w) {
+    if (kSrc == kSrcRecords) return s.in[e * s.words + w];
+    return w < s.words - 1 ? __float_as_uint(s.pts[e * s.k + w]) : (u32)e;
+}
+
+// This thread's records of a tile. kW > 0 (at most 4 words): held in
+// registers, one array per word so that every index is a compile-time
+// constant; kW = 0 (wider records): words are read from the source when
+// needed (the tile's lines are then in L2).
+template <int kSrc, int kW>
+struct RecordTile {
+    static_assert(kW >= 0 && kW <= 4 && kW != 1, "record width");
+    u32 w0[kPartItems], w1[kPartItems], w2[kPartItems], w3[kPartItems];
+
+    __device__ __forceinline__ void load(const RecordSource& s, i64 wbase) {
+        if constexpr (kW > 0) {
 #pragma unroll
-    for (int j = 0; j < kItems; ++j) {
-        const i64 e = wbase + (i64)j * 64;
-        key[j] = 0;
-        val[j] = 0;
-        if (e < a.n) {
-            if (kSrc == kSrcColumn) {
-                key[j] = float_key(__float_as_uint(a.col[e]));
-                val[j] = (u32)e;
-            } else {
-                key[j] = a.keys_in[e];
-                val[j] = a.vals_in[e];
+            for (int j = 0; j < kPartItems; ++j) {
+                const i64 e = wbase + (i64)j * 64;
+                w0[j] = w1[j] = w2[j] = w3[j] = 0;
+                if (e >= s.n) continue;
+                if constexpr (kSrc == kSrcRows) {
+                    const u32* row = reinterpret_cast<const u32*>(s.pts) + (u64)e * s.k;
+                    w0[j] = row[0];
+                    if constexpr (kW > 2) w1[j] = row[1];
+                    if constexpr (kW > 3) w2[j] = row[2];
+                    if constexpr (kW == 2) w1[j] = (u32)e;
+                    if constexpr (kW == 3) w2[j] = (u32)e;
+                    if constexpr (kW == 4) w3[j] = (u32)e;
+                } else {
+                    const u32* src = s.in + (u64)e * kW;
+                    if constexpr (kW == 4) {
+                        const uint4 v = *reinterpret_cast<const uint4*>(src);
+                        w0[j] = v.x;
+                        w1[j] = v.y;
+                        w2[j] = v.z;
+                        w3[j] = v.w;
+                    } else if constexpr (kW == 3) {
+                        w0[j] = src[0];
+                        w1[j] = src[1];
+                        w2[j] = src[2];
+                    } else {
+                        const uint2 v = *reinterpret_cast<const uint2*>(src);
+                        w0[j] = v.x;
+                        w1[j] = v.y;
+                    }
+                }
             }
         }
     }
-}
-
-// Digit counts of kChunkTiles consecutive tiles: one row per tile and the
-// chunk's total. Each group of kBlock threads counts one tile (the same
-// record layout as the scatter's tiles), all tiles of the chunk at once.
-// Counting needs no ranks, only LDS atomics; each thread merges runs of
-// equal digits among its own records first, which keeps the skewed high
-// bytes of clustered keys from piling onto one counter.
-constexpr int kCountBlock = kBlock * kChunkTiles;
-template <int kSrc>
-__global__ __launch_bounds__(kCountBlock) void k_tile_count(PassArgs a) {
-    __shared__ u32 hist[kCountBlock / 64][kRadix];
-    __shared__ u32 rows[kChunkTiles][kRadix];
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    const int g = tid / kBlock;  // tile of the chunk this thread counts
-    const int gw = w % kWaves;   // wave within that tile
-    const i64 t = (i64)blockIdx.x * kChunkTiles + g;
-    const i64 wbase = t * kTile + (i64)gw * (64 * kItems) + lane;
-    u32 key[kItems];
-#pragma unroll
-    for (int j = 0; j < kItems; ++j) {
-        const i64 e = wbase + (i64)j * 64;
-        key[j] = 0;
-        if (e < a.n)
-            key[j] = kSrc == kSrcColumn ? float_key(__float_as_uint(a.col[e])) : a.keys_in[e];
-    }
-    for (int i = lane; i < kRadix; i += 64) hist[w][i] = 0;  // this wave's own row
-    u32 last = 0, run = 0;
-#pragma unroll
-    for (int j = 0; j < kItems; ++j) {
-        if (wbase + (i64)j * 64 >= a.n) break;
-        const u32 d = (key[j] >> a.shift) & (kRadix - 1);
-        if (run && d != last) {
-            atomicAdd(&hist[w][last], run);
-            run = 0;
+    // Word w of item j (record e); w is uniform across the wave. The word is
+    // picked with masks, not a select, so that the compiler cannot turn the
+    // choice back into an indexed (scratch) array.
+    __device__ __forceinline__ u32 word(const RecordSource& s, int j, i64 e, int w) const {
+        if constexpr (kW == 0) {
+            return source_word<kSrc>(s, (u64)e, w);
+        } else {
+            const u32 m0 = w == 0 ? ~0u : 0u, m1 = w == 1 ? ~0u : 0u;
+            const u32 m2 = w == 2 ? ~0u : 0u, m3 = w == 3 ? ~0u : 0u;
+            u32 v = (w0[j] & m0) | (w1[j] & m1);
+            if constexpr (kW > 2) v |= w2[j] & m2;
+            if constexpr (kW > 3) v |= w3[j] & m3;
+            return v;
         }
-        last = d;
-        ++run;
     }
-    if (run) atomicAdd(&hist[w][last], run);
-    __syncthreads();
-    const int d = tid % kRadix;
-    u32 total = 0;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) total += hist[g * kWaves + v][d];
-    const i64 tiles = (a.n + kTile - 1) / kTile;
-    if (t < tiles) a.tile_counts[(u64)t * kRadix + d] = total;
-    rows[g][d] = total;
-    __syncthreads();
-    if (tid < kRadix) {
-        u32 sum = 0;
-#pragma unroll
-        for (int c = 0; c < kChunkTiles; ++c) sum += rows[c][tid];
-        a.chunk_slots[(u64)blockIdx.x * kRadix + tid] = sum;
+    __device__ __forceinline__ uint4 quad(int j) const { return make_uint4(w0[j], w1[j], w2[j], w3[j]); }
+    __device__ __forceinline__ void store(const RecordSource& s, u32* out, int j, i64 e, u64 pos) const {
+        if constexpr (kW == 4) {
+            *reinterpret_cast<uint4*>(out + pos * 4) = quad(j);
+        } else if constexpr (kW == 3) {
+            out[pos * 3] = w0[j];
+            out[pos * 3 + 1] = w1[j];
+            out[pos * 3 + 2] = w2[j];
+        } else if constexpr (kW == 2) {
+            *reinterpret_cast<uint2*>(out + pos * 2) = make_uint2(w0[j], w1[j]);
+        } else {
+            u32* dst = out + pos * s.words;
+            for (int w = 0; w < s.words; ++w) dst[w] = source_word<kSrc>(s, (u64)e, w);
+        }
     }
-}
+};
 
-// One workgroup per digit d: slots[c][d] = counts of d in the chunks before
-// c (rows of `bins` digits); totals[d] = all counts of d (if totals is
-// given). Each thread scans a contiguous run of up to kScanRun chunks held
-// in registers (one batch of loads); longer inputs loop over runs.
+// One workgroup per digit d: slots[c][d] = counts of d in the tiles (chunks)
+// before c (rows of `bins` digits); totals[d] = all counts of d (if totals
+// is given). Each thread scans a contiguous run of up to kScanRun chunks
+// held in registers (one batch of loads); longer inputs loop over runs.
 constexpr int kScanRun = 16;
 __global__ __launch_bounds__(kBlock) void k_tile_scan(u32* __restrict__ slots, i64 chunks,
                                                       int bins, u32* __restrict__ totals) {
@@ -426,62 +416,95 @@ __global__ __launch_bounds__(kBlock) void k_tile_scan(u32* __restrict__ slots, i
     if (totals && tid == 0) totals[d] = s_carry;
 }
 
-// Writes the record of point v (its first words-1 coordinates, then v) to
-// record slot dst. kW > 0: compile-time record width; 0: a.words.
-template <int kW>
-__device__ inline void write_point_record(const PassArgs& a, u64 dst, u32 v) {
-    const u32* row = reinterpret_cast<const u32*>(a.pts) + (u64)v * a.k;
-    if constexpr (kW == 4) {
-        *reinterpret_cast<uint4*>(a.recs_out + dst * 4) = make_uint4(row[0], row[1], row[2], v);
-    } else if constexpr (kW == 2) {
-        *reinterpret_cast<uint2*>(a.recs_out + dst * 2) = make_uint2(row[0], v);
-    } else {
-        const int words = kW > 0 ? kW : a.words;
-        u32* out = a.recs_out + dst * words;
-        for (int d = 0; d < words - 1; ++d) out[d] = row[d];
-        out[words - 1] = v;
+// ------------------------------------------------- presort (LSD radix sort)
+// The presort of dimension d is kKeyBytes stable passes over the point
+// records, each by one byte of key(x_d), least significant first, starting
+// from index order (the first pass builds the records from the rows). A
+// pass is three launches: k_sort_count (digit counts of each tile),
+// k_tile_scan (per digit, exclusive scan over the tiles, and the digit
+// totals) and k_sort_scatter (ranks each tile again, stages it in LDS in
+// sorted order and writes each digit's run contiguously). No workgroup
+// ever waits on another.
+struct SortArgs {
+    RecordSource src;
+    u32* out;           // records, words each, in this pass's order
+    int dim;            // coordinate whose key is sorted
+    int shift;          // digit = (key >> shift) & 255
+    u32 tiles;
+    u32* slots;         // tiles x 256: digit counts of each tile, then the
+                        //   counts of the digit in the tiles before it
+    const u32* totals;  // 256: records of each digit
+};
+
+template <int kSrc>
+__global__ __launch_bounds__(kBlock) void k_sort_count(SortArgs a) {
+    __shared__ u32 hist[kWaves][kRadix];
+    const u32 t = xcd_tile(a.tiles);
+    if (t >= a.tiles) return;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const i64 wbase = (i64)t * kPartTile + (i64)w * (64 * kPartItems) + lane;
+    u32 key[kPartItems];
+#pragma unroll
+    for (int j = 0; j < kPartItems; ++j) {
+        const i64 e = wbase + (i64)j * 64;
+        key[j] = e < a.src.n ? float_key(source_word<kSrc>(a.src, (u64)e, a.dim)) : 0u;
     }
+    for (int i = lane; i < kRadix; i += 64) hist[w][i] = 0;  // this wave's own row
+    // Each thread merges runs of equal digits among its own records first,
+    // which keeps the skewed bytes of clustered keys off one counter.
+    u32 last = 0, run = 0;
+#pragma unroll
+    for (int j = 0; j < kPartItems; ++j) {
+        if (wbase + (i64)j * 64 >= a.src.n) break;
+        const u32 d = (key[j] >> a.shift) & (kRadix - 1);
+        if (run && d != last) {
+            atomicAdd(&hist[w][last], run);
+            run = 0;
+        }
+        last = d;
+        ++run;
+    }
+    if (run) atomicAdd(&hist[w][last], run);
+    __syncthreads();
+    u32 total = 0;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) total += hist[v][tid];
+    a.slots[(u64)t * kRadix + tid] = total;
 }
 
-template <int kSrc, int kSink, int kW>
-__global__ __launch_bounds__(kBlock) void k_tile_scatter(PassArgs a) {
+template <int kSrc, int kW>
+__global__ __launch_bounds__(kBlock) void k_sort_scatter(SortArgs a) {
     __shared__ union {
         u32 count[kWaves][kRadix];  // ranking: per-wave digit counts, then prefixes
-        u32 keys[kTile];            // staging of the sorted tile
-        u32 vals[kTile];
+        uint4 quads[kW == 4 ? kPartTile : 1];  // staging of the sorted tile
+        u32 words[kPartTile];
     } sm;
-    __shared__ u8 s_digit[kTile];
+    __shared__ u8 s_digit[kPartTile];
     __shared__ u32 s_local[kRadix];  // first tile-local slot of each digit
     __shared__ u32 s_base[kRadix];   // global slot of tile-local slot 0 of each digit
     __shared__ u64 s_wave[kWaves];
     __shared__ u32 s_valid;          // records of the tile
 
-    const int tid = threadIdx.x, w = tid >> 6;
-    const i64 base = (i64)blockIdx.x * kTile;
-    const i64 wbase = base + (i64)w * (64 * kItems) + (tid & 63);
-    u32 key[kItems], val[kItems], rank[kItems], digit[kItems];
-    bool valid[kItems];
-    load_tile<kSrc>(a, wbase, key, val);
+    const u32 t = xcd_tile(a.tiles);
+    if (t >= a.tiles) return;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const i64 wbase = (i64)t * kPartTile + (i64)w * (64 * kPartItems) + lane;
+    RecordTile<kSrc, kW> tr;
+    tr.load(a.src, wbase);
+    u32 digit[kPartItems], rank[kPartItems];
+    bool valid[kPartItems];
 #pragma unroll
-    for (int j = 0; j < kItems; ++j) {
-        valid[j] = (wbase + (i64)j * 64) < a.n;
-        digit[j] = (key[j] >> a.shift) & (kRadix - 1);
+    for (int j = 0; j < kPartItems; ++j) {
+        const i64 e = wbase + (i64)j * 64;
+        valid[j] = e < a.src.n;
+        digit[j] = valid[j] ? (float_key(tr.word(a.src, j, e, a.dim)) >> a.shift) & (kRadix - 1) : 0u;
     }
-    // First global slot of digit tid in this tile: where the digit starts in
-    // the output, plus its counts in earlier chunks and in the chunk's
-    // earlier tiles.
-    const u32 digit_total = a.digit_totals[tid];
-    const i64 chunk = blockIdx.x / kChunkTiles;
-    u32 global_start = a.chunk_slots[(u64)chunk * kRadix + tid];
-#pragma unroll
-    for (int c = 0; c < kChunkTiles - 1; ++c) {
-        const i64 t = chunk * kChunkTiles + c;
-        if (t < (i64)blockIdx.x) global_start += a.tile_counts[(u64)t * kRadix + tid];
-    }
-    for (int i = tid & 63; i < kRadix; i += 64) sm.count[w][i] = 0;
+    // Digit tid: its records before this tile, and before this digit.
+    u32 global_start = a.slots[(u64)t * kRadix + tid];
+    const u32 digit_total = a.totals[tid];
+    for (int i = lane; i < kRadix; i += 64) sm.count[w][i] = 0;
     wave_rank(digit, valid, kRadixBits, sm.count[w], rank);
     __syncthreads();
-
     // Thread tid owns digit tid: per-wave prefixes and the tile total.
     u32 agg = 0;
 #pragma unroll
@@ -491,7 +514,7 @@ __global__ __launch_bounds__(kBlock) void k_tile_scatter(PassArgs a) {
         agg += c;
     }
     // Both exclusive scans at once: digit totals (high word) and the tile's
-    // digit counts (low word, at most kTile in all).
+    // digit counts (low word, at most kPartTile in all).
     const u64 starts = block_exclusive_scan64(((u64)digit_total << 32) | agg, s_wave);
     const u32 local_start = (u32)starts;
     global_start += (u32)(starts >> 32);
@@ -499,42 +522,40 @@ __global__ __launch_bounds__(kBlock) void k_tile_scatter(PassArgs a) {
     s_base[tid] = global_start - local_start;  // modular; base + slot < n
     if (tid == kBlock - 1) s_valid = local_start + agg;
 #pragma unroll
-    for (int j = 0; j < kItems; ++j)
+    for (int j = 0; j < kPartItems; ++j)
         if (valid[j]) rank[j] += sm.count[w][digit[j]];
     __syncthreads();  // s_local written, count reads done
-
     const int valid_here = (int)s_valid;
     // rank[j] becomes the record's slot in the tile's sorted order.
 #pragma unroll
-    for (int j = 0; j < kItems; ++j)
-        if (valid[j]) rank[j] += s_local[digit[j]];
-    if (kSink == kSinkArrays) {
+    for (int j = 0; j < kPartItems; ++j) {
+        if (!valid[j]) continue;
+        rank[j] += s_local[digit[j]];
+        s_digit[rank[j]] = (u8)digit[j];
+    }
+    if constexpr (kW == 4) {
 #pragma unroll
-        for (int j = 0; j < kItems; ++j) {
-            if (!valid[j]) continue;
-            sm.keys[rank[j]] = key[j];
-            s_digit[rank[j]] = (u8)digit[j];
-        }
+        for (int j = 0; j < kPartItems; ++j)
+            if (valid[j]) sm.quads[rank[j]] = tr.quad(j);
         __syncthreads();
         for (int i = tid; i < valid_here; i += kBlock) {
             const u32 dst = s_base[s_digit[i]] + (u32)i;
-            if (dst < (u64)a.n) a.keys_out[dst] = sm.keys[i];
+            if (dst < (u64)a.src.n) *reinterpret_cast<uint4*>(a.out + (u64)dst * 4) = sm.quads[i];
         }
-        __syncthreads();
-    }
+    } else {
+        // one word of every record per staging round
+        const int words = kW > 0 ? kW : a.src.words;
+        for (int ww = 0; ww < words; ++ww) {
+            __syncthreads();  // the previous round's reads are done
 #pragma unroll
-    for (int j = 0; j < kItems; ++j) {
-        if (!valid[j]) continue;
-        sm.vals[rank[j]] = val[j];
-        if (kSink == kSinkRecords) s_digit[rank[j]] = (u8)digit[j];
-    }
-    __syncthreads();
-    for (int i = tid; i < valid_here; i += kBlock) {
-        const u32 dst = s_base[s_digit[i]] + (u32)i;
-        if (dst >= (u64)a.n) continue;
-        const u32 v = sm.vals[i];
-        if (kSink == kSinkArrays) a.vals_out[dst] = v;
-        else if (v < (u64)a.n) write_point_record<kW>(a, dst, v);
+            for (int j = 0; j < kPartItems; ++j)
+                if (valid[j]) sm.words[rank[j]] = tr.word(a.src, j, wbase + (i64)j * 64, ww);
+            __syncthreads();
+            for (int i = tid; i < valid_here; i += kBlock) {
+                const u32 dst = s_base[s_digit[i]] + (u32)i;
+                if (dst < (u64)a.src.n) a.out[(u64)dst * words + ww] = sm.words[i];
+            }
+        }
     }
 }
 
@@ -551,84 +572,18 @@ __global__ __launch_bounds__(kBlock) void k_tile_scatter(PassArgs a) {
 //   + (points of its digit before it in `in`)
 //   - (those in earlier level-l0 segments: bin_prefix, closed form).
 struct PartArgs {
-    const u32* in;     // records live on level l0: n_in x words
+    RecordSource src;  // records live on level l0 (src.n of them)
     u32* out;          // records live on level l1: n_out x words
-    i64 n_in, n_out;
-    int words;         // record width: coordinates 0 .. words-2, then the index
+    i64 n_out;
     int k;             // dimensions: level l splits coordinate l mod k
     int l0, l1;        // levels before and after (1 <= l1 - l0 <= kMaxDescent)
     int dim0;          // l0 mod k
     Geometry geo;
     LevelShape s0, s1; // the closed-form constants of levels l0 and l1
     const u64* piv;    // pivot of node s: key(coordinate) << 32 | index
-    u32* chunk_slots;  // tiles x bins: digit counts of each tile, then the
+    u32 tiles;
+    u32* slots;        // tiles x bins: digit counts of each tile, then the
                        //   counts of the digit in the tiles before it
-};
-
-// This thread's records of a tile. kW > 0 (at most 4 words): held in
-// registers, one array per word so that every index is a compile-time
-// constant; kW = 0 (wider records): words are read from `in` when needed.
-template <int kW>
-struct TileRecords {
-    static_assert(kW >= 0 && kW <= 4 && kW != 1, "record width");
-    u32 w0[kPartItems], w1[kPartItems], w2[kPartItems], w3[kPartItems];
-
-    __device__ __forceinline__ void load(const PartArgs& a, i64 wbase) {
-        if constexpr (kW > 0) {
-#pragma unroll
-            for (int j = 0; j < kPartItems; ++j) {
-                const i64 e = wbase + (i64)j * 64;
-                w0[j] = w1[j] = w2[j] = w3[j] = 0;
-                if (e >= a.n_in) continue;
-                const u32* src = a.in + (u64)e * kW;
-                if constexpr (kW == 4) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(src);
-                    w0[j] = v.x;
-                    w1[j] = v.y;
-                    w2[j] = v.z;
-                    w3[j] = v.w;
-                } else if constexpr (kW == 3) {
-                    w0[j] = src[0];
-                    w1[j] = src[1];
-                    w2[j] = src[2];
-                } else {
-                    const uint2 v = *reinterpret_cast<const uint2*>(src);
-                    w0[j] = v.x;
-                    w1[j] = v.y;
-                }
-            }
-        }
-    }
-    // Word w of item j (record e); w is uniform across the wave. The word is
-    // picked with masks, not a select, so that the compiler cannot turn the
-    // choice back into an indexed (scratch) array.
-    __device__ __forceinline__ u32 word(const PartArgs& a, int j, i64 e, int w) const {
-        if constexpr (kW == 0) {
-            return a.in[(u64)e * a.words + w];
-        } else {
-            const u32 m0 = w == 0 ? ~0u : 0u, m1 = w == 1 ? ~0u : 0u;
-            const u32 m2 = w == 2 ? ~0u : 0u, m3 = w == 3 ? ~0u : 0u;
-            u32 v = (w0[j] & m0) | (w1[j] & m1);
-            if constexpr (kW > 2) v |= w2[j] & m2;
-            if constexpr (kW > 3) v |= w3[j] & m3;
-            return v;
-        }
-    }
-    __device__ __forceinline__ void store(const PartArgs& a, int j, i64 e, u64 pos) const {
-        if constexpr (kW == 4) {
-            *reinterpret_cast<uint4*>(a.out + pos * 4) = make_uint4(w0[j], w1[j], w2[j], w3[j]);
-        } else if constexpr (kW == 3) {
-            a.out[pos * 3] = w0[j];
-            a.out[pos * 3 + 1] = w1[j];
-            a.out[pos * 3 + 2] = w2[j];
-        } else if constexpr (kW == 2) {
-            *reinterpret_cast<uint2*>(a.out + pos * 2) = make_uint2(w0[j], w1[j]);
-        } else {
-            const u32* src = a.in + (u64)e * a.words;
-            u32* dst = a.out + pos * a.words;
-            for (int w = 0; w < a.words; ++w) dst[w] = src[w];
-        }
-    }
 };
 
 // For every item: node[j], the in-level index of its node on level l1,
@@ -638,9 +593,9 @@ struct TileRecords {
 // compares (key(coordinate l mod k), index) with the pivot of the current
 // node on each level l ([W], tag paragraph: before the pivot -> left child).
 template <int kW>
-__device__ __forceinline__ void part_nodes(const PartArgs& a, const TileRecords<kW>& tr,
-                                           i64 wbase, u32 (&node)[kPartItems],
-                                           bool (&valid)[kPartItems]) {
+__device__ __forceinline__ void part_nodes(const PartArgs& a,
+                                           const RecordTile<kSrcRecords, kW>& tr, i64 wbase,
+                                           u32 (&node)[kPartItems], bool (&valid)[kPartItems]) {
     // Level-l0 segment of each record: one division for the wave's first
     // record, then each lane steps over the segment starts it passes (its
     // records are 64 positions apart, in increasing order).
@@ -650,7 +605,7 @@ __device__ __forceinline__ void part_nodes(const PartArgs& a, const TileRecords<
 #pragma unroll
     for (int j = 0; j < kPartItems; ++j) {
         const u32 e = (u32)(wbase + (i64)j * 64);
-        valid[j] = e < (u64)a.n_in;
+        valid[j] = e < (u64)a.src.n;
         if (valid[j]) {
             while (e >= next) {
                 ++j0;
@@ -665,8 +620,8 @@ __device__ __forceinline__ void part_nodes(const PartArgs& a, const TileRecords<
 #pragma unroll
         for (int j = 0; j < kPartItems; ++j) {
             const i64 e = wbase + (i64)j * 64;
-            const u64 me = ((u64)float_key(tr.word(a, j, e, dim)) << 32) |
-                           tr.word(a, j, e, a.words - 1);
+            const u64 me = ((u64)float_key(tr.word(a.src, j, e, dim)) << 32) |
+                           tr.word(a.src, j, e, a.src.words - 1);
             const u64 p = valid[j] ? a.piv[node[j]] : 0;
             if (me == p) valid[j] = false;  // the pivot itself: a node already
             node[j] = 2 * node[j] + (me < p ? 1u : 2u);
@@ -678,16 +633,17 @@ __device__ __forceinline__ void part_nodes(const PartArgs& a, const TileRecords<
     for (int j = 0; j < kPartItems; ++j) node[j] -= first;
 }
 
-// Digit counts of one tile of a re-sort pass (a row of `bins`; the tiles
-// are the chunks of the scan).
+// Digit counts of one tile of a re-sort pass (a row of `bins`).
 template <int kW>
 __global__ __launch_bounds__(kBlock) void k_part_count(PartArgs a) {
     __shared__ u32 hist[kWaves][kRadix];
+    const u32 t = xcd_tile(a.tiles);
+    if (t >= a.tiles) return;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    const i64 wbase = (i64)blockIdx.x * kPartTile + (i64)w * (64 * kPartItems) + lane;
+    const i64 wbase = (i64)t * kPartTile + (i64)w * (64 * kPartItems) + lane;
     const int bins = 1 << (a.l1 - a.l0);
-    TileRecords<kW> tr;
-    tr.load(a, wbase);
+    RecordTile<kSrcRecords, kW> tr;
+    tr.load(a.src, wbase);
     u32 node[kPartItems];
     bool valid[kPartItems];
     part_nodes<kW>(a, tr, wbase, node, valid);
@@ -710,19 +666,21 @@ __global__ __launch_bounds__(kBlock) void k_part_count(PartArgs a) {
         u32 total = 0;
 #pragma unroll
         for (int v = 0; v < kWaves; ++v) total += hist[v][tid];
-        a.chunk_slots[(u64)blockIdx.x * bins + tid] = total;
+        a.slots[(u64)t * bins + tid] = total;
     }
 }
 
 template <int kW>
 __global__ __launch_bounds__(kBlock) void k_part_scatter(PartArgs a) {
     __shared__ u32 count[kWaves][kRadix];  // per-wave digit counts, then first slots
+    const u32 t = xcd_tile(a.tiles);
+    if (t >= a.tiles) return;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    const i64 wbase = (i64)blockIdx.x * kPartTile + (i64)w * (64 * kPartItems) + lane;
+    const i64 wbase = (i64)t * kPartTile + (i64)w * (64 * kPartItems) + lane;
     const int delta = a.l1 - a.l0;
     const int bins = 1 << delta;
-    TileRecords<kW> tr;
-    tr.load(a, wbase);
+    RecordTile<kSrcRecords, kW> tr;
+    tr.load(a.src, wbase);
     u32 node[kPartItems], rank[kPartItems];
     bool valid[kPartItems];
     part_nodes<kW>(a, tr, wbase, node, valid);
@@ -736,7 +694,7 @@ __global__ __launch_bounds__(kBlock) void k_part_scatter(PartArgs a) {
     __syncthreads();
     if (tid < bins) {
         // points of this digit before the tile, then before each wave
-        u32 run = a.chunk_slots[(u64)blockIdx.x * bins + tid];
+        u32 run = a.slots[(u64)t * bins + tid];
 #pragma unroll
         for (int v = 0; v < kWaves; ++v) {
             const u32 c = count[v][tid];
@@ -752,7 +710,7 @@ __global__ __launch_bounds__(kBlock) void k_part_scatter(PartArgs a) {
         const u32 pos = live_begin32(a.s1, node[j]) -
                         bin_prefix32(a.s1, node[j] >> delta, digit, delta) + count[w][digit] +
                         rank[j];
-        if (pos < (u64)a.n_out) tr.store(a, j, wbase + (i64)j * 64, pos);
+        if (pos < (u64)a.n_out) tr.store(a.src, a.out, j, wbase + (i64)j * 64, pos);
     }
 }
 
@@ -1233,9 +1191,8 @@ struct Layout {
     int kr;              // coordinates a record carries: dimensions 0 .. kr-1
     int words;           // record width, kr + 1
     int nbuf;            // record arrays
-    i64 tiles, chunks;   // of a pass over all n points
-    size_t cols, keys0, keys1, vals0, vals1, recs, piv, totals, slots, chunk_slots, part_slots,
-        stage, total;
+    i64 tiles;           // of a pass over all n points
+    size_t tmp0, tmp1, recs, piv, totals, slots, stage, total;
 };
 
 // Workspace of `rounds` global rounds and, with `stage`, of the subtree stage.
@@ -1262,19 +1219,14 @@ bool make_layout(i64 n, int k, int rounds, bool stage, Layout* out) {
         // every dimension used again keeps its array, plus one to re-sort
         // into (a dimension used once needs its array only for its round)
         lay.nbuf = (k < rounds ? k : 1) + 1;
-        lay.tiles = (n + kTile - 1) / kTile;
-        lay.chunks = (lay.tiles + kChunkTiles - 1) / kChunkTiles;
-        lay.cols = take((size_t)lay.kr * n * sizeof(float));
-        lay.keys0 = take((size_t)n * sizeof(u32));
-        lay.keys1 = take((size_t)n * sizeof(u32));
-        lay.vals0 = take((size_t)n * sizeof(u32));
-        lay.vals1 = take((size_t)n * sizeof(u32));
-        lay.recs = take((size_t)lay.nbuf * n * lay.words * sizeof(u32));
+        lay.tiles = (n + kPartTile - 1) / kPartTile;
+        const size_t rec_bytes = (size_t)n * lay.words * sizeof(u32);
+        lay.tmp0 = take(rec_bytes);  // presort pass outputs
+        lay.tmp1 = take(rec_bytes);
+        lay.recs = take((size_t)lay.nbuf * rec_bytes);
         lay.piv = take((size_t)full_nodes(rounds) * sizeof(u64));
         lay.totals = take((size_t)kRadix * sizeof(u32));
         lay.slots = take((size_t)lay.tiles * kRadix * sizeof(u32));
-        lay.chunk_slots = take((size_t)lay.chunks * kRadix * sizeof(u32));
-        lay.part_slots = take((size_t)((n + kPartTile - 1) / kPartTile) * kRadix * sizeof(u32));
     }
     if (stage) lay.stage = take((size_t)(k + 1) * n * sizeof(u32));
     lay.total = off;
@@ -1347,67 +1299,70 @@ struct Timer {  // no-op unless a Profiler is attached
 
 // Kernel names as the profiler prints them, per record width 0, 2, 3, 4.
 int width_slot(int words) { return words == 2 ? 1 : words == 3 ? 2 : words == 4 ? 3 : 0; }
-const char* const kRecordScatterNames[4] = {"k_tile_scatter<1, 1, 0>", "k_tile_scatter<1, 1, 2>",
-                                            "k_tile_scatter<1, 1, 3>", "k_tile_scatter<1, 1, 4>"};
+const char* const kSortScatterNames[2][4] = {
+    {"k_sort_scatter<0, 0>", "k_sort_scatter<0, 2>", "k_sort_scatter<0, 3>", "k_sort_scatter<0, 4>"},
+    {"k_sort_scatter<1, 0>", "k_sort_scatter<1, 2>", "k_sort_scatter<1, 3>", "k_sort_scatter<1, 4>"}};
 const char* const kPartCountNames[4] = {"k_part_count<0>", "k_part_count<2>", "k_part_count<3>",
                                         "k_part_count<4>"};
 const char* const kPartScatterNames[4] = {"k_part_scatter<0>", "k_part_scatter<2>",
                                           "k_part_scatter<3>", "k_part_scatter<4>"};
 
 struct Launcher {
-    u32* tile_counts;
-    u32* chunk_slots;
-    u32* part_slots;
+    u32* slots;
     u32* totals;
     hipStream_t stream;
     Timer timer;
 
     // One stable pass of the presort (count, scan, scatter).
-    template <int kSrc, int kSink, int kW>
-    void pass(PassArgs a) {
-        a.tile_counts = tile_counts;
-        a.chunk_slots = chunk_slots;
-        a.digit_totals = totals;
-        const i64 tiles = (a.n + kTile - 1) / kTile;
-        const i64 chunks = (tiles + kChunkTiles - 1) / kChunkTiles;
-        const double n = (double)a.n;
-        timer.begin(kSrc == kSrcColumn ? "k_tile_count<0>" : "k_tile_count<1>", n * 4);
-        k_tile_count<kSrc><<<(unsigned)chunks, kCountBlock, 0, stream>>>(a);
+    template <int kSrc, int kW>
+    void sort(SortArgs a) {
+        const u64 tiles = (a.src.n + kPartTile - 1) / kPartTile;
+        a.tiles = (u32)tiles;
+        a.slots = slots;
+        a.totals = totals;
+        const double n = (double)a.src.n, rec = 4.0 * a.src.words;
+        timer.begin(kSrc == kSrcRows ? "k_sort_count<0>" : "k_sort_count<1>", n * 4);
+        k_sort_count<kSrc><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
         timer.end();
-        timer.begin("k_tile_scan", (double)chunks * kRadix * 8);
-        k_tile_scan<<<kRadix, kBlock, 0, stream>>>(chunk_slots, chunks, kRadix, totals);
+        timer.begin("k_tile_scan", (double)tiles * kRadix * 8);
+        k_tile_scan<<<kRadix, kBlock, 0, stream>>>(slots, (i64)tiles, kRadix, totals);
         timer.end();
-        // in: the column (4) or key + val (8); out: key + val (8), or the
-        // gathered row and the record
-        const double in = kSrc == kSrcColumn ? 4 : 8;
-        const double out = kSink == kSinkArrays ? 8 : 4.0 * (a.words - 1) + 4.0 * a.words;
-        const char* name = kSink == kSinkRecords ? kRecordScatterNames[width_slot(a.words)]
-                           : kSrc == kSrcColumn  ? "k_tile_scatter<0, 0, 0>"
-                                                 : "k_tile_scatter<1, 0, 0>";
-        timer.begin(name, n * (in + out));
-        k_tile_scatter<kSrc, kSink, kW><<<(unsigned)tiles, kBlock, 0, stream>>>(a);
+        // in: the rows' coordinates (and the implicit index) or the records
+        const double in = kSrc == kSrcRows ? rec - 4 : rec;
+        timer.begin(kSortScatterNames[kSrc][width_slot(kW)], n * (in + rec));
+        k_sort_scatter<kSrc, kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
         timer.end();
+    }
+    template <int kSrc>
+    void sort_any(const SortArgs& a) {
+        switch (a.src.words) {
+            case 2: sort<kSrc, 2>(a); break;
+            case 3: sort<kSrc, 3>(a); break;
+            case 4: sort<kSrc, 4>(a); break;
+            default: sort<kSrc, 0>(a); break;
+        }
     }
 
     // One re-sort pass by tag (count, scan, scatter).
     template <int kW>
     void part(PartArgs a) {
-        a.chunk_slots = part_slots;  // one row of digit counts per tile
-        const i64 tiles = (a.n_in + kPartTile - 1) / kPartTile;
+        const u64 tiles = (a.src.n + kPartTile - 1) / kPartTile;
+        a.tiles = (u32)tiles;
+        a.slots = slots;  // one row of digit counts per tile
         const int bins = 1 << (a.l1 - a.l0);
-        const double rec = 4.0 * a.words;
-        timer.begin(kPartCountNames[width_slot(kW)], (double)a.n_in * rec);
-        k_part_count<kW><<<(unsigned)tiles, kBlock, 0, stream>>>(a);
+        const double rec = 4.0 * a.src.words;
+        timer.begin(kPartCountNames[width_slot(kW)], (double)a.src.n * rec);
+        k_part_count<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
         timer.end();
         timer.begin("k_tile_scan", (double)tiles * bins * 8);
-        k_tile_scan<<<bins, kBlock, 0, stream>>>(part_slots, tiles, bins, nullptr);
+        k_tile_scan<<<bins, kBlock, 0, stream>>>(slots, (i64)tiles, bins, nullptr);
         timer.end();
-        timer.begin(kPartScatterNames[width_slot(kW)], (double)(a.n_in + a.n_out) * rec);
-        k_part_scatter<kW><<<(unsigned)tiles, kBlock, 0, stream>>>(a);
+        timer.begin(kPartScatterNames[width_slot(kW)], (double)(a.src.n + a.n_out) * rec);
+        k_part_scatter<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
         timer.end();
     }
     void part_any(const PartArgs& a) {
-        switch (a.words) {
+        switch (a.src.words) {
             case 2: part<2>(a); break;
             case 3: part<3>(a); break;
             case 4: part<4>(a); break;
@@ -1425,18 +1380,10 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
                       const u32** last) {
     const int R = lay.rounds, W = lay.words;
     const Geometry geo = make_geometry(n);
-    float* cols = (float*)(ws + lay.cols);
-    u32* keys[2] = {(u32*)(ws + lay.keys0), (u32*)(ws + lay.keys1)};
-    u32* vals[2] = {(u32*)(ws + lay.vals0), (u32*)(ws + lay.vals1)};
+    u32* tmp[2] = {(u32*)(ws + lay.tmp0), (u32*)(ws + lay.tmp1)};
     u64* piv = (u64*)(ws + lay.piv);
     auto recs = [&](int b) { return (u32*)(ws + lay.recs) + (size_t)b * n * W; };
-    Launcher launch{(u32*)(ws + lay.slots), (u32*)(ws + lay.chunk_slots),
-                    (u32*)(ws + lay.part_slots), (u32*)(ws + lay.totals), stream, timer};
-    const double N = (double)n;
-
-    timer.begin("k_init", N * lay.kr * 8);
-    k_init<<<grid_for(n, kBlock, 1 << 30), kBlock, 0, stream>>>(pts, n, k, lay.kr, cols);
-    timer.end();
+    Launcher launch{(u32*)(ws + lay.slots), (u32*)(ws + lay.totals), stream, timer};
 
     int holder[kMaxRounds + 1];  // dimension whose array a buffer holds, or -1
     for (int b = 0; b <= kMaxRounds; ++b) holder[b] = -1;
@@ -1451,35 +1398,19 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
         const int d = l % k;
         if (l < k) {
             // First use of dimension d: A_d = the points by (coordinate d,
-            // index), one level-0 segment. Pass p reads buffer (p+1)&1 and
-            // writes buffer p&1; the last one writes the records.
+            // index), one level-0 segment. Pass 0 reads the rows in index
+            // order, pass p > 0 reads tmp[(p+1)&1]; pass p writes tmp[p&1],
+            // the last one the array itself.
             const int b = take(-1);
             if (b < 0) return KDT_ERR_WORKSPACE;  // cannot happen: nbuf covers the rounds
             for (int p = 0; p < kKeyBytes; ++p) {
-                PassArgs a{};
-                a.n = n;
+                SortArgs a{};
+                a.src = RecordSource{pts, k, p == 0 ? nullptr : tmp[(p + 1) & 1], W, n};
+                a.out = p == kKeyBytes - 1 ? recs(b) : tmp[p & 1];
+                a.dim = d;
                 a.shift = 8 * p;
-                a.col = cols + (size_t)d * n;
-                a.keys_in = keys[(p + 1) & 1];
-                a.vals_in = vals[(p + 1) & 1];
-                a.keys_out = keys[p & 1];
-                a.vals_out = vals[p & 1];
-                a.recs_out = recs(b);
-                a.words = W;
-                a.pts = pts;
-                a.k = k;
-                if (p == 0) {
-                    launch.pass<kSrcColumn, kSinkArrays, 0>(a);
-                } else if (p < kKeyBytes - 1) {
-                    launch.pass<kSrcArrays, kSinkArrays, 0>(a);
-                } else {
-                    switch (W) {
-                        case 2: launch.pass<kSrcArrays, kSinkRecords, 2>(a); break;
-                        case 3: launch.pass<kSrcArrays, kSinkRecords, 3>(a); break;
-                        case 4: launch.pass<kSrcArrays, kSinkRecords, 4>(a); break;
-                        default: launch.pass<kSrcArrays, kSinkRecords, 0>(a); break;
-                    }
-                }
+                if (p == 0) launch.sort_any<kSrcRows>(a);
+                else launch.sort_any<kSrcRecords>(a);
             }
             holder[b] = d;
             buf_of[d] = b;
@@ -1492,11 +1423,9 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
             const int b = take(buf_of[d]);
             if (b < 0) return KDT_ERR_WORKSPACE;
             PartArgs a{};
-            a.in = recs(buf_of[d]);
+            a.src = RecordSource{pts, k, recs(buf_of[d]), W, n - (i64)full_nodes(level_of[d])};
             a.out = recs(b);
-            a.n_in = n - (i64)full_nodes(level_of[d]);
             a.n_out = n - (i64)full_nodes(l1);
-            a.words = W;
             a.k = k;
             a.l0 = level_of[d];
             a.l1 = l1;
