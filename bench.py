@@ -189,14 +189,16 @@ def main():
         roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                     "kernel": dom, "avg_us": d["avg_us"], "bytes_per_launch": d["bytes_per_launch"]}
-        passes = [kk for kk in kernels if kk.startswith(("k_tile_",
-                                                         "k_invert", "k_cross", "k_round0"))]
+        # every global sort and tag-update pass: presort histograms and passes,
+        # per-round re-sorts, pivot extraction
+        passes = [kk for kk in kernels if kk.startswith(("k_sort_", "k_part_", "k_pivots"))]
         tot_b = sum(agg[kk]["bytes"] for kk in passes)
         tot_ms = sum(agg[kk]["ms"] for kk in passes)
-        roofline["sort_and_update_passes"] = {
-            "GBps": round(tot_b / (tot_ms * 1e-3) / 1e9, 1),
-            "frac": round(tot_b / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "ms_per_build": round(tot_ms / args.steps, 4)}
+        if tot_ms > 0:
+            roofline["sort_and_update_passes"] = {
+                "GBps": round(tot_b / (tot_ms * 1e-3) / 1e9, 1),
+                "frac": round(tot_b / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "ms_per_build": round(tot_ms / args.steps, 4)}
         for kind, kv in sorted(kernels.items(), key=lambda kv: -kv[1]["ms_per_build"]):
             log("  %-36s %4d/build  avg %8.2f us  %8.1f GB/s  %.3f ms/build"
                 % (kind, kv["launches_per_build"], kv["avg_us"], kv["GBps"], kv["ms_per_build"]))
