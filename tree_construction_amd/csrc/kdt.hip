@@ -430,24 +430,39 @@ struct SortArgs {
     u32* out;           // records, words each, in this pass's order
     int dim;            // coordinate whose key is sorted
     int shift;          // digit = (key >> shift) & 255
+    const u8* digits;   // this pass's digit of every record, in input order
+    u8* next_digits;    // the next pass's digit of every record, in output
+                        //   order (nullptr after the last pass)
     u32 tiles;
     u32* slots;         // tiles x 256: digit counts of each tile, then the
                         //   counts of the digit in the tiles before it
     const u32* totals;  // 256: records of each digit
 };
 
-template <int kSrc>
+// The first presort pass's digit (low key byte) of every point in every
+// dimension the rounds use: digits0[d][e], from one read of the rows.
+__global__ __launch_bounds__(kBlock) void k_first_digits(const float* __restrict__ pts, i64 n,
+                                                         int k, int kr, u8* __restrict__ digits0) {
+    const i64 stride = (i64)gridDim.x * kBlock;
+    for (i64 e = (i64)blockIdx.x * kBlock + threadIdx.x; e < n; e += stride) {
+        const u32* row = reinterpret_cast<const u32*>(pts) + (u64)e * k;
+        for (int d = 0; d < kr; ++d) digits0[(u64)d * n + e] = (u8)float_key(row[d]);
+    }
+}
+
+// Digit counts of one tile, from the pass's digit bytes (one byte read per
+// record instead of the record).
 __global__ __launch_bounds__(kBlock) void k_sort_count(SortArgs a) {
     __shared__ u32 hist[kWaves][kRadix];
     const u32 t = xcd_tile(a.tiles);
     if (t >= a.tiles) return;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const i64 wbase = (i64)t * kPartTile + (i64)w * (64 * kPartItems) + lane;
-    u32 key[kPartItems];
+    u32 digit[kPartItems];
 #pragma unroll
     for (int j = 0; j < kPartItems; ++j) {
         const i64 e = wbase + (i64)j * 64;
-        key[j] = e < a.src.n ? float_key(source_word<kSrc>(a.src, (u64)e, a.dim)) : 0u;
+        digit[j] = e < a.src.n ? a.digits[e] : 0u;
     }
     for (int i = lane; i < kRadix; i += 64) hist[w][i] = 0;  // this wave's own row
     // Each thread merges runs of equal digits among its own records first,
@@ -456,7 +471,7 @@ __global__ __launch_bounds__(kBlock) void k_sort_count(SortArgs a) {
 #pragma unroll
     for (int j = 0; j < kPartItems; ++j) {
         if (wbase + (i64)j * 64 >= a.src.n) break;
-        const u32 d = (key[j] >> a.shift) & (kRadix - 1);
+        const u32 d = digit[j];
         if (run && d != last) {
             atomicAdd(&hist[w][last], run);
             run = 0;
@@ -540,7 +555,14 @@ __global__ __launch_bounds__(kBlock) void k_sort_scatter(SortArgs a) {
         __syncthreads();
         for (int i = tid; i < valid_here; i += kBlock) {
             const u32 dst = s_base[s_digit[i]] + (u32)i;
-            if (dst < (u64)a.src.n) *reinterpret_cast<uint4*>(a.out + (u64)dst * 4) = sm.quads[i];
+            if (dst >= (u64)a.src.n) continue;
+            const uint4 q = sm.quads[i];
+            *reinterpret_cast<uint4*>(a.out + (u64)dst * 4) = q;
+            if (a.next_digits) {
+                const u32 c = (q.x & (a.dim == 0 ? ~0u : 0u)) | (q.y & (a.dim == 1 ? ~0u : 0u)) |
+                              (q.z & (a.dim == 2 ? ~0u : 0u));
+                a.next_digits[dst] = (u8)(float_key(c) >> (a.shift + kRadixBits));
+            }
         }
     } else {
         // one word of every record per staging round
@@ -553,7 +575,10 @@ __global__ __launch_bounds__(kBlock) void k_sort_scatter(SortArgs a) {
             __syncthreads();
             for (int i = tid; i < valid_here; i += kBlock) {
                 const u32 dst = s_base[s_digit[i]] + (u32)i;
-                if (dst < (u64)a.src.n) a.out[(u64)dst * words + ww] = sm.words[i];
+                if (dst >= (u64)a.src.n) continue;
+                a.out[(u64)dst * words + ww] = sm.words[i];
+                if (ww == a.dim && a.next_digits)
+                    a.next_digits[dst] = (u8)(float_key(sm.words[i]) >> (a.shift + kRadixBits));
             }
         }
     }
@@ -1192,7 +1217,7 @@ struct Layout {
     int words;           // record width, kr + 1
     int nbuf;            // record arrays
     i64 tiles;           // of a pass over all n points
-    size_t tmp0, tmp1, recs, piv, totals, slots, stage, total;
+    size_t tmp0, tmp1, digits, digits0, recs, piv, totals, slots, stage, total;
 };
 
 // Workspace of `rounds` global rounds and, with `stage`, of the subtree stage.
@@ -1223,6 +1248,8 @@ bool make_layout(i64 n, int k, int rounds, bool stage, Layout* out) {
         const size_t rec_bytes = (size_t)n * lay.words * sizeof(u32);
         lay.tmp0 = take(rec_bytes);  // presort pass outputs
         lay.tmp1 = take(rec_bytes);
+        lay.digits = take((size_t)n);  // a presort pass's digit of each record
+        lay.digits0 = take((size_t)lay.kr * n);  // the first pass's, per dimension
         lay.recs = take((size_t)lay.nbuf * rec_bytes);
         lay.piv = take((size_t)full_nodes(rounds) * sizeof(u64));
         lay.totals = take((size_t)kRadix * sizeof(u32));
@@ -1321,15 +1348,15 @@ struct Launcher {
         a.slots = slots;
         a.totals = totals;
         const double n = (double)a.src.n, rec = 4.0 * a.src.words;
-        timer.begin(kSrc == kSrcRows ? "k_sort_count<0>" : "k_sort_count<1>", n * 4);
-        k_sort_count<kSrc><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
+        timer.begin("k_sort_count", n);
+        k_sort_count<<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
         timer.end();
         timer.begin("k_tile_scan", (double)tiles * kRadix * 8);
         k_tile_scan<<<kRadix, kBlock, 0, stream>>>(slots, (i64)tiles, kRadix, totals);
         timer.end();
         // in: the rows' coordinates (and the implicit index) or the records
         const double in = kSrc == kSrcRows ? rec - 4 : rec;
-        timer.begin(kSortScatterNames[kSrc][width_slot(kW)], n * (in + rec));
+        timer.begin(kSortScatterNames[kSrc][width_slot(kW)], n * (in + rec + (a.next_digits ? 1 : 0)));
         k_sort_scatter<kSrc, kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
         timer.end();
     }
@@ -1381,9 +1408,15 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
     const int R = lay.rounds, W = lay.words;
     const Geometry geo = make_geometry(n);
     u32* tmp[2] = {(u32*)(ws + lay.tmp0), (u32*)(ws + lay.tmp1)};
+    u8* digits = (u8*)(ws + lay.digits);
+    u8* digits0 = (u8*)(ws + lay.digits0);
     u64* piv = (u64*)(ws + lay.piv);
     auto recs = [&](int b) { return (u32*)(ws + lay.recs) + (size_t)b * n * W; };
     Launcher launch{(u32*)(ws + lay.slots), (u32*)(ws + lay.totals), stream, timer};
+
+    timer.begin("k_first_digits", (double)n * 5.0 * lay.kr);
+    k_first_digits<<<grid_for(n, kBlock, 1 << 30), kBlock, 0, stream>>>(pts, n, k, lay.kr, digits0);
+    timer.end();
 
     int holder[kMaxRounds + 1];  // dimension whose array a buffer holds, or -1
     for (int b = 0; b <= kMaxRounds; ++b) holder[b] = -1;
@@ -1409,6 +1442,8 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
                 a.out = p == kKeyBytes - 1 ? recs(b) : tmp[p & 1];
                 a.dim = d;
                 a.shift = 8 * p;
+                a.digits = p == 0 ? digits0 + (size_t)d * n : digits;
+                a.next_digits = p == kKeyBytes - 1 ? nullptr : digits;
                 if (p == 0) launch.sort_any<kSrcRows>(a);
                 else launch.sort_any<kSrcRecords>(a);
             }
