@@ -191,7 +191,8 @@ def main():
                     "kernel": dom, "avg_us": d["avg_us"], "bytes_per_launch": d["bytes_per_launch"]}
         # every global sort and tag-update pass: presort histograms and passes,
         # per-round re-sorts, pivot extraction
-        passes = [kk for kk in kernels if kk.startswith(("k_sort_", "k_part_", "k_pivots"))]
+        passes = [kk for kk in kernels if kk.startswith(("k_sort_", "k_part_", "k_pivots", "k_chunk_scan",
+                                                         "k_first_digits"))]
         tot_b = sum(agg[kk]["bytes"] for kk in passes)
         tot_ms = sum(agg[kk]["ms"] for kk in passes)
         if tot_ms > 0:

@@ -383,23 +383,30 @@ struct RecordTile {
     }
 };
 
-// One workgroup per digit d: slots[c][d] = counts of d in the tiles (chunks)
-// before c (rows of `bins` digits); totals[d] = all counts of d (if totals
-// is given). Each thread scans a contiguous run of up to kScanRun chunks
-// held in registers (one batch of loads); longer inputs loop over runs.
+// Digit counts are kept per tile (tile-major rows, for the tiles of one
+// chunk) and per chunk of kChunkTiles tiles (digit-major rows, scanned).
+constexpr int kChunkTiles = 4;
+constexpr int kCountBlock = kBlock * kChunkTiles;  // one count workgroup per chunk
+static_assert(kCountBlock <= 1024, "one workgroup counts a whole chunk");
+
+// One workgroup per digit d: row d of `chunk` (the digit's count in each
+// chunk) becomes the exclusive prefix over the chunks; totals[d] = the
+// row's sum (if totals is given). Each thread scans a contiguous run of
+// kScanRun chunks held in registers; longer rows loop over runs.
 constexpr int kScanRun = 16;
-__global__ __launch_bounds__(kBlock) void k_tile_scan(u32* __restrict__ slots, i64 chunks,
-                                                      int bins, u32* __restrict__ totals) {
+__global__ __launch_bounds__(kBlock) void k_chunk_scan(u32* __restrict__ chunk, i64 chunks,
+                                                       u32* __restrict__ totals) {
     __shared__ u32 s_wave[kWaves];
     __shared__ u32 s_carry;
     const int tid = threadIdx.x, d = blockIdx.x;
+    u32* row = chunk + (u64)d * chunks;
     if (tid == kBlock - 1) s_carry = 0;
     for (i64 t0 = 0; t0 < chunks; t0 += (i64)kBlock * kScanRun) {
         const i64 mine = t0 + (i64)tid * kScanRun;
         u32 v[kScanRun], sum = 0;
 #pragma unroll
         for (int i = 0; i < kScanRun; ++i) {
-            v[i] = mine + i < chunks ? slots[(u64)(mine + i) * bins + d] : 0u;
+            v[i] = mine + i < chunks ? row[mine + i] : 0u;
             sum += v[i];
         }
         __syncthreads();  // s_carry written
@@ -408,7 +415,7 @@ __global__ __launch_bounds__(kBlock) void k_tile_scan(u32* __restrict__ slots, i
         if (tid == kBlock - 1) s_carry = off + sum;
 #pragma unroll
         for (int i = 0; i < kScanRun; ++i) {
-            if (mine + i < chunks) slots[(u64)(mine + i) * bins + d] = off;
+            if (mine + i < chunks) row[mine + i] = off;
             off += v[i];
         }
     }
@@ -416,12 +423,46 @@ __global__ __launch_bounds__(kBlock) void k_tile_scan(u32* __restrict__ slots, i
     if (totals && tid == 0) totals[d] = s_carry;
 }
 
+// Given each wave's digit counts hist[v][d] for the kChunkTiles tiles of a
+// chunk (waves g*kWaves .. g*kWaves+kWaves-1 counted tile g), writes every
+// tile's row of `bins` counts and the chunk's count of each digit.
+__device__ inline void write_chunk_counts(const u32 (*hist)[kRadix], u32 (*rows)[kRadix], int bins,
+                                          u32 chunk_index, u64 chunks, u64 tiles,
+                                          u32* tile_counts, u32* chunk_counts) {
+    const int tid = threadIdx.x, g = tid / kBlock, d = tid % kBlock;
+    const u64 t = (u64)chunk_index * kChunkTiles + g;
+    if (d < bins) {
+        u32 total = 0;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) total += hist[g * kWaves + v][d];
+        if (t < tiles) tile_counts[t * bins + d] = total;
+        rows[g][d] = total;
+    }
+    __syncthreads();
+    if (tid < bins) {
+        u32 sum = 0;
+#pragma unroll
+        for (int c = 0; c < kChunkTiles; ++c) sum += rows[c][tid];
+        chunk_counts[(u64)tid * chunks + chunk_index] = sum;
+    }
+}
+
+// Points of digit d before tile t: its chunk's prefix plus the counts of the
+// chunk's earlier tiles.
+__device__ inline u32 tile_prefix(const u32* tile_counts, const u32* chunk_prefix, int bins,
+                                  u64 chunks, u32 t, int d) {
+    const u32 c = t / kChunkTiles;
+    u32 before = chunk_prefix[(u64)d * chunks + c];
+    for (u32 tt = c * kChunkTiles; tt < t; ++tt) before += tile_counts[(u64)tt * bins + d];
+    return before;
+}
+
 // ------------------------------------------------- presort (LSD radix sort)
 // The presort of dimension d is kKeyBytes stable passes over the point
 // records, each by one byte of key(x_d), least significant first, starting
 // from index order (the first pass builds the records from the rows). A
 // pass is three launches: k_sort_count (digit counts of each tile),
-// k_tile_scan (per digit, exclusive scan over the tiles, and the digit
+// k_chunk_scan (per digit, exclusive scan over the chunks, and the digit
 // totals) and k_sort_scatter (ranks each tile again, stages it in LDS in
 // sorted order and writes each digit's run contiguously). No workgroup
 // ever waits on another.
@@ -434,8 +475,10 @@ struct SortArgs {
     u8* next_digits;    // the next pass's digit of every record, in output
                         //   order (nullptr after the last pass)
     u32 tiles;
-    u32* slots;         // tiles x 256: digit counts of each tile, then the
-                        //   counts of the digit in the tiles before it
+    u64 chunks;
+    u32* tile_counts;   // tiles x 256: digit counts of each tile
+    u32* chunk_counts;  // 256 x chunks: digit counts of each chunk, then the
+                        //   counts of the digit in the chunks before it
     const u32* totals;  // 256: records of each digit
 };
 
@@ -450,14 +493,15 @@ __global__ __launch_bounds__(kBlock) void k_first_digits(const float* __restrict
     }
 }
 
-// Digit counts of one tile, from the pass's digit bytes (one byte read per
-// record instead of the record).
-__global__ __launch_bounds__(kBlock) void k_sort_count(SortArgs a) {
-    __shared__ u32 hist[kWaves][kRadix];
-    const u32 t = xcd_tile(a.tiles);
-    if (t >= a.tiles) return;
+// Digit counts of the tiles of one chunk, from the pass's digit bytes (one
+// byte read per record instead of the record).
+__global__ __launch_bounds__(kCountBlock) void k_sort_count(SortArgs a) {
+    __shared__ u32 hist[kCountBlock / 64][kRadix];
+    __shared__ u32 rows[kChunkTiles][kRadix];
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    const i64 wbase = (i64)t * kPartTile + (i64)w * (64 * kPartItems) + lane;
+    const int g = tid / kBlock, gw = w % kWaves;  // tile of the chunk, wave in the tile
+    const i64 t = (i64)blockIdx.x * kChunkTiles + g;
+    const i64 wbase = t * kPartTile + (i64)gw * (64 * kPartItems) + lane;
     u32 digit[kPartItems];
 #pragma unroll
     for (int j = 0; j < kPartItems; ++j) {
@@ -481,10 +525,8 @@ __global__ __launch_bounds__(kBlock) void k_sort_count(SortArgs a) {
     }
     if (run) atomicAdd(&hist[w][last], run);
     __syncthreads();
-    u32 total = 0;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) total += hist[v][tid];
-    a.slots[(u64)t * kRadix + tid] = total;
+    write_chunk_counts(hist, rows, kRadix, blockIdx.x, a.chunks, a.tiles, a.tile_counts,
+                       a.chunk_counts);
 }
 
 template <int kSrc, int kW>
@@ -515,7 +557,7 @@ __global__ __launch_bounds__(kBlock) void k_sort_scatter(SortArgs a) {
         digit[j] = valid[j] ? (float_key(tr.word(a.src, j, e, a.dim)) >> a.shift) & (kRadix - 1) : 0u;
     }
     // Digit tid: its records before this tile, and before this digit.
-    u32 global_start = a.slots[(u64)t * kRadix + tid];
+    u32 global_start = tile_prefix(a.tile_counts, a.chunk_counts, kRadix, a.chunks, t, tid);
     const u32 digit_total = a.totals[tid];
     for (int i = lane; i < kRadix; i += 64) sm.count[w][i] = 0;
     wave_rank(digit, valid, kRadixBits, sm.count[w], rank);
@@ -607,7 +649,7 @@ struct PartArgs {
     LevelShape s0, s1; // the closed-form constants of levels l0 and l1
     const u64* piv;    // pivot of node s: key(coordinate) << 32 | index
     u32 tiles;
-    u32* slots;        // tiles x bins: digit counts of each tile, then the
+    u32* chunk_counts; // bins x tiles: digit counts of each tile, then the
                        //   counts of the digit in the tiles before it
 };
 
@@ -658,7 +700,9 @@ __device__ __forceinline__ void part_nodes(const PartArgs& a,
     for (int j = 0; j < kPartItems; ++j) node[j] -= first;
 }
 
-// Digit counts of one tile of a re-sort pass (a row of `bins`).
+// Digit counts of one tile of a re-sort pass. A re-sort pass has at most
+// 2^kMaxDescent digits, usually a handful, so every tile is its own chunk:
+// its count of digit d goes straight to row d of the digit-major counts.
 template <int kW>
 __global__ __launch_bounds__(kBlock) void k_part_count(PartArgs a) {
     __shared__ u32 hist[kWaves][kRadix];
@@ -691,7 +735,7 @@ __global__ __launch_bounds__(kBlock) void k_part_count(PartArgs a) {
         u32 total = 0;
 #pragma unroll
         for (int v = 0; v < kWaves; ++v) total += hist[v][tid];
-        a.slots[(u64)t * bins + tid] = total;
+        a.chunk_counts[(u64)tid * a.tiles + t] = total;
     }
 }
 
@@ -719,7 +763,7 @@ __global__ __launch_bounds__(kBlock) void k_part_scatter(PartArgs a) {
     __syncthreads();
     if (tid < bins) {
         // points of this digit before the tile, then before each wave
-        u32 run = a.slots[(u64)t * bins + tid];
+        u32 run = a.chunk_counts[(u64)tid * a.tiles + t];
 #pragma unroll
         for (int v = 0; v < kWaves; ++v) {
             const u32 c = count[v][tid];
@@ -1217,7 +1261,7 @@ struct Layout {
     int words;           // record width, kr + 1
     int nbuf;            // record arrays
     i64 tiles;           // of a pass over all n points
-    size_t tmp0, tmp1, digits, digits0, recs, piv, totals, slots, stage, total;
+    size_t tmp0, tmp1, digits, digits0, recs, piv, totals, slots, chunk_slots, stage, total;
 };
 
 // Workspace of `rounds` global rounds and, with `stage`, of the subtree stage.
@@ -1254,6 +1298,8 @@ bool make_layout(i64 n, int k, int rounds, bool stage, Layout* out) {
         lay.piv = take((size_t)full_nodes(rounds) * sizeof(u64));
         lay.totals = take((size_t)kRadix * sizeof(u32));
         lay.slots = take((size_t)lay.tiles * kRadix * sizeof(u32));
+        lay.chunk_slots =
+            take((size_t)((lay.tiles + kChunkTiles - 1) / kChunkTiles) * kRadix * sizeof(u32));
     }
     if (stage) lay.stage = take((size_t)(k + 1) * n * sizeof(u32));
     lay.total = off;
@@ -1335,7 +1381,8 @@ const char* const kPartScatterNames[4] = {"k_part_scatter<0>", "k_part_scatter<2
                                           "k_part_scatter<3>", "k_part_scatter<4>"};
 
 struct Launcher {
-    u32* slots;
+    u32* tile_counts;
+    u32* chunk_counts;
     u32* totals;
     hipStream_t stream;
     Timer timer;
@@ -1344,15 +1391,18 @@ struct Launcher {
     template <int kSrc, int kW>
     void sort(SortArgs a) {
         const u64 tiles = (a.src.n + kPartTile - 1) / kPartTile;
+        const u64 chunks = (tiles + kChunkTiles - 1) / kChunkTiles;
         a.tiles = (u32)tiles;
-        a.slots = slots;
+        a.chunks = chunks;
+        a.tile_counts = tile_counts;
+        a.chunk_counts = chunk_counts;
         a.totals = totals;
         const double n = (double)a.src.n, rec = 4.0 * a.src.words;
-        timer.begin("k_sort_count", n);
-        k_sort_count<<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
+        timer.begin("k_sort_count", n + (double)(tiles + chunks) * kRadix * 4);
+        k_sort_count<<<(unsigned)chunks, kCountBlock, 0, stream>>>(a);
         timer.end();
-        timer.begin("k_tile_scan", (double)tiles * kRadix * 8);
-        k_tile_scan<<<kRadix, kBlock, 0, stream>>>(slots, (i64)tiles, kRadix, totals);
+        timer.begin("k_chunk_scan", (double)chunks * kRadix * 8);
+        k_chunk_scan<<<kRadix, kBlock, 0, stream>>>(chunk_counts, (i64)chunks, totals);
         timer.end();
         // in: the rows' coordinates (and the implicit index) or the records
         const double in = kSrc == kSrcRows ? rec - 4 : rec;
@@ -1375,14 +1425,14 @@ struct Launcher {
     void part(PartArgs a) {
         const u64 tiles = (a.src.n + kPartTile - 1) / kPartTile;
         a.tiles = (u32)tiles;
-        a.slots = slots;  // one row of digit counts per tile
+        a.chunk_counts = tile_counts;  // digit-major rows of per-tile counts
         const int bins = 1 << (a.l1 - a.l0);
         const double rec = 4.0 * a.src.words;
         timer.begin(kPartCountNames[width_slot(kW)], (double)a.src.n * rec);
         k_part_count<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
         timer.end();
-        timer.begin("k_tile_scan", (double)tiles * bins * 8);
-        k_tile_scan<<<bins, kBlock, 0, stream>>>(slots, (i64)tiles, bins, nullptr);
+        timer.begin("k_chunk_scan", (double)tiles * bins * 8);
+        k_chunk_scan<<<bins, kBlock, 0, stream>>>(tile_counts, (i64)tiles, nullptr);
         timer.end();
         timer.begin(kPartScatterNames[width_slot(kW)], (double)(a.src.n + a.n_out) * rec);
         k_part_scatter<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
@@ -1412,7 +1462,8 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
     u8* digits0 = (u8*)(ws + lay.digits0);
     u64* piv = (u64*)(ws + lay.piv);
     auto recs = [&](int b) { return (u32*)(ws + lay.recs) + (size_t)b * n * W; };
-    Launcher launch{(u32*)(ws + lay.slots), (u32*)(ws + lay.totals), stream, timer};
+    Launcher launch{(u32*)(ws + lay.slots), (u32*)(ws + lay.chunk_slots), (u32*)(ws + lay.totals),
+                    stream, timer};
 
     timer.begin("k_first_digits", (double)n * 5.0 * lay.kr);
     k_first_digits<<<grid_for(n, kBlock, 1 << 30), kBlock, 0, stream>>>(pts, n, k, lay.kr, digits0);
