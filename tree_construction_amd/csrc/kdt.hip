@@ -47,6 +47,8 @@ typedef uint8_t u8;
 typedef uint32_t u32;
 typedef uint64_t u64;
 typedef int64_t i64;
+typedef u32 v4u __attribute__((ext_vector_type(4)));  // for the non-temporal builtins
+typedef u32 v2u __attribute__((ext_vector_type(2)));
 
 constexpr int kRadixBits = 8;
 constexpr int kRadix = 1 << kRadixBits;
@@ -240,6 +242,17 @@ __device__ inline u64 block_exclusive_scan64(u64 v, u64* s_wave) {
     return off + inc - v;
 }
 
+// One bit of the wave's digit match: ORs into miss the lanes whose bit b of
+// their digit differs from this lane's. The sign-extending bit extract gives
+// this lane's bit as a mask (0 or all ones) in one instruction, and the
+// ballot reads the same mask.
+__device__ inline void match_bit(u32 d, int b, u32& miss_lo, u32& miss_hi) {
+    const u32 m = (u32)__builtin_amdgcn_sbfe((int)d, b, 1);
+    const u64 vote = __ballot(m != 0);
+    miss_lo |= (u32)vote ^ m;
+    miss_hi |= (u32)(vote >> 32) ^ m;
+}
+
 // Rank inside the wave of each of this thread's records by its digit
 // (nbits bits): lanes holding the same digit are found with nbits ballots
 // (a lane's peers are the lanes that never disagree with it on a bit: the OR
@@ -257,12 +270,7 @@ __device__ inline void wave_rank(const u32 (&digit)[kN], const bool (&valid)[kN]
     for (int j = 0; j < kN; ++j) {
         const u32 d = digit[j];
         u32 miss_lo = 0, miss_hi = 0;
-        for (int b = 0; b < nbits; ++b) {
-            const u64 vote = __ballot((d >> b) & 1);
-            const u32 m = (u32)((int)(d << (31 - b)) >> 31);  // all ones where the bit is set
-            miss_lo |= (u32)vote ^ m;
-            miss_hi |= (u32)(vote >> 32) ^ m;
-        }
+        for (int b = 0; b < nbits; ++b) match_bit(d, b, miss_lo, miss_hi);
         const u64 peers = __ballot(valid[j]) & ~(((u64)miss_hi << 32) | miss_lo);
         const u32 before = __popcll(peers & below);
         u32 seen = 0;
@@ -367,15 +375,19 @@ struct RecordTile {
         }
     }
     __device__ __forceinline__ uint4 quad(int j) const { return make_uint4(w0[j], w1[j], w2[j], w3[j]); }
+    // Non-temporal stores: the output is read by a later pass, not this one,
+    // and write-backs of dirty lines would otherwise land in the next pass.
     __device__ __forceinline__ void store(const RecordSource& s, u32* out, int j, i64 e, u64 pos) const {
         if constexpr (kW == 4) {
-            *reinterpret_cast<uint4*>(out + pos * 4) = quad(j);
+            const v4u v = {w0[j], w1[j], w2[j], w3[j]};
+            __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(out + pos * 4));
         } else if constexpr (kW == 3) {
-            out[pos * 3] = w0[j];
-            out[pos * 3 + 1] = w1[j];
-            out[pos * 3 + 2] = w2[j];
+            __builtin_nontemporal_store(w0[j], out + pos * 3);
+            __builtin_nontemporal_store(w1[j], out + pos * 3 + 1);
+            __builtin_nontemporal_store(w2[j], out + pos * 3 + 2);
         } else if constexpr (kW == 2) {
-            *reinterpret_cast<uint2*>(out + pos * 2) = make_uint2(w0[j], w1[j]);
+            const v2u v = {w0[j], w1[j]};
+            __builtin_nontemporal_store(v, reinterpret_cast<v2u*>(out + pos * 2));
         } else {
             u32* dst = out + pos * s.words;
             for (int w = 0; w < s.words; ++w) dst[w] = source_word<kSrc>(s, (u64)e, w);
@@ -933,12 +945,7 @@ __device__ void local_pass(u64 (&rec)[kLocalItems], int shift, LocalShared& sh) 
         const u32 d = (u32)(rec[j] >> shift) & (kRadix - 1);
         u32 miss_lo = 0, miss_hi = 0;
 #pragma unroll
-        for (int b = 0; b < kRadixBits; ++b) {
-            const u64 vote = __ballot((d >> b) & 1);
-            const u32 m = (u32)((int)(d << (31 - b)) >> 31);  // all ones where the bit is set
-            miss_lo |= (u32)vote ^ m;
-            miss_hi |= (u32)(vote >> 32) ^ m;
-        }
+        for (int b = 0; b < kRadixBits; ++b) match_bit(d, b, miss_lo, miss_hi);
         const u64 peers = ~(((u64)miss_hi << 32) | miss_lo);
         const u32 before = __popcll(peers & below);
         const u32 seen = sh.count[w][d];
@@ -1067,12 +1074,7 @@ __device__ void local_round(const uint16_t* order, u32 nc, int t, const Geometry
         const u32 b = live ? st - fl : 0;
         seg[j] = st;
         u32 miss_lo = 0, miss_hi = 0;
-        for (int bit = 0; bit < t; ++bit) {
-            const u64 vote = __ballot((b >> bit) & 1);
-            const u32 m = (u32)((int)(b << (31 - bit)) >> 31);
-            miss_lo |= (u32)vote ^ m;
-            miss_hi |= (u32)(vote >> 32) ^ m;
-        }
+        for (int bit = 0; bit < t; ++bit) match_bit(b, bit, miss_lo, miss_hi);
         const u64 peers = __ballot(live) & ~(((u64)miss_hi << 32) | miss_lo);
         const u32 before = __popcll(peers & below);
         u32 seen = 0;
