@@ -227,8 +227,10 @@ __device__ inline u64 wave_inclusive_scan64(u64 v) {
     return v;
 }
 
-// Exclusive scan of one 64-bit value per thread across the workgroup (used
-// for two 32-bit scans at once whose sums cannot carry out of 32 bits).
+// Exclusive scan of one 64-bit value per thread across a workgroup of
+// kNWaves waves (used for two 32-bit scans at once whose sums cannot carry
+// out of 32 bits).
+template <int kNWaves>
 __device__ inline u64 block_exclusive_scan64(u64 v, u64* s_wave) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     u64 inc = wave_inclusive_scan64(v);
@@ -236,7 +238,7 @@ __device__ inline u64 block_exclusive_scan64(u64 v, u64* s_wave) {
     __syncthreads();
     u64 off = 0;
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i)
+    for (int i = 0; i < kNWaves; ++i)
         if (i < w) off += s_wave[i];
     __syncthreads();
     return off + inc - v;
@@ -395,11 +397,18 @@ struct RecordTile {
     }
 };
 
-// Digit counts are kept per tile (tile-major rows, for the tiles of one
-// chunk) and per chunk of kChunkTiles tiles (digit-major rows, scanned).
-constexpr int kChunkTiles = 4;
-constexpr int kCountBlock = kBlock * kChunkTiles;  // one count workgroup per chunk
+// A presort tile is larger than a re-sort tile: kSortBlock threads of
+// kPartItems records, so that each of the 256 digit runs a tile writes is
+// twice as long. Presort digit counts are kept per tile (tile-major rows,
+// for the tiles of one chunk) and per chunk of kChunkTiles tiles
+// (digit-major rows, scanned).
+constexpr int kSortBlock = 512;
+constexpr int kSortWaves = kSortBlock / 64;
+constexpr int kSortTile = kSortBlock * kPartItems;
+constexpr int kChunkTiles = 2;
+constexpr int kCountBlock = kSortBlock * kChunkTiles;  // one count workgroup per chunk
 static_assert(kCountBlock <= 1024, "one workgroup counts a whole chunk");
+static_assert(kSortBlock >= kRadix, "a presort thread per digit");
 
 // One workgroup per digit d: row d of `chunk` (the digit's count in each
 // chunk) becomes the exclusive prefix over the chunks; totals[d] = the
@@ -441,12 +450,12 @@ __global__ __launch_bounds__(kBlock) void k_chunk_scan(u32* __restrict__ chunk, 
 __device__ inline void write_chunk_counts(const u32 (*hist)[kRadix], u32 (*rows)[kRadix], int bins,
                                           u32 chunk_index, u64 chunks, u64 tiles,
                                           u32* tile_counts, u32* chunk_counts) {
-    const int tid = threadIdx.x, g = tid / kBlock, d = tid % kBlock;
+    const int tid = threadIdx.x, g = tid / kSortBlock, d = tid % kSortBlock;
     const u64 t = (u64)chunk_index * kChunkTiles + g;
     if (d < bins) {
         u32 total = 0;
 #pragma unroll
-        for (int v = 0; v < kWaves; ++v) total += hist[g * kWaves + v][d];
+        for (int v = 0; v < kSortWaves; ++v) total += hist[g * kSortWaves + v][d];
         if (t < tiles) tile_counts[t * bins + d] = total;
         rows[g][d] = total;
     }
@@ -511,9 +520,9 @@ __global__ __launch_bounds__(kCountBlock) void k_sort_count(SortArgs a) {
     __shared__ u32 hist[kCountBlock / 64][kRadix];
     __shared__ u32 rows[kChunkTiles][kRadix];
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    const int g = tid / kBlock, gw = w % kWaves;  // tile of the chunk, wave in the tile
+    const int g = tid / kSortBlock, gw = w % kSortWaves;  // tile of the chunk, wave in the tile
     const i64 t = (i64)blockIdx.x * kChunkTiles + g;
-    const i64 wbase = t * kPartTile + (i64)gw * (64 * kPartItems) + lane;
+    const i64 wbase = t * kSortTile + (i64)gw * (64 * kPartItems) + lane;
     u32 digit[kPartItems];
 #pragma unroll
     for (int j = 0; j < kPartItems; ++j) {
@@ -542,22 +551,22 @@ __global__ __launch_bounds__(kCountBlock) void k_sort_count(SortArgs a) {
 }
 
 template <int kSrc, int kW>
-__global__ __launch_bounds__(kBlock) void k_sort_scatter(SortArgs a) {
+__global__ __launch_bounds__(kSortBlock) void k_sort_scatter(SortArgs a) {
     __shared__ union {
-        u32 count[kWaves][kRadix];  // ranking: per-wave digit counts, then prefixes
-        uint4 quads[kW == 4 ? kPartTile : 1];  // staging of the sorted tile
-        u32 words[kPartTile];
+        u32 count[kSortWaves][kRadix];  // ranking: per-wave digit counts, then prefixes
+        uint4 quads[kW == 4 ? kSortTile : 1];  // staging of the sorted tile
+        u32 words[kSortTile];
     } sm;
-    __shared__ u8 s_digit[kPartTile];
+    __shared__ u8 s_digit[kSortTile];
     __shared__ u32 s_local[kRadix];  // first tile-local slot of each digit
     __shared__ u32 s_base[kRadix];   // global slot of tile-local slot 0 of each digit
-    __shared__ u64 s_wave[kWaves];
+    __shared__ u64 s_wave[kSortWaves];
     __shared__ u32 s_valid;          // records of the tile
 
     const u32 t = xcd_tile(a.tiles);
     if (t >= a.tiles) return;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    const i64 wbase = (i64)t * kPartTile + (i64)w * (64 * kPartItems) + lane;
+    const i64 wbase = (i64)t * kSortTile + (i64)w * (64 * kPartItems) + lane;
     RecordTile<kSrc, kW> tr;
     tr.load(a.src, wbase);
     u32 digit[kPartItems], rank[kPartItems];
@@ -568,28 +577,37 @@ __global__ __launch_bounds__(kBlock) void k_sort_scatter(SortArgs a) {
         valid[j] = e < a.src.n;
         digit[j] = valid[j] ? (float_key(tr.word(a.src, j, e, a.dim)) >> a.shift) & (kRadix - 1) : 0u;
     }
-    // Digit tid: its records before this tile, and before this digit.
-    u32 global_start = tile_prefix(a.tile_counts, a.chunk_counts, kRadix, a.chunks, t, tid);
-    const u32 digit_total = a.totals[tid];
+    // Thread tid < 256 owns digit tid: its records before this tile, and
+    // the digit's total.
+    const bool owner = tid < kRadix;
+    u32 global_start = 0, digit_total = 0;
+    if (owner) {
+        global_start = tile_prefix(a.tile_counts, a.chunk_counts, kRadix, a.chunks, t, tid);
+        digit_total = a.totals[tid];
+    }
     for (int i = lane; i < kRadix; i += 64) sm.count[w][i] = 0;
     wave_rank(digit, valid, kRadixBits, sm.count[w], rank);
     __syncthreads();
-    // Thread tid owns digit tid: per-wave prefixes and the tile total.
+    // Per-wave prefixes and the tile total of each digit.
     u32 agg = 0;
+    if (owner) {
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
-        const u32 c = sm.count[v][tid];
-        sm.count[v][tid] = agg;
-        agg += c;
+        for (int v = 0; v < kSortWaves; ++v) {
+            const u32 c = sm.count[v][tid];
+            sm.count[v][tid] = agg;
+            agg += c;
+        }
     }
     // Both exclusive scans at once: digit totals (high word) and the tile's
-    // digit counts (low word, at most kPartTile in all).
-    const u64 starts = block_exclusive_scan64(((u64)digit_total << 32) | agg, s_wave);
-    const u32 local_start = (u32)starts;
-    global_start += (u32)(starts >> 32);
-    s_local[tid] = local_start;
-    s_base[tid] = global_start - local_start;  // modular; base + slot < n
-    if (tid == kBlock - 1) s_valid = local_start + agg;
+    // digit counts (low word, at most kSortTile in all).
+    const u64 starts = block_exclusive_scan64<kSortWaves>(((u64)digit_total << 32) | agg, s_wave);
+    if (owner) {
+        const u32 local_start = (u32)starts;
+        global_start += (u32)(starts >> 32);
+        s_local[tid] = local_start;
+        s_base[tid] = global_start - local_start;  // modular; base + slot < n
+        if (tid == kRadix - 1) s_valid = local_start + agg;
+    }
 #pragma unroll
     for (int j = 0; j < kPartItems; ++j)
         if (valid[j]) rank[j] += sm.count[w][digit[j]];
@@ -607,7 +625,7 @@ __global__ __launch_bounds__(kBlock) void k_sort_scatter(SortArgs a) {
         for (int j = 0; j < kPartItems; ++j)
             if (valid[j]) sm.quads[rank[j]] = tr.quad(j);
         __syncthreads();
-        for (int i = tid; i < valid_here; i += kBlock) {
+        for (int i = tid; i < valid_here; i += kSortBlock) {
             const u32 dst = s_base[s_digit[i]] + (u32)i;
             if (dst >= (u64)a.src.n) continue;
             const uint4 q = sm.quads[i];
@@ -627,7 +645,7 @@ __global__ __launch_bounds__(kBlock) void k_sort_scatter(SortArgs a) {
             for (int j = 0; j < kPartItems; ++j)
                 if (valid[j]) sm.words[rank[j]] = tr.word(a.src, j, wbase + (i64)j * 64, ww);
             __syncthreads();
-            for (int i = tid; i < valid_here; i += kBlock) {
+            for (int i = tid; i < valid_here; i += kSortBlock) {
                 const u32 dst = s_base[s_digit[i]] + (u32)i;
                 if (dst >= (u64)a.src.n) continue;
                 a.out[(u64)dst * words + ww] = sm.words[i];
@@ -1392,7 +1410,7 @@ struct Launcher {
     // One stable pass of the presort (count, scan, scatter).
     template <int kSrc, int kW>
     void sort(SortArgs a) {
-        const u64 tiles = (a.src.n + kPartTile - 1) / kPartTile;
+        const u64 tiles = (a.src.n + kSortTile - 1) / kSortTile;
         const u64 chunks = (tiles + kChunkTiles - 1) / kChunkTiles;
         a.tiles = (u32)tiles;
         a.chunks = chunks;
@@ -1409,7 +1427,7 @@ struct Launcher {
         // in: the rows' coordinates (and the implicit index) or the records
         const double in = kSrc == kSrcRows ? rec - 4 : rec;
         timer.begin(kSortScatterNames[kSrc][width_slot(kW)], n * (in + rec + (a.next_digits ? 1 : 0)));
-        k_sort_scatter<kSrc, kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
+        k_sort_scatter<kSrc, kW><<<xcd_grid(tiles), kSortBlock, 0, stream>>>(a);
         timer.end();
     }
     template <int kSrc>
