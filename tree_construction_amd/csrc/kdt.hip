@@ -173,6 +173,13 @@ __device__ inline u32 live_begin32(const LevelShape& s, u32 j) {
     return j * ((1u << s.dd) - 1) + (under < s.last ? under : s.last);
 }
 
+// Size of the subtree of the node with in-level index i on the level of s.
+__device__ inline u32 subtree_size32(const LevelShape& s, u32 i) {
+    const u32 u = 1u << s.dd, under = i << s.dd;
+    const u32 extra = s.last > under ? (s.last - under < u ? s.last - under : u) : 0u;
+    return (u - 1) + extra;
+}
+
 __device__ inline u32 bin_prefix32(const LevelShape& s, u32 j0, u32 b, int delta) {
     const u32 u = 1u << s.dd;
     u32 h = j0 * (u - 1);
@@ -520,14 +527,18 @@ __global__ __launch_bounds__(kCountBlock) void k_sort_count(SortArgs a) {
     __shared__ u32 hist[kCountBlock / 64][kRadix];
     __shared__ u32 rows[kChunkTiles][kRadix];
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    const int g = tid / kSortBlock, gw = w % kSortWaves;  // tile of the chunk, wave in the tile
+    // Counts do not depend on which thread counts which record: each thread
+    // takes kPartItems consecutive records of its tile (one 8-byte load).
+    const int g = tid / kSortBlock;  // tile of the chunk
     const i64 t = (i64)blockIdx.x * kChunkTiles + g;
-    const i64 wbase = t * kSortTile + (i64)gw * (64 * kPartItems) + lane;
-    u32 digit[kPartItems];
-#pragma unroll
-    for (int j = 0; j < kPartItems; ++j) {
-        const i64 e = wbase + (i64)j * 64;
-        digit[j] = e < a.src.n ? a.digits[e] : 0u;
+    const i64 first = t * kSortTile + (i64)(tid % kSortBlock) * kPartItems;
+    static_assert(kPartItems == 8, "one 8-byte load of digits per thread");
+    u64 packed = 0;
+    if (first + kPartItems <= a.src.n) {
+        packed = *reinterpret_cast<const u64*>(a.digits + first);
+    } else {
+        for (int j = 0; j < kPartItems; ++j)
+            if (first + j < a.src.n) packed |= (u64)a.digits[first + j] << (8 * j);
     }
     for (int i = lane; i < kRadix; i += 64) hist[w][i] = 0;  // this wave's own row
     // Each thread merges runs of equal digits among its own records first,
@@ -535,8 +546,8 @@ __global__ __launch_bounds__(kCountBlock) void k_sort_count(SortArgs a) {
     u32 last = 0, run = 0;
 #pragma unroll
     for (int j = 0; j < kPartItems; ++j) {
-        if (wbase + (i64)j * 64 >= a.src.n) break;
-        const u32 d = digit[j];
+        if (first + j >= a.src.n) break;
+        const u32 d = (u32)(packed >> (8 * j)) & (kRadix - 1);
         if (run && d != last) {
             atomicAdd(&hist[w][last], run);
             run = 0;
@@ -681,6 +692,14 @@ struct PartArgs {
     u32 tiles;
     u32* chunk_counts; // bins x tiles: digit counts of each tile, then the
                        //   counts of the digit in the tiles before it
+    // When l1 is the round's level, the pass also fixes that level's nodes:
+    // the record whose rank in its new segment is the left subtree's size
+    // is the node's pivot ([W], sb/ss paragraph).
+    u64* piv_out;      // pivot table, or nullptr for an intermediate pass
+    int dim1;          // l1 mod k
+    LevelShape s2;     // closed-form constants of level l1 + 1
+    int32_t* perm;     // optional outputs for the nodes of level l1
+    float* tree;
 };
 
 // For every item: node[j], the in-level index of its node on level l1,
@@ -806,10 +825,23 @@ __global__ __launch_bounds__(kBlock) void k_part_scatter(PartArgs a) {
     for (int j = 0; j < kPartItems; ++j) {
         if (!valid[j]) continue;
         const u32 digit = node[j] & (bins - 1);
-        const u32 pos = live_begin32(a.s1, node[j]) -
-                        bin_prefix32(a.s1, node[j] >> delta, digit, delta) + count[w][digit] +
-                        rank[j];
-        if (pos < (u64)a.n_out) tr.store(a.src, a.out, j, wbase + (i64)j * 64, pos);
+        const u32 in_segment = count[w][digit] + rank[j] - bin_prefix32(a.s1, node[j] >> delta, digit, delta);
+        const u32 pos = live_begin32(a.s1, node[j]) + in_segment;
+        const i64 e = wbase + (i64)j * 64;
+        if (pos < (u64)a.n_out) tr.store(a.src, a.out, j, e, pos);
+        if (a.piv_out && in_segment == subtree_size32(a.s2, 2 * node[j])) {
+            const u64 s = full_nodes(a.l1) + node[j];
+            const u32 idx = tr.word(a.src, j, e, a.src.words - 1);
+            a.piv_out[s] = ((u64)float_key(tr.word(a.src, j, e, a.dim1)) << 32) | idx;
+            if (a.perm) a.perm[s] = (int32_t)idx;
+            if (a.tree) {
+                for (int d = 0; d < a.k; ++d) {
+                    const u32 bits = d < a.src.words - 1 ? tr.word(a.src, j, e, d)
+                                                         : __float_as_uint(a.src.pts[(u64)idx * a.k + d]);
+                    a.tree[s * a.k + d] = __uint_as_float(bits);
+                }
+            }
+        }
     }
 }
 
@@ -1524,6 +1556,7 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
         }
         // Bring A_d from the tags of its last use to the level-l tags, at
         // most kMaxDescent levels per pass.
+        bool pivots_done = false;
         while (level_of[d] < l) {
             const int l1 = level_of[d] + kMaxDescent < l ? level_of[d] + kMaxDescent : l;
             const int b = take(buf_of[d]);
@@ -1540,18 +1573,28 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
             a.s0 = level_shape(geo, a.l0);
             a.s1 = level_shape(geo, a.l1);
             a.piv = piv;
+            if (l1 == l) {  // this pass also fixes round l's nodes
+                a.piv_out = piv;
+                a.dim1 = l % k;
+                a.s2 = level_shape(geo, l + 1);
+                a.perm = perm;
+                a.tree = tree;
+                pivots_done = true;
+            }
             launch.part_any(a);
             holder[buf_of[d]] = -1;
             holder[b] = d;
             buf_of[d] = b;
             level_of[d] = l1;
         }
-        // Round l's nodes and their pivots.
-        const u64 nodes = 1ull << l;
-        timer.begin("k_pivots", (double)nodes * (4.0 * W + 8 + (perm ? 4 : 0) + (tree ? 8.0 * k : 0)));
-        k_pivots<<<(unsigned)((nodes + kBlock - 1) / kBlock), kBlock, 0, stream>>>(
-            recs(buf_of[d]), W, geo, l, d, piv, pts, k, perm, tree);
-        timer.end();
+        // Round l's nodes and their pivots (round 0 has no re-sort to do it).
+        if (!pivots_done) {
+            const u64 nodes = 1ull << l;
+            timer.begin("k_pivots", (double)nodes * (4.0 * W + 8 + (perm ? 4 : 0) + (tree ? 8.0 * k : 0)));
+            k_pivots<<<(unsigned)((nodes + kBlock - 1) / kBlock), kBlock, 0, stream>>>(
+                recs(buf_of[d]), W, geo, l, d, piv, pts, k, perm, tree);
+            timer.end();
+        }
         // A dimension not split on again frees its array (except the last
         // round's, which the subtree stage reads).
         if (l + k >= R && l != R - 1) holder[buf_of[d]] = -1;
