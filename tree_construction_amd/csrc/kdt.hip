@@ -1142,14 +1142,25 @@ __device__ void local_round(const uint16_t* order, u32 nc, int t, const Geometry
         }
     }
     __syncthreads();
+    // A point's sorted position is its segment's start plus its rank among
+    // the segment's points (the counts of earlier waves plus its rank in its
+    // wave), and the pivot's is the start plus |S(2s+1)|: only the rank and
+    // the left subtree's size need comparing. The left child of s = F(t) + b
+    // is the node with in-level index 2b on level t+1, whose subtree holds
+    // u - 1 full-level nodes and min(max(M - 2b u, 0), u) last-level ones
+    // (u = 2^(L-2-t), M = last-level nodes of the subtree's own tree).
+    const u32 dd = (u32)(lg.levels - 2 - t);  // t <= L-2
+    const u32 u = 1u << dd, last = (u32)lg.last;
 #pragma unroll
     for (int j = 0; j < kLocalItems; ++j) {
         const u32 q = (u32)local_slot(j);
-        const u64 s = seg[j];
+        const u32 s = seg[j];
         if (q >= nc || s < fl) continue;
-        const u64 p = segment_begin(lg, s, t) + seg_count[w * segs + (s - fl)] + rank[j];
-        const u64 pivot = segment_begin(lg, s, t) + subtree_size(lg, 2 * s + 1);
-        sh.tag[order[q]] = (uint16_t)(p < pivot ? 2 * s + 1 : (p > pivot ? 2 * s + 2 : s));
+        const u32 b = s - fl;
+        const u32 in_segment = seg_count[w * segs + b] + rank[j];
+        const u32 under = (2 * b) << dd;
+        const u32 left = (u - 1) + (last > under ? (last - under < u ? last - under : u) : 0u);
+        sh.tag[order[q]] = (uint16_t)(in_segment < left ? 2 * s + 1 : (in_segment > left ? 2 * s + 2 : s));
     }
     __syncthreads();
 }
