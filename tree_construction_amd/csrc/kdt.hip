@@ -198,6 +198,9 @@ __host__ __device__ inline u32 float_key(u32 b) {
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// Float bits of a key: exact except that both zeros come back as +0.
+__host__ __device__ inline u32 key_bits(u32 key) { return key >= 0x80000000u ? key & 0x7fffffffu : ~key; }
+
 // ------------------------------------------------------------- block scans
 
 __device__ inline u32 wave_inclusive_scan(u32 v) {
@@ -307,8 +310,10 @@ inline u32 xcd_grid(u64 tiles) { return (u32)((tiles + kXcds - 1) / kXcds * kXcd
 enum Src { kSrcRows = 0, kSrcRecords = 1 };
 
 // Where the records of a pass come from: kSrcRows builds the record of
-// point e from its row of `points` (its first words-1 coordinates as bits,
-// then e), in index order; kSrcRecords reads records of `words` words.
+// point e from its row of `points` (the keys of its first words-1
+// coordinates, then e), in index order; kSrcRecords reads records of
+// `words` words. Records carry keys, not float bits, so that every
+// comparison and digit is a plain unsigned one.
 struct RecordSource {
     const float* pts;
     int k;
@@ -320,7 +325,7 @@ struct RecordSource {
 template <int kSrc>
 __device__ inline u32 source_word(const RecordSource& s, u64 e, int w) {
     if (kSrc == kSrcRecords) return s.in[e * s.words + w];
-    return w < s.words - 1 ? __float_as_uint(s.pts[e * s.k + w]) : (u32)e;
+    return w < s.words - 1 ? float_key(__float_as_uint(s.pts[e * s.k + w])) : (u32)e;
 }
 
 // This thread's records of a tile. kW > 0 (at most 4 words): held in
@@ -364,6 +369,16 @@ struct RecordTile {
                         w0[j] = v.x;
                         w1[j] = v.y;
                     }
+                }
+            }
+            if constexpr (kSrc == kSrcRows) {
+                // keys only once every row load is in flight (inside the
+                // loads' branches the first use would wait for each load)
+#pragma unroll
+                for (int j = 0; j < kPartItems; ++j) {
+                    w0[j] = float_key(w0[j]);
+                    if constexpr (kW > 2) w1[j] = float_key(w1[j]);
+                    if constexpr (kW > 3) w2[j] = float_key(w2[j]);
                 }
             }
         }
@@ -586,7 +601,7 @@ __global__ __launch_bounds__(kSortBlock) void k_sort_scatter(SortArgs a) {
     for (int j = 0; j < kPartItems; ++j) {
         const i64 e = wbase + (i64)j * 64;
         valid[j] = e < a.src.n;
-        digit[j] = valid[j] ? (float_key(tr.word(a.src, j, e, a.dim)) >> a.shift) & (kRadix - 1) : 0u;
+        digit[j] = valid[j] ? (tr.word(a.src, j, e, a.dim) >> a.shift) & (kRadix - 1) : 0u;
     }
     // Thread tid < 256 owns digit tid: its records before this tile, and
     // the digit's total.
@@ -644,7 +659,7 @@ __global__ __launch_bounds__(kSortBlock) void k_sort_scatter(SortArgs a) {
             if (a.next_digits) {
                 const u32 c = (q.x & (a.dim == 0 ? ~0u : 0u)) | (q.y & (a.dim == 1 ? ~0u : 0u)) |
                               (q.z & (a.dim == 2 ? ~0u : 0u));
-                a.next_digits[dst] = (u8)(float_key(c) >> (a.shift + kRadixBits));
+                a.next_digits[dst] = (u8)(c >> (a.shift + kRadixBits));
             }
         }
     } else {
@@ -661,7 +676,7 @@ __global__ __launch_bounds__(kSortBlock) void k_sort_scatter(SortArgs a) {
                 if (dst >= (u64)a.src.n) continue;
                 a.out[(u64)dst * words + ww] = sm.words[i];
                 if (ww == a.dim && a.next_digits)
-                    a.next_digits[dst] = (u8)(float_key(sm.words[i]) >> (a.shift + kRadixBits));
+                    a.next_digits[dst] = (u8)(sm.words[i] >> (a.shift + kRadixBits));
             }
         }
     }
@@ -736,8 +751,7 @@ __device__ __forceinline__ void part_nodes(const PartArgs& a,
 #pragma unroll
         for (int j = 0; j < kPartItems; ++j) {
             const i64 e = wbase + (i64)j * 64;
-            const u64 me = ((u64)float_key(tr.word(a.src, j, e, dim)) << 32) |
-                           tr.word(a.src, j, e, a.src.words - 1);
+            const u64 me = ((u64)tr.word(a.src, j, e, dim) << 32) | tr.word(a.src, j, e, a.src.words - 1);
             const u64 p = valid[j] ? a.piv[node[j]] : 0;
             if (me == p) valid[j] = false;  // the pivot itself: a node already
             node[j] = 2 * node[j] + (me < p ? 1u : 2u);
@@ -832,15 +846,11 @@ __global__ __launch_bounds__(kBlock) void k_part_scatter(PartArgs a) {
         if (a.piv_out && in_segment == subtree_size32(a.s2, 2 * node[j])) {
             const u64 s = full_nodes(a.l1) + node[j];
             const u32 idx = tr.word(a.src, j, e, a.src.words - 1);
-            a.piv_out[s] = ((u64)float_key(tr.word(a.src, j, e, a.dim1)) << 32) | idx;
+            a.piv_out[s] = ((u64)tr.word(a.src, j, e, a.dim1) << 32) | idx;
             if (a.perm) a.perm[s] = (int32_t)idx;
-            if (a.tree) {
-                for (int d = 0; d < a.k; ++d) {
-                    const u32 bits = d < a.src.words - 1 ? tr.word(a.src, j, e, d)
-                                                         : __float_as_uint(a.src.pts[(u64)idx * a.k + d]);
-                    a.tree[s * a.k + d] = __uint_as_float(bits);
-                }
-            }
+            // (the row from `points`: a key does not keep the sign of zero)
+            if (a.tree)
+                for (int d = 0; d < a.k; ++d) a.tree[s * a.k + d] = a.src.pts[(u64)idx * a.k + d];
         }
     }
 }
@@ -861,7 +871,7 @@ __global__ __launch_bounds__(kBlock) void k_pivots(const u32* __restrict__ recs,
     if (s >= (u64)geo.n || p >= (u64)geo.n - full_nodes(l)) return;  // not for l < L-1
     const u32* r = recs + p * words;
     const u32 idx = r[words - 1];
-    piv[s] = ((u64)float_key(r[dim]) << 32) | idx;
+    piv[s] = ((u64)r[dim] << 32) | idx;
     if (perm) perm[s] = (int32_t)idx;
     if (tree && idx < (u64)geo.n)
         for (int d = 0; d < k; ++d) tree[s * k + d] = pts[(u64)idx * k + d];
@@ -1066,7 +1076,7 @@ struct SubtreeArgs {
     const u32* recs;        // l0 > 0: records (coordinates 0 .. words-2, then the
     int words;              // index) live on level l0-1, in round l0-1's order
     int index_bytes;        // bytes of a point index that can differ
-    u32* stage;             // (k+1) x n words: index, then coordinate columns; the
+    u32* stage;             // (k+1) x n words: index, then coordinate key columns; the
                             // subtree owns [first, first + |S(c)|) of each
     int32_t* perm;
     float* tree;
@@ -1082,7 +1092,7 @@ __device__ void local_order(const u32* __restrict__ col, u32 nc, uint16_t* order
     for (int j = 0; j < kLocalItems; ++j) {
         const int e = local_slot(j);
         rec[j] = ~0ull;
-        if ((u32)e < nc) rec[j] = ((u64)float_key(col[e]) << 16) | (u32)e;
+        if ((u32)e < nc) rec[j] = ((u64)col[e] << 16) | (u32)e;
     }
     local_sort(rec, 16, kKeyBytes, nc, sh);
 #pragma unroll
@@ -1178,13 +1188,13 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
         const u64 pivot = seg + subtree_size(a.geo, 2 * parent + 1);
         first = (c == 2 * parent + 1) ? seg : pivot + 1;
     }
-    // Coordinate d (bits) of the point with index i that arrived at
+    // Key of coordinate d of the point with index i that arrived at
     // position q: from its record while the record carries it, else from
     // its row of `points`.
     const int kr = a.recs ? a.words - 1 : 0;
     auto coord = [&](u32 q, u32 i, int d) -> u32 {
         return d < kr ? a.recs[(first + q) * a.words + d]
-                      : __float_as_uint(a.pts[(i64)i * a.k + d]);
+                      : float_key(__float_as_uint(a.pts[(i64)i * a.k + d]));
     };
 
     // Order the subtree's points by original index: slot e = index rank.
@@ -1288,19 +1298,27 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
         const int lvl = level_of(node);
         const u64 g = ((c + 1) << lvl) - 1 + (node - full_nodes(lvl));
         if (g >= (u64)a.n) continue;  // cannot happen: local nodes map inside the tree
-        a.perm[g] = (int32_t)stage_idx[e];
+        const u32 idx = stage_idx[e];
+        a.perm[g] = (int32_t)idx;
         if (!a.tree) continue;
+        // Coordinates from their keys; a zero key (both zeros have it) is
+        // read back from the row, which keeps the sign of zero.
         if (a.k <= kRowRegs) {
             u32 row[kRowRegs];
 #pragma unroll
             for (int d = 0; d < kRowRegs; ++d)
                 row[d] = d < a.k ? a.stage[(u64)(d + 1) * a.n + first + e] : 0u;
 #pragma unroll
-            for (int d = 0; d < kRowRegs; ++d)
-                if (d < a.k) a.tree[(i64)g * a.k + d] = __uint_as_float(row[d]);
+            for (int d = 0; d < kRowRegs; ++d) {
+                if (d >= a.k) continue;
+                const float v = row[d] == 0x80000000u ? a.pts[(i64)idx * a.k + d] : __uint_as_float(key_bits(row[d]));
+                a.tree[(i64)g * a.k + d] = v;
+            }
         } else {
-            for (int d = 0; d < a.k; ++d)
-                a.tree[(i64)g * a.k + d] = __uint_as_float(a.stage[(u64)(d + 1) * a.n + first + e]);
+            for (int d = 0; d < a.k; ++d) {
+                const u32 key = a.stage[(u64)(d + 1) * a.n + first + e];
+                a.tree[(i64)g * a.k + d] = key == 0x80000000u ? a.pts[(i64)idx * a.k + d] : __uint_as_float(key_bits(key));
+            }
         }
     }
 }
