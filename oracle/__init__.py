@@ -15,6 +15,8 @@ of Left-Balanced k-d Trees" (arXiv 2211.00120).
   ``kdt_check.cpp`` (strict k-d condition against every ancestor).
 * ``subtree_size`` -- size of a level-order subtree by counting its levels.
 * ``brute`` -- exhaustive enumeration for N <= 8 (module ``oracle.brute``).
+* ``knn`` -- brute-force K nearest neighbours in float32 (module
+  ``oracle.knn``), the reference for the tree's nearest-neighbour query.
 """
 from __future__ import annotations
 
