@@ -13,6 +13,12 @@ Prints ONE JSON line on stdout (progress goes to stderr):
              launch duration (HIP events on the build's stream), against the
              8 TB/s HBM peak
   cpu_baseline  the CPU oracle on a bounded sample of the same workload
+
+With --knn it instead times the K-nearest-neighbour query over the headline
+tree (the tree is built once, untimed): --knn-queries query points drawn with
+the workload's recipe, K = --knn-k; value in Mqueries/s, the roofline from the
+bytes of the tree points each search examined, and the brute-force oracle on a
+few sampled queries as cpu_baseline.
 """
 import argparse
 import csv
@@ -54,6 +60,74 @@ def cpu_baseline(name, sample_n):
             "sample": ("the whole workload %s" % name if sample_n == w.n else
                        "same recipe and seed as %s at N=%d" % (name, sample_n))
                       + " (k=%d), %.1f s wall" % (w.k, dt)}
+
+
+def knn_cpu_baseline(pts, qs, K, sample):
+    from oracle import knn as knn_oracle  # test infrastructure, used only for this baseline
+    t0 = time.perf_counter()
+    knn_oracle.knn(pts, qs[:sample], K)
+    dt = time.perf_counter() - t0
+    return {"value": round(sample / dt / 1e6, 9), "unit": "Mqueries/s", "cores": 1, "kind": "oracle",
+            "sample": "brute force (numpy, float32) for the first %d queries against all %d points, "
+                      "%.1f s wall" % (sample, len(pts), dt)}
+
+
+def run_knn(args):
+    import torch
+    from tree_construction_amd import datagen, kdt
+    name = args.workload or datagen.HEADLINE
+    pts = datagen.cached(name)
+    qs = datagen.generate(name, n=args.knn_queries)  # same recipe and seed, other draws
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(pts).to(dev)
+    q = torch.from_numpy(qs).to(dev)
+    n, k = pts.shape
+    Q, K = len(qs), args.knn_k
+    log("bench: building the %s tree (untimed)" % name)
+    perm, tree = kdt.build(x)
+    idx = torch.empty((Q, K), dtype=torch.int32, device=dev)
+    d2 = torch.empty((Q, K), dtype=torch.float32, device=dev)
+    visits = torch.empty(Q, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    kdt.knn(tree, perm, q, K, idx, d2, visits)
+    torch.cuda.synchronize(dev)
+    examined = float(visits.double().sum().item())
+    for _ in range(args.warmup):
+        kdt.knn(tree, perm, q, K, idx, d2)
+    log("bench: timing %d kNN passes (Q=%d, K=%d)" % (args.steps, Q, K))
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    start.record(stream)
+    for _ in range(args.steps):
+        kdt.knn(tree, perm, q, K, idx, d2)
+    stop.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = start.elapsed_time(stop) / args.steps
+    # algorithmic bytes of one pass: every examined tree point's coordinates,
+    # the queries, and the two outputs
+    nbytes = examined * 4 * k + Q * (4.0 * k + 8.0 * K)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log("bench: %.3f ms per pass, %.1f Mqueries/s, %.1f points examined per query, %.1f GB/s"
+        % (ms, Q / ms / 1e3, examined / Q, gbs))
+    base = None if args.no_cpu_baseline else knn_cpu_baseline(pts, qs, K, args.knn_cpu_sample)
+    if base:
+        log("  %s" % base)
+    out = {
+        "metric": "k-d tree kNN queries (K=%d) per second over the N=16M k=3 tree" % K,
+        "value": round(Q / ms / 1e3, 3),
+        "unit": "Mqueries/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "knn over %s" % name, "n_points": n, "k": k, "queries": Q, "K": K,
+                   "queries_from": "the workload's recipe and seed, %d further draws" % Q},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "k_knn",
+                     "points_examined_per_query": round(examined / Q, 2),
+                     "bytes_per_launch": int(nbytes)},
+        "cpu_baseline": base,
+    }
+    print(json.dumps(out), flush=True)
 
 
 def kernel_short_name(name):
@@ -111,6 +185,10 @@ def main():
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event loop")
     ap.add_argument("--no-counters", action="store_true",
                     help="skip the rocprofv3 FETCH_SIZE/WRITE_SIZE runs behind roofline.traffic")
+    ap.add_argument("--knn", action="store_true", help="time the kNN query instead of the build")
+    ap.add_argument("--knn-queries", type=int, default=1 << 20)
+    ap.add_argument("--knn-k", type=int, default=8)
+    ap.add_argument("--knn-cpu-sample", type=int, default=8, help="queries the brute-force baseline runs")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy, the reference "
                          "dispatch for scaling hardware traffic counters")
@@ -120,6 +198,9 @@ def main():
         log("bench.py: this build runs on one GPU only (no multi-GPU path); "
             "run it with --gpus 1")
         sys.exit(2)
+    if args.knn:
+        run_knn(args)
+        return
 
     import torch
     from tree_construction_amd import datagen, kdt

@@ -143,6 +143,33 @@ int64_t kdt_closed_segment_begin(int64_t N, int64_t s, int32_t l);
 int64_t kdt_closed_live_segment(int64_t N, int32_t l, int64_t p);
 int64_t kdt_closed_bin_prefix(int64_t N, int32_t l1, int32_t delta, int64_t j0, int64_t b);
 
+/* K nearest neighbours of each query point among the N points of a tree
+ * built by kdt_build (round-robin split dimensions), exactly as a brute-force
+ * search ranks them. The search is the two-phase descent and backtrack of
+ * F. Gieseke et al., "Bigger Buffer k-d Trees on Multi-Many-Core Systems"
+ * (arXiv 1512.02831), section 2.3, over the left-balanced level-order tree.
+ * Distances are float32 squared Euclidean distances, summed in dimension
+ * order with separately rounded products and sums; neighbours are ordered
+ * by (squared distance, original index).
+ *   tree      device, N*k float32: the tree_out of kdt_build (level order).
+ *   perm      device, N int32: the perm_out of the same build.
+ *   queries   device, Q*k float32, row-major. Read only.
+ *   K         neighbours per query, 1 <= K <= 32.
+ *   idx_out   device, Q*K int32: row q holds the original indices of query
+ *             q's K nearest points, nearest first; -1 where N < K.
+ *   d2_out    device, Q*K float32 or NULL: the matching squared distances
+ *             (+inf where N < K).
+ *   visits_out device, Q uint32 or NULL: the number of tree points the
+ *             search of each query examined (N when K >= N).
+ * Coordinates of points and queries must be finite. 0 <= N, Q <= 2^31 - 1;
+ * 1 <= k <= 65535. The outputs must not overlap the inputs or each other.
+ * Allocates nothing; enqueued on `stream`; argument errors
+ * (KDT_ERR_INVALID_ARG) are detected before anything is enqueued. */
+kdt_status kdt_knn(const float* tree, const int32_t* perm, int64_t N, int32_t k,
+                   const float* queries, int64_t Q, int32_t K,
+                   int32_t* idx_out, float* d2_out, uint32_t* visits_out,
+                   hipStream_t stream);
+
 /* Static description of a status code. */
 const char* kdt_status_string(kdt_status status);
 

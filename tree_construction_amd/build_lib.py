@@ -7,7 +7,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", "kdt.hip")]
+SOURCES = [os.path.join(PKG, "csrc", "kdt.hip"), os.path.join(PKG, "csrc", "knn.hip")]
 LIB_PATH = os.path.join(PKG, "libkdt.so")
 
 HIPCC_FLAGS = [

@@ -1,0 +1,246 @@
+// knn.hip -- K nearest neighbours over the left-balanced level-order tree
+// that kdt_build writes, on MI355X (gfx950).
+//
+// The search is the two-phase one of F. Gieseke et al., "Bigger Buffer k-d
+// Trees on Multi-Many-Core Systems" (arXiv 1512.02831), section 2.3: go down
+// the tree to the cell of the query, then back up, and on the way check the
+// other side of every splitting plane that lies closer to the query than the
+// current K-th neighbour. Here every node is a point (I. Wald's left-balanced
+// tree: node s has children 2s+1, 2s+2 and splits dimension level(s) mod k),
+// so each node visited on the way down is also a candidate. The way back up
+// follows the implicit parent links (s-1)/2 instead of a stack: a thread
+// remembers only the node it came from.
+//
+// Exactness. Distances are float32 squared distances summed in dimension
+// order with separately rounded products and sums, and neighbours are ranked
+// by (squared distance, original index), as the brute-force reference does.
+// The far side of a plane is skipped only when the squared plane distance is
+// strictly larger than the K-th squared distance: every point there differs
+// from the query by at least the plane distance in that dimension, rounding
+// is monotone, and a sum of non-negative rounded terms is at least each term,
+// so no skipped point could rank within the K (ties included). The result is
+// therefore identical to brute force, not an approximation.
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kdt.h"
+
+namespace {
+
+typedef uint32_t u32;
+typedef uint64_t u64;
+typedef int64_t i64;
+
+constexpr int kKnnBlock = 256;
+constexpr int kKnnMaxK = 32;  // neighbours per query at most
+
+struct KnnArgs {
+    const float* tree;   // N x k, level order
+    const int32_t* perm; // N: original index of each node's point
+    i64 n;
+    int k;
+    const float* queries;  // Q x k
+    i64 q;
+    int K;
+    int32_t* idx_out;    // Q x K
+    float* d2_out;       // Q x K or nullptr
+    uint32_t* visits_out;  // Q or nullptr: nodes examined per query
+};
+
+// The query's coordinates: kDims > 0 keeps them in registers (k == kDims);
+// kDims == 0 reads them from memory (any k).
+template <int kDims>
+struct Query {
+    float c[kDims > 0 ? kDims : 1];
+    const float* row;
+
+    __device__ __forceinline__ void load(const float* queries, u64 qi, int k) {
+        row = queries + qi * (u64)k;
+        if constexpr (kDims > 0) {
+#pragma unroll
+            for (int d = 0; d < kDims; ++d) c[d] = row[d];
+        }
+    }
+    // coordinate d (uniform or not); a select chain, never an indexed array
+    __device__ __forceinline__ float at(int d) const {
+        if constexpr (kDims == 0) {
+            return row[d];
+        } else {
+            float v = c[0];
+#pragma unroll
+            for (int i = 1; i < kDims; ++i) v = d == i ? c[i] : v;
+            return v;
+        }
+    }
+};
+
+template <int kDims>
+__device__ __forceinline__ float squared_distance(const Query<kDims>& q, const float* node, int k) {
+#pragma clang fp contract(off)
+    float acc = 0.0f;  // 0 + t0*t0 is t0*t0 exactly
+    if constexpr (kDims > 0) {
+        float p[kDims];
+#pragma unroll
+        for (int d = 0; d < kDims; ++d) p[d] = node[d];
+#pragma unroll
+        for (int d = 0; d < kDims; ++d) {
+            const float t = q.c[d] - p[d];
+            acc = acc + t * t;
+        }
+    } else {
+        for (int d = 0; d < k; ++d) {
+            const float t = q.row[d] - node[d];
+            acc = acc + t * t;
+        }
+    }
+    return acc;
+}
+
+// The K best candidates as 64-bit keys (float bits of the squared distance,
+// which order like the values for non-negative floats, then the index), in
+// descending order: slot[0] is the K-th best. Slots K .. kK-1 hold 0, below
+// every key, so they never move and the K best stay in slots 0 .. K-1.
+template <int kK>
+struct Best {
+    u64 slot[kK];
+
+    __device__ __forceinline__ void init(int K) {
+#pragma unroll
+        for (int i = 0; i < kK; ++i) slot[i] = i < K ? ~0ull : 0ull;
+    }
+    __device__ __forceinline__ u32 worst_bits() const { return (u32)(slot[0] >> 32); }
+    // key < slot[0]: slot[0] leaves, the larger keys move up one, key enters
+    __device__ __forceinline__ void insert(u64 key) {
+        bool placed = false;
+#pragma unroll
+        for (int i = 0; i < kK - 1; ++i) {
+            const u64 next = slot[i + 1];
+            const bool up = !placed && next > key;
+            slot[i] = up ? next : (placed ? slot[i] : key);
+            placed = placed || !up;
+        }
+        if (!placed) slot[kK - 1] = key;
+    }
+};
+
+template <int kK, int kDims>
+__global__ __launch_bounds__(kKnnBlock) void k_knn(KnnArgs a) {
+    const u64 qi = (u64)blockIdx.x * kKnnBlock + threadIdx.x;
+    if (qi >= (u64)a.q) return;
+    Query<kDims> q;
+    q.load(a.queries, qi, a.k);
+    Best<kK> best;
+    best.init(a.K);
+    const u32 n = (u32)a.n;
+    const int k = kDims > 0 ? kDims : a.k;
+    u32 visits = 0;
+    if (n > 0) {
+        // prev: the node the thread arrived from (~0 = from above the root)
+        u32 curr = 0, prev = ~0u;
+        int dim = 0;  // split dimension of curr's level
+        for (;;) {
+            if (curr >= n) {  // a child that does not exist: back to its parent
+                prev = curr;
+                curr = (curr - 1) >> 1;
+                dim = dim == 0 ? k - 1 : dim - 1;
+                continue;
+            }
+            const u32 parent = curr == 0 ? ~0u : (curr - 1) >> 1;
+            const float* node = a.tree + (u64)curr * (u64)k;
+            const float diff = q.at(dim) - node[dim];
+            const u32 left = 2 * curr + 1;
+            const u32 near = diff < 0.0f ? left : left + 1;
+            const u32 far = diff < 0.0f ? left + 1 : left;
+            const int down = dim + 1 == k ? 0 : dim + 1;
+            if (prev == parent) {
+                // first visit: the node's point is a candidate; go to the
+                // query's side first
+                ++visits;
+                const u32 bits = __float_as_uint(squared_distance<kDims>(q, node, k));
+                if (bits <= best.worst_bits()) {
+                    const u64 key = ((u64)bits << 32) | (u32)a.perm[curr];
+                    if (key < best.slot[0]) best.insert(key);
+                }
+                prev = curr;
+                curr = near;
+                dim = down;
+                continue;
+            }
+            if (prev == near && far < n && __float_as_uint(diff * diff) <= best.worst_bits()) {
+                prev = curr;
+                curr = far;
+                dim = down;
+                continue;
+            }
+            if (curr == 0) break;
+            prev = curr;
+            curr = parent;
+            dim = dim == 0 ? k - 1 : dim - 1;
+        }
+    }
+    if (a.visits_out) a.visits_out[qi] = visits;
+    // ascending output: slot K-1 first
+    int32_t* out_idx = a.idx_out + qi * (u64)a.K;
+    float* out_d2 = a.d2_out ? a.d2_out + qi * (u64)a.K : nullptr;
+#pragma unroll
+    for (int i = 0; i < kK; ++i) {
+        if (i >= a.K) continue;
+        const u64 key = best.slot[i];
+        const int at = a.K - 1 - i;
+        const bool empty = key == ~0ull;
+        out_idx[at] = empty ? -1 : (int32_t)(u32)key;
+        if (out_d2) out_d2[at] = empty ? __uint_as_float(0x7f800000u) : __uint_as_float((u32)(key >> 32));
+    }
+}
+
+template <int kK>
+void launch_knn(const KnnArgs& a, hipStream_t stream) {
+    const unsigned grid = (unsigned)((a.q + kKnnBlock - 1) / kKnnBlock);
+    switch (a.k) {
+        case 2: k_knn<kK, 2><<<grid, kKnnBlock, 0, stream>>>(a); break;
+        case 3: k_knn<kK, 3><<<grid, kKnnBlock, 0, stream>>>(a); break;
+        case 4: k_knn<kK, 4><<<grid, kKnnBlock, 0, stream>>>(a); break;
+        default: k_knn<kK, 0><<<grid, kKnnBlock, 0, stream>>>(a); break;
+    }
+}
+
+bool overlap(const void* a, size_t an, const void* b, size_t bn) {
+    if (!a || !b || an == 0 || bn == 0) return false;
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + bn && y < x + an;
+}
+
+}  // namespace
+
+extern "C" kdt_status kdt_knn(const float* tree, const int32_t* perm, int64_t N, int32_t k,
+                              const float* queries, int64_t Q, int32_t K, int32_t* idx_out,
+                              float* d2_out, uint32_t* visits_out, hipStream_t stream) {
+    if (N < 0 || N > INT32_MAX || k < 1 || k > 65535 || Q < 0 || Q > INT32_MAX || K < 1 ||
+        K > kKnnMaxK)
+        return KDT_ERR_INVALID_ARG;
+    if (Q == 0) return KDT_OK;
+    if (!queries || !idx_out || (N > 0 && (!tree || !perm))) return KDT_ERR_INVALID_ARG;
+    const size_t tree_b = (size_t)N * k * sizeof(float), perm_b = (size_t)N * sizeof(int32_t);
+    const size_t q_b = (size_t)Q * k * sizeof(float), out_b = (size_t)Q * K * sizeof(int32_t);
+    const void* ins[3] = {tree, perm, queries};
+    const size_t in_b[3] = {tree_b, perm_b, q_b};
+    for (int i = 0; i < 3; ++i)
+        if (overlap(idx_out, out_b, ins[i], in_b[i]) || overlap(d2_out, out_b, ins[i], in_b[i]))
+            return KDT_ERR_INVALID_ARG;
+    const size_t v_b = (size_t)Q * sizeof(uint32_t);
+    for (int i = 0; i < 3; ++i)
+        if (overlap(visits_out, v_b, ins[i], in_b[i])) return KDT_ERR_INVALID_ARG;
+    if (overlap(idx_out, out_b, d2_out, out_b) || overlap(visits_out, v_b, idx_out, out_b) ||
+        overlap(visits_out, v_b, d2_out, out_b))
+        return KDT_ERR_INVALID_ARG;
+    KnnArgs a{tree, perm, N, k, queries, Q, K, idx_out, d2_out, visits_out};
+    if (K <= 1) launch_knn<1>(a, stream);
+    else if (K <= 2) launch_knn<2>(a, stream);
+    else if (K <= 4) launch_knn<4>(a, stream);
+    else if (K <= 8) launch_knn<8>(a, stream);
+    else if (K <= 16) launch_knn<16>(a, stream);
+    else launch_knn<32>(a, stream);
+    return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
+}

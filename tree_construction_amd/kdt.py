@@ -49,8 +49,12 @@ SIGNATURES = {
     "kdt_debug_workspace_size": (_SZ, [_I64, _I32, _I32]),
     "kdt_closed_live_segment": (_I64, [_I64, _I32, _I64]),
     "kdt_closed_bin_prefix": (_I64, [_I64, _I32, _I32, _I64, _I64]),
+    "kdt_knn": (ctypes.c_int, [_VOIDP, _VOIDP, _I64, _I32, _VOIDP, _I64, _I32, _VOIDP, _VOIDP, _VOIDP,
+                               _VOIDP]),
     "kdt_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
+
+KNN_MAX_K = 32
 
 _lock = threading.Lock()
 _lib = None
@@ -192,3 +196,36 @@ def build(points, want_tree: bool = True, stream=None):
     _validate_points(points)
     n, k = points.shape
     return Builder(n, k, points.device).build(points, want_tree=want_tree, stream=stream)
+
+
+def knn(tree, perm, queries, K: int, idx=None, d2=None, visits=None, stream=None):
+    """K nearest neighbours of every query among the points of a built tree.
+
+    tree, perm: the outputs of build() ((N, k) float32 and (N,) int32 on a
+    HIP device); queries: (Q, k) float32 on the same device. Returns (idx, d2):
+    (Q, K) int32 original indices, nearest first (-1 past N), and their
+    (Q, K) float32 squared distances. A (Q,) int32 tensor passed as `visits`
+    receives the number of tree points each search examined."""
+    import torch
+    _validate_points(queries)
+    if tree is not None:
+        _validate_points(tree)
+    n = 0 if tree is None else tree.shape[0]
+    k = queries.shape[1]
+    if tree is not None and tree.shape[1] != k:
+        raise ValueError("tree has k=%d, queries k=%d" % (tree.shape[1], k))
+    if perm is not None and (perm.dtype != torch.int32 or perm.numel() != n or not perm.is_contiguous()):
+        raise ValueError("perm must be a contiguous int32 tensor of N entries")
+    q = queries.shape[0]
+    if idx is None:
+        idx = torch.empty((q, K), dtype=torch.int32, device=queries.device)
+    if d2 is None:
+        d2 = torch.empty((q, K), dtype=torch.float32, device=queries.device)
+    st = lib().kdt_knn(ctypes.c_void_p(tree.data_ptr() if n else 0),
+                       ctypes.c_void_p(perm.data_ptr() if n else 0), n, k,
+                       ctypes.c_void_p(queries.data_ptr()), q, int(K),
+                       ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(d2.data_ptr()),
+                       ctypes.c_void_p(visits.data_ptr() if visits is not None else 0),
+                       _stream_handle(queries.device, stream))
+    _check(st, "kdt_knn")
+    return idx, d2
