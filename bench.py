@@ -32,6 +32,8 @@ import sys
 import tempfile
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -91,18 +93,33 @@ def run_knn(args):
     stream = torch.cuda.current_stream(dev)
     kdt.knn(tree, perm, q, K, idx, d2, visits)
     torch.cuda.synchronize(dev)
-    examined = float(visits.double().sum().item())
+    v = visits.cpu().numpy()
+    examined = float(v.astype(np.float64).sum())
     for _ in range(args.warmup):
         kdt.knn(tree, perm, q, K, idx, d2)
+
+    def timed(qq):
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize(dev)
+        start.record(stream)
+        for _ in range(args.steps):
+            kdt.knn(tree, perm, qq, K)
+        stop.record(stream)
+        torch.cuda.synchronize(dev)
+        return start.elapsed_time(stop) / args.steps
+
     log("bench: timing %d kNN passes (Q=%d, K=%d)" % (args.steps, Q, K))
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize(dev)
-    start.record(stream)
-    for _ in range(args.steps):
-        kdt.knn(tree, perm, q, K, idx, d2)
-    stop.record(stream)
-    torch.cuda.synchronize(dev)
-    ms = start.elapsed_time(stop) / args.steps
+    ms = timed(q)
+    # the spread of the work: the pass without its 100 most expensive
+    # queries, and the most expensive one alone
+    order = np.argsort(-v, kind="stable")
+    rest_ms = timed(q[torch.from_numpy(np.sort(order[100:])).to(dev)].contiguous())
+    worst_ms = timed(q[int(order[0]):int(order[0]) + 1].contiguous())
+    spread = {"mean": round(examined / Q, 2), "p50": int(np.percentile(v, 50)),
+              "p99": int(np.percentile(v, 99)), "max": int(v.max()),
+              "ms_without_100_most_expensive": round(rest_ms, 4),
+              "ms_most_expensive_alone": round(worst_ms, 4)}
+    log("bench: examined points per query %s" % spread)
     # algorithmic bytes of one pass: every examined tree point's coordinates,
     # the queries, and the two outputs
     nbytes = examined * 4 * k + Q * (4.0 * k + 8.0 * K)
@@ -123,7 +140,7 @@ def run_knn(args):
                    "queries_from": "the workload's recipe and seed, %d further draws" % Q},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "k_knn",
-                     "points_examined_per_query": round(examined / Q, 2),
+                     "points_examined_per_query": spread,
                      "bytes_per_launch": int(nbytes)},
         "cpu_baseline": base,
     }
