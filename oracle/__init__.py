@@ -17,6 +17,10 @@ of Left-Balanced k-d Trees" (arXiv 2211.00120).
 * ``brute`` -- exhaustive enumeration for N <= 8 (module ``oracle.brute``).
 * ``knn`` -- brute-force K nearest neighbours in float32 (module
   ``oracle.knn``), the reference for the tree's nearest-neighbour query.
+* ``build_tree_widest`` -- the split-widest-dimension variant's recursive
+  builder (``kdt_widest.cpp``); ``widest_check.check`` verifies such a tree
+  by the page's other formulation (domains clipped bottom-up from each node
+  to the root).
 """
 from __future__ import annotations
 
@@ -28,7 +32,7 @@ import threading
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SOURCES = ("kdt_oracle.cpp", "kdt_check.cpp")
+_SOURCES = ("kdt_oracle.cpp", "kdt_check.cpp", "kdt_widest.cpp")
 LIB_PATH = os.path.join(_HERE, "libkdt_oracle.so")
 _lock = threading.Lock()
 _lib = None
@@ -55,6 +59,9 @@ def _bind(lib):
     lib.kdto_subtree_size.argtypes = [ctypes.c_int64, ctypes.c_int64]
     lib.kdto_check.restype = ctypes.c_int64
     lib.kdto_check.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
+    lib.kdto_build_widest.restype = ctypes.c_int
+    lib.kdto_build_widest.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
     lib.kdto_max_threads.restype = ctypes.c_int
     lib.kdto_max_threads.argtypes = []
     return lib
@@ -91,6 +98,20 @@ def build_tree(points, nthreads: int = 0, lib=None) -> np.ndarray:
     if rc != 0:
         raise ValueError("oracle rejected arguments (N=%d, k=%d)" % (n, k))
     return perm
+
+
+def build_tree_widest(points, nthreads: int = 0, lib=None):
+    """Split-widest-dimension tree (kdt_widest.cpp): (perm, dims), perm[node]
+    = original index of its point, dims[node] = its split dimension."""
+    lib = lib or load_lib()
+    pts = _points(points)
+    n, k = pts.shape
+    perm = np.empty(n, dtype=np.int32)
+    dims = np.empty(n, dtype=np.int32)
+    rc = lib.kdto_build_widest(pts.ctypes.data, n, k, perm.ctypes.data, dims.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected arguments (N=%d, k=%d)" % (n, k))
+    return perm, dims
 
 
 def check_tree(points, perm, lib=None) -> int:

@@ -278,7 +278,7 @@ def test_unmutated_oracle_passes_in_child():
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_planted_mistakes_are_caught(name, tmp_path):
     src_dir = os.path.dirname(oracle.__file__)
-    for f in ("kdt_oracle.cpp", "kdt_check.cpp"):
+    for f in oracle._SOURCES:
         shutil.copy(os.path.join(src_dir, f), tmp_path / f)
     path = tmp_path / "kdt_oracle.cpp"
     text = path.read_text()
