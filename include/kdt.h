@@ -143,6 +143,32 @@ int64_t kdt_closed_segment_begin(int64_t N, int64_t s, int32_t l);
 int64_t kdt_closed_live_segment(int64_t N, int32_t l, int64_t p);
 int64_t kdt_closed_bin_prefix(int64_t N, int32_t l1, int32_t delta, int64_t j0, int64_t b);
 
+/* Split-widest-dimension variant ([W], split-widest-dimension section).
+ * The same left-balanced complete level-order tree, except that node s
+ * splits along the dimension in which its domain is widest: the root's
+ * domain is the bounding box of all points (per-dimension minimum and
+ * maximum); a child's domain is its parent's, bounded at the parent's point
+ * in the parent's dimension (upper bound on the left, lower bound on the
+ * right); "widest" compares float32 extents hi - lo and takes the lowest
+ * dimension on ties. The point at s is the element of rank |S(2s+1)| of
+ * its subtree's points by (coordinate in s's dimension, original index).
+ *   dims_out  device, N int32 or NULL: dims_out[s] = split dimension of
+ *             node s (every node, leaves included).
+ * Other arguments, ownership and errors as kdt_build; the workspace is
+ * kdt_workspace_size_widest(N, k) bytes. Every level runs as a global pass
+ * over all points here, so a build costs more than kdt_build's. */
+size_t kdt_workspace_size_widest(int64_t N, int32_t k);
+kdt_status kdt_build_widest(const float* points, int64_t N, int32_t k,
+                            int32_t* perm_out, float* tree_out, int32_t* dims_out,
+                            void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/* kdt_build_widest with per-kernel timing, as kdt_build_profiled. */
+kdt_status kdt_build_widest_profiled(const float* points, int64_t N, int32_t k,
+                                     int32_t* perm_out, float* tree_out, int32_t* dims_out,
+                                     void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream, kdt_profile* profile);
+
 /* K nearest neighbours of each query point among the N points of a tree
  * built by kdt_build (round-robin split dimensions), exactly as a brute-force
  * search ranks them. The search is the two-phase descent and backtrack of

@@ -39,6 +39,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "kdt.h"
 
 namespace {
@@ -715,6 +717,13 @@ struct PartArgs {
     LevelShape s2;     // closed-form constants of level l1 + 1
     int32_t* perm;     // optional outputs for the nodes of level l1
     float* tree;
+    // Split-widest-dimension trees: every node's split dimension (nullptr:
+    // level mod k). The array is sorted by coordinate array_dim, so the pass
+    // fixes only the level-l1 nodes that split it; leaf_level: l1 is the
+    // last level, whose nodes have empty subtrees below them.
+    const uint16_t* dimtab;
+    int array_dim;
+    int leaf_level;
 };
 
 // For every item: node[j], the in-level index of its node on level l1,
@@ -745,13 +754,15 @@ __device__ __forceinline__ void part_nodes(const PartArgs& a,
         }
         node[j] = (u32)full_nodes(a.l0) + j0;
     }
-    // One level at a time: compare with the pivot of the current node.
+    // One level at a time: compare with the pivot of the current node, in
+    // the level's dimension (or the node's own, from the table).
     int dim = a.dim0;
     for (int l = a.l0; l < a.l1; ++l) {
 #pragma unroll
         for (int j = 0; j < kPartItems; ++j) {
             const i64 e = wbase + (i64)j * 64;
-            const u64 me = ((u64)tr.word(a.src, j, e, dim) << 32) | tr.word(a.src, j, e, a.src.words - 1);
+            const int dj = a.dimtab ? (valid[j] ? (int)a.dimtab[node[j]] : 0) : dim;
+            const u64 me = ((u64)tr.word(a.src, j, e, dj) << 32) | tr.word(a.src, j, e, a.src.words - 1);
             const u64 p = valid[j] ? a.piv[node[j]] : 0;
             if (me == p) valid[j] = false;  // the pivot itself: a node already
             node[j] = 2 * node[j] + (me < p ? 1u : 2u);
@@ -843,7 +854,9 @@ __global__ __launch_bounds__(kBlock) void k_part_scatter(PartArgs a) {
         const u32 pos = live_begin32(a.s1, node[j]) + in_segment;
         const i64 e = wbase + (i64)j * 64;
         if (pos < (u64)a.n_out) tr.store(a.src, a.out, j, e, pos);
-        if (a.piv_out && in_segment == subtree_size32(a.s2, 2 * node[j])) {
+        const u32 left = a.leaf_level ? 0u : subtree_size32(a.s2, 2 * node[j]);
+        if (a.piv_out && in_segment == left &&
+            (!a.dimtab || a.dimtab[full_nodes(a.l1) + node[j]] == (uint16_t)a.array_dim)) {
             const u64 s = full_nodes(a.l1) + node[j];
             const u32 idx = tr.word(a.src, j, e, a.src.words - 1);
             a.piv_out[s] = ((u64)tr.word(a.src, j, e, a.dim1) << 32) | idx;
@@ -863,12 +876,14 @@ __global__ __launch_bounds__(kBlock) void k_pivots(const u32* __restrict__ recs,
                                                    u64* __restrict__ piv,
                                                    const float* __restrict__ pts, int k,
                                                    int32_t* __restrict__ perm,
-                                                   float* __restrict__ tree) {
+                                                   float* __restrict__ tree,
+                                                   const uint16_t* __restrict__ dimtab) {
     const u64 j = (u64)blockIdx.x * kBlock + threadIdx.x;
     if (j >= (1ull << l)) return;
     const u64 s = full_nodes(l) + j;
     const u64 p = live_begin(geo, j, l) + subtree_size(geo, 2 * s + 1);
     if (s >= (u64)geo.n || p >= (u64)geo.n - full_nodes(l)) return;  // not for l < L-1
+    if (dimtab && dimtab[s] != (uint16_t)dim) return;  // another array's node
     const u32* r = recs + p * words;
     const u32 idx = r[words - 1];
     piv[s] = ((u64)r[dim] << 32) | idx;
@@ -896,6 +911,129 @@ __global__ __launch_bounds__(kBlock) void k_descend_tags(const float* __restrict
         }
         tags[i] = (u32)s;
     }
+}
+
+// ------------------------------------ split-widest-dimension domains
+// [W], split-widest-dimension section: the root's domain is the bounding box
+// of all points; every node splits the dimension in which its domain is
+// widest (float32 extent hi - lo, the lower dimension on ties); a child's
+// domain is its parent's, bounded at the parent's plane (its point's
+// coordinate in the parent's dimension: upper bound for the left child,
+// lower bound for the right one).
+
+// Per-dimension minimum and maximum of one chunk of points (grid: chunks x
+// k); partial[(d * chunks + c) * 2 + {0, 1}].
+__global__ __launch_bounds__(kBlock) void k_box_partial(const float* __restrict__ pts, i64 n, int k,
+                                                        i64 chunk, float* __restrict__ partial) {
+    const int d = blockIdx.y;
+    const i64 c = blockIdx.x, first = c * chunk;
+    const i64 last = first + chunk < n ? first + chunk : n;
+    float lo = __uint_as_float(0x7f800000u), hi = __uint_as_float(0xff800000u);  // +inf, -inf
+    for (i64 i = first + threadIdx.x; i < last; i += kBlock) {
+        const float x = pts[i * k + d];
+        if (x < lo) lo = x;
+        if (hi < x) hi = x;
+    }
+    __shared__ float s_lo[kWaves], s_hi[kWaves];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float ol = __shfl_xor(lo, o, 64), oh = __shfl_xor(hi, o, 64);
+        if (ol < lo) lo = ol;
+        if (hi < oh) hi = oh;
+    }
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        s_lo[w] = lo;
+        s_hi[w] = hi;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int v = 1; v < kWaves; ++v) {
+            if (s_lo[v] < lo) lo = s_lo[v];
+            if (hi < s_hi[v]) hi = s_hi[v];
+        }
+        partial[(d * (i64)gridDim.x + c) * 2] = lo;
+        partial[(d * (i64)gridDim.x + c) * 2 + 1] = hi;
+    }
+}
+
+// The root domain (lo[0..k), hi[0..k)) from the chunks' (grid: k blocks).
+__global__ __launch_bounds__(kBlock) void k_box_final(const float* __restrict__ partial, i64 chunks,
+                                                      int k, float* __restrict__ box) {
+    const int d = blockIdx.x;
+    float lo = __uint_as_float(0x7f800000u), hi = __uint_as_float(0xff800000u);
+    for (i64 c = threadIdx.x; c < chunks; c += kBlock) {
+        const float pl = partial[(d * chunks + c) * 2], ph = partial[(d * chunks + c) * 2 + 1];
+        if (pl < lo) lo = pl;
+        if (hi < ph) hi = ph;
+    }
+    __shared__ float s_lo[kWaves], s_hi[kWaves];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float ol = __shfl_xor(lo, o, 64), oh = __shfl_xor(hi, o, 64);
+        if (ol < lo) lo = ol;
+        if (hi < oh) hi = oh;
+    }
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        s_lo[w] = lo;
+        s_hi[w] = hi;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int v = 1; v < kWaves; ++v) {
+            if (s_lo[v] < lo) lo = s_lo[v];
+            if (hi < s_hi[v]) hi = s_hi[v];
+        }
+        box[d] = lo;
+        box[k + d] = hi;
+    }
+}
+
+// Domains and split dimensions of the nodes of level l (2k floats a node:
+// lo then hi), from their parents' (the root's from the bounding box). The
+// parents' pivots are fixed.
+__global__ __launch_bounds__(kBlock) void k_widest_level(Geometry geo, int l, int k,
+                                                         const u64* __restrict__ piv,
+                                                         const float* __restrict__ root_box,
+                                                         float* __restrict__ boxes,
+                                                         uint16_t* __restrict__ dimtab,
+                                                         int32_t* __restrict__ dims_out) {
+    const u64 j = (u64)blockIdx.x * kBlock + threadIdx.x;
+    if (j >= (1ull << l)) return;
+    const u64 s = full_nodes(l) + j;
+    if (s >= (u64)geo.n) return;
+    const float* from = root_box;
+    int pd = -1;
+    float plane = 0.0f;
+    bool left = false;
+    if (l > 0) {
+        const u64 p = (s - 1) / 2;
+        from = boxes + p * 2 * (u64)k;
+        pd = dimtab[p];
+        plane = __uint_as_float(key_bits((u32)(piv[p] >> 32)));  // a zero's sign is lost: extents agree
+        left = s == 2 * p + 1;
+    }
+    float* box = boxes + s * 2 * (u64)k;
+    int best = 0;
+    float best_extent = 0.0f;
+    for (int d = 0; d < k; ++d) {
+        float lo = from[d], hi = from[k + d];
+        if (d == pd) {
+            if (left) hi = plane;
+            else lo = plane;
+        }
+        box[d] = lo;
+        box[k + d] = hi;
+        const float extent = hi - lo;
+        if (d == 0) best_extent = extent;
+        else if (extent > best_extent) {
+            best = d;
+            best_extent = extent;
+        }
+    }
+    dimtab[s] = (uint16_t)best;
+    if (dims_out) dims_out[s] = best;
 }
 
 __global__ __launch_bounds__(kBlock) void k_zero(u32* __restrict__ out, i64 n) {
@@ -1388,6 +1526,56 @@ bool make_layout(i64 n, int k, int rounds, bool stage, Layout* out) {
     return true;
 }
 
+// Workspace of a split-widest build: every level is a global round (its
+// nodes' dimensions differ, so no subtree finishes in LDS), every dimension
+// keeps an array, and each node has a domain and a split dimension.
+constexpr i64 kBoxChunk = 1 << 16;  // points per partial bounding box
+
+struct WidestLayout {
+    Layout base;  // rounds = levels; records carry all k coordinates
+    size_t boxes, dimtab, root_box, box_partial;
+    i64 box_chunks;
+};
+
+bool make_layout_widest(i64 n, int k, WidestLayout* out) {
+    if (n < 0 || n > INT32_MAX || k < 1 || k > 65535) return false;
+    WidestLayout w{};
+    if (n <= 1) {
+        *out = w;
+        return true;
+    }
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align_up(off + bytes);
+        return at;
+    };
+    Layout& lay = w.base;
+    lay.rounds = make_geometry(n).levels;
+    lay.kr = k;
+    lay.words = k + 1;
+    lay.nbuf = k + 1;
+    lay.tiles = (n + kPartTile - 1) / kPartTile;
+    const size_t rec_bytes = (size_t)n * lay.words * sizeof(u32);
+    lay.tmp0 = take(rec_bytes);
+    lay.tmp1 = take(rec_bytes);
+    lay.digits = take((size_t)n);
+    lay.digits0 = take((size_t)k * n);
+    lay.recs = take((size_t)lay.nbuf * rec_bytes);
+    lay.piv = take((size_t)full_nodes(lay.rounds) * sizeof(u64));
+    lay.totals = take((size_t)kRadix * sizeof(u32));
+    lay.slots = take((size_t)lay.tiles * kRadix * sizeof(u32));
+    lay.chunk_slots = take((size_t)((lay.tiles + kChunkTiles - 1) / kChunkTiles) * kRadix * sizeof(u32));
+    w.boxes = take((size_t)n * 2 * k * sizeof(float));
+    w.dimtab = take((size_t)n * sizeof(uint16_t));
+    w.root_box = take((size_t)2 * k * sizeof(float));
+    w.box_chunks = (n + kBoxChunk - 1) / kBoxChunk;
+    w.box_partial = take((size_t)w.box_chunks * k * 2 * sizeof(float));
+    lay.total = off;
+    *out = w;
+    return true;
+}
+
 inline int grid_for(i64 work, int per_block, int cap) {
     i64 g = (work + per_block - 1) / per_block;
     if (g < 1) g = 1;
@@ -1621,7 +1809,7 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
             const u64 nodes = 1ull << l;
             timer.begin("k_pivots", (double)nodes * (4.0 * W + 8 + (perm ? 4 : 0) + (tree ? 8.0 * k : 0)));
             k_pivots<<<(unsigned)((nodes + kBlock - 1) / kBlock), kBlock, 0, stream>>>(
-                recs(buf_of[d]), W, geo, l, d, piv, pts, k, perm, tree);
+                recs(buf_of[d]), W, geo, l, d, piv, pts, k, perm, tree, nullptr);
             timer.end();
         }
         // A dimension not split on again frees its array (except the last
@@ -1629,6 +1817,102 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
         if (l + k >= R && l != R - 1) holder[buf_of[d]] = -1;
     }
     *last = recs(buf_of[(R - 1) % k]);
+    return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
+}
+
+// A split-widest-dimension build ([W], split-widest-dimension section): the
+// root domain and dimension first; every dimension's array presorted; then
+// level by level, every array re-sorted by the new tags (one pass of one
+// level), each fixing the nodes of the level that split its dimension, and
+// the next level's domains and dimensions from the pivots just fixed. The
+// last level's pass places the leaves.
+kdt_status run_widest(const float* pts, i64 n, int k, const WidestLayout& wl, char* ws,
+                      hipStream_t stream, Timer timer, int32_t* perm, float* tree,
+                      int32_t* dims_out) {
+    const Layout& lay = wl.base;
+    const int L = lay.rounds, W = lay.words;
+    const Geometry geo = make_geometry(n);
+    u32* tmp[2] = {(u32*)(ws + lay.tmp0), (u32*)(ws + lay.tmp1)};
+    u8* digits = (u8*)(ws + lay.digits);
+    u8* digits0 = (u8*)(ws + lay.digits0);
+    u64* piv = (u64*)(ws + lay.piv);
+    float* boxes = (float*)(ws + wl.boxes);
+    uint16_t* dimtab = (uint16_t*)(ws + wl.dimtab);
+    float* root_box = (float*)(ws + wl.root_box);
+    float* partial = (float*)(ws + wl.box_partial);
+    auto recs = [&](int b) { return (u32*)(ws + lay.recs) + (size_t)b * n * W; };
+    Launcher launch{(u32*)(ws + lay.slots), (u32*)(ws + lay.chunk_slots), (u32*)(ws + lay.totals),
+                    stream, timer};
+    auto level = [&](int l) {
+        const u64 nodes = 1ull << l;
+        timer.begin("k_widest_level", (double)nodes * (16.0 * k + 10 + (dims_out ? 4 : 0)));
+        k_widest_level<<<(unsigned)((nodes + kBlock - 1) / kBlock), kBlock, 0, stream>>>(
+            geo, l, k, piv, root_box, boxes, dimtab, dims_out);
+        timer.end();
+    };
+
+    timer.begin("k_box_partial", (double)n * 4.0 * k);
+    k_box_partial<<<dim3((unsigned)wl.box_chunks, (unsigned)k), kBlock, 0, stream>>>(pts, n, k, kBoxChunk,
+                                                                                   partial);
+    timer.end();
+    timer.begin("k_box_final", (double)wl.box_chunks * k * 8.0 + 8.0 * k);
+    k_box_final<<<(unsigned)k, kBlock, 0, stream>>>(partial, wl.box_chunks, k, root_box);
+    timer.end();
+    level(0);
+
+    timer.begin("k_first_digits", (double)n * 5.0 * k);
+    k_first_digits<<<grid_for(n, kBlock, 1 << 30), kBlock, 0, stream>>>(pts, n, k, k, digits0);
+    timer.end();
+    // A_d in buffer d, by (coordinate d, index): the order of level 0.
+    for (int d = 0; d < k; ++d)
+        for (int p = 0; p < kKeyBytes; ++p) {
+            SortArgs a{};
+            a.src = RecordSource{pts, k, p == 0 ? nullptr : tmp[(p + 1) & 1], W, n};
+            a.out = p == kKeyBytes - 1 ? recs(d) : tmp[p & 1];
+            a.dim = d;
+            a.shift = 8 * p;
+            a.digits = p == 0 ? digits0 + (size_t)d * n : digits;
+            a.next_digits = p == kKeyBytes - 1 ? nullptr : digits;
+            if (p == 0) launch.sort_any<kSrcRows>(a);
+            else launch.sort_any<kSrcRecords>(a);
+        }
+    std::vector<int> buffer(k);
+    for (int d = 0; d < k; ++d) buffer[d] = d;
+    int spare = k;
+    // The root's pivot, from the array of its dimension.
+    for (int d = 0; d < k; ++d) {
+        timer.begin("k_pivots", 4.0 * W + 8 + (perm ? 4 : 0) + (tree ? 8.0 * k : 0));
+        k_pivots<<<1, kBlock, 0, stream>>>(recs(buffer[d]), W, geo, 0, d, piv, pts, k, perm, tree, dimtab);
+        timer.end();
+    }
+    if (L > 1) level(1);
+    for (int l = 1; l < L; ++l) {
+        for (int d = 0; d < k; ++d) {
+            PartArgs a{};
+            a.src = RecordSource{pts, k, recs(buffer[d]), W, n - (i64)full_nodes(l - 1)};
+            a.out = recs(spare);
+            a.n_out = n - (i64)full_nodes(l);
+            a.k = k;
+            a.l0 = l - 1;
+            a.l1 = l;
+            a.dim0 = 0;
+            a.geo = geo;
+            a.s0 = level_shape(geo, l - 1);
+            a.s1 = level_shape(geo, l);
+            a.piv = piv;
+            a.piv_out = piv;
+            a.dim1 = d;
+            if (l + 1 < L) a.s2 = level_shape(geo, l + 1);
+            a.perm = perm;
+            a.tree = tree;
+            a.dimtab = dimtab;
+            a.array_dim = d;
+            a.leaf_level = l == L - 1;
+            launch.part_any(a);
+            std::swap(buffer[d], spare);
+        }
+        if (l + 1 < L) level(l + 1);
+    }
     return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
 }
 
@@ -1714,6 +1998,68 @@ kdt_status build_impl(const float* points, int64_t N, int32_t k, int32_t* perm_o
     return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
 }
 
+kdt_status build_widest_impl(const float* points, int64_t N, int32_t k, int32_t* perm_out,
+                             float* tree_out, int32_t* dims_out, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream, Timer timer) {
+    WidestLayout wl;
+    if (!valid_size(N, k) || !make_layout_widest(N, k, &wl)) return KDT_ERR_INVALID_ARG;
+    const size_t perm_bytes = (size_t)N * sizeof(int32_t);
+    const size_t tree_bytes = tree_out ? (size_t)N * k * sizeof(float) : 0;
+    const size_t dims_bytes = dims_out ? (size_t)N * sizeof(int32_t) : 0;
+    kdt_status st = validate(points, N, k, perm_out, perm_bytes, tree_out, tree_bytes, workspace,
+                             workspace_bytes, wl.base);
+    if (st != KDT_OK) return st;
+    if (dims_out && N > 0) {
+        const size_t pts_bytes = (size_t)N * k * sizeof(float);
+        if (ranges_overlap(dims_out, dims_bytes, points, pts_bytes) ||
+            ranges_overlap(dims_out, dims_bytes, perm_out, perm_bytes) ||
+            ranges_overlap(dims_out, dims_bytes, tree_out, tree_bytes) ||
+            ranges_overlap(dims_out, dims_bytes, workspace, wl.base.total))
+            return KDT_ERR_INVALID_ARG;
+    }
+    if (N == 0) return KDT_OK;
+    if (N == 1) {  // one point: its domain has no extent, so dimension 0
+        timer.begin("k_single", 4.0 + (tree_out ? 8.0 * k : 0));
+        k_single<<<1, 64, 0, stream>>>(points, k, perm_out, tree_out);
+        timer.end();
+        if (dims_out) k_zero<<<1, kBlock, 0, stream>>>(reinterpret_cast<u32*>(dims_out), 1);
+        return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
+    }
+    return run_widest(points, N, k, wl, (char*)workspace, stream, timer, perm_out, tree_out, dims_out);
+}
+
+// Runs `build` with a HIP event pair around every kernel, synchronises and
+// fills *profile.
+template <typename Build>
+kdt_status run_profiled(hipStream_t stream, kdt_profile* profile, Build build) {
+    if (!profile) return KDT_ERR_INVALID_ARG;
+    Profiler* prof = new Profiler();
+    prof->stream = stream;
+    kdt_status st = build(Timer{prof});
+    if (hipStreamSynchronize(stream) != hipSuccess && st == KDT_OK) st = KDT_ERR_HIP;
+    *profile = kdt_profile{};
+    profile->kinds = prof->kinds;
+    for (int i = 0; i < prof->kinds; ++i)
+        for (int c = 0; prof->names[i][c] && c < KDT_PROFILE_NAME_LEN - 1; ++c)
+            profile->name[i][c] = prof->names[i][c];
+    for (int i = 0; i < prof->count; ++i) {
+        Profiler::Rec& r = prof->recs[i];
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess && st == KDT_OK)
+            st = KDT_ERR_HIP;
+        profile->ms[r.kind] += ms;
+        profile->launches[r.kind] += 1;
+        profile->bytes[r.kind] += r.bytes;
+    }
+    for (int i = 0; i < prof->count; ++i) {
+        (void)hipEventDestroy(prof->recs[i].start);
+        (void)hipEventDestroy(prof->recs[i].stop);
+    }
+    if (prof->failed && st == KDT_OK) st = KDT_ERR_HIP;  // event API failure or too many kinds
+    delete prof;
+    return st;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1743,33 +2089,32 @@ kdt_status kdt_build(const float* points, int64_t N, int32_t k, int32_t* perm_ou
 kdt_status kdt_build_profiled(const float* points, int64_t N, int32_t k, int32_t* perm_out,
                               float* tree_out, void* workspace, size_t workspace_bytes,
                               hipStream_t stream, kdt_profile* profile) {
-    if (!profile) return KDT_ERR_INVALID_ARG;
-    Profiler* prof = new Profiler();
-    prof->stream = stream;
-    kdt_status st = build_impl(points, N, k, perm_out, tree_out, workspace, workspace_bytes,
-                               stream, Timer{prof});
-    if (hipStreamSynchronize(stream) != hipSuccess && st == KDT_OK) st = KDT_ERR_HIP;
-    *profile = kdt_profile{};
-    profile->kinds = prof->kinds;
-    for (int i = 0; i < prof->kinds; ++i)
-        for (int c = 0; prof->names[i][c] && c < KDT_PROFILE_NAME_LEN - 1; ++c)
-            profile->name[i][c] = prof->names[i][c];
-    for (int i = 0; i < prof->count; ++i) {
-        Profiler::Rec& r = prof->recs[i];
-        float ms = 0.f;
-        if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess && st == KDT_OK)
-            st = KDT_ERR_HIP;
-        profile->ms[r.kind] += ms;
-        profile->launches[r.kind] += 1;
-        profile->bytes[r.kind] += r.bytes;
-    }
-    for (int i = 0; i < prof->count; ++i) {
-        (void)hipEventDestroy(prof->recs[i].start);
-        (void)hipEventDestroy(prof->recs[i].stop);
-    }
-    if (prof->failed && st == KDT_OK) st = KDT_ERR_HIP;  // event API failure or too many kinds
-    delete prof;
-    return st;
+    return run_profiled(stream, profile, [&](Timer timer) {
+        return build_impl(points, N, k, perm_out, tree_out, workspace, workspace_bytes, stream, timer);
+    });
+}
+
+size_t kdt_workspace_size_widest(int64_t N, int32_t k) {
+    WidestLayout wl;
+    if (!valid_size(N, k) || !make_layout_widest(N, k, &wl)) return 0;
+    return wl.base.total;
+}
+
+kdt_status kdt_build_widest(const float* points, int64_t N, int32_t k, int32_t* perm_out,
+                            float* tree_out, int32_t* dims_out, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    return build_widest_impl(points, N, k, perm_out, tree_out, dims_out, workspace, workspace_bytes,
+                             stream, Timer{nullptr});
+}
+
+kdt_status kdt_build_widest_profiled(const float* points, int64_t N, int32_t k, int32_t* perm_out,
+                                     float* tree_out, int32_t* dims_out, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream,
+                                     kdt_profile* profile) {
+    return run_profiled(stream, profile, [&](Timer timer) {
+        return build_widest_impl(points, N, k, perm_out, tree_out, dims_out, workspace,
+                                 workspace_bytes, stream, timer);
+    });
 }
 
 kdt_status kdt_debug_tags(const float* points, int64_t N, int32_t k, int32_t rounds,

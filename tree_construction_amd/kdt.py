@@ -51,6 +51,10 @@ SIGNATURES = {
     "kdt_closed_bin_prefix": (_I64, [_I64, _I32, _I32, _I64, _I64]),
     "kdt_knn": (ctypes.c_int, [_VOIDP, _VOIDP, _I64, _I32, _VOIDP, _I64, _I32, _VOIDP, _VOIDP, _VOIDP,
                                _VOIDP]),
+    "kdt_workspace_size_widest": (_SZ, [_I64, _I32]),
+    "kdt_build_widest": (ctypes.c_int, [_VOIDP, _I64, _I32, _VOIDP, _VOIDP, _VOIDP, _VOIDP, _SZ, _VOIDP]),
+    "kdt_build_widest_profiled": (ctypes.c_int, [_VOIDP, _I64, _I32, _VOIDP, _VOIDP, _VOIDP, _VOIDP, _SZ,
+                                                 _VOIDP, ctypes.POINTER(Profile)]),
     "kdt_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -186,6 +190,69 @@ class Builder:
                                   nbytes, _stream_handle(points.device, stream))
         _check(st, "kdt_debug_tags")
         return out
+
+
+def workspace_size_widest(n: int, k: int) -> int:
+    return int(lib().kdt_workspace_size_widest(int(n), int(k)))
+
+
+class WidestBuilder:
+    """Split-widest-dimension builds of (N, k) points with a held workspace."""
+
+    def __init__(self, n: int, k: int, device="cuda"):
+        import torch
+        self.n, self.k = int(n), int(k)
+        self.device = torch.device(device)
+        nbytes = workspace_size_widest(self.n, self.k)
+        if nbytes == 0 and self.n > 1:
+            raise ValueError("unsupported size N=%d k=%d" % (self.n, self.k))
+        self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=self.device)
+        self.workspace_bytes = nbytes
+
+    def _outputs(self, points, perm, tree, dims, want_tree):
+        import torch
+        _validate_points(points)
+        if tuple(points.shape) != (self.n, self.k):
+            raise ValueError("points shape %s != (%d, %d)" % (tuple(points.shape), self.n, self.k))
+        if perm is None:
+            perm = torch.empty(self.n, dtype=torch.int32, device=points.device)
+        if tree is None and want_tree:
+            tree = torch.empty_like(points)
+        if dims is None:
+            dims = torch.empty(self.n, dtype=torch.int32, device=points.device)
+        return perm, tree, dims
+
+    def build(self, points, perm=None, tree=None, dims=None, want_tree=True, stream=None):
+        perm, tree, dims = self._outputs(points, perm, tree, dims, want_tree)
+        st = lib().kdt_build_widest(ctypes.c_void_p(points.data_ptr()), self.n, self.k,
+                                    ctypes.c_void_p(perm.data_ptr()),
+                                    ctypes.c_void_p(tree.data_ptr() if tree is not None else 0),
+                                    ctypes.c_void_p(dims.data_ptr()),
+                                    ctypes.c_void_p(self.workspace.data_ptr()), self.workspace_bytes,
+                                    _stream_handle(points.device, stream))
+        _check(st, "kdt_build_widest")
+        return perm, tree, dims
+
+    def build_profiled(self, points, perm, tree=None, dims=None, stream=None):
+        perm, tree, dims = self._outputs(points, perm, tree, dims, tree is not None)
+        prof = Profile()
+        st = lib().kdt_build_widest_profiled(ctypes.c_void_p(points.data_ptr()), self.n, self.k,
+                                             ctypes.c_void_p(perm.data_ptr()),
+                                             ctypes.c_void_p(tree.data_ptr() if tree is not None else 0),
+                                             ctypes.c_void_p(dims.data_ptr()),
+                                             ctypes.c_void_p(self.workspace.data_ptr()),
+                                             self.workspace_bytes, _stream_handle(points.device, stream),
+                                             ctypes.byref(prof))
+        _check(st, "kdt_build_widest_profiled")
+        return prof.as_dict()
+
+
+def build_widest(points, want_tree: bool = True, stream=None):
+    """Split-widest-dimension tree of `points`: (perm, tree, dims), dims[s]
+    (int32) the split dimension of node s."""
+    _validate_points(points)
+    n, k = points.shape
+    return WidestBuilder(n, k, points.device).build(points, want_tree=want_tree, stream=stream)
 
 
 def build(points, want_tree: bool = True, stream=None):
