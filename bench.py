@@ -14,6 +14,9 @@ Prints ONE JSON line on stdout (progress goes to stderr):
              8 TB/s HBM peak
   cpu_baseline  the CPU oracle on a bounded sample of the same workload
 
+With --widest it times the split-widest-dimension build of the same workload
+instead (value, roofline and cpu_baseline as above, for that variant).
+
 With --knn it instead times the K-nearest-neighbour query over the headline
 tree (the tree is built once, untimed): --knn-queries query points drawn with
 the workload's recipe, K = --knn-k; value in Mqueries/s, the roofline from the
@@ -48,14 +51,17 @@ def log(msg):
     sys.stderr.flush()
 
 
-def cpu_baseline(name, sample_n):
+def cpu_baseline(name, sample_n, widest=False):
     import oracle  # test infrastructure, used only for this reported baseline
     from tree_construction_amd import datagen
     w = datagen.WORKLOADS[name]
     pts = datagen.cached(name) if sample_n == w.n else datagen.generate(name, n=sample_n)
     oracle.load_lib()
     t0 = time.perf_counter()
-    oracle.build_tree(pts)
+    if widest:
+        oracle.build_tree_widest(pts)
+    else:
+        oracle.build_tree(pts)
     dt = time.perf_counter() - t0
     return {"value": round(sample_n / dt / 1e6, 3), "unit": "Mpoints/s",
             "cores": oracle.max_threads(), "kind": "oracle",
@@ -153,7 +159,7 @@ def kernel_short_name(name):
     return re.sub(r"\(.*", "", name).strip()
 
 
-def counter_traffic(workload, kernel):
+def counter_traffic(workload, kernel, widest=False):
     """Per-launch HBM bytes of `kernel` from two rocprofv3 counter runs of this
     benchmark (FETCH_SIZE, then WRITE_SIZE), each scaled by what the counter
     reads for a plain 256 MiB device copy. None if rocprofv3 is unavailable."""
@@ -167,7 +173,7 @@ def counter_traffic(workload, kernel):
             cmd = ["timeout", "-s", "KILL", "150", prof, "--pmc", counter, "--output-format", "csv",
                    "-d", d, "-o", "kdt", "--", sys.executable, os.path.abspath(__file__),
                    "--workload", workload, "--steps", "1", "--warmup", "1", "--no-profile",
-                   "--no-cpu-baseline", "--no-counters", "--calibration-copy"]
+                   "--no-cpu-baseline", "--no-counters", "--calibration-copy"] + (["--widest"] if widest else [])
             r = subprocess.run(cmd, stdout=subprocess.DEVNULL, stderr=subprocess.PIPE, text=True)
             files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
             if r.returncode != 0 or not files:
@@ -202,6 +208,7 @@ def main():
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event loop")
     ap.add_argument("--no-counters", action="store_true",
                     help="skip the rocprofv3 FETCH_SIZE/WRITE_SIZE runs behind roofline.traffic")
+    ap.add_argument("--widest", action="store_true", help="time the split-widest-dimension build")
     ap.add_argument("--knn", action="store_true", help="time the kNN query instead of the build")
     ap.add_argument("--knn-queries", type=int, default=1 << 20)
     ap.add_argument("--knn-k", type=int, default=8)
@@ -229,9 +236,23 @@ def main():
     dev = torch.device("cuda:0")
     x = torch.from_numpy(pts).to(dev)
     n, k = pts.shape
-    builder = kdt.Builder(n, k, dev)
     perm = torch.empty(n, dtype=torch.int32, device=dev)
     tree = torch.empty_like(x)
+    if args.widest:
+        wb = kdt.WidestBuilder(n, k, dev)
+        dims = torch.empty(n, dtype=torch.int32, device=dev)
+
+        class _Widest:  # the same two calls as kdt.Builder
+            @staticmethod
+            def build(x_, perm_, tree_):
+                return wb.build(x_, perm_, tree_, dims)
+
+            @staticmethod
+            def build_profiled(x_, perm_, tree_):
+                return wb.build_profiled(x_, perm_, tree_, dims)
+        builder = _Widest()
+    else:
+        builder = kdt.Builder(n, k, dev)
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize(dev)
 
@@ -305,7 +326,7 @@ def main():
                 % (kind, kv["launches_per_build"], kv["avg_us"], kv["GBps"], kv["ms_per_build"]))
         if not args.no_counters:
             log("bench: rocprofv3 FETCH_SIZE / WRITE_SIZE runs for %s" % dom)
-            tr = counter_traffic(name, dom)
+            tr = counter_traffic(name, dom, widest=args.widest)
             if tr:
                 total = tr["FETCH_SIZE"]["bytes"] + tr["WRITE_SIZE"]["bytes"]
                 roofline["traffic"] = int(total)
@@ -321,11 +342,12 @@ def main():
     if not args.no_cpu_baseline:
         sample = args.cpu_sample or n
         log("bench: CPU oracle baseline on %d points" % sample)
-        base = cpu_baseline(name, sample)
+        base = cpu_baseline(name, sample, widest=args.widest)
         log("  %s" % base)
 
     out = {
-        "metric": "k-d tree build Mpoints/s at N=16M k=3 fp32; achieved HBM GB/s vs peak",
+        "metric": ("k-d tree (split widest dimension) build Mpoints/s at N=16M k=3 fp32; achieved HBM GB/s vs peak"
+                   if args.widest else "k-d tree build Mpoints/s at N=16M k=3 fp32; achieved HBM GB/s vs peak"),
         "value": round(value, 2),
         "unit": "Mpoints/s",
         "n_gpus": 1,
