@@ -313,7 +313,7 @@ def main():
         # every global sort and tag-update pass: presort histograms and passes,
         # per-round re-sorts, pivot extraction
         passes = [kk for kk in kernels if kk.startswith(("k_sort_", "k_part_", "k_pivots", "k_chunk_scan",
-                                                         "k_first_digits"))]
+                                                         "k_first_digits", "k_widest_level", "k_box_"))]
         tot_b = sum(agg[kk]["bytes"] for kk in passes)
         tot_ms = sum(agg[kk]["ms"] for kk in passes)
         if tot_ms > 0:

@@ -732,7 +732,7 @@ struct PartArgs {
 // records past the end and for the pivots of levels l0 .. l1-1. The walk
 // compares (key(coordinate l mod k), index) with the pivot of the current
 // node on each level l ([W], tag paragraph: before the pivot -> left child).
-template <int kW>
+template <int kW, bool kNodeDims>
 __device__ __forceinline__ void part_nodes(const PartArgs& a,
                                            const RecordTile<kSrcRecords, kW>& tr, i64 wbase,
                                            u32 (&node)[kPartItems], bool (&valid)[kPartItems]) {
@@ -761,7 +761,8 @@ __device__ __forceinline__ void part_nodes(const PartArgs& a,
 #pragma unroll
         for (int j = 0; j < kPartItems; ++j) {
             const i64 e = wbase + (i64)j * 64;
-            const int dj = a.dimtab ? (valid[j] ? (int)a.dimtab[node[j]] : 0) : dim;
+            int dj = dim;
+            if constexpr (kNodeDims) dj = valid[j] ? (int)a.dimtab[node[j]] : 0;
             const u64 me = ((u64)tr.word(a.src, j, e, dj) << 32) | tr.word(a.src, j, e, a.src.words - 1);
             const u64 p = valid[j] ? a.piv[node[j]] : 0;
             if (me == p) valid[j] = false;  // the pivot itself: a node already
@@ -777,8 +778,8 @@ __device__ __forceinline__ void part_nodes(const PartArgs& a,
 // Digit counts of one tile of a re-sort pass. A re-sort pass has at most
 // 2^kMaxDescent digits, usually a handful, so every tile is its own chunk:
 // its count of digit d goes straight to row d of the digit-major counts.
-template <int kW>
-__global__ __launch_bounds__(kBlock) void k_part_count(PartArgs a) {
+template <int kW, bool kNodeDims>
+__device__ __forceinline__ void part_count(const PartArgs& a) {
     __shared__ u32 hist[kWaves][kRadix];
     const u32 t = xcd_tile(a.tiles);
     if (t >= a.tiles) return;
@@ -789,7 +790,7 @@ __global__ __launch_bounds__(kBlock) void k_part_count(PartArgs a) {
     tr.load(a.src, wbase);
     u32 node[kPartItems];
     bool valid[kPartItems];
-    part_nodes<kW>(a, tr, wbase, node, valid);
+    part_nodes<kW, kNodeDims>(a, tr, wbase, node, valid);
     for (int i = lane; i < bins; i += 64) hist[w][i] = 0;  // this wave's own row
     u32 last = 0, run = 0;
 #pragma unroll
@@ -813,8 +814,15 @@ __global__ __launch_bounds__(kBlock) void k_part_count(PartArgs a) {
     }
 }
 
+// Split dimension l mod k (round-robin trees) / from the node table
+// (split-widest trees).
 template <int kW>
-__global__ __launch_bounds__(kBlock) void k_part_scatter(PartArgs a) {
+__global__ __launch_bounds__(kBlock) void k_part_count(PartArgs a) { part_count<kW, false>(a); }
+template <int kW>
+__global__ __launch_bounds__(kBlock) void k_part_count_widest(PartArgs a) { part_count<kW, true>(a); }
+
+template <int kW, bool kNodeDims>
+__device__ __forceinline__ void part_scatter(const PartArgs& a) {
     __shared__ u32 count[kWaves][kRadix];  // per-wave digit counts, then first slots
     const u32 t = xcd_tile(a.tiles);
     if (t >= a.tiles) return;
@@ -826,7 +834,7 @@ __global__ __launch_bounds__(kBlock) void k_part_scatter(PartArgs a) {
     tr.load(a.src, wbase);
     u32 node[kPartItems], rank[kPartItems];
     bool valid[kPartItems];
-    part_nodes<kW>(a, tr, wbase, node, valid);
+    part_nodes<kW, kNodeDims>(a, tr, wbase, node, valid);
     for (int i = lane; i < bins; i += 64) count[w][i] = 0;
     {
         u32 digit[kPartItems];
@@ -855,8 +863,9 @@ __global__ __launch_bounds__(kBlock) void k_part_scatter(PartArgs a) {
         const i64 e = wbase + (i64)j * 64;
         if (pos < (u64)a.n_out) tr.store(a.src, a.out, j, e, pos);
         const u32 left = a.leaf_level ? 0u : subtree_size32(a.s2, 2 * node[j]);
-        if (a.piv_out && in_segment == left &&
-            (!a.dimtab || a.dimtab[full_nodes(a.l1) + node[j]] == (uint16_t)a.array_dim)) {
+        bool mine = true;  // the node splits this array's dimension
+        if constexpr (kNodeDims) mine = a.dimtab[full_nodes(a.l1) + node[j]] == (uint16_t)a.array_dim;
+        if (a.piv_out && in_segment == left && mine) {
             const u64 s = full_nodes(a.l1) + node[j];
             const u32 idx = tr.word(a.src, j, e, a.src.words - 1);
             a.piv_out[s] = ((u64)tr.word(a.src, j, e, a.dim1) << 32) | idx;
@@ -867,6 +876,11 @@ __global__ __launch_bounds__(kBlock) void k_part_scatter(PartArgs a) {
         }
     }
 }
+
+template <int kW>
+__global__ __launch_bounds__(kBlock) void k_part_scatter(PartArgs a) { part_scatter<kW, false>(a); }
+template <int kW>
+__global__ __launch_bounds__(kBlock) void k_part_scatter_widest(PartArgs a) { part_scatter<kW, true>(a); }
 
 // Round l's nodes: the pivot of node s = F(l) + j is the record at live
 // position live_begin(j) + |S(2s+1)| of the array sorted for round l
@@ -1648,6 +1662,10 @@ const char* const kPartCountNames[4] = {"k_part_count<0>", "k_part_count<2>", "k
                                         "k_part_count<4>"};
 const char* const kPartScatterNames[4] = {"k_part_scatter<0>", "k_part_scatter<2>",
                                           "k_part_scatter<3>", "k_part_scatter<4>"};
+const char* const kPartCountWidestNames[4] = {"k_part_count_widest<0>", "k_part_count_widest<2>",
+                                              "k_part_count_widest<3>", "k_part_count_widest<4>"};
+const char* const kPartScatterWidestNames[4] = {"k_part_scatter_widest<0>", "k_part_scatter_widest<2>",
+                                                "k_part_scatter_widest<3>", "k_part_scatter_widest<4>"};
 
 struct Launcher {
     u32* tile_counts;
@@ -1697,14 +1715,18 @@ struct Launcher {
         a.chunk_counts = tile_counts;  // digit-major rows of per-tile counts
         const int bins = 1 << (a.l1 - a.l0);
         const double rec = 4.0 * a.src.words;
-        timer.begin(kPartCountNames[width_slot(kW)], (double)a.src.n * rec);
-        k_part_count<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
+        const bool widest = a.dimtab != nullptr;  // split dimensions from the node table
+        timer.begin((widest ? kPartCountWidestNames : kPartCountNames)[width_slot(kW)], (double)a.src.n * rec);
+        if (widest) k_part_count_widest<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
+        else k_part_count<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
         timer.end();
         timer.begin("k_chunk_scan", (double)tiles * bins * 8);
         k_chunk_scan<<<bins, kBlock, 0, stream>>>(tile_counts, (i64)tiles, nullptr);
         timer.end();
-        timer.begin(kPartScatterNames[width_slot(kW)], (double)(a.src.n + a.n_out) * rec);
-        k_part_scatter<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
+        timer.begin((widest ? kPartScatterWidestNames : kPartScatterNames)[width_slot(kW)],
+                    (double)(a.src.n + a.n_out) * rec);
+        if (widest) k_part_scatter_widest<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
+        else k_part_scatter<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
         timer.end();
     }
     void part_any(const PartArgs& a) {
