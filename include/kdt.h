@@ -186,15 +186,27 @@ kdt_status kdt_build_widest_profiled(const float* points, int64_t N, int32_t k,
  *   d2_out    device, Q*K float32 or NULL: the matching squared distances
  *             (+inf where N < K).
  *   visits_out device, Q uint32 or NULL: the number of tree points the
- *             search of each query examined (N when K >= N).
+ *             search of each query examined (N when K >= N; a query that
+ *             the wave pass finishes counts both passes' points).
  * Coordinates of points and queries must be finite. 0 <= N, Q <= 2^31 - 1;
  * 1 <= k <= 65535. The outputs must not overlap the inputs or each other.
- * Allocates nothing; enqueued on `stream`; argument errors
- * (KDT_ERR_INVALID_ARG) are detected before anything is enqueued. */
+ * Allocates nothing; enqueued on `stream` (two kernels: one thread per
+ * query, then one wave per query whose search outgrew the first pass);
+ * argument errors (KDT_ERR_INVALID_ARG) are detected before anything is
+ * enqueued. */
 kdt_status kdt_knn(const float* tree, const int32_t* perm, int64_t N, int32_t k,
                    const float* queries, int64_t Q, int32_t K,
                    int32_t* idx_out, float* d2_out, uint32_t* visits_out,
                    hipStream_t stream);
+
+/* Diagnostic: kdt_knn with the first pass's budget given. A first-pass
+ * thread examines at most `budget` tree points before handing its query to
+ * the wave pass (kdt_knn uses max(256, 64 K)); 0 hands every query over. The results
+ * do not depend on the budget. Same arguments and errors as kdt_knn. */
+kdt_status kdt_knn_budget(const float* tree, const int32_t* perm, int64_t N, int32_t k,
+                          const float* queries, int64_t Q, int32_t K,
+                          int32_t* idx_out, float* d2_out, uint32_t* visits_out,
+                          uint32_t budget, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* kdt_status_string(kdt_status status);

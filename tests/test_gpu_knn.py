@@ -86,6 +86,28 @@ def test_knn_sizes(torch_dev, gen):
         assert_same(pts, qs, K, idx, d2, "%s N=%d k=%d K=%d" % (gen, n, k, K))
 
 
+@pytest.mark.parametrize("budget", [0, 1, 37])
+def test_knn_wave_pass(torch_dev, budget):
+    """Small first-pass budgets hand (nearly) every query to the wave pass."""
+    torch, dev = torch_dev
+    rng = np.random.default_rng(budget + 3)
+    cases = [("gmm", 30000, 3, 8), ("ties", 5000, 3, 5), ("uniform", 4097, 2, 32), ("normal", 3000, 5, 16),
+             ("zeros", 2000, 4, 3), ("equal", 700, 3, 9), ("uniform", 5, 3, 8), ("gmm", 200000, 3, 1)]
+    for gen, n, k, K in cases:
+        pts = make(gen, n, k, 70 + n % 13)
+        qs = make(gen if gen != "equal" else "uniform", 333, k, 71)
+        qs[:50] = pts[rng.integers(0, n, 50)]
+        x = torch.from_numpy(pts).to(dev)
+        perm, tree = kdt.build(x)
+        visits = torch.empty(len(qs), dtype=torch.int32, device=dev)
+        say("case knn wave budget=%d gen=%s N=%d k=%d K=%d" % (budget, gen, n, k, K))
+        idx, d2 = kdt.knn(tree, perm, torch.from_numpy(qs).to(dev), K, visits=visits, budget=budget)
+        torch.cuda.synchronize(dev)
+        assert_same(pts, qs, K, idx.cpu().numpy(), d2.cpu().numpy(), "wave budget=%d %s" % (budget, gen))
+        v = visits.cpu().numpy()
+        assert (v >= 1).all() and (v <= n + budget).all()
+
+
 def test_knn_every_k_bucket(torch_dev):
     pts = datagen.gaussian_mixture(50000, 3, 8)
     qs = datagen.gaussian_mixture(777, 3, 8)  # same centres, other draws

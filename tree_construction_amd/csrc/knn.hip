@@ -11,6 +11,15 @@
 // follows the implicit parent links (s-1)/2 instead of a stack: a thread
 // remembers only the node it came from.
 //
+// Most searches examine a few hundred points, but a few (queries in sparse
+// regions next to dense clusters) examine tens of thousands, and one thread
+// per query would leave the whole pass waiting for them. So a thread gives up
+// after a budget of points and marks the query; a second pass then runs each
+// marked query on a whole wave: the lanes pop subtrees from a shared stack in
+// LDS, each with a lower bound on its squared distance, and prune with the
+// smallest K-th distance over all lanes' lists (every lane's K-th distance
+// bounds the true K-th from above). Merging the lanes' lists gives the same K.
+//
 // Exactness. Distances are float32 squared distances summed in dimension
 // order with separately rounded products and sums, and neighbours are ranked
 // by (squared distance, original index), as the brute-force reference does.
@@ -34,7 +43,13 @@ typedef uint64_t u64;
 typedef int64_t i64;
 
 constexpr int kKnnBlock = 256;
-constexpr int kKnnMaxK = 32;  // neighbours per query at most
+constexpr int kKnnMaxK = 32;       // neighbours per query at most
+// Points one first-pass thread examines before handing its query over:
+// max(256, 64 K), a few times the 99th percentile of a typical search (the
+// work grows with K); measured best within 10 % for K = 1, 8 and 32.
+inline u32 default_budget(int K) { return K * 64u < 256u ? 256u : K * 64u; }
+constexpr int kWaveStack = 2048;   // shared stack entries of a wave's search
+constexpr int32_t kHandedOver = -2;  // first output index of a query handed to a wave
 
 struct KnnArgs {
     const float* tree;   // N x k, level order
@@ -47,6 +62,7 @@ struct KnnArgs {
     int32_t* idx_out;    // Q x K
     float* d2_out;       // Q x K or nullptr
     uint32_t* visits_out;  // Q or nullptr: nodes examined per query
+    u32 budget;          // points a first-pass thread examines before handing over
 };
 
 // The query's coordinates: kDims > 0 keeps them in registers (k == kDims);
@@ -63,15 +79,16 @@ struct Query {
             for (int d = 0; d < kDims; ++d) c[d] = row[d];
         }
     }
-    // coordinate d (uniform or not); a select chain, never an indexed array
+    // coordinate d (uniform or not), picked with bit masks so that the
+    // compiler cannot turn the choice into an indexed (scratch) array
     __device__ __forceinline__ float at(int d) const {
         if constexpr (kDims == 0) {
             return row[d];
         } else {
-            float v = c[0];
+            u32 v = 0;
 #pragma unroll
-            for (int i = 1; i < kDims; ++i) v = d == i ? c[i] : v;
-            return v;
+            for (int i = 0; i < kDims; ++i) v |= __float_as_uint(c[i]) & (d == i ? ~0u : 0u);
+            return __uint_as_float(v);
         }
     }
 };
@@ -125,6 +142,30 @@ struct Best {
     }
 };
 
+// Writes query qi's result: its K keys ascending (slot K-1 first), or the
+// hand-over mark.
+template <int kK>
+__device__ __forceinline__ void write_result(const KnnArgs& a, u64 qi, const Best<kK>& best, bool handed,
+                                             u32 visits) {
+    if (a.visits_out) a.visits_out[qi] = visits;
+    int32_t* out_idx = a.idx_out + qi * (u64)a.K;
+    if (handed) {
+        out_idx[0] = kHandedOver;
+        return;
+    }
+    float* out_d2 = a.d2_out ? a.d2_out + qi * (u64)a.K : nullptr;
+#pragma unroll
+    for (int i = 0; i < kK; ++i) {
+        if (i >= a.K) continue;
+        const u64 key = best.slot[i];
+        const int at = a.K - 1 - i;
+        const bool empty = key == ~0ull;
+        out_idx[at] = empty ? -1 : (int32_t)(u32)key;
+        if (out_d2) out_d2[at] = empty ? __uint_as_float(0x7f800000u) : __uint_as_float((u32)(key >> 32));
+    }
+}
+
+// First pass: one thread per query.
 template <int kK, int kDims>
 __global__ __launch_bounds__(kKnnBlock) void k_knn(KnnArgs a) {
     const u64 qi = (u64)blockIdx.x * kKnnBlock + threadIdx.x;
@@ -136,6 +177,7 @@ __global__ __launch_bounds__(kKnnBlock) void k_knn(KnnArgs a) {
     const u32 n = (u32)a.n;
     const int k = kDims > 0 ? kDims : a.k;
     u32 visits = 0;
+    bool handed = false;
     if (n > 0) {
         // prev: the node the thread arrived from (~0 = from above the root)
         u32 curr = 0, prev = ~0u;
@@ -157,6 +199,10 @@ __global__ __launch_bounds__(kKnnBlock) void k_knn(KnnArgs a) {
             if (prev == parent) {
                 // first visit: the node's point is a candidate; go to the
                 // query's side first
+                if (visits == a.budget) {
+                    handed = true;
+                    break;
+                }
                 ++visits;
                 const u32 bits = __float_as_uint(squared_distance<kDims>(q, node, k));
                 if (bits <= best.worst_bits()) {
@@ -180,29 +226,209 @@ __global__ __launch_bounds__(kKnnBlock) void k_knn(KnnArgs a) {
             dim = dim == 0 ? k - 1 : dim - 1;
         }
     }
-    if (a.visits_out) a.visits_out[qi] = visits;
-    // ascending output: slot K-1 first
-    int32_t* out_idx = a.idx_out + qi * (u64)a.K;
-    float* out_d2 = a.d2_out ? a.d2_out + qi * (u64)a.K : nullptr;
+    write_result<kK>(a, qi, best, handed, visits);
+}
+
+__device__ __forceinline__ u32 wave_sum(u32 v) {
 #pragma unroll
-    for (int i = 0; i < kK; ++i) {
-        if (i >= a.K) continue;
-        const u64 key = best.slot[i];
-        const int at = a.K - 1 - i;
-        const bool empty = key == ~0ull;
-        out_idx[at] = empty ? -1 : (int32_t)(u32)key;
-        if (out_d2) out_d2[at] = empty ? __uint_as_float(0x7f800000u) : __uint_as_float((u32)(key >> 32));
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ u32 wave_min32(u32 v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const u32 w = __shfl_xor(v, o, 64);
+        v = w < v ? w : v;
+    }
+    return v;
+}
+__device__ __forceinline__ u64 wave_min64(u64 v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const u64 w = __shfl_xor(v, o, 64);
+        v = w < v ? w : v;
+    }
+    return v;
+}
+
+__device__ __forceinline__ int level_of32(u32 i) { return 31 - __clz(i + 1); }
+
+// The whole subtree of node c, by one lane, with the parent-link walk of the
+// first pass (it ends when it climbs back out of c); radius: the wave's
+// smallest K-th distance when the lane started.
+template <int kK, int kDims>
+__device__ __forceinline__ void lane_subtree(const KnnArgs& a, const Query<kDims>& q, Best<kK>& best, u32 c, u32 radius,
+                             int k, u32& examined) {
+    const u32 n = (u32)a.n;
+    u32 curr = c, prev = c == 0 ? ~0u : (c - 1) >> 1;
+    int dim = level_of32(c) % k;
+    for (;;) {
+        const u32 worst = best.worst_bits() < radius ? best.worst_bits() : radius;
+        if (curr >= n) {
+            prev = curr;
+            curr = (curr - 1) >> 1;
+            dim = dim == 0 ? k - 1 : dim - 1;
+            continue;
+        }
+        const u32 parent = curr == 0 ? ~0u : (curr - 1) >> 1;
+        const float* node = a.tree + (u64)curr * (u64)k;
+        const float diff = q.at(dim) - node[dim];
+        const u32 left = 2 * curr + 1;
+        const u32 near = diff < 0.0f ? left : left + 1;
+        const u32 far = diff < 0.0f ? left + 1 : left;
+        const int down = dim + 1 == k ? 0 : dim + 1;
+        if (prev == parent) {
+            ++examined;
+            const u32 bits = __float_as_uint(squared_distance<kDims>(q, node, k));
+            if (bits <= worst) {
+                const u64 key = ((u64)bits << 32) | (u32)a.perm[curr];
+                if (key < best.slot[0]) best.insert(key);
+            }
+            prev = curr;
+            curr = near;
+            dim = down;
+            continue;
+        }
+        if (prev == near && far < n && __float_as_uint(diff * diff) <= worst) {
+            prev = curr;
+            curr = far;
+            dim = down;
+            continue;
+        }
+        if (curr == c) break;
+        prev = curr;
+        curr = parent;
+        dim = dim == 0 ? k - 1 : dim - 1;
+    }
+}
+
+// Second pass: every query the first pass handed over, searched by one
+// 64-lane workgroup. Workgroup w owns queries [64w, 64w + 64).
+template <int kK, int kDims>
+__global__ __launch_bounds__(64) void k_knn_wave(KnnArgs a) {
+    __shared__ u64 stack[kWaveStack];  // (lower bound bits << 32) | node
+    const int lane = threadIdx.x;
+    const u64 base = (u64)blockIdx.x * 64;
+    const u64 me = base + lane;
+    const bool marked = me < (u64)a.q && a.idx_out[me * (u64)a.K] == kHandedOver;
+    u64 todo = __ballot(marked);
+    const u32 n = (u32)a.n;
+    const int k = kDims > 0 ? kDims : a.k;
+    while (todo) {
+        const int owner = __ffsll((long long)todo) - 1;
+        todo &= todo - 1;
+        const u64 qi = base + owner;
+        Query<kDims> q;
+        q.load(a.queries, qi, a.k);
+        Best<kK> best;
+        best.init(a.K);
+        u32 examined = 0, top = 1, radius = ~0u;
+        if (lane == 0) stack[0] = 0;  // the root, bound 0
+        __syncthreads();
+        while (top > 0) {
+            const u32 take = top < 64 ? top : 64;
+            const bool have = (u32)lane < take;
+            u64 entry = 0;
+            if (have) entry = stack[top - 1 - lane];
+            top -= take;
+            __syncthreads();  // every pop read before pushes overwrite
+            const u32 node = (u32)entry, bound = (u32)(entry >> 32);
+            u64 push0 = 0, push1 = 0;  // (two scalars: an indexed pair would live in scratch)
+            u32 npush = 0;
+            if (have && bound <= radius && node < n) {
+                ++examined;
+                const int dim = level_of32(node) % k;
+                const float* row = a.tree + (u64)node * (u64)k;
+                const u32 bits = __float_as_uint(squared_distance<kDims>(q, row, k));
+                const u32 worst0 = best.worst_bits() < radius ? best.worst_bits() : radius;
+                if (bits <= worst0) {
+                    const u64 key = ((u64)bits << 32) | (u32)a.perm[node];
+                    if (key < best.slot[0]) best.insert(key);
+                }
+                const u32 worst = best.worst_bits() < radius ? best.worst_bits() : radius;
+                const float diff = q.at(dim) - row[dim];
+                const u32 left = 2 * node + 1;
+                const u32 near = diff < 0.0f ? left : left + 1;
+                const u32 far = diff < 0.0f ? left + 1 : left;
+                const u32 db = __float_as_uint(diff * diff);
+                const u32 far_bound = db > bound ? db : bound;
+                // far first, near on top: the near side is popped first
+                if (far < n && far_bound <= worst) {
+                    push0 = ((u64)far_bound << 32) | far;
+                    npush = 1;
+                }
+                if (near < n && bound <= worst) {
+                    const u64 v = ((u64)bound << 32) | near;
+                    if (npush == 0) push0 = v;
+                    else push1 = v;
+                    ++npush;
+                }
+            }
+            // stack slots of this lane's pushes: a wave prefix sum
+            u32 incl = npush;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const u32 t = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += t;
+            }
+            const u32 total = __shfl(incl, 63, 64);
+            if (top + total <= (u32)kWaveStack) {
+                const u32 at = top + incl - npush;
+                if (npush > 0) stack[at] = push0;
+                if (npush > 1) stack[at + 1] = push1;
+                top += total;
+            } else {
+                // no room: each lane searches its own children itself
+                if (npush > 0) lane_subtree<kK, kDims>(a, q, best, (u32)push0, radius, k, examined);
+                if (npush > 1) lane_subtree<kK, kDims>(a, q, best, (u32)push1, radius, k, examined);
+            }
+            __syncthreads();
+            radius = wave_min32(best.worst_bits());
+        }
+        // merge: K rounds, each taking the smallest remaining key of all lanes
+        int pos = a.K - 1;  // this lane's next key: slot[pos] (slots descend)
+        int32_t* out_idx = a.idx_out + qi * (u64)a.K;
+        float* out_d2 = a.d2_out ? a.d2_out + qi * (u64)a.K : nullptr;
+        for (int r = 0; r < a.K; ++r) {
+            u64 cand = ~0ull;
+#pragma unroll
+            for (int i = 0; i < kK; ++i)
+                if (i == pos) cand = best.slot[i];
+            const u64 m = wave_min64(cand);
+            if (cand == m && m != ~0ull) --pos;  // keys are distinct: one lane holds m
+            if (lane == 0) {
+                const bool empty = m == ~0ull;
+                out_idx[r] = empty ? -1 : (int32_t)(u32)m;
+                if (out_d2) out_d2[r] = empty ? __uint_as_float(0x7f800000u) : __uint_as_float((u32)(m >> 32));
+            }
+        }
+        const u32 all = wave_sum(examined);
+        if (lane == 0 && a.visits_out) a.visits_out[qi] += all;
+        __syncthreads();
     }
 }
 
 template <int kK>
 void launch_knn(const KnnArgs& a, hipStream_t stream) {
     const unsigned grid = (unsigned)((a.q + kKnnBlock - 1) / kKnnBlock);
+    const unsigned waves = (unsigned)((a.q + 63) / 64);
     switch (a.k) {
-        case 2: k_knn<kK, 2><<<grid, kKnnBlock, 0, stream>>>(a); break;
-        case 3: k_knn<kK, 3><<<grid, kKnnBlock, 0, stream>>>(a); break;
-        case 4: k_knn<kK, 4><<<grid, kKnnBlock, 0, stream>>>(a); break;
-        default: k_knn<kK, 0><<<grid, kKnnBlock, 0, stream>>>(a); break;
+        case 2:
+            k_knn<kK, 2><<<grid, kKnnBlock, 0, stream>>>(a);
+            k_knn_wave<kK, 2><<<waves, 64, 0, stream>>>(a);
+            break;
+        case 3:
+            k_knn<kK, 3><<<grid, kKnnBlock, 0, stream>>>(a);
+            k_knn_wave<kK, 3><<<waves, 64, 0, stream>>>(a);
+            break;
+        case 4:
+            k_knn<kK, 4><<<grid, kKnnBlock, 0, stream>>>(a);
+            k_knn_wave<kK, 4><<<waves, 64, 0, stream>>>(a);
+            break;
+        default:
+            k_knn<kK, 0><<<grid, kKnnBlock, 0, stream>>>(a);
+            k_knn_wave<kK, 0><<<waves, 64, 0, stream>>>(a);
+            break;
     }
 }
 
@@ -212,11 +438,9 @@ bool overlap(const void* a, size_t an, const void* b, size_t bn) {
     return x < y + bn && y < x + an;
 }
 
-}  // namespace
-
-extern "C" kdt_status kdt_knn(const float* tree, const int32_t* perm, int64_t N, int32_t k,
-                              const float* queries, int64_t Q, int32_t K, int32_t* idx_out,
-                              float* d2_out, uint32_t* visits_out, hipStream_t stream) {
+kdt_status knn_impl(const float* tree, const int32_t* perm, int64_t N, int32_t k,
+                    const float* queries, int64_t Q, int32_t K, int32_t* idx_out, float* d2_out,
+                    uint32_t* visits_out, uint32_t budget, hipStream_t stream) {
     if (N < 0 || N > INT32_MAX || k < 1 || k > 65535 || Q < 0 || Q > INT32_MAX || K < 1 ||
         K > kKnnMaxK)
         return KDT_ERR_INVALID_ARG;
@@ -235,7 +459,7 @@ extern "C" kdt_status kdt_knn(const float* tree, const int32_t* perm, int64_t N,
     if (overlap(idx_out, out_b, d2_out, out_b) || overlap(visits_out, v_b, idx_out, out_b) ||
         overlap(visits_out, v_b, d2_out, out_b))
         return KDT_ERR_INVALID_ARG;
-    KnnArgs a{tree, perm, N, k, queries, Q, K, idx_out, d2_out, visits_out};
+    KnnArgs a{tree, perm, N, k, queries, Q, K, idx_out, d2_out, visits_out, budget};
     if (K <= 1) launch_knn<1>(a, stream);
     else if (K <= 2) launch_knn<2>(a, stream);
     else if (K <= 4) launch_knn<4>(a, stream);
@@ -243,4 +467,20 @@ extern "C" kdt_status kdt_knn(const float* tree, const int32_t* perm, int64_t N,
     else if (K <= 16) launch_knn<16>(a, stream);
     else launch_knn<32>(a, stream);
     return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" kdt_status kdt_knn(const float* tree, const int32_t* perm, int64_t N, int32_t k,
+                              const float* queries, int64_t Q, int32_t K, int32_t* idx_out,
+                              float* d2_out, uint32_t* visits_out, hipStream_t stream) {
+    return knn_impl(tree, perm, N, k, queries, Q, K, idx_out, d2_out, visits_out, default_budget(K),
+                    stream);
+}
+
+extern "C" kdt_status kdt_knn_budget(const float* tree, const int32_t* perm, int64_t N, int32_t k,
+                                     const float* queries, int64_t Q, int32_t K, int32_t* idx_out,
+                                     float* d2_out, uint32_t* visits_out, uint32_t budget,
+                                     hipStream_t stream) {
+    return knn_impl(tree, perm, N, k, queries, Q, K, idx_out, d2_out, visits_out, budget, stream);
 }

@@ -51,6 +51,8 @@ SIGNATURES = {
     "kdt_closed_bin_prefix": (_I64, [_I64, _I32, _I32, _I64, _I64]),
     "kdt_knn": (ctypes.c_int, [_VOIDP, _VOIDP, _I64, _I32, _VOIDP, _I64, _I32, _VOIDP, _VOIDP, _VOIDP,
                                _VOIDP]),
+    "kdt_knn_budget": (ctypes.c_int, [_VOIDP, _VOIDP, _I64, _I32, _VOIDP, _I64, _I32, _VOIDP, _VOIDP,
+                                      _VOIDP, ctypes.c_uint32, _VOIDP]),
     "kdt_workspace_size_widest": (_SZ, [_I64, _I32]),
     "kdt_build_widest": (ctypes.c_int, [_VOIDP, _I64, _I32, _VOIDP, _VOIDP, _VOIDP, _VOIDP, _SZ, _VOIDP]),
     "kdt_build_widest_profiled": (ctypes.c_int, [_VOIDP, _I64, _I32, _VOIDP, _VOIDP, _VOIDP, _VOIDP, _SZ,
@@ -265,14 +267,16 @@ def build(points, want_tree: bool = True, stream=None):
     return Builder(n, k, points.device).build(points, want_tree=want_tree, stream=stream)
 
 
-def knn(tree, perm, queries, K: int, idx=None, d2=None, visits=None, stream=None):
+def knn(tree, perm, queries, K: int, idx=None, d2=None, visits=None, stream=None, budget=None):
     """K nearest neighbours of every query among the points of a built tree.
 
     tree, perm: the outputs of build() ((N, k) float32 and (N,) int32 on a
     HIP device); queries: (Q, k) float32 on the same device. Returns (idx, d2):
     (Q, K) int32 original indices, nearest first (-1 past N), and their
     (Q, K) float32 squared distances. A (Q,) int32 tensor passed as `visits`
-    receives the number of tree points each search examined."""
+    receives the number of tree points each search examined. `budget`
+    (diagnostic) sets how many points a first-pass thread examines before
+    handing its query to the wave pass."""
     import torch
     _validate_points(queries)
     if tree is not None:
@@ -288,11 +292,13 @@ def knn(tree, perm, queries, K: int, idx=None, d2=None, visits=None, stream=None
         idx = torch.empty((q, K), dtype=torch.int32, device=queries.device)
     if d2 is None:
         d2 = torch.empty((q, K), dtype=torch.float32, device=queries.device)
-    st = lib().kdt_knn(ctypes.c_void_p(tree.data_ptr() if n else 0),
-                       ctypes.c_void_p(perm.data_ptr() if n else 0), n, k,
-                       ctypes.c_void_p(queries.data_ptr()), q, int(K),
-                       ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(d2.data_ptr()),
-                       ctypes.c_void_p(visits.data_ptr() if visits is not None else 0),
-                       _stream_handle(queries.device, stream))
+    args = [ctypes.c_void_p(tree.data_ptr() if n else 0), ctypes.c_void_p(perm.data_ptr() if n else 0), n, k,
+            ctypes.c_void_p(queries.data_ptr()), q, int(K),
+            ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(d2.data_ptr()),
+            ctypes.c_void_p(visits.data_ptr() if visits is not None else 0)]
+    if budget is None:
+        st = lib().kdt_knn(*args, _stream_handle(queries.device, stream))
+    else:
+        st = lib().kdt_knn_budget(*args, int(budget), _stream_handle(queries.device, stream))
     _check(st, "kdt_knn")
     return idx, d2
