@@ -91,25 +91,29 @@ def run_knn(args):
     q = torch.from_numpy(qs).to(dev)
     n, k = pts.shape
     Q, K = len(qs), args.knn_k
-    log("bench: building the %s tree (untimed)" % name)
-    perm, tree = kdt.build(x)
+    log("bench: building the %s tree (untimed)%s" % (name, ", split widest dimension" if args.widest else ""))
+    dims = None
+    if args.widest:
+        perm, tree, dims = kdt.build_widest(x)
+    else:
+        perm, tree = kdt.build(x)
     idx = torch.empty((Q, K), dtype=torch.int32, device=dev)
     d2 = torch.empty((Q, K), dtype=torch.float32, device=dev)
     visits = torch.empty(Q, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    kdt.knn(tree, perm, q, K, idx, d2, visits)
+    kdt.knn(tree, perm, q, K, idx, d2, visits, dims=dims)
     torch.cuda.synchronize(dev)
     v = visits.cpu().numpy()
     examined = float(v.astype(np.float64).sum())
     for _ in range(args.warmup):
-        kdt.knn(tree, perm, q, K, idx, d2)
+        kdt.knn(tree, perm, q, K, idx, d2, dims=dims)
 
     def timed(qq):
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize(dev)
         start.record(stream)
         for _ in range(args.steps):
-            kdt.knn(tree, perm, qq, K)
+            kdt.knn(tree, perm, qq, K, dims=dims)
         stop.record(stream)
         torch.cuda.synchronize(dev)
         return start.elapsed_time(stop) / args.steps
@@ -136,13 +140,15 @@ def run_knn(args):
     if base:
         log("  %s" % base)
     out = {
-        "metric": "k-d tree kNN queries (K=%d) per second over the N=16M k=3 tree" % K,
+        "metric": "k-d tree kNN queries (K=%d) per second over the N=16M k=3 %stree" % (
+            K, "split-widest " if args.widest else ""),
         "value": round(Q / ms / 1e3, 3),
         "unit": "Mqueries/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "knn over %s" % name, "n_points": n, "k": k, "queries": Q, "K": K,
+        "config": {"workload": "knn over %s%s" % (name, " (split-widest tree)" if args.widest else ""),
+                   "n_points": n, "k": k, "queries": Q, "K": K,
                    "queries_from": "the workload's recipe and seed, %d further draws" % Q},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "k_knn",

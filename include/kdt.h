@@ -170,8 +170,8 @@ kdt_status kdt_build_widest_profiled(const float* points, int64_t N, int32_t k,
                                      hipStream_t stream, kdt_profile* profile);
 
 /* K nearest neighbours of each query point among the N points of a tree
- * built by kdt_build (round-robin split dimensions), exactly as a brute-force
- * search ranks them. The search is the two-phase descent and backtrack of
+ * built by kdt_build or kdt_build_widest, exactly as a brute-force search
+ * ranks them. The search is the two-phase descent and backtrack of
  * F. Gieseke et al., "Bigger Buffer k-d Trees on Multi-Many-Core Systems"
  * (arXiv 1512.02831), section 2.3, over the left-balanced level-order tree.
  * Distances are float32 squared Euclidean distances, summed in dimension
@@ -179,6 +179,9 @@ kdt_status kdt_build_widest_profiled(const float* points, int64_t N, int32_t k,
  * by (squared distance, original index).
  *   tree      device, N*k float32: the tree_out of kdt_build (level order).
  *   perm      device, N int32: the perm_out of the same build.
+ *   dims      device, N int32 or NULL: the dims_out of kdt_build_widest
+ *             (each node's split dimension); NULL for a kdt_build tree
+ *             (node s splits dimension level(s) mod k).
  *   queries   device, Q*k float32, row-major. Read only.
  *   K         neighbours per query, 1 <= K <= 32.
  *   idx_out   device, Q*K int32: row q holds the original indices of query
@@ -194,8 +197,8 @@ kdt_status kdt_build_widest_profiled(const float* points, int64_t N, int32_t k,
  * query, then one wave per query whose search outgrew the first pass);
  * argument errors (KDT_ERR_INVALID_ARG) are detected before anything is
  * enqueued. */
-kdt_status kdt_knn(const float* tree, const int32_t* perm, int64_t N, int32_t k,
-                   const float* queries, int64_t Q, int32_t K,
+kdt_status kdt_knn(const float* tree, const int32_t* perm, const int32_t* dims,
+                   int64_t N, int32_t k, const float* queries, int64_t Q, int32_t K,
                    int32_t* idx_out, float* d2_out, uint32_t* visits_out,
                    hipStream_t stream);
 
@@ -203,8 +206,8 @@ kdt_status kdt_knn(const float* tree, const int32_t* perm, int64_t N, int32_t k,
  * thread examines at most `budget` tree points before handing its query to
  * the wave pass (kdt_knn uses max(256, 64 K)); 0 hands every query over. The results
  * do not depend on the budget. Same arguments and errors as kdt_knn. */
-kdt_status kdt_knn_budget(const float* tree, const int32_t* perm, int64_t N, int32_t k,
-                          const float* queries, int64_t Q, int32_t K,
+kdt_status kdt_knn_budget(const float* tree, const int32_t* perm, const int32_t* dims,
+                          int64_t N, int32_t k, const float* queries, int64_t Q, int32_t K,
                           int32_t* idx_out, float* d2_out, uint32_t* visits_out,
                           uint32_t budget, hipStream_t stream);
 

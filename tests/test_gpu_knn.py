@@ -108,6 +108,24 @@ def test_knn_wave_pass(torch_dev, budget):
         assert (v >= 1).all() and (v <= n + budget).all()
 
 
+@pytest.mark.parametrize("budget", [None, 0])
+def test_knn_split_widest_tree(torch_dev, budget):
+    """Over a split-widest tree (per-node dimensions) the answers are the same
+    brute-force ones."""
+    torch, dev = torch_dev
+    for gen, n, k, K in [("gmm", 40000, 3, 8), ("ties", 3000, 2, 5), ("uniform", 4097, 4, 32),
+                         ("normal", 2500, 5, 3), ("zeros", 1000, 3, 7)]:
+        pts = make(gen, n, k, 500 + n % 7)
+        qs = make(gen, 300, k, 501)
+        qs[:30] = pts[:30]
+        x = torch.from_numpy(pts).to(dev)
+        perm, tree, dims = kdt.build_widest(x)
+        say("case knn widest budget=%s gen=%s N=%d k=%d K=%d" % (budget, gen, n, k, K))
+        idx, d2 = kdt.knn(tree, perm, torch.from_numpy(qs).to(dev), K, dims=dims, budget=budget)
+        torch.cuda.synchronize(dev)
+        assert_same(pts, qs, K, idx.cpu().numpy(), d2.cpu().numpy(), "widest %s" % gen)
+
+
 def test_knn_every_k_bucket(torch_dev):
     pts = datagen.gaussian_mixture(50000, 3, 8)
     qs = datagen.gaussian_mixture(777, 3, 8)  # same centres, other draws

@@ -161,20 +161,21 @@ def test_build_rejects_bad_arguments_before_launch(args, code):
     assert kdt.lib().kdt_build(*args) == code
 
 
-# kdt_knn(tree, perm, N, k, queries, Q, K, idx_out, d2_out, visits_out, stream)
+# kdt_knn(tree, perm, dims, N, k, queries, Q, K, idx_out, d2_out, visits_out, stream)
 @pytest.mark.parametrize("args,code", [
-    ((FAKE, FAKE + 2**30, 10, 3, FAKE + 2**31, 5, 0, FAKE + 2**32, 0, 0, None), 1),   # K = 0
-    ((FAKE, FAKE + 2**30, 10, 3, FAKE + 2**31, 5, 33, FAKE + 2**32, 0, 0, None), 1),  # K > 32
-    ((FAKE, FAKE + 2**30, -1, 3, FAKE + 2**31, 5, 4, FAKE + 2**32, 0, 0, None), 1),   # N < 0
-    ((FAKE, FAKE + 2**30, 10, 0, FAKE + 2**31, 5, 4, FAKE + 2**32, 0, 0, None), 1),   # k = 0
-    ((FAKE, FAKE + 2**30, 10, 3, FAKE + 2**31, -2, 4, FAKE + 2**32, 0, 0, None), 1),  # Q < 0
-    ((FAKE, FAKE + 2**30, 10, 3, 0, 5, 4, FAKE + 2**32, 0, 0, None), 1),              # queries NULL
-    ((FAKE, FAKE + 2**30, 10, 3, FAKE + 2**31, 5, 4, 0, 0, 0, None), 1),              # idx_out NULL
-    ((0, FAKE + 2**30, 10, 3, FAKE + 2**31, 5, 4, FAKE + 2**32, 0, 0, None), 1),      # tree NULL
-    ((FAKE, FAKE + 2**30, 10, 3, FAKE + 2**31, 5, 4, FAKE + 2**31 + 8, 0, 0, None), 1),  # idx on queries
-    ((FAKE, FAKE + 2**30, 10, 3, FAKE + 2**31, 5, 4, FAKE + 2**32, FAKE + 2**32 + 4, 0, None), 1),  # d2 on idx
-    ((FAKE, FAKE + 2**30, 10, 3, FAKE + 2**31, 5, 4, FAKE + 2**32, 0, FAKE + 4, None), 1),  # visits on tree
-    ((FAKE, FAKE + 2**30, 10, 3, FAKE + 2**31, 0, 4, FAKE + 2**32, 0, 0, None), 0),   # Q = 0: nothing
+    ((FAKE, FAKE + 2**30, 0, 10, 3, FAKE + 2**31, 5, 0, FAKE + 2**32, 0, 0, None), 1),   # K = 0
+    ((FAKE, FAKE + 2**30, 0, 10, 3, FAKE + 2**31, 5, 33, FAKE + 2**32, 0, 0, None), 1),  # K > 32
+    ((FAKE, FAKE + 2**30, 0, -1, 3, FAKE + 2**31, 5, 4, FAKE + 2**32, 0, 0, None), 1),   # N < 0
+    ((FAKE, FAKE + 2**30, 0, 10, 0, FAKE + 2**31, 5, 4, FAKE + 2**32, 0, 0, None), 1),   # k = 0
+    ((FAKE, FAKE + 2**30, 0, 10, 3, FAKE + 2**31, -2, 4, FAKE + 2**32, 0, 0, None), 1),  # Q < 0
+    ((FAKE, FAKE + 2**30, 0, 10, 3, 0, 5, 4, FAKE + 2**32, 0, 0, None), 1),              # queries NULL
+    ((FAKE, FAKE + 2**30, 0, 10, 3, FAKE + 2**31, 5, 4, 0, 0, 0, None), 1),              # idx_out NULL
+    ((0, FAKE + 2**30, 0, 10, 3, FAKE + 2**31, 5, 4, FAKE + 2**32, 0, 0, None), 1),      # tree NULL
+    ((FAKE, FAKE + 2**30, 0, 10, 3, FAKE + 2**31, 5, 4, FAKE + 2**31 + 8, 0, 0, None), 1),  # idx on queries
+    ((FAKE, FAKE + 2**30, 0, 10, 3, FAKE + 2**31, 5, 4, FAKE + 2**32, FAKE + 2**32 + 4, 0, None), 1),  # d2 on idx
+    ((FAKE, FAKE + 2**30, 0, 10, 3, FAKE + 2**31, 5, 4, FAKE + 2**32, 0, FAKE + 4, None), 1),  # visits on tree
+    ((FAKE, FAKE + 2**30, 0, 10, 3, FAKE + 2**31, 0, 4, FAKE + 2**32, 0, 0, None), 0),   # Q = 0: nothing
+    ((FAKE, FAKE + 2**30, FAKE + 2**33, 10, 3, FAKE + 2**31, 5, 4, FAKE + 2**33 + 8, 0, 0, None), 1),  # idx on dims
 ])
 def test_knn_rejects_bad_arguments_before_launch(args, code):
     assert kdt.lib().kdt_knn(*args) == code

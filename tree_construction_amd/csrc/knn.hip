@@ -54,6 +54,7 @@ constexpr int32_t kHandedOver = -2;  // first output index of a query handed to 
 struct KnnArgs {
     const float* tree;   // N x k, level order
     const int32_t* perm; // N: original index of each node's point
+    const int32_t* dims; // N split dimensions (split-widest trees) or nullptr: level mod k
     i64 n;
     int k;
     const float* queries;  // Q x k
@@ -93,22 +94,47 @@ struct Query {
     }
 };
 
+// A node's point as the search needs it: the coordinate in its split
+// dimension and (for the distance) the row. With k <= 4 the whole row is
+// loaded together with the node's dimension, so neither load waits for the
+// other; picking the split coordinate is then register work.
 template <int kDims>
-__device__ __forceinline__ float squared_distance(const Query<kDims>& q, const float* node, int k) {
+struct NodeRow {
+    float p[kDims > 0 ? kDims : 1];
+    const float* row;
+
+    __device__ __forceinline__ void load(const float* tree, u32 node, int k) {
+        row = tree + (u64)node * (u64)k;
+        if constexpr (kDims > 0) {
+#pragma unroll
+            for (int d = 0; d < kDims; ++d) p[d] = row[d];
+        }
+    }
+    __device__ __forceinline__ float at(int d) const {
+        if constexpr (kDims == 0) {
+            return row[d];
+        } else {
+            u32 v = 0;
+#pragma unroll
+            for (int i = 0; i < kDims; ++i) v |= __float_as_uint(p[i]) & (d == i ? ~0u : 0u);
+            return __uint_as_float(v);
+        }
+    }
+};
+
+template <int kDims>
+__device__ __forceinline__ float squared_distance(const Query<kDims>& q, const NodeRow<kDims>& node, int k) {
 #pragma clang fp contract(off)
     float acc = 0.0f;  // 0 + t0*t0 is t0*t0 exactly
     if constexpr (kDims > 0) {
-        float p[kDims];
-#pragma unroll
-        for (int d = 0; d < kDims; ++d) p[d] = node[d];
 #pragma unroll
         for (int d = 0; d < kDims; ++d) {
-            const float t = q.c[d] - p[d];
+            const float t = q.c[d] - node.p[d];
             acc = acc + t * t;
         }
     } else {
         for (int d = 0; d < k; ++d) {
-            const float t = q.row[d] - node[d];
+            const float t = q.row[d] - node.row[d];
             acc = acc + t * t;
         }
     }
@@ -190,8 +216,10 @@ __global__ __launch_bounds__(kKnnBlock) void k_knn(KnnArgs a) {
                 continue;
             }
             const u32 parent = curr == 0 ? ~0u : (curr - 1) >> 1;
-            const float* node = a.tree + (u64)curr * (u64)k;
-            const float diff = q.at(dim) - node[dim];
+            NodeRow<kDims> node;
+            node.load(a.tree, curr, k);
+            const int split = a.dims ? a.dims[curr] : dim;
+            const float diff = q.at(split) - node.at(split);
             const u32 left = 2 * curr + 1;
             const u32 near = diff < 0.0f ? left : left + 1;
             const u32 far = diff < 0.0f ? left + 1 : left;
@@ -271,8 +299,10 @@ __device__ __forceinline__ void lane_subtree(const KnnArgs& a, const Query<kDims
             continue;
         }
         const u32 parent = curr == 0 ? ~0u : (curr - 1) >> 1;
-        const float* node = a.tree + (u64)curr * (u64)k;
-        const float diff = q.at(dim) - node[dim];
+        NodeRow<kDims> node;
+        node.load(a.tree, curr, k);
+        const int split = a.dims ? a.dims[curr] : dim;
+        const float diff = q.at(split) - node.at(split);
         const u32 left = 2 * curr + 1;
         const u32 near = diff < 0.0f ? left : left + 1;
         const u32 far = diff < 0.0f ? left + 1 : left;
@@ -337,8 +367,9 @@ __global__ __launch_bounds__(64) void k_knn_wave(KnnArgs a) {
             u32 npush = 0;
             if (have && bound <= radius && node < n) {
                 ++examined;
-                const int dim = level_of32(node) % k;
-                const float* row = a.tree + (u64)node * (u64)k;
+                NodeRow<kDims> row;
+                row.load(a.tree, node, k);
+                const int dim = a.dims ? a.dims[node] : level_of32(node) % k;
                 const u32 bits = __float_as_uint(squared_distance<kDims>(q, row, k));
                 const u32 worst0 = best.worst_bits() < radius ? best.worst_bits() : radius;
                 if (bits <= worst0) {
@@ -346,7 +377,7 @@ __global__ __launch_bounds__(64) void k_knn_wave(KnnArgs a) {
                     if (key < best.slot[0]) best.insert(key);
                 }
                 const u32 worst = best.worst_bits() < radius ? best.worst_bits() : radius;
-                const float diff = q.at(dim) - row[dim];
+                const float diff = q.at(dim) - row.at(dim);
                 const u32 left = 2 * node + 1;
                 const u32 near = diff < 0.0f ? left : left + 1;
                 const u32 far = diff < 0.0f ? left + 1 : left;
@@ -438,7 +469,7 @@ bool overlap(const void* a, size_t an, const void* b, size_t bn) {
     return x < y + bn && y < x + an;
 }
 
-kdt_status knn_impl(const float* tree, const int32_t* perm, int64_t N, int32_t k,
+kdt_status knn_impl(const float* tree, const int32_t* perm, const int32_t* dims, int64_t N, int32_t k,
                     const float* queries, int64_t Q, int32_t K, int32_t* idx_out, float* d2_out,
                     uint32_t* visits_out, uint32_t budget, hipStream_t stream) {
     if (N < 0 || N > INT32_MAX || k < 1 || k > 65535 || Q < 0 || Q > INT32_MAX || K < 1 ||
@@ -448,18 +479,18 @@ kdt_status knn_impl(const float* tree, const int32_t* perm, int64_t N, int32_t k
     if (!queries || !idx_out || (N > 0 && (!tree || !perm))) return KDT_ERR_INVALID_ARG;
     const size_t tree_b = (size_t)N * k * sizeof(float), perm_b = (size_t)N * sizeof(int32_t);
     const size_t q_b = (size_t)Q * k * sizeof(float), out_b = (size_t)Q * K * sizeof(int32_t);
-    const void* ins[3] = {tree, perm, queries};
-    const size_t in_b[3] = {tree_b, perm_b, q_b};
-    for (int i = 0; i < 3; ++i)
+    const void* ins[4] = {tree, perm, queries, dims};
+    const size_t in_b[4] = {tree_b, perm_b, q_b, dims ? perm_b : 0};
+    for (int i = 0; i < 4; ++i)
         if (overlap(idx_out, out_b, ins[i], in_b[i]) || overlap(d2_out, out_b, ins[i], in_b[i]))
             return KDT_ERR_INVALID_ARG;
     const size_t v_b = (size_t)Q * sizeof(uint32_t);
-    for (int i = 0; i < 3; ++i)
+    for (int i = 0; i < 4; ++i)
         if (overlap(visits_out, v_b, ins[i], in_b[i])) return KDT_ERR_INVALID_ARG;
     if (overlap(idx_out, out_b, d2_out, out_b) || overlap(visits_out, v_b, idx_out, out_b) ||
         overlap(visits_out, v_b, d2_out, out_b))
         return KDT_ERR_INVALID_ARG;
-    KnnArgs a{tree, perm, N, k, queries, Q, K, idx_out, d2_out, visits_out, budget};
+    KnnArgs a{tree, perm, dims, N, k, queries, Q, K, idx_out, d2_out, visits_out, budget};
     if (K <= 1) launch_knn<1>(a, stream);
     else if (K <= 2) launch_knn<2>(a, stream);
     else if (K <= 4) launch_knn<4>(a, stream);
@@ -471,16 +502,16 @@ kdt_status knn_impl(const float* tree, const int32_t* perm, int64_t N, int32_t k
 
 }  // namespace
 
-extern "C" kdt_status kdt_knn(const float* tree, const int32_t* perm, int64_t N, int32_t k,
-                              const float* queries, int64_t Q, int32_t K, int32_t* idx_out,
+extern "C" kdt_status kdt_knn(const float* tree, const int32_t* perm, const int32_t* dims, int64_t N,
+                              int32_t k, const float* queries, int64_t Q, int32_t K, int32_t* idx_out,
                               float* d2_out, uint32_t* visits_out, hipStream_t stream) {
-    return knn_impl(tree, perm, N, k, queries, Q, K, idx_out, d2_out, visits_out, default_budget(K),
-                    stream);
+    return knn_impl(tree, perm, dims, N, k, queries, Q, K, idx_out, d2_out, visits_out,
+                    default_budget(K), stream);
 }
 
-extern "C" kdt_status kdt_knn_budget(const float* tree, const int32_t* perm, int64_t N, int32_t k,
-                                     const float* queries, int64_t Q, int32_t K, int32_t* idx_out,
-                                     float* d2_out, uint32_t* visits_out, uint32_t budget,
-                                     hipStream_t stream) {
-    return knn_impl(tree, perm, N, k, queries, Q, K, idx_out, d2_out, visits_out, budget, stream);
+extern "C" kdt_status kdt_knn_budget(const float* tree, const int32_t* perm, const int32_t* dims,
+                                     int64_t N, int32_t k, const float* queries, int64_t Q, int32_t K,
+                                     int32_t* idx_out, float* d2_out, uint32_t* visits_out,
+                                     uint32_t budget, hipStream_t stream) {
+    return knn_impl(tree, perm, dims, N, k, queries, Q, K, idx_out, d2_out, visits_out, budget, stream);
 }

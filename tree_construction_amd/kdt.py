@@ -49,9 +49,9 @@ SIGNATURES = {
     "kdt_debug_workspace_size": (_SZ, [_I64, _I32, _I32]),
     "kdt_closed_live_segment": (_I64, [_I64, _I32, _I64]),
     "kdt_closed_bin_prefix": (_I64, [_I64, _I32, _I32, _I64, _I64]),
-    "kdt_knn": (ctypes.c_int, [_VOIDP, _VOIDP, _I64, _I32, _VOIDP, _I64, _I32, _VOIDP, _VOIDP, _VOIDP,
+    "kdt_knn": (ctypes.c_int, [_VOIDP, _VOIDP, _VOIDP, _I64, _I32, _VOIDP, _I64, _I32, _VOIDP, _VOIDP, _VOIDP,
                                _VOIDP]),
-    "kdt_knn_budget": (ctypes.c_int, [_VOIDP, _VOIDP, _I64, _I32, _VOIDP, _I64, _I32, _VOIDP, _VOIDP,
+    "kdt_knn_budget": (ctypes.c_int, [_VOIDP, _VOIDP, _VOIDP, _I64, _I32, _VOIDP, _I64, _I32, _VOIDP, _VOIDP,
                                       _VOIDP, ctypes.c_uint32, _VOIDP]),
     "kdt_workspace_size_widest": (_SZ, [_I64, _I32]),
     "kdt_build_widest": (ctypes.c_int, [_VOIDP, _I64, _I32, _VOIDP, _VOIDP, _VOIDP, _VOIDP, _SZ, _VOIDP]),
@@ -267,13 +267,14 @@ def build(points, want_tree: bool = True, stream=None):
     return Builder(n, k, points.device).build(points, want_tree=want_tree, stream=stream)
 
 
-def knn(tree, perm, queries, K: int, idx=None, d2=None, visits=None, stream=None, budget=None):
+def knn(tree, perm, queries, K: int, idx=None, d2=None, visits=None, stream=None, budget=None, dims=None):
     """K nearest neighbours of every query among the points of a built tree.
 
     tree, perm: the outputs of build() ((N, k) float32 and (N,) int32 on a
     HIP device); queries: (Q, k) float32 on the same device. Returns (idx, d2):
     (Q, K) int32 original indices, nearest first (-1 past N), and their
-    (Q, K) float32 squared distances. A (Q,) int32 tensor passed as `visits`
+    (Q, K) float32 squared distances. For a split-widest tree pass its `dims`
+    (build_widest's third output). A (Q,) int32 tensor passed as `visits`
     receives the number of tree points each search examined. `budget`
     (diagnostic) sets how many points a first-pass thread examines before
     handing its query to the wave pass."""
@@ -292,7 +293,10 @@ def knn(tree, perm, queries, K: int, idx=None, d2=None, visits=None, stream=None
         idx = torch.empty((q, K), dtype=torch.int32, device=queries.device)
     if d2 is None:
         d2 = torch.empty((q, K), dtype=torch.float32, device=queries.device)
-    args = [ctypes.c_void_p(tree.data_ptr() if n else 0), ctypes.c_void_p(perm.data_ptr() if n else 0), n, k,
+    if dims is not None and (dims.dtype != torch.int32 or dims.numel() != n or not dims.is_contiguous()):
+        raise ValueError("dims must be a contiguous int32 tensor of N entries")
+    args = [ctypes.c_void_p(tree.data_ptr() if n else 0), ctypes.c_void_p(perm.data_ptr() if n else 0),
+            ctypes.c_void_p(dims.data_ptr() if (dims is not None and n) else 0), n, k,
             ctypes.c_void_p(queries.data_ptr()), q, int(K),
             ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(d2.data_ptr()),
             ctypes.c_void_p(visits.data_ptr() if visits is not None else 0)]
