@@ -169,6 +169,28 @@ kdt_status kdt_build_widest_profiled(const float* points, int64_t N, int32_t k,
                                      void* workspace, size_t workspace_bytes,
                                      hipStream_t stream, kdt_profile* profile);
 
+/* Duplicate removal, the optional pre-pass of J. Robinson's KdTreeGPU
+ * wiki (duplicate-removal section): tuples equal in every coordinate
+ * (IEEE '==', so -0.0 equals +0.0) collapse to one. Of each group of equal
+ * tuples the one with the smallest original index is kept.
+ *   points     device, N*k float32, row-major. Read only.
+ *   keep_out   device, N int32: its first *count_out entries are the kept
+ *              indices, ascending; the rest are unspecified.
+ *   count_out  device, one int64: the number of distinct tuples.
+ * Workspace: kdt_unique_workspace_size(N, k) bytes, 256-byte aligned.
+ * Ownership, streams and errors as kdt_build (NULL count_out is
+ * KDT_ERR_INVALID_ARG). NaN coordinates are outside the definition. */
+size_t kdt_unique_workspace_size(int64_t N, int32_t k);
+kdt_status kdt_unique(const float* points, int64_t N, int32_t k,
+                      int32_t* keep_out, int64_t* count_out,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* kdt_unique with per-kernel timing, as kdt_build_profiled. */
+kdt_status kdt_unique_profiled(const float* points, int64_t N, int32_t k,
+                               int32_t* keep_out, int64_t* count_out,
+                               void* workspace, size_t workspace_bytes,
+                               hipStream_t stream, kdt_profile* profile);
+
 /* K nearest neighbours of each query point among the N points of a tree
  * built by kdt_build or kdt_build_widest, exactly as a brute-force search
  * ranks them. The search is the two-phase descent and backtrack of

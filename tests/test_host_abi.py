@@ -200,3 +200,26 @@ def test_debug_tags_rejects_bad_rounds():
 def test_status_strings():
     for code in range(4):
         assert kdt.lib().kdt_status_string(code)
+
+
+# kdt_unique(points, N, k, keep_out, count_out, workspace, workspace_bytes, stream)
+@pytest.mark.parametrize("args,code", [
+    ((FAKE, 10, 0, FAKE + 2**20, FAKE + 2**21, FAKE + 2**22, 1 << 20, None), 1),   # k = 0
+    ((FAKE, -3, 3, FAKE + 2**20, FAKE + 2**21, FAKE + 2**22, 1 << 20, None), 1),   # N < 0
+    ((0, 10, 3, FAKE + 2**20, FAKE + 2**21, FAKE + 2**22, 1 << 20, None), 1),      # points NULL
+    ((FAKE, 10, 3, 0, FAKE + 2**21, FAKE + 2**22, 1 << 20, None), 1),              # keep NULL
+    ((FAKE, 10, 3, FAKE + 2**20, 0, FAKE + 2**22, 1 << 20, None), 1),              # count NULL
+    ((FAKE, 10, 3, FAKE + 2**20, FAKE + 2**21, 0, 1 << 20, None), 2),              # workspace NULL
+    ((FAKE, 10, 3, FAKE + 2**20, FAKE + 2**21, FAKE + 2**22, 8, None), 2),         # workspace small
+    ((FAKE, 10, 3, FAKE + 4, FAKE + 2**21, FAKE + 2**22, 1 << 20, None), 1),       # keep on points
+    ((FAKE, 10, 3, FAKE + 2**20, FAKE + 2**20 + 8, FAKE + 2**22, 1 << 20, None), 1),  # count on keep
+])
+def test_unique_rejects_bad_arguments_before_launch(args, code):
+    assert kdt.lib().kdt_unique(*args) == code
+
+
+def test_unique_workspace_size():
+    assert kdt.unique_workspace_size(0, 3) == 0
+    assert kdt.unique_workspace_size(10, 0) == 0
+    a, b = kdt.unique_workspace_size(1 << 20, 3), kdt.unique_workspace_size(1 << 21, 3)
+    assert 0 < a < b

@@ -519,6 +519,8 @@ struct SortArgs {
     const u8* digits;   // this pass's digit of every record, in input order
     u8* next_digits;    // the next pass's digit of every record, in output
                         //   order (nullptr after the last pass)
+    int next_dim;       // the next pass's digit: (key of next_dim >> next_shift) & 255
+    int next_shift;
     u32 tiles;
     u64 chunks;
     u32* tile_counts;   // tiles x 256: digit counts of each tile
@@ -659,9 +661,9 @@ __global__ __launch_bounds__(kSortBlock) void k_sort_scatter(SortArgs a) {
             const uint4 q = sm.quads[i];
             *reinterpret_cast<uint4*>(a.out + (u64)dst * 4) = q;
             if (a.next_digits) {
-                const u32 c = (q.x & (a.dim == 0 ? ~0u : 0u)) | (q.y & (a.dim == 1 ? ~0u : 0u)) |
-                              (q.z & (a.dim == 2 ? ~0u : 0u));
-                a.next_digits[dst] = (u8)(c >> (a.shift + kRadixBits));
+                const u32 c = (q.x & (a.next_dim == 0 ? ~0u : 0u)) | (q.y & (a.next_dim == 1 ? ~0u : 0u)) |
+                              (q.z & (a.next_dim == 2 ? ~0u : 0u));
+                a.next_digits[dst] = (u8)(c >> a.next_shift);
             }
         }
     } else {
@@ -677,8 +679,8 @@ __global__ __launch_bounds__(kSortBlock) void k_sort_scatter(SortArgs a) {
                 const u32 dst = s_base[s_digit[i]] + (u32)i;
                 if (dst >= (u64)a.src.n) continue;
                 a.out[(u64)dst * words + ww] = sm.words[i];
-                if (ww == a.dim && a.next_digits)
-                    a.next_digits[dst] = (u8)(sm.words[i] >> (a.shift + kRadixBits));
+                if (ww == a.next_dim && a.next_digits)
+                    a.next_digits[dst] = (u8)(sm.words[i] >> a.next_shift);
             }
         }
     }
@@ -1048,6 +1050,79 @@ __global__ __launch_bounds__(kBlock) void k_widest_level(Geometry geo, int l, in
     }
     dimtab[s] = (uint16_t)best;
     if (dims_out) dims_out[s] = best;
+}
+
+// ------------------------------------------------- duplicate removal
+// [R], duplicate-removal section: with the tuples sorted by all their
+// coordinates, equal tuples are adjacent and all but one of each run go. Here
+// the records are sorted by the keys of coordinates 0 .. k-1 (coordinate 0
+// most significant) and then by index, so the first record of a run has the
+// group's smallest index; its index is flagged, and a compaction in index
+// order lists the kept indices ascending.
+
+constexpr int kFlagItems = 16;                  // flags per thread (one 16-byte load)
+constexpr int kFlagTile = kBlock * kFlagItems;  // flags per compaction workgroup
+
+// keep[idx] = 1 for the first record of every run of equal tuples, else 0.
+__global__ __launch_bounds__(kBlock) void k_unique_mark(const u32* __restrict__ recs, i64 n, int words,
+                                                        u8* __restrict__ keep) {
+    const int k = words - 1;
+    const i64 stride = (i64)gridDim.x * kBlock;
+    for (i64 r = (i64)blockIdx.x * kBlock + threadIdx.x; r < n; r += stride) {
+        const u32* me = recs + r * words;
+        bool head = r == 0;
+        if (!head) {
+            const u32* prev = me - words;
+            for (int d = 0; d < k && !head; ++d) head = me[d] != prev[d];  // keys: equal iff the floats are
+        }
+        keep[me[k]] = head ? 1 : 0;
+    }
+}
+
+// The kFlagItems flags of this thread (0 past n).
+__device__ inline void load_flags(const u8* keep, i64 n, i64 first, u32 (&w)[4]) {
+    if (first + kFlagItems <= n) {
+        const uint4 v = *reinterpret_cast<const uint4*>(keep + first);
+        w[0] = v.x;
+        w[1] = v.y;
+        w[2] = v.z;
+        w[3] = v.w;
+    } else {
+        w[0] = w[1] = w[2] = w[3] = 0;
+        for (int j = 0; j < kFlagItems; ++j)
+            if (first + j < n) w[j >> 2] |= (u32)keep[first + j] << (8 * (j & 3));
+    }
+}
+
+// Kept indices per tile of kFlagTile flags.
+__global__ __launch_bounds__(kBlock) void k_flag_count(const u8* __restrict__ keep, i64 n,
+                                                       u32* __restrict__ counts) {
+    __shared__ u32 s_wave[kWaves];
+    const i64 first = (i64)blockIdx.x * kFlagTile + (i64)threadIdx.x * kFlagItems;
+    u32 w[4];
+    load_flags(keep, n, first, w);
+    const u32 mine = __popc(w[0]) + __popc(w[1]) + __popc(w[2]) + __popc(w[3]);  // flags are 0 or 1
+    const u32 before = block_exclusive_scan(mine, s_wave);
+    if (threadIdx.x == kBlock - 1) counts[blockIdx.x] = before + mine;
+}
+
+// Writes the kept indices of one tile at their places (prefix: kept indices
+// in the tiles before, from k_chunk_scan), and the total to *count_out.
+__global__ __launch_bounds__(kBlock) void k_flag_compact(const u8* __restrict__ keep, i64 n,
+                                                         const u32* __restrict__ prefix,
+                                                         const u32* __restrict__ totals,
+                                                         int32_t* __restrict__ keep_out,
+                                                         int64_t* __restrict__ count_out) {
+    __shared__ u32 s_wave[kWaves];
+    const i64 first = (i64)blockIdx.x * kFlagTile + (i64)threadIdx.x * kFlagItems;
+    u32 w[4];
+    load_flags(keep, n, first, w);
+    const u32 mine = __popc(w[0]) + __popc(w[1]) + __popc(w[2]) + __popc(w[3]);
+    u32 at = prefix[blockIdx.x] + block_exclusive_scan(mine, s_wave);
+#pragma unroll
+    for (int j = 0; j < kFlagItems; ++j)
+        if ((w[j >> 2] >> (8 * (j & 3))) & 1u) keep_out[at++] = (int32_t)(first + j);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *count_out = (int64_t)totals[0];
 }
 
 __global__ __launch_bounds__(kBlock) void k_zero(u32* __restrict__ out, i64 n) {
@@ -1786,6 +1861,8 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
                 a.shift = 8 * p;
                 a.digits = p == 0 ? digits0 + (size_t)d * n : digits;
                 a.next_digits = p == kKeyBytes - 1 ? nullptr : digits;
+                a.next_dim = d;
+                a.next_shift = 8 * (p + 1);
                 if (p == 0) launch.sort_any<kSrcRows>(a);
                 else launch.sort_any<kSrcRecords>(a);
             }
@@ -1842,6 +1919,100 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
     return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
 }
 
+// Workspace of duplicate removal: the presort's buffers for records of all k
+// coordinates, one flag per point, and the compaction's tile counts.
+struct UniqueLayout {
+    Layout base;
+    size_t keep, flag_counts;
+    i64 flag_tiles;
+};
+
+bool make_layout_unique(i64 n, int k, UniqueLayout* out) {
+    if (n < 0 || n > INT32_MAX || k < 1 || k > 65535) return false;
+    UniqueLayout u{};
+    if (n == 0) {
+        *out = u;
+        return true;
+    }
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align_up(off + bytes);
+        return at;
+    };
+    Layout& lay = u.base;
+    lay.kr = k;
+    lay.words = k + 1;
+    lay.tiles = (n + kPartTile - 1) / kPartTile;
+    const size_t rec_bytes = (size_t)n * lay.words * sizeof(u32);
+    lay.tmp0 = take(rec_bytes);
+    lay.tmp1 = take(rec_bytes);
+    lay.digits = take((size_t)n);
+    lay.digits0 = take((size_t)k * n);
+    lay.totals = take((size_t)kRadix * sizeof(u32));
+    lay.slots = take((size_t)lay.tiles * kRadix * sizeof(u32));
+    lay.chunk_slots = take((size_t)((lay.tiles + kChunkTiles - 1) / kChunkTiles) * kRadix * sizeof(u32));
+    u.keep = take((size_t)n);
+    u.flag_tiles = (n + kFlagTile - 1) / kFlagTile;
+    u.flag_counts = take((size_t)u.flag_tiles * sizeof(u32));
+    lay.total = off;
+    *out = u;
+    return true;
+}
+
+// Duplicate removal: stable LSD radix passes over the keys of coordinates
+// k-1, ..., 0 (4 passes each; each pass also writes the next pass's digit
+// byte, across a change of coordinate too), then the run heads, then the
+// compaction in index order.
+kdt_status run_unique(const float* pts, i64 n, int k, const UniqueLayout& ul, char* ws,
+                      hipStream_t stream, Timer timer, int32_t* keep_out, int64_t* count_out) {
+    const Layout& lay = ul.base;
+    const int W = lay.words;
+    u32* tmp[2] = {(u32*)(ws + lay.tmp0), (u32*)(ws + lay.tmp1)};
+    u8* digits = (u8*)(ws + lay.digits);
+    u8* digits0 = (u8*)(ws + lay.digits0);
+    u32* totals = (u32*)(ws + lay.totals);
+    u8* keep = (u8*)(ws + ul.keep);
+    u32* flag_counts = (u32*)(ws + ul.flag_counts);
+    Launcher launch{(u32*)(ws + lay.slots), (u32*)(ws + lay.chunk_slots), totals, stream, timer};
+
+    timer.begin("k_first_digits", (double)n * 5.0 * k);
+    k_first_digits<<<grid_for(n, kBlock, 1 << 30), kBlock, 0, stream>>>(pts, n, k, k, digits0);
+    timer.end();
+    int pass = 0;
+    const u32* sorted = nullptr;
+    for (int d = k - 1; d >= 0; --d)
+        for (int p = 0; p < kKeyBytes; ++p, ++pass) {
+            SortArgs a{};
+            a.src = RecordSource{pts, k, pass == 0 ? nullptr : tmp[(pass + 1) & 1], W, n};
+            a.out = tmp[pass & 1];
+            a.dim = d;
+            a.shift = 8 * p;
+            a.digits = pass == 0 ? digits0 + (size_t)(k - 1) * n : digits;
+            const bool last = d == 0 && p == kKeyBytes - 1;
+            a.next_digits = last ? nullptr : digits;
+            a.next_dim = p + 1 < kKeyBytes ? d : d - 1;
+            a.next_shift = p + 1 < kKeyBytes ? 8 * (p + 1) : 0;
+            if (pass == 0) launch.sort_any<kSrcRows>(a);
+            else launch.sort_any<kSrcRecords>(a);
+            sorted = a.out;
+        }
+    timer.begin("k_unique_mark", (double)n * (8.0 * W + 1));
+    k_unique_mark<<<grid_for(n, kBlock, 1 << 16), kBlock, 0, stream>>>(sorted, n, W, keep);
+    timer.end();
+    const i64 T = ul.flag_tiles;
+    timer.begin("k_flag_count", (double)n + 4.0 * T);
+    k_flag_count<<<(unsigned)T, kBlock, 0, stream>>>(keep, n, flag_counts);
+    timer.end();
+    timer.begin("k_chunk_scan", (double)T * 8);
+    k_chunk_scan<<<1, kBlock, 0, stream>>>(flag_counts, T, totals);
+    timer.end();
+    timer.begin("k_flag_compact", (double)n * 5.0);
+    k_flag_compact<<<(unsigned)T, kBlock, 0, stream>>>(keep, n, flag_counts, totals, keep_out, count_out);
+    timer.end();
+    return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
+}
+
 // A split-widest-dimension build ([W], split-widest-dimension section): the
 // root domain and dimension first; every dimension's array presorted; then
 // level by level, every array re-sorted by the new tags (one pass of one
@@ -1895,6 +2066,8 @@ kdt_status run_widest(const float* pts, i64 n, int k, const WidestLayout& wl, ch
             a.shift = 8 * p;
             a.digits = p == 0 ? digits0 + (size_t)d * n : digits;
             a.next_digits = p == kKeyBytes - 1 ? nullptr : digits;
+            a.next_dim = d;
+            a.next_shift = 8 * (p + 1);
             if (p == 0) launch.sort_any<kSrcRows>(a);
             else launch.sort_any<kSrcRecords>(a);
         }
@@ -2050,6 +2223,22 @@ kdt_status build_widest_impl(const float* points, int64_t N, int32_t k, int32_t*
     return run_widest(points, N, k, wl, (char*)workspace, stream, timer, perm_out, tree_out, dims_out);
 }
 
+kdt_status unique_impl(const float* points, int64_t N, int32_t k, int32_t* keep_out, int64_t* count_out,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream, Timer timer) {
+    UniqueLayout ul;
+    if (!valid_size(N, k) || !make_layout_unique(N, k, &ul)) return KDT_ERR_INVALID_ARG;
+    if (!count_out) return KDT_ERR_INVALID_ARG;
+    const size_t keep_bytes = (size_t)N * sizeof(int32_t);
+    kdt_status st = validate(points, N, k, keep_out, keep_bytes, count_out, sizeof(int64_t), workspace,
+                             workspace_bytes, ul.base);
+    if (st != KDT_OK) return st;
+    if (N == 0) {
+        k_zero<<<1, kBlock, 0, stream>>>(reinterpret_cast<u32*>(count_out), 2);
+        return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
+    }
+    return run_unique(points, N, k, ul, (char*)workspace, stream, timer, keep_out, count_out);
+}
+
 // Runs `build` with a HIP event pair around every kernel, synchronises and
 // fills *profile.
 template <typename Build>
@@ -2113,6 +2302,25 @@ kdt_status kdt_build_profiled(const float* points, int64_t N, int32_t k, int32_t
                               hipStream_t stream, kdt_profile* profile) {
     return run_profiled(stream, profile, [&](Timer timer) {
         return build_impl(points, N, k, perm_out, tree_out, workspace, workspace_bytes, stream, timer);
+    });
+}
+
+size_t kdt_unique_workspace_size(int64_t N, int32_t k) {
+    UniqueLayout ul;
+    if (!valid_size(N, k) || !make_layout_unique(N, k, &ul)) return 0;
+    return ul.base.total;
+}
+
+kdt_status kdt_unique(const float* points, int64_t N, int32_t k, int32_t* keep_out, int64_t* count_out,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return unique_impl(points, N, k, keep_out, count_out, workspace, workspace_bytes, stream, Timer{nullptr});
+}
+
+kdt_status kdt_unique_profiled(const float* points, int64_t N, int32_t k, int32_t* keep_out,
+                               int64_t* count_out, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream, kdt_profile* profile) {
+    return run_profiled(stream, profile, [&](Timer timer) {
+        return unique_impl(points, N, k, keep_out, count_out, workspace, workspace_bytes, stream, timer);
     });
 }
 

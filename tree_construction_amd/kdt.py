@@ -53,6 +53,10 @@ SIGNATURES = {
                                _VOIDP]),
     "kdt_knn_budget": (ctypes.c_int, [_VOIDP, _VOIDP, _VOIDP, _I64, _I32, _VOIDP, _I64, _I32, _VOIDP, _VOIDP,
                                       _VOIDP, ctypes.c_uint32, _VOIDP]),
+    "kdt_unique_workspace_size": (_SZ, [_I64, _I32]),
+    "kdt_unique": (ctypes.c_int, [_VOIDP, _I64, _I32, _VOIDP, _VOIDP, _VOIDP, _SZ, _VOIDP]),
+    "kdt_unique_profiled": (ctypes.c_int, [_VOIDP, _I64, _I32, _VOIDP, _VOIDP, _VOIDP, _SZ, _VOIDP,
+                                           ctypes.POINTER(Profile)]),
     "kdt_workspace_size_widest": (_SZ, [_I64, _I32]),
     "kdt_build_widest": (ctypes.c_int, [_VOIDP, _I64, _I32, _VOIDP, _VOIDP, _VOIDP, _VOIDP, _SZ, _VOIDP]),
     "kdt_build_widest_profiled": (ctypes.c_int, [_VOIDP, _I64, _I32, _VOIDP, _VOIDP, _VOIDP, _VOIDP, _SZ,
@@ -192,6 +196,58 @@ class Builder:
                                   nbytes, _stream_handle(points.device, stream))
         _check(st, "kdt_debug_tags")
         return out
+
+
+def unique_workspace_size(n: int, k: int) -> int:
+    return int(lib().kdt_unique_workspace_size(int(n), int(k)))
+
+
+class UniqueFinder:
+    """Duplicate removal for (N, k) points with a held workspace."""
+
+    def __init__(self, n: int, k: int, device="cuda"):
+        import torch
+        self.n, self.k = int(n), int(k)
+        self.device = torch.device(device)
+        nbytes = unique_workspace_size(self.n, self.k)
+        if nbytes == 0 and self.n > 0:
+            raise ValueError("unsupported size N=%d k=%d" % (self.n, self.k))
+        self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=self.device)
+        self.workspace_bytes = nbytes
+        self.count = torch.empty(1, dtype=torch.int64, device=self.device)
+
+    def _args(self, points, keep, stream):
+        return (ctypes.c_void_p(points.data_ptr()), self.n, self.k, ctypes.c_void_p(keep.data_ptr()),
+                ctypes.c_void_p(self.count.data_ptr()), ctypes.c_void_p(self.workspace.data_ptr()),
+                self.workspace_bytes, _stream_handle(points.device, stream))
+
+    def run(self, points, keep=None, stream=None):
+        """Enqueue; returns (keep, count) with count a 1-element device tensor."""
+        import torch
+        _validate_points(points)
+        if tuple(points.shape) != (self.n, self.k):
+            raise ValueError("points shape %s != (%d, %d)" % (tuple(points.shape), self.n, self.k))
+        if keep is None:
+            keep = torch.empty(max(self.n, 1), dtype=torch.int32, device=points.device)
+        _check(lib().kdt_unique(*self._args(points, keep, stream)), "kdt_unique")
+        return keep, self.count
+
+    def run_profiled(self, points, keep, stream=None):
+        _validate_points(points)
+        prof = Profile()
+        _check(lib().kdt_unique_profiled(*self._args(points, keep, stream), ctypes.byref(prof)),
+               "kdt_unique_profiled")
+        return prof.as_dict()
+
+
+def unique(points, stream=None):
+    """Ascending original indices of one point (the smallest index) of every
+    distinct tuple of `points` ((N, k) float32 on a HIP device): an int32
+    device tensor (synchronises to read the count)."""
+    _validate_points(points)
+    n, k = points.shape
+    keep, count = UniqueFinder(n, k, points.device).run(points, stream=stream)
+    return keep[: int(count.item())]
 
 
 def workspace_size_widest(n: int, k: int) -> int:
