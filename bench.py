@@ -17,6 +17,9 @@ Prints ONE JSON line on stdout (progress goes to stderr):
 With --widest it times the split-widest-dimension build of the same workload
 instead (value, roofline and cpu_baseline as above, for that variant).
 
+With --unique it times the duplicate-removal pre-pass on the same workload
+(kept indices of the distinct tuples), the numpy oracle as cpu_baseline.
+
 With --knn it instead times the K-nearest-neighbour query over the headline
 tree (the tree is built once, untimed): --knn-queries query points drawn with
 the workload's recipe, K = --knn-k; value in Mqueries/s, the roofline from the
@@ -159,6 +162,69 @@ def run_knn(args):
     print(json.dumps(out), flush=True)
 
 
+def run_unique(args):
+    import torch
+    from tree_construction_amd import datagen, kdt
+    name = args.workload or datagen.HEADLINE
+    w = datagen.WORKLOADS[name]
+    pts = datagen.cached(name)
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(pts).to(dev)
+    n, k = pts.shape
+    finder = kdt.UniqueFinder(n, k, dev)
+    keep = torch.empty(n, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        finder.run(x, keep)
+    torch.cuda.synchronize(dev)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        finder.run(x, keep)
+    stop.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = start.elapsed_time(stop) / args.steps
+    distinct = int(finder.count.item())
+    log("bench: %.3f ms per pass, %.1f Mpoints/s, %d distinct of %d" % (ms, n / ms / 1e3, distinct, n))
+    agg = {}
+    for _ in range(args.steps):
+        for kind, rec in finder.run_profiled(x, keep).items():
+            a = agg.setdefault(kind, {"launches": 0, "ms": 0.0, "bytes": 0.0})
+            for f in a:
+                a[f] += rec[f]
+    kernels = {kk: {"launches_per_pass": a["launches"] // args.steps, "avg_us": round(a["ms"] / a["launches"] * 1e3, 2),
+                    "ms_per_pass": round(a["ms"] / args.steps, 4),
+                    "GBps": round(a["bytes"] / (a["ms"] * 1e-3) / 1e9, 1) if a["ms"] > 0 else 0.0}
+               for kk, a in agg.items() if a["launches"]}
+    for kk, kv in sorted(kernels.items(), key=lambda kv: -kv[1]["ms_per_pass"]):
+        log("  %-36s %4d/pass  avg %8.2f us  %8.1f GB/s  %.3f ms/pass"
+            % (kk, kv["launches_per_pass"], kv["avg_us"], kv["GBps"], kv["ms_per_pass"]))
+    dom = max(kernels, key=lambda kk: kernels[kk]["ms_per_pass"])
+    base = None
+    if not args.no_cpu_baseline:
+        from oracle import unique as unique_oracle  # test infrastructure, used only for this baseline
+        t0 = time.perf_counter()
+        unique_oracle.unique_indices(pts)
+        dt = time.perf_counter() - t0
+        base = {"value": round(n / dt / 1e6, 3), "unit": "Mpoints/s", "cores": 1, "kind": "oracle",
+                "sample": "the whole workload %s (numpy), %.1f s wall" % (name, dt)}
+        log("  %s" % base)
+    out = {
+        "metric": "duplicate removal Mpoints/s at N=16M k=3 fp32",
+        "value": round(n / ms / 1e3, 2), "unit": "Mpoints/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "u32", "data": "synthetic",
+        "config": {"workload": "unique over %s" % name, "n_points": n, "k": k, "distinct": distinct,
+                   "description": w.note},
+        "roofline": {"bound": "hbm", "achieved": kernels[dom]["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(kernels[dom]["GBps"] / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                     "avg_us": kernels[dom]["avg_us"]},
+        "cpu_baseline": base,
+        "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def kernel_short_name(name):
     """'void (anonymous namespace)::k_x<1, 2>((anonymous namespace)::Args)' -> 'k_x<1, 2>'."""
     name = name.replace("(anonymous namespace)::", "").replace("void ", "")
@@ -215,6 +281,7 @@ def main():
     ap.add_argument("--no-counters", action="store_true",
                     help="skip the rocprofv3 FETCH_SIZE/WRITE_SIZE runs behind roofline.traffic")
     ap.add_argument("--widest", action="store_true", help="time the split-widest-dimension build")
+    ap.add_argument("--unique", action="store_true", help="time the duplicate-removal pre-pass")
     ap.add_argument("--knn", action="store_true", help="time the kNN query instead of the build")
     ap.add_argument("--knn-queries", type=int, default=1 << 20)
     ap.add_argument("--knn-k", type=int, default=8)
@@ -230,6 +297,9 @@ def main():
         sys.exit(2)
     if args.knn:
         run_knn(args)
+        return
+    if args.unique:
+        run_unique(args)
         return
 
     import torch
