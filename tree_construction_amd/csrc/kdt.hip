@@ -39,6 +39,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
 #include <vector>
 
 #include "kdt.h"
@@ -60,6 +61,11 @@ constexpr int kPartItems = 8;              // records per thread in a tile
 constexpr int kPartTile = kBlock * kPartItems;  // records per tile
 constexpr int kKeyBytes = 4;               // order-preserving coordinate key
 constexpr int kMaxDescent = kRadixBits;    // levels one re-sort pass walks
+#ifndef KDT_SELECT_DEPTH
+#define KDT_SELECT_DEPTH 6
+#endif
+constexpr int kSelectDepth = KDT_SELECT_DEPTH;  // deepest walk a round may leave to the array's next re-sort
+static_assert(kSelectDepth <= kMaxDescent, "one pass per walk");
 constexpr int kMaxRounds = 32;             // global rounds (levels) at most
 static_assert(kBlock == kRadix, "the tile kernels map one thread to one digit");
 
@@ -823,11 +829,41 @@ __global__ __launch_bounds__(kBlock) void k_part_count(PartArgs a) { part_count<
 template <int kW>
 __global__ __launch_bounds__(kBlock) void k_part_count_widest(PartArgs a) { part_count<kW, true>(a); }
 
-template <int kW, bool kNodeDims>
+// Whether tile t of a pass holds the pivot of some level-l1 node. The node
+// with in-level index j0 * 2^delta + b has its pivot where the count of
+// digit-b records before it reaches bin_prefix(j0, b) + |S(left child)|, and
+// tile t holds the digit-b records counted from chunk_counts[b][t] up to
+// chunk_counts[b][t+1] (the last tile: all the rest). Only the level-l0
+// segments the tile overlaps can have their pivots in it.
+__device__ bool tile_has_pivot(const PartArgs& a, u32 t) {
+    const int delta = a.l1 - a.l0;
+    const u32 bins = 1u << delta;
+    const u64 p0 = (u64)t * kPartTile;
+    const u64 p1 = p0 + kPartTile < (u64)a.src.n ? p0 + kPartTile : (u64)a.src.n;
+    const u32 j_first = (u32)live_segment(a.geo, p0, a.l0);
+    const u32 j_last = (u32)live_segment(a.geo, p1 - 1, a.l0);
+    const u32 pairs = (j_last - j_first + 1) << delta;
+    const bool tail = t + 1 == a.tiles;
+    int hit = 0;
+    for (u32 i = threadIdx.x; i < pairs; i += kBlock) {
+        const u32 j0 = j_first + (i >> delta), b = i & (bins - 1);
+        const u32 target = bin_prefix32(a.s1, j0, b, delta) + subtree_size32(a.s2, 2 * ((j0 << delta) | b));
+        const u32* row = a.chunk_counts + (u64)b * a.tiles;
+        if (target >= row[t] && (tail || target < row[t + 1])) hit = 1;
+    }
+    return __syncthreads_or(hit) != 0;
+}
+
+// kSelect: the pass only fixes the level-l1 nodes; it reads the tiles that
+// hold their pivots and writes no records (the array keeps its level-l0
+// order, and its next re-sort walks the levels in between as well).
+template <int kW, bool kNodeDims, bool kSelect = false>
 __device__ __forceinline__ void part_scatter(const PartArgs& a) {
     __shared__ u32 count[kWaves][kRadix];  // per-wave digit counts, then first slots
     const u32 t = xcd_tile(a.tiles);
     if (t >= a.tiles) return;
+    if constexpr (kSelect)
+        if (!tile_has_pivot(a, t)) return;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const i64 wbase = (i64)t * kPartTile + (i64)w * (64 * kPartItems) + lane;
     const int delta = a.l1 - a.l0;
@@ -861,9 +897,11 @@ __device__ __forceinline__ void part_scatter(const PartArgs& a) {
         if (!valid[j]) continue;
         const u32 digit = node[j] & (bins - 1);
         const u32 in_segment = count[w][digit] + rank[j] - bin_prefix32(a.s1, node[j] >> delta, digit, delta);
-        const u32 pos = live_begin32(a.s1, node[j]) + in_segment;
         const i64 e = wbase + (i64)j * 64;
-        if (pos < (u64)a.n_out) tr.store(a.src, a.out, j, e, pos);
+        if constexpr (!kSelect) {
+            const u32 pos = live_begin32(a.s1, node[j]) + in_segment;
+            if (pos < (u64)a.n_out) tr.store(a.src, a.out, j, e, pos);
+        }
         const u32 left = a.leaf_level ? 0u : subtree_size32(a.s2, 2 * node[j]);
         bool mine = true;  // the node splits this array's dimension
         if constexpr (kNodeDims) mine = a.dimtab[full_nodes(a.l1) + node[j]] == (uint16_t)a.array_dim;
@@ -883,6 +921,8 @@ template <int kW>
 __global__ __launch_bounds__(kBlock) void k_part_scatter(PartArgs a) { part_scatter<kW, false>(a); }
 template <int kW>
 __global__ __launch_bounds__(kBlock) void k_part_scatter_widest(PartArgs a) { part_scatter<kW, true>(a); }
+template <int kW>
+__global__ __launch_bounds__(kBlock) void k_part_select(PartArgs a) { part_scatter<kW, false, true>(a); }
 
 // Round l's nodes: the pivot of node s = F(l) + j is the record at live
 // position live_begin(j) + |S(2s+1)| of the array sorted for round l
@@ -1162,6 +1202,13 @@ struct LocalShared {
     uint16_t order[kCachedDims][kLocalMax];  // points sorted by (coordinate, index)
 };
 
+// Key of one coordinate of the point in slot e, from its staged column (or
+// from the exchange buffer, where it was put by slot).
+struct ColumnKey {
+    const u32* col;
+    __device__ u32 operator()(u32 e) const { return col[e]; }
+};
+
 // The tag rounds keep per-wave segment counters in the exchange buffer: at
 // local level t there are 2^t segments, t <= 11 for kLocalMax points, and
 // 8-bit counters for 2048 segments must fit.
@@ -1312,14 +1359,14 @@ struct SubtreeArgs {
 // order[q] = slot (index rank) of the q-th point of the subtree by
 // (coordinate dim, original index): stable sort by the coordinate key,
 // starting from index order.
-__device__ void local_order(const u32* __restrict__ col, u32 nc, uint16_t* order,
-                            LocalShared& sh) {
+template <typename KeyOf>
+__device__ __forceinline__ void local_order(KeyOf key_of, u32 nc, uint16_t* order, LocalShared& sh) {
     u64 rec[kLocalItems];
 #pragma unroll
     for (int j = 0; j < kLocalItems; ++j) {
         const int e = local_slot(j);
         rec[j] = ~0ull;
-        if ((u32)e < nc) rec[j] = ((u64)col[e] << 16) | (u32)e;
+        if ((u32)e < nc) rec[j] = ((u64)key_of((u32)e) << 16) | (u32)e;
     }
     local_sort(rec, 16, kKeyBytes, nc, sh);
 #pragma unroll
@@ -1342,7 +1389,7 @@ __device__ void local_order(const u32* __restrict__ col, u32 nc, uint16_t* order
 // 16-bit ones no longer fit the exchange buffer (with 4096-point subtrees
 // 16-bit ones always fit).
 template <typename Count>
-__device__ void local_round(const uint16_t* order, u32 nc, int t, const Geometry& lg,
+__device__ __forceinline__ void local_round(const uint16_t* order, u32 nc, int t, const Geometry& lg,
                             LocalShared& sh) {
     Count* seg_count = reinterpret_cast<Count*>(sh.exch);  // [kLocalWaves][2^t]
     const u32 fl = (u32)full_nodes(t);
@@ -1402,6 +1449,11 @@ __device__ void local_round(const uint16_t* order, u32 nc, int t, const Geometry
     __syncthreads();
 }
 
+// kRecs: the records carry every coordinate (k <= kCachedDims, l0 > 0), so
+// nothing is staged: the records are read in arrival order and moved to
+// slot or node order through the exchange buffer. Otherwise the slots are
+// staged to global memory as columns.
+template <bool kRecs>
 __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
     __shared__ LocalShared sh;
 
@@ -1437,9 +1489,14 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
     }
     if (a.recs) local_sort(rec, 16, a.index_bytes, nc, sh);
     // Stage the subtree's points once, by index rank: their indices and their
-    // coordinate columns (each point is read exactly once here).
+    // coordinate columns (each point is read exactly once here); records
+    // that carry every coordinate are not staged.
     u32* stage_idx = a.stage + first;
-    if (a.k <= kRowRegs) {
+    if constexpr (kRecs) {
+#pragma unroll
+        for (int j = 0; j < kLocalItems; ++j)
+            if ((u32)local_slot(j) < nc) sh.tag[local_slot(j)] = 0;
+    } else if (a.k <= kRowRegs) {
         // Row loads are issued kRowBatch items at a time, before their stores.
 #pragma unroll
         for (int j0 = 0; j0 < kLocalItems; j0 += kRowBatch) {
@@ -1473,7 +1530,7 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
             sh.tag[e] = 0;
         }
     }
-    auto column = [&](int d) { return a.stage + (u64)(d + 1) * a.n + first; };
+    auto column = [&](int d) { return ColumnKey{a.stage + (u64)(d + 1) * a.n + first}; };
 
     const Geometry lg = make_geometry((i64)nc);
     const int rounds = lg.levels - 1;
@@ -1491,9 +1548,24 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
         }
     }
     if (cached)
-        for (int u = 0; u < a.k && u < rounds; ++u)
-            if ((a.l0 + u) % a.k != arrived_dim)
-                local_order(column((a.l0 + u) % a.k), nc, sh.order[u], sh);
+        for (int u = 0; u < a.k && u < rounds; ++u) {
+            const int d = (a.l0 + u) % a.k;
+            if (d == arrived_dim) continue;
+            if constexpr (kRecs) {
+                // coordinate d by slot: read in arrival order, moved to the
+                // slot through the exchange buffer
+                __syncthreads();  // arrived complete, the buffer's last readers done
+#pragma unroll
+                for (int j = 0; j < kLocalItems; ++j) {
+                    const int q = local_slot(j);
+                    if ((u32)q < nc) sh.exch[arrived[q]] = a.recs[(first + q) * a.words + d];
+                }
+                __syncthreads();
+                local_order(ColumnKey{sh.exch}, nc, sh.order[u], sh);
+            } else {
+                local_order(column(d), nc, sh.order[u], sh);
+            }
+        }
     __syncthreads();
 
     for (int t = 0; t < rounds; ++t) {
@@ -1513,6 +1585,45 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
     // Level-order output of the subtree, in node order: the nodes of each
     // local level are one contiguous range of global ids, so the writes of
     // consecutive threads are contiguous.
+    if constexpr (kRecs) {
+        // One record word at a time (the index first, then the keys): read in
+        // arrival order, put at its node in the exchange buffer, written out
+        // by node. A zero key (both zeros have it) is read back from the row,
+        // which keeps the sign of zero.
+        u32 node_at[kLocalItems], idx_of[kLocalItems];
+#pragma unroll
+        for (int j = 0; j < kLocalItems; ++j) {
+            const int q = local_slot(j);
+            node_at[j] = (u32)q < nc ? sh.tag[arrived[q]] : 0u;
+        }
+        const int words_out = a.tree ? a.words : 1;
+        for (int pass = 0; pass < words_out; ++pass) {
+            const int f = pass == 0 ? a.words - 1 : pass - 1;
+            __syncthreads();  // the buffer's last readers done
+#pragma unroll
+            for (int j = 0; j < kLocalItems; ++j) {
+                const int q = local_slot(j);
+                if ((u32)q < nc) sh.exch[node_at[j]] = a.recs[(first + q) * a.words + f];
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < kLocalItems; ++i) {
+                const u32 node = threadIdx.x + (u32)i * kLocalBlock;
+                if (node >= nc) continue;
+                const int lvl = level_of(node);
+                const u64 g = ((c + 1) << lvl) - 1 + (node - full_nodes(lvl));
+                const u32 v = sh.exch[node];
+                if (pass == 0) {
+                    idx_of[i] = v;
+                    a.perm[g] = (int32_t)v;
+                } else {
+                    a.tree[(i64)g * a.k + f] =
+                        v == 0x80000000u ? a.pts[(i64)idx_of[i] * a.k + f] : __uint_as_float(key_bits(v));
+                }
+            }
+        }
+        return;
+    }
     uint16_t* slot_of = sh.order[0];  // the orders are no longer needed
 #pragma unroll
     for (int j = 0; j < kLocalItems; ++j) {
@@ -1737,6 +1848,8 @@ const char* const kPartCountNames[4] = {"k_part_count<0>", "k_part_count<2>", "k
                                         "k_part_count<4>"};
 const char* const kPartScatterNames[4] = {"k_part_scatter<0>", "k_part_scatter<2>",
                                           "k_part_scatter<3>", "k_part_scatter<4>"};
+const char* const kPartSelectNames[4] = {"k_part_select<0>", "k_part_select<2>", "k_part_select<3>",
+                                         "k_part_select<4>"};
 const char* const kPartCountWidestNames[4] = {"k_part_count_widest<0>", "k_part_count_widest<2>",
                                               "k_part_count_widest<3>", "k_part_count_widest<4>"};
 const char* const kPartScatterWidestNames[4] = {"k_part_scatter_widest<0>", "k_part_scatter_widest<2>",
@@ -1812,6 +1925,37 @@ struct Launcher {
             default: part<0>(a); break;
         }
     }
+
+    // The nodes of level a.l1 without re-sorting (count, scan, select): only
+    // the tiles holding pivots are read again, at most one per node.
+    template <int kW>
+    void select(PartArgs a) {
+        const u64 tiles = (a.src.n + kPartTile - 1) / kPartTile;
+        a.tiles = (u32)tiles;
+        a.chunk_counts = tile_counts;
+        const int bins = 1 << (a.l1 - a.l0);
+        const double rec = 4.0 * a.src.words;
+        timer.begin(kPartCountNames[width_slot(kW)], (double)a.src.n * rec);
+        k_part_count<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
+        timer.end();
+        timer.begin("k_chunk_scan", (double)tiles * bins * 8);
+        k_chunk_scan<<<bins, kBlock, 0, stream>>>(tile_counts, (i64)tiles, nullptr);
+        timer.end();
+        const u64 nodes = 1ull << a.l1;
+        const u64 read = (nodes < tiles ? nodes : tiles) * (u64)kPartTile;
+        timer.begin(kPartSelectNames[width_slot(kW)],
+                    (double)(read < (u64)a.src.n ? read : (u64)a.src.n) * rec);
+        k_part_select<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
+        timer.end();
+    }
+    void select_any(const PartArgs& a) {
+        switch (a.src.words) {
+            case 2: select<2>(a); break;
+            case 3: select<3>(a); break;
+            case 4: select<4>(a); break;
+            default: select<0>(a); break;
+        }
+    }
 };
 
 // Global rounds 0 .. lay.rounds-1 over all points: presorts each dimension
@@ -1871,10 +2015,36 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
             level_of[d] = 0;
         }
         // Bring A_d from the tags of its last use to the level-l tags, at
-        // most kMaxDescent levels per pass.
+        // most kMaxDescent levels per pass. The pass that reaches level l
+        // only selects the pivots (the array stays where it is) when A_d is
+        // not sorted again before the subtree stage, or when its next use
+        // can still walk from its current level in one pass of at most
+        // kSelectDepth levels; the last global round always re-sorts (the
+        // subtree stage reads its array).
         bool pivots_done = false;
         while (level_of[d] < l) {
             const int l1 = level_of[d] + kMaxDescent < l ? level_of[d] + kMaxDescent : l;
+            const int next_use = l + k;
+            if (l1 == l && l != R - 1 && (next_use >= R || next_use - level_of[d] <= kSelectDepth)) {
+                PartArgs a{};
+                a.src = RecordSource{pts, k, recs(buf_of[d]), W, n - (i64)full_nodes(level_of[d])};
+                a.k = k;
+                a.l0 = level_of[d];
+                a.l1 = l;
+                a.dim0 = level_of[d] % k;
+                a.geo = geo;
+                a.s0 = level_shape(geo, a.l0);
+                a.s1 = level_shape(geo, l);
+                a.piv = piv;
+                a.piv_out = piv;
+                a.dim1 = d;
+                a.s2 = level_shape(geo, l + 1);
+                a.perm = perm;
+                a.tree = tree;
+                launch.select_any(a);
+                pivots_done = true;
+                break;
+            }
             const int b = take(buf_of[d]);
             if (b < 0) return KDT_ERR_WORKSPACE;
             PartArgs a{};
@@ -2187,8 +2357,12 @@ kdt_status build_impl(const float* points, int64_t N, int32_t k, int32_t* perm_o
     // tree out
     const double row = 4.0 * k;
     const double in = l0 > 0 ? 4.0 * lay.words + 4.0 * (k - lay.kr) : row;
-    timer.begin("k_subtree", (double)below * (in + 2 * (4 + row) + 4 + (tree_out ? row : 0)));
-    k_subtree<<<(unsigned)(1ull << l0), kLocalBlock, 0, stream>>>(sa);
+    // records that carry every coordinate are read in place, else staged
+    const bool from_recs = recs && lay.words - 1 == k && k <= kCachedDims;
+    timer.begin(from_recs ? "k_subtree<true>" : "k_subtree<false>",
+                (double)below * (in + (from_recs ? 0.0 : 2 * (4 + row)) + 4 + (tree_out ? row : 0)));
+    if (from_recs) k_subtree<true><<<(unsigned)(1ull << l0), kLocalBlock, 0, stream>>>(sa);
+    else k_subtree<false><<<(unsigned)(1ull << l0), kLocalBlock, 0, stream>>>(sa);
     timer.end();
     return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
 }
