@@ -835,6 +835,7 @@ __global__ __launch_bounds__(kBlock) void k_part_count_widest(PartArgs a) { part
 // tile t holds the digit-b records counted from chunk_counts[b][t] up to
 // chunk_counts[b][t+1] (the last tile: all the rest). Only the level-l0
 // segments the tile overlaps can have their pivots in it.
+template <bool kNodeDims>
 __device__ bool tile_has_pivot(const PartArgs& a, u32 t) {
     const int delta = a.l1 - a.l0;
     const u32 bins = 1u << delta;
@@ -847,7 +848,12 @@ __device__ bool tile_has_pivot(const PartArgs& a, u32 t) {
     int hit = 0;
     for (u32 i = threadIdx.x; i < pairs; i += kBlock) {
         const u32 j0 = j_first + (i >> delta), b = i & (bins - 1);
-        const u32 target = bin_prefix32(a.s1, j0, b, delta) + subtree_size32(a.s2, 2 * ((j0 << delta) | b));
+        const u32 node = (j0 << delta) | b;
+        if (full_nodes(a.l1) + node >= (u64)a.geo.n) continue;  // past the last leaf
+        if constexpr (kNodeDims)  // another array's node
+            if (a.dimtab[full_nodes(a.l1) + node] != (uint16_t)a.array_dim) continue;
+        const u32 left = a.leaf_level ? 0u : subtree_size32(a.s2, 2 * node);
+        const u32 target = bin_prefix32(a.s1, j0, b, delta) + left;
         const u32* row = a.chunk_counts + (u64)b * a.tiles;
         if (target >= row[t] && (tail || target < row[t + 1])) hit = 1;
     }
@@ -863,7 +869,7 @@ __device__ __forceinline__ void part_scatter(const PartArgs& a) {
     const u32 t = xcd_tile(a.tiles);
     if (t >= a.tiles) return;
     if constexpr (kSelect)
-        if (!tile_has_pivot(a, t)) return;
+        if (!tile_has_pivot<kNodeDims>(a, t)) return;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const i64 wbase = (i64)t * kPartTile + (i64)w * (64 * kPartItems) + lane;
     const int delta = a.l1 - a.l0;
@@ -923,6 +929,8 @@ template <int kW>
 __global__ __launch_bounds__(kBlock) void k_part_scatter_widest(PartArgs a) { part_scatter<kW, true>(a); }
 template <int kW>
 __global__ __launch_bounds__(kBlock) void k_part_select(PartArgs a) { part_scatter<kW, false, true>(a); }
+template <int kW>
+__global__ __launch_bounds__(kBlock) void k_part_select_widest(PartArgs a) { part_scatter<kW, true, true>(a); }
 
 // Round l's nodes: the pivot of node s = F(l) + j is the record at live
 // position live_begin(j) + |S(2s+1)| of the array sorted for round l
@@ -1850,6 +1858,8 @@ const char* const kPartScatterNames[4] = {"k_part_scatter<0>", "k_part_scatter<2
                                           "k_part_scatter<3>", "k_part_scatter<4>"};
 const char* const kPartSelectNames[4] = {"k_part_select<0>", "k_part_select<2>", "k_part_select<3>",
                                          "k_part_select<4>"};
+const char* const kPartSelectWidestNames[4] = {"k_part_select_widest<0>", "k_part_select_widest<2>",
+                                               "k_part_select_widest<3>", "k_part_select_widest<4>"};
 const char* const kPartCountWidestNames[4] = {"k_part_count_widest<0>", "k_part_count_widest<2>",
                                               "k_part_count_widest<3>", "k_part_count_widest<4>"};
 const char* const kPartScatterWidestNames[4] = {"k_part_scatter_widest<0>", "k_part_scatter_widest<2>",
@@ -1935,17 +1945,20 @@ struct Launcher {
         a.chunk_counts = tile_counts;
         const int bins = 1 << (a.l1 - a.l0);
         const double rec = 4.0 * a.src.words;
-        timer.begin(kPartCountNames[width_slot(kW)], (double)a.src.n * rec);
-        k_part_count<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
+        const bool widest = a.dimtab != nullptr;  // split dimensions from the node table
+        timer.begin((widest ? kPartCountWidestNames : kPartCountNames)[width_slot(kW)], (double)a.src.n * rec);
+        if (widest) k_part_count_widest<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
+        else k_part_count<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
         timer.end();
         timer.begin("k_chunk_scan", (double)tiles * bins * 8);
         k_chunk_scan<<<bins, kBlock, 0, stream>>>(tile_counts, (i64)tiles, nullptr);
         timer.end();
         const u64 nodes = 1ull << a.l1;
         const u64 read = (nodes < tiles ? nodes : tiles) * (u64)kPartTile;
-        timer.begin(kPartSelectNames[width_slot(kW)],
+        timer.begin((widest ? kPartSelectWidestNames : kPartSelectNames)[width_slot(kW)],
                     (double)(read < (u64)a.src.n ? read : (u64)a.src.n) * rec);
-        k_part_select<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
+        if (widest) k_part_select_widest<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
+        else k_part_select<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
         timer.end();
     }
     void select_any(const PartArgs& a) {
@@ -2251,18 +2264,25 @@ kdt_status run_widest(const float* pts, i64 n, int k, const WidestLayout& wl, ch
         timer.end();
     }
     if (L > 1) level(1);
+    // Every level finds each array's nodes' pivots in that array. An array
+    // is re-sorted to the level only where that is cheaper than a select:
+    // not on the last level (no later level reads it), and not while the
+    // level has few nodes for the tiles (2^l <= tiles / 2) and the array's
+    // next walk stays within kSelectDepth levels.
+    const u64 tiles = ((u64)n + kPartTile - 1) / kPartTile;
+    std::vector<int> level_of(k, 0);
     for (int l = 1; l < L; ++l) {
         for (int d = 0; d < k; ++d) {
             PartArgs a{};
-            a.src = RecordSource{pts, k, recs(buffer[d]), W, n - (i64)full_nodes(l - 1)};
+            a.src = RecordSource{pts, k, recs(buffer[d]), W, n - (i64)full_nodes(level_of[d])};
             a.out = recs(spare);
             a.n_out = n - (i64)full_nodes(l);
             a.k = k;
-            a.l0 = l - 1;
+            a.l0 = level_of[d];
             a.l1 = l;
             a.dim0 = 0;
             a.geo = geo;
-            a.s0 = level_shape(geo, l - 1);
+            a.s0 = level_shape(geo, level_of[d]);
             a.s1 = level_shape(geo, l);
             a.piv = piv;
             a.piv_out = piv;
@@ -2273,8 +2293,14 @@ kdt_status run_widest(const float* pts, i64 n, int k, const WidestLayout& wl, ch
             a.dimtab = dimtab;
             a.array_dim = d;
             a.leaf_level = l == L - 1;
-            launch.part_any(a);
-            std::swap(buffer[d], spare);
+            const bool select = l == L - 1 || ((2ull << l) <= tiles && l + 1 - level_of[d] <= kSelectDepth);
+            if (select) {
+                launch.select_any(a);
+            } else {
+                launch.part_any(a);
+                std::swap(buffer[d], spare);
+                level_of[d] = l;
+            }
         }
         if (l + 1 < L) level(l + 1);
     }
