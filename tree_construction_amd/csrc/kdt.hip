@@ -1054,6 +1054,31 @@ __global__ __launch_bounds__(kBlock) void k_box_final(const float* __restrict__ 
     }
 }
 
+// A child's domain (2k floats: lo then hi) from its parent's domain `from`,
+// bounded at `plane` in the parent's dimension pd (pd < 0: the domain
+// itself); returns the dimension of its widest extent.
+__device__ __forceinline__ int child_domain(const float* from, int pd, float plane, bool left, int k,
+                                            float* box) {
+    int best = 0;
+    float best_extent = 0.0f;
+    for (int d = 0; d < k; ++d) {
+        float lo = from[d], hi = from[k + d];
+        if (d == pd) {
+            if (left) hi = plane;
+            else lo = plane;
+        }
+        box[d] = lo;
+        box[k + d] = hi;
+        const float extent = hi - lo;
+        if (d == 0) best_extent = extent;
+        else if (extent > best_extent) {
+            best = d;
+            best_extent = extent;
+        }
+    }
+    return best;
+}
+
 // Domains and split dimensions of the nodes of level l (2k floats a node:
 // lo then hi), from their parents' (the root's from the bounding box). The
 // parents' pivots are fixed.
@@ -1078,24 +1103,7 @@ __global__ __launch_bounds__(kBlock) void k_widest_level(Geometry geo, int l, in
         plane = __uint_as_float(key_bits((u32)(piv[p] >> 32)));  // a zero's sign is lost: extents agree
         left = s == 2 * p + 1;
     }
-    float* box = boxes + s * 2 * (u64)k;
-    int best = 0;
-    float best_extent = 0.0f;
-    for (int d = 0; d < k; ++d) {
-        float lo = from[d], hi = from[k + d];
-        if (d == pd) {
-            if (left) hi = plane;
-            else lo = plane;
-        }
-        box[d] = lo;
-        box[k + d] = hi;
-        const float extent = hi - lo;
-        if (d == 0) best_extent = extent;
-        else if (extent > best_extent) {
-            best = d;
-            best_extent = extent;
-        }
-    }
+    const int best = child_domain(from, pd, plane, left, k, boxes + s * 2 * (u64)k);
     dimtab[s] = (uint16_t)best;
     if (dims_out) dims_out[s] = best;
 }
@@ -1396,23 +1404,37 @@ __device__ __forceinline__ void local_order(KeyOf key_of, u32 nc, uint16_t* orde
 // most 2^(levels-t) - 1 points, so 8-bit counters would suffice wherever
 // 16-bit ones no longer fit the exchange buffer (with 4096-point subtrees
 // 16-bit ones always fit).
-template <typename Count>
+template <typename Count, bool kFilter = false>
 __device__ __forceinline__ void local_round(const uint16_t* order, u32 nc, int t, const Geometry& lg,
-                            LocalShared& sh) {
+                                            LocalShared& sh, const uint8_t* nodedim = nullptr, int dim = 0) {
     Count* seg_count = reinterpret_cast<Count*>(sh.exch);  // [kLocalWaves][2^t]
     const u32 fl = (u32)full_nodes(t);
     const int segs = 1 << t;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    for (int i = threadIdx.x; i < kLocalWaves * segs; i += kLocalBlock) seg_count[i] = 0;
+    // Counters are cleared and prefixed a word (4 / sizeof(Count) of them) at
+    // a time where a wave's row is whole words.
+    u32* words = reinterpret_cast<u32*>(sh.exch);
+    const int row_words = segs * (int)sizeof(Count) / 4;
+    const bool packed = segs * (int)sizeof(Count) % 4 == 0;
+    if (packed)
+        for (int i = threadIdx.x; i < kLocalWaves * row_words; i += kLocalBlock) words[i] = 0;
+    else
+        for (int i = threadIdx.x; i < kLocalWaves * segs; i += kLocalBlock) seg_count[i] = 0;
     __syncthreads();
     const u64 below = (1ull << lane) - 1;
     u32 seg[kLocalItems], rank[kLocalItems];
+    bool alive[kLocalItems];
 #pragma unroll
     for (int j = 0; j < kLocalItems; ++j) {
         const u32 q = (u32)local_slot(j);
         u32 st = fl;  // fixed points (tags < F(t)) are not ranked
         if (q < nc) st = sh.tag[order[q]];
-        const bool live = st >= fl && q < nc;
+        bool live = st >= fl && q < nc;
+        // kFilter: only the segments whose node splits `dim` (the others
+        // are ranked in their own dimension's order; points that an earlier
+        // sub-round of this level moved to a child are on level t+1)
+        if constexpr (kFilter) live = live && st < fl + (u32)segs && nodedim[st] == (uint8_t)dim;
+        alive[j] = live;
         const u32 b = live ? st - fl : 0;
         seg[j] = st;
         u32 miss_lo = 0, miss_hi = 0;
@@ -1425,12 +1447,26 @@ __device__ __forceinline__ void local_round(const uint16_t* order, u32 nc, int t
         if (live && before == 0) seg_count[w * segs + b] = (Count)(seen + __popcll(peers));
     }
     __syncthreads();
-    for (int b = threadIdx.x; b < segs; b += kLocalBlock) {
-        u32 run = 0;
-        for (int v = 0; v < kLocalWaves; ++v) {
-            const u32 c = seg_count[v * segs + b];
-            seg_count[v * segs + b] = (Count)run;
-            run += c;
+    if (packed) {
+        // Packed sums do not carry between counters: a segment's total is
+        // below 2^(8 sizeof(Count)) (16-bit: at most kLocalMax points; 8-bit
+        // counters are only used where segments hold at most 3).
+        for (int i = threadIdx.x; i < row_words; i += kLocalBlock) {
+            u32 run = 0;
+            for (int v = 0; v < kLocalWaves; ++v) {
+                const u32 c = words[v * row_words + i];
+                words[v * row_words + i] = run;
+                run += c;
+            }
+        }
+    } else {
+        for (int b = threadIdx.x; b < segs; b += kLocalBlock) {
+            u32 run = 0;
+            for (int v = 0; v < kLocalWaves; ++v) {
+                const u32 c = seg_count[v * segs + b];
+                seg_count[v * segs + b] = (Count)run;
+                run += c;
+            }
         }
     }
     __syncthreads();
@@ -1447,7 +1483,7 @@ __device__ __forceinline__ void local_round(const uint16_t* order, u32 nc, int t
     for (int j = 0; j < kLocalItems; ++j) {
         const u32 q = (u32)local_slot(j);
         const u32 s = seg[j];
-        if (q >= nc || s < fl) continue;
+        if (!alive[j]) continue;
         const u32 b = s - fl;
         const u32 in_segment = seg_count[w * segs + b] + rank[j];
         const u32 under = (2 * b) << dd;
@@ -1664,6 +1700,194 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
             for (int d = 0; d < a.k; ++d) {
                 const u32 key = a.stage[(u64)(d + 1) * a.n + first + e];
                 a.tree[(i64)g * a.k + d] = key == 0x80000000u ? a.pts[(i64)idx * a.k + d] : __uint_as_float(key_bits(key));
+            }
+        }
+    }
+}
+
+// ------------------------------- split-widest subtrees finished in LDS
+// The subtree stage for split-widest trees (k <= kCachedDims): the order of
+// every dimension is kept, and a level's nodes are ranked in one sub-round
+// per dimension, over that dimension's order and only for the segments
+// whose node splits it. After a level, the thread holding each node's pivot
+// derives the children's domains and split dimensions (child_domain, as on
+// the global levels). The subtree's records are A_0's on level l0 (in
+// (coordinate 0, index) order), or the rows themselves when the whole tree
+// is one subtree.
+struct WidestSubtreeArgs {
+    const float* pts;
+    i64 n;
+    int k;
+    int l0;                  // level of the subtree roots
+    Geometry geo;
+    const u32* recs;         // l0 > 0: A_0 on level l0 (k keys, then the index); nullptr: rows
+    int index_bytes;         // bytes of a point index that can differ
+    float* boxes;            // N x 2k domains: the roots' are there; the stage writes its nodes'
+    const uint16_t* dimtab;  // the roots' split dimensions
+    int32_t* perm;
+    float* tree;
+    int32_t* dims_out;
+};
+
+struct WidestShared : LocalShared {
+    uint8_t nodedim[kLocalMax];  // split dimension of each local node
+    u32 dim_mask[2];             // dimensions split on a level (by level parity)
+};
+
+__global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_widest(WidestSubtreeArgs a) {
+    __shared__ WidestShared sh;
+
+    const u64 c = full_nodes(a.l0) + blockIdx.x;  // subtree root (global node id)
+    const u32 nc = (u32)subtree_size(a.geo, c);
+    if (nc == 0) return;
+    const int k = a.k, words = k + 1;
+    const u64 first = a.recs ? live_begin(a.geo, c - full_nodes(a.l0), a.l0) : 0;
+    // Word f of the point at arrival position q: the key of coordinate f < k,
+    // or (f == k) its index.
+    auto word = [&](u32 q, int f) -> u32 {
+        if (a.recs) return a.recs[(first + q) * words + f];
+        return f == k ? q : float_key(__float_as_uint(a.pts[(i64)q * k + f]));
+    };
+
+    // Slot = index rank (rows arrive in index order already).
+    u64 rec[kLocalItems];
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) {
+        const u32 q = (u32)local_slot(j);
+        rec[j] = ~0ull;
+        if (q < nc) rec[j] = ((u64)word(q, k) << 16) | q;
+    }
+    if (a.recs) local_sort(rec, 16, a.index_bytes, nc, sh);
+    // The records arrived by (coordinate 0, index): arrival position -> slot
+    // is the order of dimension 0.
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) {
+        const int e = local_slot(j);
+        if ((u32)e >= nc) continue;
+        sh.tag[e] = 0;
+        if (a.recs) sh.order[0][rec[j] & 0xffff] = (uint16_t)e;
+    }
+    if (threadIdx.x == 0) {
+        sh.nodedim[0] = (uint8_t)a.dimtab[c];
+        sh.dim_mask[0] = 1u << a.dimtab[c];
+    }
+
+    auto slot_at = [&](u32 q) -> u32 { return a.recs ? sh.order[0][q] : q; };
+    // The other orders (every one for rows): keys read in arrival order,
+    // put at their slots in the exchange buffer, sorted.
+    for (int d = a.recs ? 1 : 0; d < k; ++d) {
+        __syncthreads();  // slots known; the buffer's last readers done
+#pragma unroll
+        for (int j = 0; j < kLocalItems; ++j) {
+            const u32 q = (u32)local_slot(j);
+            if (q < nc) sh.exch[slot_at(q)] = word(q, d);
+        }
+        __syncthreads();
+        local_order(ColumnKey{sh.exch}, nc, sh.order[d], sh);
+    }
+    __syncthreads();
+
+    const Geometry lg = make_geometry((i64)nc);
+    const int rounds = lg.levels - 1;
+    for (int t = 0; t < rounds; ++t) {
+        const u32 fl = (u32)full_nodes(t), fl1 = (u32)full_nodes(t + 1);
+        const u32 used = sh.dim_mask[t & 1];  // dimensions this level's nodes split
+        if (threadIdx.x == 0) sh.dim_mask[(t + 1) & 1] = 0;  // read a level ago; rounds' barriers follow
+        const bool small = (size_t)kLocalWaves * ((size_t)2 << t) <= sizeof(sh.exch);
+        for (int d = 0; d < k; ++d) {
+            if (!((used >> d) & 1u)) continue;
+            if (small) local_round<uint16_t, true>(sh.order[d], nc, t, lg, sh, sh.nodedim, d);
+            else local_round<uint8_t, true>(sh.order[d], nc, t, lg, sh, sh.nodedim, d);
+        }
+        // Level t's pivots carry their node's tag now: each one's thread
+        // bounds its node's domain at its coordinate for the two children.
+#pragma unroll
+        for (int j = 0; j < kLocalItems; ++j) {
+            const u32 q = (u32)local_slot(j);
+            if (q >= nc) continue;
+            const u32 s = sh.tag[slot_at(q)];
+            if (s < fl || s >= fl1) continue;
+            const int ds = sh.nodedim[s];
+            // the parent's domain and the plane, loaded together
+            const float* from = a.boxes + ((((c + 1) << t) - 1) + (s - fl)) * 2 * (u64)k;
+            float lo[kCachedDims], hi[kCachedDims];
+#pragma unroll
+            for (int d = 0; d < kCachedDims; ++d) {
+                lo[d] = d < k ? from[d] : 0.0f;
+                hi[d] = d < k ? from[k + d] : 0.0f;
+            }
+            const float plane = __uint_as_float(key_bits(word(q, ds)));  // a zero's sign: extents agree
+            for (u32 ch = 2 * s + 1; ch <= 2 * s + 2 && ch < nc; ++ch) {
+                const u64 g = (((c + 1) << (t + 1)) - 1) + (ch - fl1);
+                const bool left = ch == 2 * s + 1;
+                // child_domain's bounds and extents, in registers
+                float clo[kCachedDims], chi[kCachedDims];
+                int best = 0;
+                float best_extent = 0.0f;
+#pragma unroll
+                for (int d = 0; d < kCachedDims; ++d) {
+                    clo[d] = lo[d];
+                    chi[d] = hi[d];
+                    if (d == ds) {
+                        if (left) chi[d] = plane;
+                        else clo[d] = plane;
+                    }
+                    const float extent = chi[d] - clo[d];
+                    if (d == 0) best_extent = extent;
+                    else if (d < k && extent > best_extent) {
+                        best = d;
+                        best_extent = extent;
+                    }
+                }
+                if (t + 1 < rounds) {  // a parent in the next round: keep its domain
+                    float* box = a.boxes + g * 2 * (u64)k;
+#pragma unroll
+                    for (int d = 0; d < kCachedDims; ++d)
+                        if (d < k) {
+                            box[d] = clo[d];
+                            box[k + d] = chi[d];
+                        }
+                }
+                sh.nodedim[ch] = (uint8_t)best;
+                atomicOr(&sh.dim_mask[(t + 1) & 1], 1u << best);
+                if (a.dims_out) a.dims_out[g] = best;
+            }
+        }
+        __syncthreads();
+    }
+
+    // Level-order output, one record word at a time (the index first, then
+    // the keys): read in arrival order, put at its node in the exchange
+    // buffer, written out by node. A zero key is read back from the row.
+    u32 node_at[kLocalItems], idx_of[kLocalItems];
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) {
+        const u32 q = (u32)local_slot(j);
+        node_at[j] = q < nc ? sh.tag[slot_at(q)] : 0u;
+    }
+    const int words_out = a.tree ? words : 1;
+    for (int pass = 0; pass < words_out; ++pass) {
+        const int f = pass == 0 ? k : pass - 1;
+        __syncthreads();  // the buffer's last readers done
+#pragma unroll
+        for (int j = 0; j < kLocalItems; ++j) {
+            const u32 q = (u32)local_slot(j);
+            if (q < nc) sh.exch[node_at[j]] = word(q, f);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kLocalItems; ++i) {
+            const u32 node = threadIdx.x + (u32)i * kLocalBlock;
+            if (node >= nc) continue;
+            const int lvl = level_of(node);
+            const u64 g = ((c + 1) << lvl) - 1 + (node - full_nodes(lvl));
+            const u32 v = sh.exch[node];
+            if (pass == 0) {
+                idx_of[i] = v;
+                a.perm[g] = (int32_t)v;
+            } else {
+                a.tree[(i64)g * k + f] =
+                    v == 0x80000000u ? a.pts[(i64)idx_of[i] * k + f] : __uint_as_float(key_bits(v));
             }
         }
     }
@@ -2202,9 +2426,12 @@ kdt_status run_unique(const float* pts, i64 n, int k, const UniqueLayout& ul, ch
 // level), each fixing the nodes of the level that split its dimension, and
 // the next level's domains and dimensions from the pivots just fixed. The
 // last level's pass places the leaves.
+// Levels 0 .. lds_from-1 as global passes (every level when lds_from = L),
+// then, if lds_from < L, the subtrees of level lds_from in LDS (k <=
+// kCachedDims).
 kdt_status run_widest(const float* pts, i64 n, int k, const WidestLayout& wl, char* ws,
                       hipStream_t stream, Timer timer, int32_t* perm, float* tree,
-                      int32_t* dims_out) {
+                      int32_t* dims_out, int lds_from) {
     const Layout& lay = wl.base;
     const int L = lay.rounds, W = lay.words;
     const Geometry geo = make_geometry(n);
@@ -2236,6 +2463,33 @@ kdt_status run_widest(const float* pts, i64 n, int k, const WidestLayout& wl, ch
     timer.end();
     level(0);
 
+    auto subtrees = [&](const u32* arrival) {
+        WidestSubtreeArgs sa{};
+        sa.pts = pts;
+        sa.n = n;
+        sa.k = k;
+        sa.l0 = lds_from;
+        sa.geo = geo;
+        sa.recs = arrival;
+        int bits = 0;
+        for (u64 v = (u64)(n - 1); v; v >>= 1) ++bits;
+        sa.index_bytes = (bits + kRadixBits - 1) / kRadixBits;
+        sa.boxes = boxes;
+        sa.dimtab = dimtab;
+        sa.perm = perm;
+        sa.tree = tree;
+        sa.dims_out = dims_out;
+        const double below = (double)(n - (i64)full_nodes(lds_from));
+        timer.begin("k_subtree_widest", below * (4.0 * W + 4 + (tree ? 4.0 * k : 0) + (dims_out ? 4 : 0) +
+                                                 2 * 8.0 * k));
+        k_subtree_widest<<<(unsigned)(1ull << lds_from), kLocalBlock, 0, stream>>>(sa);
+        timer.end();
+    };
+    if (lds_from == 0) {  // the whole tree is one subtree, from the rows
+        subtrees(nullptr);
+        return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
+    }
+
     timer.begin("k_first_digits", (double)n * 5.0 * k);
     k_first_digits<<<grid_for(n, kBlock, 1 << 30), kBlock, 0, stream>>>(pts, n, k, k, digits0);
     timer.end();
@@ -2266,12 +2520,13 @@ kdt_status run_widest(const float* pts, i64 n, int k, const WidestLayout& wl, ch
     if (L > 1) level(1);
     // Every level finds each array's nodes' pivots in that array. An array
     // is re-sorted to the level only where that is cheaper than a select:
-    // not on the last level (no later level reads it), and not while the
-    // level has few nodes for the tiles (2^l <= tiles / 2) and the array's
-    // next walk stays within kSelectDepth levels.
+    // not where no later pass reads it (the last level; on the last global
+    // level, every array but A_0, which the subtree stage reads), and not
+    // while the level has few nodes for the tiles (2^l <= tiles / 2) and
+    // the array's next walk stays within kSelectDepth levels.
     const u64 tiles = ((u64)n + kPartTile - 1) / kPartTile;
     std::vector<int> level_of(k, 0);
-    for (int l = 1; l < L; ++l) {
+    for (int l = 1; l < lds_from; ++l) {
         for (int d = 0; d < k; ++d) {
             PartArgs a{};
             a.src = RecordSource{pts, k, recs(buffer[d]), W, n - (i64)full_nodes(level_of[d])};
@@ -2293,7 +2548,8 @@ kdt_status run_widest(const float* pts, i64 n, int k, const WidestLayout& wl, ch
             a.dimtab = dimtab;
             a.array_dim = d;
             a.leaf_level = l == L - 1;
-            const bool select = l == L - 1 || ((2ull << l) <= tiles && l + 1 - level_of[d] <= kSelectDepth);
+            const bool unread = lds_from == L ? l == L - 1 : l == lds_from - 1 && d != 0;
+            const bool select = unread || ((2ull << l) <= tiles && l + 1 - level_of[d] <= kSelectDepth);
             if (select) {
                 launch.select_any(a);
             } else {
@@ -2303,6 +2559,26 @@ kdt_status run_widest(const float* pts, i64 n, int k, const WidestLayout& wl, ch
             }
         }
         if (l + 1 < L) level(l + 1);
+    }
+    if (lds_from < L) {
+        // A_0 to level lds_from (no pivots: the subtree stage fixes that
+        // level's nodes), so that each subtree's records are one range.
+        PartArgs a{};
+        a.src = RecordSource{pts, k, recs(buffer[0]), W, n - (i64)full_nodes(level_of[0])};
+        a.out = recs(spare);
+        a.n_out = n - (i64)full_nodes(lds_from);
+        a.k = k;
+        a.l0 = level_of[0];
+        a.l1 = lds_from;
+        a.geo = geo;
+        a.s0 = level_shape(geo, level_of[0]);
+        a.s1 = level_shape(geo, lds_from);
+        if (lds_from + 1 < L) a.s2 = level_shape(geo, lds_from + 1);
+        a.piv = piv;
+        a.dimtab = dimtab;
+        launch.part_any(a);
+        std::swap(buffer[0], spare);
+        subtrees(recs(buffer[0]));
     }
     return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
 }
@@ -2420,7 +2696,11 @@ kdt_status build_widest_impl(const float* points, int64_t N, int32_t k, int32_t*
         if (dims_out) k_zero<<<1, kBlock, 0, stream>>>(reinterpret_cast<u32*>(dims_out), 1);
         return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
     }
-    return run_widest(points, N, k, wl, (char*)workspace, stream, timer, perm_out, tree_out, dims_out);
+    // Subtrees of at most kLocalMax points finish in LDS when every
+    // dimension's order fits there.
+    const int lds_from = k <= kCachedDims ? split_level(N) : wl.base.rounds;
+    return run_widest(points, N, k, wl, (char*)workspace, stream, timer, perm_out, tree_out, dims_out,
+                      lds_from);
 }
 
 kdt_status unique_impl(const float* points, int64_t N, int32_t k, int32_t* keep_out, int64_t* count_out,
