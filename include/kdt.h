@@ -23,8 +23,10 @@
  * the point's node, so a round re-sorts its dimension's array by the new
  * tags with one stable radix pass whose digit is the point's path down the
  * pivots of the levels since that array was last sorted; the pivots of the
- * round then sit at closed-form positions. Subtrees of at most 4096 points
- * finish their remaining rounds inside one workgroup's LDS.
+ * round then sit at closed-form positions. A round whose array is not
+ * needed in that order again only locates its pivots (counts, then the
+ * tiles that hold them). Subtrees of at most 4096 points finish their
+ * remaining rounds inside one workgroup's LDS.
  *
  * Conventions for every entry point:
  *   - All pointers marked "device" are HIP device pointers on the current
@@ -155,8 +157,10 @@ int64_t kdt_closed_bin_prefix(int64_t N, int32_t l1, int32_t delta, int64_t j0, 
  *   dims_out  device, N int32 or NULL: dims_out[s] = split dimension of
  *             node s (every node, leaves included).
  * Other arguments, ownership and errors as kdt_build; the workspace is
- * kdt_workspace_size_widest(N, k) bytes. Every level runs as a global pass
- * over all points here, so a build costs more than kdt_build's. */
+ * kdt_workspace_size_widest(N, k) bytes. Every array finds its own nodes'
+ * pivots on every global level, and for k <= 3 subtrees of at most 4096
+ * points finish in LDS (for larger k every level is a global pass), so a
+ * build costs more than kdt_build's. */
 size_t kdt_workspace_size_widest(int64_t N, int32_t k);
 kdt_status kdt_build_widest(const float* points, int64_t N, int32_t k,
                             int32_t* perm_out, float* tree_out, int32_t* dims_out,
