@@ -66,6 +66,10 @@ constexpr int kMaxDescent = kRadixBits;    // levels one re-sort pass walks
 #endif
 constexpr int kSelectDepth = KDT_SELECT_DEPTH;  // deepest walk a round may leave to the array's next re-sort
 static_assert(kSelectDepth <= kMaxDescent, "one pass per walk");
+#ifndef KDT_PLAIN_DELTA
+#define KDT_PLAIN_DELTA 4
+#endif
+constexpr int kPlainDelta = KDT_PLAIN_DELTA;  // re-sort walks from which the scatter stores plainly
 constexpr int kMaxRounds = 32;             // global rounds (levels) at most
 static_assert(kBlock == kRadix, "the tile kernels map one thread to one digit");
 
@@ -423,6 +427,21 @@ struct RecordTile {
         } else {
             u32* dst = out + pos * s.words;
             for (int w = 0; w < s.words; ++w) dst[w] = source_word<kSrc>(s, (u64)e, w);
+        }
+    }
+    // Plain stores: where a wave's stores land in many short runs, the
+    // pieces of a line meet in L2 before it is written back.
+    __device__ __forceinline__ void store_plain(const RecordSource& s, u32* out, int j, i64 e, u64 pos) const {
+        if constexpr (kW == 4) {
+            *reinterpret_cast<uint4*>(out + pos * 4) = make_uint4(w0[j], w1[j], w2[j], w3[j]);
+        } else if constexpr (kW == 3) {
+            out[pos * 3] = w0[j];
+            out[pos * 3 + 1] = w1[j];
+            out[pos * 3 + 2] = w2[j];
+        } else if constexpr (kW == 2) {
+            *reinterpret_cast<uint2*>(out + pos * 2) = make_uint2(w0[j], w1[j]);
+        } else {
+            store(s, out, j, e, pos);
         }
     }
 };
@@ -906,7 +925,12 @@ __device__ __forceinline__ void part_scatter(const PartArgs& a) {
         const i64 e = wbase + (i64)j * 64;
         if constexpr (!kSelect) {
             const u32 pos = live_begin32(a.s1, node[j]) + in_segment;
-            if (pos < (u64)a.n_out) tr.store(a.src, a.out, j, e, pos);
+            if (pos < (u64)a.n_out) {
+                // non-temporal while a wave's records fall in few runs, plain
+                // once the walk spreads them over 2^kPlainDelta or more
+                if (delta >= kPlainDelta) tr.store_plain(a.src, a.out, j, e, pos);
+                else tr.store(a.src, a.out, j, e, pos);
+            }
         }
         const u32 left = a.leaf_level ? 0u : subtree_size32(a.s2, 2 * node[j]);
         bool mine = true;  // the node splits this array's dimension
