@@ -93,6 +93,18 @@ def test_random_small_sweep(torch_dev):
         assert_same_tree(pts, perm, tree, oracle.build_tree(pts), "trial %d" % trial)
 
 
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 7])
+def test_select_rounds_many_levels(torch_dev, k):
+    """Builds deep enough (300,000 points: 6 global rounds, up to 18 levels)
+    that rounds only locate their pivots and later re-sorts walk up to six
+    levels, for several dimension cycles."""
+    for gen in ("gmm", "ties", "zeros"):
+        pts = make(gen, 300000, k, 70 + k)
+        say("case select rounds gen=%s N=300000 k=%d" % (gen, k))
+        perm, tree = gpu_build(torch_dev, pts)
+        assert_same_tree(pts, perm, tree, oracle.build_tree(pts), "%s k=%d" % (gen, k))
+
+
 def test_worked_example(torch_dev):
     from test_oracle_pins import load_worked_example
     pts, expected = load_worked_example()

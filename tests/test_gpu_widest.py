@@ -84,6 +84,19 @@ def test_widest_sizes(torch_dev, gen):
         assert_same(pts, perm, tree, dims, "%s N=%d k=%d" % (gen, n, k), check=gen != "special")
 
 
+@pytest.mark.parametrize("k", [1, 2, 3])
+def test_widest_lds_stage(torch_dev, k):
+    """For k <= 3 subtrees of at most 4096 points finish in LDS: one subtree
+    read from the rows (N <= 4096) or records on levels 1 .. 7 below the
+    global levels, with every kind of tie."""
+    for gen in ("gmm", "ties", "zeros", "equal", "skewed"):
+        for n in (4095, 4096, 4097, 12289, 300000):
+            pts = make(gen, n, k, 900 + n % 97 + k)
+            say("case widest lds gen=%s N=%d k=%d" % (gen, n, k))
+            perm, tree, dims = gpu_widest(torch_dev, pts)
+            assert_same(pts, perm, tree, dims, "%s N=%d k=%d" % (gen, n, k))
+
+
 def test_widest_hand_example(torch_dev):
     from test_widest_oracle import load_hand_example
     pts, perm, dims = load_hand_example()
