@@ -176,7 +176,10 @@ kdt_status kdt_build_widest_profiled(const float* points, int64_t N, int32_t k,
 /* Duplicate removal, the optional pre-pass of J. Robinson's KdTreeGPU
  * wiki (duplicate-removal section): tuples equal in every coordinate
  * (IEEE '==', so -0.0 equals +0.0) collapse to one. Of each group of equal
- * tuples the one with the smallest original index is kept.
+ * tuples the one with the smallest original index is kept. The GPU sorts
+ * (32-bit tuple hash, index) pairs, so equal tuples meet in index order,
+ * and compares coordinates exactly inside runs of equal hashes: distinct
+ * tuples that share a hash cost time, never a wrong answer.
  *   points     device, N*k float32, row-major. Read only.
  *   keep_out   device, N int32: its first *count_out entries are the kept
  *              indices, ascending; the rest are unspecified.

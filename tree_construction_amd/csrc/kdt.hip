@@ -410,6 +410,15 @@ struct RecordTile {
             return v;
         }
     }
+    // Word kI of item j, chosen at compile time.
+    template <int kI>
+    __device__ __forceinline__ u32 at(int j) const {
+        static_assert(kI >= 0 && kI < 4, "word");
+        if constexpr (kI == 0) return w0[j];
+        else if constexpr (kI == 1) return w1[j];
+        else if constexpr (kI == 2) return w2[j];
+        else return w3[j];
+    }
     __device__ __forceinline__ uint4 quad(int j) const { return make_uint4(w0[j], w1[j], w2[j], w3[j]); }
     // Non-temporal stores: the output is read by a later pass, not this one,
     // and write-backs of dirty lines would otherwise land in the next pass.
@@ -610,6 +619,7 @@ __global__ __launch_bounds__(kSortBlock) void k_sort_scatter(SortArgs a) {
     __shared__ union {
         u32 count[kSortWaves][kRadix];  // ranking: per-wave digit counts, then prefixes
         uint4 quads[kW == 4 ? kSortTile : 1];  // staging of the sorted tile
+        uint2 pairs[kW == 2 ? kSortTile : 1];
         u32 words[kSortTile];
     } sm;
     __shared__ u8 s_digit[kSortTile];
@@ -690,6 +700,18 @@ __global__ __launch_bounds__(kSortBlock) void k_sort_scatter(SortArgs a) {
                               (q.z & (a.next_dim == 2 ? ~0u : 0u));
                 a.next_digits[dst] = (u8)(c >> a.next_shift);
             }
+        }
+    } else if constexpr (kW == 2) {
+#pragma unroll
+        for (int j = 0; j < kPartItems; ++j)
+            if (valid[j]) sm.pairs[rank[j]] = make_uint2(tr.template at<0>(j), tr.template at<1>(j));
+        __syncthreads();
+        for (int i = tid; i < valid_here; i += kSortBlock) {
+            const u32 dst = s_base[s_digit[i]] + (u32)i;
+            if (dst >= (u64)a.src.n) continue;
+            const uint2 v = sm.pairs[i];
+            *reinterpret_cast<uint2*>(a.out + (u64)dst * 2) = v;
+            if (a.next_digits) a.next_digits[dst] = (u8)((a.next_dim == 0 ? v.x : v.y) >> a.next_shift);
         }
     } else {
         // one word of every record per staging round
@@ -1144,18 +1166,68 @@ constexpr int kFlagItems = 16;                  // flags per thread (one 16-byte
 constexpr int kFlagTile = kBlock * kFlagItems;  // flags per compaction workgroup
 
 // keep[idx] = 1 for the first record of every run of equal tuples, else 0.
-__global__ __launch_bounds__(kBlock) void k_unique_mark(const u32* __restrict__ recs, i64 n, int words,
+// Equal tuples hash equally: MurmurHash3's 32-bit finaliser chained over the
+// coordinate keys (zeros canonical, so -0.0 and +0.0 agree).
+__device__ __forceinline__ u32 fmix32(u32 h) {
+    h ^= h >> 16;
+    h *= 0x85ebca6bu;
+    h ^= h >> 13;
+    h *= 0xc2b2ae35u;
+    h ^= h >> 16;
+    return h;
+}
+
+__device__ __forceinline__ u32 tuple_hash(const float* __restrict__ pts, int k, i64 i) {
+    u32 h = 0x9e3779b9u;
+    for (int d = 0; d < k; ++d) h = fmix32(h ^ float_key(__float_as_uint(pts[i * k + d])));
+    return h;
+}
+
+// Records (hash, index) in index order, and the low hash byte (the first
+// sort pass's digit).
+__global__ __launch_bounds__(kBlock) void k_hash_records(const float* __restrict__ pts, i64 n, int k,
+                                                         u32* __restrict__ recs, u8* __restrict__ digits) {
+    const i64 stride = (i64)gridDim.x * kBlock;
+    for (i64 i = (i64)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride) {
+        const u32 h = tuple_hash(pts, k, i);
+        *reinterpret_cast<uint2*>(recs + 2 * i) = make_uint2(h, (u32)i);
+        digits[i] = (u8)h;
+    }
+}
+
+// Whether points a and b are the same tuple (keys: equal iff the floats are).
+__device__ __forceinline__ bool same_tuple(const float* __restrict__ pts, int k, u32 a, u32 b) {
+    for (int d = 0; d < k; ++d)
+        if (float_key(__float_as_uint(pts[(i64)a * k + d])) != float_key(__float_as_uint(pts[(i64)b * k + d])))
+            return false;
+    return true;
+}
+
+// keep[0 .. n) = 1, a 32-bit word at a time (the buffer is padded to 4).
+__global__ __launch_bounds__(kBlock) void k_keep_all(u32* __restrict__ keep_words, i64 words) {
+    const i64 stride = (i64)gridDim.x * kBlock;
+    for (i64 i = (i64)blockIdx.x * kBlock + threadIdx.x; i < words; i += stride) keep_words[i] = 0x01010101u;
+}
+
+// Run heads of the records sorted by (hash, index): a point is kept when no
+// earlier record of its equal-hash run (a smaller index) holds the same
+// tuple. The scan back stops at the first equal tuple, so a run of copies
+// costs one comparison per record; only distinct tuples that share a hash
+// compare further. keep[index] = 0 for the points that are not kept (keep
+// starts all ones), so only duplicates cost a scattered store.
+__global__ __launch_bounds__(kBlock) void k_unique_mark(const u32* __restrict__ recs, i64 n,
+                                                        const float* __restrict__ pts, int k,
                                                         u8* __restrict__ keep) {
-    const int k = words - 1;
     const i64 stride = (i64)gridDim.x * kBlock;
     for (i64 r = (i64)blockIdx.x * kBlock + threadIdx.x; r < n; r += stride) {
-        const u32* me = recs + r * words;
-        bool head = r == 0;
-        if (!head) {
-            const u32* prev = me - words;
-            for (int d = 0; d < k && !head; ++d) head = me[d] != prev[d];  // keys: equal iff the floats are
-        }
-        keep[me[k]] = head ? 1 : 0;
+        const uint2 me = *reinterpret_cast<const uint2*>(recs + 2 * r);
+        bool head = true;
+        for (i64 p = r - 1; p >= 0 && recs[2 * p] == me.x; --p)
+            if (same_tuple(pts, k, me.y, recs[2 * p + 1])) {
+                head = false;
+                break;
+            }
+        if (!head) keep[me.y] = 0;
     }
 }
 
@@ -1187,21 +1259,29 @@ __global__ __launch_bounds__(kBlock) void k_flag_count(const u8* __restrict__ ke
 }
 
 // Writes the kept indices of one tile at their places (prefix: kept indices
-// in the tiles before, from k_chunk_scan), and the total to *count_out.
+// in the tiles before, from k_chunk_scan), and the total to *count_out. The
+// tile's kept indices are gathered in LDS first, so that consecutive
+// threads write consecutive entries.
 __global__ __launch_bounds__(kBlock) void k_flag_compact(const u8* __restrict__ keep, i64 n,
                                                          const u32* __restrict__ prefix,
                                                          const u32* __restrict__ totals,
                                                          int32_t* __restrict__ keep_out,
                                                          int64_t* __restrict__ count_out) {
     __shared__ u32 s_wave[kWaves];
+    __shared__ int32_t s_kept[kFlagTile];
+    __shared__ u32 s_total;
     const i64 first = (i64)blockIdx.x * kFlagTile + (i64)threadIdx.x * kFlagItems;
     u32 w[4];
     load_flags(keep, n, first, w);
     const u32 mine = __popc(w[0]) + __popc(w[1]) + __popc(w[2]) + __popc(w[3]);
-    u32 at = prefix[blockIdx.x] + block_exclusive_scan(mine, s_wave);
+    u32 at = block_exclusive_scan(mine, s_wave);
+    if (threadIdx.x == kBlock - 1) s_total = at + mine;
 #pragma unroll
     for (int j = 0; j < kFlagItems; ++j)
-        if ((w[j >> 2] >> (8 * (j & 3))) & 1u) keep_out[at++] = (int32_t)(first + j);
+        if ((w[j >> 2] >> (8 * (j & 3))) & 1u) s_kept[at++] = (int32_t)(first + j);
+    __syncthreads();
+    const u32 base = prefix[blockIdx.x], total = s_total;
+    for (u32 i = threadIdx.x; i < total; i += kBlock) keep_out[base + i] = s_kept[i];
     if (blockIdx.x == 0 && threadIdx.x == 0) *count_out = (int64_t)totals[0];
 }
 
@@ -2350,8 +2430,9 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
     return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
 }
 
-// Workspace of duplicate removal: the presort's buffers for records of all k
-// coordinates, one flag per point, and the compaction's tile counts.
+// Workspace of duplicate removal: two buffers of (tuple hash, index) records
+// and the sort's digits and counts, one flag per point, and the
+// compaction's tile counts.
 struct UniqueLayout {
     Layout base;
     size_t keep, flag_counts;
@@ -2372,14 +2453,13 @@ bool make_layout_unique(i64 n, int k, UniqueLayout* out) {
         return at;
     };
     Layout& lay = u.base;
-    lay.kr = k;
-    lay.words = k + 1;
+    lay.kr = 1;
+    lay.words = 2;  // (tuple hash, index)
     lay.tiles = (n + kPartTile - 1) / kPartTile;
     const size_t rec_bytes = (size_t)n * lay.words * sizeof(u32);
     lay.tmp0 = take(rec_bytes);
     lay.tmp1 = take(rec_bytes);
     lay.digits = take((size_t)n);
-    lay.digits0 = take((size_t)k * n);
     lay.totals = take((size_t)kRadix * sizeof(u32));
     lay.slots = take((size_t)lay.tiles * kRadix * sizeof(u32));
     lay.chunk_slots = take((size_t)((lay.tiles + kChunkTiles - 1) / kChunkTiles) * kRadix * sizeof(u32));
@@ -2391,45 +2471,46 @@ bool make_layout_unique(i64 n, int k, UniqueLayout* out) {
     return true;
 }
 
-// Duplicate removal: stable LSD radix passes over the keys of coordinates
-// k-1, ..., 0 (4 passes each; each pass also writes the next pass's digit
-// byte, across a change of coordinate too), then the run heads, then the
-// compaction in index order.
+// Duplicate removal: the points' (tuple hash, index) records sorted by hash
+// with 4 stable LSD radix passes (equal tuples then sit together, in index
+// order), the run heads with exact comparisons inside equal-hash runs, then
+// the compaction in index order.
 kdt_status run_unique(const float* pts, i64 n, int k, const UniqueLayout& ul, char* ws,
                       hipStream_t stream, Timer timer, int32_t* keep_out, int64_t* count_out) {
     const Layout& lay = ul.base;
     const int W = lay.words;
     u32* tmp[2] = {(u32*)(ws + lay.tmp0), (u32*)(ws + lay.tmp1)};
     u8* digits = (u8*)(ws + lay.digits);
-    u8* digits0 = (u8*)(ws + lay.digits0);
     u32* totals = (u32*)(ws + lay.totals);
     u8* keep = (u8*)(ws + ul.keep);
     u32* flag_counts = (u32*)(ws + ul.flag_counts);
     Launcher launch{(u32*)(ws + lay.slots), (u32*)(ws + lay.chunk_slots), totals, stream, timer};
 
-    timer.begin("k_first_digits", (double)n * 5.0 * k);
-    k_first_digits<<<grid_for(n, kBlock, 1 << 30), kBlock, 0, stream>>>(pts, n, k, k, digits0);
+    timer.begin("k_hash_records", (double)n * (4.0 * k + 9));
+    k_hash_records<<<grid_for(n, kBlock, 1 << 16), kBlock, 0, stream>>>(pts, n, k, tmp[1], digits);
     timer.end();
-    int pass = 0;
+    // (hash, index) records by hash, stably from index order: 4 LSD passes,
+    // tmp[1] -> tmp[0] -> tmp[1] -> tmp[0] -> tmp[1]
     const u32* sorted = nullptr;
-    for (int d = k - 1; d >= 0; --d)
-        for (int p = 0; p < kKeyBytes; ++p, ++pass) {
-            SortArgs a{};
-            a.src = RecordSource{pts, k, pass == 0 ? nullptr : tmp[(pass + 1) & 1], W, n};
-            a.out = tmp[pass & 1];
-            a.dim = d;
-            a.shift = 8 * p;
-            a.digits = pass == 0 ? digits0 + (size_t)(k - 1) * n : digits;
-            const bool last = d == 0 && p == kKeyBytes - 1;
-            a.next_digits = last ? nullptr : digits;
-            a.next_dim = p + 1 < kKeyBytes ? d : d - 1;
-            a.next_shift = p + 1 < kKeyBytes ? 8 * (p + 1) : 0;
-            if (pass == 0) launch.sort_any<kSrcRows>(a);
-            else launch.sort_any<kSrcRecords>(a);
-            sorted = a.out;
-        }
-    timer.begin("k_unique_mark", (double)n * (8.0 * W + 1));
-    k_unique_mark<<<grid_for(n, kBlock, 1 << 16), kBlock, 0, stream>>>(sorted, n, W, keep);
+    for (int p = 0; p < kKeyBytes; ++p) {
+        SortArgs a{};
+        a.src = RecordSource{pts, k, tmp[(p + 1) & 1], W, n};
+        a.out = tmp[p & 1];
+        a.dim = 0;
+        a.shift = 8 * p;
+        a.digits = digits;
+        a.next_digits = p + 1 < kKeyBytes ? digits : nullptr;
+        a.next_dim = 0;
+        a.next_shift = 8 * (p + 1);
+        launch.sort_any<kSrcRecords>(a);
+        sorted = a.out;
+    }
+    timer.begin("k_keep_all", (double)n);
+    k_keep_all<<<grid_for((n + 3) / 4, kBlock, 1 << 16), kBlock, 0, stream>>>(reinterpret_cast<u32*>(keep),
+                                                                             (n + 3) / 4);
+    timer.end();
+    timer.begin("k_unique_mark", (double)n * 4.0 * W);
+    k_unique_mark<<<grid_for(n, kBlock, 1 << 16), kBlock, 0, stream>>>(sorted, n, pts, k, keep);
     timer.end();
     const i64 T = ul.flag_tiles;
     timer.begin("k_flag_count", (double)n + 4.0 * T);
