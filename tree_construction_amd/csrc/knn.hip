@@ -43,6 +43,7 @@ typedef uint64_t u64;
 typedef int64_t i64;
 
 constexpr int kKnnBlock = 256;
+constexpr int kPathRegs = 8;  // split offsets of the deepest path nodes a search thread keeps
 constexpr int kKnnMaxK = 32;       // neighbours per query at most
 // Points one first-pass thread examines before handing its query over:
 // max(256, 64 K), a few times the 99th percentile of a typical search (the
@@ -208,6 +209,11 @@ __global__ __launch_bounds__(kKnnBlock) void k_knn(KnnArgs a) {
         // prev: the node the thread arrived from (~0 = from above the root)
         u32 curr = 0, prev = ~0u;
         int dim = 0;  // split dimension of curr's level
+        // The split offsets (query - plane) of the nodes on the current path,
+        // innermost first, for its deepest kPathRegs nodes: coming back up
+        // to one of them needs no second load of its row.
+        float path[kPathRegs];
+        int held = 0;
         for (;;) {
             if (curr >= n) {  // a child that does not exist: back to its parent
                 prev = curr;
@@ -216,13 +222,7 @@ __global__ __launch_bounds__(kKnnBlock) void k_knn(KnnArgs a) {
                 continue;
             }
             const u32 parent = curr == 0 ? ~0u : (curr - 1) >> 1;
-            NodeRow<kDims> node;
-            node.load(a.tree, curr, k);
-            const int split = a.dims ? a.dims[curr] : dim;
-            const float diff = q.at(split) - node.at(split);
             const u32 left = 2 * curr + 1;
-            const u32 near = diff < 0.0f ? left : left + 1;
-            const u32 far = diff < 0.0f ? left + 1 : left;
             const int down = dim + 1 == k ? 0 : dim + 1;
             if (prev == parent) {
                 // first visit: the node's point is a candidate; go to the
@@ -232,22 +232,48 @@ __global__ __launch_bounds__(kKnnBlock) void k_knn(KnnArgs a) {
                     break;
                 }
                 ++visits;
+                NodeRow<kDims> node;
+                node.load(a.tree, curr, k);
+                const int split = a.dims ? a.dims[curr] : dim;
+                const float diff = q.at(split) - node.at(split);
                 const u32 bits = __float_as_uint(squared_distance<kDims>(q, node, k));
                 if (bits <= best.worst_bits()) {
                     const u64 key = ((u64)bits << 32) | (u32)a.perm[curr];
                     if (key < best.slot[0]) best.insert(key);
                 }
+#pragma unroll
+                for (int i = kPathRegs - 1; i > 0; --i) path[i] = path[i - 1];
+                path[0] = diff;
+                held = held < kPathRegs ? held + 1 : kPathRegs;
                 prev = curr;
-                curr = near;
+                curr = diff < 0.0f ? left : left + 1;
                 dim = down;
                 continue;
             }
+            // back from a child: curr's offset, held or read again
+            float diff;
+            if (held > 0) {
+                diff = path[0];
+            } else {
+                NodeRow<kDims> node;
+                node.load(a.tree, curr, k);
+                const int split = a.dims ? a.dims[curr] : dim;
+                diff = q.at(split) - node.at(split);
+                path[0] = diff;
+                held = 1;
+            }
+            const u32 near = diff < 0.0f ? left : left + 1;
+            const u32 far = diff < 0.0f ? left + 1 : left;
             if (prev == near && far < n && __float_as_uint(diff * diff) <= best.worst_bits()) {
                 prev = curr;
                 curr = far;
                 dim = down;
                 continue;
             }
+            // leaving curr upwards
+#pragma unroll
+            for (int i = 0; i < kPathRegs - 1; ++i) path[i] = path[i + 1];
+            --held;
             if (curr == 0) break;
             prev = curr;
             curr = parent;
