@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of the k-d tree build on one MI355X.
 
-One step = one complete build (every round's radix passes and tag updates,
-the column copy and the level-order placement) of the headline workload:
+One step = one complete build (every round's radix passes or pivot
+selections, and the subtree stage with its level-order output) of the
+headline workload:
 N = 16,777,216 points, k = 3, float32, from a 64-component Gaussian mixture
 with 5% of coordinates snapped to a 2^-10 grid (seed 3). Inputs, outputs and
 the workspace are resident in HBM before the timed region starts.
