@@ -273,8 +273,10 @@ __device__ inline u64 block_exclusive_scan64(u64 v, u64* s_wave) {
 __device__ inline void match_bit(u32 d, int b, u32& miss_lo, u32& miss_hi) {
     const u32 m = (u32)__builtin_amdgcn_sbfe((int)d, b, 1);
     const u64 vote = __ballot(m != 0);
-    miss_lo |= (u32)vote ^ m;
-    miss_hi |= (u32)(vote >> 32) ^ m;
+    // miss |= vote ^ m, one three-input bit operation per half (truth
+    // table 0xF6 over (miss, vote, m), miss the most significant input)
+    miss_lo = __builtin_amdgcn_bitop3_b32(miss_lo, (u32)vote, m, 0xF6);
+    miss_hi = __builtin_amdgcn_bitop3_b32(miss_hi, (u32)(vote >> 32), m, 0xF6);
 }
 
 // Rank inside the wave of each of this thread's records by its digit
