@@ -1341,19 +1341,6 @@ __device__ inline int local_slot(int j) {
     return (threadIdx.x >> 6) * (64 * kLocalItems) + j * 64 + (threadIdx.x & 63);
 }
 
-__device__ inline u32 local_exclusive_scan(u32 v, u32* s_wave) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    u32 inc = wave_inclusive_scan(v);
-    if (lane == 63) s_wave[w] = inc;
-    __syncthreads();
-    u32 off = 0;
-#pragma unroll
-    for (int i = 0; i < kLocalWaves; ++i)
-        if (i < w) off += s_wave[i];
-    __syncthreads();
-    return off + inc - v;
-}
-
 // Mask of key bits on which the records (all of the workgroup's valid
 // ones) disagree; a radix pass over a byte outside it would not move
 // anything and is skipped.
