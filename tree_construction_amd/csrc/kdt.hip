@@ -775,7 +775,16 @@ struct PartArgs {
     const uint16_t* dimtab;
     int array_dim;
     int leaf_level;
+    // Select passes of split-widest trees: bit d of level_dims[l1] says some
+    // level-l1 node splits dimension d (nullptr: do not skip); without one
+    // for array_dim the pass has no pivot to find and its kernels return.
+    const u32* level_dims;
 };
+
+// Whether a select pass of a split-widest tree has nothing to do.
+__device__ __forceinline__ bool no_nodes_here(const PartArgs& a) {
+    return a.level_dims && !((a.level_dims[a.l1] >> a.array_dim) & 1u);
+}
 
 // For every item: node[j], the in-level index of its node on level l1,
 // which is (j0 << delta) | digit for its level-l0 segment j0 and its digit
@@ -834,6 +843,8 @@ __device__ __forceinline__ void part_count(const PartArgs& a) {
     __shared__ u32 hist[kWaves][kRadix];
     const u32 t = xcd_tile(a.tiles);
     if (t >= a.tiles) return;
+    if constexpr (kNodeDims)
+        if (no_nodes_here(a)) return;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const i64 wbase = (i64)t * kPartTile + (i64)w * (64 * kPartItems) + lane;
     const int bins = 1 << (a.l1 - a.l0);
@@ -911,8 +922,11 @@ __device__ __forceinline__ void part_scatter(const PartArgs& a) {
     __shared__ u32 count[kWaves][kRadix];  // per-wave digit counts, then first slots
     const u32 t = xcd_tile(a.tiles);
     if (t >= a.tiles) return;
-    if constexpr (kSelect)
+    if constexpr (kSelect) {
+        if constexpr (kNodeDims)
+            if (no_nodes_here(a)) return;
         if (!tile_has_pivot<kNodeDims>(a, t)) return;
+    }
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const i64 wbase = (i64)t * kPartTile + (i64)w * (64 * kPartItems) + lane;
     const int delta = a.l1 - a.l0;
@@ -1130,30 +1144,41 @@ __device__ __forceinline__ int child_domain(const float* from, int pd, float pla
 // Domains and split dimensions of the nodes of level l (2k floats a node:
 // lo then hi), from their parents' (the root's from the bounding box). The
 // parents' pivots are fixed.
+// level_dims (k <= 32, else nullptr): bit d of level_dims[l] is set when
+// some node of level l splits dimension d.
 __global__ __launch_bounds__(kBlock) void k_widest_level(Geometry geo, int l, int k,
                                                          const u64* __restrict__ piv,
                                                          const float* __restrict__ root_box,
                                                          float* __restrict__ boxes,
                                                          uint16_t* __restrict__ dimtab,
-                                                         int32_t* __restrict__ dims_out) {
+                                                         int32_t* __restrict__ dims_out,
+                                                         u32* __restrict__ level_dims) {
     const u64 j = (u64)blockIdx.x * kBlock + threadIdx.x;
-    if (j >= (1ull << l)) return;
     const u64 s = full_nodes(l) + j;
-    if (s >= (u64)geo.n) return;
-    const float* from = root_box;
-    int pd = -1;
-    float plane = 0.0f;
-    bool left = false;
-    if (l > 0) {
-        const u64 p = (s - 1) / 2;
-        from = boxes + p * 2 * (u64)k;
-        pd = dimtab[p];
-        plane = __uint_as_float(key_bits((u32)(piv[p] >> 32)));  // a zero's sign is lost: extents agree
-        left = s == 2 * p + 1;
+    const bool here = j < (1ull << l) && s < (u64)geo.n;
+    u32 bits = 0;
+    if (here) {
+        const float* from = root_box;
+        int pd = -1;
+        float plane = 0.0f;
+        bool left = false;
+        if (l > 0) {
+            const u64 p = (s - 1) / 2;
+            from = boxes + p * 2 * (u64)k;
+            pd = dimtab[p];
+            plane = __uint_as_float(key_bits((u32)(piv[p] >> 32)));  // a zero's sign is lost: extents agree
+            left = s == 2 * p + 1;
+        }
+        const int best = child_domain(from, pd, plane, left, k, boxes + s * 2 * (u64)k);
+        dimtab[s] = (uint16_t)best;
+        if (dims_out) dims_out[s] = best;
+        bits = best < 32 ? 1u << best : 0u;
     }
-    const int best = child_domain(from, pd, plane, left, k, boxes + s * 2 * (u64)k);
-    dimtab[s] = (uint16_t)best;
-    if (dims_out) dims_out[s] = best;
+    if (level_dims) {  // one atomic per wave: the OR of its nodes' bits
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) bits |= __shfl_xor(bits, o, 64);
+        if ((threadIdx.x & 63) == 0 && bits) atomicOr(&level_dims[l], bits);
+    }
 }
 
 // ------------------------------------------------- duplicate removal
@@ -2058,7 +2083,7 @@ constexpr i64 kBoxChunk = 1 << 16;  // points per partial bounding box
 
 struct WidestLayout {
     Layout base;  // rounds = levels; records carry all k coordinates
-    size_t boxes, dimtab, root_box, box_partial;
+    size_t boxes, dimtab, root_box, box_partial, level_dims;
     i64 box_chunks;
 };
 
@@ -2096,6 +2121,7 @@ bool make_layout_widest(i64 n, int k, WidestLayout* out) {
     w.root_box = take((size_t)2 * k * sizeof(float));
     w.box_chunks = (n + kBoxChunk - 1) / kBoxChunk;
     w.box_partial = take((size_t)w.box_chunks * k * 2 * sizeof(float));
+    w.level_dims = take((size_t)kMaxRounds * sizeof(u32));
     lay.total = off;
     *out = w;
     return true;
@@ -2537,6 +2563,9 @@ kdt_status run_widest(const float* pts, i64 n, int k, const WidestLayout& wl, ch
     uint16_t* dimtab = (uint16_t*)(ws + wl.dimtab);
     float* root_box = (float*)(ws + wl.root_box);
     float* partial = (float*)(ws + wl.box_partial);
+    // each level's split dimensions, for skipping selects with no pivot to
+    // find (dimension masks need k <= 32)
+    u32* level_dims = k <= 32 ? (u32*)(ws + wl.level_dims) : nullptr;
     auto recs = [&](int b) { return (u32*)(ws + lay.recs) + (size_t)b * n * W; };
     Launcher launch{(u32*)(ws + lay.slots), (u32*)(ws + lay.chunk_slots), (u32*)(ws + lay.totals),
                     stream, timer};
@@ -2544,10 +2573,15 @@ kdt_status run_widest(const float* pts, i64 n, int k, const WidestLayout& wl, ch
         const u64 nodes = 1ull << l;
         timer.begin("k_widest_level", (double)nodes * (16.0 * k + 10 + (dims_out ? 4 : 0)));
         k_widest_level<<<(unsigned)((nodes + kBlock - 1) / kBlock), kBlock, 0, stream>>>(
-            geo, l, k, piv, root_box, boxes, dimtab, dims_out);
+            geo, l, k, piv, root_box, boxes, dimtab, dims_out, level_dims);
         timer.end();
     };
 
+    if (level_dims) {
+        timer.begin("k_zero", 4.0 * kMaxRounds);
+        k_zero<<<1, kBlock, 0, stream>>>(level_dims, kMaxRounds);
+        timer.end();
+    }
     timer.begin("k_box_partial", (double)n * 4.0 * k);
     k_box_partial<<<dim3((unsigned)wl.box_chunks, (unsigned)k), kBlock, 0, stream>>>(pts, n, k, kBoxChunk,
                                                                                    partial);
@@ -2645,6 +2679,7 @@ kdt_status run_widest(const float* pts, i64 n, int k, const WidestLayout& wl, ch
             const bool unread = lds_from == L ? l == L - 1 : l == lds_from - 1 && d != 0;
             const bool select = unread || ((2ull << l) <= tiles && l + 1 - level_of[d] <= kSelectDepth);
             if (select) {
+                a.level_dims = level_dims;
                 launch.select_any(a);
             } else {
                 launch.part_any(a);
