@@ -105,6 +105,16 @@ def test_select_rounds_many_levels(torch_dev, k):
         assert_same_tree(pts, perm, tree, oracle.build_tree(pts), "%s k=%d" % (gen, k))
 
 
+@pytest.mark.parametrize("k", [1, 2])
+def test_select_rounds_4m(torch_dev, k):
+    """4,194,304 points (10 global rounds): the select and deep re-sort
+    pattern of each dimension cycle at a realistic depth."""
+    pts = make("gmm", 1 << 22, k, 80 + k)
+    say("case select rounds gen=gmm N=4194304 k=%d" % k)
+    perm, tree = gpu_build(torch_dev, pts)
+    assert_same_tree(pts, perm, tree, oracle.build_tree(pts), "4M k=%d" % k)
+
+
 def test_worked_example(torch_dev):
     from test_oracle_pins import load_worked_example
     pts, expected = load_worked_example()

@@ -97,6 +97,16 @@ def test_widest_lds_stage(torch_dev, k):
             assert_same(pts, perm, tree, dims, "%s N=%d k=%d" % (gen, n, k))
 
 
+@pytest.mark.parametrize("k", [1, 2])
+def test_widest_4m(torch_dev, k):
+    """4,194,304 points: 10 global levels with selects and skipped selects,
+    then the LDS stage."""
+    pts = make("gmm", 1 << 22, k, 90 + k)
+    say("case widest gen=gmm N=4194304 k=%d" % k)
+    perm, tree, dims = gpu_widest(torch_dev, pts)
+    assert_same(pts, perm, tree, dims, "4M k=%d" % k, check=False)
+
+
 def test_widest_hand_example(torch_dev):
     from test_widest_oracle import load_hand_example
     pts, perm, dims = load_hand_example()
