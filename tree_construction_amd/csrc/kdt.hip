@@ -397,6 +397,39 @@ struct RecordTile {
             }
         }
     }
+    // The same for records (kW > 0) with no branch per item: a record past
+    // the end loads the last one instead and reads as zeros, so that every
+    // load is in flight before the first word is used.
+    __device__ __forceinline__ void load_all(const RecordSource& s, i64 wbase) {
+        static_assert(kSrc == kSrcRecords && kW > 0, "records held in registers");
+#pragma unroll
+        for (int j = 0; j < kPartItems; ++j) {
+            const i64 e = wbase + (i64)j * 64;
+            const u32* src = s.in + (u64)(e < s.n ? e : s.n - 1) * kW;
+            if constexpr (kW == 4) {
+                const uint4 v = *reinterpret_cast<const uint4*>(src);
+                w0[j] = v.x;
+                w1[j] = v.y;
+                w2[j] = v.z;
+                w3[j] = v.w;
+            } else if constexpr (kW == 3) {
+                w0[j] = src[0];
+                w1[j] = src[1];
+                w2[j] = src[2];
+                w3[j] = 0;
+            } else {
+                const uint2 v = *reinterpret_cast<const uint2*>(src);
+                w0[j] = v.x;
+                w1[j] = v.y;
+                w2[j] = w3[j] = 0;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kPartItems; ++j) {
+            if (wbase + (i64)j * 64 < s.n) continue;
+            w0[j] = w1[j] = w2[j] = w3[j] = 0;
+        }
+    }
     // Word w of item j (record e); w is uniform across the wave. The word is
     // picked with masks, not a select, so that the compiler cannot turn the
     // choice back into an indexed (scratch) array.
@@ -786,22 +819,65 @@ __device__ __forceinline__ bool no_nodes_here(const PartArgs& a) {
     return a.level_dims && !((a.level_dims[a.l1] >> a.array_dim) & 1u);
 }
 
+// Pivots one tile's walk keeps in LDS: the nodes of levels l0 .. l1-1 below
+// the level-l0 segments the tile overlaps (2 of them at most while segments
+// are as long as a tile, 2^delta - 1 nodes below each). Round-robin trees
+// only: split-widest walks read the pivots and node dimensions in place
+// (staging measured slower there).
+constexpr int kPivStage = 1024;
+
+// One level of the walk for round-robin trees, whose level dimension kD is
+// the same for the whole wave: the compared words are picked at compile
+// time. piv_level[loc] is the pivot of the item's node.
+template <int kD, int kW, typename Piv>
+__device__ __forceinline__ void walk_level(const RecordTile<kSrcRecords, kW>& tr, Piv piv_level,
+                                           u32 (&loc)[kPartItems], bool (&valid)[kPartItems]) {
+#pragma unroll
+    for (int j = 0; j < kPartItems; ++j) {
+        const u64 me = ((u64)tr.template at<kD>(j) << 32) | tr.template at<kW - 1>(j);
+        const u64 p = valid[j] ? piv_level[loc[j]] : 0;
+        if (me == p) valid[j] = false;  // the pivot itself: a node already
+        loc[j] = 2 * loc[j] + (me < p ? 0u : 1u);
+    }
+}
+
 // For every item: node[j], the in-level index of its node on level l1,
 // which is (j0 << delta) | digit for its level-l0 segment j0 and its digit
 // (offset of the level-l1 node below the level-l0 one); valid = false for
 // records past the end and for the pivots of levels l0 .. l1-1. The walk
 // compares (key(coordinate l mod k), index) with the pivot of the current
 // node on each level l ([W], tag paragraph: before the pivot -> left child).
+// Call with the whole workgroup: the pivots are staged in LDS first.
 template <int kW, bool kNodeDims>
-__device__ __forceinline__ void part_nodes(const PartArgs& a,
+__device__ __forceinline__ void part_nodes(const PartArgs& a, u32 t,
                                            const RecordTile<kSrcRecords, kW>& tr, i64 wbase,
                                            u32 (&node)[kPartItems], bool (&valid)[kPartItems]) {
+    __shared__ u64 s_piv[kNodeDims ? 1 : kPivStage];
+    const int delta = a.l1 - a.l0;
+    const u64 p0 = (u64)t * kPartTile;
+    const u64 p1 = p0 + kPartTile < (u64)a.src.n ? p0 + kPartTile : (u64)a.src.n;
+    const u32 j_first = (u32)live_segment(a.geo, p0, a.l0);
+    const u32 segs = (u32)live_segment(a.geo, p1 - 1, a.l0) - j_first + 1;
+    // Level l0 + m of the walk: nodes (j_first << m) + i, i < segs << m, at
+    // slots segs * (2^m - 1) + i (nodes past the last leaf: never visited).
+    const u32 staged_n = segs * ((1u << delta) - 1);
+    const bool staged = !kNodeDims && staged_n <= (u32)kPivStage;
+    if (staged) {
+        for (u32 s = threadIdx.x; s < staged_n; s += kBlock) {
+            const int m = 31 - __clz(s / segs + 1);
+            const u64 nd = full_nodes(a.l0 + m) + ((u64)j_first << m) + (s - segs * ((1u << m) - 1));
+            const bool real = nd < (u64)a.geo.n;
+            s_piv[s] = real ? a.piv[nd] : 0;
+        }
+    }
     // Level-l0 segment of each record: one division for the wave's first
     // record, then each lane steps over the segment starts it passes (its
-    // records are 64 positions apart, in increasing order).
+    // records are 64 positions apart, in increasing order). loc: the node's
+    // in-level index less j_first << m.
     const u32 wfirst = (u32)(wbase - (threadIdx.x & 63));
     u32 j0 = (u32)live_segment(a.geo, wfirst, a.l0);
     u32 next = live_begin32(a.s0, j0 + 1);
+    u32 loc[kPartItems];
 #pragma unroll
     for (int j = 0; j < kPartItems; ++j) {
         const u32 e = (u32)(wbase + (i64)j * 64);
@@ -812,27 +888,49 @@ __device__ __forceinline__ void part_nodes(const PartArgs& a,
                 next = live_begin32(a.s0, j0 + 1);
             }
         }
-        node[j] = (u32)full_nodes(a.l0) + j0;
+        loc[j] = j0 - j_first;
     }
+    if (staged) __syncthreads();
     // One level at a time: compare with the pivot of the current node, in
     // the level's dimension (or the node's own, from the table).
     int dim = a.dim0;
-    for (int l = a.l0; l < a.l1; ++l) {
+    for (int m = 0; m < delta; ++m) {
+        const u32 slot0 = segs * ((1u << m) - 1);
+        const u64 node0 = full_nodes(a.l0 + m) + ((u64)j_first << m);
+        if constexpr (kW > 0 && !kNodeDims) {
+            constexpr int kD1 = kW > 2 ? 1 : 0, kD2 = kW > 3 ? 2 : 0;
+            if (staged) {
+                const u64* lv = s_piv + slot0;
+                if (dim == 0) walk_level<0, kW>(tr, lv, loc, valid);
+                else if (dim == 1) walk_level<kD1, kW>(tr, lv, loc, valid);
+                else walk_level<kD2, kW>(tr, lv, loc, valid);
+            } else {
+                const u64* lv = a.piv + node0;
+                if (dim == 0) walk_level<0, kW>(tr, lv, loc, valid);
+                else if (dim == 1) walk_level<kD1, kW>(tr, lv, loc, valid);
+                else walk_level<kD2, kW>(tr, lv, loc, valid);
+            }
+        } else {
 #pragma unroll
-        for (int j = 0; j < kPartItems; ++j) {
-            const i64 e = wbase + (i64)j * 64;
-            int dj = dim;
-            if constexpr (kNodeDims) dj = valid[j] ? (int)a.dimtab[node[j]] : 0;
-            const u64 me = ((u64)tr.word(a.src, j, e, dj) << 32) | tr.word(a.src, j, e, a.src.words - 1);
-            const u64 p = valid[j] ? a.piv[node[j]] : 0;
-            if (me == p) valid[j] = false;  // the pivot itself: a node already
-            node[j] = 2 * node[j] + (me < p ? 1u : 2u);
+            for (int j = 0; j < kPartItems; ++j) {
+                const i64 e = wbase + (i64)j * 64;
+                int dj = dim;
+                u64 p = 0;
+                if (valid[j]) {
+                    p = staged ? s_piv[slot0 + loc[j]] : a.piv[node0 + loc[j]];
+                    if constexpr (kNodeDims) dj = (int)a.dimtab[node0 + loc[j]];
+                } else if constexpr (kNodeDims) {
+                    dj = 0;
+                }
+                const u64 me = ((u64)tr.word(a.src, j, e, dj) << 32) | tr.word(a.src, j, e, a.src.words - 1);
+                if (me == p) valid[j] = false;  // the pivot itself: a node already
+                loc[j] = 2 * loc[j] + (me < p ? 0u : 1u);
+            }
         }
         if (++dim == a.k) dim = 0;
     }
-    const u32 first = (u32)full_nodes(a.l1);
 #pragma unroll
-    for (int j = 0; j < kPartItems; ++j) node[j] -= first;
+    for (int j = 0; j < kPartItems; ++j) node[j] = (j_first << delta) + loc[j];
 }
 
 // Digit counts of one tile of a re-sort pass. A re-sort pass has at most
@@ -849,10 +947,11 @@ __device__ __forceinline__ void part_count(const PartArgs& a) {
     const i64 wbase = (i64)t * kPartTile + (i64)w * (64 * kPartItems) + lane;
     const int bins = 1 << (a.l1 - a.l0);
     RecordTile<kSrcRecords, kW> tr;
-    tr.load(a.src, wbase);
+    if constexpr (kW > 0) tr.load_all(a.src, wbase);
+    else tr.load(a.src, wbase);
     u32 node[kPartItems];
     bool valid[kPartItems];
-    part_nodes<kW, kNodeDims>(a, tr, wbase, node, valid);
+    part_nodes<kW, kNodeDims>(a, t, tr, wbase, node, valid);
     for (int i = lane; i < bins; i += 64) hist[w][i] = 0;  // this wave's own row
     u32 last = 0, run = 0;
 #pragma unroll
@@ -932,10 +1031,11 @@ __device__ __forceinline__ void part_scatter(const PartArgs& a) {
     const int delta = a.l1 - a.l0;
     const int bins = 1 << delta;
     RecordTile<kSrcRecords, kW> tr;
-    tr.load(a.src, wbase);
+    if constexpr (kW > 0) tr.load_all(a.src, wbase);
+    else tr.load(a.src, wbase);
     u32 node[kPartItems], rank[kPartItems];
     bool valid[kPartItems];
-    part_nodes<kW, kNodeDims>(a, tr, wbase, node, valid);
+    part_nodes<kW, kNodeDims>(a, t, tr, wbase, node, valid);
     for (int i = lane; i < bins; i += 64) count[w][i] = 0;
     {
         u32 digit[kPartItems];
