@@ -896,7 +896,7 @@ __device__ __forceinline__ void part_nodes(const PartArgs& a, u32 t,
     int dim = a.dim0;
     for (int m = 0; m < delta; ++m) {
         const u32 slot0 = segs * ((1u << m) - 1);
-        const u64 node0 = full_nodes(a.l0 + m) + ((u64)j_first << m);
+        const u32 node0 = (u32)(full_nodes(a.l0 + m) + ((u64)j_first << m));  // n < 2^31
         if constexpr (kW > 0 && !kNodeDims) {
             constexpr int kD1 = kW > 2 ? 1 : 0, kD2 = kW > 3 ? 2 : 0;
             if (staged) {
