@@ -561,16 +561,6 @@ __device__ inline void write_chunk_counts(const u32 (*hist)[kRadix], u32 (*rows)
     }
 }
 
-// Points of digit d before tile t: its chunk's prefix plus the counts of the
-// chunk's earlier tiles.
-__device__ inline u32 tile_prefix(const u32* tile_counts, const u32* chunk_prefix, int bins,
-                                  u64 chunks, u32 t, int d) {
-    const u32 c = t / kChunkTiles;
-    u32 before = chunk_prefix[(u64)d * chunks + c];
-    for (u32 tt = c * kChunkTiles; tt < t; ++tt) before += tile_counts[(u64)tt * bins + d];
-    return before;
-}
-
 // ------------------------------------------------- presort (LSD radix sort)
 // The presort of dimension d is kKeyBytes stable passes over the point
 // records, each by one byte of key(x_d), least significant first, starting
@@ -669,6 +659,20 @@ __global__ __launch_bounds__(kSortBlock) void k_sort_scatter(SortArgs a) {
     const i64 wbase = (i64)t * kSortTile + (i64)w * (64 * kPartItems) + lane;
     RecordTile<kSrc, kW> tr;
     tr.load(a.src, wbase);
+    // Thread tid < 256 owns digit tid: its records before this tile, and
+    // the digit's total (loaded while the records are in flight).
+    const bool owner = tid < kRadix;
+    u32 global_start = 0, digit_total = 0;
+    if (owner) {
+        // digit tid before this tile: its chunk's prefix, plus the first
+        // tile's count in the chunk's second tile (read with no branch)
+        static_assert(kChunkTiles == 2, "two tiles per chunk");
+        const u32 c = t / kChunkTiles;
+        const u32 chunk_before = a.chunk_counts[(u64)tid * a.chunks + c];
+        const u32 first_tile = a.tile_counts[(u64)c * kChunkTiles * kRadix + tid];
+        digit_total = a.totals[tid];
+        global_start = chunk_before + ((t & 1) ? first_tile : 0u);
+    }
     u32 digit[kPartItems], rank[kPartItems];
     bool valid[kPartItems];
 #pragma unroll
@@ -676,14 +680,6 @@ __global__ __launch_bounds__(kSortBlock) void k_sort_scatter(SortArgs a) {
         const i64 e = wbase + (i64)j * 64;
         valid[j] = e < a.src.n;
         digit[j] = valid[j] ? (tr.word(a.src, j, e, a.dim) >> a.shift) & (kRadix - 1) : 0u;
-    }
-    // Thread tid < 256 owns digit tid: its records before this tile, and
-    // the digit's total.
-    const bool owner = tid < kRadix;
-    u32 global_start = 0, digit_total = 0;
-    if (owner) {
-        global_start = tile_prefix(a.tile_counts, a.chunk_counts, kRadix, a.chunks, t, tid);
-        digit_total = a.totals[tid];
     }
     for (int i = lane; i < kRadix; i += 64) sm.count[w][i] = 0;
     wave_rank(digit, valid, kRadixBits, sm.count[w], rank);
@@ -1033,6 +1029,8 @@ __device__ __forceinline__ void part_scatter(const PartArgs& a) {
     RecordTile<kSrcRecords, kW> tr;
     if constexpr (kW > 0) tr.load_all(a.src, wbase);
     else tr.load(a.src, wbase);
+    // points of digit tid before the tile (loaded while the records are in flight)
+    const u32 before_tile = tid < bins ? a.chunk_counts[(u64)tid * a.tiles + t] : 0u;
     u32 node[kPartItems], rank[kPartItems];
     bool valid[kPartItems];
     part_nodes<kW, kNodeDims>(a, t, tr, wbase, node, valid);
@@ -1046,7 +1044,7 @@ __device__ __forceinline__ void part_scatter(const PartArgs& a) {
     __syncthreads();
     if (tid < bins) {
         // points of this digit before the tile, then before each wave
-        u32 run = a.chunk_counts[(u64)tid * a.tiles + t];
+        u32 run = before_tile;
 #pragma unroll
         for (int v = 0; v < kWaves; ++v) {
             const u32 c = count[v][tid];
