@@ -599,6 +599,61 @@ __global__ __launch_bounds__(kBlock) void k_first_digits(const float* __restrict
     }
 }
 
+// The same for kK <= 4 coordinates and rows starting on 16 bytes: a thread
+// takes four consecutive points, their rows read as kK 16-byte words, and
+// writes each dimension's four digits as one word when n is a multiple of 4
+// (every dimension's digits then start on a word), else as four bytes. The
+// n mod 4 last points go through the per-point loop.
+template <int kK>
+__global__ __launch_bounds__(kBlock) void k_first_digits4(const float* __restrict__ pts, i64 n, int kr,
+                                                          u8* __restrict__ digits0) {
+    const i64 stride = (i64)gridDim.x * kBlock;
+    const i64 quads = n / 4;
+    const bool whole = n % 4 == 0;
+    for (i64 q = (i64)blockIdx.x * kBlock + threadIdx.x; q < quads; q += stride) {
+        const uint4* src = reinterpret_cast<const uint4*>(pts) + (u64)q * kK;
+        u32 w[4 * kK];
+#pragma unroll
+        for (int i = 0; i < kK; ++i) {
+            const uint4 v = src[i];
+            w[4 * i] = v.x;
+            w[4 * i + 1] = v.y;
+            w[4 * i + 2] = v.z;
+            w[4 * i + 3] = v.w;
+        }
+#pragma unroll
+        for (int d = 0; d < kK; ++d) {
+            if (d >= kr) break;
+            u32 packed = 0;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) packed |= (float_key(w[p * kK + d]) & 0xffu) << (8 * p);
+            u8* dst = digits0 + (u64)d * n + (u64)q * 4;
+            if (whole) {
+                *reinterpret_cast<u32*>(dst) = packed;
+            } else {
+#pragma unroll
+                for (int p = 0; p < 4; ++p) dst[p] = (u8)(packed >> (8 * p));
+            }
+        }
+    }
+    for (i64 e = quads * 4 + (i64)blockIdx.x * kBlock + threadIdx.x; e < n; e += stride) {
+        const u32* row = reinterpret_cast<const u32*>(pts) + (u64)e * kK;
+        for (int d = 0; d < kr; ++d) digits0[(u64)d * n + e] = (u8)float_key(row[d]);
+    }
+}
+
+// Launches whichever of the two fits k and the rows' alignment.
+void launch_first_digits(const float* pts, i64 n, int k, int kr, u8* digits0, hipStream_t stream) {
+    const bool vec = k >= 1 && k <= 4 && reinterpret_cast<uintptr_t>(pts) % 16 == 0;
+    const i64 work = vec ? (n + 3) / 4 : (n > 0 ? n : 1);
+    const unsigned grid = (unsigned)((work + kBlock - 1) / kBlock < (1 << 30) ? (work + kBlock - 1) / kBlock : (1 << 30));
+    if (!vec) k_first_digits<<<grid, kBlock, 0, stream>>>(pts, n, k, kr, digits0);
+    else if (k == 1) k_first_digits4<1><<<grid, kBlock, 0, stream>>>(pts, n, kr, digits0);
+    else if (k == 2) k_first_digits4<2><<<grid, kBlock, 0, stream>>>(pts, n, kr, digits0);
+    else if (k == 3) k_first_digits4<3><<<grid, kBlock, 0, stream>>>(pts, n, kr, digits0);
+    else k_first_digits4<4><<<grid, kBlock, 0, stream>>>(pts, n, kr, digits0);
+}
+
 // Digit counts of the tiles of one chunk, from the pass's digit bytes (one
 // byte read per record instead of the record).
 __global__ __launch_bounds__(kCountBlock) void k_sort_count(SortArgs a) {
@@ -2430,7 +2485,7 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
                     stream, timer};
 
     timer.begin("k_first_digits", (double)n * 5.0 * lay.kr);
-    k_first_digits<<<grid_for(n, kBlock, 1 << 30), kBlock, 0, stream>>>(pts, n, k, lay.kr, digits0);
+    launch_first_digits(pts, n, k, lay.kr, digits0, stream);
     timer.end();
 
     int holder[kMaxRounds + 1];  // dimension whose array a buffer holds, or -1
@@ -2717,7 +2772,7 @@ kdt_status run_widest(const float* pts, i64 n, int k, const WidestLayout& wl, ch
     }
 
     timer.begin("k_first_digits", (double)n * 5.0 * k);
-    k_first_digits<<<grid_for(n, kBlock, 1 << 30), kBlock, 0, stream>>>(pts, n, k, k, digits0);
+    launch_first_digits(pts, n, k, k, digits0, stream);
     timer.end();
     // A_d in buffer d, by (coordinate d, index): the order of level 0.
     for (int d = 0; d < k; ++d)
