@@ -714,20 +714,23 @@ __global__ __launch_bounds__(kSortBlock) void k_sort_scatter(SortArgs a) {
     const i64 wbase = (i64)t * kSortTile + (i64)w * (64 * kPartItems) + lane;
     RecordTile<kSrc, kW> tr;
     tr.load(a.src, wbase);
-    // Thread tid < 256 owns digit tid: its records before this tile, and
-    // the digit's total (loaded while the records are in flight).
+    // Thread tid < 256 owns digit tid: its records before this tile (its
+    // chunk's prefix, plus the first tile's count in the chunk's second
+    // tile, read with no branch), and the digit's total. With 16-byte
+    // records the loads go out while the records are in flight; with
+    // narrower ones (more workgroups per CU) after the digits.
+    static_assert(kChunkTiles == 2, "two tiles per chunk");
     const bool owner = tid < kRadix;
     u32 global_start = 0, digit_total = 0;
-    if (owner) {
-        // digit tid before this tile: its chunk's prefix, plus the first
-        // tile's count in the chunk's second tile (read with no branch)
-        static_assert(kChunkTiles == 2, "two tiles per chunk");
+    auto load_prefix = [&]() {
         const u32 c = t / kChunkTiles;
         const u32 chunk_before = a.chunk_counts[(u64)tid * a.chunks + c];
         const u32 first_tile = a.tile_counts[(u64)c * kChunkTiles * kRadix + tid];
         digit_total = a.totals[tid];
         global_start = chunk_before + ((t & 1) ? first_tile : 0u);
-    }
+    };
+    if constexpr (kW == 4)
+        if (owner) load_prefix();
     u32 digit[kPartItems], rank[kPartItems];
     bool valid[kPartItems];
 #pragma unroll
@@ -736,6 +739,8 @@ __global__ __launch_bounds__(kSortBlock) void k_sort_scatter(SortArgs a) {
         valid[j] = e < a.src.n;
         digit[j] = valid[j] ? (tr.word(a.src, j, e, a.dim) >> a.shift) & (kRadix - 1) : 0u;
     }
+    if constexpr (kW != 4)
+        if (owner) load_prefix();
     for (int i = lane; i < kRadix; i += 64) sm.count[w][i] = 0;
     wave_rank(digit, valid, kRadixBits, sm.count[w], rank);
     __syncthreads();
