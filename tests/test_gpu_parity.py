@@ -115,6 +115,22 @@ def test_select_rounds_4m(torch_dev, k):
     assert_same_tree(pts, perm, tree, oracle.build_tree(pts), "4M k=%d" % k)
 
 
+@pytest.mark.parametrize("k,n", [(1, 4099), (2, 70001), (3, 100003), (4, 65536)])
+def test_rows_not_16_byte_aligned(torch_dev, k, n):
+    """Rows that do not start on 16 bytes (a view one float into a larger
+    buffer) take the per-point first-digit pass; the tree is the same."""
+    torch, dev = torch_dev
+    pts = make("gmm", n, k, 70 + k)
+    say("case offset view gen=gmm N=%d k=%d" % (n, k))
+    flat = torch.empty(n * k + 1, dtype=torch.float32, device=dev)
+    flat[1:] = torch.from_numpy(np.ascontiguousarray(pts)).to(dev).reshape(-1)
+    x = flat[1:].view(n, k)
+    assert x.is_contiguous() and x.data_ptr() % 16 != 0
+    perm, tree = kdt.build(x)
+    torch.cuda.synchronize(dev)
+    assert_same_tree(pts, perm.cpu().numpy(), tree.cpu().numpy(), oracle.build_tree(pts), "offset k=%d" % k)
+
+
 def test_worked_example(torch_dev):
     from test_oracle_pins import load_worked_example
     pts, expected = load_worked_example()
