@@ -293,7 +293,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        log("bench.py: this build runs on one GPU only (no multi-GPU path); "
+        log("bench.py: the k-d tree path runs on one GPU only (no multi-GPU path); "
             "run it with --gpus 1")
         sys.exit(2)
     if args.knn:

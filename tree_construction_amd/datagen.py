@@ -5,8 +5,8 @@ both the GPU path's tests/benchmark and the CPU oracle's tests consume its
 arrays. Every generator uses numpy's ``default_rng(seed)`` (PCG64) and returns
 a C-contiguous ``(N, k)`` float32 array.
 
-The five named workloads follow the point counts, dimensions, distributions
-and seeds fixed for this build; the pages themselves publish no dataset for
+The five named workloads use fixed point counts, dimensions, distributions
+and seeds; the pages themselves publish no dataset for
 the construction (they quote a "10 million points" build and a 16,777,216 x 4
 tuple run), so synthetic data of these shapes stands in.
 """
