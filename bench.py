@@ -12,7 +12,9 @@ Prints ONE JSON line on stdout (progress goes to stderr):
   value      whole-job build throughput, Mpoints/s (= N / seconds per build)
   roofline   the dominant kernel's algorithmic bytes per launch / its average
              launch duration (HIP events on the build's stream), against the
-             8 TB/s HBM peak
+             8 TB/s HBM peak; for the LDS-phase kernels, bound by the VALU,
+             its wave64 VALU instructions per launch (rocprofv3 SQ_INSTS_VALU)
+             x 64 lanes / that duration, against the 39.3 T lane-ops/s peak
   cpu_baseline  the CPU oracle on a bounded sample of the same workload
 
 With --widest it times the split-widest-dimension build of the same workload
@@ -46,6 +48,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published figure
+# 32-bit VALU issue peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, in T lane-ops/s
+VALU_PEAK_TLANE = 256 * 4 * 16 * 2.4e9 / 1e12
+# kernels whose bound is the VALU (ballot ranking in LDS)
+VALU_BOUND = ("k_subtree<true>", "k_subtree<false>", "k_subtree_widest")
 COPY_BYTES = 256 << 20  # the --calibration-copy dispatch reads and writes this much
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
@@ -269,6 +275,30 @@ def counter_traffic(workload, kernel, widest=False):
     return out
 
 
+def counter_valu(workload, kernel, widest=False):
+    """Wave64 VALU instructions per launch of `kernel` (rocprofv3 --pmc
+    SQ_INSTS_VALU over one build of this benchmark), or None."""
+    prof = shutil.which("rocprofv3")
+    if prof is None:
+        return None
+    with tempfile.TemporaryDirectory(prefix="kdt_pmc_") as tmp:
+        cmd = ["timeout", "-s", "KILL", "150", prof, "--pmc", "SQ_INSTS_VALU", "--output-format", "csv",
+               "-d", tmp, "-o", "kdt", "--", sys.executable, os.path.abspath(__file__),
+               "--workload", workload, "--steps", "1", "--warmup", "1", "--no-profile",
+               "--no-cpu-baseline", "--no-counters"] + (["--widest"] if widest else [])
+        r = subprocess.run(cmd, stdout=subprocess.DEVNULL, stderr=subprocess.PIPE, text=True)
+        files = glob.glob(os.path.join(tmp, "**", "*counter_collection.csv"), recursive=True)
+        if r.returncode != 0 or not files:
+            log("bench: SQ_INSTS_VALU counter run failed (rc %d)" % r.returncode)
+            return None
+        per = []
+        with open(files[0]) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") == "SQ_INSTS_VALU" and kernel_short_name(row["Kernel_Name"]) == kernel:
+                    per.append(float(row["Counter_Value"]))
+        return sum(per) / len(per) if per else None
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -401,6 +431,21 @@ def main():
         for kind, kv in sorted(kernels.items(), key=lambda kv: -kv[1]["ms_per_build"]):
             log("  %-36s %4d/build  avg %8.2f us  %8.1f GB/s  %.3f ms/build"
                 % (kind, kv["launches_per_build"], kv["avg_us"], kv["GBps"], kv["ms_per_build"]))
+        if dom in VALU_BOUND:
+            # the LDS-phase kernels rank in LDS with ballots: their bound is
+            # the 32-bit VALU issue rate, not HBM
+            roofline.update({"bound": "alu", "unit": "T lane-ops/s", "peak": VALU_PEAK_TLANE,
+                             "achieved": None, "frac": None, "hbm_GBps": achieved})
+            if not args.no_counters:
+                log("bench: rocprofv3 SQ_INSTS_VALU run for %s" % dom)
+                inst = counter_valu(name, dom, widest=args.widest)
+                if inst:
+                    lane_ops = inst * 64 / (d["avg_us"] * 1e-6) / 1e12
+                    roofline.update({"achieved": round(lane_ops, 2),
+                                     "frac": round(lane_ops / VALU_PEAK_TLANE, 4),
+                                     "valu_instructions_per_launch": int(inst)})
+                    log("  VALU %.0f M instructions per launch: %.2f T lane-ops/s (%.1f%% of %.1f)"
+                        % (inst / 1e6, lane_ops, 100 * lane_ops / VALU_PEAK_TLANE, VALU_PEAK_TLANE))
         if not args.no_counters:
             log("bench: rocprofv3 FETCH_SIZE / WRITE_SIZE runs for %s" % dom)
             tr = counter_traffic(name, dom, widest=args.widest)

@@ -367,21 +367,23 @@ struct RecordTile {
                     if constexpr (kW == 3) w2[j] = (u32)e;
                     if constexpr (kW == 4) w3[j] = (u32)e;
                 } else {
+                    // Non-temporal: a presort pass reads each record once, and
+                    // the cache is left to the partly written lines of its runs.
                     const u32* src = s.in + (u64)e * kW;
                     if constexpr (kW == 4) {
-                        const uint4 v = *reinterpret_cast<const uint4*>(src);
-                        w0[j] = v.x;
-                        w1[j] = v.y;
-                        w2[j] = v.z;
-                        w3[j] = v.w;
+                        const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(src));
+                        w0[j] = v[0];
+                        w1[j] = v[1];
+                        w2[j] = v[2];
+                        w3[j] = v[3];
                     } else if constexpr (kW == 3) {
                         w0[j] = src[0];
                         w1[j] = src[1];
                         w2[j] = src[2];
                     } else {
-                        const uint2 v = *reinterpret_cast<const uint2*>(src);
-                        w0[j] = v.x;
-                        w1[j] = v.y;
+                        const v2u v = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(src));
+                        w0[j] = v[0];
+                        w1[j] = v[1];
                     }
                 }
             }
