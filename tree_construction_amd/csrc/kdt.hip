@@ -359,10 +359,11 @@ struct RecordTile {
                 w0[j] = w1[j] = w2[j] = w3[j] = 0;
                 if (e >= s.n) continue;
                 if constexpr (kSrc == kSrcRows) {
+                    // non-temporal like the records below: one read per pass
                     const u32* row = reinterpret_cast<const u32*>(s.pts) + (u64)e * s.k;
-                    w0[j] = row[0];
-                    if constexpr (kW > 2) w1[j] = row[1];
-                    if constexpr (kW > 3) w2[j] = row[2];
+                    w0[j] = __builtin_nontemporal_load(row);
+                    if constexpr (kW > 2) w1[j] = __builtin_nontemporal_load(row + 1);
+                    if constexpr (kW > 3) w2[j] = __builtin_nontemporal_load(row + 2);
                     if constexpr (kW == 2) w1[j] = (u32)e;
                     if constexpr (kW == 3) w2[j] = (u32)e;
                     if constexpr (kW == 4) w3[j] = (u32)e;
