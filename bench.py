@@ -3,19 +3,28 @@
 
 One step = one complete build (every round's radix passes or pivot
 selections, and the subtree stage with its level-order output) of the
-headline workload:
+workload, by default the headline one:
 N = 16,777,216 points, k = 3, float32, from a 64-component Gaussian mixture
-with 5% of coordinates snapped to a 2^-10 grid (seed 3). Inputs, outputs and
-the workspace are resident in HBM before the timed region starts.
+with 5% of coordinates snapped to a 2^-10 grid (seed 3). --workload picks one
+of the others (uniform_1m_k3, normal_4m_k16, uniform_100m_k3). Inputs, outputs
+and the workspace are resident in HBM before the timed region starts.
 
 Prints ONE JSON line on stdout (progress goes to stderr):
   value      whole-job build throughput, Mpoints/s (= N / seconds per build)
-  roofline   the dominant kernel's algorithmic bytes per launch / its average
-             launch duration (HIP events on the build's stream), against the
-             8 TB/s HBM peak; for the LDS-phase kernels, bound by the VALU,
-             its wave64 VALU instructions per launch (rocprofv3 SQ_INSTS_VALU)
-             x 64 lanes / that duration, against the 39.3 T lane-ops/s peak
-  cpu_baseline  the CPU oracle on a bounded sample of the same workload
+  roofline   HBM roofline of the dominant kernel (the kind with the largest
+             time per build): its algorithmic bytes per launch (every array it
+             must read or write, once, as the library counts them) / its
+             average launch duration (HIP events on the build's stream),
+             against the 8 TB/s peak; `traffic` is its measured HBM bytes per
+             launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, each scaled by the
+             same counter on a plain 256 MiB copy). Flat extra fields give the
+             same figures for the whole build (build_*) and for the global sort
+             and tag-update passes together (passes_*), and the dominant
+             kernel's VALU issue rate (valu_issue_frac, a diagnostic)
+  kernels    per kernel kind: launches, time, algorithmic bytes and GB/s, and
+             the counter-measured bytes and GB/s beside them
+  cpu_baseline  the CPU oracle on bounded samples of the same recipe: all
+             host threads (value) and one thread, with the CPU model
 
 With --widest it times the split-widest-dimension build of the same workload
 instead (value, roofline and cpu_baseline as above, for that variant).
@@ -50,8 +59,6 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published figure
 # 32-bit VALU issue peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, in T lane-ops/s
 VALU_PEAK_TLANE = 256 * 4 * 16 * 2.4e9 / 1e12
-# kernels whose bound is the VALU (ballot ranking in LDS)
-VALU_BOUND = ("k_subtree<true>", "k_subtree<false>", "k_subtree_widest")
 COPY_BYTES = 256 << 20  # the --calibration-copy dispatch reads and writes this much
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
@@ -61,23 +68,45 @@ def log(msg):
     sys.stderr.flush()
 
 
-def cpu_baseline(name, sample_n, widest=False):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(name, sample_all, sample_one, widest=False):
+    """The oracle (never tuned for speed) on two bounded samples of the
+    workload's recipe and seed: all host threads on sample_all points (the
+    reported value), then one thread on sample_one points."""
     import oracle  # test infrastructure, used only for this reported baseline
     from tree_construction_amd import datagen
     w = datagen.WORKLOADS[name]
-    pts = datagen.cached(name) if sample_n == w.n else datagen.generate(name, n=sample_n)
-    oracle.load_lib()
-    t0 = time.perf_counter()
-    if widest:
-        oracle.build_tree_widest(pts)
-    else:
-        oracle.build_tree(pts)
-    dt = time.perf_counter() - t0
-    return {"value": round(sample_n / dt / 1e6, 3), "unit": "Mpoints/s",
-            "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": ("the whole workload %s" % name if sample_n == w.n else
-                       "same recipe and seed as %s at N=%d" % (name, sample_n))
-                      + " (k=%d), %.1f s wall" % (w.k, dt)}
+    lib = oracle.load_lib()
+    threads = oracle.max_threads(lib)  # before any run pins the count
+
+    def timed(n, nthreads):
+        pts = datagen.cached(name) if n == w.n else datagen.generate(name, n=n)
+        t0 = time.perf_counter()
+        if widest:
+            oracle.build_tree_widest(pts, nthreads=nthreads)
+        else:
+            oracle.build_tree(pts, nthreads=nthreads)
+        return time.perf_counter() - t0
+
+    n_all, n_one = min(sample_all, w.n), min(sample_one, w.n)
+    dt_all = timed(n_all, threads)
+    dt_one = timed(n_one, 1)
+    return {"value": round(n_all / dt_all / 1e6, 3), "unit": "Mpoints/s", "cores": threads, "kind": "oracle",
+            "sample": "%s recipe and seed at N=%d (k=%d), %d threads, %.1f s wall; single thread at N=%d, %.1f s"
+                      % (name, n_all, w.k, threads, dt_all, n_one, dt_one),
+            "single_thread_value": round(n_one / dt_one / 1e6, 3),
+            "cpu_model": cpu_model(), "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+            "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
 def knn_cpu_baseline(pts, qs, K, sample):
@@ -220,7 +249,7 @@ def run_unique(args):
         "metric": "duplicate removal Mpoints/s at N=16M k=3 fp32",
         "value": round(n / ms / 1e3, 2), "unit": "Mpoints/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "u32", "data": "synthetic",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "unique over %s" % name, "n_points": n, "k": k, "distinct": distinct,
                    "description": w.note},
         "roofline": {"bound": "hbm", "achieved": kernels[dom]["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -238,65 +267,65 @@ def kernel_short_name(name):
     return re.sub(r"\(.*", "", name).strip()
 
 
-def counter_traffic(workload, kernel, widest=False):
-    """Per-launch HBM bytes of `kernel` from two rocprofv3 counter runs of this
-    benchmark (FETCH_SIZE, then WRITE_SIZE), each scaled by what the counter
-    reads for a plain 256 MiB device copy. None if rocprofv3 is unavailable."""
+PMC_RUNS = (("FETCH_SIZE", "SQ_INSTS_VALU"), ("WRITE_SIZE",))  # within one run's counter limits
+
+
+def counter_runs(workload, widest=False):
+    """Per kernel kind, the summed counters of two rocprofv3 --pmc runs of this
+    benchmark (FETCH_SIZE with SQ_INSTS_VALU, then WRITE_SIZE) over its
+    builds, each HBM counter scaled by what it reads for a plain 256 MiB copy
+    (KiB -> bytes). Returns ({kind: {"fetch", "write", "valu", "dispatches"}},
+    {counter: scale}, builds) or None if rocprofv3 is unavailable or fails."""
     prof = shutil.which("rocprofv3")
     if prof is None:
         return None
-    out = {}
+    builds = 2  # --warmup 1 --steps 1 below
+    kinds, scales = {}, {}
+    field = {"FETCH_SIZE": "fetch", "WRITE_SIZE": "write", "SQ_INSTS_VALU": "valu"}
     with tempfile.TemporaryDirectory(prefix="kdt_pmc_") as tmp:
-        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
-            d = os.path.join(tmp, counter)
-            cmd = ["timeout", "-s", "KILL", "150", prof, "--pmc", counter, "--output-format", "csv",
+        for counters in PMC_RUNS:
+            d = os.path.join(tmp, counters[0])
+            cmd = ["timeout", "-s", "KILL", "300", prof, "--pmc", *counters, "--output-format", "csv",
                    "-d", d, "-o", "kdt", "--", sys.executable, os.path.abspath(__file__),
                    "--workload", workload, "--steps", "1", "--warmup", "1", "--no-profile",
                    "--no-cpu-baseline", "--no-counters", "--calibration-copy"] + (["--widest"] if widest else [])
             r = subprocess.run(cmd, stdout=subprocess.DEVNULL, stderr=subprocess.PIPE, text=True)
             files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
             if r.returncode != 0 or not files:
-                log("bench: %s counter run failed (rc %d)" % (counter, r.returncode))
+                log("bench: %s counter run failed (rc %d)" % ("+".join(counters), r.returncode))
                 return None
-            per, copy = [], []
+            copy = {}
             with open(files[0]) as f:
                 for row in csv.DictReader(f):
-                    if row.get("Counter_Name") != counter:
+                    cname = row.get("Counter_Name")
+                    if cname not in counters:
                         continue
                     kname = kernel_short_name(row["Kernel_Name"])
-                    if kname == kernel:
-                        per.append(float(row["Counter_Value"]))
-                    elif kname == COPY_KERNEL:
-                        copy.append(float(row["Counter_Value"]))
-            if not per or not copy:
-                return None
-            scale = (COPY_BYTES / 1024.0) / copy[0]
-            out[counter] = {"bytes": sum(per) / len(per) * 1024.0 * scale, "scale": round(scale, 3)}
-    return out
+                    val = float(row["Counter_Value"])
+                    if kname == COPY_KERNEL:
+                        copy.setdefault(cname, val)
+                        continue
+                    rec = kinds.setdefault(kname, {"fetch": 0.0, "write": 0.0, "valu": 0.0, "dispatches": 0})
+                    rec[field[cname]] += val
+                    if cname == "FETCH_SIZE":  # one row per dispatch and counter
+                        rec["dispatches"] += 1
+            for cname in counters:
+                if cname in ("FETCH_SIZE", "WRITE_SIZE"):
+                    if cname not in copy or copy[cname] <= 0:
+                        log("bench: no %s reading for the calibration copy" % cname)
+                        return None
+                    scales[cname] = (COPY_BYTES / 1024.0) / copy[cname]
+    for rec in kinds.values():
+        rec["fetch"] *= 1024.0 * scales["FETCH_SIZE"]
+        rec["write"] *= 1024.0 * scales["WRITE_SIZE"]
+    return kinds, scales, builds
 
 
-def counter_valu(workload, kernel, widest=False):
-    """Wave64 VALU instructions per launch of `kernel` (rocprofv3 --pmc
-    SQ_INSTS_VALU over one build of this benchmark), or None."""
-    prof = shutil.which("rocprofv3")
-    if prof is None:
-        return None
-    with tempfile.TemporaryDirectory(prefix="kdt_pmc_") as tmp:
-        cmd = ["timeout", "-s", "KILL", "150", prof, "--pmc", "SQ_INSTS_VALU", "--output-format", "csv",
-               "-d", tmp, "-o", "kdt", "--", sys.executable, os.path.abspath(__file__),
-               "--workload", workload, "--steps", "1", "--warmup", "1", "--no-profile",
-               "--no-cpu-baseline", "--no-counters"] + (["--widest"] if widest else [])
-        r = subprocess.run(cmd, stdout=subprocess.DEVNULL, stderr=subprocess.PIPE, text=True)
-        files = glob.glob(os.path.join(tmp, "**", "*counter_collection.csv"), recursive=True)
-        if r.returncode != 0 or not files:
-            log("bench: SQ_INSTS_VALU counter run failed (rc %d)" % r.returncode)
-            return None
-        per = []
-        with open(files[0]) as f:
-            for row in csv.DictReader(f):
-                if row.get("Counter_Name") == "SQ_INSTS_VALU" and kernel_short_name(row["Kernel_Name"]) == kernel:
-                    per.append(float(row["Counter_Value"]))
-        return sum(per) / len(per) if per else None
+# Kernel kinds of the global phase: presort, per-round re-sorts and selects,
+# their scans, the pivots and the split-widest domain kernels (everything but
+# the subtree stage and the single-point case).
+GLOBAL_PASS_PREFIXES = ("k_sort_", "k_part_", "k_pivots", "k_chunk_scan", "k_first_digits", "k_widest_level",
+                        "k_box_", "k_zero")
 
 
 def main():
@@ -306,11 +335,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=None,
-                    help="points of the CPU oracle run (default: the whole workload)")
+    ap.add_argument("--cpu-sample", type=int, default=1 << 22,
+                    help="points of the all-threads CPU oracle run (the same recipe and seed)")
+    ap.add_argument("--cpu-sample-one", type=int, default=1 << 20,
+                    help="points of the single-thread CPU oracle run")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event loop")
     ap.add_argument("--no-counters", action="store_true",
-                    help="skip the rocprofv3 FETCH_SIZE/WRITE_SIZE runs behind roofline.traffic")
+                    help="skip the rocprofv3 counter runs behind roofline.traffic and the kernels' counter bytes")
     ap.add_argument("--widest", action="store_true", help="time the split-widest-dimension build")
     ap.add_argument("--unique", action="store_true", help="time the duplicate-removal pre-pass")
     ap.add_argument("--knn", action="store_true", help="time the kNN query instead of the build")
@@ -410,66 +441,92 @@ def main():
                              "avg_us": round(per_launch_ms * 1e3, 2),
                              "ms_per_build": round(a["ms"] / args.steps, 4),
                              "bytes_per_launch": int(a["bytes"] / a["launches"]),
+                             "bytes_per_build": int(a["bytes"] / args.steps),
                              "GBps": round(gbs, 1)}
         dom = max(kernels, key=lambda kk: kernels[kk]["ms_per_build"])
         d = kernels[dom]
         achieved = d["GBps"]
+        # HBM roofline of the dominant kernel from its algorithmic bytes
         roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                     "kernel": dom, "avg_us": d["avg_us"], "bytes_per_launch": d["bytes_per_launch"]}
-        # every global sort and tag-update pass: presort histograms and passes,
-        # per-round re-sorts, pivot extraction
-        passes = [kk for kk in kernels if kk.startswith(("k_sort_", "k_part_", "k_pivots", "k_chunk_scan",
-                                                         "k_first_digits", "k_widest_level", "k_box_"))]
-        tot_b = sum(agg[kk]["bytes"] for kk in passes)
-        tot_ms = sum(agg[kk]["ms"] for kk in passes)
-        if tot_ms > 0:
-            roofline["sort_and_update_passes"] = {
-                "GBps": round(tot_b / (tot_ms * 1e-3) / 1e9, 1),
-                "frac": round(tot_b / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                "ms_per_build": round(tot_ms / args.steps, 4)}
+        # the whole build: every kernel's algorithmic bytes over the build time
+        build_bytes = sum(kv["bytes_per_build"] for kv in kernels.values())
+        build_gbs = build_bytes / (ms_per_step * 1e-3) / 1e9
+        roofline.update({"build_bytes": build_bytes, "build_GBps": round(build_gbs, 1),
+                         "build_frac": round(build_gbs / HBM_PEAK_GBS, 4)})
+        # the global sort and tag-update passes together (the subtree stage,
+        # which finishes the last rounds in LDS, is not among them)
+        passes = [kk for kk in kernels if kk.startswith(GLOBAL_PASS_PREFIXES)]
+        pass_bytes = sum(kernels[kk]["bytes_per_build"] for kk in passes)
+        pass_ms = sum(kernels[kk]["ms_per_build"] for kk in passes)
+        if pass_ms > 0:
+            roofline.update({"passes_ms_per_build": round(pass_ms, 4),
+                             "passes_GBps": round(pass_bytes / (pass_ms * 1e-3) / 1e9, 1),
+                             "passes_frac": round(pass_bytes / (pass_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
         for kind, kv in sorted(kernels.items(), key=lambda kv: -kv[1]["ms_per_build"]):
             log("  %-36s %4d/build  avg %8.2f us  %8.1f GB/s  %.3f ms/build"
                 % (kind, kv["launches_per_build"], kv["avg_us"], kv["GBps"], kv["ms_per_build"]))
-        if dom in VALU_BOUND:
-            # the LDS-phase kernels rank in LDS with ballots: their bound is
-            # the 32-bit VALU issue rate, not HBM
-            roofline.update({"bound": "alu", "unit": "T lane-ops/s", "peak": VALU_PEAK_TLANE,
-                             "achieved": None, "frac": None, "hbm_GBps": achieved})
-            if not args.no_counters:
-                log("bench: rocprofv3 SQ_INSTS_VALU run for %s" % dom)
-                inst = counter_valu(name, dom, widest=args.widest)
-                if inst:
-                    lane_ops = inst * 64 / (d["avg_us"] * 1e-6) / 1e12
-                    roofline.update({"achieved": round(lane_ops, 2),
-                                     "frac": round(lane_ops / VALU_PEAK_TLANE, 4),
-                                     "valu_instructions_per_launch": int(inst)})
-                    log("  VALU %.0f M instructions per launch: %.2f T lane-ops/s (%.1f%% of %.1f)"
-                        % (inst / 1e6, lane_ops, 100 * lane_ops / VALU_PEAK_TLANE, VALU_PEAK_TLANE))
+        log("  whole build: %.2f GB algorithmic, %.1f GB/s (%.1f%% of peak)"
+            % (build_bytes / 1e9, build_gbs, 100 * build_gbs / HBM_PEAK_GBS))
         if not args.no_counters:
-            log("bench: rocprofv3 FETCH_SIZE / WRITE_SIZE runs for %s" % dom)
-            tr = counter_traffic(name, dom, widest=args.widest)
-            if tr:
-                total = tr["FETCH_SIZE"]["bytes"] + tr["WRITE_SIZE"]["bytes"]
-                roofline["traffic"] = int(total)
-                roofline["traffic_detail"] = {
-                    "fetch_bytes": int(tr["FETCH_SIZE"]["bytes"]),
-                    "write_bytes": int(tr["WRITE_SIZE"]["bytes"]),
-                    "counter_scale": {"FETCH_SIZE": tr["FETCH_SIZE"]["scale"],
-                                      "WRITE_SIZE": tr["WRITE_SIZE"]["scale"]},
-                    "GBps": round(total / (d["avg_us"] * 1e-6) / 1e9, 1)}
-                log("  traffic %s" % roofline["traffic_detail"])
+            log("bench: rocprofv3 counter runs (FETCH_SIZE + SQ_INSTS_VALU, then WRITE_SIZE)")
+            got = counter_runs(name, widest=args.widest)
+            if got:
+                ckinds, scales, builds = got
+                roofline["counter_scale_fetch"] = round(scales["FETCH_SIZE"], 3)
+                roofline["counter_scale_write"] = round(scales["WRITE_SIZE"], 3)
+                counter_build, counter_pass = 0.0, 0.0
+                for kind, kv in kernels.items():
+                    c = ckinds.get(kind)
+                    if not c:
+                        continue
+                    cb = (c["fetch"] + c["write"]) / builds  # per build
+                    counter_build += cb
+                    if kind in passes:
+                        counter_pass += cb
+                    kv.update({"counter_fetch_per_build": int(c["fetch"] / builds),
+                               "counter_write_per_build": int(c["write"] / builds),
+                               "counter_GBps": round(cb / (kv["ms_per_build"] * 1e-3) / 1e9, 1),
+                               "counter_over_algorithmic": round(cb / kv["bytes_per_build"], 3)
+                               if kv["bytes_per_build"] else None,
+                               "valu_per_launch": int(c["valu"] / max(c["dispatches"], 1))})
+                    log("  %-36s counters %8.1f MB/build (%.2fx algorithmic), %8.1f GB/s"
+                        % (kind, cb / 1e6, kv["counter_over_algorithmic"] or 0.0, kv["counter_GBps"]))
+                c = ckinds.get(dom)
+                if c and c["dispatches"]:
+                    per_launch = (c["fetch"] + c["write"]) / c["dispatches"]
+                    inst = c["valu"] / c["dispatches"]
+                    lane_ops = inst * 64 / (d["avg_us"] * 1e-6) / 1e12
+                    roofline.update({"traffic": int(per_launch),
+                                     "traffic_fetch": int(c["fetch"] / c["dispatches"]),
+                                     "traffic_write": int(c["write"] / c["dispatches"]),
+                                     "traffic_over_algorithmic": round(per_launch / d["bytes_per_launch"], 3),
+                                     "valu_instructions_per_launch": int(inst),
+                                     "valu_issue_frac": round(lane_ops / VALU_PEAK_TLANE, 4)})
+                roofline.update({"counter_build_bytes": int(counter_build),
+                                 "counter_build_GBps": round(counter_build / (ms_per_step * 1e-3) / 1e9, 1)})
+                if pass_ms > 0:
+                    roofline["passes_counter_GBps"] = round(counter_pass / (pass_ms * 1e-3) / 1e9, 1)
+                log("  dominant %s: traffic %s B/launch (%.2fx algorithmic); whole build %.2f GB counted"
+                    % (dom, roofline["traffic"], roofline.get("traffic_over_algorithmic") or 0.0,
+                       counter_build / 1e9))
 
     base = None
     if not args.no_cpu_baseline:
-        sample = args.cpu_sample or n
-        log("bench: CPU oracle baseline on %d points" % sample)
-        base = cpu_baseline(name, sample, widest=args.widest)
+        log("bench: CPU oracle baseline (all threads on %d points, one thread on %d)"
+            % (min(args.cpu_sample, n), min(args.cpu_sample_one, n)))
+        base = cpu_baseline(name, args.cpu_sample, args.cpu_sample_one, widest=args.widest)
         log("  %s" % base)
 
+    if name == datagen.HEADLINE:
+        metric = ("k-d tree (split widest dimension) build Mpoints/s at N=16M k=3 fp32; achieved HBM GB/s vs peak"
+                  if args.widest else "k-d tree build Mpoints/s at N=16M k=3 fp32; achieved HBM GB/s vs peak")
+    else:
+        metric = "k-d tree %sbuild Mpoints/s at N=%d k=%d fp32 (%s); achieved HBM GB/s vs peak" % (
+            "(split widest dimension) " if args.widest else "", n, k, name)
     out = {
-        "metric": ("k-d tree (split widest dimension) build Mpoints/s at N=16M k=3 fp32; achieved HBM GB/s vs peak"
-                   if args.widest else "k-d tree build Mpoints/s at N=16M k=3 fp32; achieved HBM GB/s vs peak"),
+        "metric": metric,
         "value": round(value, 2),
         "unit": "Mpoints/s",
         "n_gpus": 1,
@@ -479,7 +536,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u32",
+        "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": name, "n_points": n, "k": k, "coords": "f32",
                    "description": w.note},

@@ -145,6 +145,14 @@ int64_t kdt_closed_segment_begin(int64_t N, int64_t s, int32_t l);
 int64_t kdt_closed_live_segment(int64_t N, int32_t l, int64_t p);
 int64_t kdt_closed_bin_prefix(int64_t N, int32_t l1, int32_t delta, int64_t j0, int64_t b);
 
+/* Host copy of the coordinate key every kernel compares (no HIP call), for
+ * tests: keys_out[i] = key of the float32 bit pattern bits[i], an unsigned
+ * 32-bit value whose order is IEEE '<' on the floats, with -0.0 and +0.0
+ * mapped to one key (the problem statement's k-d condition compares values,
+ * and the tie-break is the index). NaN patterns get some key (outside the
+ * definition). n < 0 or NULL pointers with n > 0: nothing is written. */
+void kdt_closed_float_keys(const uint32_t* bits, int64_t n, uint32_t* keys_out);
+
 /* Split-widest-dimension variant ([W], split-widest-dimension section).
  * The same left-balanced complete level-order tree, except that node s
  * splits along the dimension in which its domain is widest: the root's

@@ -1,0 +1,103 @@
+"""The one-call helpers (kdt.build, build_widest, unique, knn) on a side stream.
+
+Each helper allocates its workspace (and outputs) itself and returns as soon
+as the work is enqueued on the given stream. The test holds that stream back
+with a bounded GPU sleep, frees every helper temporary at once, then has the
+default stream allocate and overwrite memory of the same sizes. The results,
+read after both streams finish, must still be the oracle's: the helpers mark
+their tensors as used on the side stream, so the caching allocator cannot
+hand that memory to the default stream while the side stream still uses it.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import knn as knn_oracle
+from oracle import unique as unique_oracle
+from tree_construction_amd import datagen, kdt
+
+pytestmark = pytest.mark.gpu
+
+SLEEP_CYCLES = 50_000_000  # about 20 ms of GPU spin on the side stream
+
+
+def say(msg):
+    sys.stdout.write(msg + "\n")
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a HIP device")
+    return torch, torch.device("cuda:0")
+
+
+def clobber(torch, dev, nbytes):
+    """Allocate and overwrite memory on the default stream (it would reuse any
+    freed block the allocator believes idle)."""
+    junk = [torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev).fill_(0xA5) for _ in range(3)]
+    return junk
+
+
+def test_helpers_on_a_side_stream_survive_reuse(torch_dev):
+    torch, dev = torch_dev
+    pts = datagen.ties(400000, 3, 21)
+    n, k = pts.shape
+    x = torch.from_numpy(pts).to(dev)
+    side = torch.cuda.Stream(dev)
+    torch.cuda.synchronize(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+
+    say("case side-stream build N=%d k=%d" % (n, k))
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(SLEEP_CYCLES)
+    perm, tree = kdt.build(x, stream=side)
+    junk = clobber(torch, dev, kdt.workspace_size(n, k))
+    torch.cuda.synchronize(dev)
+    del junk
+    expected = oracle.build_tree(pts)
+    assert np.array_equal(perm.cpu().numpy(), expected)
+    assert np.array_equal(tree.cpu().numpy().view(np.uint32), pts[expected].view(np.uint32))
+
+    say("case side-stream build_widest N=%d k=%d" % (n, k))
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(SLEEP_CYCLES)
+    perm_w, _, dims_w = kdt.build_widest(x, want_tree=False, stream=side)
+    junk = clobber(torch, dev, kdt.workspace_size_widest(n, k))
+    torch.cuda.synchronize(dev)
+    del junk
+    exp_perm_w, exp_dims_w = oracle.build_tree_widest(pts)
+    assert np.array_equal(perm_w.cpu().numpy(), exp_perm_w)
+    assert np.array_equal(dims_w.cpu().numpy(), exp_dims_w)
+
+    say("case side-stream unique N=%d k=%d" % (n, k))
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(SLEEP_CYCLES)
+    # unique() waits for the side stream itself before reading the count
+    kept = kdt.unique(x, stream=side)
+    junk = clobber(torch, dev, kdt.unique_workspace_size(n, k))
+    torch.cuda.synchronize(dev)
+    del junk
+    assert np.array_equal(kept.cpu().numpy(), unique_oracle.unique_indices(pts))
+
+    say("case side-stream knn Q=4096 K=8")
+    qs = datagen.uniform(4096, 3, 22)
+    q = torch.from_numpy(qs).to(dev)
+    tree_d = torch.from_numpy(pts[expected]).to(dev)
+    perm_d = torch.from_numpy(expected).to(dev)
+    torch.cuda.synchronize(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(SLEEP_CYCLES)
+    idx, d2 = kdt.knn(tree_d, perm_d, q, 8, stream=side)
+    junk = clobber(torch, dev, 4096 * 8 * 4)
+    torch.cuda.synchronize(dev)
+    del junk
+    want_idx, want_d2 = knn_oracle.knn(pts, qs, 8)
+    assert np.array_equal(idx.cpu().numpy(), want_idx)
+    assert np.array_equal(d2.cpu().numpy().view(np.uint32), want_d2.view(np.uint32))
+

@@ -3173,6 +3173,11 @@ int64_t kdt_closed_bin_prefix(int64_t N, int32_t l1, int32_t delta, int64_t j0, 
     return (int64_t)bin_prefix(g, (u64)j0, (u32)b, l1, delta);
 }
 
+void kdt_closed_float_keys(const uint32_t* bits, int64_t n, uint32_t* keys_out) {
+    if (n <= 0 || !bits || !keys_out) return;
+    for (int64_t i = 0; i < n; ++i) keys_out[i] = float_key(bits[i]);
+}
+
 const char* kdt_status_string(kdt_status status) {
     switch (status) {
         case KDT_OK: return "ok";

@@ -49,6 +49,7 @@ SIGNATURES = {
     "kdt_debug_workspace_size": (_SZ, [_I64, _I32, _I32]),
     "kdt_closed_live_segment": (_I64, [_I64, _I32, _I64]),
     "kdt_closed_bin_prefix": (_I64, [_I64, _I32, _I32, _I64, _I64]),
+    "kdt_closed_float_keys": (None, [_VOIDP, _I64, _VOIDP]),
     "kdt_knn": (ctypes.c_int, [_VOIDP, _VOIDP, _VOIDP, _I64, _I32, _VOIDP, _I64, _I32, _VOIDP, _VOIDP, _VOIDP,
                                _VOIDP]),
     "kdt_knn_budget": (ctypes.c_int, [_VOIDP, _VOIDP, _VOIDP, _I64, _I32, _VOIDP, _I64, _I32, _VOIDP, _VOIDP,
@@ -118,6 +119,16 @@ def closed_bin_prefix(n: int, l1: int, delta: int, j0: int, b: int) -> int:
     return int(lib().kdt_closed_bin_prefix(int(n), int(l1), int(delta), int(j0), int(b)))
 
 
+def closed_float_keys(bits):
+    """Keys of float32 bit patterns (a uint32 numpy array), computed by the
+    library's host copy of the kernels' key transform."""
+    import numpy as np
+    b = np.ascontiguousarray(bits, dtype=np.uint32)
+    out = np.empty_like(b)
+    lib().kdt_closed_float_keys(b.ctypes.data, b.size, out.ctypes.data)
+    return out
+
+
 def _check(status: int, where: str):
     if status != KDT_OK:
         raise KdtError(status, where)
@@ -127,6 +138,18 @@ def _stream_handle(device, stream):
     import torch
     s = stream if stream is not None else torch.cuda.current_stream(device)
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _used_on(stream, device, *tensors):
+    """Mark tensors that kernels enqueued on `stream` use, when that stream is
+    not the current one: the caching allocator then keeps their memory until
+    that work is done, even if the tensors are freed earlier."""
+    import torch
+    if stream is None or stream == torch.cuda.current_stream(device):
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
 
 
 def _validate_points(points):
@@ -167,6 +190,7 @@ class Builder:
                              ctypes.c_void_p(self.workspace.data_ptr()), self.workspace_bytes,
                              _stream_handle(points.device, stream))
         _check(st, "kdt_build")
+        _used_on(stream, points.device, self.workspace, points, perm, tree)
         return perm, tree
 
     def build_profiled(self, points, perm, tree=None, stream=None):
@@ -195,6 +219,7 @@ class Builder:
                                   ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
                                   nbytes, _stream_handle(points.device, stream))
         _check(st, "kdt_debug_tags")
+        _used_on(stream, points.device, ws, points, out)
         return out
 
 
@@ -230,6 +255,7 @@ class UniqueFinder:
         if keep is None:
             keep = torch.empty(max(self.n, 1), dtype=torch.int32, device=points.device)
         _check(lib().kdt_unique(*self._args(points, keep, stream)), "kdt_unique")
+        _used_on(stream, points.device, self.workspace, self.count, points, keep)
         return keep, self.count
 
     def run_profiled(self, points, keep, stream=None):
@@ -244,9 +270,12 @@ def unique(points, stream=None):
     """Ascending original indices of one point (the smallest index) of every
     distinct tuple of `points` ((N, k) float32 on a HIP device): an int32
     device tensor (synchronises to read the count)."""
+    import torch
     _validate_points(points)
     n, k = points.shape
     keep, count = UniqueFinder(n, k, points.device).run(points, stream=stream)
+    # the count is written on `stream`: wait for that stream, not the current one
+    (stream if stream is not None else torch.cuda.current_stream(points.device)).synchronize()
     return keep[: int(count.item())]
 
 
@@ -289,6 +318,7 @@ class WidestBuilder:
                                     ctypes.c_void_p(self.workspace.data_ptr()), self.workspace_bytes,
                                     _stream_handle(points.device, stream))
         _check(st, "kdt_build_widest")
+        _used_on(stream, points.device, self.workspace, points, perm, tree, dims)
         return perm, tree, dims
 
     def build_profiled(self, points, perm, tree=None, dims=None, stream=None):
@@ -361,4 +391,5 @@ def knn(tree, perm, queries, K: int, idx=None, d2=None, visits=None, stream=None
     else:
         st = lib().kdt_knn_budget(*args, int(budget), _stream_handle(queries.device, stream))
     _check(st, "kdt_knn")
+    _used_on(stream, queries.device, tree, perm, dims, queries, idx, d2, visits)
     return idx, d2
