@@ -32,7 +32,8 @@
  *   - All pointers marked "device" are HIP device pointers on the current
  *     device. The caller owns every buffer; the library allocates nothing,
  *     keeps no global state and is re-entrant: calls on different streams
- *     with different workspaces may run concurrently.
+ *     with different workspaces may run concurrently. The one exception is
+ *     kdt_build_static, whose workspace is a static device array per GPU.
  *   - All work is enqueued on `stream` (0 = the null stream) and the call
  *     returns before it finishes; synchronise the stream before reading
  *     outputs. Argument errors are detected before anything is enqueued.
@@ -57,7 +58,8 @@ typedef enum {
     KDT_OK = 0,
     KDT_ERR_INVALID_ARG = 1, /* bad N or k, NULL pointer, overlapping buffers */
     KDT_ERR_WORKSPACE = 2,   /* workspace NULL or smaller than kdt_workspace_size() */
-    KDT_ERR_HIP = 3          /* a kernel launch failed (hipGetLastError) */
+    KDT_ERR_HIP = 3,         /* a kernel launch failed (hipGetLastError) */
+    KDT_ERR_TOO_LARGE = 4    /* kdt_build_static: N, k need more than its scratch array */
 } kdt_status;
 
 /* Bytes of device workspace kdt_build() needs for N points of dimension k.
@@ -81,6 +83,25 @@ kdt_status kdt_build(const float* points, int64_t N, int32_t k,
                      int32_t* perm_out, float* tree_out,
                      void* workspace, size_t workspace_bytes,
                      hipStream_t stream);
+
+/* Allocation-free build, for callers that cannot call hipMalloc (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * Identical to kdt_build, except that the workspace is a file-scope device
+ * array of KDT_STATIC_SCRATCH_BYTES bytes inside the library (one per GPU,
+ * held until the process ends; its device address is looked up once per
+ * device on the first call made with that device current). The caller still
+ * passes the points and the outputs, as for kdt_build.
+ *   Returns KDT_ERR_TOO_LARGE, before anything is enqueued, when
+ *   kdt_workspace_size(N, k) > KDT_STATIC_SCRATCH_BYTES (for k = 3 that is
+ *   N above about 570,000 points).
+ *   Every call on one GPU shares that GPU's array and it keeps the last
+ *   call's contents (the build needs no zeroed workspace). Calls that overlap
+ *   on one GPU (on different streams, or from several threads without
+ *   ordering) race on it and give unspecified outputs: serialise them.
+ * Other arguments, the stream rule and the errors are those of kdt_build. */
+#define KDT_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+kdt_status kdt_build_static(const float* points, int64_t N, int32_t k,
+                            int32_t* perm_out, float* tree_out, hipStream_t stream);
 
 /* Diagnostic: run only the first `rounds` sort+update rounds (0 <= rounds
  * <= numLevels(N) - 1) over the whole point set and copy every point's tag

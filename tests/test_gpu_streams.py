@@ -101,3 +101,21 @@ def test_helpers_on_a_side_stream_survive_reuse(torch_dev):
     assert np.array_equal(idx.cpu().numpy(), want_idx)
     assert np.array_equal(d2.cpu().numpy().view(np.uint32), want_d2.view(np.uint32))
 
+
+def test_static_build_on_a_side_stream(torch_dev):
+    torch, dev = torch_dev
+    pts = datagen.gaussian_mixture(200000, 3, 23)
+    x = torch.from_numpy(pts).to(dev)
+    side = torch.cuda.Stream(dev)
+    torch.cuda.synchronize(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    say("case side-stream static build N=%d" % len(pts))
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(SLEEP_CYCLES)
+    perm, tree = kdt.build_static(x, stream=side)
+    junk = clobber(torch, dev, 4 * len(pts) * 4)
+    torch.cuda.synchronize(dev)
+    del junk
+    expected = oracle.build_tree(pts)
+    assert np.array_equal(perm.cpu().numpy(), expected)
+    assert np.array_equal(tree.cpu().numpy().view(np.uint32), pts[expected].view(np.uint32))

@@ -39,6 +39,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 #include <vector>
 
@@ -3043,6 +3044,37 @@ kdt_status run_profiled(hipStream_t stream, kdt_profile* profile, Build build) {
 
 }  // namespace
 
+// ------------------------------------------ allocation-free entry point
+// kdt_build_static runs kdt_build with this file-scope device array as its
+// workspace, for callers that cannot allocate. Each device holds its own
+// copy for the life of the process. In host code `scratch` names a host-side
+// stand-in, never the device memory: the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[KDT_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call per device).
+kdt_status scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KDT_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KDT_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return KDT_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t kdt_workspace_size(int64_t N, int32_t k) {
@@ -3064,6 +3096,19 @@ kdt_status kdt_build(const float* points, int64_t N, int32_t k, int32_t* perm_ou
                      float* tree_out, void* workspace, size_t workspace_bytes,
                      hipStream_t stream) {
     return build_impl(points, N, k, perm_out, tree_out, workspace, workspace_bytes, stream,
+                      Timer{nullptr});
+}
+
+kdt_status kdt_build_static(const float* points, int64_t N, int32_t k, int32_t* perm_out,
+                            float* tree_out, hipStream_t stream) {
+    if (!valid_size(N, k)) return KDT_ERR_INVALID_ARG;
+    if (kdt_workspace_size(N, k) > KDT_STATIC_SCRATCH_BYTES) return KDT_ERR_TOO_LARGE;
+    void* ws = nullptr;
+    if (N > 1) {
+        const kdt_status st = scratch_address(&ws);
+        if (st != KDT_OK) return st;
+    }
+    return build_impl(points, N, k, perm_out, tree_out, ws, KDT_STATIC_SCRATCH_BYTES, stream,
                       Timer{nullptr});
 }
 
@@ -3184,6 +3229,7 @@ const char* kdt_status_string(kdt_status status) {
         case KDT_ERR_INVALID_ARG: return "invalid argument";
         case KDT_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
         case KDT_ERR_HIP: return "HIP kernel launch failed";
+        case KDT_ERR_TOO_LARGE: return "N and k need more workspace than the static scratch array holds";
     }
     return "unknown status";
 }

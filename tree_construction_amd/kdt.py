@@ -15,7 +15,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libkdt.so")
 
 KDT_OK = 0
-STATUS_NAMES = {0: "KDT_OK", 1: "KDT_ERR_INVALID_ARG", 2: "KDT_ERR_WORKSPACE", 3: "KDT_ERR_HIP"}
+STATUS_NAMES = {0: "KDT_OK", 1: "KDT_ERR_INVALID_ARG", 2: "KDT_ERR_WORKSPACE", 3: "KDT_ERR_HIP",
+                4: "KDT_ERR_TOO_LARGE"}
+STATIC_SCRATCH_BYTES = 64 << 20  # KDT_STATIC_SCRATCH_BYTES
 
 PROFILE_MAX_KINDS = 32
 PROFILE_NAME_LEN = 48
@@ -41,6 +43,7 @@ _VOIDP, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctype
 SIGNATURES = {
     "kdt_workspace_size": (_SZ, [_I64, _I32]),
     "kdt_build": (ctypes.c_int, [_VOIDP, _I64, _I32, _VOIDP, _VOIDP, _VOIDP, _SZ, _VOIDP]),
+    "kdt_build_static": (ctypes.c_int, [_VOIDP, _I64, _I32, _VOIDP, _VOIDP, _VOIDP]),
     "kdt_debug_tags": (ctypes.c_int, [_VOIDP, _I64, _I32, _I32, _VOIDP, _VOIDP, _SZ, _VOIDP]),
     "kdt_build_profiled": (ctypes.c_int, [_VOIDP, _I64, _I32, _VOIDP, _VOIDP, _VOIDP, _SZ, _VOIDP,
                                           ctypes.POINTER(Profile)]),
@@ -341,6 +344,24 @@ def build_widest(points, want_tree: bool = True, stream=None):
     _validate_points(points)
     n, k = points.shape
     return WidestBuilder(n, k, points.device).build(points, want_tree=want_tree, stream=stream)
+
+
+def build_static(points, want_tree: bool = True, stream=None):
+    """The build of `points` through kdt_build_static: the library's static
+    scratch array is the workspace, so only the outputs are allocated here.
+    Sizes whose workspace exceeds STATIC_SCRATCH_BYTES raise KdtError
+    (KDT_ERR_TOO_LARGE). Calls that overlap on one GPU race on that array."""
+    import torch
+    _validate_points(points)
+    n, k = points.shape
+    perm = torch.empty(n, dtype=torch.int32, device=points.device)
+    tree = torch.empty_like(points) if want_tree else None
+    st = lib().kdt_build_static(ctypes.c_void_p(points.data_ptr()), n, k, ctypes.c_void_p(perm.data_ptr()),
+                                ctypes.c_void_p(tree.data_ptr() if tree is not None else 0),
+                                _stream_handle(points.device, stream))
+    _check(st, "kdt_build_static")
+    _used_on(stream, points.device, points, perm, tree)
+    return perm, tree
 
 
 def build(points, want_tree: bool = True, stream=None):
