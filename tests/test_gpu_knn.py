@@ -183,13 +183,40 @@ def test_knn_headline_workload_sampled(torch_dev):
     perm, tree = kdt.build(x)
     K = 8
     say("case knn %s Q=%d K=%d" % (name, len(qs), K))
-    idx, d2 = kdt.knn(tree, perm, q, K)
+    visits = torch.empty(len(qs), dtype=torch.int32, device=dev)
+    idx, d2 = kdt.knn(tree, perm, q, K, visits=visits)
     torch.cuda.synchronize(dev)
-    idx, d2 = idx.cpu().numpy(), d2.cpu().numpy()
+    idx, d2, v = idx.cpu().numpy(), d2.cpu().numpy(), visits.cpu().numpy()
+    # the 100 most expensive searches (the first pass hands them to the wave
+    # pass: more than max(256, 64 K) points examined), 256 random ones, and
+    # the first and last query
+    costly = np.argsort(-v.astype(np.int64), kind="stable")[:100]
+    assert v[costly[-1]] > max(256, 64 * K), "the sample must include wave-pass queries"
     rng = np.random.default_rng(17)
-    sample = np.sort(rng.choice(len(qs), 24, replace=False))
-    sample[0] = 0
-    sample[-1] = len(qs) - 1
+    sample = np.unique(np.concatenate([costly, rng.choice(len(qs), 256, replace=False), [0, len(qs) - 1]]))
+    say("  checking %d queries against brute force" % len(sample))
     want_idx, want_d2 = knn_oracle.knn(pts, qs[sample], K)
     assert np.array_equal(idx[sample], want_idx)
     assert np.array_equal(d2[sample].view(np.uint32), want_d2.view(np.uint32))
+
+
+def test_knn_wave_stack_overflow(torch_dev):
+    """Identical points never prune (a far side is skipped only when strictly
+    farther than the K-th distance), so the wave pass's shared stack outgrows
+    its LDS and lanes finish subtrees alone; the answer is still the K
+    smallest indices."""
+    torch, dev = torch_dev
+    pts = datagen.all_equal(50000, 3)
+    x = torch.from_numpy(pts).to(dev)
+    perm, tree = kdt.build(x)
+    qs = np.concatenate([pts[:8], datagen.uniform(56, 3, 41)]).astype(np.float32)
+    q = torch.from_numpy(qs).to(dev)
+    for K in (1, 8, 32):
+        say("case knn wave overflow N=50000 K=%d budget=0" % K)
+        visits = torch.empty(len(qs), dtype=torch.int32, device=dev)
+        idx, d2 = kdt.knn(tree, perm, q, K, visits=visits, budget=0)
+        torch.cuda.synchronize(dev)
+        want_idx, want_d2 = knn_oracle.knn(pts, qs, K)
+        assert np.array_equal(idx.cpu().numpy(), want_idx)
+        assert np.array_equal(d2.cpu().numpy().view(np.uint32), want_d2.view(np.uint32))
+        assert (visits.cpu().numpy() == 50000).all()

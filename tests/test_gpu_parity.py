@@ -184,7 +184,7 @@ def test_side_streams_and_determinism(torch_dev):
     ba, bb = kdt.Builder(*pts_a.shape, dev), kdt.Builder(*pts_b.shape, dev)
     sa, sb = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
     torch.cuda.synchronize(dev)
-    for rep in range(5):
+    for rep in range(20):
         say("case streams rep=%d" % rep)
         with torch.cuda.stream(sa):
             pa, _ = ba.build(xa, want_tree=False)
