@@ -1985,6 +1985,432 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
     }
 }
 
+// ------------------------- subtree stage from records with every coordinate
+// The subtree stage for k <= kCachedDims, where the records of the last
+// global round carry all k coordinate keys: the same rounds as k_subtree,
+// organised so that each record is read once as one vector, and every radix
+// pass in LDS moves one 32-bit word per point. A pass sorts a value stably:
+// the value less its minimum over the subtree, so that only the bits in which
+// the subtree's values differ are sorted (for a level-12 subtree of the
+// headline workload about 19 bits of a coordinate key), in passes of at most
+// 8 bits; as soon as the unsorted rest fits 20 bits it travels together with
+// a 12-bit payload (the point's arrival position or slot) in one word.
+// Positions past the subtree's size hold padding that sorts last and whose
+// tag is never live, so no per-item loop tests for them.
+constexpr int kPay = 12;  // bits of a slot or an arrival position
+static_assert(kLocalMax <= (1 << kPay), "a slot fits the payload");
+constexpr u32 kPadTag = 0xffffu;  // tag of a padding slot: never on a level
+
+struct RecScratch {
+    u32 exch[2][kLocalMax];                // record exchange; the rounds' segment counters
+    uint16_t count[kLocalWaves][kRadix];   // per-wave digit counters of a pass
+    u32 start[kRadix];                     // first position of each digit
+    u32 wave[kLocalWaves];
+    u32 red[2 * (kCachedDims + 1)][kLocalWaves];  // per-wave minima and maxima
+    uint16_t dummy[64];                    // counter of the items a round does not rank
+};
+
+struct RecShared {
+    union {
+        struct {
+            uint16_t tag[kLocalMax];                 // local tag of each slot
+            uint16_t order[kCachedDims][kLocalMax];  // slots by (coordinate d, index)
+            RecScratch s;
+        } m;
+        uint4 rows[kLocalMax];  // output: the record of each local node
+    };
+};
+
+// Lanes below this one in a 64-bit lane mask.
+__device__ __forceinline__ u32 lanes_below(u32 m_lo, u32 m_hi) {
+    return __builtin_amdgcn_mbcnt_hi(m_hi, __builtin_amdgcn_mbcnt_lo(m_lo, 0u));
+}
+
+// One stable pass by the low `bits` bits of each item's unsorted value.
+// Wide form: hi = the value, lo = the payload. Narrow form: hi = value << kPay
+// | payload. The pass drops the sorted bits; kWideOut keeps the wide form
+// (the rest does not fit 32 - kPay bits yet).
+template <bool kWideIn, bool kWideOut>
+__device__ __forceinline__ void rec_pass(u32 (&hi)[kLocalItems], u32 (&lo)[kLocalItems], int bits,
+                                         RecScratch& s) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const u32 mask = (1u << bits) - 1, bins = 1u << bits;
+    uint16_t* cnt = s.count[w];
+    // (cleared through the same type the ranking reads: no barrier between)
+    for (u32 i = lane; i < bins; i += 64) cnt[i] = 0;
+    auto digit = [&](int j) { return (kWideIn ? hi[j] : hi[j] >> kPay) & mask; };
+    u32 rank[kLocalItems];
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) {
+        const u32 d = digit(j);
+        u32 miss_lo = 0, miss_hi = 0;
+        for (int b = 0; b < bits; ++b) match_bit(d, b, miss_lo, miss_hi);
+        const u32 before = lanes_below(~miss_lo, ~miss_hi);
+        const u32 seen = cnt[d];
+        rank[j] = seen + before;
+        // every lane of the digit writes the same count
+        cnt[d] = (uint16_t)(seen + __popc(~miss_lo) + __popc(~miss_hi));
+    }
+    __syncthreads();
+    // per digit: prefix over the waves, then the exclusive scan of the totals
+    u32 agg = 0;
+    if ((u32)tid < bins) {
+#pragma unroll
+        for (int v = 0; v < kLocalWaves; ++v) {
+            const u32 c = s.count[v][tid];
+            s.count[v][tid] = (uint16_t)agg;
+            agg += c;
+        }
+    }
+    const u32 inc = wave_inclusive_scan(agg);
+    if (lane == 63) s.wave[w] = inc;
+    __syncthreads();
+    if ((u32)tid < bins) {
+        u32 off = 0;
+#pragma unroll
+        for (int i = 0; i < kLocalWaves; ++i)
+            if (i < w) off += s.wave[i];
+        s.start[tid] = off + inc - agg;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) {
+        const u32 d = digit(j);
+        const u32 pos = s.start[d] + s.count[w][d] + rank[j];
+        if constexpr (kWideOut) {
+            s.exch[0][pos] = hi[j] >> bits;
+            s.exch[1][pos] = lo[j];
+        } else {
+            const u32 rest = kWideIn ? hi[j] >> bits : hi[j] >> (kPay + bits);
+            const u32 pay = kWideIn ? lo[j] : hi[j] & ((1u << kPay) - 1);
+            s.exch[0][pos] = (rest << kPay) | pay;
+        }
+    }
+    __syncthreads();
+    // (the next pass's first barrier orders these reads before its writes)
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) {
+        const int q = local_slot(j);
+        hi[j] = s.exch[0][q];
+        if constexpr (kWideOut) lo[j] = s.exch[1][q];
+    }
+}
+
+// Stable sort of the items (value v[j] below 2^vbits, payload pay[j]) from
+// their current order; returns with pay[j] = the payload of the item at
+// position local_slot(j). vbits = 0: nothing to sort.
+__device__ __forceinline__ void rec_sort(u32 (&v)[kLocalItems], u32 (&pay)[kLocalItems], int vbits,
+                                         RecScratch& s) {
+    if (vbits == 0) return;
+    const int passes = (vbits + kRadixBits - 1) / kRadixBits;
+    int left = vbits;
+    bool wide = true;
+    for (int p = 0; p < passes; ++p) {
+        const int bits = (left + (passes - p) - 1) / (passes - p);
+        const bool out_wide = left - bits > 32 - kPay;
+        if (wide && out_wide) rec_pass<true, true>(v, pay, bits, s);
+        else if (wide) rec_pass<true, false>(v, pay, bits, s);
+        else rec_pass<false, false>(v, pay, bits, s);
+        wide = out_wide;
+        left -= bits;
+    }
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) pay[j] = v[j] & ((1u << kPay) - 1);
+}
+
+// Workgroup minimum and maximum of each of kV values, from each thread's own.
+template <int kV>
+__device__ __forceinline__ void rec_min_max(u32 (&mn)[kV], u32 (&mx)[kV], RecScratch& s) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < kV; ++i) {
+        u32 a = mn[i], b = mx[i];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const u32 oa = __shfl_xor(a, o, 64), ob = __shfl_xor(b, o, 64);
+            a = oa < a ? oa : a;
+            b = ob > b ? ob : b;
+        }
+        if (lane == 0) {
+            s.red[2 * i][w] = a;
+            s.red[2 * i + 1][w] = b;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kV; ++i) {
+        u32 a = ~0u, b = 0;
+#pragma unroll
+        for (int v = 0; v < kLocalWaves; ++v) {
+            a = s.red[2 * i][v] < a ? s.red[2 * i][v] : a;
+            b = s.red[2 * i + 1][v] > b ? s.red[2 * i + 1][v] : b;
+        }
+        // uniform over the workgroup: scalar registers
+        mn[i] = __builtin_amdgcn_readfirstlane(a);
+        mx[i] = __builtin_amdgcn_readfirstlane(b);
+    }
+}
+
+// Bits that values 0 .. span (and the padding value above them) need.
+__device__ __forceinline__ int value_bits(u32 span) { return span == ~0u ? 32 : 32 - __clz(span + 1); }
+
+// Round t in LDS, as local_round, over a subtree whose padding slots carry
+// kPadTag: per-wave counters of the 2^t segments live in the exchange
+// buffers (16-bit, 8 x 2048 at most); items that are not live count into a
+// dummy and write their tag back unchanged.
+__device__ __forceinline__ void rec_round(const uint16_t* order, int t, const Geometry& lg, RecShared& sh) {
+    RecScratch& s = sh.m.s;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const u32 fl = (1u << t) - 1, segs = 1u << t;
+    uint16_t* cnt = reinterpret_cast<uint16_t*>(&s.exch[0][0]);  // [kLocalWaves][segs]
+    u32* cnt_words = &s.exch[0][0];
+    const u32 words = (kLocalWaves * segs + 1) / 2;
+    for (u32 i = tid; i < words; i += kLocalBlock) cnt_words[i] = 0;
+    __syncthreads();
+    u32 e[kLocalItems], st[kLocalItems], rank[kLocalItems];
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) {
+        e[j] = order[local_slot(j)];
+        st[j] = sh.m.tag[e[j]];
+        const u32 b = st[j] - fl;
+        const bool live = b < segs;
+        u32 miss_lo = 0, miss_hi = 0;
+        for (int bit = 0; bit < t; ++bit) match_bit(b, bit, miss_lo, miss_hi);
+        const u64 lv = __ballot(live);
+        const u32 p_lo = (u32)lv & ~miss_lo, p_hi = (u32)(lv >> 32) & ~miss_hi;
+        const u32 before = lanes_below(p_lo, p_hi);
+        uint16_t* cp = live ? &cnt[w * segs + b] : &s.dummy[lane];
+        const u32 seen = *cp;
+        rank[j] = seen + before;
+        *cp = (uint16_t)(seen + __popc(p_lo) + __popc(p_hi));
+    }
+    __syncthreads();
+    // prefix over the waves, two 16-bit counters a word (a segment's total
+    // is at most kLocalMax, so the halves never carry into each other)
+    if (segs >= 2) {
+        const u32 row = segs / 2;
+        for (u32 i = tid; i < row; i += kLocalBlock) {
+            u32 run = 0;
+#pragma unroll
+            for (int v = 0; v < kLocalWaves; ++v) {
+                const u32 c = cnt_words[v * row + i];
+                cnt_words[v * row + i] = run;
+                run += c;
+            }
+        }
+    } else if (tid == 0) {
+        u32 run = 0;
+#pragma unroll
+        for (int v = 0; v < kLocalWaves; ++v) {
+            const u32 c = cnt[v];
+            cnt[v] = (uint16_t)run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    // the pivot of segment s = F(t) + b has rank |S(2s+1)|: u - 1 full-level
+    // nodes and min(max(M - 2b u, 0), u) last-level ones (u = 2^(L-2-t))
+    const u32 dd = (u32)(lg.levels - 2 - t), u = 1u << dd, last = (u32)lg.last;
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) {
+        const u32 b = st[j] - fl;
+        const bool live = b < segs;
+        const u32 in_seg = cnt[w * segs + (live ? b : 0)] + rank[j];
+        const u32 under = (2 * b) << dd;
+        const u32 left = (u - 1) + (last > under ? (last - under < u ? last - under : u) : 0u);
+        const u32 next = in_seg < left ? 2 * st[j] + 1 : (in_seg > left ? 2 * st[j] + 2 : st[j]);
+        sh.m.tag[e[j]] = (uint16_t)(live ? next : st[j]);
+    }
+    __syncthreads();
+}
+
+template <int kK>
+__global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_recs(SubtreeArgs a) {
+    static_assert(kK >= 1 && kK <= kCachedDims, "every coordinate in the record");
+    constexpr int kW = kK + 1;  // record words: the keys, then the index
+    __shared__ RecShared sh;
+    RecScratch& s = sh.m.s;
+
+    const u64 c = full_nodes(a.l0) + blockIdx.x;  // subtree root (global node id)
+    const u32 nc = (u32)subtree_size(a.geo, c);
+    if (nc == 0) return;
+    // live position of the subtree's first point in round l0-1's order
+    const u64 parent = (c - 1) / 2;
+    const u64 seg = live_begin(a.geo, parent - full_nodes(a.l0 - 1), a.l0 - 1);
+    const u64 first = c == 2 * parent + 1 ? seg : seg + subtree_size(a.geo, 2 * parent + 1) + 1;
+    const u32* recs = a.recs + first * kW;
+    auto load_record = [&](u32 q, u32 (&r)[kW]) {
+        const u32* src = recs + (u64)(q < nc ? q : nc - 1) * kW;
+        if constexpr (kW == 4) {
+            const uint4 v = *reinterpret_cast<const uint4*>(src);
+            r[0] = v.x; r[1] = v.y; r[2] = v.z; r[3] = v.w;
+        } else if constexpr (kW == 2) {
+            const uint2 v = *reinterpret_cast<const uint2*>(src);
+            r[0] = v.x; r[1] = v.y;
+        } else {
+#pragma unroll
+            for (int f = 0; f < kW; ++f) r[f] = src[f];
+        }
+    };
+
+    // Word f of a record held as four registers (f uniform: selects, so that
+    // no register array is indexed at run time).
+    auto pick = [](const u32 (&r)[4], int f) {
+        return f == 0 ? r[0] : f == 1 ? r[1] : f == 2 ? r[2] : r[3];
+    };
+    // Dimensions: d_a arrived sorted (round l0-1's order: by coordinate d_a,
+    // then index); dA = d_a + 1 and dB = d_a + 2 (mod k), as far as k has
+    // them, are sorted here.
+    const int d_a = (a.l0 - 1) % kK;
+    const int dA = (d_a + 1) % kK, dB = (d_a + 2) % kK;
+    constexpr int kOther = kK - 1;
+    // While the slots are sorted, the tags and orders are unused: the other
+    // dimensions' keys wait there by arrival position.
+    u32* stash = reinterpret_cast<u32*>(&sh.m.tag[0]);
+    static_assert(sizeof(sh.m.tag) + sizeof(sh.m.order) >= 2 * kLocalMax * sizeof(u32), "stash");
+
+    // The records in arrival order, one vector load each: index and the
+    // other keys; minima and maxima over the subtree's points.
+    u32 idx[kLocalItems];
+    u32 mn[1 + kOther], mx[1 + kOther];
+#pragma unroll
+    for (int i = 0; i <= kOther; ++i) {
+        mn[i] = ~0u;
+        mx[i] = 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) {
+        const u32 q = (u32)local_slot(j);
+        u32 r[4] = {0, 0, 0, 0};
+        load_record(q, reinterpret_cast<u32(&)[kW]>(r));
+        const bool ok = q < nc;
+        idx[j] = r[kK];
+        mn[0] = ok && idx[j] < mn[0] ? idx[j] : mn[0];
+        mx[0] = ok && idx[j] > mx[0] ? idx[j] : mx[0];
+#pragma unroll
+        for (int u = 0; u < kOther; ++u) {
+            const u32 key = pick(r, u == 0 ? dA : dB);
+            stash[u * kLocalMax + q] = key;
+            mn[1 + u] = ok && key < mn[1 + u] ? key : mn[1 + u];
+            mx[1 + u] = ok && key > mx[1 + u] ? key : mx[1 + u];
+        }
+    }
+    rec_min_max<1 + kOther>(mn, mx, s);
+    int vbits[1 + kOther];
+    u32 pad[1 + kOther];
+#pragma unroll
+    for (int i = 0; i <= kOther; ++i) {
+        vbits[i] = value_bits(mx[i] - mn[i]);
+        pad[i] = vbits[i] == 32 ? ~0u : (1u << vbits[i]) - 1;  // above every point's value
+    }
+
+    // Slot = index rank: sort (index - min, arrival position).
+    u32 arr[kLocalItems];  // arrival position of the point in slot local_slot(j)
+    {
+        u32 v[kLocalItems];
+#pragma unroll
+        for (int j = 0; j < kLocalItems; ++j) {
+            const u32 q = (u32)local_slot(j);
+            v[j] = q < nc ? idx[j] - mn[0] : pad[0];
+            arr[j] = q;
+        }
+        rec_sort(v, arr, vbits[0], s);
+    }
+    // The other dimensions' keys by slot, straight from the stash; the second
+    // one waits in LDS again (by slot) while the first is sorted.
+    u32 key[kLocalItems], key2[kLocalItems];
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) {
+        const bool ok = (u32)local_slot(j) < nc;
+        if constexpr (kOther > 0) key[j] = ok ? stash[arr[j]] - mn[1] : pad[1];
+        if constexpr (kOther > 1) key2[j] = ok ? stash[kLocalMax + arr[j]] - mn[2] : pad[2];
+    }
+    __syncthreads();  // stash read before the tags and orders overwrite it
+    // Orders by role: [0] dimension d_a, [1] dA, [2] dB. The arrival order is
+    // d_a's: order[0][q] = slot of arrival position q (padding positions map
+    // to padding slots). dB's keys wait in roles 1 and 2 (one 16 KB range).
+    u32* wait2 = reinterpret_cast<u32*>(&sh.m.order[1][0]);
+    static_assert(sizeof(sh.m.order[1]) + sizeof(sh.m.order[2]) == kLocalMax * sizeof(u32), "one range");
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) {
+        const u32 e = (u32)local_slot(j);
+        sh.m.order[0][arr[j]] = (uint16_t)e;
+        sh.m.tag[e] = e < nc ? 0 : kPadTag;
+        if constexpr (kOther > 1) wait2[e] = key2[j];
+    }
+    // The other orders: stable sorts of (key - min, slot) from slot order.
+    if constexpr (kOther > 0) {
+        u32 pay[kLocalItems];
+#pragma unroll
+        for (int j = 0; j < kLocalItems; ++j) pay[j] = (u32)local_slot(j);
+        rec_sort(key, pay, vbits[1], s);
+        if constexpr (kOther > 1) {
+#pragma unroll
+            for (int j = 0; j < kLocalItems; ++j) key[j] = wait2[local_slot(j)];
+            __syncthreads();  // dB's keys read before role 1's order overwrites them
+        }
+#pragma unroll
+        for (int j = 0; j < kLocalItems; ++j) sh.m.order[1][local_slot(j)] = (uint16_t)pay[j];
+        if constexpr (kOther > 1) {
+#pragma unroll
+            for (int j = 0; j < kLocalItems; ++j) pay[j] = (u32)local_slot(j);
+            rec_sort(key, pay, vbits[2], s);
+#pragma unroll
+            for (int j = 0; j < kLocalItems; ++j) sh.m.order[2][local_slot(j)] = (uint16_t)pay[j];
+        }
+    }
+    __syncthreads();
+
+    const Geometry lg = make_geometry((i64)nc);
+    const int rounds = lg.levels - 1;
+    // round t splits dimension (l0 + t) mod k, whose role is (t + 1) mod k
+    for (int t = 0; t < rounds; ++t) rec_round(sh.m.order[(t + 1) % kK], t, lg, sh);
+
+    // Level-order output: each point's record (read again, one vector) goes
+    // to its node's row in LDS; the nodes of a local level are one
+    // contiguous range of global ids ((c << level) + node), written a word
+    // per thread.
+    u32 node[kLocalItems];
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) node[j] = sh.m.tag[sh.m.order[0][local_slot(j)]];
+    __syncthreads();  // the rows overlay the tags and orders
+    constexpr int kBatch = 4;  // records in flight at once
+#pragma unroll
+    for (int j0 = 0; j0 < kLocalItems; j0 += kBatch) {
+        u32 r[kBatch][4];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            r[j][0] = r[j][1] = r[j][2] = r[j][3] = 0;
+            load_record((u32)local_slot(j0 + j), reinterpret_cast<u32(&)[kW]>(r[j]));
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+            if ((u32)local_slot(j0 + j) < nc) sh.rows[node[j0 + j]] = make_uint4(r[j][0], r[j][1], r[j][2], r[j][3]);
+    }
+    __syncthreads();
+    auto word_of = [&](u32 n, int f) -> u32 {
+        const uint4 v = sh.rows[n];
+        return f == 0 ? v.x : f == 1 ? v.y : f == 2 ? v.z : v.w;
+    };
+    for (u32 n = threadIdx.x; n < nc; n += kLocalBlock) {
+        const u64 g = (c << level_of(n)) + n;
+        if (g < (u64)a.n) a.perm[g] = (int32_t)word_of(n, kK);
+    }
+    if (a.tree) {
+        for (u32 f = threadIdx.x; f < (u32)kK * nc; f += kLocalBlock) {
+            const u32 n = f / kK, dim = f - n * kK;
+            const u64 g = (c << level_of(n)) + n;
+            if (g >= (u64)a.n) continue;
+            const u32 key = word_of(n, (int)dim);
+            // a zero key (both zeros have it) is read back from the row,
+            // which keeps the sign of zero
+            const float x = key == 0x80000000u ? a.pts[(u64)word_of(n, kK) * kK + dim]
+                                               : __uint_as_float(key_bits(key));
+            a.tree[g * kK + dim] = x;
+        }
+    }
+}
+
 // ------------------------------- split-widest subtrees finished in LDS
 // The subtree stage for split-widest trees (k <= kCachedDims): the order of
 // every dimension is kept, and a level's nodes are ranked in one sub-round
@@ -2952,10 +3378,15 @@ kdt_status build_impl(const float* points, int64_t N, int32_t k, int32_t* perm_o
     const double in = l0 > 0 ? 4.0 * lay.words + 4.0 * (k - lay.kr) : row;
     // records that carry every coordinate are read in place, else staged
     const bool from_recs = recs && lay.words - 1 == k && k <= kCachedDims;
-    timer.begin(from_recs ? "k_subtree<true>" : "k_subtree<false>",
+    static const char* const kRecNames[kCachedDims + 1] = {"", "k_subtree_recs<1>", "k_subtree_recs<2>",
+                                                           "k_subtree_recs<3>"};
+    timer.begin(from_recs ? kRecNames[k] : "k_subtree<false>",
                 (double)below * (in + (from_recs ? 0.0 : 2 * (4 + row)) + 4 + (tree_out ? row : 0)));
-    if (from_recs) k_subtree<true><<<(unsigned)(1ull << l0), kLocalBlock, 0, stream>>>(sa);
-    else k_subtree<false><<<(unsigned)(1ull << l0), kLocalBlock, 0, stream>>>(sa);
+    const unsigned subtrees = (unsigned)(1ull << l0);
+    if (from_recs && k == 1) k_subtree_recs<1><<<subtrees, kLocalBlock, 0, stream>>>(sa);
+    else if (from_recs && k == 2) k_subtree_recs<2><<<subtrees, kLocalBlock, 0, stream>>>(sa);
+    else if (from_recs) k_subtree_recs<3><<<subtrees, kLocalBlock, 0, stream>>>(sa);
+    else k_subtree<false><<<subtrees, kLocalBlock, 0, stream>>>(sa);
     timer.end();
     return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
 }
