@@ -2026,6 +2026,23 @@ __device__ __forceinline__ u32 lanes_below(u32 m_lo, u32 m_hi) {
     return __builtin_amdgcn_mbcnt_hi(m_hi, __builtin_amdgcn_mbcnt_lo(m_lo, 0u));
 }
 
+// The lanes of `within` (a lane mask) whose low `bits` bits of d equal this
+// lane's: per bit, the lanes whose bit agrees with this lane's are NOT(vote
+// ^ own-bit-mask); the AND over the bits is kept with one three-input bit
+// operation per half (truth table 0x90 over (mask, vote, m): mask & ~(vote ^
+// m)), so no mask needs inverting or clearing.
+__device__ __forceinline__ void peer_mask(u32 d, int bits, u32 within_lo, u32 within_hi, u32& p_lo,
+                                          u32& p_hi) {
+    p_lo = within_lo;
+    p_hi = within_hi;
+    for (int b = 0; b < bits; ++b) {
+        const u32 m = (u32)__builtin_amdgcn_sbfe((int)d, b, 1);
+        const u64 vote = __ballot(m != 0);
+        p_lo = __builtin_amdgcn_bitop3_b32(p_lo, (u32)vote, m, 0x90);
+        p_hi = __builtin_amdgcn_bitop3_b32(p_hi, (u32)(vote >> 32), m, 0x90);
+    }
+}
+
 // One stable pass by the low `bits` bits of each item's unsorted value.
 // Wide form: hi = the value, lo = the payload. Narrow form: hi = value << kPay
 // | payload. The pass drops the sorted bits; kWideOut keeps the wide form
@@ -2034,22 +2051,22 @@ template <bool kWideIn, bool kWideOut>
 __device__ __forceinline__ void rec_pass(u32 (&hi)[kLocalItems], u32 (&lo)[kLocalItems], int bits,
                                          RecScratch& s) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const u32 mask = (1u << bits) - 1, bins = 1u << bits;
+    const u32 bins = 1u << bits;
     uint16_t* cnt = s.count[w];
     // (cleared through the same type the ranking reads: no barrier between)
     for (u32 i = lane; i < bins; i += 64) cnt[i] = 0;
-    auto digit = [&](int j) { return (kWideIn ? hi[j] : hi[j] >> kPay) & mask; };
+    auto digit = [&](int j) { return __builtin_amdgcn_ubfe(hi[j], kWideIn ? 0 : kPay, bits); };
     u32 rank[kLocalItems];
 #pragma unroll
     for (int j = 0; j < kLocalItems; ++j) {
         const u32 d = digit(j);
-        u32 miss_lo = 0, miss_hi = 0;
-        for (int b = 0; b < bits; ++b) match_bit(d, b, miss_lo, miss_hi);
-        const u32 before = lanes_below(~miss_lo, ~miss_hi);
+        u32 p_lo, p_hi;
+        peer_mask(d, bits, ~0u, ~0u, p_lo, p_hi);
+        const u32 before = lanes_below(p_lo, p_hi);
         const u32 seen = cnt[d];
         rank[j] = seen + before;
         // every lane of the digit writes the same count
-        cnt[d] = (uint16_t)(seen + __popc(~miss_lo) + __popc(~miss_hi));
+        cnt[d] = (uint16_t)(seen + __popc(p_lo) + __popc(p_hi));
     }
     __syncthreads();
     // per digit: prefix over the waves, then the exclusive scan of the totals
@@ -2074,9 +2091,13 @@ __device__ __forceinline__ void rec_pass(u32 (&hi)[kLocalItems], u32 (&lo)[kLoca
     }
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < kLocalItems; ++j) {
+    for (int j = 0; j < kLocalItems; ++j) {  // all reads before the exchange writes
         const u32 d = digit(j);
-        const u32 pos = s.start[d] + s.count[w][d] + rank[j];
+        rank[j] += s.start[d] + s.count[w][d];
+    }
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) {
+        const u32 pos = rank[j];
         if constexpr (kWideOut) {
             s.exch[0][pos] = hi[j] >> bits;
             s.exch[1][pos] = lo[j];
@@ -2167,17 +2188,21 @@ __device__ __forceinline__ void rec_round(const uint16_t* order, int t, const Ge
     const u32 words = (kLocalWaves * segs + 1) / 2;
     for (u32 i = tid; i < words; i += kLocalBlock) cnt_words[i] = 0;
     __syncthreads();
+    // Every item's slot and tag first: reads issued back to back (the
+    // counter writes below could alias them, so they would otherwise wait
+    // for each other item by item).
     u32 e[kLocalItems], st[kLocalItems], rank[kLocalItems];
 #pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) e[j] = order[local_slot(j)];
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) st[j] = sh.m.tag[e[j]];
+#pragma unroll
     for (int j = 0; j < kLocalItems; ++j) {
-        e[j] = order[local_slot(j)];
-        st[j] = sh.m.tag[e[j]];
         const u32 b = st[j] - fl;
         const bool live = b < segs;
-        u32 miss_lo = 0, miss_hi = 0;
-        for (int bit = 0; bit < t; ++bit) match_bit(b, bit, miss_lo, miss_hi);
         const u64 lv = __ballot(live);
-        const u32 p_lo = (u32)lv & ~miss_lo, p_hi = (u32)(lv >> 32) & ~miss_hi;
+        u32 p_lo, p_hi;
+        peer_mask(b, t, (u32)lv, (u32)(lv >> 32), p_lo, p_hi);
         const u32 before = lanes_below(p_lo, p_hi);
         uint16_t* cp = live ? &cnt[w * segs + b] : &s.dummy[lane];
         const u32 seen = *cp;
@@ -2214,8 +2239,13 @@ __device__ __forceinline__ void rec_round(const uint16_t* order, int t, const Ge
 #pragma unroll
     for (int j = 0; j < kLocalItems; ++j) {
         const u32 b = st[j] - fl;
+        rank[j] += cnt[w * segs + (b < segs ? b : 0)];  // all reads before the tag writes
+    }
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) {
+        const u32 b = st[j] - fl;
         const bool live = b < segs;
-        const u32 in_seg = cnt[w * segs + (live ? b : 0)] + rank[j];
+        const u32 in_seg = rank[j];
         const u32 under = (2 * b) << dd;
         const u32 left = (u - 1) + (last > under ? (last - under < u ? last - under : u) : 0u);
         const u32 next = in_seg < left ? 2 * st[j] + 1 : (in_seg > left ? 2 * st[j] + 2 : st[j]);
