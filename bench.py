@@ -324,7 +324,7 @@ def counter_runs(workload, widest=False):
 # Kernel kinds of the global phase: presort, per-round re-sorts and selects,
 # their scans, the pivots and the split-widest domain kernels (everything but
 # the subtree stage and the single-point case).
-GLOBAL_PASS_PREFIXES = ("k_sort_", "k_part_", "k_pivots", "k_chunk_scan", "k_first_digits", "k_widest_level",
+GLOBAL_PASS_PREFIXES = ("k_sort_", "k_part_", "k_pivots", "k_chunk_scan", "k_first_digits", "k_planar_records", "k_widest_level",
                         "k_box_", "k_zero")
 
 

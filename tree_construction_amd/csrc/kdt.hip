@@ -329,17 +329,27 @@ enum Src { kSrcRows = 0, kSrcRecords = 1 };
 // coordinates, then e), in index order; kSrcRecords reads records of
 // `words` words. Records carry keys, not float bits, so that every
 // comparison and digit is a plain unsigned one.
+// Records of at most four words are stored whole (one vector access each);
+// wider records are planar: word w of every record in plane w, `plane`
+// words long, so that each per-word access of a wave is one contiguous run.
+constexpr int kWholeWords = 4;
+
+__host__ __device__ inline u64 rec_word_index(int words, u64 plane, u64 e, int w) {
+    return words > kWholeWords ? (u64)w * plane + e : e * (u64)words + (u64)w;
+}
+
 struct RecordSource {
     const float* pts;
     int k;
     const u32* in;
     int words;
     i64 n;
+    u64 plane;  // words > kWholeWords: distance between the planes of `in`
 };
 
 template <int kSrc>
 __device__ inline u32 source_word(const RecordSource& s, u64 e, int w) {
-    if (kSrc == kSrcRecords) return s.in[e * s.words + w];
+    if (kSrc == kSrcRecords) return s.in[rec_word_index(s.words, s.plane, e, w)];
     return w < s.words - 1 ? float_key(__float_as_uint(s.pts[e * s.k + w])) : (u32)e;
 }
 
@@ -473,8 +483,7 @@ struct RecordTile {
             const v2u v = {w0[j], w1[j]};
             __builtin_nontemporal_store(v, reinterpret_cast<v2u*>(out + pos * 2));
         } else {
-            u32* dst = out + pos * s.words;
-            for (int w = 0; w < s.words; ++w) dst[w] = source_word<kSrc>(s, (u64)e, w);
+            for (int w = 0; w < s.words; ++w) out[rec_word_index(s.words, s.plane, pos, w)] = source_word<kSrc>(s, (u64)e, w);
         }
     }
     // Plain stores: where a wave's stores land in many short runs, the
@@ -643,6 +652,26 @@ __global__ __launch_bounds__(kBlock) void k_first_digits4(const float* __restric
     for (i64 e = quads * 4 + (i64)blockIdx.x * kBlock + threadIdx.x; e < n; e += stride) {
         const u32* row = reinterpret_cast<const u32*>(pts) + (u64)e * kK;
         for (int d = 0; d < kr; ++d) digits0[(u64)d * n + e] = (u8)float_key(row[d]);
+    }
+}
+
+// Records wider than kWholeWords, of every point in index order, from one
+// read of the rows: planar (plane d < words-1 the key of coordinate d, the
+// last plane the index), with the first presort pass's digit of each
+// dimension (the keys' low bytes). The presorts read their first pass from
+// here instead of gathering one word of every row per staging round.
+__global__ __launch_bounds__(kBlock) void k_planar_records(const float* __restrict__ pts, i64 n, int k,
+                                                           int words, u32* __restrict__ out,
+                                                           u8* __restrict__ digits0) {
+    const i64 stride = (i64)gridDim.x * kBlock;
+    for (i64 e = (i64)blockIdx.x * kBlock + threadIdx.x; e < n; e += stride) {
+        const u32* row = reinterpret_cast<const u32*>(pts) + (u64)e * k;
+        for (int d = 0; d < words - 1; ++d) {
+            const u32 key = float_key(row[d]);
+            out[(u64)d * n + e] = key;
+            digits0[(u64)d * n + e] = (u8)key;
+        }
+        out[(u64)(words - 1) * n + e] = (u32)e;
     }
 }
 
@@ -820,7 +849,7 @@ __global__ __launch_bounds__(kSortBlock) void k_sort_scatter(SortArgs a) {
             for (int i = tid; i < valid_here; i += kSortBlock) {
                 const u32 dst = s_base[s_digit[i]] + (u32)i;
                 if (dst >= (u64)a.src.n) continue;
-                a.out[(u64)dst * words + ww] = sm.words[i];
+                a.out[rec_word_index(words, a.src.plane, dst, ww)] = sm.words[i];
                 if (ww == a.next_dim && a.next_digits)
                     a.next_digits[dst] = (u8)(sm.words[i] >> a.next_shift);
             }
@@ -950,6 +979,15 @@ __device__ __forceinline__ void part_nodes(const PartArgs& a, u32 t,
         }
         loc[j] = j0 - j_first;
     }
+    // (records without registers: the index word once per item)
+    u32 index_of[kW > 0 && !kNodeDims ? 1 : kPartItems];
+    if constexpr (!(kW > 0 && !kNodeDims)) {
+#pragma unroll
+        for (int j = 0; j < kPartItems; ++j) {
+            const i64 e = wbase + (i64)j * 64;
+            index_of[j] = valid[j] ? tr.word(a.src, j, e, a.src.words - 1) : 0u;
+        }
+    }
     if (staged) __syncthreads();
     // One level at a time: compare with the pivot of the current node, in
     // the level's dimension (or the node's own, from the table).
@@ -982,7 +1020,7 @@ __device__ __forceinline__ void part_nodes(const PartArgs& a, u32 t,
                 } else if constexpr (kNodeDims) {
                     dj = 0;
                 }
-                const u64 me = ((u64)tr.word(a.src, j, e, dj) << 32) | tr.word(a.src, j, e, a.src.words - 1);
+                const u64 me = ((u64)tr.word(a.src, j, e, dj) << 32) | index_of[j];
                 if (me == p) valid[j] = false;  // the pivot itself: a node already
                 loc[j] = 2 * loc[j] + (me < p ? 0u : 1u);
             }
@@ -1159,7 +1197,7 @@ __global__ __launch_bounds__(kBlock) void k_part_select_widest(PartArgs a) { par
 // Round l's nodes: the pivot of node s = F(l) + j is the record at live
 // position live_begin(j) + |S(2s+1)| of the array sorted for round l
 // ([W], sb/ss paragraph). It goes to the pivot table, perm and tree.
-__global__ __launch_bounds__(kBlock) void k_pivots(const u32* __restrict__ recs, int words,
+__global__ __launch_bounds__(kBlock) void k_pivots(const u32* __restrict__ recs, int words, u64 plane,
                                                    Geometry geo, int l, int dim,
                                                    u64* __restrict__ piv,
                                                    const float* __restrict__ pts, int k,
@@ -1172,9 +1210,8 @@ __global__ __launch_bounds__(kBlock) void k_pivots(const u32* __restrict__ recs,
     const u64 p = live_begin(geo, j, l) + subtree_size(geo, 2 * s + 1);
     if (s >= (u64)geo.n || p >= (u64)geo.n - full_nodes(l)) return;  // not for l < L-1
     if (dimtab && dimtab[s] != (uint16_t)dim) return;  // another array's node
-    const u32* r = recs + p * words;
-    const u32 idx = r[words - 1];
-    piv[s] = ((u64)r[dim] << 32) | idx;
+    const u32 idx = recs[rec_word_index(words, plane, p, words - 1)];
+    piv[s] = ((u64)recs[rec_word_index(words, plane, p, dim)] << 32) | idx;
     if (perm) perm[s] = (int32_t)idx;
     if (tree && idx < (u64)geo.n)
         for (int d = 0; d < k; ++d) tree[s * k + d] = pts[(u64)idx * k + d];
@@ -1645,6 +1682,7 @@ struct SubtreeArgs {
     Geometry geo;
     const u32* recs;        // l0 > 0: records (coordinates 0 .. words-2, then the
     int words;              // index) live on level l0-1, in round l0-1's order
+    u64 plane;              // their plane stride (records wider than kWholeWords)
     int index_bytes;        // bytes of a point index that can differ
     u32* stage;             // (k+1) x n words: index, then coordinate key columns; the
                             // subtree owns [first, first + |S(c)|) of each
@@ -1773,11 +1811,10 @@ __device__ __forceinline__ void local_round(const uint16_t* order, u32 nc, int t
     __syncthreads();
 }
 
-// kRecs: the records carry every coordinate (k <= kCachedDims, l0 > 0), so
-// nothing is staged: the records are read in arrival order and moved to
-// slot or node order through the exchange buffer. Otherwise the slots are
-// staged to global memory as columns.
-template <bool kRecs>
+// The subtree stage when the records do not carry every coordinate (k >
+// kCachedDims), or when the whole tree is one subtree read from the rows
+// (l0 = 0): each point's index and coordinate keys are staged once, by index
+// rank, as columns of the workspace, and the orders are sorted from there.
 __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
     __shared__ LocalShared sh;
 
@@ -1791,43 +1828,39 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
         const u64 pivot = seg + subtree_size(a.geo, 2 * parent + 1);
         first = (c == 2 * parent + 1) ? seg : pivot + 1;
     }
+    // Word f of the record that arrived at position q.
+    auto rec = [&](u32 q, int f) -> u32 { return a.recs[rec_word_index(a.words, a.plane, first + q, f)]; };
     // Key of coordinate d of the point with index i that arrived at
     // position q: from its record while the record carries it, else from
     // its row of `points`.
     const int kr = a.recs ? a.words - 1 : 0;
     auto coord = [&](u32 q, u32 i, int d) -> u32 {
-        return d < kr ? a.recs[(first + q) * a.words + d]
-                      : float_key(__float_as_uint(a.pts[(i64)i * a.k + d]));
+        return d < kr ? rec(q, d) : float_key(__float_as_uint(a.pts[(i64)i * a.k + d]));
     };
 
     // Order the subtree's points by original index: slot e = index rank.
-    u64 rec[kLocalItems];
+    u64 rec_idx[kLocalItems];
 #pragma unroll
     for (int j = 0; j < kLocalItems; ++j) {
         const int q = local_slot(j);
-        rec[j] = ~0ull;
+        rec_idx[j] = ~0ull;
         if ((u32)q < nc) {
-            const u32 i = a.recs ? a.recs[(first + q) * a.words + a.words - 1] : (u32)q;
-            rec[j] = ((u64)i << 16) | (u32)q;
+            const u32 i = a.recs ? rec(q, a.words - 1) : (u32)q;
+            rec_idx[j] = ((u64)i << 16) | (u32)q;
         }
     }
-    if (a.recs) local_sort(rec, 16, a.index_bytes, nc, sh);
+    if (a.recs) local_sort(rec_idx, 16, a.index_bytes, nc, sh);
     // Stage the subtree's points once, by index rank: their indices and their
-    // coordinate columns (each point is read exactly once here); records
-    // that carry every coordinate are not staged.
+    // coordinate columns (each point is read exactly once here).
     u32* stage_idx = a.stage + first;
-    if constexpr (kRecs) {
-#pragma unroll
-        for (int j = 0; j < kLocalItems; ++j)
-            if ((u32)local_slot(j) < nc) sh.tag[local_slot(j)] = 0;
-    } else if (a.k <= kRowRegs) {
+    if (a.k <= kRowRegs) {
         // Row loads are issued kRowBatch items at a time, before their stores.
 #pragma unroll
         for (int j0 = 0; j0 < kLocalItems; j0 += kRowBatch) {
             u32 row[kRowBatch][kRowRegs];
 #pragma unroll
             for (int j = 0; j < kRowBatch; ++j) {
-                const u32 i = (u32)(rec[j0 + j] >> 16), q = (u32)(rec[j0 + j] & 0xffff);
+                const u32 i = (u32)(rec_idx[j0 + j] >> 16), q = (u32)(rec_idx[j0 + j] & 0xffff);
                 const bool ok = (u32)local_slot(j0 + j) < nc;
 #pragma unroll
                 for (int d = 0; d < kRowRegs; ++d) row[j][d] = ok && d < a.k ? coord(q, i, d) : 0u;
@@ -1836,7 +1869,7 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
             for (int j = 0; j < kRowBatch; ++j) {
                 const int e = local_slot(j0 + j);
                 if ((u32)e >= nc) continue;
-                stage_idx[e] = (u32)(rec[j0 + j] >> 16);
+                stage_idx[e] = (u32)(rec_idx[j0 + j] >> 16);
 #pragma unroll
                 for (int d = 0; d < kRowRegs; ++d)
                     if (d < a.k) a.stage[(u64)(d + 1) * a.n + first + e] = row[j][d];
@@ -1848,7 +1881,7 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
         for (int j = 0; j < kLocalItems; ++j) {
             const int e = local_slot(j);
             if ((u32)e >= nc) continue;
-            const u32 i = (u32)(rec[j] >> 16), q = (u32)(rec[j] & 0xffff);
+            const u32 i = (u32)(rec_idx[j] >> 16), q = (u32)(rec_idx[j] & 0xffff);
             stage_idx[e] = i;
             for (int d = 0; d < a.k; ++d) a.stage[(u64)(d + 1) * a.n + first + e] = coord(q, i, d);
             sh.tag[e] = 0;
@@ -1861,34 +1894,21 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
     const bool cached = a.k <= kCachedDims;
     // The points arrived in round l0-1's sorted order, i.e. ordered by
     // (coordinate (l0-1) mod k, index): that is already the subtree's order
-    // for that dimension (slot of the arrival position q = rec's low bits).
+    // for that dimension (slot of the arrival position q = rec_idx's low bits).
     const int arrived_dim = a.recs ? (a.l0 - 1) % a.k : -1;
     uint16_t* arrived = a.recs ? sh.order[cached ? a.k - 1 : 1] : nullptr;
     if (arrived) {
 #pragma unroll
         for (int j = 0; j < kLocalItems; ++j) {
             const int e = local_slot(j);
-            if ((u32)e < nc) arrived[rec[j] & 0xffff] = (uint16_t)e;
+            if ((u32)e < nc) arrived[rec_idx[j] & 0xffff] = (uint16_t)e;
         }
     }
     if (cached)
         for (int u = 0; u < a.k && u < rounds; ++u) {
             const int d = (a.l0 + u) % a.k;
             if (d == arrived_dim) continue;
-            if constexpr (kRecs) {
-                // coordinate d by slot: read in arrival order, moved to the
-                // slot through the exchange buffer
-                __syncthreads();  // arrived complete, the buffer's last readers done
-#pragma unroll
-                for (int j = 0; j < kLocalItems; ++j) {
-                    const int q = local_slot(j);
-                    if ((u32)q < nc) sh.exch[arrived[q]] = a.recs[(first + q) * a.words + d];
-                }
-                __syncthreads();
-                local_order(ColumnKey{sh.exch}, nc, sh.order[u], sh);
-            } else {
-                local_order(column(d), nc, sh.order[u], sh);
-            }
+            local_order(column(d), nc, sh.order[u], sh);
         }
     __syncthreads();
 
@@ -1909,45 +1929,6 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
     // Level-order output of the subtree, in node order: the nodes of each
     // local level are one contiguous range of global ids, so the writes of
     // consecutive threads are contiguous.
-    if constexpr (kRecs) {
-        // One record word at a time (the index first, then the keys): read in
-        // arrival order, put at its node in the exchange buffer, written out
-        // by node. A zero key (both zeros have it) is read back from the row,
-        // which keeps the sign of zero.
-        u32 node_at[kLocalItems], idx_of[kLocalItems];
-#pragma unroll
-        for (int j = 0; j < kLocalItems; ++j) {
-            const int q = local_slot(j);
-            node_at[j] = (u32)q < nc ? sh.tag[arrived[q]] : 0u;
-        }
-        const int words_out = a.tree ? a.words : 1;
-        for (int pass = 0; pass < words_out; ++pass) {
-            const int f = pass == 0 ? a.words - 1 : pass - 1;
-            __syncthreads();  // the buffer's last readers done
-#pragma unroll
-            for (int j = 0; j < kLocalItems; ++j) {
-                const int q = local_slot(j);
-                if ((u32)q < nc) sh.exch[node_at[j]] = a.recs[(first + q) * a.words + f];
-            }
-            __syncthreads();
-#pragma unroll
-            for (int i = 0; i < kLocalItems; ++i) {
-                const u32 node = threadIdx.x + (u32)i * kLocalBlock;
-                if (node >= nc) continue;
-                const int lvl = level_of(node);
-                const u64 g = ((c + 1) << lvl) - 1 + (node - full_nodes(lvl));
-                const u32 v = sh.exch[node];
-                if (pass == 0) {
-                    idx_of[i] = v;
-                    a.perm[g] = (int32_t)v;
-                } else {
-                    a.tree[(i64)g * a.k + f] =
-                        v == 0x80000000u ? a.pts[(i64)idx_of[i] * a.k + f] : __uint_as_float(key_bits(v));
-                }
-            }
-        }
-        return;
-    }
     uint16_t* slot_of = sh.order[0];  // the orders are no longer needed
 #pragma unroll
     for (int j = 0; j < kLocalItems; ++j) {
@@ -2649,6 +2630,7 @@ struct Layout {
     int nbuf;            // record arrays
     i64 tiles;           // of a pass over all n points
     size_t tmp0, tmp1, digits, digits0, recs, piv, totals, slots, chunk_slots, stage, total;
+    size_t planar0;      // records wider than kWholeWords: all of them in index order, planar
 };
 
 // Workspace of `rounds` global rounds and, with `stage`, of the subtree stage.
@@ -2682,6 +2664,7 @@ bool make_layout(i64 n, int k, int rounds, bool stage, Layout* out) {
         lay.digits = take((size_t)n);  // a presort pass's digit of each record
         lay.digits0 = take((size_t)lay.kr * n);  // the first pass's, per dimension
         lay.recs = take((size_t)lay.nbuf * rec_bytes);
+        if (lay.words > kWholeWords) lay.planar0 = take(rec_bytes);
         lay.piv = take((size_t)full_nodes(rounds) * sizeof(u64));
         lay.totals = take((size_t)kRadix * sizeof(u32));
         lay.slots = take((size_t)lay.tiles * kRadix * sizeof(u32));
@@ -2730,6 +2713,7 @@ bool make_layout_widest(i64 n, int k, WidestLayout* out) {
     lay.digits = take((size_t)n);
     lay.digits0 = take((size_t)k * n);
     lay.recs = take((size_t)lay.nbuf * rec_bytes);
+    if (lay.words > kWholeWords) lay.planar0 = take(rec_bytes);
     lay.piv = take((size_t)full_nodes(lay.rounds) * sizeof(u64));
     lay.totals = take((size_t)kRadix * sizeof(u32));
     lay.slots = take((size_t)lay.tiles * kRadix * sizeof(u32));
@@ -2949,9 +2933,18 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
     Launcher launch{(u32*)(ws + lay.slots), (u32*)(ws + lay.chunk_slots), (u32*)(ws + lay.totals),
                     stream, timer};
 
-    timer.begin("k_first_digits", (double)n * 5.0 * lay.kr);
-    launch_first_digits(pts, n, k, lay.kr, digits0, stream);
-    timer.end();
+    // Wide records are planar; their first presort pass reads them from an
+    // index-ordered planar copy built here (with the first digits).
+    u32* planar0 = W > kWholeWords ? (u32*)(ws + lay.planar0) : nullptr;
+    if (planar0) {
+        timer.begin("k_planar_records", (double)n * (4.0 * k + 4.0 * W + lay.kr));
+        k_planar_records<<<grid_for(n, kBlock, 1 << 16), kBlock, 0, stream>>>(pts, n, k, W, planar0, digits0);
+        timer.end();
+    } else {
+        timer.begin("k_first_digits", (double)n * 5.0 * lay.kr);
+        launch_first_digits(pts, n, k, lay.kr, digits0, stream);
+        timer.end();
+    }
 
     int holder[kMaxRounds + 1];  // dimension whose array a buffer holds, or -1
     for (int b = 0; b <= kMaxRounds; ++b) holder[b] = -1;
@@ -2973,7 +2966,7 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
             if (b < 0) return KDT_ERR_WORKSPACE;  // cannot happen: nbuf covers the rounds
             for (int p = 0; p < kKeyBytes; ++p) {
                 SortArgs a{};
-                a.src = RecordSource{pts, k, p == 0 ? nullptr : tmp[(p + 1) & 1], W, n};
+                a.src = RecordSource{pts, k, p == 0 ? planar0 : tmp[(p + 1) & 1], W, n, (u64)n};
                 a.out = p == kKeyBytes - 1 ? recs(b) : tmp[p & 1];
                 a.dim = d;
                 a.shift = 8 * p;
@@ -2981,7 +2974,7 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
                 a.next_digits = p == kKeyBytes - 1 ? nullptr : digits;
                 a.next_dim = d;
                 a.next_shift = 8 * (p + 1);
-                if (p == 0) launch.sort_any<kSrcRows>(a);
+                if (p == 0 && !planar0) launch.sort_any<kSrcRows>(a);
                 else launch.sort_any<kSrcRecords>(a);
             }
             holder[b] = d;
@@ -3001,7 +2994,7 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
             const int next_use = l + k;
             if (l1 == l && l != R - 1 && (next_use >= R || next_use - level_of[d] <= kSelectDepth)) {
                 PartArgs a{};
-                a.src = RecordSource{pts, k, recs(buf_of[d]), W, n - (i64)full_nodes(level_of[d])};
+                a.src = RecordSource{pts, k, recs(buf_of[d]), W, n - (i64)full_nodes(level_of[d]), (u64)n};
                 a.k = k;
                 a.l0 = level_of[d];
                 a.l1 = l;
@@ -3022,7 +3015,7 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
             const int b = take(buf_of[d]);
             if (b < 0) return KDT_ERR_WORKSPACE;
             PartArgs a{};
-            a.src = RecordSource{pts, k, recs(buf_of[d]), W, n - (i64)full_nodes(level_of[d])};
+            a.src = RecordSource{pts, k, recs(buf_of[d]), W, n - (i64)full_nodes(level_of[d]), (u64)n};
             a.out = recs(b);
             a.n_out = n - (i64)full_nodes(l1);
             a.k = k;
@@ -3052,7 +3045,7 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
             const u64 nodes = 1ull << l;
             timer.begin("k_pivots", (double)nodes * (4.0 * W + 8 + (perm ? 4 : 0) + (tree ? 8.0 * k : 0)));
             k_pivots<<<(unsigned)((nodes + kBlock - 1) / kBlock), kBlock, 0, stream>>>(
-                recs(buf_of[d]), W, geo, l, d, piv, pts, k, perm, tree, nullptr);
+                recs(buf_of[d]), W, (u64)n, geo, l, d, piv, pts, k, perm, tree, nullptr);
             timer.end();
         }
         // A dimension not split on again frees its array (except the last
@@ -3127,7 +3120,7 @@ kdt_status run_unique(const float* pts, i64 n, int k, const UniqueLayout& ul, ch
     const u32* sorted = nullptr;
     for (int p = 0; p < kKeyBytes; ++p) {
         SortArgs a{};
-        a.src = RecordSource{pts, k, tmp[(p + 1) & 1], W, n};
+        a.src = RecordSource{pts, k, tmp[(p + 1) & 1], W, n, (u64)n};
         a.out = tmp[p & 1];
         a.dim = 0;
         a.shift = 8 * p;
@@ -3236,14 +3229,21 @@ kdt_status run_widest(const float* pts, i64 n, int k, const WidestLayout& wl, ch
         return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
     }
 
-    timer.begin("k_first_digits", (double)n * 5.0 * k);
-    launch_first_digits(pts, n, k, k, digits0, stream);
-    timer.end();
+    u32* planar0 = W > kWholeWords ? (u32*)(ws + lay.planar0) : nullptr;
+    if (planar0) {
+        timer.begin("k_planar_records", (double)n * (4.0 * k + 4.0 * W + k));
+        k_planar_records<<<grid_for(n, kBlock, 1 << 16), kBlock, 0, stream>>>(pts, n, k, W, planar0, digits0);
+        timer.end();
+    } else {
+        timer.begin("k_first_digits", (double)n * 5.0 * k);
+        launch_first_digits(pts, n, k, k, digits0, stream);
+        timer.end();
+    }
     // A_d in buffer d, by (coordinate d, index): the order of level 0.
     for (int d = 0; d < k; ++d)
         for (int p = 0; p < kKeyBytes; ++p) {
             SortArgs a{};
-            a.src = RecordSource{pts, k, p == 0 ? nullptr : tmp[(p + 1) & 1], W, n};
+            a.src = RecordSource{pts, k, p == 0 ? planar0 : tmp[(p + 1) & 1], W, n, (u64)n};
             a.out = p == kKeyBytes - 1 ? recs(d) : tmp[p & 1];
             a.dim = d;
             a.shift = 8 * p;
@@ -3251,7 +3251,7 @@ kdt_status run_widest(const float* pts, i64 n, int k, const WidestLayout& wl, ch
             a.next_digits = p == kKeyBytes - 1 ? nullptr : digits;
             a.next_dim = d;
             a.next_shift = 8 * (p + 1);
-            if (p == 0) launch.sort_any<kSrcRows>(a);
+            if (p == 0 && !planar0) launch.sort_any<kSrcRows>(a);
             else launch.sort_any<kSrcRecords>(a);
         }
     std::vector<int> buffer(k);
@@ -3260,7 +3260,7 @@ kdt_status run_widest(const float* pts, i64 n, int k, const WidestLayout& wl, ch
     // The root's pivot, from the array of its dimension.
     for (int d = 0; d < k; ++d) {
         timer.begin("k_pivots", 4.0 * W + 8 + (perm ? 4 : 0) + (tree ? 8.0 * k : 0));
-        k_pivots<<<1, kBlock, 0, stream>>>(recs(buffer[d]), W, geo, 0, d, piv, pts, k, perm, tree, dimtab);
+        k_pivots<<<1, kBlock, 0, stream>>>(recs(buffer[d]), W, (u64)n, geo, 0, d, piv, pts, k, perm, tree, dimtab);
         timer.end();
     }
     if (L > 1) level(1);
@@ -3275,7 +3275,7 @@ kdt_status run_widest(const float* pts, i64 n, int k, const WidestLayout& wl, ch
     for (int l = 1; l < lds_from; ++l) {
         for (int d = 0; d < k; ++d) {
             PartArgs a{};
-            a.src = RecordSource{pts, k, recs(buffer[d]), W, n - (i64)full_nodes(level_of[d])};
+            a.src = RecordSource{pts, k, recs(buffer[d]), W, n - (i64)full_nodes(level_of[d]), (u64)n};
             a.out = recs(spare);
             a.n_out = n - (i64)full_nodes(l);
             a.k = k;
@@ -3311,7 +3311,7 @@ kdt_status run_widest(const float* pts, i64 n, int k, const WidestLayout& wl, ch
         // A_0 to level lds_from (no pivots: the subtree stage fixes that
         // level's nodes), so that each subtree's records are one range.
         PartArgs a{};
-        a.src = RecordSource{pts, k, recs(buffer[0]), W, n - (i64)full_nodes(level_of[0])};
+        a.src = RecordSource{pts, k, recs(buffer[0]), W, n - (i64)full_nodes(level_of[0]), (u64)n};
         a.out = recs(spare);
         a.n_out = n - (i64)full_nodes(lds_from);
         a.k = k;
@@ -3395,6 +3395,7 @@ kdt_status build_impl(const float* points, int64_t N, int32_t k, int32_t* perm_o
     sa.geo = geo;
     sa.recs = recs;
     sa.words = lay.words;
+    sa.plane = (u64)N;
     int bits = 0;
     for (u64 v = (u64)(N - 1); v; v >>= 1) ++bits;
     sa.index_bytes = (bits + kRadixBits - 1) / kRadixBits;
@@ -3410,13 +3411,13 @@ kdt_status build_impl(const float* points, int64_t N, int32_t k, int32_t* perm_o
     const bool from_recs = recs && lay.words - 1 == k && k <= kCachedDims;
     static const char* const kRecNames[kCachedDims + 1] = {"", "k_subtree_recs<1>", "k_subtree_recs<2>",
                                                            "k_subtree_recs<3>"};
-    timer.begin(from_recs ? kRecNames[k] : "k_subtree<false>",
+    timer.begin(from_recs ? kRecNames[k] : "k_subtree",
                 (double)below * (in + (from_recs ? 0.0 : 2 * (4 + row)) + 4 + (tree_out ? row : 0)));
     const unsigned subtrees = (unsigned)(1ull << l0);
     if (from_recs && k == 1) k_subtree_recs<1><<<subtrees, kLocalBlock, 0, stream>>>(sa);
     else if (from_recs && k == 2) k_subtree_recs<2><<<subtrees, kLocalBlock, 0, stream>>>(sa);
     else if (from_recs) k_subtree_recs<3><<<subtrees, kLocalBlock, 0, stream>>>(sa);
-    else k_subtree<false><<<subtrees, kLocalBlock, 0, stream>>>(sa);
+    else k_subtree<<<subtrees, kLocalBlock, 0, stream>>>(sa);
     timer.end();
     return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
 }
