@@ -675,9 +675,20 @@ __global__ __launch_bounds__(kBlock) void k_planar_records(const float* __restri
     }
 }
 
+// Whether the four-points-per-thread variant fits k and the rows' alignment,
+// and the kernel's name as the profiler prints it.
+inline bool first_digits_vec(const float* pts, int k) {
+    return k >= 1 && k <= 4 && reinterpret_cast<uintptr_t>(pts) % 16 == 0;
+}
+inline const char* first_digits_name(const float* pts, int k) {
+    static const char* const names[5] = {"k_first_digits", "k_first_digits4<1>", "k_first_digits4<2>",
+                                         "k_first_digits4<3>", "k_first_digits4<4>"};
+    return first_digits_vec(pts, k) ? names[k] : names[0];
+}
+
 // Launches whichever of the two fits k and the rows' alignment.
 void launch_first_digits(const float* pts, i64 n, int k, int kr, u8* digits0, hipStream_t stream) {
-    const bool vec = k >= 1 && k <= 4 && reinterpret_cast<uintptr_t>(pts) % 16 == 0;
+    const bool vec = first_digits_vec(pts, k);
     const i64 work = vec ? (n + 3) / 4 : (n > 0 ? n : 1);
     const unsigned grid = (unsigned)((work + kBlock - 1) / kBlock < (1 << 30) ? (work + kBlock - 1) / kBlock : (1 << 30));
     if (!vec) k_first_digits<<<grid, kBlock, 0, stream>>>(pts, n, k, kr, digits0);
@@ -2941,7 +2952,7 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
         k_planar_records<<<grid_for(n, kBlock, 1 << 16), kBlock, 0, stream>>>(pts, n, k, W, planar0, digits0);
         timer.end();
     } else {
-        timer.begin("k_first_digits", (double)n * 5.0 * lay.kr);
+        timer.begin(first_digits_name(pts, k), (double)n * 5.0 * lay.kr);
         launch_first_digits(pts, n, k, lay.kr, digits0, stream);
         timer.end();
     }
@@ -3235,7 +3246,7 @@ kdt_status run_widest(const float* pts, i64 n, int k, const WidestLayout& wl, ch
         k_planar_records<<<grid_for(n, kBlock, 1 << 16), kBlock, 0, stream>>>(pts, n, k, W, planar0, digits0);
         timer.end();
     } else {
-        timer.begin("k_first_digits", (double)n * 5.0 * k);
+        timer.begin(first_digits_name(pts, k), (double)n * 5.0 * k);
         launch_first_digits(pts, n, k, k, digits0, stream);
         timer.end();
     }
