@@ -928,7 +928,8 @@ constexpr int kPivStage = 1024;
 
 // One level of the walk for round-robin trees, whose level dimension kD is
 // the same for the whole wave: the compared words are picked at compile
-// time. piv_level[loc] is the pivot of the item's node.
+// time. piv_level[loc] is the pivot of the item's node; only valid items
+// read it.
 template <int kD, int kW, typename Piv>
 __device__ __forceinline__ void walk_level(const RecordTile<kSrcRecords, kW>& tr, Piv piv_level,
                                            u32 (&loc)[kPartItems], bool (&valid)[kPartItems]) {
@@ -941,6 +942,53 @@ __device__ __forceinline__ void walk_level(const RecordTile<kSrcRecords, kW>& tr
     }
 }
 
+// One step of a walk kept as r = ~loc: the next node is 2 loc + (me >= p),
+// so ~loc' = 2 r + (me < p), and (me < p) is the borrow of the 64-bit
+// subtraction (key:index) - (pivot key:pivot index). Three 32-bit ALU
+// instructions on the words as they are; compiled code would pair the words
+// into 64-bit registers and materialise the comparison bit instead.
+__device__ __forceinline__ u32 walk_step(u32 r, u32 key, u32 index, u32 pkey, u32 pindex) {
+    u32 diff;
+    u64 borrow;
+    asm("v_sub_co_u32_e64 %1, %2, %3, %5\n\t"
+        "v_subb_co_u32_e64 %1, %2, %4, %6, %2\n\t"
+        "v_addc_co_u32_e64 %0, %2, %0, %0, %2"
+        : "+v"(r), "=&v"(diff), "=&s"(borrow)
+        : "v"(index), "v"(key), "v"(pindex), "v"(pkey));
+    return r;
+}
+
+// One level of a walk over staged pivots, stored in reverse within the
+// level: the pivot of loc sits at level_end[-1 - loc] = level_end[r]. Every
+// item's r is in range (past-the-end items walk from slot 0), so the read
+// needs no mask. The pivot itself is found by its index word alone (indices
+// are unique, and its key is the compared one).
+template <int kD, int kW>
+__device__ __forceinline__ void walk_level_staged(const RecordTile<kSrcRecords, kW>& tr, const u64* level_end,
+                                                  u32 (&r)[kPartItems], bool (&valid)[kPartItems]) {
+#pragma unroll
+    for (int j = 0; j < kPartItems; ++j) {
+        const u64 p = level_end[(int)r[j]];
+        const u32 index = tr.template at<kW - 1>(j);
+        if (index == (u32)p) valid[j] = false;  // the pivot itself: a node already
+        r[j] = walk_step(r[j], tr.template at<kD>(j), index, (u32)(p >> 32), (u32)p);
+    }
+}
+
+// Levels kM .. delta-1 of a walk over staged pivots, the dimension of level
+// l0 + m being (kD0 + m) mod (kW - 1) at compile time (records of kW words
+// hold kW - 1 keys, one per dimension). Level m's pivots end at slot
+// segs * (2^(m+1) - 1).
+template <int kD0, int kW, int kM>
+__device__ __forceinline__ void walk_staged(const RecordTile<kSrcRecords, kW>& tr, const u64* s_piv, u32 segs,
+                                            int delta, u32 (&r)[kPartItems], bool (&valid)[kPartItems]) {
+    if constexpr (kM < kMaxDescent) {
+        if (kM >= delta) return;
+        walk_level_staged<(kD0 + kM) % (kW - 1), kW>(tr, s_piv + segs * ((2u << kM) - 1), r, valid);
+        walk_staged<kD0, kW, kM + 1>(tr, s_piv, segs, delta, r, valid);
+    }
+}
+
 // For every item: node[j], the in-level index of its node on level l1,
 // which is (j0 << delta) | digit for its level-l0 segment j0 and its digit
 // (offset of the level-l1 node below the level-l0 one); valid = false for
@@ -948,11 +996,14 @@ __device__ __forceinline__ void walk_level(const RecordTile<kSrcRecords, kW>& tr
 // compares (key(coordinate l mod k), index) with the pivot of the current
 // node on each level l ([W], tag paragraph: before the pivot -> left child).
 // Call with the whole workgroup: the pivots are staged in LDS first.
-template <int kW, bool kNodeDims>
+// Records held in registers (kW > 0) of round-robin trees always stage them
+// (the host checks that every tile's fit: pivots_fit), unless kInPlace: then
+// the walk reads them where they are.
+template <int kW, bool kNodeDims, bool kInPlace = false>
 __device__ __forceinline__ void part_nodes(const PartArgs& a, u32 t,
                                            const RecordTile<kSrcRecords, kW>& tr, i64 wbase,
                                            u32 (&node)[kPartItems], bool (&valid)[kPartItems]) {
-    __shared__ u64 s_piv[kNodeDims ? 1 : kPivStage];
+    __shared__ u64 s_piv[kNodeDims || kInPlace ? 1 : kPivStage];
     const int delta = a.l1 - a.l0;
     const u64 p0 = (u64)t * kPartTile;
     const u64 p1 = p0 + kPartTile < (u64)a.src.n ? p0 + kPartTile : (u64)a.src.n;
@@ -961,13 +1012,17 @@ __device__ __forceinline__ void part_nodes(const PartArgs& a, u32 t,
     // Level l0 + m of the walk: nodes (j_first << m) + i, i < segs << m, at
     // slots segs * (2^m - 1) + i (nodes past the last leaf: never visited).
     const u32 staged_n = segs * ((1u << delta) - 1);
-    const bool staged = !kNodeDims && staged_n <= (u32)kPivStage;
+    // (records held in registers walk each level's pivots in reverse)
+    constexpr bool kReversed = kW > 0 && !kNodeDims && !kInPlace;
+    const bool staged = kReversed || (!kNodeDims && !kInPlace && staged_n <= (u32)kPivStage);
     if (staged) {
-        for (u32 s = threadIdx.x; s < staged_n; s += kBlock) {
+        const u32 stage_n = staged_n < (u32)kPivStage ? staged_n : (u32)kPivStage;
+        for (u32 s = threadIdx.x; s < stage_n; s += kBlock) {
             const int m = 31 - __clz(s / segs + 1);
-            const u64 nd = full_nodes(a.l0 + m) + ((u64)j_first << m) + (s - segs * ((1u << m) - 1));
+            const u32 i = s - segs * ((1u << m) - 1);
+            const u64 nd = full_nodes(a.l0 + m) + ((u64)j_first << m) + i;
             const bool real = nd < (u64)a.geo.n;
-            s_piv[s] = real ? a.piv[nd] : 0;
+            s_piv[kReversed ? segs * ((2u << m) - 1) - 1 - i : s] = real ? a.piv[nd] : 0;
         }
     }
     // Level-l0 segment of each record: one division for the wave's first
@@ -988,7 +1043,8 @@ __device__ __forceinline__ void part_nodes(const PartArgs& a, u32 t,
                 next = live_begin32(a.s0, j0 + 1);
             }
         }
-        loc[j] = j0 - j_first;
+        // past the end: slot 0, so that every loc stays below segs << m
+        loc[j] = valid[j] ? j0 - j_first : 0u;
     }
     // (records without registers: the index word once per item)
     u32 index_of[kW > 0 && !kNodeDims ? 1 : kPartItems];
@@ -1000,25 +1056,32 @@ __device__ __forceinline__ void part_nodes(const PartArgs& a, u32 t,
         }
     }
     if (staged) __syncthreads();
+    if constexpr (kReversed) {
+        {  // levels unrolled, dimensions fixed at compile time
+            constexpr int kK = kW - 1;
+#pragma unroll
+            for (int j = 0; j < kPartItems; ++j) loc[j] = ~loc[j];
+            if (a.dim0 == 0) walk_staged<0, kW, 0>(tr, s_piv, segs, delta, loc, valid);
+            else if (a.dim0 == 1) walk_staged<1 % kK, kW, 0>(tr, s_piv, segs, delta, loc, valid);
+            else walk_staged<2 % kK, kW, 0>(tr, s_piv, segs, delta, loc, valid);
+#pragma unroll
+            for (int j = 0; j < kPartItems; ++j) node[j] = (j_first << delta) + ~loc[j];
+            return;
+        }
+    }
     // One level at a time: compare with the pivot of the current node, in
     // the level's dimension (or the node's own, from the table).
     int dim = a.dim0;
     for (int m = 0; m < delta; ++m) {
         const u32 slot0 = segs * ((1u << m) - 1);
         const u32 node0 = (u32)(full_nodes(a.l0 + m) + ((u64)j_first << m));  // n < 2^31
-        if constexpr (kW > 0 && !kNodeDims) {
+        (void)slot0;
+        if constexpr (kW > 0 && !kNodeDims && kInPlace) {
             constexpr int kD1 = kW > 2 ? 1 : 0, kD2 = kW > 3 ? 2 : 0;
-            if (staged) {
-                const u64* lv = s_piv + slot0;
-                if (dim == 0) walk_level<0, kW>(tr, lv, loc, valid);
-                else if (dim == 1) walk_level<kD1, kW>(tr, lv, loc, valid);
-                else walk_level<kD2, kW>(tr, lv, loc, valid);
-            } else {
-                const u64* lv = a.piv + node0;
-                if (dim == 0) walk_level<0, kW>(tr, lv, loc, valid);
-                else if (dim == 1) walk_level<kD1, kW>(tr, lv, loc, valid);
-                else walk_level<kD2, kW>(tr, lv, loc, valid);
-            }
+            const u64* lv = a.piv + node0;  // (unstaged: read in place)
+            if (dim == 0) walk_level<0, kW>(tr, lv, loc, valid);
+            else if (dim == 1) walk_level<kD1, kW>(tr, lv, loc, valid);
+            else walk_level<kD2, kW>(tr, lv, loc, valid);
         } else {
 #pragma unroll
             for (int j = 0; j < kPartItems; ++j) {
@@ -1045,7 +1108,7 @@ __device__ __forceinline__ void part_nodes(const PartArgs& a, u32 t,
 // Digit counts of one tile of a re-sort pass. A re-sort pass has at most
 // 2^kMaxDescent digits, usually a handful, so every tile is its own chunk:
 // its count of digit d goes straight to row d of the digit-major counts.
-template <int kW, bool kNodeDims>
+template <int kW, bool kNodeDims, bool kInPlace = false>
 __device__ __forceinline__ void part_count(const PartArgs& a) {
     __shared__ u32 hist[kWaves][kRadix];
     const u32 t = xcd_tile(a.tiles);
@@ -1060,7 +1123,7 @@ __device__ __forceinline__ void part_count(const PartArgs& a) {
     else tr.load(a.src, wbase);
     u32 node[kPartItems];
     bool valid[kPartItems];
-    part_nodes<kW, kNodeDims>(a, t, tr, wbase, node, valid);
+    part_nodes<kW, kNodeDims, kInPlace>(a, t, tr, wbase, node, valid);
     for (int i = lane; i < bins; i += 64) hist[w][i] = 0;  // this wave's own row
     u32 last = 0, run = 0;
 #pragma unroll
@@ -1090,6 +1153,8 @@ template <int kW>
 __global__ __launch_bounds__(kBlock) void k_part_count(PartArgs a) { part_count<kW, false>(a); }
 template <int kW>
 __global__ __launch_bounds__(kBlock) void k_part_count_widest(PartArgs a) { part_count<kW, true>(a); }
+template <int kW>
+__global__ __launch_bounds__(kBlock) void k_part_count_inplace(PartArgs a) { part_count<kW, false, true>(a); }
 
 // Whether tile t of a pass holds the pivot of some level-l1 node. The node
 // with in-level index j0 * 2^delta + b has its pivot where the count of
@@ -1125,7 +1190,7 @@ __device__ bool tile_has_pivot(const PartArgs& a, u32 t) {
 // kSelect: the pass only fixes the level-l1 nodes; it reads the tiles that
 // hold their pivots and writes no records (the array keeps its level-l0
 // order, and its next re-sort walks the levels in between as well).
-template <int kW, bool kNodeDims, bool kSelect = false>
+template <int kW, bool kNodeDims, bool kSelect = false, bool kInPlace = false>
 __device__ __forceinline__ void part_scatter(const PartArgs& a) {
     __shared__ u32 count[kWaves][kRadix];  // per-wave digit counts, then first slots
     const u32 t = xcd_tile(a.tiles);
@@ -1146,7 +1211,7 @@ __device__ __forceinline__ void part_scatter(const PartArgs& a) {
     const u32 before_tile = tid < bins ? a.chunk_counts[(u64)tid * a.tiles + t] : 0u;
     u32 node[kPartItems], rank[kPartItems];
     bool valid[kPartItems];
-    part_nodes<kW, kNodeDims>(a, t, tr, wbase, node, valid);
+    part_nodes<kW, kNodeDims, kInPlace>(a, t, tr, wbase, node, valid);
     for (int i = lane; i < bins; i += 64) count[w][i] = 0;
     {
         u32 digit[kPartItems];
@@ -1204,6 +1269,11 @@ template <int kW>
 __global__ __launch_bounds__(kBlock) void k_part_select(PartArgs a) { part_scatter<kW, false, true>(a); }
 template <int kW>
 __global__ __launch_bounds__(kBlock) void k_part_select_widest(PartArgs a) { part_scatter<kW, true, true>(a); }
+// Round-robin passes whose tiles' pivots may not fit the LDS stage.
+template <int kW>
+__global__ __launch_bounds__(kBlock) void k_part_scatter_inplace(PartArgs a) { part_scatter<kW, false, false, true>(a); }
+template <int kW>
+__global__ __launch_bounds__(kBlock) void k_part_select_inplace(PartArgs a) { part_scatter<kW, false, true, true>(a); }
 
 // Round l's nodes: the pivot of node s = F(l) + j is the record at live
 // position live_begin(j) + |S(2s+1)| of the array sorted for round l
@@ -2820,6 +2890,24 @@ const char* const kPartCountWidestNames[4] = {"k_part_count_widest<0>", "k_part_
                                               "k_part_count_widest<3>", "k_part_count_widest<4>"};
 const char* const kPartScatterWidestNames[4] = {"k_part_scatter_widest<0>", "k_part_scatter_widest<2>",
                                                 "k_part_scatter_widest<3>", "k_part_scatter_widest<4>"};
+const char* const kPartCountInPlaceNames[4] = {"k_part_count_inplace<0>", "k_part_count_inplace<2>",
+                                               "k_part_count_inplace<3>", "k_part_count_inplace<4>"};
+const char* const kPartScatterInPlaceNames[4] = {"k_part_scatter_inplace<0>", "k_part_scatter_inplace<2>",
+                                                 "k_part_scatter_inplace<3>", "k_part_scatter_inplace<4>"};
+const char* const kPartSelectInPlaceNames[4] = {"k_part_select_inplace<0>", "k_part_select_inplace<2>",
+                                                "k_part_select_inplace<3>", "k_part_select_inplace<4>"};
+
+// Whether the pivots of levels l0 .. l1-1 below every tile's level-l0
+// segments fit the LDS stage of the round-robin kernels. A tile of T
+// positions overlapping s segments holds s - 2 of them whole, so
+// s <= (T - 2) / (shortest segment) + 2; level-l0 segments hold at least
+// 2^dd - 1 points (dd = L - 1 - l0 levels below), the last level one each.
+bool pivots_fit(const PartArgs& a) {
+    const int dd = a.geo.levels - 1 - a.l0;
+    const u64 shortest = dd == 0 ? 1 : (1ull << dd) - 1;
+    const u64 segs = (u64)(kPartTile - 2) / shortest + 2;
+    return segs * ((1ull << (a.l1 - a.l0)) - 1) <= (u64)kPivStage;
+}
 
 struct Launcher {
     u32* tile_counts;
@@ -2870,16 +2958,20 @@ struct Launcher {
         const int bins = 1 << (a.l1 - a.l0);
         const double rec = 4.0 * a.src.words;
         const bool widest = a.dimtab != nullptr;  // split dimensions from the node table
-        timer.begin((widest ? kPartCountWidestNames : kPartCountNames)[width_slot(kW)], (double)a.src.n * rec);
+        const bool in_place = kW > 0 && !widest && !pivots_fit(a);
+        timer.begin((widest ? kPartCountWidestNames : in_place ? kPartCountInPlaceNames : kPartCountNames)[width_slot(kW)],
+                    (double)a.src.n * rec);
         if (widest) k_part_count_widest<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
+        else if (in_place) k_part_count_inplace<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
         else k_part_count<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
         timer.end();
         timer.begin("k_chunk_scan", (double)tiles * bins * 8);
         k_chunk_scan<<<bins, kBlock, 0, stream>>>(tile_counts, (i64)tiles, nullptr);
         timer.end();
-        timer.begin((widest ? kPartScatterWidestNames : kPartScatterNames)[width_slot(kW)],
+        timer.begin((widest ? kPartScatterWidestNames : in_place ? kPartScatterInPlaceNames : kPartScatterNames)[width_slot(kW)],
                     (double)(a.src.n + a.n_out) * rec);
         if (widest) k_part_scatter_widest<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
+        else if (in_place) k_part_scatter_inplace<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
         else k_part_scatter<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
         timer.end();
     }
@@ -2902,8 +2994,11 @@ struct Launcher {
         const int bins = 1 << (a.l1 - a.l0);
         const double rec = 4.0 * a.src.words;
         const bool widest = a.dimtab != nullptr;  // split dimensions from the node table
-        timer.begin((widest ? kPartCountWidestNames : kPartCountNames)[width_slot(kW)], (double)a.src.n * rec);
+        const bool in_place = kW > 0 && !widest && !pivots_fit(a);
+        timer.begin((widest ? kPartCountWidestNames : in_place ? kPartCountInPlaceNames : kPartCountNames)[width_slot(kW)],
+                    (double)a.src.n * rec);
         if (widest) k_part_count_widest<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
+        else if (in_place) k_part_count_inplace<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
         else k_part_count<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
         timer.end();
         timer.begin("k_chunk_scan", (double)tiles * bins * 8);
@@ -2911,9 +3006,10 @@ struct Launcher {
         timer.end();
         const u64 nodes = 1ull << a.l1;
         const u64 read = (nodes < tiles ? nodes : tiles) * (u64)kPartTile;
-        timer.begin((widest ? kPartSelectWidestNames : kPartSelectNames)[width_slot(kW)],
+        timer.begin((widest ? kPartSelectWidestNames : in_place ? kPartSelectInPlaceNames : kPartSelectNames)[width_slot(kW)],
                     (double)(read < (u64)a.src.n ? read : (u64)a.src.n) * rec);
         if (widest) k_part_select_widest<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
+        else if (in_place) k_part_select_inplace<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
         else k_part_select<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
         timer.end();
     }
