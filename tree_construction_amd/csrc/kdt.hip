@@ -975,6 +975,47 @@ __device__ __forceinline__ void walk_level_staged(const RecordTile<kSrcRecords, 
     }
 }
 
+// a where the lane's bit of `mask` is clear, else b: one v_cndmask. Written
+// out because a chain of such selects among a thread's record words is
+// otherwise compiled into an indexed load from a scratch copy of them.
+__device__ __forceinline__ u32 pick_lanes(u32 a, u32 b, u64 mask) {
+    u32 r;
+    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(mask));
+    return r;
+}
+
+// The same for split-widest trees: each node's split dimension is staged
+// beside its pivot (reversed the same way) and picks the compared key.
+template <int kW>
+__device__ __forceinline__ void walk_level_staged_dims(const RecordTile<kSrcRecords, kW>& tr, const u64* level_end,
+                                                       const uint8_t* dims_end, u32 (&r)[kPartItems],
+                                                       bool (&valid)[kPartItems]) {
+#pragma unroll
+    for (int j = 0; j < kPartItems; ++j) {
+        const u64 p = level_end[(int)r[j]];
+        const u32 dj = dims_end[(int)r[j]];
+        const u32 index = tr.template at<kW - 1>(j);
+        // (lane masks of dj == 1 and dj == 2; ICMP_EQ = 32)
+        u32 key = tr.template at<0>(j);
+        if constexpr (kW > 2) key = pick_lanes(key, tr.template at<1>(j), __builtin_amdgcn_uicmp(dj, 1u, 32));
+        if constexpr (kW > 3) key = pick_lanes(key, tr.template at<2>(j), __builtin_amdgcn_uicmp(dj, 2u, 32));
+        if (index == (u32)p) valid[j] = false;  // the pivot itself: a node already
+        r[j] = walk_step(r[j], key, index, (u32)(p >> 32), (u32)p);
+    }
+}
+
+template <int kW, int kM>
+__device__ __forceinline__ void walk_staged_dims(const RecordTile<kSrcRecords, kW>& tr, const u64* s_piv,
+                                                 const uint8_t* s_dim, u32 segs, int delta, u32 (&r)[kPartItems],
+                                                 bool (&valid)[kPartItems]) {
+    if constexpr (kM < kMaxDescent) {
+        if (kM >= delta) return;
+        const u32 end = segs * ((2u << kM) - 1);
+        walk_level_staged_dims<kW>(tr, s_piv + end, s_dim + end, r, valid);
+        walk_staged_dims<kW, kM + 1>(tr, s_piv, s_dim, segs, delta, r, valid);
+    }
+}
+
 // Levels kM .. delta-1 of a walk over staged pivots, the dimension of level
 // l0 + m being (kD0 + m) mod (kW - 1) at compile time (records of kW words
 // hold kW - 1 keys, one per dimension). Level m's pivots end at slot
@@ -989,88 +1030,15 @@ __device__ __forceinline__ void walk_staged(const RecordTile<kSrcRecords, kW>& t
     }
 }
 
-// For every item: node[j], the in-level index of its node on level l1,
-// which is (j0 << delta) | digit for its level-l0 segment j0 and its digit
-// (offset of the level-l1 node below the level-l0 one); valid = false for
-// records past the end and for the pivots of levels l0 .. l1-1. The walk
-// compares (key(coordinate l mod k), index) with the pivot of the current
-// node on each level l ([W], tag paragraph: before the pivot -> left child).
-// Call with the whole workgroup: the pivots are staged in LDS first.
-// Records held in registers (kW > 0) of round-robin trees always stage them
-// (the host checks that every tile's fit: pivots_fit), unless kInPlace: then
-// the walk reads them where they are.
-template <int kW, bool kNodeDims, bool kInPlace = false>
-__device__ __forceinline__ void part_nodes(const PartArgs& a, u32 t,
-                                           const RecordTile<kSrcRecords, kW>& tr, i64 wbase,
-                                           u32 (&node)[kPartItems], bool (&valid)[kPartItems]) {
-    __shared__ u64 s_piv[kNodeDims || kInPlace ? 1 : kPivStage];
+// The walk one level at a time, for records without registers (kW = 0) and
+// for pivots read in place: compare with the pivot of the current node, in
+// the level's dimension (or the node's own, from the table).
+template <int kW, bool kNodeDims, bool kInPlace, int kIdx>
+__device__ __forceinline__ void part_nodes_loop(const PartArgs& a, const RecordTile<kSrcRecords, kW>& tr, i64 wbase,
+                                                u32 j_first, u32 segs, bool staged, const u64* s_piv,
+                                                const u32 (&index_of)[kIdx], u32 (&loc)[kPartItems],
+                                                bool (&valid)[kPartItems]) {
     const int delta = a.l1 - a.l0;
-    const u64 p0 = (u64)t * kPartTile;
-    const u64 p1 = p0 + kPartTile < (u64)a.src.n ? p0 + kPartTile : (u64)a.src.n;
-    const u32 j_first = (u32)live_segment(a.geo, p0, a.l0);
-    const u32 segs = (u32)live_segment(a.geo, p1 - 1, a.l0) - j_first + 1;
-    // Level l0 + m of the walk: nodes (j_first << m) + i, i < segs << m, at
-    // slots segs * (2^m - 1) + i (nodes past the last leaf: never visited).
-    const u32 staged_n = segs * ((1u << delta) - 1);
-    // (records held in registers walk each level's pivots in reverse)
-    constexpr bool kReversed = kW > 0 && !kNodeDims && !kInPlace;
-    const bool staged = kReversed || (!kNodeDims && !kInPlace && staged_n <= (u32)kPivStage);
-    if (staged) {
-        const u32 stage_n = staged_n < (u32)kPivStage ? staged_n : (u32)kPivStage;
-        for (u32 s = threadIdx.x; s < stage_n; s += kBlock) {
-            const int m = 31 - __clz(s / segs + 1);
-            const u32 i = s - segs * ((1u << m) - 1);
-            const u64 nd = full_nodes(a.l0 + m) + ((u64)j_first << m) + i;
-            const bool real = nd < (u64)a.geo.n;
-            s_piv[kReversed ? segs * ((2u << m) - 1) - 1 - i : s] = real ? a.piv[nd] : 0;
-        }
-    }
-    // Level-l0 segment of each record: one division for the wave's first
-    // record, then each lane steps over the segment starts it passes (its
-    // records are 64 positions apart, in increasing order). loc: the node's
-    // in-level index less j_first << m.
-    const u32 wfirst = (u32)(wbase - (threadIdx.x & 63));
-    u32 j0 = (u32)live_segment(a.geo, wfirst, a.l0);
-    u32 next = live_begin32(a.s0, j0 + 1);
-    u32 loc[kPartItems];
-#pragma unroll
-    for (int j = 0; j < kPartItems; ++j) {
-        const u32 e = (u32)(wbase + (i64)j * 64);
-        valid[j] = e < (u64)a.src.n;
-        if (valid[j]) {
-            while (e >= next) {
-                ++j0;
-                next = live_begin32(a.s0, j0 + 1);
-            }
-        }
-        // past the end: slot 0, so that every loc stays below segs << m
-        loc[j] = valid[j] ? j0 - j_first : 0u;
-    }
-    // (records without registers: the index word once per item)
-    u32 index_of[kW > 0 && !kNodeDims ? 1 : kPartItems];
-    if constexpr (!(kW > 0 && !kNodeDims)) {
-#pragma unroll
-        for (int j = 0; j < kPartItems; ++j) {
-            const i64 e = wbase + (i64)j * 64;
-            index_of[j] = valid[j] ? tr.word(a.src, j, e, a.src.words - 1) : 0u;
-        }
-    }
-    if (staged) __syncthreads();
-    if constexpr (kReversed) {
-        {  // levels unrolled, dimensions fixed at compile time
-            constexpr int kK = kW - 1;
-#pragma unroll
-            for (int j = 0; j < kPartItems; ++j) loc[j] = ~loc[j];
-            if (a.dim0 == 0) walk_staged<0, kW, 0>(tr, s_piv, segs, delta, loc, valid);
-            else if (a.dim0 == 1) walk_staged<1 % kK, kW, 0>(tr, s_piv, segs, delta, loc, valid);
-            else walk_staged<2 % kK, kW, 0>(tr, s_piv, segs, delta, loc, valid);
-#pragma unroll
-            for (int j = 0; j < kPartItems; ++j) node[j] = (j_first << delta) + ~loc[j];
-            return;
-        }
-    }
-    // One level at a time: compare with the pivot of the current node, in
-    // the level's dimension (or the node's own, from the table).
     int dim = a.dim0;
     for (int m = 0; m < delta; ++m) {
         const u32 slot0 = segs * ((1u << m) - 1);
@@ -1101,8 +1069,96 @@ __device__ __forceinline__ void part_nodes(const PartArgs& a, u32 t,
         }
         if (++dim == a.k) dim = 0;
     }
+}
+
+// For every item: node[j], the in-level index of its node on level l1,
+// which is (j0 << delta) | digit for its level-l0 segment j0 and its digit
+// (offset of the level-l1 node below the level-l0 one); valid = false for
+// records past the end and for the pivots of levels l0 .. l1-1. The walk
+// compares (key(coordinate l mod k), index) with the pivot of the current
+// node on each level l ([W], tag paragraph: before the pivot -> left child).
+// Call with the whole workgroup: the pivots are staged in LDS first.
+// Records held in registers (kW > 0) always stage them, with the node
+// dimensions of split-widest trees (the host checks that every tile's fit:
+// pivots_fit), unless kInPlace: then the walk reads them where they are.
+template <int kW, bool kNodeDims, bool kInPlace = false>
+__device__ __forceinline__ void part_nodes(const PartArgs& a, u32 t,
+                                           const RecordTile<kSrcRecords, kW>& tr, i64 wbase,
+                                           u32 (&node)[kPartItems], bool (&valid)[kPartItems]) {
+    // (records held in registers walk each level's pivots in reverse)
+    constexpr bool kReversed = kW > 0 && !kInPlace;
+    __shared__ u64 s_piv[kInPlace || (kNodeDims && !kReversed) ? 1 : kPivStage];
+    __shared__ uint8_t s_dim[kNodeDims && kReversed ? kPivStage : 1];
+    const int delta = a.l1 - a.l0;
+    const u64 p0 = (u64)t * kPartTile;
+    const u64 p1 = p0 + kPartTile < (u64)a.src.n ? p0 + kPartTile : (u64)a.src.n;
+    const u32 j_first = (u32)live_segment(a.geo, p0, a.l0);
+    const u32 segs = (u32)live_segment(a.geo, p1 - 1, a.l0) - j_first + 1;
+    // Level l0 + m of the walk: nodes (j_first << m) + i, i < segs << m, at
+    // slots segs * (2^m - 1) + i (nodes past the last leaf: never visited).
+    const u32 staged_n = segs * ((1u << delta) - 1);
+    const bool staged = kReversed || (!kNodeDims && !kInPlace && staged_n <= (u32)kPivStage);
+    if (staged) {
+        const u32 stage_n = staged_n < (u32)kPivStage ? staged_n : (u32)kPivStage;
+        for (u32 s = threadIdx.x; s < stage_n; s += kBlock) {
+            const int m = 31 - __clz(s / segs + 1);
+            const u32 i = s - segs * ((1u << m) - 1);
+            const u64 nd = full_nodes(a.l0 + m) + ((u64)j_first << m) + i;
+            const bool real = nd < (u64)a.geo.n;
+            const u32 slot = kReversed ? segs * ((2u << m) - 1) - 1 - i : s;
+            s_piv[slot] = real ? a.piv[nd] : 0;
+            if constexpr (kNodeDims && kReversed) s_dim[slot] = real ? (uint8_t)a.dimtab[nd] : (uint8_t)0;
+        }
+    }
+    // Level-l0 segment of each record: one division for the wave's first
+    // record, then each lane steps over the segment starts it passes (its
+    // records are 64 positions apart, in increasing order). loc: the node's
+    // in-level index less j_first << m.
+    const u32 wfirst = (u32)(wbase - (threadIdx.x & 63));
+    u32 j0 = (u32)live_segment(a.geo, wfirst, a.l0);
+    u32 next = live_begin32(a.s0, j0 + 1);
+    u32 loc[kPartItems];
 #pragma unroll
-    for (int j = 0; j < kPartItems; ++j) node[j] = (j_first << delta) + loc[j];
+    for (int j = 0; j < kPartItems; ++j) {
+        const u32 e = (u32)(wbase + (i64)j * 64);
+        valid[j] = e < (u64)a.src.n;
+        if (valid[j]) {
+            while (e >= next) {
+                ++j0;
+                next = live_begin32(a.s0, j0 + 1);
+            }
+        }
+        // past the end: slot 0, so that every loc stays below segs << m
+        loc[j] = valid[j] ? j0 - j_first : 0u;
+    }
+    // (records without registers: the index word once per item)
+    u32 index_of[kReversed || (kW > 0 && !kNodeDims) ? 1 : kPartItems];
+    if constexpr (!(kReversed || (kW > 0 && !kNodeDims))) {
+#pragma unroll
+        for (int j = 0; j < kPartItems; ++j) {
+            const i64 e = wbase + (i64)j * 64;
+            index_of[j] = valid[j] ? tr.word(a.src, j, e, a.src.words - 1) : 0u;
+        }
+    }
+    if (staged) __syncthreads();
+    if constexpr (kReversed) {  // levels unrolled
+#pragma unroll
+        for (int j = 0; j < kPartItems; ++j) loc[j] = ~loc[j];
+        if constexpr (kNodeDims) {
+            walk_staged_dims<kW, 0>(tr, s_piv, s_dim, segs, delta, loc, valid);
+        } else {  // dimensions fixed at compile time
+            constexpr int kK = kW - 1;
+            if (a.dim0 == 0) walk_staged<0, kW, 0>(tr, s_piv, segs, delta, loc, valid);
+            else if (a.dim0 == 1) walk_staged<1 % kK, kW, 0>(tr, s_piv, segs, delta, loc, valid);
+            else walk_staged<2 % kK, kW, 0>(tr, s_piv, segs, delta, loc, valid);
+        }
+#pragma unroll
+        for (int j = 0; j < kPartItems; ++j) node[j] = (j_first << delta) + ~loc[j];
+    } else {
+        part_nodes_loop<kW, kNodeDims, kInPlace>(a, tr, wbase, j_first, segs, staged, s_piv, index_of, loc, valid);
+#pragma unroll
+        for (int j = 0; j < kPartItems; ++j) node[j] = (j_first << delta) + loc[j];
+    }
 }
 
 // Digit counts of one tile of a re-sort pass. A re-sort pass has at most
@@ -1155,6 +1211,8 @@ template <int kW>
 __global__ __launch_bounds__(kBlock) void k_part_count_widest(PartArgs a) { part_count<kW, true>(a); }
 template <int kW>
 __global__ __launch_bounds__(kBlock) void k_part_count_inplace(PartArgs a) { part_count<kW, false, true>(a); }
+template <int kW>
+__global__ __launch_bounds__(kBlock) void k_part_count_widest_inplace(PartArgs a) { part_count<kW, true, true>(a); }
 
 // Whether tile t of a pass holds the pivot of some level-l1 node. The node
 // with in-level index j0 * 2^delta + b has its pivot where the count of
@@ -1274,6 +1332,10 @@ template <int kW>
 __global__ __launch_bounds__(kBlock) void k_part_scatter_inplace(PartArgs a) { part_scatter<kW, false, false, true>(a); }
 template <int kW>
 __global__ __launch_bounds__(kBlock) void k_part_select_inplace(PartArgs a) { part_scatter<kW, false, true, true>(a); }
+template <int kW>
+__global__ __launch_bounds__(kBlock) void k_part_scatter_widest_inplace(PartArgs a) { part_scatter<kW, true, false, true>(a); }
+template <int kW>
+__global__ __launch_bounds__(kBlock) void k_part_select_widest_inplace(PartArgs a) { part_scatter<kW, true, true, true>(a); }
 
 // Round l's nodes: the pivot of node s = F(l) + j is the record at live
 // position live_begin(j) + |S(2s+1)| of the array sorted for round l
@@ -2878,24 +2940,19 @@ int width_slot(int words) { return words == 2 ? 1 : words == 3 ? 2 : words == 4 
 const char* const kSortScatterNames[2][4] = {
     {"k_sort_scatter<0, 0>", "k_sort_scatter<0, 2>", "k_sort_scatter<0, 3>", "k_sort_scatter<0, 4>"},
     {"k_sort_scatter<1, 0>", "k_sort_scatter<1, 2>", "k_sort_scatter<1, 3>", "k_sort_scatter<1, 4>"}};
-const char* const kPartCountNames[4] = {"k_part_count<0>", "k_part_count<2>", "k_part_count<3>",
-                                        "k_part_count<4>"};
-const char* const kPartScatterNames[4] = {"k_part_scatter<0>", "k_part_scatter<2>",
-                                          "k_part_scatter<3>", "k_part_scatter<4>"};
-const char* const kPartSelectNames[4] = {"k_part_select<0>", "k_part_select<2>", "k_part_select<3>",
-                                         "k_part_select<4>"};
-const char* const kPartSelectWidestNames[4] = {"k_part_select_widest<0>", "k_part_select_widest<2>",
-                                               "k_part_select_widest<3>", "k_part_select_widest<4>"};
-const char* const kPartCountWidestNames[4] = {"k_part_count_widest<0>", "k_part_count_widest<2>",
-                                              "k_part_count_widest<3>", "k_part_count_widest<4>"};
-const char* const kPartScatterWidestNames[4] = {"k_part_scatter_widest<0>", "k_part_scatter_widest<2>",
-                                                "k_part_scatter_widest<3>", "k_part_scatter_widest<4>"};
-const char* const kPartCountInPlaceNames[4] = {"k_part_count_inplace<0>", "k_part_count_inplace<2>",
-                                               "k_part_count_inplace<3>", "k_part_count_inplace<4>"};
-const char* const kPartScatterInPlaceNames[4] = {"k_part_scatter_inplace<0>", "k_part_scatter_inplace<2>",
-                                                 "k_part_scatter_inplace<3>", "k_part_scatter_inplace<4>"};
-const char* const kPartSelectInPlaceNames[4] = {"k_part_select_inplace<0>", "k_part_select_inplace<2>",
-                                                "k_part_select_inplace<3>", "k_part_select_inplace<4>"};
+// [round-robin, in place, split-widest, split-widest in place][width 0, 2, 3, 4]
+#define KDT_PART_NAMES(kind)                                                                          \
+    {{"k_part_" kind "<0>", "k_part_" kind "<2>", "k_part_" kind "<3>", "k_part_" kind "<4>"},         \
+     {"k_part_" kind "_inplace<0>", "k_part_" kind "_inplace<2>", "k_part_" kind "_inplace<3>",       \
+      "k_part_" kind "_inplace<4>"},                                                                  \
+     {"k_part_" kind "_widest<0>", "k_part_" kind "_widest<2>", "k_part_" kind "_widest<3>",          \
+      "k_part_" kind "_widest<4>"},                                                                   \
+     {"k_part_" kind "_widest_inplace<0>", "k_part_" kind "_widest_inplace<2>",                       \
+      "k_part_" kind "_widest_inplace<3>", "k_part_" kind "_widest_inplace<4>"}}
+const char* const kPartCountNames[4][4] = KDT_PART_NAMES("count");
+const char* const kPartScatterNames[4][4] = KDT_PART_NAMES("scatter");
+const char* const kPartSelectNames[4][4] = KDT_PART_NAMES("select");
+#undef KDT_PART_NAMES
 
 // Whether the pivots of levels l0 .. l1-1 below every tile's level-l0
 // segments fit the LDS stage of the round-robin kernels. A tile of T
@@ -2949,6 +3006,21 @@ struct Launcher {
         }
     }
 
+    // The count kernel of a re-sort or select pass: split dimensions by
+    // level (round-robin) or from the node table (split-widest); pivots
+    // staged in LDS or, where a tile's may not fit, read in place.
+    template <int kW>
+    void count(const PartArgs& a, u64 tiles, bool widest, bool in_place) {
+        const int v = (widest ? 2 : 0) + (in_place ? 1 : 0);
+        timer.begin(kPartCountNames[v][width_slot(kW)], (double)a.src.n * 4.0 * a.src.words);
+        const u32 g = xcd_grid(tiles);
+        if (v == 0) k_part_count<kW><<<g, kBlock, 0, stream>>>(a);
+        else if (v == 1) k_part_count_inplace<kW><<<g, kBlock, 0, stream>>>(a);
+        else if (v == 2) k_part_count_widest<kW><<<g, kBlock, 0, stream>>>(a);
+        else k_part_count_widest_inplace<kW><<<g, kBlock, 0, stream>>>(a);
+        timer.end();
+    }
+
     // One re-sort pass by tag (count, scan, scatter).
     template <int kW>
     void part(PartArgs a) {
@@ -2958,21 +3030,18 @@ struct Launcher {
         const int bins = 1 << (a.l1 - a.l0);
         const double rec = 4.0 * a.src.words;
         const bool widest = a.dimtab != nullptr;  // split dimensions from the node table
-        const bool in_place = kW > 0 && !widest && !pivots_fit(a);
-        timer.begin((widest ? kPartCountWidestNames : in_place ? kPartCountInPlaceNames : kPartCountNames)[width_slot(kW)],
-                    (double)a.src.n * rec);
-        if (widest) k_part_count_widest<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
-        else if (in_place) k_part_count_inplace<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
-        else k_part_count<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
-        timer.end();
+        const bool in_place = kW > 0 && !pivots_fit(a);
+        count<kW>(a, tiles, widest, in_place);
         timer.begin("k_chunk_scan", (double)tiles * bins * 8);
         k_chunk_scan<<<bins, kBlock, 0, stream>>>(tile_counts, (i64)tiles, nullptr);
         timer.end();
-        timer.begin((widest ? kPartScatterWidestNames : in_place ? kPartScatterInPlaceNames : kPartScatterNames)[width_slot(kW)],
-                    (double)(a.src.n + a.n_out) * rec);
-        if (widest) k_part_scatter_widest<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
-        else if (in_place) k_part_scatter_inplace<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
-        else k_part_scatter<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
+        const int v = (widest ? 2 : 0) + (in_place ? 1 : 0);
+        timer.begin(kPartScatterNames[v][width_slot(kW)], (double)(a.src.n + a.n_out) * rec);
+        const u32 g = xcd_grid(tiles);
+        if (v == 0) k_part_scatter<kW><<<g, kBlock, 0, stream>>>(a);
+        else if (v == 1) k_part_scatter_inplace<kW><<<g, kBlock, 0, stream>>>(a);
+        else if (v == 2) k_part_scatter_widest<kW><<<g, kBlock, 0, stream>>>(a);
+        else k_part_scatter_widest_inplace<kW><<<g, kBlock, 0, stream>>>(a);
         timer.end();
     }
     void part_any(const PartArgs& a) {
@@ -2994,23 +3063,20 @@ struct Launcher {
         const int bins = 1 << (a.l1 - a.l0);
         const double rec = 4.0 * a.src.words;
         const bool widest = a.dimtab != nullptr;  // split dimensions from the node table
-        const bool in_place = kW > 0 && !widest && !pivots_fit(a);
-        timer.begin((widest ? kPartCountWidestNames : in_place ? kPartCountInPlaceNames : kPartCountNames)[width_slot(kW)],
-                    (double)a.src.n * rec);
-        if (widest) k_part_count_widest<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
-        else if (in_place) k_part_count_inplace<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
-        else k_part_count<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
-        timer.end();
+        const bool in_place = kW > 0 && !pivots_fit(a);
+        count<kW>(a, tiles, widest, in_place);
         timer.begin("k_chunk_scan", (double)tiles * bins * 8);
         k_chunk_scan<<<bins, kBlock, 0, stream>>>(tile_counts, (i64)tiles, nullptr);
         timer.end();
         const u64 nodes = 1ull << a.l1;
         const u64 read = (nodes < tiles ? nodes : tiles) * (u64)kPartTile;
-        timer.begin((widest ? kPartSelectWidestNames : in_place ? kPartSelectInPlaceNames : kPartSelectNames)[width_slot(kW)],
-                    (double)(read < (u64)a.src.n ? read : (u64)a.src.n) * rec);
-        if (widest) k_part_select_widest<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
-        else if (in_place) k_part_select_inplace<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
-        else k_part_select<kW><<<xcd_grid(tiles), kBlock, 0, stream>>>(a);
+        const int v = (widest ? 2 : 0) + (in_place ? 1 : 0);
+        timer.begin(kPartSelectNames[v][width_slot(kW)], (double)(read < (u64)a.src.n ? read : (u64)a.src.n) * rec);
+        const u32 g = xcd_grid(tiles);
+        if (v == 0) k_part_select<kW><<<g, kBlock, 0, stream>>>(a);
+        else if (v == 1) k_part_select_inplace<kW><<<g, kBlock, 0, stream>>>(a);
+        else if (v == 2) k_part_select_widest<kW><<<g, kBlock, 0, stream>>>(a);
+        else k_part_select_widest_inplace<kW><<<g, kBlock, 0, stream>>>(a);
         timer.end();
     }
     void select_any(const PartArgs& a) {
