@@ -2302,8 +2302,10 @@ __device__ __forceinline__ int value_bits(u32 span) { return span == ~0u ? 32 : 
 // Round t in LDS, as local_round, over a subtree whose padding slots carry
 // kPadTag: per-wave counters of the 2^t segments live in the exchange
 // buffers (16-bit, 8 x 2048 at most); items that are not live count into a
-// dummy and write their tag back unchanged.
-__device__ __forceinline__ void rec_round(const uint16_t* order, int t, const Geometry& lg, RecShared& sh) {
+// dummy and write their tag back unchanged. With nodedim (split-widest
+// trees), only the segments whose node splits dimension d are live.
+__device__ __forceinline__ void rec_round(const uint16_t* order, int t, const Geometry& lg, RecShared& sh,
+                                          const uint8_t* nodedim = nullptr, u32 d = 0) {
     RecScratch& s = sh.m.s;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const u32 fl = (1u << t) - 1, segs = 1u << t;
@@ -2320,10 +2322,17 @@ __device__ __forceinline__ void rec_round(const uint16_t* order, int t, const Ge
     for (int j = 0; j < kLocalItems; ++j) e[j] = order[local_slot(j)];
 #pragma unroll
     for (int j = 0; j < kLocalItems; ++j) st[j] = sh.m.tag[e[j]];
+    // (a padding tag is never below fl + segs, so nodedim is read in range)
+    bool on[kLocalItems];
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) {
+        on[j] = st[j] - fl < segs;
+        if (nodedim && on[j]) on[j] = nodedim[st[j]] == d;
+    }
 #pragma unroll
     for (int j = 0; j < kLocalItems; ++j) {
         const u32 b = st[j] - fl;
-        const bool live = b < segs;
+        const bool live = on[j];
         const u64 lv = __ballot(live);
         u32 p_lo, p_hi;
         peer_mask(b, t, (u32)lv, (u32)(lv >> 32), p_lo, p_hi);
@@ -2368,7 +2377,7 @@ __device__ __forceinline__ void rec_round(const uint16_t* order, int t, const Ge
 #pragma unroll
     for (int j = 0; j < kLocalItems; ++j) {
         const u32 b = st[j] - fl;
-        const bool live = b < segs;
+        const bool live = on[j];
         const u32 in_seg = rank[j];
         const u32 under = (2 * b) << dd;
         const u32 left = (u - 1) + (last > under ? (last - under < u ? last - under : u) : 0u);
@@ -2581,7 +2590,6 @@ struct WidestSubtreeArgs {
     int l0;                  // level of the subtree roots
     Geometry geo;
     const u32* recs;         // l0 > 0: A_0 on level l0 (k keys, then the index); nullptr: rows
-    int index_bytes;         // bytes of a point index that can differ
     float* boxes;            // N x 2k domains: the roots' are there; the stage writes its nodes'
     const uint16_t* dimtab;  // the roots' split dimensions
     int32_t* perm;
@@ -2589,61 +2597,176 @@ struct WidestSubtreeArgs {
     int32_t* dims_out;
 };
 
-struct WidestShared : LocalShared {
+struct WidestRecShared {
+    RecShared r;
     uint8_t nodedim[kLocalMax];  // split dimension of each local node
     u32 dim_mask[2];             // dimensions split on a level (by level parity)
 };
 
+template <int kK>
 __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_widest(WidestSubtreeArgs a) {
-    __shared__ WidestShared sh;
+    static_assert(kK >= 1 && kK <= kCachedDims, "every coordinate in the record");
+    constexpr int kW = kK + 1;  // record words: the keys, then the index
+    __shared__ WidestRecShared wsh;
+    RecShared& sh = wsh.r;
+    RecScratch& s = sh.m.s;
 
     const u64 c = full_nodes(a.l0) + blockIdx.x;  // subtree root (global node id)
     const u32 nc = (u32)subtree_size(a.geo, c);
     if (nc == 0) return;
-    const int k = a.k, words = k + 1;
-    const u64 first = a.recs ? live_begin(a.geo, c - full_nodes(a.l0), a.l0) : 0;
-    // Word f of the point at arrival position q: the key of coordinate f < k,
-    // or (f == k) its index.
-    auto word = [&](u32 q, int f) -> u32 {
-        if (a.recs) return a.recs[(first + q) * words + f];
-        return f == k ? q : float_key(__float_as_uint(a.pts[(i64)q * k + f]));
+    // Records of A_0 on level l0 arrive by (coordinate 0, index); the rows
+    // (the whole tree as one subtree) arrive by index.
+    const bool rows = a.recs == nullptr;
+    const u64 first = rows ? 0 : live_begin(a.geo, c - full_nodes(a.l0), a.l0);
+    const u32* recs = rows ? nullptr : a.recs + first * kW;
+    auto load_record = [&](u32 q, u32 (&r)[4]) {
+        const u32 qq = q < nc ? q : nc - 1;
+        if (rows) {
+#pragma unroll
+            for (int f = 0; f < kK; ++f) r[f] = float_key(__float_as_uint(a.pts[(u64)qq * kK + f]));
+            r[kK] = qq;
+        } else if constexpr (kW == 4) {
+            const uint4 v = *reinterpret_cast<const uint4*>(recs + (u64)qq * kW);
+            r[0] = v.x; r[1] = v.y; r[2] = v.z; r[3] = v.w;
+        } else if constexpr (kW == 2) {
+            const uint2 v = *reinterpret_cast<const uint2*>(recs + (u64)qq * kW);
+            r[0] = v.x; r[1] = v.y;
+        } else {
+#pragma unroll
+            for (int f = 0; f < kW; ++f) r[f] = recs[(u64)qq * kW + f];
+        }
     };
+    auto pick = [](const u32 (&r)[4], int f) {
+        return f == 0 ? r[0] : f == 1 ? r[1] : f == 2 ? r[2] : r[3];
+    };
+    // Keys that wait by arrival position while the slots are sorted.
+    u32* stash = reinterpret_cast<u32*>(&sh.m.tag[0]);
+    static_assert(sizeof(sh.m.tag) + sizeof(sh.m.order) >= 2 * kLocalMax * sizeof(u32), "stash");
 
-    // Slot = index rank (rows arrive in index order already).
-    u64 rec[kLocalItems];
+    // arr[j]: arrival position of the point in slot local_slot(j) (slot =
+    // index rank); kept for reading a pivot's coordinate back.
+    u32 arr[kLocalItems];
+    if (rows) {
+        // Slot = arrival: each dimension's order is a stable sort of
+        // (key - min, slot), its keys read from the rows by slot.
 #pragma unroll
-    for (int j = 0; j < kLocalItems; ++j) {
-        const u32 q = (u32)local_slot(j);
-        rec[j] = ~0ull;
-        if (q < nc) rec[j] = ((u64)word(q, k) << 16) | q;
-    }
-    if (a.recs) local_sort(rec, 16, a.index_bytes, nc, sh);
-    // The records arrived by (coordinate 0, index): arrival position -> slot
-    // is the order of dimension 0.
+        for (int j = 0; j < kLocalItems; ++j) {
+            const u32 e = (u32)local_slot(j);
+            arr[j] = e;
+            sh.m.tag[e] = e < nc ? 0 : kPadTag;
+        }
+        for (int d = 0; d < kK; ++d) {
+            u32 key[kLocalItems], pay[kLocalItems];
+            u32 mn[1] = {~0u}, mx[1] = {0u};
 #pragma unroll
-    for (int j = 0; j < kLocalItems; ++j) {
-        const int e = local_slot(j);
-        if ((u32)e >= nc) continue;
-        sh.tag[e] = 0;
-        if (a.recs) sh.order[0][rec[j] & 0xffff] = (uint16_t)e;
-    }
-    if (threadIdx.x == 0) {
-        sh.nodedim[0] = (uint8_t)a.dimtab[c];
-        sh.dim_mask[0] = 1u << a.dimtab[c];
-    }
-
-    auto slot_at = [&](u32 q) -> u32 { return a.recs ? sh.order[0][q] : q; };
-    // The other orders (every one for rows): keys read in arrival order,
-    // put at their slots in the exchange buffer, sorted.
-    for (int d = a.recs ? 1 : 0; d < k; ++d) {
-        __syncthreads();  // slots known; the buffer's last readers done
+            for (int j = 0; j < kLocalItems; ++j) {
+                const u32 e = (u32)local_slot(j);
+                key[j] = float_key(__float_as_uint(a.pts[(u64)(e < nc ? e : nc - 1) * kK + d]));
+                if (e < nc) {
+                    mn[0] = key[j] < mn[0] ? key[j] : mn[0];
+                    mx[0] = key[j] > mx[0] ? key[j] : mx[0];
+                }
+            }
+            rec_min_max<1>(mn, mx, s);
+            const int vbits = value_bits(mx[0] - mn[0]);
+            const u32 pad = vbits == 32 ? ~0u : (1u << vbits) - 1;
+#pragma unroll
+            for (int j = 0; j < kLocalItems; ++j) {
+                const u32 e = (u32)local_slot(j);
+                key[j] = e < nc ? key[j] - mn[0] : pad;
+                pay[j] = e;
+            }
+            rec_sort(key, pay, vbits, s);
+#pragma unroll
+            for (int j = 0; j < kLocalItems; ++j) sh.m.order[d][local_slot(j)] = (uint16_t)pay[j];
+        }
+    } else {
+        // As the round-robin stage with dimension 0 arrived: one vector load
+        // per record; dimensions 1 and 2 wait in the stash.
+        constexpr int kOther = kK - 1;
+        u32 idx[kLocalItems];
+        u32 mn[1 + kOther], mx[1 + kOther];
+#pragma unroll
+        for (int i = 0; i <= kOther; ++i) {
+            mn[i] = ~0u;
+            mx[i] = 0;
+        }
 #pragma unroll
         for (int j = 0; j < kLocalItems; ++j) {
             const u32 q = (u32)local_slot(j);
-            if (q < nc) sh.exch[slot_at(q)] = word(q, d);
+            u32 r[4] = {0, 0, 0, 0};
+            load_record(q, r);
+            const bool ok = q < nc;
+            idx[j] = r[kK];
+            mn[0] = ok && idx[j] < mn[0] ? idx[j] : mn[0];
+            mx[0] = ok && idx[j] > mx[0] ? idx[j] : mx[0];
+#pragma unroll
+            for (int u = 0; u < kOther; ++u) {
+                const u32 key = pick(r, 1 + u);
+                stash[u * kLocalMax + q] = key;
+                mn[1 + u] = ok && key < mn[1 + u] ? key : mn[1 + u];
+                mx[1 + u] = ok && key > mx[1 + u] ? key : mx[1 + u];
+            }
         }
-        __syncthreads();
-        local_order(ColumnKey{sh.exch}, nc, sh.order[d], sh);
+        rec_min_max<1 + kOther>(mn, mx, s);
+        int vbits[1 + kOther];
+        u32 pad[1 + kOther];
+#pragma unroll
+        for (int i = 0; i <= kOther; ++i) {
+            vbits[i] = value_bits(mx[i] - mn[i]);
+            pad[i] = vbits[i] == 32 ? ~0u : (1u << vbits[i]) - 1;
+        }
+        {
+            u32 v[kLocalItems];
+#pragma unroll
+            for (int j = 0; j < kLocalItems; ++j) {
+                const u32 q = (u32)local_slot(j);
+                v[j] = q < nc ? idx[j] - mn[0] : pad[0];
+                arr[j] = q;
+            }
+            rec_sort(v, arr, vbits[0], s);
+        }
+        u32 key[kLocalItems], key2[kLocalItems];
+#pragma unroll
+        for (int j = 0; j < kLocalItems; ++j) {
+            const bool ok = (u32)local_slot(j) < nc;
+            if constexpr (kOther > 0) key[j] = ok ? stash[arr[j]] - mn[1] : pad[1];
+            if constexpr (kOther > 1) key2[j] = ok ? stash[kLocalMax + arr[j]] - mn[2] : pad[2];
+        }
+        __syncthreads();  // stash read before the tags and orders overwrite it
+        u32* wait2 = reinterpret_cast<u32*>(&sh.m.order[1][0]);
+        static_assert(sizeof(sh.m.order[1]) + sizeof(sh.m.order[2]) == kLocalMax * sizeof(u32), "one range");
+#pragma unroll
+        for (int j = 0; j < kLocalItems; ++j) {
+            const u32 e = (u32)local_slot(j);
+            sh.m.order[0][arr[j]] = (uint16_t)e;
+            sh.m.tag[e] = e < nc ? 0 : kPadTag;
+            if constexpr (kOther > 1) wait2[e] = key2[j];
+        }
+        if constexpr (kOther > 0) {
+            u32 pay[kLocalItems];
+#pragma unroll
+            for (int j = 0; j < kLocalItems; ++j) pay[j] = (u32)local_slot(j);
+            rec_sort(key, pay, vbits[1], s);
+            if constexpr (kOther > 1) {
+#pragma unroll
+                for (int j = 0; j < kLocalItems; ++j) key[j] = wait2[local_slot(j)];
+                __syncthreads();  // dimension 2's keys read before order 1 overwrites them
+            }
+#pragma unroll
+            for (int j = 0; j < kLocalItems; ++j) sh.m.order[1][local_slot(j)] = (uint16_t)pay[j];
+            if constexpr (kOther > 1) {
+#pragma unroll
+                for (int j = 0; j < kLocalItems; ++j) pay[j] = (u32)local_slot(j);
+                rec_sort(key, pay, vbits[2], s);
+#pragma unroll
+                for (int j = 0; j < kLocalItems; ++j) sh.m.order[2][local_slot(j)] = (uint16_t)pay[j];
+            }
+        }
+    }
+    if (threadIdx.x == 0) {
+        wsh.nodedim[0] = (uint8_t)a.dimtab[c];
+        wsh.dim_mask[0] = 1u << a.dimtab[c];
     }
     __syncthreads();
 
@@ -2651,41 +2774,39 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_widest(WidestSubtree
     const int rounds = lg.levels - 1;
     for (int t = 0; t < rounds; ++t) {
         const u32 fl = (u32)full_nodes(t), fl1 = (u32)full_nodes(t + 1);
-        const u32 used = sh.dim_mask[t & 1];  // dimensions this level's nodes split
-        if (threadIdx.x == 0) sh.dim_mask[(t + 1) & 1] = 0;  // read a level ago; rounds' barriers follow
-        const bool small = (size_t)kLocalWaves * ((size_t)2 << t) <= sizeof(sh.exch);
-        for (int d = 0; d < k; ++d) {
-            if (!((used >> d) & 1u)) continue;
-            if (small) local_round<uint16_t, true>(sh.order[d], nc, t, lg, sh, sh.nodedim, d);
-            else local_round<uint8_t, true>(sh.order[d], nc, t, lg, sh, sh.nodedim, d);
-        }
+        const u32 used = wsh.dim_mask[t & 1];  // dimensions this level's nodes split
+        if (threadIdx.x == 0) wsh.dim_mask[(t + 1) & 1] = 0;  // read a level ago; the rounds' barriers follow
+#pragma unroll
+        for (int d = 0; d < kK; ++d)
+            if ((used >> d) & 1u) rec_round(sh.m.order[d], t, lg, sh, wsh.nodedim, (u32)d);
         // Level t's pivots carry their node's tag now: each one's thread
         // bounds its node's domain at its coordinate for the two children.
 #pragma unroll
         for (int j = 0; j < kLocalItems; ++j) {
-            const u32 q = (u32)local_slot(j);
-            if (q >= nc) continue;
-            const u32 s = sh.tag[slot_at(q)];
-            if (s < fl || s >= fl1) continue;
-            const int ds = sh.nodedim[s];
-            // the parent's domain and the plane, loaded together
-            const float* from = a.boxes + ((((c + 1) << t) - 1) + (s - fl)) * 2 * (u64)k;
-            float lo[kCachedDims], hi[kCachedDims];
+            const u32 e = (u32)local_slot(j);
+            const u32 sn = sh.m.tag[e];  // (padding: kPadTag, above every level)
+            if (sn < fl || sn >= fl1) continue;
+            const int ds = wsh.nodedim[sn];
+            const float* from = a.boxes + ((((c + 1) << t) - 1) + (sn - fl)) * 2 * (u64)kK;
+            float lo[kK], hi[kK];
 #pragma unroll
-            for (int d = 0; d < kCachedDims; ++d) {
-                lo[d] = d < k ? from[d] : 0.0f;
-                hi[d] = d < k ? from[k + d] : 0.0f;
+            for (int d = 0; d < kK; ++d) {
+                lo[d] = from[d];
+                hi[d] = from[kK + d];
             }
-            const float plane = __uint_as_float(key_bits(word(q, ds)));  // a zero's sign: extents agree
-            for (u32 ch = 2 * s + 1; ch <= 2 * s + 2 && ch < nc; ++ch) {
+            // the pivot's coordinate ds (a zero's sign: the extents agree)
+            u32 pkey;
+            if (rows) pkey = float_key(__float_as_uint(a.pts[(u64)e * kK + ds]));
+            else pkey = recs[(u64)arr[j] * kW + ds];
+            const float plane = __uint_as_float(key_bits(pkey));
+            for (u32 ch = 2 * sn + 1; ch <= 2 * sn + 2 && ch < nc; ++ch) {
                 const u64 g = (((c + 1) << (t + 1)) - 1) + (ch - fl1);
-                const bool left = ch == 2 * s + 1;
-                // child_domain's bounds and extents, in registers
-                float clo[kCachedDims], chi[kCachedDims];
+                const bool left = ch == 2 * sn + 1;
+                float clo[kK], chi[kK];
                 int best = 0;
                 float best_extent = 0.0f;
 #pragma unroll
-                for (int d = 0; d < kCachedDims; ++d) {
+                for (int d = 0; d < kK; ++d) {
                     clo[d] = lo[d];
                     chi[d] = hi[d];
                     if (d == ds) {
@@ -2693,62 +2814,67 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_widest(WidestSubtree
                         else clo[d] = plane;
                     }
                     const float extent = chi[d] - clo[d];
-                    if (d == 0) best_extent = extent;
-                    else if (d < k && extent > best_extent) {
+                    if (d == 0 || extent > best_extent) {
                         best = d;
                         best_extent = extent;
                     }
                 }
                 if (t + 1 < rounds) {  // a parent in the next round: keep its domain
-                    float* box = a.boxes + g * 2 * (u64)k;
+                    float* box = a.boxes + g * 2 * (u64)kK;
 #pragma unroll
-                    for (int d = 0; d < kCachedDims; ++d)
-                        if (d < k) {
-                            box[d] = clo[d];
-                            box[k + d] = chi[d];
-                        }
+                    for (int d = 0; d < kK; ++d) {
+                        box[d] = clo[d];
+                        box[kK + d] = chi[d];
+                    }
                 }
-                sh.nodedim[ch] = (uint8_t)best;
-                atomicOr(&sh.dim_mask[(t + 1) & 1], 1u << best);
+                wsh.nodedim[ch] = (uint8_t)best;
+                atomicOr(&wsh.dim_mask[(t + 1) & 1], 1u << best);
                 if (a.dims_out) a.dims_out[g] = best;
             }
         }
         __syncthreads();
     }
 
-    // Level-order output, one record word at a time (the index first, then
-    // the keys): read in arrival order, put at its node in the exchange
-    // buffer, written out by node. A zero key is read back from the row.
-    u32 node_at[kLocalItems], idx_of[kLocalItems];
+    // Level-order output as in the round-robin stage: each point's record
+    // (read again) goes to its node's row in LDS, then out by node.
+    u32 node[kLocalItems];
 #pragma unroll
     for (int j = 0; j < kLocalItems; ++j) {
         const u32 q = (u32)local_slot(j);
-        node_at[j] = q < nc ? sh.tag[slot_at(q)] : 0u;
+        node[j] = sh.m.tag[rows ? q : sh.m.order[0][q]];
     }
-    const int words_out = a.tree ? words : 1;
-    for (int pass = 0; pass < words_out; ++pass) {
-        const int f = pass == 0 ? k : pass - 1;
-        __syncthreads();  // the buffer's last readers done
+    __syncthreads();  // the rows overlay the tags and orders
+    constexpr int kBatch = 4;  // records in flight at once
 #pragma unroll
-        for (int j = 0; j < kLocalItems; ++j) {
-            const u32 q = (u32)local_slot(j);
-            if (q < nc) sh.exch[node_at[j]] = word(q, f);
+    for (int j0 = 0; j0 < kLocalItems; j0 += kBatch) {
+        u32 r[kBatch][4];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            r[j][0] = r[j][1] = r[j][2] = r[j][3] = 0;
+            load_record((u32)local_slot(j0 + j), r[j]);
         }
-        __syncthreads();
 #pragma unroll
-        for (int i = 0; i < kLocalItems; ++i) {
-            const u32 node = threadIdx.x + (u32)i * kLocalBlock;
-            if (node >= nc) continue;
-            const int lvl = level_of(node);
-            const u64 g = ((c + 1) << lvl) - 1 + (node - full_nodes(lvl));
-            const u32 v = sh.exch[node];
-            if (pass == 0) {
-                idx_of[i] = v;
-                a.perm[g] = (int32_t)v;
-            } else {
-                a.tree[(i64)g * k + f] =
-                    v == 0x80000000u ? a.pts[(i64)idx_of[i] * k + f] : __uint_as_float(key_bits(v));
-            }
+        for (int j = 0; j < kBatch; ++j)
+            if ((u32)local_slot(j0 + j) < nc) sh.rows[node[j0 + j]] = make_uint4(r[j][0], r[j][1], r[j][2], r[j][3]);
+    }
+    __syncthreads();
+    auto word_of = [&](u32 n, int f) -> u32 {
+        const uint4 v = sh.rows[n];
+        return f == 0 ? v.x : f == 1 ? v.y : f == 2 ? v.z : v.w;
+    };
+    for (u32 n = threadIdx.x; n < nc; n += kLocalBlock) {
+        const u64 g = ((c + 1) << level_of(n)) - 1 + (n - full_nodes(level_of(n)));
+        a.perm[g] = (int32_t)word_of(n, kK);
+    }
+    if (a.tree) {
+        for (u32 f = threadIdx.x; f < (u32)kK * nc; f += kLocalBlock) {
+            const u32 n = f / kK, dim = f - n * kK;
+            const u64 g = ((c + 1) << level_of(n)) - 1 + (n - full_nodes(level_of(n)));
+            const u32 key = word_of(n, (int)dim);
+            // a zero key (both zeros have it) is read back from the row,
+            // which keeps the sign of zero
+            a.tree[g * kK + dim] = key == 0x80000000u ? a.pts[(u64)word_of(n, kK) * kK + dim]
+                                                      : __uint_as_float(key_bits(key));
         }
     }
 }
@@ -3383,18 +3509,21 @@ kdt_status run_widest(const float* pts, i64 n, int k, const WidestLayout& wl, ch
         sa.l0 = lds_from;
         sa.geo = geo;
         sa.recs = arrival;
-        int bits = 0;
-        for (u64 v = (u64)(n - 1); v; v >>= 1) ++bits;
-        sa.index_bytes = (bits + kRadixBits - 1) / kRadixBits;
         sa.boxes = boxes;
         sa.dimtab = dimtab;
         sa.perm = perm;
         sa.tree = tree;
         sa.dims_out = dims_out;
         const double below = (double)(n - (i64)full_nodes(lds_from));
-        timer.begin("k_subtree_widest", below * (4.0 * W + 4 + (tree ? 4.0 * k : 0) + (dims_out ? 4 : 0) +
-                                                 2 * 8.0 * k));
-        k_subtree_widest<<<(unsigned)(1ull << lds_from), kLocalBlock, 0, stream>>>(sa);
+        static const char* const kNames[kCachedDims + 1] = {"", "k_subtree_widest<1>", "k_subtree_widest<2>",
+                                                            "k_subtree_widest<3>"};
+        // records (or rows) in and out; each node's domain written (the last
+        // level's excepted) and read once by its children's pivot thread
+        timer.begin(kNames[k], below * (4.0 * W + 4 + (tree ? 4.0 * k : 0) + (dims_out ? 4 : 0) + 2 * 8.0 * k));
+        const unsigned subtrees_n = (unsigned)(1ull << lds_from);
+        if (k == 1) k_subtree_widest<1><<<subtrees_n, kLocalBlock, 0, stream>>>(sa);
+        else if (k == 2) k_subtree_widest<2><<<subtrees_n, kLocalBlock, 0, stream>>>(sa);
+        else k_subtree_widest<3><<<subtrees_n, kLocalBlock, 0, stream>>>(sa);
         timer.end();
     };
     if (lds_from == 0) {  // the whole tree is one subtree, from the rows
