@@ -262,12 +262,24 @@ kdt_status kdt_knn(const float* tree, const int32_t* perm, const int32_t* dims,
 
 /* Diagnostic: kdt_knn with the first pass's budget given. A first-pass
  * thread examines at most `budget` tree points before handing its query to
- * the wave pass (kdt_knn uses max(256, 64 K)); 0 hands every query over. The results
- * do not depend on the budget. Same arguments and errors as kdt_knn. */
+ * the wave pass (kdt_knn uses 32 K, clamped to [128, 512]); 0 hands every
+ * query over. The results do not depend on the budget. Same arguments and
+ * errors as kdt_knn. */
 kdt_status kdt_knn_budget(const float* tree, const int32_t* perm, const int32_t* dims,
                           int64_t N, int32_t k, const float* queries, int64_t Q, int32_t K,
                           int32_t* idx_out, float* d2_out, uint32_t* visits_out,
                           uint32_t budget, hipStream_t stream);
+
+/* Diagnostic: kdt_knn_budget with the wave pass's shared stack capped at
+ * `wave_stack` entries (1 <= wave_stack <= 2048; kdt_knn uses 2048; else
+ * KDT_ERR_INVALID_ARG). When a step's far sides do not fit, each lane walks
+ * its own by parent links, so a small cap exercises that path. budget =
+ * 0xFFFFFFFF selects kdt_knn's own budget. The results depend on neither.
+ * Same arguments and errors as kdt_knn otherwise. */
+kdt_status kdt_knn_debug(const float* tree, const int32_t* perm, const int32_t* dims,
+                         int64_t N, int32_t k, const float* queries, int64_t Q, int32_t K,
+                         int32_t* idx_out, float* d2_out, uint32_t* visits_out,
+                         uint32_t budget, uint32_t wave_stack, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* kdt_status_string(kdt_status status);

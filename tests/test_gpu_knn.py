@@ -173,7 +173,13 @@ def test_knn_rejects_bad_arguments(torch_dev):
             kdt.knn(tree, perm, pts, K)
 
 
-def test_knn_headline_workload_sampled(torch_dev):
+def default_budget(K):
+    """The first pass's hand-over budget of kdt_knn: 32 K within [128, 512]."""
+    return min(max(32 * K, 128), 512)
+
+
+@pytest.mark.parametrize("K", [8, 32])
+def test_knn_headline_workload_sampled(torch_dev, K):
     torch, dev = torch_dev
     name = datagen.HEADLINE
     pts = datagen.cached(name)
@@ -181,17 +187,16 @@ def test_knn_headline_workload_sampled(torch_dev):
     x = torch.from_numpy(pts).to(dev)
     q = torch.from_numpy(qs).to(dev)
     perm, tree = kdt.build(x)
-    K = 8
     say("case knn %s Q=%d K=%d" % (name, len(qs), K))
     visits = torch.empty(len(qs), dtype=torch.int32, device=dev)
     idx, d2 = kdt.knn(tree, perm, q, K, visits=visits)
     torch.cuda.synchronize(dev)
     idx, d2, v = idx.cpu().numpy(), d2.cpu().numpy(), visits.cpu().numpy()
     # the 100 most expensive searches (the first pass hands them to the wave
-    # pass: more than max(256, 64 K) points examined), 256 random ones, and
+    # pass: more than its budget of points examined), 256 random ones, and
     # the first and last query
     costly = np.argsort(-v.astype(np.int64), kind="stable")[:100]
-    assert v[costly[-1]] > max(256, 64 * K), "the sample must include wave-pass queries"
+    assert v[costly[-1]] > default_budget(K), "the sample must include wave-pass queries"
     rng = np.random.default_rng(17)
     sample = np.unique(np.concatenate([costly, rng.choice(len(qs), 256, replace=False), [0, len(qs) - 1]]))
     say("  checking %d queries against brute force" % len(sample))
@@ -200,23 +205,37 @@ def test_knn_headline_workload_sampled(torch_dev):
     assert np.array_equal(d2[sample].view(np.uint32), want_d2.view(np.uint32))
 
 
-def test_knn_wave_stack_overflow(torch_dev):
-    """Identical points never prune (a far side is skipped only when strictly
-    farther than the K-th distance), so the wave pass's shared stack outgrows
-    its LDS and lanes finish subtrees alone; the answer is still the K
-    smallest indices."""
+@pytest.mark.parametrize("gen,cap", [("equal", 1), ("equal", 64), ("gmm", 1), ("gmm", 100), ("ties", 7)])
+def test_knn_wave_stack_overflow(torch_dev, gen, cap):
+    """With the wave pass's stack capped, the far sides that do not fit are
+    walked by their lanes alone (the path a full stack takes); the answer is
+    still brute force's. Identical points never prune (a far side is skipped
+    only when strictly farther than the K-th distance): every point is
+    examined."""
     torch, dev = torch_dev
-    pts = datagen.all_equal(50000, 3)
+    n = 50000
+    pts = {"equal": lambda: datagen.all_equal(n, 3), "gmm": lambda: datagen.gaussian_mixture(n, 3, 5),
+           "ties": lambda: datagen.ties(n, 3, 6)}[gen]()
     x = torch.from_numpy(pts).to(dev)
     perm, tree = kdt.build(x)
     qs = np.concatenate([pts[:8], datagen.uniform(56, 3, 41)]).astype(np.float32)
     q = torch.from_numpy(qs).to(dev)
     for K in (1, 8, 32):
-        say("case knn wave overflow N=50000 K=%d budget=0" % K)
+        say("case knn wave stack cap=%d %s N=%d K=%d budget=0" % (cap, gen, n, K))
         visits = torch.empty(len(qs), dtype=torch.int32, device=dev)
-        idx, d2 = kdt.knn(tree, perm, q, K, visits=visits, budget=0)
+        idx, d2 = kdt.knn(tree, perm, q, K, visits=visits, budget=0, wave_stack=cap)
         torch.cuda.synchronize(dev)
         want_idx, want_d2 = knn_oracle.knn(pts, qs, K)
         assert np.array_equal(idx.cpu().numpy(), want_idx)
         assert np.array_equal(d2.cpu().numpy().view(np.uint32), want_d2.view(np.uint32))
-        assert (visits.cpu().numpy() == 50000).all()
+        if gen == "equal":
+            assert (visits.cpu().numpy() == n).all()
+
+
+def test_knn_wave_stack_cap_rejected(torch_dev):
+    torch, dev = torch_dev
+    pts = torch.from_numpy(datagen.uniform(100, 3, 3)).to(dev)
+    perm, tree = kdt.build(pts)
+    for cap in (0, 2049):
+        with pytest.raises(kdt.KdtError):
+            kdt.knn(tree, perm, pts, 4, wave_stack=cap)

@@ -16,9 +16,11 @@
 // per query would leave the whole pass waiting for them. So a thread gives up
 // after a budget of points and marks the query; a second pass then runs each
 // marked query on a whole wave: the lanes pop subtrees from a shared stack in
-// LDS, each with a lower bound on its squared distance, and prune with the
-// smallest K-th distance over all lanes' lists (every lane's K-th distance
-// bounds the true K-th from above). Merging the lanes' lists gives the same K.
+// LDS, each with a lower bound on its squared distance, and insert their
+// candidates into one K-best list spread over the wave's lanes, so every
+// lane prunes with the query's own K-th distance so far. The K-th distance
+// the first pass had reached when it gave up bounds the answer's from the
+// start, and is handed over in the query's mark.
 //
 // Exactness. Distances are float32 squared distances summed in dimension
 // order with separately rounded products and sums, and neighbours are ranked
@@ -46,11 +48,22 @@ constexpr int kKnnBlock = 256;
 constexpr int kPathRegs = 8;  // split offsets of the deepest path nodes a search thread keeps
 constexpr int kKnnMaxK = 32;       // neighbours per query at most
 // Points one first-pass thread examines before handing its query over:
-// max(256, 64 K), a few times the 99th percentile of a typical search (the
-// work grows with K); measured best within 10 % for K = 1, 8 and 32.
-inline u32 default_budget(int K) { return K * 64u < 256u ? 256u : K * 64u; }
+// 32 K within [128, 512], about the 99th percentile of a typical search (the
+// work grows with K). The wave pass is cheap enough that handing over early
+// pays, down to a point: on a 16M-point tree (1M queries) this was the best
+// budget for K = 1, 8 and 32 (128, 256, 512), where half or twice it cost
+// 10-70 % more.
+inline u32 default_budget(int K) {
+    const u32 b = 32u * (u32)K;
+    return b < 128u ? 128u : (b > 512u ? 512u : b);
+}
 constexpr int kWaveStack = 2048;   // shared stack entries of a wave's search
-constexpr int32_t kHandedOver = -2;  // first output index of a query handed to a wave
+// First output index of a query handed to a wave: kHandedOver when the first
+// pass found fewer than K points, else kHandedOver - 1 - b for the float
+// bits b of its K-th squared distance (a finite or infinite square has
+// b <= 0x7f800000, so the mark stays within int32).
+constexpr int32_t kHandedOver = -2;
+constexpr u32 kInfBits = 0x7f800000u;
 
 struct KnnArgs {
     const float* tree;   // N x k, level order
@@ -65,6 +78,7 @@ struct KnnArgs {
     float* d2_out;       // Q x K or nullptr
     uint32_t* visits_out;  // Q or nullptr: nodes examined per query
     u32 budget;          // points a first-pass thread examines before handing over
+    u32 wave_stack;      // entries of the wave pass's LDS stack in use (<= kWaveStack)
 };
 
 // The query's coordinates: kDims > 0 keeps them in registers (k == kDims);
@@ -177,7 +191,8 @@ __device__ __forceinline__ void write_result(const KnnArgs& a, u64 qi, const Bes
     if (a.visits_out) a.visits_out[qi] = visits;
     int32_t* out_idx = a.idx_out + qi * (u64)a.K;
     if (handed) {
-        out_idx[0] = kHandedOver;
+        const u32 b = best.worst_bits();
+        out_idx[0] = b <= kInfBits ? kHandedOver - 1 - (int32_t)b : kHandedOver;
         return;
     }
     float* out_d2 = a.d2_out ? a.d2_out + qi * (u64)a.K : nullptr;
@@ -288,176 +303,214 @@ __device__ __forceinline__ u32 wave_sum(u32 v) {
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
     return v;
 }
-__device__ __forceinline__ u32 wave_min32(u32 v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const u32 w = __shfl_xor(v, o, 64);
-        v = w < v ? w : v;
-    }
-    return v;
-}
-__device__ __forceinline__ u64 wave_min64(u64 v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const u64 w = __shfl_xor(v, o, 64);
-        v = w < v ? w : v;
-    }
-    return v;
-}
-
 __device__ __forceinline__ int level_of32(u32 i) { return 31 - __clz(i + 1); }
 
-// The whole subtree of node c, by one lane, with the parent-link walk of the
-// first pass (it ends when it climbs back out of c); radius: the wave's
-// smallest K-th distance when the lane started.
-template <int kK, int kDims>
-__device__ __forceinline__ void lane_subtree(const KnnArgs& a, const Query<kDims>& q, Best<kK>& best, u32 c, u32 radius,
-                             int k, u32& examined) {
-    const u32 n = (u32)a.n;
-    u32 curr = c, prev = c == 0 ? ~0u : (c - 1) >> 1;
-    int dim = level_of32(c) % k;
-    for (;;) {
-        const u32 worst = best.worst_bits() < radius ? best.worst_bits() : radius;
-        if (curr >= n) {
-            prev = curr;
-            curr = (curr - 1) >> 1;
-            dim = dim == 0 ? k - 1 : dim - 1;
-            continue;
-        }
-        const u32 parent = curr == 0 ? ~0u : (curr - 1) >> 1;
-        NodeRow<kDims> node;
-        node.load(a.tree, curr, k);
-        const int split = a.dims ? a.dims[curr] : dim;
-        const float diff = q.at(split) - node.at(split);
-        const u32 left = 2 * curr + 1;
-        const u32 near = diff < 0.0f ? left : left + 1;
-        const u32 far = diff < 0.0f ? left + 1 : left;
-        const int down = dim + 1 == k ? 0 : dim + 1;
-        if (prev == parent) {
-            ++examined;
-            const u32 bits = __float_as_uint(squared_distance<kDims>(q, node, k));
-            if (bits <= worst) {
-                const u64 key = ((u64)bits << 32) | (u32)a.perm[curr];
-                if (key < best.slot[0]) best.insert(key);
-            }
-            prev = curr;
-            curr = near;
-            dim = down;
-            continue;
-        }
-        if (prev == near && far < n && __float_as_uint(diff * diff) <= worst) {
-            prev = curr;
-            curr = far;
-            dim = down;
-            continue;
-        }
-        if (curr == c) break;
-        prev = curr;
-        curr = parent;
-        dim = dim == 0 ? k - 1 : dim - 1;
-    }
+__device__ __forceinline__ u64 read_lane64(u64 v, int lane) {
+    const u32 lo = __builtin_amdgcn_readlane((u32)v, lane), hi = __builtin_amdgcn_readlane((u32)(v >> 32), lane);
+    return ((u64)hi << 32) | lo;
 }
 
+// The K best keys of the wave's query so far, one per lane: lanes 0 .. K-1
+// hold them in ascending order (~0 = empty), lanes K .. 63 are unused. Every
+// lane's candidates go into the one list, so the pruning radius is the
+// query's own K-th distance so far, or the cap if that is smaller: a key
+// that K points the first pass examined are all at or below (so that the
+// true K-th is too).
+struct WaveBest {
+    u64 key;   // this lane's slot
+    u64 cap;   // a key known to be no better than the K-th (~0: none)
+    u64 kth;   // min(slot K-1, cap), the same in every lane
+
+    __device__ __forceinline__ void init(u64 bound) {
+        key = ~0ull;
+        cap = kth = bound;
+    }
+    __device__ __forceinline__ u32 worst_bits() const { return (u32)(kth >> 32); }
+    // Inserts every lane's candidate c (~0: none), lowest lane first; each
+    // one shifts the larger keys up one lane and drops slot K-1.
+    __device__ __forceinline__ void insert_all(u64 c, int K) {
+        const int lane = threadIdx.x & 63;
+        u64 want = __ballot(c < kth);
+        while (want) {
+            const int src = __ffsll((long long)want) - 1;
+            want &= want - 1;
+            const u64 ck = read_lane64(c, src);
+            if (ck >= kth) continue;  // (the K-th may have dropped below it meanwhile)
+            const u32 pos = (u32)__popcll(__ballot(lane < K && key < ck));
+            const u64 up = __shfl_up(key, 1, 64);
+            key = (u32)lane < pos ? key : ((u32)lane == pos ? ck : up);
+            const u64 last = read_lane64(key, K - 1);
+            kth = last < cap ? last : cap;
+        }
+    }
+};
+
+// One lane's walk of a subtree by parent links (as in the first pass; it
+// ends when it climbs back out of its root), advanced to its next candidate.
+template <int kDims>
+struct LaneWalk {
+    u32 curr, prev, root;
+    int dim;
+
+    __device__ __forceinline__ void start(u32 c, int k) {
+        root = c;
+        curr = c;
+        prev = c == 0 ? ~0u : (c - 1) >> 1;
+        dim = level_of32(c) % k;
+    }
+    // Walks to the next node visited for the first time and sets *cand to its
+    // key if its distance is within `worst` (else ~0); false when the walk
+    // is over.
+    __device__ __forceinline__ bool next(const KnnArgs& a, const Query<kDims>& q, u32 worst, int k, u64* cand) {
+        const u32 n = (u32)a.n;
+        for (;;) {
+            if (curr >= n) {
+                prev = curr;
+                curr = (curr - 1) >> 1;
+                dim = dim == 0 ? k - 1 : dim - 1;
+                continue;
+            }
+            const u32 parent = curr == 0 ? ~0u : (curr - 1) >> 1;
+            NodeRow<kDims> node;
+            node.load(a.tree, curr, k);
+            const int split = a.dims ? a.dims[curr] : dim;
+            const float diff = q.at(split) - node.at(split);
+            const u32 left = 2 * curr + 1;
+            const u32 near = diff < 0.0f ? left : left + 1;
+            const u32 far = diff < 0.0f ? left + 1 : left;
+            const int down = dim + 1 == k ? 0 : dim + 1;
+            if (prev == parent) {
+                const u32 bits = __float_as_uint(squared_distance<kDims>(q, node, k));
+                *cand = bits <= worst ? ((u64)bits << 32) | (u32)a.perm[curr] : ~0ull;
+                prev = curr;
+                curr = near;
+                dim = down;
+                return true;
+            }
+            if (prev == near && far < n && __float_as_uint(diff * diff) <= worst) {
+                prev = curr;
+                curr = far;
+                dim = down;
+                continue;
+            }
+            if (curr == root) return false;
+            prev = curr;
+            curr = parent;
+            dim = dim == 0 ? k - 1 : dim - 1;
+        }
+    }
+};
+
 // Second pass: every query the first pass handed over, searched by one
-// 64-lane workgroup. Workgroup w owns queries [64w, 64w + 64).
-template <int kK, int kDims>
+// 64-lane workgroup. Workgroup w owns queries [64w, 64w + 64). As in the
+// first pass, a search goes down the near side of every plane first; here
+// each lane follows one such path, one node a step, and leaves the far side
+// of each plane it passes on a shared stack in LDS with a lower bound on its
+// squared distance. A lane whose path ends takes the most recently left far
+// side that is still within the (shared) K-th distance.
+template <int kDims>
 __global__ __launch_bounds__(64) void k_knn_wave(KnnArgs a) {
     __shared__ u64 stack[kWaveStack];  // (lower bound bits << 32) | node
     const int lane = threadIdx.x;
     const u64 base = (u64)blockIdx.x * 64;
     const u64 me = base + lane;
-    const bool marked = me < (u64)a.q && a.idx_out[me * (u64)a.K] == kHandedOver;
+    const int32_t mark = me < (u64)a.q ? a.idx_out[me * (u64)a.K] : 0;
+    const bool marked = mark <= kHandedOver;
     u64 todo = __ballot(marked);
     const u32 n = (u32)a.n;
     const int k = kDims > 0 ? kDims : a.k;
+    constexpr u32 kNone = ~0u;
     while (todo) {
         const int owner = __ffsll((long long)todo) - 1;
         todo &= todo - 1;
         const u64 qi = base + owner;
         Query<kDims> q;
         q.load(a.queries, qi, a.k);
-        Best<kK> best;
-        best.init(a.K);
-        u32 examined = 0, top = 1, radius = ~0u;
-        if (lane == 0) stack[0] = 0;  // the root, bound 0
-        __syncthreads();
-        while (top > 0) {
-            const u32 take = top < 64 ? top : 64;
-            const bool have = (u32)lane < take;
-            u64 entry = 0;
-            if (have) entry = stack[top - 1 - lane];
+        // The first pass's K-th distance bounds the answer's: start from it.
+        const int32_t owner_mark = __shfl(mark, owner, 64);
+        WaveBest best;
+        best.init(owner_mark == kHandedOver ? ~0ull : ((u64)(u32)(kHandedOver - 1 - owner_mark) << 32) | 0xffffffffu);
+        u32 examined = 0, top = 0;
+        // this lane's path: its next node and that node's bound
+        u32 cur = lane == 0 && n > 0 ? 0u : kNone, cur_bound = 0;
+        for (;;) {
+            // lanes without a path take the most recent far sides
+            const u64 idle = __ballot(cur == kNone);
+            const u32 want = (u32)__popcll(idle);
+            const u32 take = want < top ? want : top;
+            if (take == 0 && want == 64) break;  // no path and no far side left
+            if (cur == kNone) {
+                const u32 r = (u32)__popcll(idle & ((1ull << lane) - 1));  // idle lanes below
+                if (r < take) {
+                    const u64 entry = stack[top - 1 - r];
+                    cur = (u32)entry;
+                    cur_bound = (u32)(entry >> 32);
+                }
+            }
             top -= take;
             __syncthreads();  // every pop read before pushes overwrite
-            const u32 node = (u32)entry, bound = (u32)(entry >> 32);
-            u64 push0 = 0, push1 = 0;  // (two scalars: an indexed pair would live in scratch)
-            u32 npush = 0;
-            if (have && bound <= radius && node < n) {
+            // one node of each path: a candidate, then the near side next
+            u64 cand = ~0ull;
+            float diff = 0.0f;
+            bool live = cur != kNone && cur_bound <= best.worst_bits();
+            if (live) {
                 ++examined;
                 NodeRow<kDims> row;
-                row.load(a.tree, node, k);
-                const int dim = a.dims ? a.dims[node] : level_of32(node) % k;
+                row.load(a.tree, cur, k);
+                const int dim = a.dims ? a.dims[cur] : level_of32(cur) % k;
                 const u32 bits = __float_as_uint(squared_distance<kDims>(q, row, k));
-                const u32 worst0 = best.worst_bits() < radius ? best.worst_bits() : radius;
-                if (bits <= worst0) {
-                    const u64 key = ((u64)bits << 32) | (u32)a.perm[node];
-                    if (key < best.slot[0]) best.insert(key);
-                }
-                const u32 worst = best.worst_bits() < radius ? best.worst_bits() : radius;
-                const float diff = q.at(dim) - row.at(dim);
-                const u32 left = 2 * node + 1;
+                if (bits <= best.worst_bits()) cand = ((u64)bits << 32) | (u32)a.perm[cur];
+                diff = q.at(dim) - row.at(dim);
+            }
+            best.insert_all(cand, a.K);
+            const u32 worst = best.worst_bits();
+            u64 push = 0;
+            u32 npush = 0;
+            if (live) {
+                const u32 left = 2 * cur + 1;
                 const u32 near = diff < 0.0f ? left : left + 1;
                 const u32 far = diff < 0.0f ? left + 1 : left;
                 const u32 db = __float_as_uint(diff * diff);
-                const u32 far_bound = db > bound ? db : bound;
-                // far first, near on top: the near side is popped first
+                const u32 far_bound = db > cur_bound ? db : cur_bound;
                 if (far < n && far_bound <= worst) {
-                    push0 = ((u64)far_bound << 32) | far;
+                    push = ((u64)far_bound << 32) | far;
                     npush = 1;
                 }
-                if (near < n && bound <= worst) {
-                    const u64 v = ((u64)bound << 32) | near;
-                    if (npush == 0) push0 = v;
-                    else push1 = v;
-                    ++npush;
-                }
+                cur = near < n ? near : kNone;  // (its bound is cur_bound: checked next step)
+            } else {
+                cur = kNone;
             }
-            // stack slots of this lane's pushes: a wave prefix sum
-            u32 incl = npush;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const u32 t = __shfl_up(incl, o, 64);
-                if (lane >= o) incl += t;
-            }
-            const u32 total = __shfl(incl, 63, 64);
-            if (top + total <= (u32)kWaveStack) {
-                const u32 at = top + incl - npush;
-                if (npush > 0) stack[at] = push0;
-                if (npush > 1) stack[at + 1] = push1;
+            // stack slots of the pushes: lanes in order
+            const u64 pushers = __ballot(npush != 0);
+            const u32 total = (u32)__popcll(pushers);
+            if (top + total <= a.wave_stack) {
+                if (npush) stack[top + (u32)__popcll(pushers & ((1ull << lane) - 1))] = push;
                 top += total;
             } else {
-                // no room: each lane searches its own children itself
-                if (npush > 0) lane_subtree<kK, kDims>(a, q, best, (u32)push0, radius, k, examined);
-                if (npush > 1) lane_subtree<kK, kDims>(a, q, best, (u32)push1, radius, k, examined);
+                // No room: each such lane walks its far side itself, by
+                // parent links, the wave inserting the candidates of every
+                // step; its own path waits.
+                LaneWalk<kDims> walk;
+                bool walking = npush != 0;
+                if (walking) walk.start((u32)push, k);
+                while (__ballot(walking)) {
+                    u64 c = ~0ull;
+                    if (walking) {
+                        if (walk.next(a, q, best.worst_bits(), k, &c)) ++examined;
+                        else walking = false;
+                    }
+                    best.insert_all(c, a.K);
+                }
             }
             __syncthreads();
-            radius = wave_min32(best.worst_bits());
         }
-        // merge: K rounds, each taking the smallest remaining key of all lanes
-        int pos = a.K - 1;  // this lane's next key: slot[pos] (slots descend)
-        int32_t* out_idx = a.idx_out + qi * (u64)a.K;
-        float* out_d2 = a.d2_out ? a.d2_out + qi * (u64)a.K : nullptr;
-        for (int r = 0; r < a.K; ++r) {
-            u64 cand = ~0ull;
-#pragma unroll
-            for (int i = 0; i < kK; ++i)
-                if (i == pos) cand = best.slot[i];
-            const u64 m = wave_min64(cand);
-            if (cand == m && m != ~0ull) --pos;  // keys are distinct: one lane holds m
-            if (lane == 0) {
-                const bool empty = m == ~0ull;
-                out_idx[r] = empty ? -1 : (int32_t)(u32)m;
-                if (out_d2) out_d2[r] = empty ? __uint_as_float(0x7f800000u) : __uint_as_float((u32)(m >> 32));
-            }
+        // the list is in lane order: lane i holds the (i+1)-th neighbour
+        if (lane < a.K) {
+            const bool empty = best.key == ~0ull;
+            a.idx_out[qi * (u64)a.K + lane] = empty ? -1 : (int32_t)(u32)best.key;
+            if (a.d2_out)
+                a.d2_out[qi * (u64)a.K + lane] = empty ? __uint_as_float(0x7f800000u)
+                                                       : __uint_as_float((u32)(best.key >> 32));
         }
         const u32 all = wave_sum(examined);
         if (lane == 0 && a.visits_out) a.visits_out[qi] += all;
@@ -472,19 +525,19 @@ void launch_knn(const KnnArgs& a, hipStream_t stream) {
     switch (a.k) {
         case 2:
             k_knn<kK, 2><<<grid, kKnnBlock, 0, stream>>>(a);
-            k_knn_wave<kK, 2><<<waves, 64, 0, stream>>>(a);
+            k_knn_wave<2><<<waves, 64, 0, stream>>>(a);
             break;
         case 3:
             k_knn<kK, 3><<<grid, kKnnBlock, 0, stream>>>(a);
-            k_knn_wave<kK, 3><<<waves, 64, 0, stream>>>(a);
+            k_knn_wave<3><<<waves, 64, 0, stream>>>(a);
             break;
         case 4:
             k_knn<kK, 4><<<grid, kKnnBlock, 0, stream>>>(a);
-            k_knn_wave<kK, 4><<<waves, 64, 0, stream>>>(a);
+            k_knn_wave<4><<<waves, 64, 0, stream>>>(a);
             break;
         default:
             k_knn<kK, 0><<<grid, kKnnBlock, 0, stream>>>(a);
-            k_knn_wave<kK, 0><<<waves, 64, 0, stream>>>(a);
+            k_knn_wave<0><<<waves, 64, 0, stream>>>(a);
             break;
     }
 }
@@ -497,9 +550,9 @@ bool overlap(const void* a, size_t an, const void* b, size_t bn) {
 
 kdt_status knn_impl(const float* tree, const int32_t* perm, const int32_t* dims, int64_t N, int32_t k,
                     const float* queries, int64_t Q, int32_t K, int32_t* idx_out, float* d2_out,
-                    uint32_t* visits_out, uint32_t budget, hipStream_t stream) {
+                    uint32_t* visits_out, uint32_t budget, uint32_t wave_stack, hipStream_t stream) {
     if (N < 0 || N > INT32_MAX || k < 1 || k > 65535 || Q < 0 || Q > INT32_MAX || K < 1 ||
-        K > kKnnMaxK)
+        K > kKnnMaxK || wave_stack < 1 || wave_stack > (uint32_t)kWaveStack)
         return KDT_ERR_INVALID_ARG;
     if (Q == 0) return KDT_OK;
     if (!queries || !idx_out || (N > 0 && (!tree || !perm))) return KDT_ERR_INVALID_ARG;
@@ -516,7 +569,7 @@ kdt_status knn_impl(const float* tree, const int32_t* perm, const int32_t* dims,
     if (overlap(idx_out, out_b, d2_out, out_b) || overlap(visits_out, v_b, idx_out, out_b) ||
         overlap(visits_out, v_b, d2_out, out_b))
         return KDT_ERR_INVALID_ARG;
-    KnnArgs a{tree, perm, dims, N, k, queries, Q, K, idx_out, d2_out, visits_out, budget};
+    KnnArgs a{tree, perm, dims, N, k, queries, Q, K, idx_out, d2_out, visits_out, budget, wave_stack};
     if (K <= 1) launch_knn<1>(a, stream);
     else if (K <= 2) launch_knn<2>(a, stream);
     else if (K <= 4) launch_knn<4>(a, stream);
@@ -532,12 +585,21 @@ extern "C" kdt_status kdt_knn(const float* tree, const int32_t* perm, const int3
                               int32_t k, const float* queries, int64_t Q, int32_t K, int32_t* idx_out,
                               float* d2_out, uint32_t* visits_out, hipStream_t stream) {
     return knn_impl(tree, perm, dims, N, k, queries, Q, K, idx_out, d2_out, visits_out,
-                    default_budget(K), stream);
+                    default_budget(K), kWaveStack, stream);
 }
 
 extern "C" kdt_status kdt_knn_budget(const float* tree, const int32_t* perm, const int32_t* dims,
                                      int64_t N, int32_t k, const float* queries, int64_t Q, int32_t K,
                                      int32_t* idx_out, float* d2_out, uint32_t* visits_out,
                                      uint32_t budget, hipStream_t stream) {
-    return knn_impl(tree, perm, dims, N, k, queries, Q, K, idx_out, d2_out, visits_out, budget, stream);
+    return knn_impl(tree, perm, dims, N, k, queries, Q, K, idx_out, d2_out, visits_out, budget, kWaveStack,
+                    stream);
+}
+
+extern "C" kdt_status kdt_knn_debug(const float* tree, const int32_t* perm, const int32_t* dims,
+                                    int64_t N, int32_t k, const float* queries, int64_t Q, int32_t K,
+                                    int32_t* idx_out, float* d2_out, uint32_t* visits_out,
+                                    uint32_t budget, uint32_t wave_stack, hipStream_t stream) {
+    return knn_impl(tree, perm, dims, N, k, queries, Q, K, idx_out, d2_out, visits_out,
+                    budget == 0xffffffffu ? default_budget(K) : budget, wave_stack, stream);
 }

@@ -57,6 +57,8 @@ SIGNATURES = {
                                _VOIDP]),
     "kdt_knn_budget": (ctypes.c_int, [_VOIDP, _VOIDP, _VOIDP, _I64, _I32, _VOIDP, _I64, _I32, _VOIDP, _VOIDP,
                                       _VOIDP, ctypes.c_uint32, _VOIDP]),
+    "kdt_knn_debug": (ctypes.c_int, [_VOIDP, _VOIDP, _VOIDP, _I64, _I32, _VOIDP, _I64, _I32, _VOIDP, _VOIDP,
+                                     _VOIDP, ctypes.c_uint32, ctypes.c_uint32, _VOIDP]),
     "kdt_unique_workspace_size": (_SZ, [_I64, _I32]),
     "kdt_unique": (ctypes.c_int, [_VOIDP, _I64, _I32, _VOIDP, _VOIDP, _VOIDP, _SZ, _VOIDP]),
     "kdt_unique_profiled": (ctypes.c_int, [_VOIDP, _I64, _I32, _VOIDP, _VOIDP, _VOIDP, _SZ, _VOIDP,
@@ -374,7 +376,8 @@ def build(points, want_tree: bool = True, stream=None):
     return Builder(n, k, points.device).build(points, want_tree=want_tree, stream=stream)
 
 
-def knn(tree, perm, queries, K: int, idx=None, d2=None, visits=None, stream=None, budget=None, dims=None):
+def knn(tree, perm, queries, K: int, idx=None, d2=None, visits=None, stream=None, budget=None, dims=None,
+        wave_stack=None):
     """K nearest neighbours of every query among the points of a built tree.
 
     tree, perm: the outputs of build() ((N, k) float32 and (N,) int32 on a
@@ -384,7 +387,8 @@ def knn(tree, perm, queries, K: int, idx=None, d2=None, visits=None, stream=None
     (build_widest's third output). A (Q,) int32 tensor passed as `visits`
     receives the number of tree points each search examined. `budget`
     (diagnostic) sets how many points a first-pass thread examines before
-    handing its query to the wave pass."""
+    handing its query to the wave pass; `wave_stack` (diagnostic, 1..2048)
+    caps the wave pass's shared stack."""
     import torch
     _validate_points(queries)
     if tree is not None:
@@ -407,7 +411,10 @@ def knn(tree, perm, queries, K: int, idx=None, d2=None, visits=None, stream=None
             ctypes.c_void_p(queries.data_ptr()), q, int(K),
             ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(d2.data_ptr()),
             ctypes.c_void_p(visits.data_ptr() if visits is not None else 0)]
-    if budget is None:
+    if wave_stack is not None:
+        st = lib().kdt_knn_debug(*args, 0xFFFFFFFF if budget is None else int(budget), int(wave_stack),
+                                 _stream_handle(queries.device, stream))
+    elif budget is None:
         st = lib().kdt_knn(*args, _stream_handle(queries.device, stream))
     else:
         st = lib().kdt_knn_budget(*args, int(budget), _stream_handle(queries.device, stream))
