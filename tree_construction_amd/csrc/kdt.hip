@@ -2597,6 +2597,127 @@ struct WidestSubtreeArgs {
     int32_t* dims_out;
 };
 
+// The live points of level t of a split-widest subtree as one list: for each
+// dimension d that some level-t node splits, in turn, the slots of the
+// points whose node splits d, in the order of d. Each node's points are then
+// in its own dimension's order, and one round over the list ranks them all.
+// Returns the list's length (uniform).
+__device__ __forceinline__ u32 rec_live_list(RecShared& sh, const uint8_t* nodedim, u32 used, int t, int dims,
+                                             uint16_t* list) {
+    RecScratch& s = sh.m.s;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const u32 fl = (1u << t) - 1, segs = 1u << t;
+    u32 base = 0;
+    for (int d = 0; d < dims; ++d) {
+        if (!((used >> d) & 1u)) continue;
+        u32 e[kLocalItems];
+        u64 keep[kLocalItems];
+        u32 wave_total = 0;
+#pragma unroll
+        for (int j = 0; j < kLocalItems; ++j) e[j] = sh.m.order[d][local_slot(j)];
+#pragma unroll
+        for (int j = 0; j < kLocalItems; ++j) {
+            const u32 st = sh.m.tag[e[j]];  // (padding: kPadTag, on no level)
+            const bool on = st - fl < segs && nodedim[st] == (uint8_t)d;
+            keep[j] = __ballot(on);
+            wave_total += (u32)__popcll(keep[j]);
+        }
+        if (lane == 0) s.wave[w] = wave_total;
+        __syncthreads();
+        u32 at = base, total = 0;
+#pragma unroll
+        for (int v = 0; v < kLocalWaves; ++v) {
+            const u32 c = s.wave[v];
+            at += v < w ? c : 0u;
+            total += c;
+        }
+#pragma unroll
+        for (int j = 0; j < kLocalItems; ++j) {
+            if ((keep[j] >> lane) & 1u) list[at + lanes_below((u32)keep[j], (u32)(keep[j] >> 32))] = (uint16_t)e[j];
+            at += (u32)__popcll(keep[j]);
+        }
+        base += total;
+        __syncthreads();  // s.wave read before the next dimension writes it
+    }
+    return base;
+}
+
+// Round t over such a list of n_live slots, as rec_round with every listed
+// point live. Per-wave segment counters of type Count (16-bit, or 8-bit on
+// levels whose segments hold at most 255 points) in exch[0].
+template <typename Count>
+__device__ __forceinline__ void rec_round_list(const uint16_t* list, u32 n_live, int t, const Geometry& lg,
+                                               RecShared& sh) {
+    RecScratch& s = sh.m.s;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const u32 fl = (1u << t) - 1, segs = 1u << t;
+    constexpr u32 kPer = 4 / sizeof(Count);  // counters a word
+    Count* cnt = reinterpret_cast<Count*>(&s.exch[0][0]);  // [kLocalWaves][segs]
+    u32* cnt_words = &s.exch[0][0];
+    const u32 words = (kLocalWaves * segs + kPer - 1) / kPer;
+    for (u32 i = tid; i < words; i += kLocalBlock) cnt_words[i] = 0;
+    __syncthreads();
+    u32 e[kLocalItems], st[kLocalItems], rank[kLocalItems];
+    bool in[kLocalItems];
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) {
+        in[j] = (u32)local_slot(j) < n_live;
+        e[j] = in[j] ? list[local_slot(j)] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) st[j] = in[j] ? sh.m.tag[e[j]] : fl;
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) {
+        const u32 b = st[j] - fl;
+        const u64 lv = __ballot(in[j]);
+        u32 p_lo, p_hi;
+        peer_mask(b, t, (u32)lv, (u32)(lv >> 32), p_lo, p_hi);
+        const u32 before = lanes_below(p_lo, p_hi);
+        Count* cp = in[j] ? &cnt[w * segs + b] : reinterpret_cast<Count*>(&s.dummy[lane]);
+        const u32 seen = *cp;
+        rank[j] = seen + before;
+        *cp = (Count)(seen + __popc(p_lo) + __popc(p_hi));
+    }
+    __syncthreads();
+    // prefix over the waves, kPer counters a word (a segment's total fits
+    // one counter, so the lanes of a word never carry into each other)
+    if (segs >= kPer) {
+        const u32 row = segs / kPer;
+        for (u32 i = tid; i < row; i += kLocalBlock) {
+            u32 run = 0;
+#pragma unroll
+            for (int v = 0; v < kLocalWaves; ++v) {
+                const u32 c = cnt_words[v * row + i];
+                cnt_words[v * row + i] = run;
+                run += c;
+            }
+        }
+    } else if (tid < (int)segs) {
+        u32 run = 0;
+#pragma unroll
+        for (int v = 0; v < kLocalWaves; ++v) {
+            const u32 c = cnt[v * segs + tid];
+            cnt[v * segs + tid] = (Count)run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    const u32 dd = (u32)(lg.levels - 2 - t), u = 1u << dd, last = (u32)lg.last;
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) rank[j] += in[j] ? (u32)cnt[w * segs + (st[j] - fl)] : 0u;
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) {
+        if (!in[j]) continue;
+        const u32 b = st[j] - fl;
+        const u32 in_seg = rank[j];
+        const u32 under = (2 * b) << dd;
+        const u32 left = (u - 1) + (last > under ? (last - under < u ? last - under : u) : 0u);
+        const u32 next = in_seg < left ? 2 * st[j] + 1 : (in_seg > left ? 2 * st[j] + 2 : st[j]);
+        sh.m.tag[e[j]] = (uint16_t)next;
+    }
+    __syncthreads();
+}
+
 struct WidestRecShared {
     RecShared r;
     uint8_t nodedim[kLocalMax];  // split dimension of each local node
@@ -2776,9 +2897,17 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_widest(WidestSubtree
         const u32 fl = (u32)full_nodes(t), fl1 = (u32)full_nodes(t + 1);
         const u32 used = wsh.dim_mask[t & 1];  // dimensions this level's nodes split
         if (threadIdx.x == 0) wsh.dim_mask[(t + 1) & 1] = 0;  // read a level ago; the rounds' barriers follow
-#pragma unroll
-        for (int d = 0; d < kK; ++d)
-            if ((used >> d) & 1u) rec_round(sh.m.order[d], t, lg, sh, wsh.nodedim, (u32)d);
+        if (__popc(used) == 1) {  // one dimension: its order is the list
+            rec_round(sh.m.order[__ffs(used) - 1], t, lg, sh, wsh.nodedim, (u32)(__ffs(used) - 1));
+        } else {
+            // the list in exch[1], the counters in exch[0] (16 KB: 16-bit
+            // up to 1024 segments; 8-bit where a segment holds at most 255
+            // points, which is every level with more segments)
+            uint16_t* list = reinterpret_cast<uint16_t*>(&s.exch[1][0]);
+            const u32 n_live = rec_live_list(sh, wsh.nodedim, used, t, kK, list);
+            if (lg.levels - t <= 8) rec_round_list<uint8_t>(list, n_live, t, lg, sh);
+            else rec_round_list<uint16_t>(list, n_live, t, lg, sh);
+        }
         // Level t's pivots carry their node's tag now: each one's thread
         // bounds its node's domain at its coordinate for the two children.
 #pragma unroll
