@@ -1245,19 +1245,50 @@ __device__ bool tile_has_pivot(const PartArgs& a, u32 t) {
     return __syncthreads_or(hit) != 0;
 }
 
+// The tile of a pass that holds the pivot of level-l1 node i = j0 * 2^delta
+// + b: the pivot is the record where the count of digit-b records reaches
+// bin_prefix(j0, b) + |S(left child)|, and tile t holds the digit-b records
+// counted from chunk_counts[b][t] (scanned: the count before the tile) up to
+// chunk_counts[b][t+1], so the pivot's tile is the last t whose count before
+// it is at most that target. Only the tiles of segment j0 can hold it; they
+// are searched 256 probes at a time, one every `stride` tiles, each round
+// narrowing the range to the stride the target fell in, until one tile is
+// left. Call with the whole workgroup.
+__device__ u32 pivot_tile(const PartArgs& a, u32 i) {
+    const int delta = a.l1 - a.l0;
+    const u32 j0 = i >> delta, b = i & ((1u << delta) - 1);
+    const u32 left = a.leaf_level ? 0u : subtree_size32(a.s2, 2 * i);
+    const u32 target = bin_prefix32(a.s1, j0, b, delta) + left;
+    const u32* row = a.chunk_counts + (u64)b * a.tiles;
+    const u32 t_lo = live_begin32(a.s0, j0) / kPartTile;
+    const u32 end = live_begin32(a.s0, j0 + 1);  // (a segment is never empty)
+    u32 t_hi = (end - 1) / kPartTile;
+    if (t_hi >= a.tiles) t_hi = a.tiles - 1;
+    // Counts before the tiles do not decrease, and the first tile's is at
+    // most the target (only earlier segments' records precede it): of the
+    // probes, those at most the target are a leading run of at least one.
+    u32 lo = t_lo, len = t_hi - t_lo + 1;
+    while (len > 1) {
+        const u32 stride = (len + kBlock - 1) / kBlock;
+        const u32 probe = lo + threadIdx.x * stride;
+        const u32 c = (u32)__syncthreads_count(probe < lo + len && row[probe] <= target);
+        lo += (c - 1) * stride;
+        const u32 rest = t_hi + 1 - lo;
+        len = stride < rest ? stride : rest;
+    }
+    return lo;
+}
+
 // kSelect: the pass only fixes the level-l1 nodes; it reads the tiles that
 // hold their pivots and writes no records (the array keeps its level-l0
 // order, and its next re-sort walks the levels in between as well).
-template <int kW, bool kNodeDims, bool kSelect = false, bool kInPlace = false>
-__device__ __forceinline__ void part_scatter(const PartArgs& a) {
+// only: for a select, the in-level index of the one node whose pivot this
+// workgroup writes, or kEveryNode: every pivot in the tile (of this array's
+// dimension, for split-widest trees).
+constexpr u32 kEveryNode = ~0u;
+template <int kW, bool kNodeDims, bool kSelect, bool kInPlace>
+__device__ __forceinline__ void part_tile(const PartArgs& a, u32 t, u32 only) {
     __shared__ u32 count[kWaves][kRadix];  // per-wave digit counts, then first slots
-    const u32 t = xcd_tile(a.tiles);
-    if (t >= a.tiles) return;
-    if constexpr (kSelect) {
-        if constexpr (kNodeDims)
-            if (no_nodes_here(a)) return;
-        if (!tile_has_pivot<kNodeDims>(a, t)) return;
-    }
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const i64 wbase = (i64)t * kPartTile + (i64)w * (64 * kPartItems) + lane;
     const int delta = a.l1 - a.l0;
@@ -1306,7 +1337,8 @@ __device__ __forceinline__ void part_scatter(const PartArgs& a) {
         }
         const u32 left = a.leaf_level ? 0u : subtree_size32(a.s2, 2 * node[j]);
         bool mine = true;  // the node splits this array's dimension
-        if constexpr (kNodeDims) mine = a.dimtab[full_nodes(a.l1) + node[j]] == (uint16_t)a.array_dim;
+        if (kSelect && only != kEveryNode) mine = node[j] == only;  // (whose dimension the caller checked)
+        else if constexpr (kNodeDims) mine = a.dimtab[full_nodes(a.l1) + node[j]] == (uint16_t)a.array_dim;
         if (a.piv_out && in_segment == left && mine) {
             const u64 s = full_nodes(a.l1) + node[j];
             const u32 idx = tr.word(a.src, j, e, a.src.words - 1);
@@ -1319,23 +1351,63 @@ __device__ __forceinline__ void part_scatter(const PartArgs& a) {
     }
 }
 
+template <int kW, bool kNodeDims, bool kInPlace = false>
+__device__ __forceinline__ void part_scatter(const PartArgs& a) {
+    const u32 t = xcd_tile(a.tiles);
+    if (t >= a.tiles) return;
+    part_tile<kW, kNodeDims, false, kInPlace>(a, t, 0);
+}
+
+// A select: one workgroup per node of level l1 (of this array's dimension,
+// for split-widest trees), on the tile that holds its pivot.
+template <int kW, bool kNodeDims, bool kInPlace = false>
+__device__ __forceinline__ void part_select(const PartArgs& a) {
+    const u32 i = blockIdx.x;
+    if (full_nodes(a.l1) + i >= (u64)a.geo.n) return;
+    if constexpr (kNodeDims)
+        if (a.dimtab[full_nodes(a.l1) + i] != (uint16_t)a.array_dim) return;
+    part_tile<kW, kNodeDims, true, kInPlace>(a, pivot_tile(a, i), i);
+}
+
+// A select over levels with more nodes: one workgroup per tile, those that
+// hold pivots writing them all.
+template <int kW, bool kNodeDims, bool kInPlace = false>
+__device__ __forceinline__ void part_select_tiles(const PartArgs& a) {
+    const u32 t = xcd_tile(a.tiles);
+    if (t >= a.tiles) return;
+    if constexpr (kNodeDims)
+        if (no_nodes_here(a)) return;
+    if (!tile_has_pivot<kNodeDims>(a, t)) return;
+    part_tile<kW, kNodeDims, true, kInPlace>(a, t, kEveryNode);
+}
+
 template <int kW>
 __global__ __launch_bounds__(kBlock) void k_part_scatter(PartArgs a) { part_scatter<kW, false>(a); }
 template <int kW>
 __global__ __launch_bounds__(kBlock) void k_part_scatter_widest(PartArgs a) { part_scatter<kW, true>(a); }
 template <int kW>
-__global__ __launch_bounds__(kBlock) void k_part_select(PartArgs a) { part_scatter<kW, false, true>(a); }
+__global__ __launch_bounds__(kBlock) void k_part_select(PartArgs a) { part_select<kW, false>(a); }
 template <int kW>
-__global__ __launch_bounds__(kBlock) void k_part_select_widest(PartArgs a) { part_scatter<kW, true, true>(a); }
+__global__ __launch_bounds__(kBlock) void k_part_select_widest(PartArgs a) { part_select<kW, true>(a); }
 // Round-robin passes whose tiles' pivots may not fit the LDS stage.
 template <int kW>
-__global__ __launch_bounds__(kBlock) void k_part_scatter_inplace(PartArgs a) { part_scatter<kW, false, false, true>(a); }
+__global__ __launch_bounds__(kBlock) void k_part_scatter_inplace(PartArgs a) { part_scatter<kW, false, true>(a); }
 template <int kW>
-__global__ __launch_bounds__(kBlock) void k_part_select_inplace(PartArgs a) { part_scatter<kW, false, true, true>(a); }
+__global__ __launch_bounds__(kBlock) void k_part_select_inplace(PartArgs a) { part_select<kW, false, true>(a); }
 template <int kW>
-__global__ __launch_bounds__(kBlock) void k_part_scatter_widest_inplace(PartArgs a) { part_scatter<kW, true, false, true>(a); }
+__global__ __launch_bounds__(kBlock) void k_part_scatter_widest_inplace(PartArgs a) { part_scatter<kW, true, true>(a); }
 template <int kW>
-__global__ __launch_bounds__(kBlock) void k_part_select_widest_inplace(PartArgs a) { part_scatter<kW, true, true, true>(a); }
+__global__ __launch_bounds__(kBlock) void k_part_select_widest_inplace(PartArgs a) { part_select<kW, true, true>(a); }
+template <int kW>
+__global__ __launch_bounds__(kBlock) void k_part_select_tiles(PartArgs a) { part_select_tiles<kW, false>(a); }
+template <int kW>
+__global__ __launch_bounds__(kBlock) void k_part_select_tiles_inplace(PartArgs a) { part_select_tiles<kW, false, true>(a); }
+template <int kW>
+__global__ __launch_bounds__(kBlock) void k_part_select_tiles_widest(PartArgs a) { part_select_tiles<kW, true>(a); }
+template <int kW>
+__global__ __launch_bounds__(kBlock) void k_part_select_tiles_widest_inplace(PartArgs a) {
+    part_select_tiles<kW, true, true>(a);
+}
 
 // Round l's nodes: the pivot of node s = F(l) + j is the record at live
 // position live_begin(j) + |S(2s+1)| of the array sorted for round l
@@ -3207,6 +3279,7 @@ const char* const kSortScatterNames[2][4] = {
 const char* const kPartCountNames[4][4] = KDT_PART_NAMES("count");
 const char* const kPartScatterNames[4][4] = KDT_PART_NAMES("scatter");
 const char* const kPartSelectNames[4][4] = KDT_PART_NAMES("select");
+const char* const kPartSelectTilesNames[4][4] = KDT_PART_NAMES("select_tiles");
 #undef KDT_PART_NAMES
 
 // Whether the pivots of levels l0 .. l1-1 below every tile's level-l0
@@ -3323,15 +3396,27 @@ struct Launcher {
         timer.begin("k_chunk_scan", (double)tiles * bins * 8);
         k_chunk_scan<<<bins, kBlock, 0, stream>>>(tile_counts, (i64)tiles, nullptr);
         timer.end();
-        const u64 nodes = 1ull << a.l1;
-        const u64 read = (nodes < tiles ? nodes : tiles) * (u64)kPartTile;
+        // At most one node per two tiles: one workgroup per node (nodes past
+        // the last leaf return), each on the tile its search finds. Else one
+        // per tile, those holding pivots writing them.
+        const u64 level_nodes = 1ull << a.l1, exist = (u64)a.geo.n - full_nodes(a.l1);
+        const u64 nodes = level_nodes < exist ? level_nodes : exist;
         const int v = (widest ? 2 : 0) + (in_place ? 1 : 0);
-        timer.begin(kPartSelectNames[v][width_slot(kW)], (double)(read < (u64)a.src.n ? read : (u64)a.src.n) * rec);
-        const u32 g = xcd_grid(tiles);
-        if (v == 0) k_part_select<kW><<<g, kBlock, 0, stream>>>(a);
-        else if (v == 1) k_part_select_inplace<kW><<<g, kBlock, 0, stream>>>(a);
-        else if (v == 2) k_part_select_widest<kW><<<g, kBlock, 0, stream>>>(a);
-        else k_part_select_widest_inplace<kW><<<g, kBlock, 0, stream>>>(a);
+        if (2 * nodes <= tiles) {
+            timer.begin(kPartSelectNames[v][width_slot(kW)], (double)nodes * kPartTile * rec);
+            const u32 g = (u32)nodes;
+            if (v == 0) k_part_select<kW><<<g, kBlock, 0, stream>>>(a);
+            else if (v == 1) k_part_select_inplace<kW><<<g, kBlock, 0, stream>>>(a);
+            else if (v == 2) k_part_select_widest<kW><<<g, kBlock, 0, stream>>>(a);
+            else k_part_select_widest_inplace<kW><<<g, kBlock, 0, stream>>>(a);
+        } else {
+            timer.begin(kPartSelectTilesNames[v][width_slot(kW)], (double)a.src.n * rec);
+            const u32 g = xcd_grid(tiles);
+            if (v == 0) k_part_select_tiles<kW><<<g, kBlock, 0, stream>>>(a);
+            else if (v == 1) k_part_select_tiles_inplace<kW><<<g, kBlock, 0, stream>>>(a);
+            else if (v == 2) k_part_select_tiles_widest<kW><<<g, kBlock, 0, stream>>>(a);
+            else k_part_select_tiles_widest_inplace<kW><<<g, kBlock, 0, stream>>>(a);
+        }
         timer.end();
     }
     void select_any(const PartArgs& a) {
