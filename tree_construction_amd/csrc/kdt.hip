@@ -345,11 +345,17 @@ struct RecordSource {
     int words;
     i64 n;
     u64 plane;  // words > kWholeWords: distance between the planes of `in`
+    // planar records in index order: the index word of record e is e, not
+    // read (so that the first words-1 planes of a wider copy serve)
+    bool position_index;
 };
 
 template <int kSrc>
 __device__ inline u32 source_word(const RecordSource& s, u64 e, int w) {
-    if (kSrc == kSrcRecords) return s.in[rec_word_index(s.words, s.plane, e, w)];
+    if (kSrc == kSrcRecords) {
+        if (s.position_index && w == s.words - 1) return (u32)e;
+        return s.in[rec_word_index(s.words, s.plane, e, w)];
+    }
     return w < s.words - 1 ? float_key(__float_as_uint(s.pts[e * s.k + w])) : (u32)e;
 }
 
@@ -3445,9 +3451,18 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
     auto recs = [&](int b) { return (u32*)(ws + lay.recs) + (size_t)b * n * W; };
     Launcher launch{(u32*)(ws + lay.slots), (u32*)(ws + lay.chunk_slots), (u32*)(ws + lay.totals),
                     stream, timer};
+    // Record width of A_d. With every dimension split in one round only
+    // (k >= R), A_d is used in round d alone, whose walk compares
+    // coordinates 0 .. d-1 (level m splits m) and whose pivots are keyed by
+    // d: its records carry the keys of 0 .. d and the index. Reused arrays
+    // carry every used coordinate.
+    const bool narrow = k >= R;
+    auto width = [&](int d) { return narrow ? d + 2 : W; };
 
     // Wide records are planar; their first presort pass reads them from an
-    // index-ordered planar copy built here (with the first digits).
+    // index-ordered planar copy of every used key built here (with the first
+    // digits), the index being the position: a narrow array's first d + 1
+    // planes are its keys.
     u32* planar0 = W > kWholeWords ? (u32*)(ws + lay.planar0) : nullptr;
     if (planar0) {
         timer.begin("k_planar_records", (double)n * (4.0 * k + 4.0 * W + lay.kr));
@@ -3479,7 +3494,9 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
             if (b < 0) return KDT_ERR_WORKSPACE;  // cannot happen: nbuf covers the rounds
             for (int p = 0; p < kKeyBytes; ++p) {
                 SortArgs a{};
-                a.src = RecordSource{pts, k, p == 0 ? planar0 : tmp[(p + 1) & 1], W, n, (u64)n};
+                // (records of at most four words are built from the rows)
+                const bool from_planar = p == 0 && planar0 && width(d) > kWholeWords;
+                a.src = RecordSource{pts, k, p == 0 ? planar0 : tmp[(p + 1) & 1], width(d), n, (u64)n, from_planar};
                 a.out = p == kKeyBytes - 1 ? recs(b) : tmp[p & 1];
                 a.dim = d;
                 a.shift = 8 * p;
@@ -3487,7 +3504,7 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
                 a.next_digits = p == kKeyBytes - 1 ? nullptr : digits;
                 a.next_dim = d;
                 a.next_shift = 8 * (p + 1);
-                if (p == 0 && !planar0) launch.sort_any<kSrcRows>(a);
+                if (p == 0 && !from_planar) launch.sort_any<kSrcRows>(a);
                 else launch.sort_any<kSrcRecords>(a);
             }
             holder[b] = d;
@@ -3507,7 +3524,7 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
             const int next_use = l + k;
             if (l1 == l && l != R - 1 && (next_use >= R || next_use - level_of[d] <= kSelectDepth)) {
                 PartArgs a{};
-                a.src = RecordSource{pts, k, recs(buf_of[d]), W, n - (i64)full_nodes(level_of[d]), (u64)n};
+                a.src = RecordSource{pts, k, recs(buf_of[d]), width(d), n - (i64)full_nodes(level_of[d]), (u64)n};
                 a.k = k;
                 a.l0 = level_of[d];
                 a.l1 = l;
@@ -3528,7 +3545,7 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
             const int b = take(buf_of[d]);
             if (b < 0) return KDT_ERR_WORKSPACE;
             PartArgs a{};
-            a.src = RecordSource{pts, k, recs(buf_of[d]), W, n - (i64)full_nodes(level_of[d]), (u64)n};
+            a.src = RecordSource{pts, k, recs(buf_of[d]), width(d), n - (i64)full_nodes(level_of[d]), (u64)n};
             a.out = recs(b);
             a.n_out = n - (i64)full_nodes(l1);
             a.k = k;
@@ -3556,9 +3573,9 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
         // Round l's nodes and their pivots (round 0 has no re-sort to do it).
         if (!pivots_done) {
             const u64 nodes = 1ull << l;
-            timer.begin("k_pivots", (double)nodes * (4.0 * W + 8 + (perm ? 4 : 0) + (tree ? 8.0 * k : 0)));
+            timer.begin("k_pivots", (double)nodes * (4.0 * width(d) + 8 + (perm ? 4 : 0) + (tree ? 8.0 * k : 0)));
             k_pivots<<<(unsigned)((nodes + kBlock - 1) / kBlock), kBlock, 0, stream>>>(
-                recs(buf_of[d]), W, (u64)n, geo, l, d, piv, pts, k, perm, tree, nullptr);
+                recs(buf_of[d]), width(d), (u64)n, geo, l, d, piv, pts, k, perm, tree, nullptr);
             timer.end();
         }
         // A dimension not split on again frees its array (except the last
