@@ -489,7 +489,23 @@ struct RecordTile {
             const v2u v = {w0[j], w1[j]};
             __builtin_nontemporal_store(v, reinterpret_cast<v2u*>(out + pos * 2));
         } else {
-            for (int w = 0; w < s.words; ++w) out[rec_word_index(s.words, s.plane, pos, w)] = source_word<kSrc>(s, (u64)e, w);
+            copy_words(s, out, e, pos);
+        }
+    }
+    // Wide records (kW = 0), from the source word by word: a batch of loads
+    // in flight before their stores (as far as the compiler knows the
+    // source and the output may alias, so a load behind a store would wait
+    // for the one before it).
+    __device__ __forceinline__ static void copy_words(const RecordSource& s, u32* out, i64 e, u64 pos) {
+        constexpr int kBatch = 8;
+        for (int w0 = 0; w0 < s.words; w0 += kBatch) {
+            u32 v[kBatch];
+#pragma unroll
+            for (int g = 0; g < kBatch; ++g)
+                if (w0 + g < s.words) v[g] = source_word<kSrc>(s, (u64)e, w0 + g);
+#pragma unroll
+            for (int g = 0; g < kBatch; ++g)
+                if (w0 + g < s.words) out[rec_word_index(s.words, s.plane, pos, w0 + g)] = v[g];
         }
     }
     // Plain stores: where a wave's stores land in many short runs, the
@@ -1295,6 +1311,16 @@ constexpr u32 kEveryNode = ~0u;
 template <int kW, bool kNodeDims, bool kSelect, bool kInPlace>
 __device__ __forceinline__ void part_tile(const PartArgs& a, u32 t, u32 only) {
     __shared__ u32 count[kWaves][kRadix];  // per-wave digit counts, then first slots
+    // Wide (planar) records of a re-sort are staged in LDS in output order
+    // and written a word plane at a time as the tile's runs: written record
+    // by record, each store of a wave would touch up to 64 lines per plane.
+    constexpr bool kStage = kW == 0 && !kSelect;
+    __shared__ u32 s_words[kStage ? kPartTile : 1];  // one word of each staged record
+    __shared__ u32 s_pos[kStage ? kPartTile : 1];    // its output position (~0: none)
+    __shared__ u32 s_first[kStage ? kRadix : 1];     // tile slot of a digit's first record, less
+                                                     //   the digit's count before the tile
+    __shared__ u32 s_scan[kWaves];
+    __shared__ u32 s_staged;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const i64 wbase = (i64)t * kPartTile + (i64)w * (64 * kPartItems) + lane;
     const int delta = a.l1 - a.l0;
@@ -1315,6 +1341,7 @@ __device__ __forceinline__ void part_tile(const PartArgs& a, u32 t, u32 only) {
         wave_rank(digit, valid, delta, count[w], rank);
     }
     __syncthreads();
+    u32 tile_total = 0;
     if (tid < bins) {
         // points of this digit before the tile, then before each wave
         u32 run = before_tile;
@@ -1324,15 +1351,27 @@ __device__ __forceinline__ void part_tile(const PartArgs& a, u32 t, u32 only) {
             count[v][tid] = run;
             run += c;
         }
+        tile_total = run - before_tile;
+    }
+    if constexpr (kStage) {
+        // (the scan's own barriers also order the counts above)
+        const u32 start = block_exclusive_scan(tile_total, s_scan);
+        if (tid < bins) s_first[tid] = start - before_tile;
+        if (tid == bins - 1) s_staged = start + tile_total;
     }
     __syncthreads();
+    u32 slot[kStage ? kPartItems : 1];
 #pragma unroll
     for (int j = 0; j < kPartItems; ++j) {
         if (!valid[j]) continue;
         const u32 digit = node[j] & (bins - 1);
         const u32 in_segment = count[w][digit] + rank[j] - bin_prefix32(a.s1, node[j] >> delta, digit, delta);
         const i64 e = wbase + (i64)j * 64;
-        if constexpr (!kSelect) {
+        if constexpr (kStage) {
+            const u32 pos = live_begin32(a.s1, node[j]) + in_segment;
+            slot[j] = s_first[digit] + count[w][digit] + rank[j];
+            s_pos[slot[j]] = pos < (u64)a.n_out ? pos : ~0u;
+        } else if constexpr (!kSelect) {
             const u32 pos = live_begin32(a.s1, node[j]) + in_segment;
             if (pos < (u64)a.n_out) {
                 // non-temporal while a wave's records fall in few runs, plain
@@ -1353,6 +1392,20 @@ __device__ __forceinline__ void part_tile(const PartArgs& a, u32 t, u32 only) {
             // (the row from `points`: a key does not keep the sign of zero)
             if (a.tree)
                 for (int d = 0; d < a.k; ++d) a.tree[s * a.k + d] = a.src.pts[(u64)idx * a.k + d];
+        }
+    }
+    if constexpr (kStage) {
+        const u32 staged = s_staged;  // (written before the barrier above)
+        for (int ww = 0; ww < a.src.words; ++ww) {
+            __syncthreads();  // positions written; the previous round's reads done
+#pragma unroll
+            for (int j = 0; j < kPartItems; ++j)
+                if (valid[j]) s_words[slot[j]] = tr.word(a.src, j, wbase + (i64)j * 64, ww);
+            __syncthreads();
+            for (u32 i = tid; i < staged; i += kBlock) {
+                const u32 pos = s_pos[i];
+                if (pos != ~0u) a.out[rec_word_index(a.src.words, a.src.plane, pos, ww)] = s_words[i];
+            }
         }
     }
 }
