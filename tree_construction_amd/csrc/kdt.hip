@@ -871,13 +871,23 @@ __global__ __launch_bounds__(kSortBlock) void k_sort_scatter(SortArgs a) {
             if (a.next_digits) a.next_digits[dst] = (u8)((a.next_dim == 0 ? v.x : v.y) >> a.next_shift);
         }
     } else {
-        // one word of every record per staging round
+        // one word of every record per staging round; wide records (kW = 0)
+        // are read from the source a round ahead, so that the loads of word
+        // ww + 1 are in flight during round ww
         const int words = kW > 0 ? kW : a.src.words;
+        u32 next[kPartItems];
+#pragma unroll
+        for (int j = 0; j < kPartItems; ++j) next[j] = valid[j] ? tr.word(a.src, j, wbase + (i64)j * 64, 0) : 0u;
         for (int ww = 0; ww < words; ++ww) {
             __syncthreads();  // the previous round's reads are done
 #pragma unroll
             for (int j = 0; j < kPartItems; ++j)
-                if (valid[j]) sm.words[rank[j]] = tr.word(a.src, j, wbase + (i64)j * 64, ww);
+                if (valid[j]) sm.words[rank[j]] = next[j];
+            if (ww + 1 < words) {
+#pragma unroll
+                for (int j = 0; j < kPartItems; ++j)
+                    next[j] = valid[j] ? tr.word(a.src, j, wbase + (i64)j * 64, ww + 1) : 0u;
+            }
             __syncthreads();
             for (int i = tid; i < valid_here; i += kSortBlock) {
                 const u32 dst = s_base[s_digit[i]] + (u32)i;
@@ -1396,11 +1406,20 @@ __device__ __forceinline__ void part_tile(const PartArgs& a, u32 t, u32 only) {
     }
     if constexpr (kStage) {
         const u32 staged = s_staged;  // (written before the barrier above)
+        // each word read a round ahead (its loads in flight meanwhile)
+        u32 next[kPartItems];
+#pragma unroll
+        for (int j = 0; j < kPartItems; ++j) next[j] = valid[j] ? tr.word(a.src, j, wbase + (i64)j * 64, 0) : 0u;
         for (int ww = 0; ww < a.src.words; ++ww) {
             __syncthreads();  // positions written; the previous round's reads done
 #pragma unroll
             for (int j = 0; j < kPartItems; ++j)
-                if (valid[j]) s_words[slot[j]] = tr.word(a.src, j, wbase + (i64)j * 64, ww);
+                if (valid[j]) s_words[slot[j]] = next[j];
+            if (ww + 1 < a.src.words) {
+#pragma unroll
+                for (int j = 0; j < kPartItems; ++j)
+                    next[j] = valid[j] ? tr.word(a.src, j, wbase + (i64)j * 64, ww + 1) : 0u;
+            }
             __syncthreads();
             for (u32 i = tid; i < staged; i += kBlock) {
                 const u32 pos = s_pos[i];
