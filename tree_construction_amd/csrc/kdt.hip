@@ -543,14 +543,17 @@ static_assert(kSortBlock >= kRadix, "a presort thread per digit");
 // row's sum (if totals is given). Each thread scans a contiguous run of
 // kScanRun chunks held in registers; longer rows loop over runs.
 constexpr int kScanRun = 16;
-__global__ __launch_bounds__(kBlock) void k_chunk_scan(u32* __restrict__ chunk, i64 chunks,
-                                                       u32* __restrict__ totals) {
-    __shared__ u32 s_wave[kWaves];
+// One workgroup of kThreads scans one row (digit) in runs of
+// kThreads * kScanRun entries.
+template <int kThreads>
+__device__ __forceinline__ void chunk_scan(u32* __restrict__ chunk, i64 chunks, u32* __restrict__ totals) {
+    constexpr int kW = kThreads / 64;
+    __shared__ u32 s_wave[kW];
     __shared__ u32 s_carry;
-    const int tid = threadIdx.x, d = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, d = blockIdx.x;
     u32* row = chunk + (u64)d * chunks;
-    if (tid == kBlock - 1) s_carry = 0;
-    for (i64 t0 = 0; t0 < chunks; t0 += (i64)kBlock * kScanRun) {
+    if (tid == kThreads - 1) s_carry = 0;
+    for (i64 t0 = 0; t0 < chunks; t0 += (i64)kThreads * kScanRun) {
         const i64 mine = t0 + (i64)tid * kScanRun;
         u32 v[kScanRun], sum = 0;
 #pragma unroll
@@ -558,10 +561,17 @@ __global__ __launch_bounds__(kBlock) void k_chunk_scan(u32* __restrict__ chunk, 
             v[i] = mine + i < chunks ? row[mine + i] : 0u;
             sum += v[i];
         }
-        __syncthreads();  // s_carry written
+        __syncthreads();  // s_carry written; s_wave's last readers done
         const u32 carry = s_carry;
-        u32 off = block_exclusive_scan(sum, s_wave) + carry;
-        if (tid == kBlock - 1) s_carry = off + sum;
+        const u32 inc = wave_inclusive_scan(sum);
+        if (lane == 63) s_wave[w] = inc;
+        __syncthreads();
+        u32 off = carry + inc - sum;
+#pragma unroll
+        for (int i = 0; i < kW; ++i)
+            if (i < w) off += s_wave[i];
+        // (every thread read s_carry before the barrier above)
+        if (tid == kThreads - 1) s_carry = off + sum;
 #pragma unroll
         for (int i = 0; i < kScanRun; ++i) {
             if (mine + i < chunks) row[mine + i] = off;
@@ -570,6 +580,17 @@ __global__ __launch_bounds__(kBlock) void k_chunk_scan(u32* __restrict__ chunk, 
     }
     __syncthreads();
     if (totals && tid == 0) totals[d] = s_carry;
+}
+
+__global__ __launch_bounds__(kBlock) void k_chunk_scan(u32* __restrict__ chunk, i64 chunks,
+                                                       u32* __restrict__ totals) {
+    chunk_scan<kBlock>(chunk, chunks, totals);
+}
+// Rows longer than one run of kBlock threads: four times the threads.
+constexpr int kWideScanBlock = 1024;
+__global__ __launch_bounds__(kWideScanBlock) void k_chunk_scan_wide(u32* __restrict__ chunk, i64 chunks,
+                                                                    u32* __restrict__ totals) {
+    chunk_scan<kWideScanBlock>(chunk, chunks, totals);
 }
 
 // Given each wave's digit counts hist[v][d] for the kChunkTiles tiles of a
@@ -3372,6 +3393,15 @@ bool pivots_fit(const PartArgs& a) {
     return segs * ((1ull << (a.l1 - a.l0)) - 1) <= (u64)kPivStage;
 }
 
+// Exclusive scan of each of `rows` rows of `len` counts (and their totals):
+// one workgroup a row, four times wider for rows longer than one run.
+bool wide_scan(i64 len) { return len > (i64)kBlock * kScanRun; }
+const char* scan_name(i64 len) { return wide_scan(len) ? "k_chunk_scan_wide" : "k_chunk_scan"; }
+void scan_rows(u32* counts, int rows, i64 len, u32* totals, hipStream_t stream) {
+    if (wide_scan(len)) k_chunk_scan_wide<<<rows, kWideScanBlock, 0, stream>>>(counts, len, totals);
+    else k_chunk_scan<<<rows, kBlock, 0, stream>>>(counts, len, totals);
+}
+
 struct Launcher {
     u32* tile_counts;
     u32* chunk_counts;
@@ -3393,8 +3423,8 @@ struct Launcher {
         timer.begin("k_sort_count", n + (double)(tiles + chunks) * kRadix * 4);
         k_sort_count<<<(unsigned)chunks, kCountBlock, 0, stream>>>(a);
         timer.end();
-        timer.begin("k_chunk_scan", (double)chunks * kRadix * 8);
-        k_chunk_scan<<<kRadix, kBlock, 0, stream>>>(chunk_counts, (i64)chunks, totals);
+        timer.begin(scan_name((i64)chunks), (double)chunks * kRadix * 8);
+        scan_rows(chunk_counts, kRadix, (i64)chunks, totals, stream);
         timer.end();
         // in: the rows' coordinates (and the implicit index) or the records
         const double in = kSrc == kSrcRows ? rec - 4 : rec;
@@ -3438,8 +3468,8 @@ struct Launcher {
         const bool widest = a.dimtab != nullptr;  // split dimensions from the node table
         const bool in_place = kW > 0 && !pivots_fit(a);
         count<kW>(a, tiles, widest, in_place);
-        timer.begin("k_chunk_scan", (double)tiles * bins * 8);
-        k_chunk_scan<<<bins, kBlock, 0, stream>>>(tile_counts, (i64)tiles, nullptr);
+        timer.begin(scan_name((i64)tiles), (double)tiles * bins * 8);
+        scan_rows(tile_counts, bins, (i64)tiles, nullptr, stream);
         timer.end();
         const int v = (widest ? 2 : 0) + (in_place ? 1 : 0);
         timer.begin(kPartScatterNames[v][width_slot(kW)], (double)(a.src.n + a.n_out) * rec);
@@ -3471,8 +3501,8 @@ struct Launcher {
         const bool widest = a.dimtab != nullptr;  // split dimensions from the node table
         const bool in_place = kW > 0 && !pivots_fit(a);
         count<kW>(a, tiles, widest, in_place);
-        timer.begin("k_chunk_scan", (double)tiles * bins * 8);
-        k_chunk_scan<<<bins, kBlock, 0, stream>>>(tile_counts, (i64)tiles, nullptr);
+        timer.begin(scan_name((i64)tiles), (double)tiles * bins * 8);
+        scan_rows(tile_counts, bins, (i64)tiles, nullptr, stream);
         timer.end();
         // At most one node per two tiles: one workgroup per node (nodes past
         // the last leaf return), each on the tile its search finds. Else one
