@@ -322,6 +322,13 @@ __device__ inline u32 xcd_tile(u32 tiles) {
 
 inline u32 xcd_grid(u64 tiles) { return (u32)((tiles + kXcds - 1) / kXcds * kXcds); }
 
+// The same for block b of a pass whose blocks start at a multiple of kXcds
+// within a batched launch (so that b and blockIdx.x share the XCD).
+__device__ inline u32 xcd_tile_of(u32 b, u32 tiles) {
+    const u32 per = (tiles + kXcds - 1) / kXcds;
+    return (b % kXcds) * per + b / kXcds;
+}
+
 enum Src { kSrcRows = 0, kSrcRecords = 1 };
 
 // Where the records of a pass come from: kSrcRows builds the record of
@@ -546,12 +553,11 @@ constexpr int kScanRun = 16;
 // One workgroup of kThreads scans one row (digit) in runs of
 // kThreads * kScanRun entries.
 template <int kThreads>
-__device__ __forceinline__ void chunk_scan(u32* __restrict__ chunk, i64 chunks, u32* __restrict__ totals) {
+__device__ __forceinline__ void chunk_scan_row(u32* __restrict__ row, i64 chunks, u32* __restrict__ totals, int d) {
     constexpr int kW = kThreads / 64;
     __shared__ u32 s_wave[kW];
     __shared__ u32 s_carry;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, d = blockIdx.x;
-    u32* row = chunk + (u64)d * chunks;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     if (tid == kThreads - 1) s_carry = 0;
     for (i64 t0 = 0; t0 < chunks; t0 += (i64)kThreads * kScanRun) {
         const i64 mine = t0 + (i64)tid * kScanRun;
@@ -580,6 +586,11 @@ __device__ __forceinline__ void chunk_scan(u32* __restrict__ chunk, i64 chunks, 
     }
     __syncthreads();
     if (totals && tid == 0) totals[d] = s_carry;
+}
+
+template <int kThreads>
+__device__ __forceinline__ void chunk_scan(u32* __restrict__ chunk, i64 chunks, u32* __restrict__ totals) {
+    chunk_scan_row<kThreads>(chunk + (u64)blockIdx.x * chunks, chunks, totals, blockIdx.x);
 }
 
 __global__ __launch_bounds__(kBlock) void k_chunk_scan(u32* __restrict__ chunk, i64 chunks,
@@ -1218,9 +1229,8 @@ __device__ __forceinline__ void part_nodes(const PartArgs& a, u32 t,
 // 2^kMaxDescent digits, usually a handful, so every tile is its own chunk:
 // its count of digit d goes straight to row d of the digit-major counts.
 template <int kW, bool kNodeDims, bool kInPlace = false>
-__device__ __forceinline__ void part_count(const PartArgs& a) {
+__device__ __forceinline__ void part_count_tile(const PartArgs& a, u32 t) {
     __shared__ u32 hist[kWaves][kRadix];
-    const u32 t = xcd_tile(a.tiles);
     if (t >= a.tiles) return;
     if constexpr (kNodeDims)
         if (no_nodes_here(a)) return;
@@ -1254,6 +1264,11 @@ __device__ __forceinline__ void part_count(const PartArgs& a) {
         for (int v = 0; v < kWaves; ++v) total += hist[v][tid];
         a.chunk_counts[(u64)tid * a.tiles + t] = total;
     }
+}
+
+template <int kW, bool kNodeDims, bool kInPlace = false>
+__device__ __forceinline__ void part_count(const PartArgs& a) {
+    part_count_tile<kW, kNodeDims, kInPlace>(a, xcd_tile(a.tiles));
 }
 
 // Split dimension l mod k (round-robin trees) / from the node table
@@ -1506,6 +1521,51 @@ __global__ __launch_bounds__(kBlock) void k_part_select_tiles_widest(PartArgs a)
 template <int kW>
 __global__ __launch_bounds__(kBlock) void k_part_select_tiles_widest_inplace(PartArgs a) {
     part_select_tiles<kW, true, true>(a);
+}
+
+// Up to kMaxBatch passes of one split-widest level (one per array) in one
+// launch per kernel: pass i owns blocks [first[i], first[i+1]) of the grid.
+// Count and select kernels are short next to their launch and drain, so a
+// level's passes share them.
+constexpr int kMaxBatch = 4;
+struct PartBatch {
+    PartArgs a[kMaxBatch];
+    u32 first[kMaxBatch + 1];  // first block of each pass (count: multiples of kXcds)
+    u32 rows[kMaxBatch + 1];   // first scan row of each pass (its digits)
+    int count;
+};
+static_assert(sizeof(PartBatch) <= 4096, "a kernel argument");
+
+__device__ __forceinline__ int batch_pass(const u32 (&first)[kMaxBatch + 1], int count, u32& local) {
+    int i = 0;
+    while (i + 1 < count && blockIdx.x >= first[i + 1]) ++i;
+    local = blockIdx.x - first[i];
+    return i;
+}
+
+template <int kW>
+__global__ __launch_bounds__(kBlock) void k_part_count_widest_batch(PartBatch b) {
+    u32 local;
+    const int i = batch_pass(b.first, b.count, local);
+    part_count_tile<kW, true>(b.a[i], xcd_tile_of(local, b.a[i].tiles));
+}
+
+template <int kW>
+__global__ __launch_bounds__(kBlock) void k_part_select_widest_batch(PartBatch b) {
+    u32 local;
+    const int i = batch_pass(b.first, b.count, local);
+    const PartArgs& a = b.a[i];
+    if (full_nodes(a.l1) + local >= (u64)a.geo.n) return;
+    if (a.dimtab[full_nodes(a.l1) + local] != (uint16_t)a.array_dim) return;
+    part_tile<kW, true, true, false>(a, pivot_tile(a, local), local);
+}
+
+// Each pass's digit rows of tile counts, one workgroup a row.
+__global__ __launch_bounds__(kBlock) void k_chunk_scan_batch(PartBatch b) {
+    u32 row;
+    const int i = batch_pass(b.rows, b.count, row);
+    const PartArgs& a = b.a[i];
+    chunk_scan_row<kBlock>(a.chunk_counts + (u64)row * a.tiles, (i64)a.tiles, nullptr, 0);
 }
 
 // Round l's nodes: the pivot of node s = F(l) + j is the record at live
@@ -3379,6 +3439,10 @@ const char* const kPartCountNames[4][4] = KDT_PART_NAMES("count");
 const char* const kPartScatterNames[4][4] = KDT_PART_NAMES("scatter");
 const char* const kPartSelectNames[4][4] = KDT_PART_NAMES("select");
 const char* const kPartSelectTilesNames[4][4] = KDT_PART_NAMES("select_tiles");
+const char* const kPartCountBatchNames[4] = {"k_part_count_widest_batch<0>", "k_part_count_widest_batch<2>",
+                                             "k_part_count_widest_batch<3>", "k_part_count_widest_batch<4>"};
+const char* const kPartSelectBatchNames[4] = {"k_part_select_widest_batch<0>", "k_part_select_widest_batch<2>",
+                                              "k_part_select_widest_batch<3>", "k_part_select_widest_batch<4>"};
 #undef KDT_PART_NAMES
 
 // Whether the pivots of levels l0 .. l1-1 below every tile's level-l0
@@ -3526,6 +3590,68 @@ struct Launcher {
             else k_part_select_tiles_widest_inplace<kW><<<g, kBlock, 0, stream>>>(a);
         }
         timer.end();
+    }
+    // The select passes of one split-widest level, batched (one count, one
+    // scan, one select launch) where every pass stages its pivots, walks at
+    // most 6 levels (64 digit rows each: four passes fill the tile-count
+    // buffer's 256 rows) and has at most one node per two tiles; else one
+    // pass after another.
+    template <int kW>
+    void select_batch(std::vector<PartArgs> v) {
+        bool ok = kW > 0 && v.size() >= 2 && v.size() <= (size_t)kMaxBatch;
+        u64 max_tiles = 0;
+        for (const PartArgs& a : v) {
+            const u64 tiles = (a.src.n + kPartTile - 1) / kPartTile;
+            const u64 level_nodes = 1ull << a.l1, exist = (u64)a.geo.n - full_nodes(a.l1);
+            const u64 nodes = level_nodes < exist ? level_nodes : exist;
+            ok = ok && a.l1 - a.l0 <= 6 && pivots_fit(a) && 2 * nodes <= tiles;
+            max_tiles = tiles > max_tiles ? tiles : max_tiles;
+        }
+        if (!ok) {
+            for (const PartArgs& a : v) select<kW>(a);
+            return;
+        }
+        PartBatch b{};
+        b.count = (int)v.size();
+        u32 nodes_first[kMaxBatch + 1];
+        double count_bytes = 0, scan_bytes = 0, select_bytes = 0;
+        b.first[0] = b.rows[0] = nodes_first[0] = 0;
+        for (int i = 0; i < b.count; ++i) {
+            PartArgs a = v[i];
+            const u64 tiles = (a.src.n + kPartTile - 1) / kPartTile;
+            const u32 bins = 1u << (a.l1 - a.l0);
+            const u64 level_nodes = 1ull << a.l1, exist = (u64)a.geo.n - full_nodes(a.l1);
+            const u64 nodes = level_nodes < exist ? level_nodes : exist;
+            a.tiles = (u32)tiles;
+            a.chunk_counts = tile_counts + (u64)i * 64 * max_tiles;  // this pass's 64 rows
+            b.a[i] = a;
+            b.first[i + 1] = b.first[i] + xcd_grid(tiles);
+            b.rows[i + 1] = b.rows[i] + bins;
+            nodes_first[i + 1] = nodes_first[i] + (u32)nodes;
+            const double rec = 4.0 * a.src.words;
+            count_bytes += (double)a.src.n * rec;
+            scan_bytes += (double)tiles * bins * 8;
+            select_bytes += (double)nodes * kPartTile * rec;
+        }
+        timer.begin(kPartCountBatchNames[width_slot(kW)], count_bytes);
+        k_part_count_widest_batch<kW><<<b.first[b.count], kBlock, 0, stream>>>(b);
+        timer.end();
+        timer.begin("k_chunk_scan_batch", scan_bytes);
+        k_chunk_scan_batch<<<b.rows[b.count], kBlock, 0, stream>>>(b);
+        timer.end();
+        for (int i = 0; i <= b.count; ++i) b.first[i] = nodes_first[i];
+        timer.begin(kPartSelectBatchNames[width_slot(kW)], select_bytes);
+        k_part_select_widest_batch<kW><<<b.first[b.count], kBlock, 0, stream>>>(b);
+        timer.end();
+    }
+    void select_batch_any(const std::vector<PartArgs>& v) {
+        if (v.empty()) return;
+        switch (v[0].src.words) {
+            case 2: select_batch<2>(v); break;
+            case 3: select_batch<3>(v); break;
+            case 4: select_batch<4>(v); break;
+            default: select_batch<0>(v); break;
+        }
     }
     void select_any(const PartArgs& a) {
         switch (a.src.words) {
@@ -3908,6 +4034,7 @@ kdt_status run_widest(const float* pts, i64 n, int k, const WidestLayout& wl, ch
     const u64 tiles = ((u64)n + kPartTile - 1) / kPartTile;
     std::vector<int> level_of(k, 0);
     for (int l = 1; l < lds_from; ++l) {
+        std::vector<PartArgs> selects;  // this level's, launched together after the re-sorts
         for (int d = 0; d < k; ++d) {
             PartArgs a{};
             a.src = RecordSource{pts, k, recs(buffer[d]), W, n - (i64)full_nodes(level_of[d]), (u64)n};
@@ -3933,13 +4060,14 @@ kdt_status run_widest(const float* pts, i64 n, int k, const WidestLayout& wl, ch
             const bool select = unread || ((2ull << l) <= tiles && l + 1 - level_of[d] <= kSelectDepth);
             if (select) {
                 a.level_dims = level_dims;
-                launch.select_any(a);
+                selects.push_back(a);
             } else {
                 launch.part_any(a);
                 std::swap(buffer[d], spare);
                 level_of[d] = l;
             }
         }
+        launch.select_batch_any(selects);
         if (l + 1 < L) level(l + 1);
     }
     if (lds_from < L) {
