@@ -1656,6 +1656,68 @@ __global__ __launch_bounds__(kBlock) void k_box_partial(const float* __restrict_
     }
 }
 
+// The same for k <= 4 and 16-byte-aligned rows, every dimension in one
+// pass: a thread reads four points at a time as kK 16-byte words (float f
+// of the four is coordinate f mod kK of point f / kK).
+template <int kK>
+__global__ __launch_bounds__(kBlock) void k_box_partial4(const float* __restrict__ pts, i64 n, i64 chunk,
+                                                         float* __restrict__ partial) {
+    const i64 c = blockIdx.x, first = c * chunk;  // (chunk is a multiple of 4)
+    const i64 last = first + chunk < n ? first + chunk : n;
+    float lo[kK], hi[kK];
+#pragma unroll
+    for (int d = 0; d < kK; ++d) {
+        lo[d] = __uint_as_float(0x7f800000u);
+        hi[d] = __uint_as_float(0xff800000u);
+    }
+    const float4* quads = reinterpret_cast<const float4*>(pts);
+    for (i64 g = first / 4 + threadIdx.x; g < last / 4; g += kBlock) {
+        float4 w[kK];
+#pragma unroll
+        for (int q = 0; q < kK; ++q) w[q] = quads[g * kK + q];
+#pragma unroll
+        for (int f = 0; f < 4 * kK; ++f) {
+            const float4 v = w[f / 4];
+            const float x = f % 4 == 0 ? v.x : f % 4 == 1 ? v.y : f % 4 == 2 ? v.z : v.w;
+            if (x < lo[f % kK]) lo[f % kK] = x;
+            if (hi[f % kK] < x) hi[f % kK] = x;
+        }
+    }
+    for (i64 i = last / 4 * 4 + threadIdx.x; i < last; i += kBlock)  // the last chunk's tail
+#pragma unroll
+        for (int d = 0; d < kK; ++d) {
+            const float x = pts[i * kK + d];
+            if (x < lo[d]) lo[d] = x;
+            if (hi[d] < x) hi[d] = x;
+        }
+    __shared__ float s_lo[kK][kWaves], s_hi[kK][kWaves];
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int d = 0; d < kK; ++d) {
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const float ol = __shfl_xor(lo[d], o, 64), oh = __shfl_xor(hi[d], o, 64);
+            if (ol < lo[d]) lo[d] = ol;
+            if (hi[d] < oh) hi[d] = oh;
+        }
+        if ((threadIdx.x & 63) == 0) {
+            s_lo[d][w] = lo[d];
+            s_hi[d][w] = hi[d];
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < kK) {
+        const int d = threadIdx.x;
+        float l = s_lo[d][0], h = s_hi[d][0];
+        for (int v = 1; v < kWaves; ++v) {
+            if (s_lo[d][v] < l) l = s_lo[d][v];
+            if (h < s_hi[d][v]) h = s_hi[d][v];
+        }
+        partial[(d * (i64)gridDim.x + c) * 2] = l;
+        partial[(d * (i64)gridDim.x + c) * 2 + 1] = h;
+    }
+}
+
 // The root domain (lo[0..k), hi[0..k)) from the chunks' (grid: k blocks).
 __global__ __launch_bounds__(kBlock) void k_box_final(const float* __restrict__ partial, i64 chunks,
                                                       int k, float* __restrict__ box) {
@@ -3309,7 +3371,7 @@ bool make_layout(i64 n, int k, int rounds, bool stage, Layout* out) {
 // Workspace of a split-widest build: every level is a global round (its
 // nodes' dimensions differ, so no subtree finishes in LDS), every dimension
 // keeps an array, and each node has a domain and a split dimension.
-constexpr i64 kBoxChunk = 1 << 16;  // points per partial bounding box
+constexpr i64 kBoxChunk = 1 << 14;  // points per partial bounding box (a multiple of 4)
 
 struct WidestLayout {
     Layout base;  // rounds = levels; records carry all k coordinates
@@ -3951,9 +4013,14 @@ kdt_status run_widest(const float* pts, i64 n, int k, const WidestLayout& wl, ch
         k_zero<<<1, kBlock, 0, stream>>>(level_dims, kMaxRounds);
         timer.end();
     }
-    timer.begin("k_box_partial", (double)n * 4.0 * k);
-    k_box_partial<<<dim3((unsigned)wl.box_chunks, (unsigned)k), kBlock, 0, stream>>>(pts, n, k, kBoxChunk,
-                                                                                   partial);
+    static const char* const kBoxNames[5] = {"k_box_partial", "k_box_partial4<1>", "k_box_partial4<2>",
+                                             "k_box_partial4<3>", "k_box_partial4<4>"};
+    timer.begin(kBoxNames[first_digits_vec(pts, k) ? k : 0], (double)n * 4.0 * k);
+    if (first_digits_vec(pts, k) && k == 1) k_box_partial4<1><<<(unsigned)wl.box_chunks, kBlock, 0, stream>>>(pts, n, kBoxChunk, partial);
+    else if (first_digits_vec(pts, k) && k == 2) k_box_partial4<2><<<(unsigned)wl.box_chunks, kBlock, 0, stream>>>(pts, n, kBoxChunk, partial);
+    else if (first_digits_vec(pts, k) && k == 3) k_box_partial4<3><<<(unsigned)wl.box_chunks, kBlock, 0, stream>>>(pts, n, kBoxChunk, partial);
+    else if (first_digits_vec(pts, k) && k == 4) k_box_partial4<4><<<(unsigned)wl.box_chunks, kBlock, 0, stream>>>(pts, n, kBoxChunk, partial);
+    else k_box_partial<<<dim3((unsigned)wl.box_chunks, (unsigned)k), kBlock, 0, stream>>>(pts, n, k, kBoxChunk, partial);
     timer.end();
     timer.begin("k_box_final", (double)wl.box_chunks * k * 8.0 + 8.0 * k);
     k_box_final<<<(unsigned)k, kBlock, 0, stream>>>(partial, wl.box_chunks, k, root_box);
