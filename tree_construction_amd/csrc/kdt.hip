@@ -65,7 +65,7 @@ constexpr int kMaxDescent = kRadixBits;    // levels one re-sort pass walks
 #ifndef KDT_SELECT_DEPTH
 #define KDT_SELECT_DEPTH 6
 #endif
-constexpr int kSelectDepth = KDT_SELECT_DEPTH;  // deepest walk a round may leave to the array's next re-sort
+constexpr int kSelectDepth = KDT_SELECT_DEPTH;  // deepest walk a split-widest round may leave to the next pass
 static_assert(kSelectDepth <= kMaxDescent, "one pass per walk");
 #ifndef KDT_PLAIN_DELTA
 #define KDT_PLAIN_DELTA 4
@@ -3748,6 +3748,11 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
     // carry every used coordinate.
     const bool narrow = k >= R;
     auto width = [&](int d) { return narrow ? d + 2 : W; };
+    // Deepest walk a select may leave to the array's next pass: deeper walks
+    // save re-sorts but cost more digits per count and scan, which pays off
+    // with more rounds (measured best on uniform k = 3 builds: 6 up to 13
+    // rounds (2^25 points), 7 at 14, 8 from 15).
+    const int depth = R <= 13 ? 6 : (R == 14 ? 7 : kMaxDescent);
 
     // Wide records are planar; their first presort pass reads them from an
     // index-ordered planar copy of every used key built here (with the first
@@ -3806,13 +3811,13 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
         // only selects the pivots (the array stays where it is) when A_d is
         // not sorted again before the subtree stage, or when its next use
         // can still walk from its current level in one pass of at most
-        // kSelectDepth levels; the last global round always re-sorts (the
+        // `depth` levels; the last global round always re-sorts (the
         // subtree stage reads its array).
         bool pivots_done = false;
         while (level_of[d] < l) {
             const int l1 = level_of[d] + kMaxDescent < l ? level_of[d] + kMaxDescent : l;
             const int next_use = l + k;
-            if (l1 == l && l != R - 1 && (next_use >= R || next_use - level_of[d] <= kSelectDepth)) {
+            if (l1 == l && l != R - 1 && (next_use >= R || next_use - level_of[d] <= depth)) {
                 PartArgs a{};
                 a.src = RecordSource{pts, k, recs(buf_of[d]), width(d), n - (i64)full_nodes(level_of[d]), (u64)n};
                 a.k = k;
