@@ -3819,7 +3819,7 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
             const int next_use = l + k;
             if (l1 == l && l != R - 1 && (next_use >= R || next_use - level_of[d] <= depth)) {
                 PartArgs a{};
-                a.src = RecordSource{pts, k, recs(buf_of[d]), width(d), n - (i64)full_nodes(level_of[d]), (u64)n};
+                a.src = RecordSource{pts, k, recs(buf_of[d]), width(d), n - (i64)full_nodes(level_of[d]), (u64)n, false};
                 a.k = k;
                 a.l0 = level_of[d];
                 a.l1 = l;
@@ -3840,7 +3840,7 @@ kdt_status run_global(const float* pts, i64 n, int k, const Layout& lay, char* w
             const int b = take(buf_of[d]);
             if (b < 0) return KDT_ERR_WORKSPACE;
             PartArgs a{};
-            a.src = RecordSource{pts, k, recs(buf_of[d]), width(d), n - (i64)full_nodes(level_of[d]), (u64)n};
+            a.src = RecordSource{pts, k, recs(buf_of[d]), width(d), n - (i64)full_nodes(level_of[d]), (u64)n, false};
             a.out = recs(b);
             a.n_out = n - (i64)full_nodes(l1);
             a.k = k;
@@ -3945,7 +3945,7 @@ kdt_status run_unique(const float* pts, i64 n, int k, const UniqueLayout& ul, ch
     const u32* sorted = nullptr;
     for (int p = 0; p < kKeyBytes; ++p) {
         SortArgs a{};
-        a.src = RecordSource{pts, k, tmp[(p + 1) & 1], W, n, (u64)n};
+        a.src = RecordSource{pts, k, tmp[(p + 1) & 1], W, n, (u64)n, false};
         a.out = tmp[p & 1];
         a.dim = 0;
         a.shift = 8 * p;
@@ -4076,7 +4076,7 @@ kdt_status run_widest(const float* pts, i64 n, int k, const WidestLayout& wl, ch
     for (int d = 0; d < k; ++d)
         for (int p = 0; p < kKeyBytes; ++p) {
             SortArgs a{};
-            a.src = RecordSource{pts, k, p == 0 ? planar0 : tmp[(p + 1) & 1], W, n, (u64)n};
+            a.src = RecordSource{pts, k, p == 0 ? planar0 : tmp[(p + 1) & 1], W, n, (u64)n, false};
             a.out = p == kKeyBytes - 1 ? recs(d) : tmp[p & 1];
             a.dim = d;
             a.shift = 8 * p;
@@ -4109,7 +4109,7 @@ kdt_status run_widest(const float* pts, i64 n, int k, const WidestLayout& wl, ch
         std::vector<PartArgs> selects;  // this level's, launched together after the re-sorts
         for (int d = 0; d < k; ++d) {
             PartArgs a{};
-            a.src = RecordSource{pts, k, recs(buffer[d]), W, n - (i64)full_nodes(level_of[d]), (u64)n};
+            a.src = RecordSource{pts, k, recs(buffer[d]), W, n - (i64)full_nodes(level_of[d]), (u64)n, false};
             a.out = recs(spare);
             a.n_out = n - (i64)full_nodes(l);
             a.k = k;
@@ -4146,7 +4146,7 @@ kdt_status run_widest(const float* pts, i64 n, int k, const WidestLayout& wl, ch
         // A_0 to level lds_from (no pivots: the subtree stage fixes that
         // level's nodes), so that each subtree's records are one range.
         PartArgs a{};
-        a.src = RecordSource{pts, k, recs(buffer[0]), W, n - (i64)full_nodes(level_of[0]), (u64)n};
+        a.src = RecordSource{pts, k, recs(buffer[0]), W, n - (i64)full_nodes(level_of[0]), (u64)n, false};
         a.out = recs(spare);
         a.n_out = n - (i64)full_nodes(lds_from);
         a.k = k;
