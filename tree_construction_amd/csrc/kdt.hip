@@ -1970,144 +1970,11 @@ constexpr int kLocalWaves = kLocalBlock / 64;
 constexpr int kLocalItems = 8;                        // records per thread
 constexpr int kLocalMax = kLocalBlock * kLocalItems;  // points per subtree
 constexpr int kCachedDims = 3;                        // sorted orders kept in LDS
-constexpr int kRowRegs = 4;                           // row loads batched up to this k
-constexpr int kRowBatch = 4;                          // items whose rows load together
 static_assert(kLocalBlock >= kRadix, "one thread per digit");
-
-struct LocalShared {
-    u32 exch[kLocalMax];                  // record exchange of the radix passes
-    uint16_t count[kLocalWaves][kRadix];  // per-wave digit counters, then prefixes
-    u32 start[kRadix];                    // first slot of each digit
-    u32 wave[kLocalWaves];
-    u64 reduce[2][kLocalWaves];           // AND / OR of the keys, per wave
-    uint16_t tag[kLocalMax];              // local tag of each point (by index rank)
-    uint16_t order[kCachedDims][kLocalMax];  // points sorted by (coordinate, index)
-};
-
-// Key of one coordinate of the point in slot e, from its staged column (or
-// from the exchange buffer, where it was put by slot).
-struct ColumnKey {
-    const u32* col;
-    __device__ u32 operator()(u32 e) const { return col[e]; }
-};
-
-// The tag rounds keep per-wave segment counters in the exchange buffer: at
-// local level t there are 2^t segments, t <= 11 for kLocalMax points, and
-// 8-bit counters for 2048 segments must fit.
-static_assert(kLocalWaves * (kLocalMax / 2) <= sizeof(LocalShared::exch), "round counters");
 
 // Slot of item j of this thread: each wave owns kLocalItems rows of 64.
 __device__ inline int local_slot(int j) {
     return (threadIdx.x >> 6) * (64 * kLocalItems) + j * 64 + (threadIdx.x & 63);
-}
-
-// Mask of key bits on which the records (all of the workgroup's valid
-// ones) disagree; a radix pass over a byte outside it would not move
-// anything and is skipped.
-__device__ u64 local_varying_bits(const u64 (&rec)[kLocalItems], u32 nc, LocalShared& sh) {
-    u64 all_and = ~0ull, all_or = 0;
-#pragma unroll
-    for (int j = 0; j < kLocalItems; ++j)
-        if ((u32)local_slot(j) < nc) {
-            all_and &= rec[j];
-            all_or |= rec[j];
-        }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        all_and &= __shfl_xor(all_and, o, 64);
-        all_or |= __shfl_xor(all_or, o, 64);
-    }
-    const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) {
-        sh.reduce[0][w] = all_and;
-        sh.reduce[1][w] = all_or;
-    }
-    __syncthreads();
-    u64 a = ~0ull, b = 0;
-#pragma unroll
-    for (int v = 0; v < kLocalWaves; ++v) {
-        a &= sh.reduce[0][v];
-        b |= sh.reduce[1][v];
-    }
-    __syncthreads();
-    return a ^ b;
-}
-
-// One stable pass over all kLocalMax records of the workgroup by the 8-bit
-// digit at `shift`. Unused slots hold all-ones records: they sit at the end
-// and keep digit 255, so they stay behind every real record.
-__device__ void local_pass(u64 (&rec)[kLocalItems], int shift, LocalShared& sh) {
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    for (int i = lane; i < kRadix; i += 64) sh.count[w][i] = 0;
-    const u64 below = (1ull << lane) - 1;
-    // Rank inside the wave: lanes holding the same digit are found with eight
-    // ballots; the lowest such lane bumps the wave's counter for the digit.
-    u32 rank[kLocalItems];
-#pragma unroll
-    for (int j = 0; j < kLocalItems; ++j) {
-        const u32 d = (u32)(rec[j] >> shift) & (kRadix - 1);
-        u32 miss_lo = 0, miss_hi = 0;
-#pragma unroll
-        for (int b = 0; b < kRadixBits; ++b) match_bit(d, b, miss_lo, miss_hi);
-        const u64 peers = ~(((u64)miss_hi << 32) | miss_lo);
-        const u32 before = __popcll(peers & below);
-        const u32 seen = sh.count[w][d];
-        rank[j] = seen + before;
-        if (before == 0) sh.count[w][d] = seen + (u32)__popcll(peers);
-    }
-    __syncthreads();
-    u32 agg = 0;
-    if (tid < kRadix) {
-#pragma unroll
-        for (int v = 0; v < kLocalWaves; ++v) {
-            const u32 c = sh.count[v][tid];
-            sh.count[v][tid] = agg;
-            agg += c;
-        }
-    }
-    // Exclusive scan of the digit totals (threads >= kRadix contribute 0).
-    const u32 inc = wave_inclusive_scan(agg);
-    if (lane == 63) sh.wave[w] = inc;
-    __syncthreads();
-    if (tid < kRadix) {
-        u32 off = 0;
-#pragma unroll
-        for (int i = 0; i < kLocalWaves; ++i)
-            if (i < w) off += sh.wave[i];
-        sh.start[tid] = off + inc - agg;
-    }
-    __syncthreads();
-    // A record is a 32-bit key above a 16-bit slot (bits 16..47; all-ones
-    // records read back as 48 one bits, still behind every real record): it
-    // moves in two exchanges, which keeps the buffer at 4 bytes a record.
-#pragma unroll
-    for (int j = 0; j < kLocalItems; ++j) {
-        const u32 d = (u32)(rec[j] >> shift) & (kRadix - 1);
-        rank[j] += sh.start[d] + sh.count[w][d];
-        sh.exch[rank[j]] = (u32)(rec[j] >> 16);
-    }
-    __syncthreads();
-    u32 hi[kLocalItems];
-#pragma unroll
-    for (int j = 0; j < kLocalItems; ++j) hi[j] = sh.exch[local_slot(j)];
-    __syncthreads();
-    uint16_t* exch16 = reinterpret_cast<uint16_t*>(sh.exch);
-#pragma unroll
-    for (int j = 0; j < kLocalItems; ++j) exch16[rank[j]] = (uint16_t)rec[j];
-    __syncthreads();
-    // The next pass's first barrier orders these reads before its writes.
-#pragma unroll
-    for (int j = 0; j < kLocalItems; ++j) rec[j] = ((u64)hi[j] << 16) | exch16[local_slot(j)];
-}
-
-// Stable sort of the records by bits [lo, lo + 8*bytes), skipping bytes on
-// which every valid record agrees.
-__device__ void local_sort(u64 (&rec)[kLocalItems], int lo, int bytes, u32 nc, LocalShared& sh) {
-    const u64 vary = local_varying_bits(rec, nc, sh);
-    for (int b = 0; b < bytes; ++b) {
-        const int shift = lo + 8 * b;
-        if ((vary >> shift) & (kRadix - 1)) local_pass(rec, shift, sh);
-    }
 }
 
 struct SubtreeArgs {
@@ -2119,292 +1986,15 @@ struct SubtreeArgs {
     const u32* recs;        // l0 > 0: records (coordinates 0 .. words-2, then the
     int words;              // index) live on level l0-1, in round l0-1's order
     u64 plane;              // their plane stride (records wider than kWholeWords)
-    int index_bytes;        // bytes of a point index that can differ
     u32* stage;             // (k+1) x n words: index, then coordinate key columns; the
                             // subtree owns [first, first + |S(c)|) of each
     int32_t* perm;
     float* tree;
 };
 
-// order[q] = slot (index rank) of the q-th point of the subtree by
-// (coordinate dim, original index): stable sort by the coordinate key,
-// starting from index order.
-template <typename KeyOf>
-__device__ __forceinline__ void local_order(KeyOf key_of, u32 nc, uint16_t* order, LocalShared& sh) {
-    u64 rec[kLocalItems];
-#pragma unroll
-    for (int j = 0; j < kLocalItems; ++j) {
-        const int e = local_slot(j);
-        rec[j] = ~0ull;
-        if ((u32)e < nc) rec[j] = ((u64)key_of((u32)e) << 16) | (u32)e;
-    }
-    local_sort(rec, 16, kKeyBytes, nc, sh);
-#pragma unroll
-    for (int j = 0; j < kLocalItems; ++j) {
-        const int q = local_slot(j);
-        if ((u32)q < nc) order[q] = (uint16_t)(rec[j] & 0xffff);
-    }
-    __syncthreads();
-}
-
-// Round t sorts every segment's points by (tag, coordinate, index) and
-// moves each point to the child its sorted position falls in. Segment s
-// starts at a closed-form position, so a point's sorted position is that
-// start plus its rank among the points of s earlier in the (coordinate,
-// index) order; that rank is all the round needs, and no record has to
-// move. It is counted per wave over the 2^t live segments (ballot match on
-// s - F(t)), then prefixed across waves. Count is the counter type: a
-// segment on local level t of a subtree of at most kLocalMax points holds at
-// most 2^(levels-t) - 1 points, so 8-bit counters would suffice wherever
-// 16-bit ones no longer fit the exchange buffer (with 4096-point subtrees
-// 16-bit ones always fit).
-template <typename Count, bool kFilter = false>
-__device__ __forceinline__ void local_round(const uint16_t* order, u32 nc, int t, const Geometry& lg,
-                                            LocalShared& sh, const uint8_t* nodedim = nullptr, int dim = 0) {
-    Count* seg_count = reinterpret_cast<Count*>(sh.exch);  // [kLocalWaves][2^t]
-    const u32 fl = (u32)full_nodes(t);
-    const int segs = 1 << t;
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    // Counters are cleared and prefixed a word (4 / sizeof(Count) of them) at
-    // a time where a wave's row is whole words.
-    u32* words = reinterpret_cast<u32*>(sh.exch);
-    const int row_words = segs * (int)sizeof(Count) / 4;
-    const bool packed = segs * (int)sizeof(Count) % 4 == 0;
-    if (packed)
-        for (int i = threadIdx.x; i < kLocalWaves * row_words; i += kLocalBlock) words[i] = 0;
-    else
-        for (int i = threadIdx.x; i < kLocalWaves * segs; i += kLocalBlock) seg_count[i] = 0;
-    __syncthreads();
-    const u64 below = (1ull << lane) - 1;
-    u32 seg[kLocalItems], rank[kLocalItems];
-    bool alive[kLocalItems];
-#pragma unroll
-    for (int j = 0; j < kLocalItems; ++j) {
-        const u32 q = (u32)local_slot(j);
-        u32 st = fl;  // fixed points (tags < F(t)) are not ranked
-        if (q < nc) st = sh.tag[order[q]];
-        bool live = st >= fl && q < nc;
-        // kFilter: only the segments whose node splits `dim` (the others
-        // are ranked in their own dimension's order; points that an earlier
-        // sub-round of this level moved to a child are on level t+1)
-        if constexpr (kFilter) live = live && st < fl + (u32)segs && nodedim[st] == (uint8_t)dim;
-        alive[j] = live;
-        const u32 b = live ? st - fl : 0;
-        seg[j] = st;
-        u32 miss_lo = 0, miss_hi = 0;
-        for (int bit = 0; bit < t; ++bit) match_bit(b, bit, miss_lo, miss_hi);
-        const u64 peers = __ballot(live) & ~(((u64)miss_hi << 32) | miss_lo);
-        const u32 before = __popcll(peers & below);
-        u32 seen = 0;
-        if (live) seen = seg_count[w * segs + b];
-        rank[j] = seen + before;
-        if (live && before == 0) seg_count[w * segs + b] = (Count)(seen + __popcll(peers));
-    }
-    __syncthreads();
-    if (packed) {
-        // Packed sums do not carry between counters: a segment's total is
-        // below 2^(8 sizeof(Count)) (16-bit: at most kLocalMax points; 8-bit
-        // counters are only used where segments hold at most 3).
-        for (int i = threadIdx.x; i < row_words; i += kLocalBlock) {
-            u32 run = 0;
-            for (int v = 0; v < kLocalWaves; ++v) {
-                const u32 c = words[v * row_words + i];
-                words[v * row_words + i] = run;
-                run += c;
-            }
-        }
-    } else {
-        for (int b = threadIdx.x; b < segs; b += kLocalBlock) {
-            u32 run = 0;
-            for (int v = 0; v < kLocalWaves; ++v) {
-                const u32 c = seg_count[v * segs + b];
-                seg_count[v * segs + b] = (Count)run;
-                run += c;
-            }
-        }
-    }
-    __syncthreads();
-    // A point's sorted position is its segment's start plus its rank among
-    // the segment's points (the counts of earlier waves plus its rank in its
-    // wave), and the pivot's is the start plus |S(2s+1)|: only the rank and
-    // the left subtree's size need comparing. The left child of s = F(t) + b
-    // is the node with in-level index 2b on level t+1, whose subtree holds
-    // u - 1 full-level nodes and min(max(M - 2b u, 0), u) last-level ones
-    // (u = 2^(L-2-t), M = last-level nodes of the subtree's own tree).
-    const u32 dd = (u32)(lg.levels - 2 - t);  // t <= L-2
-    const u32 u = 1u << dd, last = (u32)lg.last;
-#pragma unroll
-    for (int j = 0; j < kLocalItems; ++j) {
-        const u32 q = (u32)local_slot(j);
-        const u32 s = seg[j];
-        if (!alive[j]) continue;
-        const u32 b = s - fl;
-        const u32 in_segment = seg_count[w * segs + b] + rank[j];
-        const u32 under = (2 * b) << dd;
-        const u32 left = (u - 1) + (last > under ? (last - under < u ? last - under : u) : 0u);
-        sh.tag[order[q]] = (uint16_t)(in_segment < left ? 2 * s + 1 : (in_segment > left ? 2 * s + 2 : s));
-    }
-    __syncthreads();
-}
-
-// The subtree stage when the records do not carry every coordinate (k >
-// kCachedDims), or when the whole tree is one subtree read from the rows
-// (l0 = 0): each point's index and coordinate keys are staged once, by index
-// rank, as columns of the workspace, and the orders are sorted from there.
-__global__ __launch_bounds__(kLocalBlock, 4) void k_subtree(SubtreeArgs a) {
-    __shared__ LocalShared sh;
-
-    const u64 c = full_nodes(a.l0) + blockIdx.x;  // subtree root (global node id)
-    const u32 nc = (u32)subtree_size(a.geo, c);
-    if (nc == 0) return;
-    u64 first = 0;  // live position of the subtree's first point in round l0-1's order
-    if (a.l0 > 0) {
-        const u64 parent = (c - 1) / 2;
-        const u64 seg = live_begin(a.geo, parent - full_nodes(a.l0 - 1), a.l0 - 1);
-        const u64 pivot = seg + subtree_size(a.geo, 2 * parent + 1);
-        first = (c == 2 * parent + 1) ? seg : pivot + 1;
-    }
-    // Word f of the record that arrived at position q.
-    auto rec = [&](u32 q, int f) -> u32 { return a.recs[rec_word_index(a.words, a.plane, first + q, f)]; };
-    // Key of coordinate d of the point with index i that arrived at
-    // position q: from its record while the record carries it, else from
-    // its row of `points`.
-    const int kr = a.recs ? a.words - 1 : 0;
-    auto coord = [&](u32 q, u32 i, int d) -> u32 {
-        return d < kr ? rec(q, d) : float_key(__float_as_uint(a.pts[(i64)i * a.k + d]));
-    };
-
-    // Order the subtree's points by original index: slot e = index rank.
-    u64 rec_idx[kLocalItems];
-#pragma unroll
-    for (int j = 0; j < kLocalItems; ++j) {
-        const int q = local_slot(j);
-        rec_idx[j] = ~0ull;
-        if ((u32)q < nc) {
-            const u32 i = a.recs ? rec(q, a.words - 1) : (u32)q;
-            rec_idx[j] = ((u64)i << 16) | (u32)q;
-        }
-    }
-    if (a.recs) local_sort(rec_idx, 16, a.index_bytes, nc, sh);
-    // Stage the subtree's points once, by index rank: their indices and their
-    // coordinate columns (each point is read exactly once here).
-    u32* stage_idx = a.stage + first;
-    if (a.k <= kRowRegs) {
-        // Row loads are issued kRowBatch items at a time, before their stores.
-#pragma unroll
-        for (int j0 = 0; j0 < kLocalItems; j0 += kRowBatch) {
-            u32 row[kRowBatch][kRowRegs];
-#pragma unroll
-            for (int j = 0; j < kRowBatch; ++j) {
-                const u32 i = (u32)(rec_idx[j0 + j] >> 16), q = (u32)(rec_idx[j0 + j] & 0xffff);
-                const bool ok = (u32)local_slot(j0 + j) < nc;
-#pragma unroll
-                for (int d = 0; d < kRowRegs; ++d) row[j][d] = ok && d < a.k ? coord(q, i, d) : 0u;
-            }
-#pragma unroll
-            for (int j = 0; j < kRowBatch; ++j) {
-                const int e = local_slot(j0 + j);
-                if ((u32)e >= nc) continue;
-                stage_idx[e] = (u32)(rec_idx[j0 + j] >> 16);
-#pragma unroll
-                for (int d = 0; d < kRowRegs; ++d)
-                    if (d < a.k) a.stage[(u64)(d + 1) * a.n + first + e] = row[j][d];
-                sh.tag[e] = 0;
-            }
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < kLocalItems; ++j) {
-            const int e = local_slot(j);
-            if ((u32)e >= nc) continue;
-            const u32 i = (u32)(rec_idx[j] >> 16), q = (u32)(rec_idx[j] & 0xffff);
-            stage_idx[e] = i;
-            for (int d = 0; d < a.k; ++d) a.stage[(u64)(d + 1) * a.n + first + e] = coord(q, i, d);
-            sh.tag[e] = 0;
-        }
-    }
-    auto column = [&](int d) { return ColumnKey{a.stage + (u64)(d + 1) * a.n + first}; };
-
-    const Geometry lg = make_geometry((i64)nc);
-    const int rounds = lg.levels - 1;
-    const bool cached = a.k <= kCachedDims;
-    // The points arrived in round l0-1's sorted order, i.e. ordered by
-    // (coordinate (l0-1) mod k, index): that is already the subtree's order
-    // for that dimension (slot of the arrival position q = rec_idx's low bits).
-    const int arrived_dim = a.recs ? (a.l0 - 1) % a.k : -1;
-    uint16_t* arrived = a.recs ? sh.order[cached ? a.k - 1 : 1] : nullptr;
-    if (arrived) {
-#pragma unroll
-        for (int j = 0; j < kLocalItems; ++j) {
-            const int e = local_slot(j);
-            if ((u32)e < nc) arrived[rec_idx[j] & 0xffff] = (uint16_t)e;
-        }
-    }
-    if (cached)
-        for (int u = 0; u < a.k && u < rounds; ++u) {
-            const int d = (a.l0 + u) % a.k;
-            if (d == arrived_dim) continue;
-            local_order(column(d), nc, sh.order[u], sh);
-        }
-    __syncthreads();
-
-    for (int t = 0; t < rounds; ++t) {
-        uint16_t* order = sh.order[cached ? t % a.k : 0];
-        if (!cached) {
-            if ((a.l0 + t) % a.k == arrived_dim) order = arrived;
-            else local_order(column((a.l0 + t) % a.k), nc, order, sh);
-        }
-        // Counters live in the exchange buffer: 16-bit while they fit, else
-        // 8-bit (then segments hold at most 3 points, see below).
-        if ((size_t)kLocalWaves * ((size_t)2 << t) <= sizeof(sh.exch))
-            local_round<uint16_t>(order, nc, t, lg, sh);
-        else
-            local_round<uint8_t>(order, nc, t, lg, sh);
-    }
-
-    // Level-order output of the subtree, in node order: the nodes of each
-    // local level are one contiguous range of global ids, so the writes of
-    // consecutive threads are contiguous.
-    uint16_t* slot_of = sh.order[0];  // the orders are no longer needed
-#pragma unroll
-    for (int j = 0; j < kLocalItems; ++j) {
-        const int e = local_slot(j);
-        if ((u32)e < nc) slot_of[sh.tag[e]] = (uint16_t)e;
-    }
-    __syncthreads();
-    for (u32 node = threadIdx.x; node < nc; node += kLocalBlock) {
-        const u32 e = slot_of[node];
-        const int lvl = level_of(node);
-        const u64 g = ((c + 1) << lvl) - 1 + (node - full_nodes(lvl));
-        if (g >= (u64)a.n) continue;  // cannot happen: local nodes map inside the tree
-        const u32 idx = stage_idx[e];
-        a.perm[g] = (int32_t)idx;
-        if (!a.tree) continue;
-        // Coordinates from their keys; a zero key (both zeros have it) is
-        // read back from the row, which keeps the sign of zero.
-        if (a.k <= kRowRegs) {
-            u32 row[kRowRegs];
-#pragma unroll
-            for (int d = 0; d < kRowRegs; ++d)
-                row[d] = d < a.k ? a.stage[(u64)(d + 1) * a.n + first + e] : 0u;
-#pragma unroll
-            for (int d = 0; d < kRowRegs; ++d) {
-                if (d >= a.k) continue;
-                const float v = row[d] == 0x80000000u ? a.pts[(i64)idx * a.k + d] : __uint_as_float(key_bits(row[d]));
-                a.tree[(i64)g * a.k + d] = v;
-            }
-        } else {
-            for (int d = 0; d < a.k; ++d) {
-                const u32 key = a.stage[(u64)(d + 1) * a.n + first + e];
-                a.tree[(i64)g * a.k + d] = key == 0x80000000u ? a.pts[(i64)idx * a.k + d] : __uint_as_float(key_bits(key));
-            }
-        }
-    }
-}
-
 // ------------------------- subtree stage from records with every coordinate
 // The subtree stage for k <= kCachedDims, where the records of the last
-// global round carry all k coordinate keys: the same rounds as k_subtree,
+// global round carry all k coordinate keys: the same rounds as k_subtree_cols,
 // organised so that each record is read once as one vector, and every radix
 // pass in LDS moves one 32-bit word per point. A pass sorts a value stably:
 // the value less its minimum over the subtree, so that only the bits in which
@@ -2463,10 +2053,12 @@ __device__ __forceinline__ void peer_mask(u32 d, int bits, u32 within_lo, u32 wi
 // One stable pass by the low `bits` bits of each item's unsorted value.
 // Wide form: hi = the value, lo = the payload. Narrow form: hi = value << kPay
 // | payload. The pass drops the sorted bits; kWideOut keeps the wide form
-// (the rest does not fit 32 - kPay bits yet).
-template <bool kWideIn, bool kWideOut>
-__device__ __forceinline__ void rec_pass(u32 (&hi)[kLocalItems], u32 (&lo)[kLocalItems], int bits,
-                                         RecScratch& s) {
+// (the rest does not fit 32 - kPay bits yet), its payloads exchanged through
+// pay_x (kLocalMax 16-bit entries). S is the scratch type (RecScratch or
+// ColScratch): only its first exchange buffer is used.
+template <bool kWideIn, bool kWideOut, typename S>
+__device__ __forceinline__ void rec_pass(u32 (&hi)[kLocalItems], u32 (&lo)[kLocalItems], int bits, S& s,
+                                         uint16_t* pay_x) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const u32 bins = 1u << bits;
     uint16_t* cnt = s.count[w];
@@ -2517,7 +2109,7 @@ __device__ __forceinline__ void rec_pass(u32 (&hi)[kLocalItems], u32 (&lo)[kLoca
         const u32 pos = rank[j];
         if constexpr (kWideOut) {
             s.exch[0][pos] = hi[j] >> bits;
-            s.exch[1][pos] = lo[j];
+            pay_x[pos] = (uint16_t)lo[j];
         } else {
             const u32 rest = kWideIn ? hi[j] >> bits : hi[j] >> (kPay + bits);
             const u32 pay = kWideIn ? lo[j] : hi[j] & ((1u << kPay) - 1);
@@ -2530,15 +2122,17 @@ __device__ __forceinline__ void rec_pass(u32 (&hi)[kLocalItems], u32 (&lo)[kLoca
     for (int j = 0; j < kLocalItems; ++j) {
         const int q = local_slot(j);
         hi[j] = s.exch[0][q];
-        if constexpr (kWideOut) lo[j] = s.exch[1][q];
+        if constexpr (kWideOut) lo[j] = pay_x[q];
     }
 }
 
-// Stable sort of the items (value v[j] below 2^vbits, payload pay[j]) from
-// their current order; returns with pay[j] = the payload of the item at
-// position local_slot(j). vbits = 0: nothing to sort.
-__device__ __forceinline__ void rec_sort(u32 (&v)[kLocalItems], u32 (&pay)[kLocalItems], int vbits,
-                                         RecScratch& s) {
+// Stable sort of the items (value v[j] below 2^vbits, payload pay[j] below
+// 2^kPay) from their current order; returns with pay[j] = the payload of the
+// item at position local_slot(j). vbits = 0: nothing to sort. pay_x as in
+// rec_pass (RecScratch: its second exchange buffer).
+template <typename S>
+__device__ __forceinline__ void rec_sort(u32 (&v)[kLocalItems], u32 (&pay)[kLocalItems], int vbits, S& s,
+                                         uint16_t* pay_x) {
     if (vbits == 0) return;
     const int passes = (vbits + kRadixBits - 1) / kRadixBits;
     int left = vbits;
@@ -2546,9 +2140,9 @@ __device__ __forceinline__ void rec_sort(u32 (&v)[kLocalItems], u32 (&pay)[kLoca
     for (int p = 0; p < passes; ++p) {
         const int bits = (left + (passes - p) - 1) / (passes - p);
         const bool out_wide = left - bits > 32 - kPay;
-        if (wide && out_wide) rec_pass<true, true>(v, pay, bits, s);
-        else if (wide) rec_pass<true, false>(v, pay, bits, s);
-        else rec_pass<false, false>(v, pay, bits, s);
+        if (wide && out_wide) rec_pass<true, true>(v, pay, bits, s, pay_x);
+        else if (wide) rec_pass<true, false>(v, pay, bits, s, pay_x);
+        else rec_pass<false, false>(v, pay, bits, s, pay_x);
         wide = out_wide;
         left -= bits;
     }
@@ -2556,9 +2150,14 @@ __device__ __forceinline__ void rec_sort(u32 (&v)[kLocalItems], u32 (&pay)[kLoca
     for (int j = 0; j < kLocalItems; ++j) pay[j] = v[j] & ((1u << kPay) - 1);
 }
 
+__device__ __forceinline__ void rec_sort(u32 (&v)[kLocalItems], u32 (&pay)[kLocalItems], int vbits,
+                                         RecScratch& s) {
+    rec_sort(v, pay, vbits, s, reinterpret_cast<uint16_t*>(&s.exch[1][0]));
+}
+
 // Workgroup minimum and maximum of each of kV values, from each thread's own.
-template <int kV>
-__device__ __forceinline__ void rec_min_max(u32 (&mn)[kV], u32 (&mx)[kV], RecScratch& s) {
+template <int kV, typename S>
+__device__ __forceinline__ void rec_min_max(u32 (&mn)[kV], u32 (&mx)[kV], S& s) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < kV; ++i) {
@@ -2592,19 +2191,26 @@ __device__ __forceinline__ void rec_min_max(u32 (&mn)[kV], u32 (&mx)[kV], RecScr
 // Bits that values 0 .. span (and the padding value above them) need.
 __device__ __forceinline__ int value_bits(u32 span) { return span == ~0u ? 32 : 32 - __clz(span + 1); }
 
-// Round t in LDS, as local_round, over a subtree whose padding slots carry
-// kPadTag: per-wave counters of the 2^t segments live in the exchange
-// buffers (16-bit, 8 x 2048 at most); items that are not live count into a
-// dummy and write their tag back unchanged. With nodedim (split-widest
-// trees), only the segments whose node splits dimension d are live.
-__device__ __forceinline__ void rec_round(const uint16_t* order, int t, const Geometry& lg, RecShared& sh,
-                                          const uint8_t* nodedim = nullptr, u32 d = 0) {
-    RecScratch& s = sh.m.s;
+// Round t in LDS. A segment's sorted position is its closed-form start plus
+// a point's rank among the segment's points earlier in `order` (slots by
+// (coordinate, index)); that rank is all the round needs, so no record
+// moves. It is counted per wave by ballots over the 2^t live segments, then
+// prefixed across waves, and compared with the left subtree's size: below,
+// the point goes to the left child, above to the right one, equal it is the
+// node. Padding slots carry kPadTag: per-wave counters of the 2^t segments live in the exchange
+// buffers from the first on (Count: 16-bit, 8 x 2048 of them spanning both
+// of RecScratch's; 8-bit where a segment holds at most 255 points); items
+// that are not live count into a dummy and write their tag back unchanged.
+// With nodedim (split-widest trees), only the segments whose node splits
+// dimension d are live.
+template <typename Count = uint16_t, typename S>
+__device__ __forceinline__ void rec_round(const uint16_t* order, int t, const Geometry& lg, uint16_t* tag,
+                                          S& s, const uint8_t* nodedim = nullptr, u32 d = 0) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const u32 fl = (1u << t) - 1, segs = 1u << t;
-    uint16_t* cnt = reinterpret_cast<uint16_t*>(&s.exch[0][0]);  // [kLocalWaves][segs]
+    Count* cnt = reinterpret_cast<Count*>(&s.exch[0][0]);  // [kLocalWaves][segs]
     u32* cnt_words = &s.exch[0][0];
-    const u32 words = (kLocalWaves * segs + 1) / 2;
+    const u32 words = (kLocalWaves * segs * (u32)sizeof(Count) + 3) / 4;
     for (u32 i = tid; i < words; i += kLocalBlock) cnt_words[i] = 0;
     __syncthreads();
     // Every item's slot and tag first: reads issued back to back (the
@@ -2614,7 +2220,7 @@ __device__ __forceinline__ void rec_round(const uint16_t* order, int t, const Ge
 #pragma unroll
     for (int j = 0; j < kLocalItems; ++j) e[j] = order[local_slot(j)];
 #pragma unroll
-    for (int j = 0; j < kLocalItems; ++j) st[j] = sh.m.tag[e[j]];
+    for (int j = 0; j < kLocalItems; ++j) st[j] = tag[e[j]];
     // (a padding tag is never below fl + segs, so nodedim is read in range)
     bool on[kLocalItems];
 #pragma unroll
@@ -2630,16 +2236,16 @@ __device__ __forceinline__ void rec_round(const uint16_t* order, int t, const Ge
         u32 p_lo, p_hi;
         peer_mask(b, t, (u32)lv, (u32)(lv >> 32), p_lo, p_hi);
         const u32 before = lanes_below(p_lo, p_hi);
-        uint16_t* cp = live ? &cnt[w * segs + b] : &s.dummy[lane];
+        Count* cp = live ? &cnt[w * segs + b] : reinterpret_cast<Count*>(s.dummy) + lane;
         const u32 seen = *cp;
         rank[j] = seen + before;
-        *cp = (uint16_t)(seen + __popc(p_lo) + __popc(p_hi));
+        *cp = (Count)(seen + __popc(p_lo) + __popc(p_hi));
     }
     __syncthreads();
-    // prefix over the waves, two 16-bit counters a word (a segment's total
-    // is at most kLocalMax, so the halves never carry into each other)
-    if (segs >= 2) {
-        const u32 row = segs / 2;
+    // prefix over the waves, a word of counters at a time (a segment's total
+    // fits its counter, so the counters of a word never carry into each other)
+    if (segs * sizeof(Count) >= 4) {
+        const u32 row = segs * (u32)sizeof(Count) / 4;
         for (u32 i = tid; i < row; i += kLocalBlock) {
             u32 run = 0;
 #pragma unroll
@@ -2649,12 +2255,12 @@ __device__ __forceinline__ void rec_round(const uint16_t* order, int t, const Ge
                 run += c;
             }
         }
-    } else if (tid == 0) {
+    } else if ((u32)tid < segs) {
         u32 run = 0;
 #pragma unroll
         for (int v = 0; v < kLocalWaves; ++v) {
-            const u32 c = cnt[v];
-            cnt[v] = (uint16_t)run;
+            const u32 c = cnt[v * segs + tid];
+            cnt[v * segs + tid] = (Count)run;
             run += c;
         }
     }
@@ -2675,7 +2281,7 @@ __device__ __forceinline__ void rec_round(const uint16_t* order, int t, const Ge
         const u32 under = (2 * b) << dd;
         const u32 left = (u - 1) + (last > under ? (last - under < u ? last - under : u) : 0u);
         const u32 next = in_seg < left ? 2 * st[j] + 1 : (in_seg > left ? 2 * st[j] + 2 : st[j]);
-        sh.m.tag[e[j]] = (uint16_t)(live ? next : st[j]);
+        tag[e[j]] = (uint16_t)(live ? next : st[j]);
     }
     __syncthreads();
 }
@@ -2820,7 +2426,7 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_recs(SubtreeArgs a) 
     const Geometry lg = make_geometry((i64)nc);
     const int rounds = lg.levels - 1;
     // round t splits dimension (l0 + t) mod k, whose role is (t + 1) mod k
-    for (int t = 0; t < rounds; ++t) rec_round(sh.m.order[(t + 1) % kK], t, lg, sh);
+    for (int t = 0; t < rounds; ++t) rec_round(sh.m.order[(t + 1) % kK], t, lg, sh.m.tag, s);
 
     // Level-order output: each point's record (read again, one vector) goes
     // to its node's row in LDS; the nodes of a local level are one
@@ -2863,6 +2469,192 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_recs(SubtreeArgs a) 
             const float x = key == 0x80000000u ? a.pts[(u64)word_of(n, kK) * kK + dim]
                                                : __uint_as_float(key_bits(key));
             a.tree[g * kK + dim] = x;
+        }
+    }
+}
+
+// ------------------------------------ subtree stage from staged columns
+// The subtree stage when the records do not carry every coordinate (k >
+// kCachedDims, or fewer global rounds than k), or when the whole tree is one
+// subtree read from the rows (l0 = 0). Each point's index and the keys of
+// the dimensions the local rounds split (at most kLocalRounds of them) are
+// staged once, by slot (index rank), as columns of the workspace; each
+// round then sorts its dimension's column in LDS, as the record stage does
+// (value less its minimum, only the bits that differ, a 32-bit word a
+// pass), and ranks the points with rec_round. Only the round's own order is
+// kept, which leaves 37 KB of LDS a workgroup (four a compute unit). The
+// tree rows of the output are copied from the points themselves, a level's
+// nodes being one contiguous range of rows.
+constexpr int kLocalRounds = 12;  // rounds of a kLocalMax-point subtree (13 levels)
+static_assert(kLocalMax == 1 << kLocalRounds, "levels of the largest subtree");
+
+struct ColScratch {
+    u32 exch[1][kLocalMax];               // record exchange; the rounds' segment counters
+    uint16_t count[kLocalWaves][kRadix];  // per-wave digit counters of a pass
+    u32 start[kRadix];
+    u32 wave[kLocalWaves];
+    u32 red[2][kLocalWaves];              // per-wave minimum and maximum
+    uint16_t dummy[64];
+};
+
+struct ColShared {
+    uint16_t tag[kLocalMax];    // local tag of each slot
+    uint16_t order[kLocalMax];  // the round's order: slots by (coordinate, index); during its
+                                // sort, the payload exchange of the wide passes
+    ColScratch s;
+};
+
+__global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_cols(SubtreeArgs a) {
+    __shared__ ColShared sh;
+    ColScratch& s = sh.s;
+
+    const u64 c = full_nodes(a.l0) + blockIdx.x;  // subtree root (global node id)
+    const u32 nc = (u32)subtree_size(a.geo, c);
+    if (nc == 0) return;
+    u64 first = 0;  // live position of the subtree's first point in round l0-1's order
+    if (a.l0 > 0) {
+        const u64 parent = (c - 1) / 2;
+        const u64 seg = live_begin(a.geo, parent - full_nodes(a.l0 - 1), a.l0 - 1);
+        first = c == 2 * parent + 1 ? seg : seg + subtree_size(a.geo, 2 * parent + 1) + 1;
+    }
+    auto rec = [&](u32 q, int f) -> u32 { return a.recs[rec_word_index(a.words, a.plane, first + q, f)]; };
+    const int kr = a.recs ? a.words - 1 : 0;  // coordinates the records carry
+    const int d_a = a.recs ? (a.l0 - 1) % a.k : -1;  // the arrival order is (coordinate d_a, index)
+    const Geometry lg = make_geometry((i64)nc);
+    const int rounds = lg.levels - 1;
+    const int used = rounds < a.k ? rounds : a.k;  // dimensions (l0 + t) mod k, t < used, differ
+    const int d0 = a.l0 % a.k;
+    u32* col_idx = a.stage + first;
+    auto column = [&](int d) { return a.stage + (u64)(d + 1) * (u64)a.n + first; };
+
+    // Slot = index rank: sort (index - min, arrival position). arr[j] is the
+    // arrival position of slot local_slot(j); the padding positions (q >= nc)
+    // sort last, in order, so that slot e >= nc holds arrival position e.
+    u32 arr[kLocalItems];
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) arr[j] = (u32)local_slot(j);
+    if (a.recs) {
+        u32 v[kLocalItems], mn[1] = {~0u}, mx[1] = {0u};
+#pragma unroll
+        for (int j = 0; j < kLocalItems; ++j) {
+            const u32 q = (u32)local_slot(j);
+            v[j] = q < nc ? rec(q, a.words - 1) : 0u;
+            mn[0] = q < nc && v[j] < mn[0] ? v[j] : mn[0];
+            mx[0] = q < nc && v[j] > mx[0] ? v[j] : mx[0];
+        }
+        rec_min_max<1>(mn, mx, s);
+        const int vbits = value_bits(mx[0] - mn[0]);
+        const u32 pad = vbits == 32 ? ~0u : (1u << vbits) - 1;
+#pragma unroll
+        for (int j = 0; j < kLocalItems; ++j) v[j] = (u32)local_slot(j) < nc ? v[j] - mn[0] : pad;
+        rec_sort(v, arr, vbits, s, sh.order);
+    }
+
+    // Stage by slot: the index, and the keys of the dimensions the rounds
+    // split -- for d_a, the arrival position instead, from which its order
+    // is known without a sort. A point's loads are issued together, so that
+    // its row is fetched once; one point at a time per thread (the arrival
+    // positions wait in the exchange buffer, each thread's at its own slots,
+    // which the sort's last reads were from).
+    u32* arr_of = s.exch[0];
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) arr_of[local_slot(j)] = arr[j];
+#pragma unroll 1
+    for (int j = 0; j < kLocalItems; ++j) {
+        const u32 e = (u32)local_slot(j);
+        if (e >= nc) continue;
+        const u32 q = arr_of[e];
+        const u32 idx = a.recs ? rec(q, a.words - 1) : q;
+        const float* row = a.pts + (u64)idx * (u64)a.k;
+        u32 key[kLocalRounds];
+        int d = d0;
+#pragma unroll
+        for (int u = 0; u < kLocalRounds; ++u) {
+            key[u] = 0;
+            if (u < used) key[u] = d == d_a ? q : d < kr ? rec(q, d) : float_key(__float_as_uint(row[d]));
+            d = d + 1 == a.k ? 0 : d + 1;
+        }
+        col_idx[e] = idx;
+        d = d0;
+#pragma unroll
+        for (int u = 0; u < kLocalRounds; ++u) {
+            if (u < used) column(d)[e] = key[u];
+            d = d + 1 == a.k ? 0 : d + 1;
+        }
+        sh.tag[e] = 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j)
+        if ((u32)local_slot(j) >= nc) sh.tag[local_slot(j)] = kPadTag;
+    __syncthreads();  // the columns written before a round reads them
+
+    int d = d0;
+    for (int t = 0; t < rounds; ++t) {
+        const u32* col = column(d);
+        if (d == d_a) {
+            // order[q] = slot of arrival position q
+#pragma unroll
+            for (int j = 0; j < kLocalItems; ++j) {
+                const u32 e = (u32)local_slot(j);
+                sh.order[e < nc ? col[e] : e] = (uint16_t)e;
+            }
+        } else {
+            u32 v[kLocalItems], pay[kLocalItems], mn[1] = {~0u}, mx[1] = {0u};
+#pragma unroll
+            for (int j = 0; j < kLocalItems; ++j) {
+                const u32 e = (u32)local_slot(j);
+                v[j] = e < nc ? col[e] : 0u;
+                mn[0] = e < nc && v[j] < mn[0] ? v[j] : mn[0];
+                mx[0] = e < nc && v[j] > mx[0] ? v[j] : mx[0];
+                pay[j] = e;
+            }
+            rec_min_max<1>(mn, mx, s);
+            const int vbits = value_bits(mx[0] - mn[0]);
+            const u32 pad = vbits == 32 ? ~0u : (1u << vbits) - 1;
+#pragma unroll
+            for (int j = 0; j < kLocalItems; ++j) v[j] = (u32)local_slot(j) < nc ? v[j] - mn[0] : pad;
+            // (the sort's last pass reads only the word exchange: order is free)
+            rec_sort(v, pay, vbits, s, sh.order);
+#pragma unroll
+            for (int j = 0; j < kLocalItems; ++j) sh.order[local_slot(j)] = (uint16_t)pay[j];
+        }
+        __syncthreads();
+        // 16-bit counters fill the exchange buffer at 1024 segments; past
+        // that a segment holds at most 3 points
+        if ((size_t)kLocalWaves * sizeof(uint16_t) << t <= sizeof(s.exch))
+            rec_round<uint16_t>(sh.order, t, lg, sh.tag, s);
+        else
+            rec_round<uint8_t>(sh.order, t, lg, sh.tag, s);
+        d = d + 1 == a.k ? 0 : d + 1;
+    }
+
+    // Output: the index of each local node (by its final tag), then perm and
+    // the tree rows, a level's nodes being the contiguous global range
+    // (c << level) + node.
+    u32* idx_of = s.exch[0];
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) {
+        const u32 e = (u32)local_slot(j);
+        if (e < nc) idx_of[sh.tag[e]] = col_idx[e];
+    }
+    __syncthreads();
+    for (u32 n = threadIdx.x; n < nc; n += kLocalBlock) {
+        const u64 g = (c << level_of(n)) + n;
+        if (g < (u64)a.n) a.perm[g] = (int32_t)idx_of[n];
+    }
+    if (!a.tree) return;
+    // word f = n k + dim of the subtree's rows, node n = f / k stepped along
+    const u32 k = (u32)a.k, total = k * nc;
+    const u32 step_n = kLocalBlock / k, step_d = kLocalBlock % k;
+    u32 n = threadIdx.x / k, dim = threadIdx.x % k;
+    for (u32 f = threadIdx.x; f < total; f += kLocalBlock) {
+        const u64 g = (c << level_of(n)) + n;
+        if (g < (u64)a.n) a.tree[g * k + dim] = a.pts[(u64)idx_of[n] * k + dim];
+        n += step_n;
+        dim += step_d;
+        if (dim >= k) {
+            dim -= k;
+            ++n;
         }
     }
 }
@@ -3191,7 +2983,7 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_widest(WidestSubtree
         const u32 used = wsh.dim_mask[t & 1];  // dimensions this level's nodes split
         if (threadIdx.x == 0) wsh.dim_mask[(t + 1) & 1] = 0;  // read a level ago; the rounds' barriers follow
         if (__popc(used) == 1) {  // one dimension: its order is the list
-            rec_round(sh.m.order[__ffs(used) - 1], t, lg, sh, wsh.nodedim, (u32)(__ffs(used) - 1));
+            rec_round(sh.m.order[__ffs(used) - 1], t, lg, sh.m.tag, s, wsh.nodedim, (u32)(__ffs(used) - 1));
         } else {
             // the list in exch[1], the counters in exch[0] (16 KB: 16-bit
             // up to 1024 segments; 8-bit where a segment holds at most 255
@@ -4231,28 +4023,28 @@ kdt_status build_impl(const float* points, int64_t N, int32_t k, int32_t* perm_o
     sa.recs = recs;
     sa.words = lay.words;
     sa.plane = (u64)N;
-    int bits = 0;
-    for (u64 v = (u64)(N - 1); v; v >>= 1) ++bits;
-    sa.index_bytes = (bits + kRadixBits - 1) / kRadixBits;
     sa.stage = (u32*)((char*)workspace + lay.stage);
     sa.perm = perm_out;
     sa.tree = tree_out;
     const i64 below = N - (i64)full_nodes(l0);  // points in the level-l0 subtrees
-    // the record (or the row) in, index + row staged and read back, perm and
-    // tree out
     const double row = 4.0 * k;
-    const double in = l0 > 0 ? 4.0 * lay.words + 4.0 * (k - lay.kr) : row;
     // records that carry every coordinate are read in place, else staged
     const bool from_recs = recs && lay.words - 1 == k && k <= kCachedDims;
+    // per point: records: the record in, perm and the row out. Columns: the
+    // index and the keys of the (at most kLocalRounds) dimensions the rounds
+    // split in, staged and read back, perm out and the row copied.
+    const int local_rounds = make_geometry((i64)subtree_size(geo, full_nodes(l0))).levels - 1;
+    const int used = local_rounds < k ? local_rounds : k;
+    const double cols = 4.0 * (1 + used) * 3 + 4 + (tree_out ? 2 * row : 0);
     static const char* const kRecNames[kCachedDims + 1] = {"", "k_subtree_recs<1>", "k_subtree_recs<2>",
                                                            "k_subtree_recs<3>"};
-    timer.begin(from_recs ? kRecNames[k] : "k_subtree",
-                (double)below * (in + (from_recs ? 0.0 : 2 * (4 + row)) + 4 + (tree_out ? row : 0)));
+    timer.begin(from_recs ? kRecNames[k] : "k_subtree_cols",
+                (double)below * (from_recs ? 4.0 * lay.words + 4 + (tree_out ? row : 0) : cols));
     const unsigned subtrees = (unsigned)(1ull << l0);
     if (from_recs && k == 1) k_subtree_recs<1><<<subtrees, kLocalBlock, 0, stream>>>(sa);
     else if (from_recs && k == 2) k_subtree_recs<2><<<subtrees, kLocalBlock, 0, stream>>>(sa);
     else if (from_recs) k_subtree_recs<3><<<subtrees, kLocalBlock, 0, stream>>>(sa);
-    else k_subtree<<<subtrees, kLocalBlock, 0, stream>>>(sa);
+    else k_subtree_cols<<<subtrees, kLocalBlock, 0, stream>>>(sa);
     timer.end();
     return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
 }
