@@ -2550,43 +2550,87 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_cols(SubtreeArgs a) 
         rec_sort(v, arr, vbits, s, sh.order);
     }
 
-    // Stage by slot: the index, and the keys of the dimensions the rounds
-    // split -- for d_a, the arrival position instead, from which its order
-    // is known without a sort. A point's loads are issued together, so that
-    // its row is fetched once; one point at a time per thread (the arrival
-    // positions wait in the exchange buffer, each thread's at its own slots,
-    // which the sort's last reads were from).
-    u32* arr_of = s.exch[0];
+    // Stage by slot. The record words -- the index, and the coordinates
+    // below kr -- are read coalesced by arrival position and put in slot
+    // order through LDS; for d_a the column holds the arrival position
+    // itself, from which its order is known without a sort. The other
+    // coordinates the rounds split are the run [d0, d0 + nr) of each row
+    // (the used dimensions from d0 on, up to kr's wrap), gathered two points
+    // at a time with a point's loads issued together, so that a row is
+    // fetched once.
+    uint16_t* slot_of_arr = sh.order;  // free until the first round
 #pragma unroll
-    for (int j = 0; j < kLocalItems; ++j) arr_of[local_slot(j)] = arr[j];
-#pragma unroll 1
-    for (int j = 0; j < kLocalItems; ++j) {
-        const u32 e = (u32)local_slot(j);
-        if (e >= nc) continue;
-        const u32 q = arr_of[e];
-        const u32 idx = a.recs ? rec(q, a.words - 1) : q;
-        const float* row = a.pts + (u64)idx * (u64)a.k;
-        u32 key[kLocalRounds];
-        int d = d0;
+    for (int j = 0; j < kLocalItems; ++j) slot_of_arr[arr[j]] = (uint16_t)local_slot(j);
+    __syncthreads();  // (also orders the sort's last exchange reads before its reuse)
+    auto stage_word = [&](int f, u32* dst, u32 (&got)[kLocalItems]) {
+        u32 val[kLocalItems];
 #pragma unroll
-        for (int u = 0; u < kLocalRounds; ++u) {
-            key[u] = 0;
-            if (u < used) key[u] = d == d_a ? q : d < kr ? rec(q, d) : float_key(__float_as_uint(row[d]));
-            d = d + 1 == a.k ? 0 : d + 1;
+        for (int j = 0; j < kLocalItems; ++j) {
+            const u32 q = (u32)local_slot(j);
+            val[j] = q < nc ? rec(q, f) : 0u;
         }
-        col_idx[e] = idx;
-        d = d0;
 #pragma unroll
-        for (int u = 0; u < kLocalRounds; ++u) {
-            if (u < used) column(d)[e] = key[u];
-            d = d + 1 == a.k ? 0 : d + 1;
+        for (int j = 0; j < kLocalItems; ++j) s.exch[0][slot_of_arr[local_slot(j)]] = val[j];
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kLocalItems; ++j) {
+            const u32 e = (u32)local_slot(j);
+            got[j] = s.exch[0][e];
+            if (e < nc) dst[e] = got[j];
         }
-        sh.tag[e] = 0;
+        __syncthreads();
+    };
+    u32 idx[kLocalItems];  // index of the point in slot local_slot(j)
+    if (a.recs) {
+        stage_word(a.words - 1, col_idx, idx);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kLocalItems; ++j) {
+            const u32 e = (u32)local_slot(j);
+            idx[j] = e;
+            if (e < nc) col_idx[e] = e;
+        }
+    }
+    // kr = min(k, l0) and d0 = l0 mod k: below k global rounds kr = d0, and
+    // the used dimensions from d0 to k-1 come from the rows, the wrapped
+    // ones (below kr) from the records
+    const int nr = kr == a.k ? 0 : (used < a.k - d0 ? used : a.k - d0);
+    for (int u = nr, d = (d0 + nr) % a.k; u < used; ++u, d = d + 1 == a.k ? 0 : d + 1) {
+        if (d == d_a) {
+#pragma unroll
+            for (int j = 0; j < kLocalItems; ++j)
+                if ((u32)local_slot(j) < nc) column(d)[local_slot(j)] = arr[j];
+        } else {
+            u32 got[kLocalItems];
+            stage_word(d, column(d), got);
+        }
+    }
+    if (nr > 0) {
+#pragma unroll
+        for (int j0 = 0; j0 < kLocalItems; j0 += 2) {
+            u32 key[2][kLocalRounds];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const bool ok = (u32)local_slot(j0 + h) < nc;
+                const float* row = a.pts + (u64)idx[j0 + h] * (u64)a.k + d0;
+#pragma unroll
+                for (int i = 0; i < kLocalRounds; ++i)
+                    key[h][i] = ok && i < nr ? float_key(__float_as_uint(row[i])) : 0u;
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const u32 e = (u32)local_slot(j0 + h);
+                if (e >= nc) continue;
+                u32* dst = column(d0) + e;
+#pragma unroll
+                for (int i = 0; i < kLocalRounds; ++i)
+                    if (i < nr) dst[(u64)i * (u64)a.n] = key[h][i];
+            }
+        }
     }
 #pragma unroll
-    for (int j = 0; j < kLocalItems; ++j)
-        if ((u32)local_slot(j) >= nc) sh.tag[local_slot(j)] = kPadTag;
-    __syncthreads();  // the columns written before a round reads them
+    for (int j = 0; j < kLocalItems; ++j) sh.tag[local_slot(j)] = (u32)local_slot(j) < nc ? 0 : kPadTag;
+    __syncthreads();  // the columns written before a round reads them; the tags set
 
     int d = d0;
     for (int t = 0; t < rounds; ++t) {
