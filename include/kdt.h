@@ -93,7 +93,7 @@ kdt_status kdt_build(const float* points, int64_t N, int32_t k,
  * passes the points and the outputs, as for kdt_build.
  *   Returns KDT_ERR_TOO_LARGE, before anything is enqueued, when
  *   kdt_workspace_size(N, k) > KDT_STATIC_SCRATCH_BYTES (for k = 3 that is
- *   N above about 570,000 points).
+ *   N above about 666,000 points).
  *   Every call on one GPU shares that GPU's array and it keeps the last
  *   call's contents (the build needs no zeroed workspace). Calls that overlap
  *   on one GPU (on different streams, or from several threads without

@@ -1986,8 +1986,10 @@ struct SubtreeArgs {
     const u32* recs;        // l0 > 0: records (coordinates 0 .. words-2, then the
     int words;              // index) live on level l0-1, in round l0-1's order
     u64 plane;              // their plane stride (records wider than kWholeWords)
-    u32* stage;             // (k+1) x n words: index, then coordinate key columns; the
-                            // subtree owns [first, first + |S(c)|) of each
+    u32* stage;             // 1 + min(k, kLocalRounds) columns of n words: the index, then
+                            // the key column of each dimension the local rounds split, by
+                            // round (dimension (l0 + u) mod k in column u + 1); the subtree
+                            // owns [first, first + |S(c)|) of each
     int32_t* perm;
     float* tree;
 };
@@ -2525,7 +2527,8 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_cols(SubtreeArgs a) 
     const int used = rounds < a.k ? rounds : a.k;  // dimensions (l0 + t) mod k, t < used, differ
     const int d0 = a.l0 % a.k;
     u32* col_idx = a.stage + first;
-    auto column = [&](int d) { return a.stage + (u64)(d + 1) * (u64)a.n + first; };
+    // column of the u-th dimension the rounds split, (d0 + u) mod k
+    auto column = [&](int u) { return a.stage + (u64)(u + 1) * (u64)a.n + first; };
 
     // Slot = index rank: sort (index - min, arrival position). arr[j] is the
     // arrival position of slot local_slot(j); the padding positions (q >= nc)
@@ -2599,10 +2602,10 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_cols(SubtreeArgs a) 
         if (d == d_a) {
 #pragma unroll
             for (int j = 0; j < kLocalItems; ++j)
-                if ((u32)local_slot(j) < nc) column(d)[local_slot(j)] = arr[j];
+                if ((u32)local_slot(j) < nc) column(u)[local_slot(j)] = arr[j];
         } else {
             u32 got[kLocalItems];
-            stage_word(d, column(d), got);
+            stage_word(d, column(u), got);
         }
     }
     if (nr > 0) {
@@ -2621,7 +2624,7 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_cols(SubtreeArgs a) 
             for (int h = 0; h < 2; ++h) {
                 const u32 e = (u32)local_slot(j0 + h);
                 if (e >= nc) continue;
-                u32* dst = column(d0) + e;
+                u32* dst = column(0) + e;
 #pragma unroll
                 for (int i = 0; i < kLocalRounds; ++i)
                     if (i < nr) dst[(u64)i * (u64)a.n] = key[h][i];
@@ -2632,9 +2635,9 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_cols(SubtreeArgs a) 
     for (int j = 0; j < kLocalItems; ++j) sh.tag[local_slot(j)] = (u32)local_slot(j) < nc ? 0 : kPadTag;
     __syncthreads();  // the columns written before a round reads them; the tags set
 
-    int d = d0;
+    int d = d0, u = 0;  // round t splits dimension d, staged in column u = t mod k
     for (int t = 0; t < rounds; ++t) {
-        const u32* col = column(d);
+        const u32* col = column(u);
         if (d == d_a) {
             // order[q] = slot of arrival position q
 #pragma unroll
@@ -2670,6 +2673,7 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_cols(SubtreeArgs a) 
         else
             rec_round<uint8_t>(sh.order, t, lg, sh.tag, s);
         d = d + 1 == a.k ? 0 : d + 1;
+        u = u + 1 == a.k ? 0 : u + 1;
     }
 
     // Output: the index of each local node (by its final tag), then perm and
@@ -3160,6 +3164,10 @@ struct Layout {
     size_t planar0;      // records wider than kWholeWords: all of them in index order, planar
 };
 
+// Whether the subtree stage after `rounds` global rounds reads records that
+// carry every coordinate (k_subtree_recs) rather than staging columns.
+inline bool stage_from_records(int k, int rounds) { return rounds > 0 && k <= rounds && k <= kCachedDims; }
+
 // Workspace of `rounds` global rounds and, with `stage`, of the subtree stage.
 bool make_layout(i64 n, int k, int rounds, bool stage, Layout* out) {
     if (n < 0 || n > INT32_MAX || k < 1 || k > 65535 || rounds < 0 || rounds >= kMaxRounds)
@@ -3198,7 +3206,9 @@ bool make_layout(i64 n, int k, int rounds, bool stage, Layout* out) {
         lay.chunk_slots =
             take((size_t)((lay.tiles + kChunkTiles - 1) / kChunkTiles) * kRadix * sizeof(u32));
     }
-    if (stage) lay.stage = take((size_t)(k + 1) * n * sizeof(u32));
+    // the columns stage's: the index and at most kLocalRounds key columns
+    // (none where the records carry every coordinate)
+    if (stage && !stage_from_records(k, rounds)) lay.stage = take((size_t)(1 + (k < kLocalRounds ? k : kLocalRounds)) * n * sizeof(u32));
     lay.total = off;
     *out = lay;
     return true;
@@ -4067,13 +4077,14 @@ kdt_status build_impl(const float* points, int64_t N, int32_t k, int32_t* perm_o
     sa.recs = recs;
     sa.words = lay.words;
     sa.plane = (u64)N;
-    sa.stage = (u32*)((char*)workspace + lay.stage);
+    // records that carry every coordinate (then lay.words == k + 1) are read
+    // in place, else staged
+    const bool from_recs = stage_from_records(k, l0);
+    sa.stage = from_recs ? nullptr : (u32*)((char*)workspace + lay.stage);
     sa.perm = perm_out;
     sa.tree = tree_out;
     const i64 below = N - (i64)full_nodes(l0);  // points in the level-l0 subtrees
     const double row = 4.0 * k;
-    // records that carry every coordinate are read in place, else staged
-    const bool from_recs = recs && lay.words - 1 == k && k <= kCachedDims;
     // per point: records: the record in, perm and the row out. Columns: the
     // index and the keys of the (at most kLocalRounds) dimensions the rounds
     // split in, staged and read back, perm out and the row copied.
