@@ -2058,9 +2058,12 @@ __device__ __forceinline__ void peer_mask(u32 d, int bits, u32 within_lo, u32 wi
 // (the rest does not fit 32 - kPay bits yet), its payloads exchanged through
 // pay_x (kLocalMax 16-bit entries). S is the scratch type (RecScratch or
 // ColScratch): only its first exchange buffer is used.
-template <bool kWideIn, bool kWideOut, typename S>
-__device__ __forceinline__ void rec_pass(u32 (&hi)[kLocalItems], u32 (&lo)[kLocalItems], int bits, S& s,
+// kBits > 0: the digit width as a compile-time constant (bits_rt unused), so
+// that the ballot match unrolls.
+template <bool kWideIn, bool kWideOut, int kBits, typename S>
+__device__ __forceinline__ void rec_pass(u32 (&hi)[kLocalItems], u32 (&lo)[kLocalItems], int bits_rt, S& s,
                                          uint16_t* pay_x) {
+    const int bits = kBits > 0 ? kBits : bits_rt;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const u32 bins = 1u << bits;
     uint16_t* cnt = s.count[w];
@@ -2128,6 +2131,16 @@ __device__ __forceinline__ void rec_pass(u32 (&hi)[kLocalItems], u32 (&lo)[kLoca
     }
 }
 
+// A pass of the common digit widths (6 to 8 bits) with its match unrolled.
+template <bool kWideIn, bool kWideOut, typename S>
+__device__ __forceinline__ void rec_pass_any(u32 (&hi)[kLocalItems], u32 (&lo)[kLocalItems], int bits, S& s,
+                                             uint16_t* pay_x) {
+    if (bits == 8) rec_pass<kWideIn, kWideOut, 8>(hi, lo, bits, s, pay_x);
+    else if (bits == 7) rec_pass<kWideIn, kWideOut, 7>(hi, lo, bits, s, pay_x);
+    else if (bits == 6) rec_pass<kWideIn, kWideOut, 6>(hi, lo, bits, s, pay_x);
+    else rec_pass<kWideIn, kWideOut, 0>(hi, lo, bits, s, pay_x);
+}
+
 // Stable sort of the items (value v[j] below 2^vbits, payload pay[j] below
 // 2^kPay) from their current order; returns with pay[j] = the payload of the
 // item at position local_slot(j). vbits = 0: nothing to sort. pay_x as in
@@ -2142,9 +2155,9 @@ __device__ __forceinline__ void rec_sort(u32 (&v)[kLocalItems], u32 (&pay)[kLoca
     for (int p = 0; p < passes; ++p) {
         const int bits = (left + (passes - p) - 1) / (passes - p);
         const bool out_wide = left - bits > 32 - kPay;
-        if (wide && out_wide) rec_pass<true, true>(v, pay, bits, s, pay_x);
-        else if (wide) rec_pass<true, false>(v, pay, bits, s, pay_x);
-        else rec_pass<false, false>(v, pay, bits, s, pay_x);
+        if (wide && out_wide) rec_pass_any<true, true>(v, pay, bits, s, pay_x);
+        else if (wide) rec_pass_any<true, false>(v, pay, bits, s, pay_x);
+        else rec_pass_any<false, false>(v, pay, bits, s, pay_x);
         wide = out_wide;
         left -= bits;
     }
@@ -2205,9 +2218,12 @@ __device__ __forceinline__ int value_bits(u32 span) { return span == ~0u ? 32 : 
 // that are not live count into a dummy and write their tag back unchanged.
 // With nodedim (split-widest trees), only the segments whose node splits
 // dimension d are live.
-template <typename Count = uint16_t, typename S>
-__device__ __forceinline__ void rec_round(const uint16_t* order, int t, const Geometry& lg, uint16_t* tag,
-                                          S& s, const uint8_t* nodedim = nullptr, u32 d = 0) {
+// kT >= 0: the round index as a compile-time constant (t_rt unused), so that
+// the t-bit ballot match unrolls.
+template <int kT, typename Count, typename S>
+__device__ __forceinline__ void rec_round_at(const uint16_t* order, int t_rt, const Geometry& lg, uint16_t* tag,
+                                             S& s, const uint8_t* nodedim, u32 d) {
+    const int t = kT >= 0 ? kT : t_rt;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const u32 fl = (1u << t) - 1, segs = 1u << t;
     Count* cnt = reinterpret_cast<Count*>(&s.exch[0][0]);  // [kLocalWaves][segs]
@@ -2286,6 +2302,20 @@ __device__ __forceinline__ void rec_round(const uint16_t* order, int t, const Ge
         tag[e[j]] = (uint16_t)(live ? next : st[j]);
     }
     __syncthreads();
+}
+
+template <typename Count = uint16_t, typename S>
+__device__ __forceinline__ void rec_round(const uint16_t* order, int t, const Geometry& lg, uint16_t* tag,
+                                          S& s, const uint8_t* nodedim = nullptr, u32 d = 0) {
+    switch (t) {  // every round of a kLocalMax-point subtree: t <= kLocalRounds - 1
+#define KDT_ROUND_CASE(T) \
+    case T: rec_round_at<T, Count>(order, t, lg, tag, s, nodedim, d); break;
+        KDT_ROUND_CASE(0) KDT_ROUND_CASE(1) KDT_ROUND_CASE(2) KDT_ROUND_CASE(3)
+        KDT_ROUND_CASE(4) KDT_ROUND_CASE(5) KDT_ROUND_CASE(6) KDT_ROUND_CASE(7)
+        KDT_ROUND_CASE(8) KDT_ROUND_CASE(9) KDT_ROUND_CASE(10) KDT_ROUND_CASE(11)
+#undef KDT_ROUND_CASE
+        default: rec_round_at<-1, Count>(order, t, lg, tag, s, nodedim, d); break;
+    }
 }
 
 template <int kK>
