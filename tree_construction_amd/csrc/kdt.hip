@@ -272,7 +272,8 @@ __device__ inline u64 block_exclusive_scan64(u64 v, u64* s_wave) {
 // this lane's bit as a mask (0 or all ones) in one instruction, and the
 // ballot reads the same mask.
 __device__ inline void match_bit(u32 d, int b, u32& miss_lo, u32& miss_hi) {
-    const u32 m = (u32)__builtin_amdgcn_sbfe((int)d, b, 1);
+    u32 m = (u32)__builtin_amdgcn_sbfe((int)d, b, 1);
+    asm("" : "+v"(m));  // (opaque: the vote compares m, no second bit test)
     const u64 vote = __ballot(m != 0);
     // miss |= vote ^ m, one three-input bit operation per half (truth
     // table 0xF6 over (miss, vote, m), miss the most significant input)
@@ -2045,7 +2046,10 @@ __device__ __forceinline__ void peer_mask(u32 d, int bits, u32 within_lo, u32 wi
     p_lo = within_lo;
     p_hi = within_hi;
     for (int b = 0; b < bits; ++b) {
-        const u32 m = (u32)__builtin_amdgcn_sbfe((int)d, b, 1);
+        u32 m = (u32)__builtin_amdgcn_sbfe((int)d, b, 1);
+        // (opaque, so that the vote compares m itself rather than testing the
+        // bit of d again with a shift of its own: one VALU instruction less)
+        asm("" : "+v"(m));
         const u64 vote = __ballot(m != 0);
         p_lo = __builtin_amdgcn_bitop3_b32(p_lo, (u32)vote, m, 0x90);
         p_hi = __builtin_amdgcn_bitop3_b32(p_hi, (u32)(vote >> 32), m, 0x90);
