@@ -115,6 +115,23 @@ def test_select_rounds_4m(torch_dev, k):
     assert_same_tree(pts, perm, tree, oracle.build_tree(pts), "4M k=%d" % k)
 
 
+@pytest.mark.parametrize("n,k", [(70000, 4), (70000, 9), (70000, 13), (300000, 5), (300000, 12),
+                                 (300000, 16), (300000, 33), (1100000, 20)])
+def test_columns_stage_dimension_mix(torch_dev, n, k):
+    """The LDS stage for k > 3 stages the dimensions its (11) local rounds
+    split: from the records where a global round carried them, as the run of
+    each row from l0 mod k otherwise, and, for the dimension the points
+    arrived sorted by, as arrival positions. These sizes (l0 = 5, 7, 9) give
+    every mix: all from the records with the arrived dimension reused (k = 4,
+    5), a row run plus wrapped record dimensions with it (k = 9), rows and
+    records without it (k = 12, 13, 16), and rows only (k = 20, 33)."""
+    for gen in ("gmm", "ties"):
+        pts = make(gen, n, k, 90 + k)
+        say("case columns stage gen=%s N=%d k=%d" % (gen, n, k))
+        perm, tree = gpu_build(torch_dev, pts)
+        assert_same_tree(pts, perm, tree, oracle.build_tree(pts), "%s N=%d k=%d" % (gen, n, k))
+
+
 @pytest.mark.parametrize("k,n", [(1, 4099), (2, 70001), (3, 100003), (4, 65536)])
 def test_rows_not_16_byte_aligned(torch_dev, k, n):
     """Rows that do not start on 16 bytes (a view one float into a larger
