@@ -45,7 +45,7 @@ typedef uint64_t u64;
 typedef int64_t i64;
 
 constexpr int kKnnBlock = 256;
-constexpr int kPathRegs = 8;  // split offsets of the deepest path nodes a search thread keeps
+constexpr int kPathRegs = 10;  // split offsets of the deepest path nodes a search thread keeps
 constexpr int kKnnMaxK = 32;       // neighbours per query at most
 // Points one first-pass thread examines before handing its query over:
 // 32 K within [128, 512], about the 99th percentile of a typical search (the
