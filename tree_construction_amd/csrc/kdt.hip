@@ -2518,9 +2518,10 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_recs(SubtreeArgs a) 
 // round then sorts its dimension's column in LDS, as the record stage does
 // (value less its minimum, only the bits that differ, a 32-bit word a
 // pass), and ranks the points with rec_round. Only the round's own order is
-// kept, which leaves 37 KB of LDS a workgroup (four a compute unit). The
-// tree rows of the output are copied from the points themselves, a level's
-// nodes being one contiguous range of rows.
+// kept, which leaves 37 KB of LDS a workgroup (its ~120 registers a thread
+// allow two workgroups a compute unit either way). The tree rows of the
+// output are copied from the points themselves, a level's nodes being one
+// contiguous range of rows.
 constexpr int kLocalRounds = 12;  // rounds of a kLocalMax-point subtree (13 levels)
 static_assert(kLocalMax == 1 << kLocalRounds, "levels of the largest subtree");
 
