@@ -156,6 +156,34 @@ __device__ __forceinline__ float squared_distance(const Query<kDims>& q, const N
     return acc;
 }
 
+// The split offset q[split] - p[split] and (dist non-null) the squared
+// distance, from the per-dimension differences computed once: the split
+// one is picked by selects (the same subtraction, so the same value), which
+// saves the masked picks of both coordinates. kDims == 0: read in place.
+template <int kDims>
+__device__ __forceinline__ float split_offset(const Query<kDims>& q, const NodeRow<kDims>& node, int split, int k,
+                                              float* dist) {
+#pragma clang fp contract(off)
+    if constexpr (kDims > 0) {
+        float t[kDims];
+#pragma unroll
+        for (int d = 0; d < kDims; ++d) t[d] = q.c[d] - node.p[d];
+        float diff = t[0];
+#pragma unroll
+        for (int d = 1; d < kDims; ++d) diff = split == d ? t[d] : diff;
+        if (dist) {
+            float acc = 0.0f;  // as squared_distance: 0 + t0*t0 is t0*t0 exactly
+#pragma unroll
+            for (int d = 0; d < kDims; ++d) acc = acc + t[d] * t[d];
+            *dist = acc;
+        }
+        return diff;
+    } else {
+        if (dist) *dist = squared_distance<kDims>(q, node, k);
+        return q.at(split) - node.at(split);
+    }
+}
+
 // The K best candidates as 64-bit keys (float bits of the squared distance,
 // which order like the values for non-negative floats, then the index), in
 // descending order: slot[0] is the K-th best. Slots K .. kK-1 hold 0, below
@@ -250,8 +278,9 @@ __global__ __launch_bounds__(kKnnBlock) void k_knn(KnnArgs a) {
                 NodeRow<kDims> node;
                 node.load(a.tree, curr, k);
                 const int split = a.dims ? a.dims[curr] : dim;
-                const float diff = q.at(split) - node.at(split);
-                const u32 bits = __float_as_uint(squared_distance<kDims>(q, node, k));
+                float dist;
+                const float diff = split_offset<kDims>(q, node, split, k, &dist);
+                const u32 bits = __float_as_uint(dist);
                 if (bits <= best.worst_bits()) {
                     const u64 key = ((u64)bits << 32) | (u32)a.perm[curr];
                     if (key < best.slot[0]) best.insert(key);
@@ -273,7 +302,7 @@ __global__ __launch_bounds__(kKnnBlock) void k_knn(KnnArgs a) {
                 NodeRow<kDims> node;
                 node.load(a.tree, curr, k);
                 const int split = a.dims ? a.dims[curr] : dim;
-                diff = q.at(split) - node.at(split);
+                diff = split_offset<kDims>(q, node, split, k, nullptr);
                 path[0] = diff;
                 held = 1;
             }
@@ -374,13 +403,14 @@ struct LaneWalk {
             NodeRow<kDims> node;
             node.load(a.tree, curr, k);
             const int split = a.dims ? a.dims[curr] : dim;
-            const float diff = q.at(split) - node.at(split);
+            float dist;
+            const float diff = split_offset<kDims>(q, node, split, k, &dist);
             const u32 left = 2 * curr + 1;
             const u32 near = diff < 0.0f ? left : left + 1;
             const u32 far = diff < 0.0f ? left + 1 : left;
             const int down = dim + 1 == k ? 0 : dim + 1;
             if (prev == parent) {
-                const u32 bits = __float_as_uint(squared_distance<kDims>(q, node, k));
+                const u32 bits = __float_as_uint(dist);
                 *cand = bits <= worst ? ((u64)bits << 32) | (u32)a.perm[curr] : ~0ull;
                 prev = curr;
                 curr = near;
