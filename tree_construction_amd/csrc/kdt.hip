@@ -549,26 +549,38 @@ static_assert(kSortBlock >= kRadix, "a presort thread per digit");
 // One workgroup per digit d: row d of `chunk` (the digit's count in each
 // chunk) becomes the exclusive prefix over the chunks; totals[d] = the
 // row's sum (if totals is given). Each thread scans a contiguous run of
-// kScanRun chunks held in registers; longer rows loop over runs.
+// kScanRun chunks; longer rows loop over runs. The runs are loaded and
+// stored in coalesced order and handed to their threads through LDS (rows
+// of kScanRun + 1 words, so that a thread's run reads without bank
+// conflicts): a thread reading its own run from memory would touch a
+// different line with every lane of each load.
 constexpr int kScanRun = 16;
 // One workgroup of kThreads scans one row (digit) in runs of
 // kThreads * kScanRun entries.
 template <int kThreads>
 __device__ __forceinline__ void chunk_scan_row(u32* __restrict__ row, i64 chunks, u32* __restrict__ totals, int d) {
     constexpr int kW = kThreads / 64;
+    constexpr int kPitch = kScanRun + 1;
     __shared__ u32 s_wave[kW];
     __shared__ u32 s_carry;
+    __shared__ u32 s_run[kThreads * kPitch];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // slot of the chunk at offset e of the stretch: thread e / kScanRun's run
+    auto slot = [](int e) { return (e / kScanRun) * kPitch + e % kScanRun; };
     if (tid == kThreads - 1) s_carry = 0;
     for (i64 t0 = 0; t0 < chunks; t0 += (i64)kThreads * kScanRun) {
-        const i64 mine = t0 + (i64)tid * kScanRun;
+#pragma unroll
+        for (int j = 0; j < kScanRun; ++j) {
+            const int e = j * kThreads + tid;
+            s_run[slot(e)] = t0 + e < chunks ? row[t0 + e] : 0u;
+        }
+        __syncthreads();  // the runs staged; s_carry written; s_wave's last readers done
         u32 v[kScanRun], sum = 0;
 #pragma unroll
         for (int i = 0; i < kScanRun; ++i) {
-            v[i] = mine + i < chunks ? row[mine + i] : 0u;
+            v[i] = s_run[tid * kPitch + i];
             sum += v[i];
         }
-        __syncthreads();  // s_carry written; s_wave's last readers done
         const u32 carry = s_carry;
         const u32 inc = wave_inclusive_scan(sum);
         if (lane == 63) s_wave[w] = inc;
@@ -581,11 +593,18 @@ __device__ __forceinline__ void chunk_scan_row(u32* __restrict__ row, i64 chunks
         if (tid == kThreads - 1) s_carry = off + sum;
 #pragma unroll
         for (int i = 0; i < kScanRun; ++i) {
-            if (mine + i < chunks) row[mine + i] = off;
+            s_run[tid * kPitch + i] = off;  // (this thread's own run: read above)
             off += v[i];
         }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kScanRun; ++j) {
+            const int e = j * kThreads + tid;
+            if (t0 + e < chunks) row[t0 + e] = s_run[slot(e)];
+        }
+        __syncthreads();  // the stores' LDS reads done before the next stretch's writes
     }
-    __syncthreads();
+    __syncthreads();  // (an empty row: s_carry's first write)
     if (totals && tid == 0) totals[d] = s_carry;
 }
 
