@@ -1580,12 +1580,14 @@ __global__ __launch_bounds__(kBlock) void k_part_select_widest_batch(PartBatch b
     part_tile<kW, true, true, false>(a, pivot_tile(a, local), local);
 }
 
-// Each pass's digit rows of tile counts, one workgroup a row.
-__global__ __launch_bounds__(kBlock) void k_chunk_scan_batch(PartBatch b) {
+// Each pass's digit rows of tile counts, one workgroup a row (of kThreads:
+// 1024 where a row is longer than one stretch of 256 threads).
+template <int kThreads>
+__global__ __launch_bounds__(kThreads) void k_chunk_scan_batch(PartBatch b) {
     u32 row;
     const int i = batch_pass(b.rows, b.count, row);
     const PartArgs& a = b.a[i];
-    chunk_scan_row<kBlock>(a.chunk_counts + (u64)row * a.tiles, (i64)a.tiles, nullptr, 0);
+    chunk_scan_row<kThreads>(a.chunk_counts + (u64)row * a.tiles, (i64)a.tiles, nullptr, 0);
 }
 
 // Round l's nodes: the pivot of node s = F(l) + j is the record at live
@@ -3599,7 +3601,8 @@ struct Launcher {
         k_part_count_widest_batch<kW><<<b.first[b.count], kBlock, 0, stream>>>(b);
         timer.end();
         timer.begin("k_chunk_scan_batch", scan_bytes);
-        k_chunk_scan_batch<<<b.rows[b.count], kBlock, 0, stream>>>(b);
+        if (wide_scan((i64)max_tiles)) k_chunk_scan_batch<kWideScanBlock><<<b.rows[b.count], kWideScanBlock, 0, stream>>>(b);
+        else k_chunk_scan_batch<kBlock><<<b.rows[b.count], kBlock, 0, stream>>>(b);
         timer.end();
         for (int i = 0; i <= b.count; ++i) b.first[i] = nodes_first[i];
         timer.begin(kPartSelectBatchNames[width_slot(kW)], select_bytes);
