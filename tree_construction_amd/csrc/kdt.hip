@@ -567,6 +567,21 @@ __device__ __forceinline__ void chunk_scan_row(u32* __restrict__ row, i64 chunks
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     // slot of the chunk at offset e of the stretch: thread e / kScanRun's run
     auto slot = [](int e) { return (e / kScanRun) * kPitch + e % kScanRun; };
+    if (chunks <= kThreads) {  // a short row: one count a thread, no staging
+        const u32 v = tid < chunks ? row[tid] : 0u;
+        const u32 inc = wave_inclusive_scan(v);
+        if (lane == 63) s_wave[w] = inc;
+        __syncthreads();
+        u32 off = inc - v, total = 0;
+#pragma unroll
+        for (int i = 0; i < kW; ++i) {
+            off += i < w ? s_wave[i] : 0u;
+            total += s_wave[i];
+        }
+        if (tid < chunks) row[tid] = off;
+        if (totals && tid == 0) totals[d] = total;
+        return;
+    }
     if (tid == kThreads - 1) s_carry = 0;
     for (i64 t0 = 0; t0 < chunks; t0 += (i64)kThreads * kScanRun) {
 #pragma unroll
