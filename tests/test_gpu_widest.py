@@ -84,11 +84,12 @@ def test_widest_sizes(torch_dev, gen):
         assert_same(pts, perm, tree, dims, "%s N=%d k=%d" % (gen, n, k), check=gen != "special")
 
 
-@pytest.mark.parametrize("k", [1, 2, 3])
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 8, 16])
 def test_widest_lds_stage(torch_dev, k):
-    """For k <= 3 subtrees of at most 4096 points finish in LDS: one subtree
-    read from the rows (N <= 4096) or records on levels 1 .. 7 below the
-    global levels, with every kind of tie."""
+    """Subtrees of at most 4096 points finish in LDS: one subtree read from
+    the rows (N <= 4096) or records on levels 1 .. 7 below the global
+    levels, with every kind of tie. k <= 3 keeps every dimension's order
+    there; wider points sort each level by their nodes' own dimensions."""
     for gen in ("gmm", "ties", "zeros", "equal", "skewed"):
         for n in (4095, 4096, 4097, 12289, 300000):
             pts = make(gen, n, k, 900 + n % 97 + k)
@@ -97,7 +98,7 @@ def test_widest_lds_stage(torch_dev, k):
             assert_same(pts, perm, tree, dims, "%s N=%d k=%d" % (gen, n, k))
 
 
-@pytest.mark.parametrize("k", [1, 2])
+@pytest.mark.parametrize("k", [1, 2, 5])
 def test_widest_4m(torch_dev, k):
     """4,194,304 points: 10 global levels with selects and skipped selects,
     then the LDS stage."""

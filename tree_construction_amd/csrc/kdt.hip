@@ -3212,6 +3212,156 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_widest(WidestSubtree
     }
 }
 
+// ------------------------- split-widest subtrees with more than 3 dimensions
+// The subtree stage of split-widest trees for k > kCachedDims, where no
+// order of every dimension fits LDS. A round ranks each node's points by its
+// own split dimension only within the node's segment, so one sort per level
+// of every live point by the key of its node's dimension (keys of different
+// dimensions interleave, but never within a segment) gives every segment its
+// order: each level is one sort and one round, as in the columns stage. The
+// keys are read from the subtree's records of A_0 (planar: coordinate d in
+// plane d) at each point's arrival position, kept in LDS by slot; the node
+// dimensions (16-bit: k up to 65535) are in LDS too, and after each round
+// the thread holding a new pivot derives both children's domains and
+// dimensions with child_domain, as the global levels do. The whole tree as
+// one subtree (l0 = 0) reads the rows instead.
+struct WidestColShared {
+    ColShared c;
+    uint16_t nodedim[kLocalMax];  // split dimension of each local node
+    uint16_t arr[kLocalMax];      // arrival position of each slot
+};
+
+__global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_widest_cols(WidestSubtreeArgs a) {
+    __shared__ WidestColShared sh;
+    ColScratch& s = sh.c.s;
+    const u64 c = full_nodes(a.l0) + blockIdx.x;  // subtree root (global node id)
+    const u32 nc = (u32)subtree_size(a.geo, c);
+    if (nc == 0) return;
+    const bool rows = a.recs == nullptr;
+    const u64 first = rows ? 0 : live_begin(a.geo, c - full_nodes(a.l0), a.l0);
+    const u32 k = (u32)a.k;
+    // key of coordinate d of the point that arrived at position q (its index
+    // i: the rows' case)
+    auto key = [&](u32 q, u32 d) -> u32 {
+        if (rows) return float_key(__float_as_uint(a.pts[(u64)q * k + d]));
+        return a.recs[(u64)d * (u64)a.n + first + q];
+    };
+
+    // Slot = index rank: sort (index - min, arrival position); the rows
+    // arrive by index.
+    u32 arr[kLocalItems];
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) arr[j] = (u32)local_slot(j);
+    if (!rows) {
+        u32 v[kLocalItems], mn[1] = {~0u}, mx[1] = {0u};
+#pragma unroll
+        for (int j = 0; j < kLocalItems; ++j) {
+            const u32 q = (u32)local_slot(j);
+            v[j] = q < nc ? key(q, k) : 0u;  // word k: the index
+            mn[0] = q < nc && v[j] < mn[0] ? v[j] : mn[0];
+            mx[0] = q < nc && v[j] > mx[0] ? v[j] : mx[0];
+        }
+        rec_min_max<1>(mn, mx, s);
+        const int vbits = value_bits(mx[0] - mn[0]);
+        const u32 pad = vbits == 32 ? ~0u : (1u << vbits) - 1;
+#pragma unroll
+        for (int j = 0; j < kLocalItems; ++j) v[j] = (u32)local_slot(j) < nc ? v[j] - mn[0] : pad;
+        rec_sort(v, arr, vbits, s, sh.c.order);
+    }
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) {
+        const int e = local_slot(j);
+        sh.arr[e] = (uint16_t)arr[j];
+        sh.c.tag[e] = (u32)e < nc ? 0 : kPadTag;
+    }
+    if (threadIdx.x == 0) sh.nodedim[0] = a.dimtab[c];
+    __syncthreads();
+
+    const Geometry lg = make_geometry((i64)nc);
+    const int rounds = lg.levels - 1;
+    for (int t = 0; t < rounds; ++t) {
+        const u32 fl = (u32)full_nodes(t), fl1 = (u32)full_nodes(t + 1);
+        // every live point's key in its node's dimension (fixed points and
+        // padding sort last: they are not ranked)
+        u32 v[kLocalItems], pay[kLocalItems], mn[1] = {~0u}, mx[1] = {0u};
+        u32 live = 0;  // bit j: slot local_slot(j) holds a point of level t
+#pragma unroll
+        for (int j = 0; j < kLocalItems; ++j) {
+            const u32 e = (u32)local_slot(j);
+            const u32 st = sh.c.tag[e];
+            const bool on = st - fl < fl1 - fl;
+            live |= (u32)on << j;
+            v[j] = on ? key(sh.arr[e], sh.nodedim[st]) : 0u;
+            mn[0] = on && v[j] < mn[0] ? v[j] : mn[0];
+            mx[0] = on && v[j] > mx[0] ? v[j] : mx[0];
+        }
+        rec_min_max<1>(mn, mx, s);
+        const int vbits = value_bits(mx[0] - mn[0]);
+        const u32 pad = vbits == 32 ? ~0u : (1u << vbits) - 1;
+#pragma unroll
+        for (int j = 0; j < kLocalItems; ++j) {
+            v[j] = (live >> j) & 1u ? v[j] - mn[0] : pad;
+            pay[j] = (u32)local_slot(j);
+        }
+        rec_sort(v, pay, vbits, s, sh.c.order);
+#pragma unroll
+        for (int j = 0; j < kLocalItems; ++j) sh.c.order[local_slot(j)] = (uint16_t)pay[j];
+        __syncthreads();
+        if ((size_t)kLocalWaves * sizeof(uint16_t) << t <= sizeof(s.exch))
+            rec_round<uint16_t>(sh.c.order, t, lg, sh.c.tag, s);
+        else
+            rec_round<uint8_t>(sh.c.order, t, lg, sh.c.tag, s);
+        // Level t's pivots carry their node's tag now: each one's thread
+        // bounds its node's domain at its coordinate for the two children.
+#pragma unroll 1
+        for (int j = 0; j < kLocalItems; ++j) {
+            const u32 e = (u32)local_slot(j);
+            const u32 sn = sh.c.tag[e];  // (padding: kPadTag, above every level)
+            if (sn < fl || sn >= fl1) continue;
+            const u32 ds = sh.nodedim[sn];
+            const float* from = a.boxes + ((((c + 1) << t) - 1) + (sn - fl)) * 2 * (u64)k;
+            // the pivot's coordinate ds (a zero's sign: the extents agree)
+            const float plane = __uint_as_float(key_bits(key(sh.arr[e], ds)));
+            for (u32 ch = 2 * sn + 1; ch <= 2 * sn + 2 && ch < nc; ++ch) {
+                const u64 g = (((c + 1) << (t + 1)) - 1) + (ch - fl1);
+                const int best = child_domain(from, (int)ds, plane, ch == 2 * sn + 1, (int)k, a.boxes + g * 2 * (u64)k);
+                sh.nodedim[ch] = (uint16_t)best;
+                if (a.dims_out) a.dims_out[g] = best;
+            }
+        }
+        __syncthreads();
+    }
+
+    // Output as in the columns stage: each node's index (by its final tag),
+    // then perm and the tree rows, a level's nodes being the contiguous
+    // global range (c << level) + node.
+    u32* idx_of = s.exch[0];
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) {
+        const u32 e = (u32)local_slot(j);
+        if (e < nc) idx_of[sh.c.tag[e]] = rows ? sh.arr[e] : key(sh.arr[e], k);
+    }
+    __syncthreads();
+    for (u32 n = threadIdx.x; n < nc; n += kLocalBlock) {
+        const u64 g = (c << level_of(n)) + n;
+        if (g < (u64)a.n) a.perm[g] = (int32_t)idx_of[n];
+    }
+    if (!a.tree) return;
+    const u32 total = k * nc;
+    const u32 step_n = kLocalBlock / k, step_d = kLocalBlock % k;
+    u32 n = threadIdx.x / k, dim = threadIdx.x % k;
+    for (u32 f = threadIdx.x; f < total; f += kLocalBlock) {
+        const u64 g = (c << level_of(n)) + n;
+        if (g < (u64)a.n) a.tree[g * k + dim] = a.pts[(u64)idx_of[n] * k + dim];
+        n += step_n;
+        dim += step_d;
+        if (dim >= k) {
+            dim -= k;
+            ++n;
+        }
+    }
+}
+
 // A single point is the whole tree (no workspace is needed for N = 1).
 __global__ void k_single(const float* __restrict__ pts, int k, int32_t* __restrict__ perm,
                          float* __restrict__ tree) {
@@ -3901,8 +4051,7 @@ kdt_status run_unique(const float* pts, i64 n, int k, const UniqueLayout& ul, ch
 // the next level's domains and dimensions from the pivots just fixed. The
 // last level's pass places the leaves.
 // Levels 0 .. lds_from-1 as global passes (every level when lds_from = L),
-// then, if lds_from < L, the subtrees of level lds_from in LDS (k <=
-// kCachedDims).
+// then, if lds_from < L, the subtrees of level lds_from in LDS.
 kdt_status run_widest(const float* pts, i64 n, int k, const WidestLayout& wl, char* ws,
                       hipStream_t stream, Timer timer, int32_t* perm, float* tree,
                       int32_t* dims_out, int lds_from) {
@@ -3964,15 +4113,17 @@ kdt_status run_widest(const float* pts, i64 n, int k, const WidestLayout& wl, ch
         sa.tree = tree;
         sa.dims_out = dims_out;
         const double below = (double)(n - (i64)full_nodes(lds_from));
-        static const char* const kNames[kCachedDims + 1] = {"", "k_subtree_widest<1>", "k_subtree_widest<2>",
-                                                            "k_subtree_widest<3>"};
+        static const char* const kNames[kCachedDims + 2] = {"", "k_subtree_widest<1>", "k_subtree_widest<2>",
+                                                            "k_subtree_widest<3>", "k_subtree_widest_cols"};
         // records (or rows) in and out; each node's domain written (the last
         // level's excepted) and read once by its children's pivot thread
-        timer.begin(kNames[k], below * (4.0 * W + 4 + (tree ? 4.0 * k : 0) + (dims_out ? 4 : 0) + 2 * 8.0 * k));
+        timer.begin(kNames[k <= kCachedDims ? k : kCachedDims + 1],
+                    below * (4.0 * W + 4 + (tree ? 4.0 * k : 0) + (dims_out ? 4 : 0) + 2 * 8.0 * k));
         const unsigned subtrees_n = (unsigned)(1ull << lds_from);
         if (k == 1) k_subtree_widest<1><<<subtrees_n, kLocalBlock, 0, stream>>>(sa);
         else if (k == 2) k_subtree_widest<2><<<subtrees_n, kLocalBlock, 0, stream>>>(sa);
-        else k_subtree_widest<3><<<subtrees_n, kLocalBlock, 0, stream>>>(sa);
+        else if (k == 3) k_subtree_widest<3><<<subtrees_n, kLocalBlock, 0, stream>>>(sa);
+        else k_subtree_widest_cols<<<subtrees_n, kLocalBlock, 0, stream>>>(sa);
         timer.end();
     };
     if (lds_from == 0) {  // the whole tree is one subtree, from the rows
@@ -4203,9 +4354,8 @@ kdt_status build_widest_impl(const float* points, int64_t N, int32_t k, int32_t*
         if (dims_out) k_zero<<<1, kBlock, 0, stream>>>(reinterpret_cast<u32*>(dims_out), 1);
         return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
     }
-    // Subtrees of at most kLocalMax points finish in LDS when every
-    // dimension's order fits there.
-    const int lds_from = k <= kCachedDims ? split_level(N) : wl.base.rounds;
+    // Subtrees of at most kLocalMax points finish in LDS.
+    const int lds_from = split_level(N);
     return run_widest(points, N, k, wl, (char*)workspace, stream, timer, perm_out, tree_out, dims_out,
                       lds_from);
 }
