@@ -2009,6 +2009,13 @@ constexpr int kLocalMax = kLocalBlock * kLocalItems;  // points per subtree
 constexpr int kCachedDims = 3;                        // sorted orders kept in LDS
 static_assert(kLocalBlock >= kRadix, "one thread per digit");
 
+// x, which the compiler can neither fold nor hoist out of a loop: keeps a
+// cheap per-lane value from being held (or spilled) across a long loop.
+__device__ __forceinline__ u32 opaque(u32 x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 // Slot of item j of this thread: each wave owns kLocalItems rows of 64.
 __device__ inline int local_slot(int j) {
     return (threadIdx.x >> 6) * (64 * kLocalItems) + j * 64 + (threadIdx.x & 63);
@@ -3089,6 +3096,12 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_widest(WidestSubtree
             }
         }
     }
+    // From here on arr[j] is the byte offset of that point's record (or
+    // row) from `src`: a 32-bit offset to a uniform base, not a pointer per
+    // slot.
+    const char* src = rows ? reinterpret_cast<const char*>(a.pts) : reinterpret_cast<const char*>(recs);
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) arr[j] *= (rows ? kK : kW) * 4u;
     if (threadIdx.x == 0) {
         wsh.nodedim[0] = (uint8_t)a.dimtab[c];
         wsh.dim_mask[0] = 1u << a.dimtab[c];
@@ -3112,26 +3125,41 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_widest(WidestSubtree
             if (lg.levels - t <= 8) rec_round_list<uint8_t>(list, n_live, t, lg, sh);
             else rec_round_list<uint16_t>(list, n_live, t, lg, sh);
         }
-        // Level t's pivots carry their node's tag now: each one's thread
-        // bounds its node's domain at its coordinate for the two children.
-#pragma unroll
-        for (int j = 0; j < kLocalItems; ++j) {
-            const u32 e = (u32)local_slot(j);
-            const u32 sn = sh.m.tag[e];  // (padding: kPadTag, above every level)
-            if (sn < fl || sn >= fl1) continue;
-            const int ds = wsh.nodedim[sn];
-            const float* from = a.boxes + ((((c + 1) << t) - 1) + (sn - fl)) * 2 * (u64)kK;
-            float lo[kK], hi[kK];
+        // Level t's pivots carry their node's tag now. Each pivot's thread
+        // leaves its coordinate in its node's dimension in LDS (the round's
+        // counters are dead), then one thread a node bounds the node's domain
+        // at that plane for both children and picks their dimensions.
+        const u32 nodes = fl1 - fl;
+        float* plane_of = reinterpret_cast<float*>(&s.exch[0][0]);  // [nodes]
+        const u64 level_first = ((c + 1) << t) - 1;  // global id of local node fl
+        float lo[kK], hi[kK];
+        auto load_domain = [&](u32 i) {
+            const float* from = a.boxes + (level_first + i) * 2 * (u64)kK;
 #pragma unroll
             for (int d = 0; d < kK; ++d) {
                 lo[d] = from[d];
                 hi[d] = from[kK + d];
             }
-            // the pivot's coordinate ds (a zero's sign: the extents agree)
-            u32 pkey;
-            if (rows) pkey = float_key(__float_as_uint(a.pts[(u64)e * kK + ds]));
-            else pkey = recs[(u64)arr[j] * kW + ds];
-            const float plane = __uint_as_float(key_bits(pkey));
+        };
+        // (the first node's domain is in flight during the pivots' pass)
+        if (threadIdx.x < nodes && 2 * (fl + threadIdx.x) + 1 < nc) load_domain(threadIdx.x);
+#pragma unroll
+        for (int j = 0; j < kLocalItems; ++j) {
+            const u32 e = (u32)local_slot(j);
+            const u32 sn = sh.m.tag[e];  // (padding: kPadTag, above every level)
+            if (sn - fl >= nodes) continue;
+            // the pivot's coordinate (a zero's sign: the extents agree)
+            u32 pkey = *reinterpret_cast<const u32*>(src + (arr[j] + 4u * (u32)wsh.nodedim[sn]));
+            if (rows) pkey = float_key(pkey);
+            plane_of[sn - fl] = __uint_as_float(key_bits(pkey));
+        }
+        __syncthreads();
+        for (u32 i = threadIdx.x; i < nodes; i += kLocalBlock) {
+            const u32 sn = fl + i;
+            if (2 * sn + 1 >= nc) break;  // a leaf, as is every later node of the level
+            if (i != threadIdx.x) load_domain(i);
+            const int ds = wsh.nodedim[sn];
+            const float plane = plane_of[i];
             for (u32 ch = 2 * sn + 1; ch <= 2 * sn + 2 && ch < nc; ++ch) {
                 const u64 g = (((c + 1) << (t + 1)) - 1) + (ch - fl1);
                 const bool left = ch == 2 * sn + 1;
@@ -3281,13 +3309,15 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_widest_cols(WidestSu
     const int rounds = lg.levels - 1;
     for (int t = 0; t < rounds; ++t) {
         const u32 fl = (u32)full_nodes(t), fl1 = (u32)full_nodes(t + 1);
+        // slot of item j: slot0 + 64 j (recomputed each level, not held)
+        const u32 slot0 = opaque((u32)local_slot(0));
         // every live point's key in its node's dimension (fixed points and
         // padding sort last: they are not ranked)
         u32 v[kLocalItems], pay[kLocalItems], mn[1] = {~0u}, mx[1] = {0u};
-        u32 live = 0;  // bit j: slot local_slot(j) holds a point of level t
+        u32 live = 0;  // bit j: slot slot0 + 64 j holds a point of level t
 #pragma unroll
         for (int j = 0; j < kLocalItems; ++j) {
-            const u32 e = (u32)local_slot(j);
+            const u32 e = (slot0 + 64u * j);
             const u32 st = sh.c.tag[e];
             const bool on = st - fl < fl1 - fl;
             live |= (u32)on << j;
@@ -3301,30 +3331,40 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_widest_cols(WidestSu
 #pragma unroll
         for (int j = 0; j < kLocalItems; ++j) {
             v[j] = (live >> j) & 1u ? v[j] - mn[0] : pad;
-            pay[j] = (u32)local_slot(j);
+            pay[j] = (slot0 + 64u * j);
         }
         rec_sort(v, pay, vbits, s, sh.c.order);
 #pragma unroll
-        for (int j = 0; j < kLocalItems; ++j) sh.c.order[local_slot(j)] = (uint16_t)pay[j];
+        for (int j = 0; j < kLocalItems; ++j) sh.c.order[slot0 + 64u * j] = (uint16_t)pay[j];
         __syncthreads();
         if ((size_t)kLocalWaves * sizeof(uint16_t) << t <= sizeof(s.exch))
             rec_round<uint16_t>(sh.c.order, t, lg, sh.c.tag, s);
         else
             rec_round<uint8_t>(sh.c.order, t, lg, sh.c.tag, s);
         // Level t's pivots carry their node's tag now: each one's thread
-        // bounds its node's domain at its coordinate for the two children.
+        // leaves its coordinate in its node's dimension in LDS (the round's
+        // counters are dead), then one thread a node derives both children's
+        // domains and dimensions.
+        const u32 nodes = fl1 - fl;
+        float* plane_of = reinterpret_cast<float*>(&s.exch[0][0]);  // [nodes]
 #pragma unroll 1
         for (int j = 0; j < kLocalItems; ++j) {
-            const u32 e = (u32)local_slot(j);
+            const u32 e = (slot0 + 64u * j);
             const u32 sn = sh.c.tag[e];  // (padding: kPadTag, above every level)
-            if (sn < fl || sn >= fl1) continue;
+            if (sn - fl >= nodes) continue;
+            // (a zero's sign: the extents agree)
+            plane_of[sn - fl] = __uint_as_float(key_bits(key(sh.arr[e], sh.nodedim[sn])));
+        }
+        __syncthreads();
+        for (u32 i = threadIdx.x; i < nodes; i += kLocalBlock) {
+            const u32 sn = fl + i;
+            if (2 * sn + 1 >= nc) break;  // a leaf, as is every later node of the level
             const u32 ds = sh.nodedim[sn];
-            const float* from = a.boxes + ((((c + 1) << t) - 1) + (sn - fl)) * 2 * (u64)k;
-            // the pivot's coordinate ds (a zero's sign: the extents agree)
-            const float plane = __uint_as_float(key_bits(key(sh.arr[e], ds)));
+            const float* from = a.boxes + ((((c + 1) << t) - 1) + i) * 2 * (u64)k;
             for (u32 ch = 2 * sn + 1; ch <= 2 * sn + 2 && ch < nc; ++ch) {
                 const u64 g = (((c + 1) << (t + 1)) - 1) + (ch - fl1);
-                const int best = child_domain(from, (int)ds, plane, ch == 2 * sn + 1, (int)k, a.boxes + g * 2 * (u64)k);
+                const int best =
+                    child_domain(from, (int)ds, plane_of[i], ch == 2 * sn + 1, (int)k, a.boxes + g * 2 * (u64)k);
                 sh.nodedim[ch] = (uint16_t)best;
                 if (a.dims_out) a.dims_out[g] = best;
             }
@@ -3336,9 +3376,10 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_widest_cols(WidestSu
     // then perm and the tree rows, a level's nodes being the contiguous
     // global range (c << level) + node.
     u32* idx_of = s.exch[0];
+    const u32 slot0 = opaque((u32)local_slot(0));
 #pragma unroll
     for (int j = 0; j < kLocalItems; ++j) {
-        const u32 e = (u32)local_slot(j);
+        const u32 e = slot0 + 64u * j;
         if (e < nc) idx_of[sh.c.tag[e]] = rows ? sh.arr[e] : key(sh.arr[e], k);
     }
     __syncthreads();
