@@ -2812,12 +2812,24 @@ struct WidestSubtreeArgs {
 // dimension d that some level-t node splits, in turn, the slots of the
 // points whose node splits d, in the order of d. Each node's points are then
 // in its own dimension's order, and one round over the list ranks them all.
-// Returns the list's length (uniform).
+// A first pass looks up each slot's node dimension once (0xff: no point of
+// level t), in exch[0], so that each dimension's pass makes one gather an
+// item. Returns the list's length (uniform).
 __device__ __forceinline__ u32 rec_live_list(RecShared& sh, const uint8_t* nodedim, u32 used, int t, int dims,
                                              uint16_t* list) {
     RecScratch& s = sh.m.s;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const u32 fl = (1u << t) - 1, segs = 1u << t;
+    uint8_t* sdim = reinterpret_cast<uint8_t*>(&s.exch[0][0]);
+#pragma unroll
+    for (int j = 0; j < kLocalItems; ++j) {
+        const u32 e = (u32)local_slot(j);
+        const u32 st = sh.m.tag[e];  // (padding: kPadTag, on no level)
+        const bool on = st - fl < segs;
+        const uint8_t nd = nodedim[on ? st : 0u];
+        sdim[e] = on ? nd : (uint8_t)0xff;
+    }
+    __syncthreads();
     u32 base = 0;
     for (int d = 0; d < dims; ++d) {
         if (!((used >> d) & 1u)) continue;
@@ -2828,9 +2840,7 @@ __device__ __forceinline__ u32 rec_live_list(RecShared& sh, const uint8_t* noded
         for (int j = 0; j < kLocalItems; ++j) e[j] = sh.m.order[d][local_slot(j)];
 #pragma unroll
         for (int j = 0; j < kLocalItems; ++j) {
-            const u32 st = sh.m.tag[e[j]];  // (padding: kPadTag, on no level)
-            const bool on = st - fl < segs && nodedim[st] == (uint8_t)d;
-            keep[j] = __ballot(on);
+            keep[j] = __ballot(sdim[e[j]] == (uint8_t)d);
             wave_total += (u32)__popcll(keep[j]);
         }
         if (lane == 0) s.wave[w] = wave_total;
@@ -2842,9 +2852,12 @@ __device__ __forceinline__ u32 rec_live_list(RecShared& sh, const uint8_t* noded
             at += v < w ? c : 0u;
             total += c;
         }
+        // (items not kept write to a dummy: no branch an item)
 #pragma unroll
         for (int j = 0; j < kLocalItems; ++j) {
-            if ((keep[j] >> lane) & 1u) list[at + lanes_below((u32)keep[j], (u32)(keep[j] >> 32))] = (uint16_t)e[j];
+            const bool kept = (keep[j] >> lane) & 1u;
+            uint16_t* to = kept ? &list[at + lanes_below((u32)keep[j], (u32)(keep[j] >> 32))] : &s.dummy[lane];
+            *to = (uint16_t)e[j];
             at += (u32)__popcll(keep[j]);
         }
         base += total;
@@ -3154,6 +3167,7 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_widest(WidestSubtree
             plane_of[sn - fl] = __uint_as_float(key_bits(pkey));
         }
         __syncthreads();
+        u32 split_bits = 0;  // dimensions this thread's children split
         for (u32 i = threadIdx.x; i < nodes; i += kLocalBlock) {
             const u32 sn = fl + i;
             if (2 * sn + 1 >= nc) break;  // a leaf, as is every later node of the level
@@ -3189,10 +3203,15 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_widest(WidestSubtree
                     }
                 }
                 wsh.nodedim[ch] = (uint8_t)best;
-                atomicOr(&wsh.dim_mask[(t + 1) & 1], 1u << best);
+                split_bits |= 1u << best;
                 if (a.dims_out) a.dims_out[g] = best;
             }
         }
+        // one LDS atomic a wave
+        u32 wave_bits = 0;
+#pragma unroll
+        for (int d = 0; d < kK; ++d) wave_bits |= __ballot((split_bits >> d) & 1u) != 0 ? 1u << d : 0u;
+        if ((threadIdx.x & 63) == 0 && wave_bits) atomicOr(&wsh.dim_mask[(t + 1) & 1], wave_bits);
         __syncthreads();
     }
 
