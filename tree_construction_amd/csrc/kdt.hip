@@ -2869,11 +2869,15 @@ __device__ __forceinline__ u32 rec_live_list(RecShared& sh, const uint8_t* noded
 // Round t over such a list of n_live slots, as rec_round with every listed
 // point live. Per-wave segment counters of type Count (16-bit, or 8-bit on
 // levels whose segments hold at most 255 points) in exch[0].
-template <typename Count>
-__device__ __forceinline__ void rec_round_list(const uint16_t* list, u32 n_live, int t, const Geometry& lg,
-                                               RecShared& sh) {
+// kT >= 0: the round index as a compile-time constant (t_rt unused), so that
+// the t-bit ballot match unrolls.
+template <int kT, typename Count>
+__device__ __forceinline__ void rec_round_list_at(const uint16_t* list, u32 n_live, int t_rt, const Geometry& lg,
+                                                  RecShared& sh) {
+    const int t = kT >= 0 ? kT : t_rt;
     RecScratch& s = sh.m.s;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // (thread-derived offsets recomputed a call, not held across the level loop)
+    const int tid = (int)opaque(threadIdx.x), lane = tid & 63, w = tid >> 6;
     const u32 fl = (1u << t) - 1, segs = 1u << t;
     constexpr u32 kPer = 4 / sizeof(Count);  // counters a word
     Count* cnt = reinterpret_cast<Count*>(&s.exch[0][0]);  // [kLocalWaves][segs]
@@ -2940,6 +2944,20 @@ __device__ __forceinline__ void rec_round_list(const uint16_t* list, u32 n_live,
         sh.m.tag[e[j]] = (uint16_t)next;
     }
     __syncthreads();
+}
+
+template <typename Count>
+__device__ __forceinline__ void rec_round_list(const uint16_t* list, u32 n_live, int t, const Geometry& lg,
+                                               RecShared& sh) {
+    switch (t) {  // every round of a kLocalMax-point subtree: t <= kLocalRounds - 1
+#define KDT_LIST_ROUND_CASE(T) \
+    case T: rec_round_list_at<T, Count>(list, n_live, t, lg, sh); break;
+        KDT_LIST_ROUND_CASE(0) KDT_LIST_ROUND_CASE(1) KDT_LIST_ROUND_CASE(2) KDT_LIST_ROUND_CASE(3)
+        KDT_LIST_ROUND_CASE(4) KDT_LIST_ROUND_CASE(5) KDT_LIST_ROUND_CASE(6) KDT_LIST_ROUND_CASE(7)
+        KDT_LIST_ROUND_CASE(8) KDT_LIST_ROUND_CASE(9) KDT_LIST_ROUND_CASE(10) KDT_LIST_ROUND_CASE(11)
+#undef KDT_LIST_ROUND_CASE
+        default: rec_round_list_at<-1, Count>(list, n_live, t, lg, sh); break;
+    }
 }
 
 struct WidestRecShared {
