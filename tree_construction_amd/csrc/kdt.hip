@@ -2271,7 +2271,8 @@ template <int kT, typename Count, typename S>
 __device__ __forceinline__ void rec_round_at(const uint16_t* order, int t_rt, const Geometry& lg, uint16_t* tag,
                                              S& s, const uint8_t* nodedim, u32 d) {
     const int t = kT >= 0 ? kT : t_rt;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // (thread-derived offsets recomputed a call, not held across the level loop)
+    const int tid = (int)opaque(threadIdx.x), lane = tid & 63, w = tid >> 6;
     const u32 fl = (1u << t) - 1, segs = 1u << t;
     Count* cnt = reinterpret_cast<Count*>(&s.exch[0][0]);  // [kLocalWaves][segs]
     u32* cnt_words = &s.exch[0][0];
