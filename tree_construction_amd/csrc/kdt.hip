@@ -1628,6 +1628,66 @@ __global__ __launch_bounds__(kBlock) void k_pivots(const u32* __restrict__ recs,
         for (int d = 0; d < k; ++d) tree[s * k + d] = pts[(u64)idx * k + d];
 }
 
+// Rounds by per-point tags (every round splits a new dimension, k >= R, and
+// records of every coordinate above it would be wide): each point keeps the
+// node it is in as a 32-bit tag, in index order, with kFixedTag set once it
+// is its node's pivot. Round l brings every tag from level l-1 to level l
+// (the point against its node's pivot by (key, index) in dimension l-1: the
+// left child below it, the right one above), then writes the point's record
+// for the round's sort: (key in dimension l, node offset on level l, index),
+// a fixed point's node offset ~0 so that it sorts after every live one
+// ([W], tag paragraph: the tag is the node; sort order paragraph).
+constexpr u32 kFixedTag = 0x80000000u;
+
+__device__ __forceinline__ u32 tag_descend(u32 t, u32 key, u32 p, const u64* __restrict__ piv) {
+    if (t & kFixedTag) return t;
+    const u64 me = ((u64)key << 32) | p, pv = piv[t];
+    return me == pv ? (t | kFixedTag) : (me < pv ? 2 * t + 1 : 2 * t + 2);
+}
+
+__global__ __launch_bounds__(kBlock) void k_tag_level(i64 n, int l, const u32* __restrict__ planar0,
+                                                      const u64* __restrict__ piv, u32* __restrict__ tags,
+                                                      u32* __restrict__ recs) {
+    const i64 stride = (i64)gridDim.x * kBlock;
+    const u32 fl = (u32)full_nodes(l);
+    for (i64 p = (i64)blockIdx.x * kBlock + threadIdx.x; p < n; p += stride) {
+        u32 t = 0;
+        if (l > 0) t = tag_descend(tags[p], planar0[(u64)(l - 1) * (u64)n + p], (u32)p, piv);
+        tags[p] = t;
+        // (every record keeps its key: the first pass's digits come from it)
+        recs[3 * p] = planar0[(u64)l * (u64)n + p];
+        recs[3 * p + 1] = t & kFixedTag ? ~0u : t - fl;
+        recs[3 * p + 2] = (u32)p;
+    }
+}
+
+// After the last global round R-1: each point's records for the subtree
+// stage, (position key, index), with the position key placing it where the
+// stage looks for it, in round R-1's order of the points live on level R-1:
+// node P of that level contributes its left child's points (3 (P - F(R-1))),
+// its pivot (+1), then its right child's points (+2); points fixed before
+// level R-1 sort last. Also the first sort pass's digit (the key's low byte).
+__global__ __launch_bounds__(kBlock) void k_tag_subtrees(i64 n, int R, const u32* __restrict__ planar0,
+                                                         const u64* __restrict__ piv, const u32* __restrict__ tags,
+                                                         u32* __restrict__ recs, u8* __restrict__ digits) {
+    const i64 stride = (i64)gridDim.x * kBlock;
+    const u32 fp = (u32)full_nodes(R - 1), fp1 = (u32)full_nodes(R);
+    for (i64 p = (i64)blockIdx.x * kBlock + threadIdx.x; p < n; p += stride) {
+        const u32 t = tag_descend(tags[p], planar0[(u64)(R - 1) * (u64)n + p], (u32)p, piv);
+        u32 key;
+        if (t & kFixedTag) {
+            const u32 node = t & ~kFixedTag;
+            key = node >= fp && node < fp1 ? 3 * (node - fp) + 1 : ~0u;
+        } else {
+            const u32 parent = (t - 1) / 2;
+            key = 3 * (parent - fp) + (t == 2 * parent + 1 ? 0u : 2u);
+        }
+        recs[2 * p] = key;
+        recs[2 * p + 1] = (u32)p;
+        digits[p] = (u8)key;
+    }
+}
+
 // Tags after `rounds` rounds by walking the pivots from the root (the node
 // the point reaches, or the node it became): diagnostics only.
 __global__ __launch_bounds__(kBlock) void k_descend_tags(const float* __restrict__ pts, i64 n,
@@ -2030,6 +2090,8 @@ struct SubtreeArgs {
     const u32* recs;        // l0 > 0: records (coordinates 0 .. words-2, then the
     int words;              // index) live on level l0-1, in round l0-1's order
     u64 plane;              // their plane stride (records wider than kWholeWords)
+    bool index_only;        // the records' last word is the index and they carry no
+                            // coordinate (their order: by index within each subtree)
     u32* stage;             // 1 + min(k, kLocalRounds) columns of n words: the index, then
                             // the key column of each dimension the local rounds split, by
                             // round (dimension (l0 + u) mod k in column u + 1); the subtree
@@ -2599,8 +2661,9 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_cols(SubtreeArgs a) 
         first = c == 2 * parent + 1 ? seg : seg + subtree_size(a.geo, 2 * parent + 1) + 1;
     }
     auto rec = [&](u32 q, int f) -> u32 { return a.recs[rec_word_index(a.words, a.plane, first + q, f)]; };
-    const int kr = a.recs ? a.words - 1 : 0;  // coordinates the records carry
-    const int d_a = a.recs ? (a.l0 - 1) % a.k : -1;  // the arrival order is (coordinate d_a, index)
+    const int kr = a.recs && !a.index_only ? a.words - 1 : 0;  // coordinates the records carry
+    // the arrival order is (coordinate d_a, index)
+    const int d_a = a.recs && !a.index_only ? (a.l0 - 1) % a.k : -1;
     const Geometry lg = make_geometry((i64)nc);
     const int rounds = lg.levels - 1;
     const int used = rounds < a.k ? rounds : a.k;  // dimensions (l0 + t) mod k, t < used, differ
@@ -2675,8 +2738,9 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_cols(SubtreeArgs a) 
     }
     // kr = min(k, l0) and d0 = l0 mod k: below k global rounds kr = d0, and
     // the used dimensions from d0 to k-1 come from the rows, the wrapped
-    // ones (below kr) from the records
-    const int nr = kr == a.k ? 0 : (used < a.k - d0 ? used : a.k - d0);
+    // ones (below kr) from the records; records of the index alone: every
+    // used dimension from the rows, wrapping past k-1 to 0
+    const int nr = kr == a.k ? 0 : (kr == 0 ? used : (used < a.k - d0 ? used : a.k - d0));
     for (int u = nr, d = (d0 + nr) % a.k; u < used; ++u, d = d + 1 == a.k ? 0 : d + 1) {
         if (d == d_a) {
 #pragma unroll
@@ -2694,10 +2758,12 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_cols(SubtreeArgs a) 
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const bool ok = (u32)local_slot(j0 + h) < nc;
-                const float* row = a.pts + (u64)idx[j0 + h] * (u64)a.k + d0;
+                const float* row = a.pts + (u64)idx[j0 + h] * (u64)a.k;
 #pragma unroll
-                for (int i = 0; i < kLocalRounds; ++i)
-                    key[h][i] = ok && i < nr ? float_key(__float_as_uint(row[i])) : 0u;
+                for (int i = 0; i < kLocalRounds; ++i) {
+                    const int dd = d0 + i < a.k ? d0 + i : d0 + i - a.k;
+                    key[h][i] = ok && i < nr ? float_key(__float_as_uint(row[dd])) : 0u;
+                }
             }
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -3461,12 +3527,18 @@ struct Layout {
     int nbuf;            // record arrays
     i64 tiles;           // of a pass over all n points
     size_t tmp0, tmp1, digits, digits0, recs, piv, totals, slots, chunk_slots, stage, total;
+    size_t tags;         // rounds by per-point tags (tag_rounds): a tag of each point
     size_t planar0;      // records wider than kWholeWords: all of them in index order, planar
 };
 
 // Whether the subtree stage after `rounds` global rounds reads records that
 // carry every coordinate (k_subtree_recs) rather than staging columns.
 inline bool stage_from_records(int k, int rounds) { return rounds > 0 && k <= rounds && k <= kCachedDims; }
+
+// Whether a build's global rounds run by per-point tags (run_global_tags):
+// every round splits a new dimension (k >= rounds) and there are at least
+// four of them (the planar copy of the rounds' keys exists).
+inline bool tag_rounds(int k, int rounds) { return rounds >= 4 && k >= rounds && k > kCachedDims; }
 
 // Workspace of `rounds` global rounds and, with `stage`, of the subtree stage.
 bool make_layout(i64 n, int k, int rounds, bool stage, Layout* out) {
@@ -3509,6 +3581,7 @@ bool make_layout(i64 n, int k, int rounds, bool stage, Layout* out) {
     // the columns stage's: the index and at most kLocalRounds key columns
     // (none where the records carry every coordinate)
     if (stage && !stage_from_records(k, rounds)) lay.stage = take((size_t)(1 + (k < kLocalRounds ? k : kLocalRounds)) * n * sizeof(u32));
+    if (stage && tag_rounds(k, rounds)) lay.tags = take((size_t)n * sizeof(u32));
     lay.total = off;
     *out = lay;
     return true;
@@ -4069,6 +4142,84 @@ bool make_layout_unique(i64 n, int k, UniqueLayout* out) {
     return true;
 }
 
+// Global rounds 0 .. R-1 by per-point tags (tag_rounds: every round splits a
+// new dimension). Round l sorts every point by (node on level l, key in
+// dimension l, index): stable LSD passes from index order, four over the key
+// and then over the node offset, so the index breaks the ties; each node's
+// pivot then sits at its closed-form position (k_pivots). Records are three
+// words whatever k is, where per-dimension arrays would carry the keys of
+// every dimension a round above walks. After the last round the points are
+// sorted into round R-1's order for the subtree stage: *last holds two-word
+// records (position key, index), the index alone for the stage to read.
+kdt_status run_global_tags(const float* pts, i64 n, int k, const Layout& lay, char* ws,
+                           hipStream_t stream, Timer timer, int32_t* perm, float* tree,
+                           const u32** last) {
+    const int R = lay.rounds;
+    const Geometry geo = make_geometry(n);
+    u32* tmp[2] = {(u32*)(ws + lay.tmp0), (u32*)(ws + lay.tmp1)};
+    u8* digits = (u8*)(ws + lay.digits);
+    u8* digits0 = (u8*)(ws + lay.digits0);
+    u64* piv = (u64*)(ws + lay.piv);
+    u32* tags = (u32*)(ws + lay.tags);
+    u32* planar0 = (u32*)(ws + lay.planar0);
+    u32* recs0 = (u32*)(ws + lay.recs);
+    u32* recs1 = recs0 + (size_t)n * lay.words;  // (two buffers of lay.words-word records)
+    Launcher launch{(u32*)(ws + lay.slots), (u32*)(ws + lay.chunk_slots), (u32*)(ws + lay.totals),
+                    stream, timer};
+    const unsigned grid = grid_for(n, kBlock, 1 << 16);
+    timer.begin("k_planar_records", (double)n * (4.0 * k + 4.0 * lay.words + lay.kr));
+    k_planar_records<<<grid, kBlock, 0, stream>>>(pts, n, k, lay.words, planar0, digits0);
+    timer.end();
+    // one sort pass: word `word`, byte `byte` of the records, the next
+    // pass's digit from (next_word, next_byte) (none: next_word < 0)
+    auto pass = [&](const u32* in, int words, u32* out, int word, int byte, const u8* dig, int next_word,
+                    int next_byte) {
+        SortArgs a{};
+        a.src = RecordSource{pts, k, in, words, n, (u64)n, false};
+        a.out = out;
+        a.dim = word;
+        a.shift = 8 * byte;
+        a.digits = dig;
+        a.next_digits = next_word >= 0 ? digits : nullptr;
+        a.next_dim = next_word >= 0 ? next_word : 0;
+        a.next_shift = 8 * (next_byte >= 0 ? next_byte : 0);
+        launch.sort_any<kSrcRecords>(a);
+    };
+    for (int l = 0; l < R; ++l) {
+        timer.begin("k_tag_level", (double)n * (l > 0 ? 16.0 : 4.0) + 12.0 * n + (l > 0 ? 8.0 * full_nodes(l) : 0));
+        k_tag_level<<<grid, kBlock, 0, stream>>>(n, l, planar0, piv, tags, recs0);
+        timer.end();
+        // four key bytes, then the node offset's bytes (offsets below 2^l;
+        // a fixed point's ~0 must compare above them: (l + 8) / 8 bytes)
+        const int node_bytes = l == 0 ? 0 : (l + 8) / 8, passes = 4 + node_bytes;
+        const u32* in = recs0;
+        for (int q = 0; q < passes; ++q) {
+            u32* out = tmp[q & 1];
+            const int nq = q + 1;
+            pass(in, 3, out, q < 4 ? 0 : 1, q < 4 ? q : q - 4, q == 0 ? digits0 + (size_t)l * n : digits,
+                 nq < passes ? (nq < 4 ? 0 : 1) : -1, nq < 4 ? nq : nq - 4);
+            in = out;
+        }
+        timer.begin("k_pivots", (double)(1ull << l) * (12.0 + 8 + (perm ? 4 : 0) + (tree ? 8.0 * k : 0)));
+        k_pivots<<<(unsigned)(((1ull << l) + kBlock - 1) / kBlock), kBlock, 0, stream>>>(
+            in, 3, (u64)n, geo, l, 0, piv, pts, k, perm, tree, nullptr);
+        timer.end();
+    }
+    timer.begin("k_tag_subtrees", (double)n * (4.0 + 4 + 8 + 1) + 8.0 * full_nodes(R));
+    k_tag_subtrees<<<grid, kBlock, 0, stream>>>(n, R, planar0, piv, tags, recs0, digits);
+    timer.end();
+    // position keys below 3 * 2^(R-1) < 2^(R+1), ~0 above them
+    const int key_bytes = (R + 1 + 7) / 8;
+    const u32* in = recs0;
+    for (int q = 0; q < key_bytes; ++q) {
+        u32* out = q == key_bytes - 1 ? recs1 : tmp[q & 1];
+        pass(in, 2, out, 0, q, digits, q + 1 < key_bytes ? 0 : -1, q + 1);
+        in = out;
+    }
+    *last = recs1;
+    return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
+}
+
 // Duplicate removal: the points' (tuple hash, index) records sorted by hash
 // with 4 stable LSD radix passes (equal tuples then sit together, in index
 // order), the run heads with exact comparisons inside equal-hash runs, then
@@ -4365,9 +4516,10 @@ kdt_status build_impl(const float* points, int64_t N, int32_t k, int32_t* perm_o
     }
     const Geometry geo = make_geometry(N);
     const u32* recs = nullptr;
+    const bool by_tags = tag_rounds(k, l0);
     if (l0 > 0) {
-        st = run_global(points, N, k, lay, (char*)workspace, stream, timer, perm_out, tree_out,
-                        &recs);
+        st = by_tags ? run_global_tags(points, N, k, lay, (char*)workspace, stream, timer, perm_out, tree_out, &recs)
+                     : run_global(points, N, k, lay, (char*)workspace, stream, timer, perm_out, tree_out, &recs);
         if (st != KDT_OK) return st;
     }
     SubtreeArgs sa{};
@@ -4377,7 +4529,8 @@ kdt_status build_impl(const float* points, int64_t N, int32_t k, int32_t* perm_o
     sa.l0 = l0;
     sa.geo = geo;
     sa.recs = recs;
-    sa.words = lay.words;
+    sa.words = by_tags ? 2 : lay.words;
+    sa.index_only = by_tags;
     sa.plane = (u64)N;
     // records that carry every coordinate (then lay.words == k + 1) are read
     // in place, else staged
