@@ -1634,7 +1634,7 @@ __global__ __launch_bounds__(kBlock) void k_pivots(const u32* __restrict__ recs,
 // is its node's pivot. Round l brings every tag from level l-1 to level l
 // (the point against its node's pivot by (key, index) in dimension l-1: the
 // left child below it, the right one above), then writes the point's record
-// for the round's sort: (key in dimension l, node offset on level l, index),
+// for the round's sort: (key in dimension l, node offset on level l, 0, index),
 // a fixed point's node offset ~0 so that it sorts after every live one
 // ([W], tag paragraph: the tag is the node; sort order paragraph).
 constexpr u32 kFixedTag = 0x80000000u;
@@ -1654,10 +1654,10 @@ __global__ __launch_bounds__(kBlock) void k_tag_level(i64 n, int l, const u32* _
         u32 t = 0;
         if (l > 0) t = tag_descend(tags[p], planar0[(u64)(l - 1) * (u64)n + p], (u32)p, piv);
         tags[p] = t;
-        // (every record keeps its key: the first pass's digits come from it)
-        recs[3 * p] = planar0[(u64)l * (u64)n + p];
-        recs[3 * p + 1] = t & kFixedTag ? ~0u : t - fl;
-        recs[3 * p + 2] = (u32)p;
+        // (every record keeps its key: the first pass's digits come from it;
+        // word 2 is padding, so that a record is one 16-byte access)
+        reinterpret_cast<uint4*>(recs)[p] =
+            make_uint4(planar0[(u64)l * (u64)n + p], t & kFixedTag ? ~0u : t - fl, 0u, (u32)p);
     }
 }
 
@@ -4146,8 +4146,8 @@ bool make_layout_unique(i64 n, int k, UniqueLayout* out) {
 // new dimension). Round l sorts every point by (node on level l, key in
 // dimension l, index): stable LSD passes from index order, four over the key
 // and then over the node offset, so the index breaks the ties; each node's
-// pivot then sits at its closed-form position (k_pivots). Records are three
-// words whatever k is, where per-dimension arrays would carry the keys of
+// pivot then sits at its closed-form position (k_pivots). Records are four
+// words (one vector access) whatever k is, where per-dimension arrays would carry the keys of
 // every dimension a round above walks. After the last round the points are
 // sorted into round R-1's order for the subtree stage: *last holds two-word
 // records (position key, index), the index alone for the stage to read.
@@ -4186,7 +4186,8 @@ kdt_status run_global_tags(const float* pts, i64 n, int k, const Layout& lay, ch
         launch.sort_any<kSrcRecords>(a);
     };
     for (int l = 0; l < R; ++l) {
-        timer.begin("k_tag_level", (double)n * (l > 0 ? 16.0 : 4.0) + 12.0 * n + (l > 0 ? 8.0 * full_nodes(l) : 0));
+        // tags and two keys in (one key on level 0), tags and records out
+        timer.begin("k_tag_level", (double)n * (l > 0 ? 32.0 : 24.0) + (l > 0 ? 8.0 * full_nodes(l) : 0));
         k_tag_level<<<grid, kBlock, 0, stream>>>(n, l, planar0, piv, tags, recs0);
         timer.end();
         // four key bytes, then the node offset's bytes (offsets below 2^l;
@@ -4196,13 +4197,13 @@ kdt_status run_global_tags(const float* pts, i64 n, int k, const Layout& lay, ch
         for (int q = 0; q < passes; ++q) {
             u32* out = tmp[q & 1];
             const int nq = q + 1;
-            pass(in, 3, out, q < 4 ? 0 : 1, q < 4 ? q : q - 4, q == 0 ? digits0 + (size_t)l * n : digits,
+            pass(in, 4, out, q < 4 ? 0 : 1, q < 4 ? q : q - 4, q == 0 ? digits0 + (size_t)l * n : digits,
                  nq < passes ? (nq < 4 ? 0 : 1) : -1, nq < 4 ? nq : nq - 4);
             in = out;
         }
         timer.begin("k_pivots", (double)(1ull << l) * (12.0 + 8 + (perm ? 4 : 0) + (tree ? 8.0 * k : 0)));
         k_pivots<<<(unsigned)(((1ull << l) + kBlock - 1) / kBlock), kBlock, 0, stream>>>(
-            in, 3, (u64)n, geo, l, 0, piv, pts, k, perm, tree, nullptr);
+            in, 4, (u64)n, geo, l, 0, piv, pts, k, perm, tree, nullptr);
         timer.end();
     }
     timer.begin("k_tag_subtrees", (double)n * (4.0 + 4 + 8 + 1) + 8.0 * full_nodes(R));
