@@ -2091,7 +2091,7 @@ struct SubtreeArgs {
     int words;              // index) live on level l0-1, in round l0-1's order
     u64 plane;              // their plane stride (records wider than kWholeWords)
     bool index_only;        // the records' last word is the index and they carry no
-                            // coordinate (their order: by index within each subtree)
+                            // coordinate; each subtree's arrive in index order
     u32* stage;             // 1 + min(k, kLocalRounds) columns of n words: the index, then
                             // the key column of each dimension the local rounds split, by
                             // round (dimension (l0 + u) mod k in column u + 1); the subtree
@@ -2675,10 +2675,11 @@ __global__ __launch_bounds__(kLocalBlock, 4) void k_subtree_cols(SubtreeArgs a) 
     // Slot = index rank: sort (index - min, arrival position). arr[j] is the
     // arrival position of slot local_slot(j); the padding positions (q >= nc)
     // sort last, in order, so that slot e >= nc holds arrival position e.
+    // Index-only records arrive by index: slot = arrival.
     u32 arr[kLocalItems];
 #pragma unroll
     for (int j = 0; j < kLocalItems; ++j) arr[j] = (u32)local_slot(j);
-    if (a.recs) {
+    if (a.recs && !a.index_only) {
         u32 v[kLocalItems], mn[1] = {~0u}, mx[1] = {0u};
 #pragma unroll
         for (int j = 0; j < kLocalItems; ++j) {
