@@ -122,12 +122,29 @@ def test_columns_stage_dimension_mix(torch_dev, n, k):
     split: from the records where a global round carried them, as the run of
     each row from l0 mod k otherwise, and, for the dimension the points
     arrived sorted by, as arrival positions. These sizes (l0 = 5, 7, 9) give
-    every mix: all from the records with the arrived dimension reused (k = 4,
-    5), a row run plus wrapped record dimensions with it (k = 9), rows and
-    records without it (k = 12, 13, 16), and rows only (k = 20, 33)."""
+    all from the records with the arrived dimension reused (k = 4, 5); with
+    k >= l0 the global rounds run by per-point tags and the stage reads
+    index-only records and every dimension from the rows, wrapping past k-1
+    where its rounds outnumber the dimensions left (k = 9, 12, 13, 16, 20,
+    33)."""
     for gen in ("gmm", "ties"):
         pts = make(gen, n, k, 90 + k)
         say("case columns stage gen=%s N=%d k=%d" % (gen, n, k))
+        perm, tree = gpu_build(torch_dev, pts)
+        assert_same_tree(pts, perm, tree, oracle.build_tree(pts), "%s N=%d k=%d" % (gen, n, k))
+
+
+@pytest.mark.parametrize("n,k", [(65536, 4), (65536, 5), (300000, 7), (300000, 8), (1100000, 9),
+                                 (1100000, 10), (12289, 5), (32768, 6)])
+def test_tag_rounds_boundaries(torch_dev, n, k):
+    """Global rounds by per-point tags need k >= l0 >= 4 and k > 3: these
+    sizes put k at l0 (4, 7, 9 global rounds) and one above it, where round 8
+    sorts two bytes of node offset (1,100,000 points), against the per-array
+    rounds just outside the condition (12,289 points: 2 global rounds;
+    32,768: 3), with ties, signed zeros and duplicates."""
+    for gen in ("ties", "zeros", "gmm"):
+        pts = make(gen, n, k, 700 + n % 89 + k)
+        say("case tag rounds gen=%s N=%d k=%d" % (gen, n, k))
         perm, tree = gpu_build(torch_dev, pts)
         assert_same_tree(pts, perm, tree, oracle.build_tree(pts), "%s N=%d k=%d" % (gen, n, k))
 
