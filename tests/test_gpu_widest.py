@@ -89,7 +89,8 @@ def test_widest_lds_stage(torch_dev, k):
     """Subtrees of at most 4096 points finish in LDS: one subtree read from
     the rows (N <= 4096) or records on levels 1 .. 7 below the global
     levels, with every kind of tie. k <= 3 keeps every dimension's order
-    there; wider points sort each level by their nodes' own dimensions."""
+    there; wider points sort each level by their nodes' own dimensions. For
+    k = 8 and 16 the global levels run by per-point tags."""
     for gen in ("gmm", "ties", "zeros", "equal", "skewed"):
         for n in (4095, 4096, 4097, 12289, 300000):
             pts = make(gen, n, k, 900 + n % 97 + k)
@@ -98,10 +99,11 @@ def test_widest_lds_stage(torch_dev, k):
             assert_same(pts, perm, tree, dims, "%s N=%d k=%d" % (gen, n, k))
 
 
-@pytest.mark.parametrize("k", [1, 2, 5])
+@pytest.mark.parametrize("k", [1, 2, 5, 8])
 def test_widest_4m(torch_dev, k):
-    """4,194,304 points: 10 global levels with selects and skipped selects,
-    then the LDS stage."""
+    """4,194,304 points: 10 global levels (with selects and skipped selects
+    over per-dimension arrays, or by per-point tags for k = 8), then the LDS
+    stage."""
     pts = make("gmm", 1 << 22, k, 90 + k)
     say("case widest gen=gmm N=4194304 k=%d" % k)
     perm, tree, dims = gpu_widest(torch_dev, pts)

@@ -1688,6 +1688,63 @@ __global__ __launch_bounds__(kBlock) void k_tag_subtrees(i64 n, int R, const u32
     }
 }
 
+// Split-widest rounds by per-point tags: as above, with each point's key
+// read from the plane of its node's split dimension (the node table), so a
+// round costs the same whatever k is; the record pass also writes the first
+// sort pass's digit, the planes differing from point to point.
+__global__ __launch_bounds__(kBlock) void k_wtag_level(i64 n, int l, const u32* __restrict__ planar0,
+                                                       const u64* __restrict__ piv,
+                                                       const uint16_t* __restrict__ dimtab, u32* __restrict__ tags,
+                                                       u32* __restrict__ recs, u8* __restrict__ digits) {
+    const i64 stride = (i64)gridDim.x * kBlock;
+    const u32 fl = (u32)full_nodes(l);
+    for (i64 p = (i64)blockIdx.x * kBlock + threadIdx.x; p < n; p += stride) {
+        u32 t = 0;
+        if (l > 0) {
+            t = tags[p];
+            if (!(t & kFixedTag)) t = tag_descend(t, planar0[(u64)dimtab[t] * (u64)n + p], (u32)p, piv);
+        }
+        tags[p] = t;
+        const bool fixed = t & kFixedTag;
+        const u32 key = planar0[(u64)(fixed ? 0u : dimtab[t]) * (u64)n + p];
+        reinterpret_cast<uint4*>(recs)[p] = make_uint4(key, fixed ? ~0u : t - fl, 0u, (u32)p);
+        digits[p] = (u8)key;
+    }
+}
+
+// After the last global level l0 - 1 of a split-widest build: each point's
+// node offset on level l0 (~0 for a fixed point) as two-word records
+// (offset, index), with the first sort pass's digit.
+__global__ __launch_bounds__(kBlock) void k_wtag_subtrees(i64 n, int l0, const u32* __restrict__ planar0,
+                                                          const u64* __restrict__ piv,
+                                                          const uint16_t* __restrict__ dimtab,
+                                                          const u32* __restrict__ tags, u32* __restrict__ recs,
+                                                          u8* __restrict__ digits) {
+    const i64 stride = (i64)gridDim.x * kBlock;
+    const u32 fl = (u32)full_nodes(l0);
+    for (i64 p = (i64)blockIdx.x * kBlock + threadIdx.x; p < n; p += stride) {
+        u32 t = tags[p];
+        if (!(t & kFixedTag)) t = tag_descend(t, planar0[(u64)dimtab[t] * (u64)n + p], (u32)p, piv);
+        const u32 off = t & kFixedTag ? ~0u : t - fl;
+        reinterpret_cast<uint2*>(recs)[p] = make_uint2(off, (u32)p);
+        digits[p] = (u8)off;
+    }
+}
+
+// The subtree stage's planar records (k keys, then the index) of the points
+// live on level l0, in their sorted order (subtree by subtree, each in index
+// order), from each point's row.
+__global__ __launch_bounds__(kBlock) void k_wtag_planar(i64 live, i64 n, int k, const float* __restrict__ pts,
+                                                        const u32* __restrict__ sorted, u32* __restrict__ out) {
+    const i64 stride = (i64)gridDim.x * kBlock;
+    for (i64 q = (i64)blockIdx.x * kBlock + threadIdx.x; q < live; q += stride) {
+        const u32 idx = sorted[2 * q + 1];
+        const u32* row = reinterpret_cast<const u32*>(pts) + (u64)idx * k;
+        for (int d = 0; d < k; ++d) out[(u64)d * (u64)n + q] = float_key(row[d]);
+        out[(u64)k * (u64)n + q] = idx;
+    }
+}
+
 // Tags after `rounds` rounds by walking the pivots from the root (the node
 // the point reaches, or the node it became): diagnostics only.
 __global__ __launch_bounds__(kBlock) void k_descend_tags(const float* __restrict__ pts, i64 n,
@@ -3588,16 +3645,27 @@ bool make_layout(i64 n, int k, int rounds, bool stage, Layout* out) {
     return true;
 }
 
-// Workspace of a split-widest build: every level is a global round (its
-// nodes' dimensions differ, so no subtree finishes in LDS), every dimension
-// keeps an array, and each node has a domain and a split dimension.
+// Workspace of a split-widest build: every dimension keeps an array through
+// the global levels (or, with tags, the points' tags and one array of
+// 16-byte records), the subtree stage reads A_0's records, and each node has
+// a domain and a split dimension.
 constexpr i64 kBoxChunk = 1 << 14;  // points per partial bounding box (a multiple of 4)
 
 struct WidestLayout {
     Layout base;  // rounds = levels; records carry all k coordinates
     size_t boxes, dimtab, root_box, box_partial, level_dims;
     i64 box_chunks;
+    bool by_tags;  // global levels by per-point tags (widest_tag_rounds); base.tags their array
 };
+
+int split_level(i64 n);
+
+// Whether a split-widest build runs its global levels by per-point tags:
+// with k arrays every level costs a pass over each of them, with tags a
+// fixed number of passes over 16-byte records. On 4M normal points the tags
+// win from k = 4 on (3.49 -> 3.22 ms at k = 4, 4.38 -> 3.38 ms at k = 5);
+// k <= 3 keeps the arrays, whose LDS stage holds every dimension's order.
+inline bool widest_tag_rounds(i64 n, int k) { return k > kCachedDims && split_level(n) > 0; }
 
 bool make_layout_widest(i64 n, int k, WidestLayout* out) {
     if (n < 0 || n > INT32_MAX || k < 1 || k > 65535) return false;
@@ -3616,7 +3684,9 @@ bool make_layout_widest(i64 n, int k, WidestLayout* out) {
     lay.rounds = make_geometry(n).levels;
     lay.kr = k;
     lay.words = k + 1;
-    lay.nbuf = k + 1;
+    w.by_tags = widest_tag_rounds(n, k);
+    // tags: the rounds' records, then the subtree stage's planar records
+    lay.nbuf = w.by_tags ? 2 : k + 1;
     lay.tiles = (n + kPartTile - 1) / kPartTile;
     const size_t rec_bytes = (size_t)n * lay.words * sizeof(u32);
     lay.tmp0 = take(rec_bytes);
@@ -3635,6 +3705,7 @@ bool make_layout_widest(i64 n, int k, WidestLayout* out) {
     w.box_chunks = (n + kBoxChunk - 1) / kBoxChunk;
     w.box_partial = take((size_t)w.box_chunks * k * 2 * sizeof(float));
     w.level_dims = take((size_t)kMaxRounds * sizeof(u32));
+    if (w.by_tags) lay.tags = take((size_t)n * sizeof(u32));
     lay.total = off;
     *out = w;
     return true;
@@ -4360,6 +4431,69 @@ kdt_status run_widest(const float* pts, i64 n, int k, const WidestLayout& wl, ch
     };
     if (lds_from == 0) {  // the whole tree is one subtree, from the rows
         subtrees(nullptr);
+        return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
+    }
+    if (wl.by_tags) {
+        // Levels 0 .. lds_from-1 by per-point tags: each level sorts every
+        // point by (node, key in the node's split dimension, index) with
+        // stable LSD passes from index order and takes the pivots at their
+        // closed-form positions; then the points are sorted by their node on
+        // level lds_from and written as the stage's planar records.
+        u32* planar0 = (u32*)(ws + lay.planar0);
+        u32* tags = (u32*)(ws + lay.tags);
+        u32* recs0 = recs(0);
+        u32* recs1 = recs(1);
+        const unsigned grid = grid_for(n, kBlock, 1 << 16);
+        timer.begin("k_planar_records", (double)n * (4.0 * k + 4.0 * W + k));
+        k_planar_records<<<grid, kBlock, 0, stream>>>(pts, n, k, W, planar0, digits0);
+        timer.end();
+        auto pass = [&](const u32* in, int words, u32* out, int word, int byte, int next_word, int next_byte) {
+            SortArgs a{};
+            a.src = RecordSource{pts, k, in, words, n, (u64)n, false};
+            a.out = out;
+            a.dim = word;
+            a.shift = 8 * byte;
+            a.digits = digits;
+            a.next_digits = next_word >= 0 ? digits : nullptr;
+            a.next_dim = next_word >= 0 ? next_word : 0;
+            a.next_shift = 8 * (next_byte >= 0 ? next_byte : 0);
+            launch.sort_any<kSrcRecords>(a);
+        };
+        for (int l = 0; l < lds_from; ++l) {
+            timer.begin("k_wtag_level", (double)n * (l > 0 ? 33.0 : 25.0) + (l > 0 ? 10.0 * full_nodes(l) : 0));
+            k_wtag_level<<<grid, kBlock, 0, stream>>>(n, l, planar0, piv, dimtab, tags, recs0, digits);
+            timer.end();
+            const int node_bytes = l == 0 ? 0 : (l + 8) / 8, passes = 4 + node_bytes;
+            const u32* in = recs0;
+            for (int q = 0; q < passes; ++q) {
+                u32* out = tmp[q & 1];
+                const int nq = q + 1;
+                pass(in, 4, out, q < 4 ? 0 : 1, q < 4 ? q : q - 4, nq < passes ? (nq < 4 ? 0 : 1) : -1,
+                     nq < 4 ? nq : nq - 4);
+                in = out;
+            }
+            timer.begin("k_pivots", (double)(1ull << l) * (16.0 + 8 + (perm ? 4 : 0) + (tree ? 8.0 * k : 0)));
+            k_pivots<<<(unsigned)(((1ull << l) + kBlock - 1) / kBlock), kBlock, 0, stream>>>(
+                in, 4, (u64)n, geo, l, 0, piv, pts, k, perm, tree, nullptr);
+            timer.end();
+            level(l + 1);  // (lds_from < L)
+        }
+        timer.begin("k_wtag_subtrees", (double)n * (4.0 + 4 + 2 + 8 + 1));
+        k_wtag_subtrees<<<grid, kBlock, 0, stream>>>(n, lds_from, planar0, piv, dimtab, tags, recs0, digits);
+        timer.end();
+        // node offsets below 2^lds_from, ~0 above them
+        const int key_bytes = (lds_from + 8) / 8;
+        const u32* in = recs0;
+        for (int q = 0; q < key_bytes; ++q) {
+            u32* out = tmp[q & 1];
+            pass(in, 2, out, 0, q, q + 1 < key_bytes ? 0 : -1, q + 1);
+            in = out;
+        }
+        const i64 live = n - (i64)full_nodes(lds_from);
+        timer.begin("k_wtag_planar", (double)live * (4.0 + 8.0 * k + 4));
+        k_wtag_planar<<<grid_for(live, kBlock, 1 << 16), kBlock, 0, stream>>>(live, n, k, pts, in, recs1);
+        timer.end();
+        subtrees(recs1);
         return hipGetLastError() == hipSuccess ? KDT_OK : KDT_ERR_HIP;
     }
 
