@@ -25,6 +25,9 @@ Prints ONE JSON line on stdout (progress goes to stderr):
              the counter-measured bytes and GB/s beside them
   cpu_baseline  the CPU oracle on bounded samples of the same recipe: all
              host threads (value) and one thread, with the CPU model
+  graph      the same build captured once into a HIP graph and replayed
+             --steps times (ms_per_step and Mpoints/s); value above stays the
+             eager one (--no-graph skips it)
 
 With --widest it times the split-widest-dimension build of the same workload
 instead (value, roofline and cpu_baseline as above, for that variant).
@@ -287,7 +290,7 @@ def counter_runs(workload, widest=False):
             d = os.path.join(tmp, counters[0])
             cmd = ["timeout", "-s", "KILL", "300", prof, "--pmc", *counters, "--output-format", "csv",
                    "-d", d, "-o", "kdt", "--", sys.executable, os.path.abspath(__file__),
-                   "--workload", workload, "--steps", "1", "--warmup", "1", "--no-profile",
+                   "--workload", workload, "--steps", "1", "--warmup", "1", "--no-profile", "--no-graph",
                    "--no-cpu-baseline", "--no-counters", "--calibration-copy"] + (["--widest"] if widest else [])
             r = subprocess.run(cmd, stdout=subprocess.DEVNULL, stderr=subprocess.PIPE, text=True)
             files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
@@ -340,6 +343,8 @@ def main():
     ap.add_argument("--cpu-sample-one", type=int, default=1 << 20,
                     help="points of the single-thread CPU oracle run")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event loop")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip timing the build captured into a HIP graph and replayed")
     ap.add_argument("--no-counters", action="store_true",
                     help="skip the rocprofv3 counter runs behind roofline.traffic and the kernels' counter bytes")
     ap.add_argument("--widest", action="store_true", help="time the split-widest-dimension build")
@@ -421,6 +426,33 @@ def main():
     value = n / (ms_per_step * 1e-3) / 1e6
     log("bench: %.3f ms/build (wall %.3f ms), %.1f Mpoints/s"
         % (ms_per_step, wall * 1e3 / args.steps, value))
+
+    graph = None
+    if not args.no_graph:
+        # The same build captured once into a HIP graph and replayed: the
+        # kernels are the same, the host's per-launch work is gone (what a
+        # caller that rebuilds in fixed buffers pays).
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            builder.build(x, perm, tree)
+        stream.wait_stream(side)
+        torch.cuda.synchronize(dev)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            builder.build(x, perm, tree)
+        g.replay()
+        torch.cuda.synchronize(dev)
+        start.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        stop.record(stream)
+        torch.cuda.synchronize(dev)
+        gms = start.elapsed_time(stop) / args.steps
+        graph = {"ms_per_step": round(gms, 4), "value": round(n / (gms * 1e-3) / 1e6, 2), "unit": "Mpoints/s",
+                 "note": "one build captured into a HIP graph, %d replays" % args.steps}
+        log("bench: graph replay %.3f ms/build, %.1f Mpoints/s" % (gms, graph["value"]))
+        del g
 
     roofline, kernels = None, None
     if not args.no_profile:
@@ -542,6 +574,7 @@ def main():
                    "description": w.note},
         "roofline": roofline,
         "cpu_baseline": base,
+        "graph": graph,
         "kernels": kernels,
     }
     print(json.dumps(out), flush=True)
