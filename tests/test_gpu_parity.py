@@ -135,13 +135,16 @@ def test_columns_stage_dimension_mix(torch_dev, n, k):
 
 
 @pytest.mark.parametrize("n,k", [(65536, 4), (65536, 5), (300000, 7), (300000, 8), (1100000, 9),
-                                 (1100000, 10), (12289, 5), (32768, 6)])
+                                 (1100000, 10), (12289, 5), (32768, 6), (300000, 6), (1100000, 6),
+                                 (1100000, 8), (300000, 5)])
 def test_tag_rounds_boundaries(torch_dev, n, k):
-    """Global rounds by per-point tags need k >= l0 >= 4 and k > 3: these
-    sizes put k at l0 (4, 7, 9 global rounds) and one above it, where round 8
-    sorts two bytes of node offset (1,100,000 points), against the per-array
-    rounds just outside the condition (12,289 points: 2 global rounds;
-    32,768: 3), with ties, signed zeros and duplicates."""
+    """Global rounds by per-point tags need l0 >= 4, k > 3 and either
+    k >= l0 or k >= 6: these sizes put k at l0 (4, 7, 9 global rounds) and
+    one above it, where round 8 sorts two bytes of node offset (1,100,000
+    points); k = 6 and 8 below l0, where dimensions repeat across the rounds;
+    and the per-array rounds just outside the condition (12,289 points: 2
+    global rounds; 32,768: 3; k = 5 below 7 rounds), with ties, signed zeros
+    and duplicates."""
     for gen in ("ties", "zeros", "gmm"):
         pts = make(gen, n, k, 700 + n % 89 + k)
         say("case tag rounds gen=%s N=%d k=%d" % (gen, n, k))

@@ -1628,13 +1628,13 @@ __global__ __launch_bounds__(kBlock) void k_pivots(const u32* __restrict__ recs,
         for (int d = 0; d < k; ++d) tree[s * k + d] = pts[(u64)idx * k + d];
 }
 
-// Rounds by per-point tags (every round splits a new dimension, k >= R, and
-// records of every coordinate above it would be wide): each point keeps the
-// node it is in as a 32-bit tag, in index order, with kFixedTag set once it
-// is its node's pivot. Round l brings every tag from level l-1 to level l
-// (the point against its node's pivot by (key, index) in dimension l-1: the
-// left child below it, the right one above), then writes the point's record
-// for the round's sort: (key in dimension l, node offset on level l, 0, index),
+// Rounds by per-point tags (tag_rounds: many dimensions, whose arrays would
+// each cost a pass a round): each point keeps the node it is in as a 32-bit
+// tag, in index order, with kFixedTag set once it is its node's pivot. Round
+// l brings every tag from level l-1 to level l (the point against its node's
+// pivot by (key, index) in dimension (l-1) mod k: the left child below it,
+// the right one above), then writes the point's record for the round's sort:
+// (key in dimension l mod k, node offset on level l, 0, index),
 // a fixed point's node offset ~0 so that it sorts after every live one
 // ([W], tag paragraph: the tag is the node; sort order paragraph).
 constexpr u32 kFixedTag = 0x80000000u;
@@ -1645,19 +1645,19 @@ __device__ __forceinline__ u32 tag_descend(u32 t, u32 key, u32 p, const u64* __r
     return me == pv ? (t | kFixedTag) : (me < pv ? 2 * t + 1 : 2 * t + 2);
 }
 
-__global__ __launch_bounds__(kBlock) void k_tag_level(i64 n, int l, const u32* __restrict__ planar0,
+__global__ __launch_bounds__(kBlock) void k_tag_level(i64 n, int l, int k, const u32* __restrict__ planar0,
                                                       const u64* __restrict__ piv, u32* __restrict__ tags,
                                                       u32* __restrict__ recs) {
     const i64 stride = (i64)gridDim.x * kBlock;
     const u32 fl = (u32)full_nodes(l);
+    const u64 plane = (u64)(l % k) * (u64)n, above = (u64)((l + k - 1) % k) * (u64)n;  // dimensions l, l-1
     for (i64 p = (i64)blockIdx.x * kBlock + threadIdx.x; p < n; p += stride) {
         u32 t = 0;
-        if (l > 0) t = tag_descend(tags[p], planar0[(u64)(l - 1) * (u64)n + p], (u32)p, piv);
+        if (l > 0) t = tag_descend(tags[p], planar0[above + p], (u32)p, piv);
         tags[p] = t;
         // (every record keeps its key: the first pass's digits come from it;
         // word 2 is padding, so that a record is one 16-byte access)
-        reinterpret_cast<uint4*>(recs)[p] =
-            make_uint4(planar0[(u64)l * (u64)n + p], t & kFixedTag ? ~0u : t - fl, 0u, (u32)p);
+        reinterpret_cast<uint4*>(recs)[p] = make_uint4(planar0[plane + p], t & kFixedTag ? ~0u : t - fl, 0u, (u32)p);
     }
 }
 
@@ -1667,13 +1667,13 @@ __global__ __launch_bounds__(kBlock) void k_tag_level(i64 n, int l, const u32* _
 // node P of that level contributes its left child's points (3 (P - F(R-1))),
 // its pivot (+1), then its right child's points (+2); points fixed before
 // level R-1 sort last. Also the first sort pass's digit (the key's low byte).
-__global__ __launch_bounds__(kBlock) void k_tag_subtrees(i64 n, int R, const u32* __restrict__ planar0,
+__global__ __launch_bounds__(kBlock) void k_tag_subtrees(i64 n, int R, int k, const u32* __restrict__ planar0,
                                                          const u64* __restrict__ piv, const u32* __restrict__ tags,
                                                          u32* __restrict__ recs, u8* __restrict__ digits) {
     const i64 stride = (i64)gridDim.x * kBlock;
     const u32 fp = (u32)full_nodes(R - 1), fp1 = (u32)full_nodes(R);
     for (i64 p = (i64)blockIdx.x * kBlock + threadIdx.x; p < n; p += stride) {
-        const u32 t = tag_descend(tags[p], planar0[(u64)(R - 1) * (u64)n + p], (u32)p, piv);
+        const u32 t = tag_descend(tags[p], planar0[(u64)((R - 1) % k) * (u64)n + p], (u32)p, piv);
         u32 key;
         if (t & kFixedTag) {
             const u32 node = t & ~kFixedTag;
@@ -3594,9 +3594,16 @@ struct Layout {
 inline bool stage_from_records(int k, int rounds) { return rounds > 0 && k <= rounds && k <= kCachedDims; }
 
 // Whether a build's global rounds run by per-point tags (run_global_tags):
-// every round splits a new dimension (k >= rounds) and there are at least
-// four of them (the planar copy of the rounds' keys exists).
-inline bool tag_rounds(int k, int rounds) { return rounds >= 4 && k >= rounds && k > kCachedDims; }
+// at least four of them (the planar copy of the rounds' keys exists), k > 3,
+// and either every round splits a new dimension (k >= rounds) or k is at
+// least kTagDims. Per-dimension arrays cost a pass over each of them per
+// round, tags a fixed number of 16-byte passes; normal points, arrays
+// against tags: 4M points k = 5 2.53 / 2.90 ms, k = 6 3.07 / 2.98, k = 8
+// 4.46 / 3.13; 16M points k = 5 11.28 / 11.48, k = 8 19.92 / 11.99.
+constexpr int kTagDims = 6;
+inline bool tag_rounds(int k, int rounds) {
+    return rounds >= 4 && k > kCachedDims && (k >= rounds || k >= kTagDims);
+}
 
 // Workspace of `rounds` global rounds and, with `stage`, of the subtree stage.
 bool make_layout(i64 n, int k, int rounds, bool stage, Layout* out) {
@@ -4214,13 +4221,13 @@ bool make_layout_unique(i64 n, int k, UniqueLayout* out) {
     return true;
 }
 
-// Global rounds 0 .. R-1 by per-point tags (tag_rounds: every round splits a
-// new dimension). Round l sorts every point by (node on level l, key in
-// dimension l, index): stable LSD passes from index order, four over the key
+// Global rounds 0 .. R-1 by per-point tags (tag_rounds). Round l sorts every
+// point by (node on level l, key in dimension l mod k, index): stable LSD
+// passes from index order, four over the key
 // and then over the node offset, so the index breaks the ties; each node's
 // pivot then sits at its closed-form position (k_pivots). Records are four
-// words (one vector access) whatever k is, where per-dimension arrays would carry the keys of
-// every dimension a round above walks. After the last round the points are
+// words (one vector access) whatever k is, where per-dimension arrays would each need a pass
+// a round (or, with k >= R, carry the keys of every dimension a round above walks). After the last round the points are
 // sorted into round R-1's order for the subtree stage: *last holds two-word
 // records (position key, index), the index alone for the stage to read.
 kdt_status run_global_tags(const float* pts, i64 n, int k, const Layout& lay, char* ws,
@@ -4260,7 +4267,7 @@ kdt_status run_global_tags(const float* pts, i64 n, int k, const Layout& lay, ch
     for (int l = 0; l < R; ++l) {
         // tags and two keys in (one key on level 0), tags and records out
         timer.begin("k_tag_level", (double)n * (l > 0 ? 32.0 : 24.0) + (l > 0 ? 8.0 * full_nodes(l) : 0));
-        k_tag_level<<<grid, kBlock, 0, stream>>>(n, l, planar0, piv, tags, recs0);
+        k_tag_level<<<grid, kBlock, 0, stream>>>(n, l, k, planar0, piv, tags, recs0);
         timer.end();
         // four key bytes, then the node offset's bytes (offsets below 2^l;
         // a fixed point's ~0 must compare above them: (l + 8) / 8 bytes)
@@ -4269,7 +4276,7 @@ kdt_status run_global_tags(const float* pts, i64 n, int k, const Layout& lay, ch
         for (int q = 0; q < passes; ++q) {
             u32* out = tmp[q & 1];
             const int nq = q + 1;
-            pass(in, 4, out, q < 4 ? 0 : 1, q < 4 ? q : q - 4, q == 0 ? digits0 + (size_t)l * n : digits,
+            pass(in, 4, out, q < 4 ? 0 : 1, q < 4 ? q : q - 4, q == 0 ? digits0 + (size_t)(l % k) * n : digits,
                  nq < passes ? (nq < 4 ? 0 : 1) : -1, nq < 4 ? nq : nq - 4);
             in = out;
         }
@@ -4279,7 +4286,7 @@ kdt_status run_global_tags(const float* pts, i64 n, int k, const Layout& lay, ch
         timer.end();
     }
     timer.begin("k_tag_subtrees", (double)n * (4.0 + 4 + 8 + 1) + 8.0 * full_nodes(R));
-    k_tag_subtrees<<<grid, kBlock, 0, stream>>>(n, R, planar0, piv, tags, recs0, digits);
+    k_tag_subtrees<<<grid, kBlock, 0, stream>>>(n, R, k, planar0, piv, tags, recs0, digits);
     timer.end();
     // position keys below 3 * 2^(R-1) < 2^(R+1), ~0 above them
     const int key_bytes = (R + 1 + 7) / 8;
