@@ -3627,8 +3627,9 @@ bool make_layout(i64 n, int k, int rounds, bool stage, Layout* out) {
         lay.kr = k < rounds ? k : rounds;
         lay.words = lay.kr + 1;
         // every dimension used again keeps its array, plus one to re-sort
-        // into (a dimension used once needs its array only for its round)
-        lay.nbuf = (k < rounds ? k : 1) + 1;
+        // into (a dimension used once needs its array only for its round);
+        // tag rounds: their records and the subtree stage's
+        lay.nbuf = stage && tag_rounds(k, rounds) ? 2 : (k < rounds ? k : 1) + 1;
         lay.tiles = (n + kPartTile - 1) / kPartTile;
         const size_t rec_bytes = (size_t)n * lay.words * sizeof(u32);
         lay.tmp0 = take(rec_bytes);  // presort pass outputs
