@@ -186,10 +186,10 @@ void kdt_closed_float_keys(const uint32_t* bits, int64_t n, uint32_t* keys_out);
  *   dims_out  device, N int32 or NULL: dims_out[s] = split dimension of
  *             node s (every node, leaves included).
  * Other arguments, ownership and errors as kdt_build; the workspace is
- * kdt_workspace_size_widest(N, k) bytes. Every array finds its own nodes'
- * pivots on every global level, and for k <= 3 subtrees of at most 4096
- * points finish in LDS (for larger k every level is a global pass), so a
- * build costs more than kdt_build's. */
+ * kdt_workspace_size_widest(N, k) bytes. Subtrees of at most 4096 points
+ * finish in LDS. Above them, for k <= 3 each dimension's array finds its
+ * own nodes' pivots on every level, so a build costs more than kdt_build's;
+ * for k > 3 every level sorts all points by their node's own dimension. */
 size_t kdt_workspace_size_widest(int64_t N, int32_t k);
 kdt_status kdt_build_widest(const float* points, int64_t N, int32_t k,
                             int32_t* perm_out, float* tree_out, int32_t* dims_out,
